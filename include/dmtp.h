@@ -1,0 +1,264 @@
+/*
+ * dmtp.h -- C ABI of one DMTP speculative-decoding round on MI355X (gfx950).
+ *
+ * The round the pages define ("DMTP: A Better First Token for Block Drafting
+ * via MTP", sections 2, 3 and 5): the MTP head proposes the first candidate T1
+ * from a fused hidden state, a residual built from T1's embedding and the MTP
+ * hidden is added to T1's embedding slot, one parallel block-draft forward over
+ * [E(A), E(T1)+Delta, E(MASK)...] proposes the remaining candidates, and the
+ * target verifies all of them, committing the accepted prefix plus one
+ * correction or bonus token.  Four calls cover it:
+ *
+ *   dmtp_fuse         RMSNorm-concat-projection (MTP input fusion; DMTP residual)
+ *   dmtp_block_draft  the block drafter's layers and final norm
+ *   dmtp_lm_head      the shared vocabulary head with argmax / sampling
+ *   dmtp_verify       greedy or rejection-sampling block verification
+ *
+ * Conventions (all calls)
+ *   - Tensor pointers are DEVICE pointers to row-major, contiguous data,
+ *     16-byte aligned; sizes are element counts.  Weight matrices are stored
+ *     [out, in].  Ids are int32, logits/probabilities/lse are float32.
+ *   - `dtype` (DMTP_F32 or DMTP_BF16) is the storage type of weights,
+ *     embeddings, context K/V and the rows that enter the LM head.  All other
+ *     activations (fused hidden, residual stream) are float32.  bf16 is stored
+ *     as its 16-bit pattern.  Gains are float32 [H].
+ *   - Ownership: the caller owns every buffer, including the workspace
+ *     `ws` of the size the matching *_ws() query returns.  The library never
+ *     allocates, frees, synchronises or copies to the host.  Each call only
+ *     enqueues kernels on the caller's stream and can be captured in a graph.
+ *   - Errors: every call returns an int status.  Negative values are argument
+ *     errors found on the host BEFORE anything is enqueued (nothing has run).
+ *     DMTP_E_LAUNCH reports a failed kernel launch.  Device-side faults surface
+ *     at the caller's next synchronisation.  Shapes the kernels do not support
+ *     are refused, never silently degraded.
+ *   - The library holds no state across calls and is safe to call from
+ *     several host threads on different streams; calls that share output or
+ *     workspace buffers must be ordered by the caller.
+ */
+#ifndef DMTP_H
+#define DMTP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DMTP_ABI_VERSION 1
+
+enum dmtp_status {
+  DMTP_OK = 0,
+  DMTP_E_NULL = -1,      /* a required pointer is NULL */
+  DMTP_E_SHAPE = -2,     /* a size is out of the supported range */
+  DMTP_E_DTYPE = -3,     /* unknown or unsupported dtype */
+  DMTP_E_WORKSPACE = -4, /* workspace smaller than the *_ws() query */
+  DMTP_E_ALIGN = -5,     /* a pointer is not 16-byte aligned */
+  DMTP_E_DEVICE = -6,    /* the current device is not gfx950 */
+  DMTP_E_LAUNCH = -7,    /* a kernel launch failed */
+  DMTP_E_ARG = -8        /* an inconsistent combination of arguments */
+};
+
+enum dmtp_dtype { DMTP_F32 = 0, DMTP_BF16 = 1 };
+
+/* draw_key value of a row that takes the argmax even when its temperature is
+ * positive (its lse is still taken at that temperature). */
+#define DMTP_NO_DRAW 0xFFFFFFFFFFFFFFFFull
+
+/* Rows of a fusion input: either `rows` [n, H] in `dtype` (row stride H), or,
+ * when rows == NULL, the gather table[ids[r]] with table [V, H] in the call's
+ * weight dtype.  A dmtp_rows with rows == NULL and ids == NULL is "absent". */
+typedef struct {
+  const void* rows;
+  int32_t dtype;          /* DMTP_F32 or DMTP_BF16 (rows mode) */
+  const int32_t* ids;     /* [n], each in [0, table_rows) */
+  const void* table;
+  int32_t table_rows;
+} dmtp_rows;
+
+/* ---------------------------------------------------------------- fuse ----
+ * out[r] = res[r] + W [RMSNorm(x1[r]; g1); RMSNorm(x2[r]; g2)]
+ * RMSNorm(x; g) = x / sqrt(mean(x^2) + eps) * g.  W is [H, 2H] in w_dtype:
+ * columns [0, H) act on the normalised x1, [H, 2H) on the normalised x2.
+ *   MTP input fusion ("DFlash vs MTP", "MTP: Sequential Prediction Heads
+ *   Trained With the Model": h' = M[RMSNorm(h); RMSNorm(Emb(t))]):
+ *       x1 = target hidden rows, x2 = ids of the pending token A, res absent.
+ *   DMTP residual (DMTP blog section 3, the Delta and e~ equations):
+ *       x1 = ids T1, x2 = MTP hidden rows, res = ids T1 (E(T1) + Delta).
+ * out is float32 [rows, H].  Zero W returns res bit for bit. */
+typedef struct {
+  int32_t rows;           /* >= 1 */
+  int32_t H;              /* multiple of 64, <= 16384 */
+  int32_t w_dtype;        /* dtype of W and of id-gathered tables */
+  float eps;
+  dmtp_rows x1, x2, res;  /* res may be absent */
+  const float* g1;        /* [H] */
+  const float* g2;        /* [H] */
+  const void* W;          /* [H, 2H] */
+  float* out;             /* [rows, H] */
+} dmtp_fuse_desc;
+
+size_t dmtp_fuse_ws(const dmtp_fuse_desc* d);
+int dmtp_fuse(const dmtp_fuse_desc* d, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------- block draft ----
+ * The block drafter ("DFlash vs MTP", "DFlash: Block Diffusion as a Draft
+ * Model"; DMTP blog sections 3 and 6.2).  Per sequence b the S = K - 1 +
+ * n_anchor slots are
+ *     n_anchor = 2:  [E(anchor_ids[b]), x_t1[b], E(mask_id) x (K-1)]
+ *     n_anchor = 1:  [x_t1[b], E(mask_id) x (K-1)]
+ * at positions ctx_len[b] + j (ctx_len[b] = cu_ctx[b+1] - cu_ctx[b], which must
+ * not exceed max_ctx).  Each layer: x^ = RMSNorm(X; g_attn); q, k, v
+ * = x^ Wqkv^T (rows of Wqkv: Hq query heads, Hkv key heads, Hkv value heads,
+ * d each); rotary embedding (rotate-half, base rope_base) on block q and k;
+ * every slot attends, with no mask, to the context keys of its own sequence
+ * (the last `window` when window > 0) and to all S block keys; GQA maps
+ * query head h to kv head h / (Hq / Hkv); X1 = X + o Wo^T; X = X1 +
+ * (silu(x^2 Wg^T) * (x^2 Wu^T)) Wd^T with x^2 = RMSNorm(X1; g_ffn).  After the
+ * last layer the MASK slots (slots n_anchor .. S-1) are written as
+ * RMSNorm(X; g_final) rounded to dtype: out [B, K-1, H] -- the LM-head input
+ * of candidates 1 .. K-1.  Context keys are supplied already rotated. */
+typedef struct {
+  const float* g_attn;    /* [H] */
+  const void* wqkv;       /* [(Hq + 2 Hkv) d, H] */
+  const void* wo;         /* [H, Hq d] */
+  const float* g_ffn;     /* [H] */
+  const void* wg;         /* [F, H] */
+  const void* wu;         /* [F, H] */
+  const void* wd;         /* [H, F] */
+  const void* ctx_k;      /* [sum ctx_len, Hkv, d]  (sequence b at rows cu_ctx[b] ..) */
+  const void* ctx_v;      /* [sum ctx_len, Hkv, d] */
+} dmtp_layer;
+
+typedef struct {
+  int32_t B, H, Hq, Hkv, d, F, n_layers, K, n_anchor, dtype;
+  float eps;
+  float rope_base;
+  int32_t window;         /* 0 = whole context */
+  int32_t max_ctx;        /* host-side upper bound of ctx_len[b] (plans the split) */
+  int32_t ctx_rows;       /* rows of ctx_k / ctx_v; sequences are clamped to them */
+  int32_t V;              /* rows of emb */
+  const int32_t* anchor_ids;  /* [B] (unused when n_anchor == 1) */
+  const float* x_t1;      /* [B, H] float32 (output of the DMTP residual fusion) */
+  int32_t mask_id;
+  const void* emb;        /* [V, H] */
+  const int32_t* cu_ctx;  /* [B + 1] prefix sums of the context lengths */
+  const dmtp_layer* layers;   /* HOST array of n_layers entries */
+  const float* g_final;   /* [H] */
+  void* out;              /* [B, K - 1, H] in dtype */
+} dmtp_draft_desc;
+
+size_t dmtp_block_draft_ws(const dmtp_draft_desc* d);
+int dmtp_block_draft(const dmtp_draft_desc* d, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* -------------------------------------------------------------- LM head ----
+ * The shared vocabulary head ("DFlash vs MTP": shared output head; DMTP blog
+ * section 6.5: it reads the whole [V, H] matrix for every row).  The M rows
+ * are the concatenation of up to 4 segments.  A segment with g_norm != NULL
+ * holds float32 hidden rows that are first mapped to RMSNorm(x; g_norm) and
+ * rounded to dtype; otherwise its rows are already the head input, in dtype.
+ * logits = W x (W [V, H]).  Per row m:
+ *   temperature[m] == 0 (or temperature == NULL): token = argmax (lowest
+ *       index among equal maxima), gap = top-1 minus top-2 logit;
+ *   temperature[m] > 0 and draw_key[m] != DMTP_NO_DRAW: token is a draw from
+ *       softmax(logits / t) taken as
+ *       argmax_j (logits_j / t + g_j), g the Gumbel noise of Philox4x64-10
+ *       draw (seed, draw_key[m]) -- word j of counter (j >> 3, key, 0, 0)
+ *       under key (seed, 0), 64-bit output (j & 7) >> 1, low half if j even;
+ *       g = -log(-log1p(-(x + 1/2) 2^-32)).  gap = top-2 gap of that score.
+ *       Such rows need store_row[m] >= 0 (else token = -1).
+ *   temperature[m] > 0 and draw_key[m] == DMTP_NO_DRAW: argmax, as greedy.
+ *   row_max = max logit; lse = logsumexp(logits / t) (t = 1 when 0).
+ *   store_row[m] >= 0 writes the float32 logits row to logits[store_row[m]].
+ *   plant_row[m] in [0, M) replaces the row's token by the argmax of row
+ *       plant_row[m] of the same call (a workload whose first candidate is
+ *       set to the target's choice).
+ * Ids, offsets and row indices read from device memory are range-checked in
+ * the kernels: an out-of-range embedding id reads a zero row, an
+ * out-of-range store or plant index is ignored, so bad data never leads to
+ * an out-of-bounds access.
+ * Results do not depend on M or on the other rows (row-wise arithmetic). */
+typedef struct {
+  const void* x;          /* [n, ld] rows */
+  int32_t n;              /* rows in this segment (may be 0) */
+  int32_t ld;             /* row stride in elements, >= H */
+  int32_t dtype;          /* DMTP_F32 when g_norm is set, else the head dtype */
+  const float* g_norm;    /* [H] or NULL */
+} dmtp_head_segment;
+
+typedef struct {
+  int32_t H;              /* multiple of 64 */
+  int32_t V;              /* >= 2 */
+  int32_t dtype;          /* dtype of W and of the head input */
+  float eps;
+  int32_t n_seg;          /* 1 .. 4 */
+  dmtp_head_segment seg[4];
+  const void* W;          /* [V, H] */
+  const float* temperature;   /* [M] or NULL: all greedy */
+  const uint64_t* draw_key;   /* [M], required when temperature != NULL */
+  uint64_t seed;
+  const int32_t* plant_row;   /* [M] or NULL */
+  const int32_t* store_row;   /* [M] or NULL */
+  float* logits;              /* [logits_rows, V] */
+  int32_t logits_rows;        /* store_row values >= logits_rows are not stored */
+  void* prepared;             /* optional [M, H] in dtype: the head input rows */
+  int32_t* token;             /* [M] */
+  float* row_max;             /* [M] or NULL */
+  float* lse;                 /* [M] or NULL */
+  float* gap;                 /* [M] or NULL */
+} dmtp_head_desc;
+
+size_t dmtp_lm_head_ws(const dmtp_head_desc* d);
+int dmtp_lm_head(const dmtp_head_desc* d, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* --------------------------------------------------------------- verify ----
+ * Block verification (DMTP blog section 5 step 3; the colibri notes on
+ * verify semantics; Leviathan et al. as cited by "DFlash vs MTP").  Per
+ * sequence b the candidates are d_0 = t1[b], d_i = drafts[b][i-1]; target row
+ * i (i = 0..K) is the target after the prefix and d_0 .. d_{i-1}.
+ *   temperature[b] == 0: L = first i < K with d_i != target[b][i] (else K);
+ *       commit d_0 .. d_{L-1}, target[b][L].
+ *   temperature[b] = t > 0: with p_i = softmax(lp_i / t), q_i =
+ *       softmax(lq_i / t) from the float32 logits rows of the sequence
+ *       (logits[b][i] = lq_i for i < K, logits[b][K + i] = lp_i), accept d_i
+ *       iff u_acc[b][i] < p_i(d_i) / q_i(d_i); at the first rejection i draw
+ *       the correction from normalize(max(0, p_i - q_i)) (from p_i if that is
+ *       zero); if all K are accepted draw the bonus from p_K.  Draws are
+ *       Gumbel-max over Philox draw (seed, final_key[b]), the layout of
+ *       dmtp_lm_head.  Needs the lse of every row (lse of logits / t).
+ * out_tokens [B, K+1] is -1 padded, n_out = accept_len + 1. */
+typedef struct {
+  int32_t B, K, V;
+  const int32_t* t1;          /* [B] */
+  const int32_t* drafts;      /* [B, K - 1] */
+  const int32_t* target;      /* [B, K + 1] target argmax per row */
+  const float* temperature;   /* [B] or NULL: all greedy */
+  const float* logits;        /* [B, 2K + 1, V], rows of sampled sequences only */
+  const float* t1_lse;        /* [B] */
+  const float* draft_lse;     /* [B, K - 1] */
+  const float* target_lse;    /* [B, K + 1] */
+  const float* u_acc;         /* [B, K] uniforms in [0, 1) */
+  uint64_t seed;
+  const uint64_t* final_key;  /* [B] */
+  int32_t* accept_len;        /* [B] */
+  int32_t* out_tokens;        /* [B, K + 1] */
+  int32_t* n_out;             /* [B] */
+} dmtp_verify_desc;
+
+size_t dmtp_verify_ws(const dmtp_verify_desc* d);
+int dmtp_verify(const dmtp_verify_desc* d, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------- helpers ---- */
+const char* dmtp_status_str(int status);
+const char* dmtp_version(void);
+/* sizeof of the descriptor structs, for bindings to check their layout:
+ * which = 0 rows, 1 fuse, 2 layer, 3 draft, 4 head segment, 5 head, 6 verify */
+size_t dmtp_struct_size(int which);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DMTP_H */

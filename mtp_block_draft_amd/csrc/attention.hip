@@ -1,0 +1,413 @@
+// Block attention of the drafter: every block slot's query reads all context
+// keys of its sequence (or the last `window`) and all S block keys, no mask.
+//
+// Work split: one workgroup per (context chunk, kv head, sequence).  The query
+// rows of a workgroup are the S slots x G query heads that share the kv head,
+// so GQA costs one pass over each context tile.  Context K/V tiles of 64 keys
+// are staged in LDS (V transposed so that the PV product reads it
+// K-contiguously); S = Q K^T and O += P V run on bf16 matrix cores, with the
+// float32 queries and probabilities split into hi/lo bf16 planes.  Each chunk
+// leaves an unnormalised partial (O, running max m, running sum l); a combine
+// kernel merges the chunks exactly and adds the S block keys in float32.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace dmtp {
+
+namespace {
+
+constexpr int kAttnThreads = 256;
+constexpr int KT = 64;  // keys per LDS tile
+constexpr size_t kLdsLimit = 160 * 1024;
+
+template <int RT, int D, int KVP>
+struct AttnCfg {
+  static constexpr int NQP = 16 * RT;          // padded query rows
+  static constexpr int LDQ = D + 8;            // bf16 row stride of Q and K tiles
+  static constexpr int LDT = KT + 8;           // bf16 row stride of V^T and P tiles
+  static constexpr int Q_ELEMS = 2 * NQP * LDQ;
+  static constexpr int K_ELEMS = KVP * KT * LDQ;
+  static constexpr int V_ELEMS = KVP * D * LDT;
+  static constexpr int P_ELEMS = 2 * NQP * LDT;
+  static constexpr int OT = RT * (D / 16);     // 16x16 output tiles
+  static constexpr int OT_PER_WAVE = (OT + 3) / 4;
+  static constexpr size_t LDS_BYTES =
+      (size_t)(Q_ELEMS + K_ELEMS + V_ELEMS + P_ELEMS) * 2 + (size_t)NQP * KT * 4 + (size_t)3 * NQP * 4;
+};
+
+template <int RT, int D, int KVP>
+__global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(
+    const float* __restrict__ q, const void* __restrict__ ctx_k, const void* __restrict__ ctx_v,
+    const int32_t* __restrict__ cu_ctx, int ctx_rows, int Hkv, int NQ, int chunk, int n_chunks,
+    int window, float scale, float* __restrict__ part_o, float* __restrict__ part_ml) {
+  typedef AttnCfg<RT, D, KVP> C;
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  uint16_t* Qs = smem;                      // [2][NQP][LDQ]
+  uint16_t* Ks = Qs + C::Q_ELEMS;           // [KVP][KT][LDQ]
+  uint16_t* Vt = Ks + C::K_ELEMS;           // [KVP][D][LDT]
+  uint16_t* Ps = Vt + C::V_ELEMS;           // [2][NQP][LDT]
+  float* Ss = (float*)(Ps + C::P_ELEMS);    // [NQP][KT]
+  float* m_run = Ss + C::NQP * KT;
+  float* l_run = m_run + C::NQP;
+  float* alpha = l_run + C::NQP;
+
+  const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int L = ctx_len_of(cu_ctx, b, ctx_rows);
+  const int start = (window > 0 && L > window) ? L - window : 0;
+  const int k_lo = start + c * chunk;
+  const int k_hi = min(k_lo + chunk, L);
+  const size_t pbase = (((size_t)b * Hkv + kvh) * n_chunks + c);
+  float* po = part_o + pbase * C::NQP * D;
+  float* pml = part_ml + pbase * 2 * C::NQP;
+  if (k_lo >= k_hi) {  // empty chunk: neutral partial
+    for (int r = threadIdx.x; r < C::NQP; r += blockDim.x) {
+      pml[r] = -INFINITY;
+      pml[C::NQP + r] = 0.f;
+    }
+    return;
+  }
+
+  // queries -> two bf16 planes
+  const float* qg = q + ((size_t)b * Hkv + kvh) * NQ * D;
+  for (int e = threadIdx.x; e < C::NQP * D; e += blockDim.x) {
+    const int r = e / D, k = e % D;
+    const float v = r < NQ ? qg[(size_t)r * D + k] : 0.f;
+    uint16_t hi, lo;
+    split_bf16(v, hi, lo);
+    Qs[r * C::LDQ + k] = hi;
+    Qs[C::NQP * C::LDQ + r * C::LDQ + k] = lo;
+  }
+  for (int r = threadIdx.x; r < C::NQP; r += blockDim.x) {
+    m_run[r] = -INFINITY;
+    l_run[r] = 0.f;
+  }
+
+  f32x4_t acc[C::OT_PER_WAVE];
+#pragma unroll
+  for (int t = 0; t < C::OT_PER_WAVE; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const size_t row_stride = (size_t)Hkv * D;      // elements between consecutive keys
+  const size_t seq0 = (size_t)cu_ctx[b];
+  const int fr = lane & 15, fk = (lane >> 4) * 8;
+
+  for (int kt = k_lo; kt < k_hi; kt += KT) {
+    const int nk = min(KT, k_hi - kt);
+    // ---- stage K [KT][D] and V^T [D][KT]
+    if (KVP == 1) {
+      const uint16_t* kg = (const uint16_t*)ctx_k;
+      const uint16_t* vg = (const uint16_t*)ctx_v;
+      for (int e = threadIdx.x; e < KT * D / 8; e += blockDim.x) {
+        const int key = e / (D / 8), c8 = e % (D / 8);
+        uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+        if (key < nk) {
+          const size_t off = (seq0 + kt + key) * row_stride + (size_t)kvh * D + 8 * c8;
+          kv = *(const uint4*)(kg + off);
+          vv = *(const uint4*)(vg + off);
+        }
+        *(uint4*)(Ks + key * C::LDQ + 8 * c8) = kv;
+        const uint16_t* vh = (const uint16_t*)&vv;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) Vt[(8 * c8 + j) * C::LDT + key] = vh[j];
+      }
+    } else {
+      const float* kg = (const float*)ctx_k;
+      const float* vg = (const float*)ctx_v;
+      for (int e = threadIdx.x; e < KT * D / 4; e += blockDim.x) {
+        const int key = e / (D / 4), c4 = e % (D / 4);
+        float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
+        if (key < nk) {
+          const size_t off = (seq0 + kt + key) * row_stride + (size_t)kvh * D + 4 * c4;
+          kv = *(const float4*)(kg + off);
+          vv = *(const float4*)(vg + off);
+        }
+        const float kf[4] = {kv.x, kv.y, kv.z, kv.w}, vf[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint16_t hi, lo;
+          split_bf16(kf[j], hi, lo);
+          Ks[key * C::LDQ + 4 * c4 + j] = hi;
+          Ks[KT * C::LDQ + key * C::LDQ + 4 * c4 + j] = lo;
+          split_bf16(vf[j], hi, lo);
+          Vt[(4 * c4 + j) * C::LDT + key] = hi;
+          Vt[D * C::LDT + (4 * c4 + j) * C::LDT + key] = lo;
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- S = Q K^T: wave w owns keys 16w .. 16w + 15 for all row tiles
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k0 = 0; k0 < D; k0 += 32) {
+        const uint4 qh = *(const uint4*)(Qs + (16 * rt + fr) * C::LDQ + k0 + fk);
+        const uint4 ql = *(const uint4*)(Qs + C::NQP * C::LDQ + (16 * rt + fr) * C::LDQ + k0 + fk);
+        const uint4 kh = *(const uint4*)(Ks + (16 * wave + fr) * C::LDQ + k0 + fk);
+        s = mfma_16x16x32(qh, kh, s);
+        s = mfma_16x16x32(ql, kh, s);
+        if (KVP == 2) {
+          const uint4 kl = *(const uint4*)(Ks + KT * C::LDQ + (16 * wave + fr) * C::LDQ + k0 + fk);
+          s = mfma_16x16x32(qh, kl, s);
+        }
+      }
+      const int key = 16 * wave + (lane & 15);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * rt + 4 * (lane >> 4) + i;
+        Ss[row * KT + key] = key < nk ? s[i] * scale : -INFINITY;
+      }
+    }
+    __syncthreads();
+
+    // ---- online softmax: four threads per row, 16 keys each
+    for (int t = threadIdx.x; t < C::NQP * 4; t += blockDim.x) {
+      const int row = t >> 2, qd = t & 3;
+      const float* sr = Ss + row * KT + 16 * qd;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sr[j]);
+      mx = fmaxf(mx, __shfl_xor(mx, 1, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 2, kWave));
+      const float m_old = m_run[row];
+      const float m_new = fmaxf(m_old, mx);
+      float sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float p = expf(sr[j] - m_new);
+        sum += p;
+        uint16_t hi, lo;
+        split_bf16(p, hi, lo);
+        Ps[row * C::LDT + 16 * qd + j] = hi;
+        Ps[C::NQP * C::LDT + row * C::LDT + 16 * qd + j] = lo;
+      }
+      sum += __shfl_xor(sum, 1, kWave);
+      sum += __shfl_xor(sum, 2, kWave);
+      if (qd == 0) {
+        const float a = expf(m_old - m_new);   // 0 on the first tile (m_old = -inf)
+        alpha[row] = a;
+        l_run[row] = l_run[row] * a + sum;
+        m_run[row] = m_new;
+      }
+    }
+    __syncthreads();
+
+    // ---- O = alpha O + P V
+#pragma unroll
+    for (int t = 0; t < C::OT_PER_WAVE; ++t) {
+      const int tile = wave + 4 * t;
+      if (tile >= C::OT) break;
+      const int rt = tile / (D / 16), dt = tile % (D / 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[t][i] *= alpha[16 * rt + 4 * (lane >> 4) + i];
+#pragma unroll
+      for (int k0 = 0; k0 < KT; k0 += 32) {
+        const uint4 ph = *(const uint4*)(Ps + (16 * rt + fr) * C::LDT + k0 + fk);
+        const uint4 pl = *(const uint4*)(Ps + C::NQP * C::LDT + (16 * rt + fr) * C::LDT + k0 + fk);
+        const uint4 vh = *(const uint4*)(Vt + (16 * dt + fr) * C::LDT + k0 + fk);
+        acc[t] = mfma_16x16x32(ph, vh, acc[t]);
+        acc[t] = mfma_16x16x32(pl, vh, acc[t]);
+        if (KVP == 2) {
+          const uint4 vl = *(const uint4*)(Vt + D * C::LDT + (16 * dt + fr) * C::LDT + k0 + fk);
+          acc[t] = mfma_16x16x32(ph, vl, acc[t]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- write the unnormalised partial
+#pragma unroll
+  for (int t = 0; t < C::OT_PER_WAVE; ++t) {
+    const int tile = wave + 4 * t;
+    if (tile >= C::OT) break;
+    const int rt = tile / (D / 16), dt = tile % (D / 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * rt + 4 * (lane >> 4) + i;
+      po[(size_t)row * D + 16 * dt + (lane & 15)] = acc[t][i];
+    }
+  }
+  for (int r = threadIdx.x; r < C::NQP; r += blockDim.x) {
+    pml[r] = m_run[r];
+    pml[C::NQP + r] = l_run[r];
+  }
+}
+
+// Merge the chunk partials and the S block keys; o [B * S, Hq * D].
+__global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(
+    const float* __restrict__ q, const float* __restrict__ kb, const float* __restrict__ vb,
+    const float* __restrict__ part_o, const float* __restrict__ part_ml, int Hkv, int G, int S, int D,
+    int NQP, int n_chunks, float scale, float* __restrict__ o) {
+  __shared__ float w_chunk[256];
+  __shared__ float w_blk[64];
+  __shared__ float s_blk[64];
+  __shared__ float inv_l;
+  const int kvh = blockIdx.x % Hkv, b = blockIdx.x / Hkv;
+  const int NQ = S * G;
+  const size_t bh = (size_t)b * Hkv + kvh;
+  const float* qg = q + bh * NQ * D;
+  const float* kbg = kb + bh * S * D;
+  const float* vbg = vb + bh * S * D;
+  for (int r = 0; r < NQ; ++r) {
+    // block-key scores (float32, exact products)
+    for (int j = threadIdx.x; j < S; j += blockDim.x) {
+      float acc = 0.f;
+      for (int k = 0; k < D; ++k) acc = fmaf(qg[(size_t)r * D + k], kbg[(size_t)j * D + k], acc);
+      s_blk[j] = acc * scale;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float M = -INFINITY;
+      for (int c = 0; c < n_chunks; ++c) M = fmaxf(M, part_ml[(bh * n_chunks + c) * 2 * NQP + r]);
+      for (int j = 0; j < S; ++j) M = fmaxf(M, s_blk[j]);
+      float Lsum = 0.f;
+      for (int c = 0; c < n_chunks; ++c) {
+        const float* ml = part_ml + (bh * n_chunks + c) * 2 * NQP;
+        const float w = ml[r] == -INFINITY ? 0.f : expf(ml[r] - M);
+        w_chunk[c] = w;
+        Lsum += w * ml[NQP + r];
+      }
+      for (int j = 0; j < S; ++j) {
+        const float w = expf(s_blk[j] - M);
+        w_blk[j] = w;
+        Lsum += w;
+      }
+      inv_l = 1.0f / Lsum;
+    }
+    __syncthreads();
+    const int s = r / G, g = r % G;
+    float* orow = o + ((size_t)b * S + s) * ((size_t)Hkv * G * D) + ((size_t)kvh * G + g) * D;
+    for (int k = threadIdx.x; k < D; k += blockDim.x) {
+      float acc = 0.f;
+      for (int c = 0; c < n_chunks; ++c)
+        acc += w_chunk[c] * part_o[((bh * n_chunks + c) * NQP + r) * D + k];
+      for (int j = 0; j < S; ++j) acc += w_blk[j] * vbg[(size_t)j * D + k];
+      orow[k] = acc * inv_l;
+    }
+    __syncthreads();
+  }
+}
+
+template <int RT, int D, int KVP>
+hipError_t launch_chunks(const AttnPlan& p, const float* q, const void* ck, const void* cv,
+                         const int32_t* cu, int ctx_rows, float* po, float* pml, float scale,
+                         hipStream_t s) {
+  typedef AttnCfg<RT, D, KVP> C;
+  if constexpr (C::LDS_BYTES > kLdsLimit) {
+    return hipErrorInvalidConfiguration;   // refused on the host by attn_max_nq()
+  }
+  hipError_t e = hipFuncSetAttribute((const void*)attn_chunk_kernel<RT, D, KVP>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES);
+  if (e != hipSuccess) return e;
+  dim3 grid(p.n_chunks, p.Hkv, p.B);
+  hipLaunchKernelGGL((attn_chunk_kernel<RT, D, KVP>), grid, dim3(kAttnThreads), C::LDS_BYTES, s, q,
+                     ck, cv, cu, ctx_rows, p.Hkv, p.NQ, p.chunk, p.n_chunks, p.window, scale, po,
+                     pml);
+  return hipGetLastError();
+}
+
+template <int D, int KVP>
+hipError_t dispatch_rt(const AttnPlan& p, const float* q, const void* ck, const void* cv,
+                       const int32_t* cu, int cr, float* po, float* pml, float scale,
+                       hipStream_t s) {
+  const int rt = (p.NQ + 15) / 16;
+  if (rt <= 1) return launch_chunks<1, D, KVP>(p, q, ck, cv, cu, cr, po, pml, scale, s);
+  if (rt <= 2) return launch_chunks<2, D, KVP>(p, q, ck, cv, cu, cr, po, pml, scale, s);
+  if (rt <= 4) return launch_chunks<4, D, KVP>(p, q, ck, cv, cu, cr, po, pml, scale, s);
+  if (rt <= 6) return launch_chunks<6, D, KVP>(p, q, ck, cv, cu, cr, po, pml, scale, s);
+  return launch_chunks<8, D, KVP>(p, q, ck, cv, cu, cr, po, pml, scale, s);
+}
+
+template <int D, int KVP>
+size_t AttnCfg_bytes(int rt) {
+  switch (rt) {
+    case 1: return AttnCfg<1, D, KVP>::LDS_BYTES;
+    case 2: return AttnCfg<2, D, KVP>::LDS_BYTES;
+    case 4: return AttnCfg<4, D, KVP>::LDS_BYTES;
+    case 6: return AttnCfg<6, D, KVP>::LDS_BYTES;
+    default: return AttnCfg<8, D, KVP>::LDS_BYTES;
+  }
+}
+
+int nqp_of(int NQ) {
+  const int rt = (NQ + 15) / 16;
+  return 16 * (rt <= 1 ? 1 : rt <= 2 ? 2 : rt <= 4 ? 4 : rt <= 6 ? 6 : 8);
+}
+
+}  // namespace
+
+int attn_max_nq(int d, int kv_f32) {
+  auto fits = [&](int rt) -> bool {
+    if (d == 64)
+      return kv_f32 ? AttnCfg_bytes<64, 2>(rt) <= kLdsLimit : AttnCfg_bytes<64, 1>(rt) <= kLdsLimit;
+    return kv_f32 ? AttnCfg_bytes<128, 2>(rt) <= kLdsLimit : AttnCfg_bytes<128, 1>(rt) <= kLdsLimit;
+  };
+  const int rts[5] = {8, 6, 4, 2, 1};
+  for (int rt : rts)
+    if (fits(rt)) return 16 * rt;
+  return 0;
+}
+
+AttnPlan attn_plan(int B, int Hq, int Hkv, int S, int d, int max_ctx, int window, int kv_f32) {
+  AttnPlan p;
+  p.B = B;
+  p.Hkv = Hkv;
+  p.G = Hq / Hkv;
+  p.S = S;
+  p.d = d;
+  p.NQ = S * p.G;
+  p.kv_f32 = kv_f32;
+  p.window = window;
+  const int eff = (window > 0 && max_ctx > window) ? window : max_ctx;
+  if (eff <= 0) {
+    p.chunk = KT;
+    p.n_chunks = 0;
+    return p;
+  }
+  const int pairs = B * Hkv;
+  int want = (1024 + pairs - 1) / pairs;           // chunks per (sequence, kv head)
+  int chunk = (eff + want - 1) / want;
+  chunk = ((chunk + KT - 1) / KT) * KT;
+  if (chunk < 4 * KT && eff > 4 * KT) chunk = 4 * KT;
+  if (chunk < KT) chunk = KT;
+  // the combine merges at most 256 chunk partials per row
+  const int min_chunk = (((eff + 255) / 256 + KT - 1) / KT) * KT;
+  if (chunk < min_chunk) chunk = min_chunk;
+  p.chunk = chunk;
+  p.n_chunks = (eff + chunk - 1) / chunk;
+  return p;
+}
+
+size_t attn_ws_bytes(const AttnPlan& p) {
+  const size_t nqp = nqp_of(p.NQ);
+  const size_t slots = (size_t)p.B * p.Hkv * (p.n_chunks > 0 ? p.n_chunks : 1);
+  return slots * nqp * p.d * 4 + slots * 2 * nqp * 4 + 256;
+}
+
+hipError_t attention(const AttnPlan& p, const float* q, const float* kb, const float* vb,
+                     const void* ctx_k, const void* ctx_v, const int32_t* cu_ctx, int ctx_rows,
+                     float* ws, float* o, hipStream_t s) {
+  const int nqp = nqp_of(p.NQ);
+  const size_t slots = (size_t)p.B * p.Hkv * (p.n_chunks > 0 ? p.n_chunks : 1);
+  float* po = ws;
+  float* pml = ws + slots * nqp * p.d;
+  const float scale = (float)(1.0 / sqrt((double)p.d));
+  hipError_t e = hipSuccess;
+  if (p.n_chunks > 0) {
+    const int cr = ctx_rows;
+    if (p.d == 64)
+      e = p.kv_f32 ? dispatch_rt<64, 2>(p, q, ctx_k, ctx_v, cu_ctx, cr, po, pml, scale, s)
+                   : dispatch_rt<64, 1>(p, q, ctx_k, ctx_v, cu_ctx, cr, po, pml, scale, s);
+    else
+      e = p.kv_f32 ? dispatch_rt<128, 2>(p, q, ctx_k, ctx_v, cu_ctx, cr, po, pml, scale, s)
+                   : dispatch_rt<128, 1>(p, q, ctx_k, ctx_v, cu_ctx, cr, po, pml, scale, s);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(p.B * p.Hkv), dim3(kAttnThreads), 0, s, q, kb, vb, po,
+                     pml, p.Hkv, p.G, p.S, p.d, nqp, p.n_chunks, scale, o);
+  return hipGetLastError();
+}
+
+}  // namespace dmtp

@@ -1,0 +1,188 @@
+// Device helpers shared by the DMTP kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dmtp.h"
+
+namespace dmtp {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- bf16 ----
+// bf16 values are handled as their 16-bit patterns.
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+
+// Round-to-nearest-even float32 -> bf16 (finite inputs; NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// x = hi + lo + r with |r| <= 2^-18 |x|: the two-term bf16 split that lets a
+// bf16 x bf16 matrix core product reproduce a float32 operand.
+__device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
+  hi = f32_to_bf16(x);
+  lo = f32_to_bf16(x - bf16_to_f32(hi));
+}
+
+__device__ __forceinline__ uint32_t pack2(uint16_t a, uint16_t b) {
+  return (uint32_t)a | ((uint32_t)b << 16);
+}
+
+// ---------------------------------------------------------------- MFMA ----
+// D(16x16, f32) += A(16x32, bf16) * B(32x16, bf16).  Lane l supplies row
+// (l % 16) of A and column (l % 16) of B, eight consecutive k values from the
+// lane group l / 16; it receives D rows 4 * (l / 16) + i, column l % 16.
+__device__ __forceinline__ f32x4_t mfma_16x16x32(const uint4& a, const uint4& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// ----------------------------------------------------------- reductions ----
+template <typename T>
+__device__ __forceinline__ T shfl_xor(T v, int mask) {
+  return __shfl_xor(v, mask, kWave);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += shfl_xor(v, o);
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+  for (int o = 32; o > 0; o >>= 1) v += shfl_xor(v, o);
+  return v;
+}
+
+// --------------------------------------------------------- Philox4x64-10 ----
+// The counter-based generator of Salmon, Moraes, Dror and Shaw (SC'11): ten
+// rounds, each multiplying counter words 0 and 2 by fixed odd constants and
+// mixing both product halves with the other words and the round key; the key
+// is advanced by two Weyl increments between rounds.
+struct u64x4 {
+  uint64_t x, y, z, w;
+};
+
+__device__ __forceinline__ u64x4 philox4x64_10(u64x4 c, uint64_t k0, uint64_t k1) {
+  const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += W0;
+      k1 += W1;
+    }
+    const uint64_t hi0 = __umul64hi(M0, c.x), lo0 = M0 * c.x;
+    const uint64_t hi1 = __umul64hi(M1, c.z), lo1 = M1 * c.z;
+    c = u64x4{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
+  }
+  return c;
+}
+
+// Gumbel(0, 1) variate of a 32-bit word x: t = (x + 1/2) 2^-32,
+// E = -log(1 - t) = -log1p(-t) (Exp(1)), g = -log(E).
+__device__ __forceinline__ float gumbel_of_word(uint32_t x) {
+  const float t = fmaf((float)x, 2.3283064365386963e-10f, 1.1641532182693481e-10f);
+  const float e = -log1pf(-t);
+  return -logf(e);
+}
+
+// The eight 32-bit words of block (j >> 3) of draw (seed, key).
+__device__ __forceinline__ void philox_words8(uint64_t seed, uint64_t key, uint64_t block,
+                                              uint32_t w[8]) {
+  const u64x4 o = philox4x64_10(u64x4{block, key, 0, 0}, seed, 0);
+  w[0] = (uint32_t)o.x; w[1] = (uint32_t)(o.x >> 32);
+  w[2] = (uint32_t)o.y; w[3] = (uint32_t)(o.y >> 32);
+  w[4] = (uint32_t)o.z; w[5] = (uint32_t)(o.z >> 32);
+  w[6] = (uint32_t)o.w; w[7] = (uint32_t)(o.w >> 32);
+}
+
+// ----------------------------------------------------- running maximum ----
+// Best-two tracker for argmax with a gap: (v1, i1) is the best value and its
+// index (lowest index among equals), v2 the second-best value.
+struct Top2 {
+  float v1;
+  int i1;
+  float v2;
+};
+
+__device__ __forceinline__ Top2 top2_empty() { return Top2{-INFINITY, 0x7FFFFFFF, -INFINITY}; }
+
+__device__ __forceinline__ void top2_push(Top2& t, float v, int i) {
+  if (v > t.v1 || (v == t.v1 && i < t.i1)) {
+    t.v2 = t.v1;
+    t.v1 = v;
+    t.i1 = i;
+  } else if (v > t.v2) {
+    t.v2 = v;
+  }
+}
+
+__device__ __forceinline__ Top2 top2_merge(const Top2& a, const Top2& b) {
+  Top2 r;
+  if (b.v1 > a.v1 || (b.v1 == a.v1 && b.i1 < a.i1)) {
+    r.v1 = b.v1;
+    r.i1 = b.i1;
+    r.v2 = fmaxf(a.v1, b.v2);
+  } else {
+    r.v1 = a.v1;
+    r.i1 = a.i1;
+    r.v2 = fmaxf(a.v2, b.v1);
+  }
+  return r;
+}
+
+__device__ __forceinline__ Top2 top2_shfl_xor(const Top2& t, int mask) {
+  Top2 o;
+  o.v1 = shfl_xor(t.v1, mask);
+  o.i1 = shfl_xor(t.i1, mask);
+  o.v2 = shfl_xor(t.v2, mask);
+  return o;
+}
+
+// ---------------------------------------------------------- load helpers ----
+template <int DT>
+struct Elem;
+template <>
+struct Elem<DMTP_F32> {
+  typedef float T;
+  __device__ static float load(const void* p, size_t i) { return ((const float*)p)[i]; }
+};
+template <>
+struct Elem<DMTP_BF16> {
+  typedef uint16_t T;
+  __device__ static float load(const void* p, size_t i) {
+    return bf16_to_f32(((const uint16_t*)p)[i]);
+  }
+};
+
+__device__ __forceinline__ float load_elem(const void* p, int dtype, size_t i) {
+  return dtype == DMTP_BF16 ? bf16_to_f32(((const uint16_t*)p)[i]) : ((const float*)p)[i];
+}
+
+__device__ __forceinline__ void store_elem(void* p, int dtype, size_t i, float v) {
+  if (dtype == DMTP_BF16)
+    ((uint16_t*)p)[i] = f32_to_bf16(v);
+  else
+    ((float*)p)[i] = v;
+}
+
+// Context length of sequence b from the prefix sums, clamped so that rows
+// cu_ctx[b] .. cu_ctx[b] + L - 1 lie inside [0, ctx_rows).
+__device__ __forceinline__ int ctx_len_of(const int32_t* cu_ctx, int b, int ctx_rows) {
+  const int lo = cu_ctx[b], hi = cu_ctx[b + 1];
+  if (lo < 0 || lo >= ctx_rows || hi <= lo) return 0;
+  return (hi > ctx_rows ? ctx_rows : hi) - lo;
+}
+
+}  // namespace dmtp

@@ -1,0 +1,358 @@
+// The C ABI: argument validation on the host (before anything is enqueued),
+// workspace planning, and the kernel sequence of each call.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "dmtp.h"
+#include "kernels.hpp"
+
+namespace {
+
+using namespace dmtp;
+
+constexpr size_t kAlign = 256;
+size_t al(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool valid_dtype(int t) { return t == DMTP_F32 || t == DMTP_BF16; }
+size_t esize(int t) { return t == DMTP_BF16 ? 2 : 4; }
+
+#define CHECK(cond, code) \
+  do {                    \
+    if (!(cond)) return (code); \
+  } while (0)
+
+// --- device check: gfx950 only (cached per device ordinal)
+std::atomic<int> g_arch_ok[64];
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DMTP_E_DEVICE;
+  if (dev < 0 || dev >= 64) return DMTP_E_DEVICE;
+  int s = g_arch_ok[dev].load(std::memory_order_relaxed);
+  if (s == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return DMTP_E_DEVICE;
+    s = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    g_arch_ok[dev].store(s, std::memory_order_relaxed);
+  }
+  return s == 1 ? DMTP_OK : DMTP_E_DEVICE;
+}
+
+int check_rows(const dmtp_rows& r, bool allow_absent) {
+  if (!r.rows && !r.ids) return allow_absent ? DMTP_OK : DMTP_E_NULL;
+  if (r.rows && r.ids) return DMTP_E_ARG;
+  if (r.rows) {
+    CHECK(valid_dtype(r.dtype), DMTP_E_DTYPE);
+    CHECK(aligned16(r.rows), DMTP_E_ALIGN);
+  } else {
+    CHECK(r.table != nullptr, DMTP_E_NULL);
+    CHECK(r.table_rows >= 1, DMTP_E_SHAPE);
+    CHECK(aligned16(r.table), DMTP_E_ALIGN);
+  }
+  return DMTP_OK;
+}
+
+// ---------------------------------------------------------------- fuse ----
+int validate_fuse(const dmtp_fuse_desc* d) {
+  CHECK(d != nullptr, DMTP_E_NULL);
+  CHECK(d->rows >= 1 && d->rows <= (1 << 20), DMTP_E_SHAPE);
+  CHECK(d->H >= 64 && d->H <= 16384 && d->H % 64 == 0, DMTP_E_SHAPE);
+  CHECK(valid_dtype(d->w_dtype), DMTP_E_DTYPE);
+  CHECK(d->eps >= 0.f, DMTP_E_ARG);
+  int e;
+  if ((e = check_rows(d->x1, false)) != DMTP_OK) return e;
+  if ((e = check_rows(d->x2, false)) != DMTP_OK) return e;
+  if ((e = check_rows(d->res, true)) != DMTP_OK) return e;
+  CHECK(d->g1 && d->g2 && d->W && d->out, DMTP_E_NULL);
+  CHECK(aligned16(d->g1) && aligned16(d->g2) && aligned16(d->W) && aligned16(d->out), DMTP_E_ALIGN);
+  return DMTP_OK;
+}
+
+size_t fuse_ws(const dmtp_fuse_desc* d) {
+  return al((size_t)d->rows * 2 * d->H * 4) + al(gemm_ws_bytes(d->rows, d->H, 2 * d->H));
+}
+
+// ---------------------------------------------------------- block draft ----
+int validate_draft(const dmtp_draft_desc* d) {
+  CHECK(d != nullptr, DMTP_E_NULL);
+  CHECK(d->B >= 1 && d->B <= 4096, DMTP_E_SHAPE);
+  CHECK(d->H >= 64 && d->H <= 16384 && d->H % 64 == 0, DMTP_E_SHAPE);
+  CHECK(d->d == 64 || d->d == 128, DMTP_E_SHAPE);
+  CHECK(d->Hkv >= 1 && d->Hq >= d->Hkv && d->Hq % d->Hkv == 0 && d->Hq <= 256, DMTP_E_SHAPE);
+  CHECK((d->Hq * d->d) % 64 == 0, DMTP_E_SHAPE);
+  CHECK(d->F >= 64 && d->F % 64 == 0 && d->F <= 65536, DMTP_E_SHAPE);
+  CHECK(d->n_layers >= 1 && d->n_layers <= 64, DMTP_E_SHAPE);
+  CHECK(d->K >= 2 && d->K <= 32, DMTP_E_SHAPE);
+  CHECK(d->n_anchor == 1 || d->n_anchor == 2, DMTP_E_SHAPE);
+  const int S = d->K - 1 + d->n_anchor;
+  CHECK(valid_dtype(d->dtype), DMTP_E_DTYPE);
+  // query rows per kv head that fit one workgroup's LDS
+  CHECK(S * (d->Hq / d->Hkv) <= attn_max_nq(d->d, d->dtype == DMTP_F32), DMTP_E_SHAPE);
+  CHECK(d->eps >= 0.f && d->rope_base > 1.f, DMTP_E_ARG);
+  CHECK(d->window >= 0 && d->max_ctx >= 0 && d->ctx_rows >= 0, DMTP_E_SHAPE);
+  CHECK(d->V >= 2 && d->mask_id >= 0 && d->mask_id < d->V, DMTP_E_SHAPE);
+  CHECK(d->x_t1 && d->emb && d->cu_ctx && d->layers && d->g_final && d->out, DMTP_E_NULL);
+  if (d->n_anchor == 2) CHECK(d->anchor_ids != nullptr, DMTP_E_NULL);
+  CHECK(aligned16(d->x_t1) && aligned16(d->emb) && aligned16(d->g_final) && aligned16(d->out),
+        DMTP_E_ALIGN);
+  for (int l = 0; l < d->n_layers; ++l) {
+    const dmtp_layer& L = d->layers[l];
+    CHECK(L.g_attn && L.wqkv && L.wo && L.g_ffn && L.wg && L.wu && L.wd, DMTP_E_NULL);
+    CHECK(aligned16(L.g_attn) && aligned16(L.wqkv) && aligned16(L.wo) && aligned16(L.g_ffn) &&
+              aligned16(L.wg) && aligned16(L.wu) && aligned16(L.wd),
+          DMTP_E_ALIGN);
+    if (d->max_ctx > 0 && d->ctx_rows > 0) {
+      CHECK(L.ctx_k && L.ctx_v, DMTP_E_NULL);
+      CHECK(aligned16(L.ctx_k) && aligned16(L.ctx_v), DMTP_E_ALIGN);
+    }
+  }
+  return DMTP_OK;
+}
+
+struct DraftWs {
+  size_t X, xh, qkv, q, kb, vb, o, gate, up, act, gemm, attn, total;
+  AttnPlan plan;
+};
+
+DraftWs draft_ws(const dmtp_draft_desc* d) {
+  DraftWs w;
+  const int S = d->K - 1 + d->n_anchor;
+  const size_t R = (size_t)d->B * S;
+  const int qkv_n = (d->Hq + 2 * d->Hkv) * d->d;
+  w.plan = attn_plan(d->B, d->Hq, d->Hkv, S, d->d, d->max_ctx, d->window, d->dtype == DMTP_F32);
+  size_t gemm_max = 0;
+  auto upd = [&](int M, int N, int K) {
+    const size_t b = gemm_ws_bytes(M, N, K);
+    if (b > gemm_max) gemm_max = b;
+  };
+  upd((int)R, qkv_n, d->H);
+  upd((int)R, d->H, d->Hq * d->d);
+  upd((int)R, d->F, d->H);
+  upd((int)R, d->H, d->F);
+  size_t o = 0;
+  w.X = o; o = al(o + R * d->H * 4);
+  w.xh = o; o = al(o + R * d->H * 4);
+  w.qkv = o; o = al(o + R * qkv_n * 4);
+  w.q = o; o = al(o + R * d->Hq * d->d * 4);
+  w.kb = o; o = al(o + R * d->Hkv * d->d * 4);
+  w.vb = o; o = al(o + R * d->Hkv * d->d * 4);
+  w.o = o; o = al(o + R * d->Hq * d->d * 4);
+  w.gate = o; o = al(o + R * d->F * 4);
+  w.up = o; o = al(o + R * d->F * 4);
+  w.act = o; o = al(o + R * d->F * 4);
+  w.gemm = o; o = al(o + gemm_max);
+  w.attn = o; o = al(o + attn_ws_bytes(w.plan));
+  w.total = o;
+  return w;
+}
+
+// -------------------------------------------------------------- LM head ----
+int validate_head(const dmtp_head_desc* d, int* M_out) {
+  CHECK(d != nullptr, DMTP_E_NULL);
+  CHECK(d->H >= 64 && d->H <= 16384 && d->H % 64 == 0, DMTP_E_SHAPE);
+  CHECK(d->V >= 2 && d->V <= (1 << 26), DMTP_E_SHAPE);
+  CHECK(valid_dtype(d->dtype), DMTP_E_DTYPE);
+  CHECK(d->eps >= 0.f, DMTP_E_ARG);
+  CHECK(d->n_seg >= 1 && d->n_seg <= 4, DMTP_E_SHAPE);
+  long M = 0;
+  for (int i = 0; i < d->n_seg; ++i) {
+    const dmtp_head_segment& s = d->seg[i];
+    CHECK(s.n >= 0, DMTP_E_SHAPE);
+    if (s.n == 0) continue;
+    CHECK(s.x != nullptr, DMTP_E_NULL);
+    CHECK(s.ld >= d->H, DMTP_E_SHAPE);
+    CHECK(valid_dtype(s.dtype), DMTP_E_DTYPE);
+    if (s.g_norm) {
+      CHECK(s.dtype == DMTP_F32, DMTP_E_DTYPE);
+      CHECK(aligned16(s.g_norm), DMTP_E_ALIGN);
+    } else {
+      CHECK(s.dtype == d->dtype, DMTP_E_DTYPE);
+    }
+    CHECK(aligned16(s.x) && ((size_t)s.ld * esize(s.dtype)) % 16 == 0, DMTP_E_ALIGN);
+    M += s.n;
+  }
+  CHECK(M >= 1 && M <= 65536, DMTP_E_SHAPE);
+  CHECK(d->W && d->token, DMTP_E_NULL);
+  CHECK(aligned16(d->W), DMTP_E_ALIGN);
+  if (d->temperature) CHECK(d->draw_key && d->store_row && d->logits, DMTP_E_NULL);
+  if (d->store_row) CHECK(d->logits != nullptr && d->logits_rows >= 1, DMTP_E_NULL);
+  if (d->prepared) CHECK(aligned16(d->prepared), DMTP_E_ALIGN);
+  *M_out = (int)M;
+  return DMTP_OK;
+}
+
+// --------------------------------------------------------------- verify ----
+int validate_verify(const dmtp_verify_desc* d) {
+  CHECK(d != nullptr, DMTP_E_NULL);
+  CHECK(d->B >= 1 && d->B <= (1 << 20), DMTP_E_SHAPE);
+  CHECK(d->K >= 1 && d->K <= 32, DMTP_E_SHAPE);
+  CHECK(d->V >= 2 && d->V <= (1 << 26), DMTP_E_SHAPE);
+  CHECK(d->t1 && d->target && d->accept_len && d->out_tokens && d->n_out, DMTP_E_NULL);
+  if (d->K > 1) CHECK(d->drafts != nullptr, DMTP_E_NULL);
+  if (d->temperature) {
+    CHECK(d->logits && d->t1_lse && d->target_lse && d->u_acc && d->final_key, DMTP_E_NULL);
+    if (d->K > 1) CHECK(d->draft_lse != nullptr, DMTP_E_NULL);
+  }
+  return DMTP_OK;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? DMTP_OK : DMTP_E_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+size_t dmtp_fuse_ws(const dmtp_fuse_desc* d) {
+  if (validate_fuse(d) != DMTP_OK) return 0;
+  return fuse_ws(d);
+}
+
+int dmtp_fuse(const dmtp_fuse_desc* d, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int e = validate_fuse(d);
+  if (e != DMTP_OK) return e;
+  const size_t need = fuse_ws(d);
+  CHECK(ws_bytes >= need, DMTP_E_WORKSPACE);
+  CHECK(ws != nullptr, DMTP_E_NULL);
+  CHECK(((uintptr_t)ws % kAlign) == 0, DMTP_E_ALIGN);
+  if ((e = check_device()) != DMTP_OK) return e;
+  float* cat = (float*)ws;
+  float* part = (float*)((char*)ws + al((size_t)d->rows * 2 * d->H * 4));
+  hipError_t h = fuse_prep(*d, cat, stream);
+  if (h != hipSuccess) return DMTP_E_LAUNCH;
+  const bool has_res = d->res.rows || d->res.ids;
+  GemmArgs g{cat, 1, (size_t)2 * d->H, d->rows, d->W, d->w_dtype == DMTP_F32, (size_t)2 * d->H,
+             d->H, 2 * d->H, d->out, (size_t)d->H, has_res ? d->out : nullptr, (size_t)d->H};
+  return launch_status(gemm(g, part, stream));
+}
+
+size_t dmtp_block_draft_ws(const dmtp_draft_desc* d) {
+  if (validate_draft(d) != DMTP_OK) return 0;
+  return draft_ws(d).total;
+}
+
+int dmtp_block_draft(const dmtp_draft_desc* d, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int e = validate_draft(d);
+  if (e != DMTP_OK) return e;
+  const DraftWs w = draft_ws(d);
+  CHECK(ws_bytes >= w.total, DMTP_E_WORKSPACE);
+  CHECK(ws != nullptr, DMTP_E_NULL);
+  CHECK(((uintptr_t)ws % kAlign) == 0, DMTP_E_ALIGN);
+  if ((e = check_device()) != DMTP_OK) return e;
+  char* b = (char*)ws;
+  float* X = (float*)(b + w.X);
+  float* xh = (float*)(b + w.xh);
+  float* qkv = (float*)(b + w.qkv);
+  float* q = (float*)(b + w.q);
+  float* kb = (float*)(b + w.kb);
+  float* vb = (float*)(b + w.vb);
+  float* o = (float*)(b + w.o);
+  float* gate = (float*)(b + w.gate);
+  float* up = (float*)(b + w.up);
+  float* act = (float*)(b + w.act);
+  float* gws = (float*)(b + w.gemm);
+  float* aws = (float*)(b + w.attn);
+  const int S = d->K - 1 + d->n_anchor;
+  const int R = d->B * S;
+  const int qkv_n = (d->Hq + 2 * d->Hkv) * d->d;
+  const int wf32 = d->dtype == DMTP_F32;
+  hipError_t h = build_slots(*d, X, stream);
+  for (int l = 0; l < d->n_layers && h == hipSuccess; ++l) {
+    const dmtp_layer& L = d->layers[l];
+    if ((h = rmsnorm_rows(X, L.g_attn, d->eps, xh, R, d->H, stream)) != hipSuccess) break;
+    GemmArgs g1{xh, 1, (size_t)d->H, R, L.wqkv, wf32, (size_t)d->H, qkv_n, d->H, qkv, (size_t)qkv_n,
+                nullptr, 0};
+    if ((h = gemm(g1, gws, stream)) != hipSuccess) break;
+    if ((h = rope_split(qkv, d->cu_ctx, d->ctx_rows, d->B, S, d->Hq, d->Hkv, d->d, d->rope_base, q,
+                        kb, vb, stream)) != hipSuccess)
+      break;
+    if ((h = attention(w.plan, q, kb, vb, L.ctx_k, L.ctx_v, d->cu_ctx, d->ctx_rows, aws, o,
+                       stream)) != hipSuccess)
+      break;
+    const int od = d->Hq * d->d;
+    GemmArgs g2{o, 1, (size_t)od, R, L.wo, wf32, (size_t)od, d->H, od, X, (size_t)d->H, X,
+                (size_t)d->H};
+    if ((h = gemm(g2, gws, stream)) != hipSuccess) break;
+    if ((h = rmsnorm_rows(X, L.g_ffn, d->eps, xh, R, d->H, stream)) != hipSuccess) break;
+    GemmArgs g3{xh, 1, (size_t)d->H, R, L.wg, wf32, (size_t)d->H, d->F, d->H, gate, (size_t)d->F,
+                nullptr, 0};
+    if ((h = gemm(g3, gws, stream)) != hipSuccess) break;
+    GemmArgs g4{xh, 1, (size_t)d->H, R, L.wu, wf32, (size_t)d->H, d->F, d->H, up, (size_t)d->F,
+                nullptr, 0};
+    if ((h = gemm(g4, gws, stream)) != hipSuccess) break;
+    if ((h = swiglu(gate, up, act, (size_t)R * d->F, stream)) != hipSuccess) break;
+    GemmArgs g5{act, 1, (size_t)d->F, R, L.wd, wf32, (size_t)d->F, d->H, d->F, X, (size_t)d->H, X,
+                (size_t)d->H};
+    h = gemm(g5, gws, stream);
+  }
+  if (h == hipSuccess)
+    h = final_norm_mask(X, d->g_final, d->eps, d->B, S, d->n_anchor, d->K, d->H, d->dtype, d->out,
+                        stream);
+  return launch_status(h);
+}
+
+size_t dmtp_lm_head_ws(const dmtp_head_desc* d) {
+  int M = 0;
+  if (validate_head(d, &M) != DMTP_OK) return 0;
+  return lm_head_ws_bytes(*d, M);
+}
+
+int dmtp_lm_head(const dmtp_head_desc* d, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int M = 0;
+  int e = validate_head(d, &M);
+  if (e != DMTP_OK) return e;
+  CHECK(ws_bytes >= lm_head_ws_bytes(*d, M), DMTP_E_WORKSPACE);
+  CHECK(ws != nullptr, DMTP_E_NULL);
+  CHECK(((uintptr_t)ws % kAlign) == 0, DMTP_E_ALIGN);
+  if ((e = check_device()) != DMTP_OK) return e;
+  return launch_status(lm_head_run(*d, M, ws, stream));
+}
+
+size_t dmtp_verify_ws(const dmtp_verify_desc* d) {
+  if (validate_verify(d) != DMTP_OK) return 0;
+  return verify_ws_bytes(*d);
+}
+
+int dmtp_verify(const dmtp_verify_desc* d, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int e = validate_verify(d);
+  if (e != DMTP_OK) return e;
+  CHECK(ws_bytes >= verify_ws_bytes(*d), DMTP_E_WORKSPACE);
+  CHECK(ws != nullptr, DMTP_E_NULL);
+  CHECK(((uintptr_t)ws % kAlign) == 0, DMTP_E_ALIGN);
+  if ((e = check_device()) != DMTP_OK) return e;
+  return launch_status(verify_run(*d, ws, stream));
+}
+
+const char* dmtp_status_str(int s) {
+  switch (s) {
+    case DMTP_OK: return "ok";
+    case DMTP_E_NULL: return "a required pointer is NULL";
+    case DMTP_E_SHAPE: return "a size is outside the supported range";
+    case DMTP_E_DTYPE: return "unsupported dtype";
+    case DMTP_E_WORKSPACE: return "workspace smaller than the *_ws() query";
+    case DMTP_E_ALIGN: return "pointer not aligned (16 bytes; workspace 256 bytes)";
+    case DMTP_E_DEVICE: return "current device is not gfx950";
+    case DMTP_E_LAUNCH: return "kernel launch failed";
+    case DMTP_E_ARG: return "inconsistent arguments";
+    default: return "unknown status";
+  }
+}
+
+const char* dmtp_version(void) { return "dmtp 0.1.0 (gfx950, ABI 1)"; }
+
+size_t dmtp_struct_size(int which) {
+  switch (which) {
+    case 0: return sizeof(dmtp_rows);
+    case 1: return sizeof(dmtp_fuse_desc);
+    case 2: return sizeof(dmtp_layer);
+    case 3: return sizeof(dmtp_draft_desc);
+    case 4: return sizeof(dmtp_head_segment);
+    case 5: return sizeof(dmtp_head_desc);
+    case 6: return sizeof(dmtp_verify_desc);
+    default: return 0;
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+// Internal launch interface of the DMTP kernels (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "dmtp.h"
+
+namespace dmtp {
+
+// ------------------------------------------------------------------ GEMM ----
+// C[M, N] (float32, ldc) = R[M, N] (optional, may alias C) + A[M, K] B[N, K]^T.
+struct GemmArgs {
+  const void* A;
+  int a_f32;        // A is float32 (split into two bf16 planes) or bf16
+  size_t lda;
+  int M;
+  const void* B;
+  int b_f32;
+  size_t ldb;
+  int N;
+  int K;            // multiple of 64
+  float* C;
+  size_t ldc;
+  const float* R;   // residual or NULL
+  size_t ldr;
+};
+
+// Split-K factor the launcher uses and the float32 workspace it needs.
+int gemm_splits(int M, int N, int K);
+size_t gemm_ws_bytes(int M, int N, int K);
+hipError_t gemm(const GemmArgs& a, float* ws, hipStream_t s);
+
+// -------------------------------------------------------------- elementwise --
+// y[r] = RMSNorm(x[r]; g) for float32 rows of width H.
+hipError_t rmsnorm_rows(const float* x, const float* g, float eps, float* y, int rows, int H,
+                        hipStream_t s);
+
+// Fusion prologue: cat[r] = [RMSNorm(x1[r]; g1), RMSNorm(x2[r]; g2)] (float32
+// [rows, 2H]) and out[r] = res[r] (float32) when res is present.
+hipError_t fuse_prep(const dmtp_fuse_desc& d, float* cat, hipStream_t s);
+
+// Draft slots X [B * S, H] float32 from anchor ids, x_t1 rows and the MASK row.
+hipError_t build_slots(const dmtp_draft_desc& d, float* X, hipStream_t s);
+
+// q/k/v split of the QKV projection with the rotary embedding at slot
+// positions: q [B, Hkv, S * G, d], kb and vb [B, Hkv, S, d] (float32).
+hipError_t rope_split(const float* qkv, const int32_t* cu_ctx, int ctx_rows, int B, int S, int Hq,
+                      int Hkv, int d, float rope_base, float* q, float* kb, float* vb,
+                      hipStream_t s);
+
+// a = silu(g) * u elementwise ([n] float32)
+hipError_t swiglu(const float* g, const float* u, float* a, size_t n, hipStream_t s);
+
+// out[b, j] = round_dtype(RMSNorm(X[b, n_anchor + j]; g)) for j = 0 .. K-2
+hipError_t final_norm_mask(const float* X, const float* g, float eps, int B, int S, int n_anchor,
+                           int K, int H, int dtype, void* out, hipStream_t s);
+
+// -------------------------------------------------------------- attention --
+struct AttnPlan {
+  int B, Hkv, G, S, d, NQ, chunk, n_chunks, kv_f32, window;
+};
+AttnPlan attn_plan(int B, int Hq, int Hkv, int S, int d, int max_ctx, int window, int kv_f32);
+// Largest number of query rows per kv head (S * Hq / Hkv) the kernels support.
+int attn_max_nq(int d, int kv_f32);
+size_t attn_ws_bytes(const AttnPlan& p);
+// o [B * S, Hq * d] float32 = attention of the block queries over context + block keys.
+hipError_t attention(const AttnPlan& p, const float* q, const float* kb, const float* vb,
+                     const void* ctx_k, const void* ctx_v, const int32_t* cu_ctx, int ctx_rows,
+                     float* ws, float* o, hipStream_t s);
+
+// ---------------------------------------------------------------- LM head --
+size_t lm_head_ws_bytes(const dmtp_head_desc& d, int M);
+hipError_t lm_head_run(const dmtp_head_desc& d, int M, void* ws, hipStream_t s);
+
+// ----------------------------------------------------------------- verify --
+size_t verify_ws_bytes(const dmtp_verify_desc& d);
+hipError_t verify_run(const dmtp_verify_desc& d, void* ws, hipStream_t s);
+
+}  // namespace dmtp

@@ -1,0 +1,248 @@
+// Block verification.
+//
+//   main   one thread per sequence: greedy prefix compare, or the accept tests
+//          u < p_i(d_i) / q_i(d_i) evaluated in log space from two gathered
+//          logits and the row lse values; builds a deterministic list of the
+//          sequences that need a draw (correction from max(0, p - q), or bonus
+//          from p_K)
+//   scan   the draws: HBM-bound pass over the float32 rows, split into
+//          vocabulary chunks, Gumbel-max over log(max(0, p - q)) (and over log p
+//          for the zero-residual fallback) with the same Philox noise
+//   final  merges the chunk maxima and writes the correction/bonus token
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace dmtp {
+
+namespace {
+
+constexpr int kScanThreads = 256;
+constexpr int kChunk = kScanThreads * 8;
+
+struct VerifyParams {
+  int B, K, V;
+  const int32_t* t1;
+  const int32_t* drafts;
+  const int32_t* target;
+  const float* temperature;
+  const float* logits;
+  const float* t1_lse;
+  const float* draft_lse;
+  const float* target_lse;
+  const float* u_acc;
+  uint64_t seed;
+  const uint64_t* final_key;
+  int32_t* accept_len;
+  int32_t* out_tokens;
+  int32_t* n_out;
+  // workspace
+  int32_t* list;       // [B]
+  int32_t* list_pos;   // [B]
+  int32_t* count;      // [1]
+  int32_t* mode;       // [B]: 0 greedy/done, 1 residual draw at row L, 2 bonus draw
+  Top2* part;          // [B, n_chunks, 2]
+  int n_chunks;
+};
+
+__device__ __forceinline__ int cand(const VerifyParams& p, int b, int i) {
+  return i == 0 ? p.t1[b] : p.drafts[(size_t)b * (p.K - 1) + i - 1];
+}
+
+__global__ void verify_main_kernel(VerifyParams p) {
+  __shared__ int32_t sc[1024];
+  __shared__ int32_t base;
+  if (threadIdx.x == 0) base = 0;
+  __syncthreads();
+  const int K = p.K, V = p.V;
+  for (int c0 = 0; c0 < p.B; c0 += blockDim.x) {
+    const int b = c0 + threadIdx.x;
+    int flag = 0;
+    if (b < p.B) {
+      const float t = p.temperature ? p.temperature[b] : 0.f;
+      int L = 0, md = 0;
+      if (t > 0.f) {
+        const float it = 1.f / t;
+        const float* rows = p.logits + (size_t)b * (2 * K + 1) * V;
+        L = K;
+        for (int i = 0; i < K; ++i) {
+          const int d = cand(p, b, i);
+          bool acc = false;
+          if (d >= 0 && d < V) {
+            const float lq = rows[(size_t)i * V + d] * it -
+                             (i == 0 ? p.t1_lse[b] : p.draft_lse[(size_t)b * (K - 1) + i - 1]);
+            const float lp = rows[(size_t)(K + i) * V + d] * it - p.target_lse[(size_t)b * (K + 1) + i];
+            const float u = p.u_acc[(size_t)b * K + i];
+            acc = (u <= 0.f) || (logf(u) < lp - lq);
+          }
+          if (!acc) {
+            L = i;
+            break;
+          }
+        }
+        md = L < K ? 1 : 2;
+        flag = 1;
+      } else {
+        while (L < K && cand(p, b, L) == p.target[(size_t)b * (K + 1) + L]) ++L;
+      }
+      int32_t* out = p.out_tokens + (size_t)b * (K + 1);
+      for (int i = 0; i < L; ++i) out[i] = cand(p, b, i);
+      out[L] = md ? -1 : p.target[(size_t)b * (K + 1) + L];
+      for (int i = L + 1; i <= K; ++i) out[i] = -1;
+      p.accept_len[b] = L;
+      p.n_out[b] = L + 1;
+      p.mode[b] = md;
+    }
+    sc[threadIdx.x] = flag;
+    __syncthreads();
+    for (int o = 1; o < (int)blockDim.x; o <<= 1) {
+      const int v = threadIdx.x >= (unsigned)o ? sc[threadIdx.x - o] : 0;
+      __syncthreads();
+      sc[threadIdx.x] += v;
+      __syncthreads();
+    }
+    if (b < p.B) {
+      const int pos = base + sc[threadIdx.x] - flag;
+      p.list_pos[b] = flag ? pos : -1;
+      if (flag) p.list[pos] = b;
+    }
+    __syncthreads();
+    if (threadIdx.x == blockDim.x - 1) base += sc[threadIdx.x];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) p.count[0] = base;
+}
+
+__global__ __launch_bounds__(kScanThreads) void verify_scan_kernel(VerifyParams p) {
+  __shared__ Top2 red[2][kScanThreads / kWave];
+  const int items = p.count[0] * p.n_chunks;
+  const int K = p.K, V = p.V;
+  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    const int li = item / p.n_chunks, ch = item % p.n_chunks;
+    const int b = p.list[li];
+    const int L = p.accept_len[b];
+    const int md = p.mode[b];
+    const float it = 1.f / p.temperature[b];
+    const float* rows = p.logits + (size_t)b * (2 * K + 1) * V;
+    // residual at row L: p row K + L, q row L; bonus: p row 2K
+    const float* pr = rows + (size_t)(K + L) * V;
+    const float* qr = rows + (size_t)L * V;
+    const float lse_p = p.target_lse[(size_t)b * (K + 1) + L];
+    const float lse_q = md == 1 ? (L == 0 ? p.t1_lse[b] : p.draft_lse[(size_t)b * (K - 1) + L - 1]) : 0.f;
+    Top2 tr = top2_empty(), tp = top2_empty();
+    const int j0 = ch * kChunk + 8 * threadIdx.x;
+    if (j0 < V) {
+      uint32_t w[8];
+      philox_words8(p.seed, p.final_key[b], (uint64_t)(j0 >> 3), w);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int j = j0 + k;
+        if (j >= V) break;
+        const float g = gumbel_of_word(w[k]);
+        const float a = pr[j] * it - lse_p;          // log p_j
+        top2_push(tp, a + g, j);
+        if (md == 1) {
+          const float c = qr[j] * it - lse_q;        // log q_j
+          const float s = a > c ? a + log1pf(-expf(c - a)) : -INFINITY;   // log(p_j - q_j)
+          top2_push(tr, s + g, j);
+        }
+      }
+    }
+#pragma unroll
+    for (int mask = 1; mask < kWave; mask <<= 1) {
+      tr = top2_merge(tr, top2_shfl_xor(tr, mask));
+      tp = top2_merge(tp, top2_shfl_xor(tp, mask));
+    }
+    if (threadIdx.x % kWave == 0) {
+      red[0][threadIdx.x / kWave] = tr;
+      red[1][threadIdx.x / kWave] = tp;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      for (int w2 = 1; w2 < kScanThreads / kWave; ++w2) {
+        tr = top2_merge(tr, red[0][w2]);
+        tp = top2_merge(tp, red[1][w2]);
+      }
+      p.part[((size_t)li * p.n_chunks + ch) * 2 + 0] = tr;
+      p.part[((size_t)li * p.n_chunks + ch) * 2 + 1] = tp;
+    }
+    __syncthreads();
+  }
+}
+
+__global__ void verify_final_kernel(VerifyParams p) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= p.B) return;
+  const int li = p.list_pos[b];
+  if (li < 0) return;
+  Top2 tr = top2_empty(), tp = top2_empty();
+  for (int c = 0; c < p.n_chunks; ++c) {
+    tr = top2_merge(tr, p.part[((size_t)li * p.n_chunks + c) * 2 + 0]);
+    tp = top2_merge(tp, p.part[((size_t)li * p.n_chunks + c) * 2 + 1]);
+  }
+  // residual mode with no positive residual falls back to p
+  const int y = (p.mode[b] == 1 && tr.v1 > -INFINITY) ? tr.i1 : tp.i1;
+  p.out_tokens[(size_t)b * (p.K + 1) + p.accept_len[b]] = y;
+}
+
+struct WsL {
+  size_t list, list_pos, count, mode, part, total;
+  int n_chunks;
+};
+
+size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
+
+WsL layout(const dmtp_verify_desc& d) {
+  WsL w;
+  w.n_chunks = (d.V + kChunk - 1) / kChunk;
+  size_t o = 0;
+  w.list = o; o = al(o + (size_t)d.B * 4);
+  w.list_pos = o; o = al(o + (size_t)d.B * 4);
+  w.count = o; o = al(o + 4);
+  w.mode = o; o = al(o + (size_t)d.B * 4);
+  w.part = o;
+  if (d.temperature) o = al(o + (size_t)d.B * w.n_chunks * 2 * sizeof(Top2));
+  w.total = o;
+  return w;
+}
+
+}  // namespace
+
+size_t verify_ws_bytes(const dmtp_verify_desc& d) { return layout(d).total; }
+
+hipError_t verify_run(const dmtp_verify_desc& d, void* ws, hipStream_t s) {
+  const WsL w = layout(d);
+  char* base = (char*)ws;
+  VerifyParams p;
+  p.B = d.B;
+  p.K = d.K;
+  p.V = d.V;
+  p.t1 = d.t1;
+  p.drafts = d.drafts;
+  p.target = d.target;
+  p.temperature = d.temperature;
+  p.logits = d.logits;
+  p.t1_lse = d.t1_lse;
+  p.draft_lse = d.draft_lse;
+  p.target_lse = d.target_lse;
+  p.u_acc = d.u_acc;
+  p.seed = d.seed;
+  p.final_key = d.final_key;
+  p.accept_len = d.accept_len;
+  p.out_tokens = d.out_tokens;
+  p.n_out = d.n_out;
+  p.list = (int32_t*)(base + w.list);
+  p.list_pos = (int32_t*)(base + w.list_pos);
+  p.count = (int32_t*)(base + w.count);
+  p.mode = (int32_t*)(base + w.mode);
+  p.part = (Top2*)(base + w.part);
+  p.n_chunks = w.n_chunks;
+  hipLaunchKernelGGL(verify_main_kernel, dim3(1), dim3(1024), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !d.temperature) return e;
+  hipLaunchKernelGGL(verify_scan_kernel, dim3(2048), dim3(kScanThreads), 0, s, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(verify_final_kernel, dim3((d.B + 255) / 256), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace dmtp

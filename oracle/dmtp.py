@@ -63,7 +63,7 @@ def fuse(x1: np.ndarray, x2: np.ndarray, g1: np.ndarray, g2: np.ndarray,
     DMTP residual (x1 = e_T1, x2 = h_MTP, res = e_T1: [DMTP] section 3).
     """
     cat = np.concatenate([nm.rmsnorm(x1, g1, eps), nm.rmsnorm(x2, g2, eps)], axis=-1)
-    out = cat @ np.asarray(w_cat, dtype=np.float64).T
+    out = nm.matmul_nt(cat, w_cat)
     if res is not None:
         out = np.asarray(res, dtype=np.float64) + out
     return out
@@ -84,9 +84,9 @@ class HeadRows:
     logits: np.ndarray    # [M, V] float64 logits
 
 
-def lm_logits(rows: np.ndarray, w_head64: np.ndarray) -> np.ndarray:
-    """Logits l = W_head x for each row x (W_head [V, H], rows [M, H])."""
-    return np.asarray(rows, dtype=np.float64) @ w_head64.T
+def lm_logits(rows: np.ndarray, w_head: np.ndarray) -> np.ndarray:
+    """Logits l = W_head x for each row x (W_head [V, H], rows [M, H]), float64."""
+    return nm.matmul_nt(rows, w_head)
 
 
 def select_tokens(logits: np.ndarray, tau: np.ndarray, seed: int,
@@ -108,10 +108,10 @@ def select_tokens(logits: np.ndarray, tau: np.ndarray, seed: int,
     return tok, mar
 
 
-def lm_head(rows: np.ndarray, w_head64: np.ndarray, tau: np.ndarray, seed: int = 0,
+def lm_head(rows: np.ndarray, w_head: np.ndarray, tau: np.ndarray, seed: int = 0,
             keys: Optional[np.ndarray] = None) -> HeadRows:
     """Shared LM head on rows that are already the head's input (normed, rounded)."""
-    logits = lm_logits(rows, w_head64)
+    logits = lm_logits(rows, w_head)
     tok, mar = select_tokens(logits, tau, seed, keys)
     t = np.where(np.asarray(tau) > 0.0, tau, 1.0).astype(np.float64)
     lse = nm.logsumexp(logits / t[:, None], axis=-1)
@@ -138,6 +138,7 @@ def block_slots(anchor_emb: np.ndarray, x_t1: np.ndarray, mask_emb: np.ndarray,
 
 @dataclass
 class Layer64:
+    """Weights of one drafter layer (any float dtype; products are taken in float64)."""
     g_attn: np.ndarray
     wqkv: np.ndarray
     wo: np.ndarray
@@ -148,45 +149,49 @@ class Layer64:
 
 
 def layer64(lw) -> Layer64:
-    f = lambda a: np.asarray(a, dtype=np.float64)  # noqa: E731
-    return Layer64(f(lw.g_attn), f(lw.wqkv), f(lw.wo), f(lw.g_ffn), f(lw.wg), f(lw.wu), f(lw.wd))
+    return Layer64(lw.g_attn, lw.wqkv, lw.wo, lw.g_ffn, lw.wg, lw.wu, lw.wd)
 
 
 def draft_layer(X: np.ndarray, positions: np.ndarray, lw: Layer64,
-                ctx_k: np.ndarray, ctx_v: np.ndarray, *, Hq: int, Hkv: int, d: int,
-                eps: float, rope_base: float, window: int = 0) -> np.ndarray:
-    """One pre-norm decoder layer of the block drafter on the S slots X [S, H].
+                ctx_k: Sequence[np.ndarray], ctx_v: Sequence[np.ndarray], *, Hq: int, Hkv: int,
+                d: int, eps: float, rope_base: float, window: int = 0) -> np.ndarray:
+    """One pre-norm decoder layer of the block drafter for n sequences.
 
-    Attention: every slot's query reads the context keys (the last `window`
-    of them when window > 0) and all S block keys, with no mask -- the
-    block-diagonal (bidirectional) part plus the offset block-causal part of
-    the DFlash mask, which for one block is "see everything" ([DvM] "DFlash:
-    Block Diffusion ...", three-component mask; [DMTP] section 6.2 window).
-    GQA: query head h reads kv head h // (Hq / Hkv).  Context keys arrive
-    already rotated; block q and k are rotated at the slot positions.
+    X is [n, S, H] (the S slots of each sequence), positions [n, S];
+    ctx_k[i] / ctx_v[i] are the context keys / values [L_i, Hkv, d] of sequence i.
+    Attention: every slot's query reads its own sequence's context keys (the
+    last `window` of them when window > 0) and all S block keys, with no mask
+    -- the block-diagonal (bidirectional) part plus the offset block-causal
+    part of the DFlash mask, which for one block is "see everything" ([DvM]
+    "DFlash: Block Diffusion ...", three-component mask; [DMTP] section 6.2
+    window).  GQA: query head h reads kv head h // (Hq / Hkv).  Context keys
+    arrive already rotated; block q and k are rotated at the slot positions.
+    The projections are row-wise, so they are taken for all sequences at once.
     """
-    S = X.shape[0]
+    n, S, H = X.shape
     xh = nm.rmsnorm(X, lw.g_attn, eps)
-    qkv = xh @ lw.wqkv.T
-    q = qkv[:, : Hq * d].reshape(S, Hq, d)
-    k = qkv[:, Hq * d: (Hq + Hkv) * d].reshape(S, Hkv, d)
-    v = qkv[:, (Hq + Hkv) * d:].reshape(S, Hkv, d)
-    q = nm.rope(q, positions, rope_base)
-    k = nm.rope(k, positions, rope_base)
-    ck = np.asarray(ctx_k, dtype=np.float64)
-    cv = np.asarray(ctx_v, dtype=np.float64)
-    if window > 0 and ck.shape[0] > window:
-        ck, cv = ck[-window:], cv[-window:]
-    keys = np.concatenate([ck, k], axis=0)     # [n_ctx + S, Hkv, d]
-    vals = np.concatenate([cv, v], axis=0)
+    qkv = nm.matmul_nt(xh.reshape(n * S, H), lw.wqkv).reshape(n, S, -1)
     group = Hq // Hkv
-    o = np.empty((S, Hq, d))
-    for h in range(Hq):
-        o[:, h] = nm.attention(q[:, h], keys[:, h // group], vals[:, h // group])
-    X1 = X + o.reshape(S, Hq * d) @ lw.wo.T
-    xh2 = nm.rmsnorm(X1, lw.g_ffn, eps)
-    a = nm.silu(xh2 @ lw.wg.T) * (xh2 @ lw.wu.T)
-    return X1 + a @ lw.wd.T
+    o = np.empty((n, S, Hq, d))
+    for i in range(n):
+        q = nm.rope(qkv[i, :, : Hq * d].reshape(S, Hq, d), positions[i], rope_base)
+        k = nm.rope(qkv[i, :, Hq * d: (Hq + Hkv) * d].reshape(S, Hkv, d), positions[i], rope_base)
+        v = qkv[i, :, (Hq + Hkv) * d:].reshape(S, Hkv, d)
+        ck = np.asarray(ctx_k[i], dtype=np.float64)
+        cv = np.asarray(ctx_v[i], dtype=np.float64)
+        if window > 0 and ck.shape[0] > window:
+            ck, cv = ck[-window:], cv[-window:]
+        keys = np.concatenate([ck, k], axis=0)     # [n_ctx + S, Hkv, d]
+        vals = np.concatenate([cv, v], axis=0)
+        for kv in range(Hkv):
+            kk = np.ascontiguousarray(keys[:, kv])
+            vv = np.ascontiguousarray(vals[:, kv])
+            for h in range(kv * group, (kv + 1) * group):
+                o[i, :, h] = nm.attention(q[:, h], kk, vv)
+    X1 = X + nm.matmul_nt(o.reshape(n * S, Hq * d), lw.wo).reshape(n, S, H)
+    xh2 = nm.rmsnorm(X1, lw.g_ffn, eps).reshape(n * S, H)
+    a = nm.silu(nm.matmul_nt(xh2, lw.wg)) * nm.matmul_nt(xh2, lw.wu)
+    return X1 + nm.matmul_nt(a, lw.wd).reshape(n, S, H)
 
 
 def block_draft(slots: Sequence[np.ndarray], ctx_len: np.ndarray, layers64: Sequence[Layer64],
@@ -198,16 +203,16 @@ def block_draft(slots: Sequence[np.ndarray], ctx_len: np.ndarray, layers64: Sequ
     slots[i] is [S, H] for sequence seqs[i]; slot j sits at position
     ctx_len[b] + j (the anchor A is the first position after the context).
     """
-    out = []
-    for X, b in zip(slots, seqs):
-        L = int(ctx_len[b])
-        pos = L + np.arange(X.shape[0])
-        lo, hi = int(cu_ctx[b]), int(cu_ctx[b + 1])
-        for li, lw in enumerate(layers64):
-            X = draft_layer(X, pos, lw, ctx_k[li][lo:hi], ctx_v[li][lo:hi], Hq=Hq, Hkv=Hkv,
-                            d=d, eps=eps, rope_base=rope_base, window=window)
-        out.append(rf(nm.rmsnorm(X, g_final, eps)))
-    return out
+    seqs = list(seqs)
+    X = np.stack([np.asarray(x, dtype=np.float64) for x in slots])
+    S = X.shape[1]
+    pos = np.stack([int(ctx_len[b]) + np.arange(S) for b in seqs])
+    spans = [(int(cu_ctx[b]), int(cu_ctx[b + 1])) for b in seqs]
+    for li, lw in enumerate(layers64):
+        X = draft_layer(X, pos, lw, [ctx_k[li][lo:hi] for lo, hi in spans],
+                        [ctx_v[li][lo:hi] for lo, hi in spans], Hq=Hq, Hkv=Hkv, d=d, eps=eps,
+                        rope_base=rope_base, window=window)
+    return list(rf(nm.rmsnorm(X, g_final, eps)))
 
 
 # ---------------------------------------------------------------------------
@@ -319,7 +324,7 @@ def run_round(inp, seqs: Optional[Sequence[int]] = None,
     rf = nm.round_to(cfg.dtype)
     eps = cfg.eps
     E = inp.emb
-    w_head64 = np.asarray(inp.w_head, dtype=np.float64)
+    w_head64 = inp.w_head
     tau = inp.tau[seqs].astype(np.float64)
     seed = int(inp.philox_seed)
     decisions: List[Tuple[tuple, int, float]] = []

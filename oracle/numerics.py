@@ -38,6 +38,22 @@ def round_to(dtype: str):
     raise ValueError(dtype)
 
 
+def matmul_nt(x: np.ndarray, W: np.ndarray, chunk: int = 8192) -> np.ndarray:
+    """x @ W^T in float64 for W stored [out, in] (any float dtype).
+
+    W is widened to float64 a block of rows at a time only to bound memory;
+    every output element is still one float64 dot product over the full
+    input dimension.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    n_out = W.shape[0]
+    out = np.empty(x.shape[:-1] + (n_out,), dtype=np.float64)
+    for r0 in range(0, n_out, chunk):
+        blk = np.asarray(W[r0:r0 + chunk], dtype=np.float64)
+        out[..., r0:r0 + chunk] = x @ blk.T
+    return out
+
+
 def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
     """RMSNorm over the last axis: x / sqrt(mean(x^2) + eps) * g."""
     x = np.asarray(x, dtype=np.float64)

@@ -1,0 +1,337 @@
+"""Per-call parity of the HIP library with the oracle, at sizes the oracle
+finishes in seconds that still cover several tiles and ragged tails."""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+from oracle import dmtp as odm, numerics as onm, philox as oph  # noqa: E402
+
+from tests._harness import NEAR_TIE, max_rel  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def dm():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mtp_block_draft_amd as m
+    return m
+
+
+def _bf16_trunc(x):
+    x = np.ascontiguousarray(x, dtype=np.float32).copy()
+    x.view(np.uint32)[...] &= np.uint32(0xFFFF0000)
+    return x
+
+
+def _t(a, dtype):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device="cuda", dtype=dtype)
+
+
+def _store(a, dt):
+    return _bf16_trunc(a) if dt == "bf16" else np.asarray(a, np.float32)
+
+
+TD = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+# ---------------------------------------------------------------- fuse
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("rows,H", [(1, 256), (37, 256), (32, 2048)])
+@pytest.mark.parametrize("residual", [False, True])
+def test_fuse(dm, dt, rows, H, residual):
+    print(f"fuse dt={dt} rows={rows} H={H} res={residual}", flush=True)
+    r = np.random.default_rng(rows * 7 + H + residual)
+    V = 300
+    emb = _store(0.02 * r.standard_normal((V, H)), dt)
+    x1 = _store(r.standard_normal((rows, H)), dt)
+    ids = r.integers(0, V, size=rows).astype(np.int32)
+    g1 = 1 + 0.1 * r.standard_normal(H).astype(np.float32)
+    g2 = 1 + 0.1 * r.standard_normal(H).astype(np.float32)
+    W = _store(0.02 * r.standard_normal((H, 2 * H)), dt)
+    out = torch.empty(rows, H, dtype=torch.float32, device="cuda")
+    E = _t(emb, TD[dt])
+    I = _t(ids, torch.int32)
+    dm.fuse(out, _t(W, TD[dt]), _t(g1, torch.float32), _t(g2, torch.float32), x1=_t(x1, TD[dt]),
+            x2_ids=I, res_ids=I if residual else None, table=E, eps=1e-6)
+    got = out.cpu().numpy()
+    want = odm.fuse(x1, emb[ids], g1, g2, W, 1e-6, res=emb[ids] if residual else None)
+    err = max_rel(got, want)
+    print("  max rel", err)
+    assert err < 1e-5
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_fuse_zero_projection_is_bitwise_residual(dm, dt):
+    r = np.random.default_rng(5)
+    rows, H, V = 19, 512, 64
+    emb = _store(0.02 * r.standard_normal((V, H)), dt)
+    ids = r.integers(0, V, size=rows).astype(np.int32)
+    x2 = r.standard_normal((rows, H)).astype(np.float32)
+    out = torch.empty(rows, H, dtype=torch.float32, device="cuda")
+    I = _t(ids, torch.int32)
+    dm.fuse(out, torch.zeros(H, 2 * H, dtype=TD[dt], device="cuda"), _t(np.ones(H), torch.float32),
+            _t(np.ones(H), torch.float32), x1_ids=I, x2=_t(x2, torch.float32), res_ids=I,
+            table=_t(emb, TD[dt]))
+    np.testing.assert_array_equal(out.cpu().numpy(), emb[ids].astype(np.float32))
+
+
+# ---------------------------------------------------------------- LM head
+
+
+def _head_case(seed, H, V, dt, M_norm=5, M_rows=20, M_strided=12):
+    r = np.random.default_rng(seed)
+    W = _store(0.02 * r.standard_normal((V, H)), dt)
+    hid = r.standard_normal((M_norm, H)).astype(np.float32)
+    g = (1 + 0.1 * r.standard_normal(H)).astype(np.float32)
+    rows = _store(r.standard_normal((M_rows, H)), dt)
+    strided = _store(r.standard_normal((M_strided, 2 * H)), dt)
+    rf = onm.round_to(dt)
+    x = np.concatenate([rf(onm.rmsnorm(hid, g, 1e-6)), rows.astype(np.float64),
+                        strided[:, :H].astype(np.float64)])
+    return W, hid, g, rows, strided, x
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("H,V", [(256, 5003), (2048, 151936)])
+def test_lm_head_greedy(dm, dt, H, V):
+    print(f"lm_head greedy dt={dt} H={H} V={V}", flush=True)
+    W, hid, g, rows, strided, x = _head_case(H + V, H, V, dt)
+    M = x.shape[0]
+    td = TD[dt]
+    segs = [dm.head_segment(_t(hid, torch.float32), _t(g, torch.float32)),
+            dm.head_segment(_t(rows, td)),
+            dm.head_segment(_t(strided, td), n=strided.shape[0], ld=2 * H)]
+    tok = torch.empty(M, dtype=torch.int32, device="cuda")
+    lse = torch.empty(M, dtype=torch.float32, device="cuda")
+    rmax = torch.empty(M, dtype=torch.float32, device="cuda")
+    gap = torch.empty(M, dtype=torch.float32, device="cuda")
+    prep = torch.empty(M, H, dtype=td, device="cuda")
+    dm.lm_head(_t(W, td), segs, tok, eps=1e-6, prepared=prep, lse=lse, row_max=rmax, gap=gap)
+    # prepared rows: normalised rows rounded to the head dtype
+    assert max_rel(prep.float().cpu().numpy(), x) < 2e-2
+    ref = odm.lm_head(x, W.astype(np.float64), np.zeros(M))
+    got = tok.cpu().numpy()
+    for m in range(M):
+        if got[m] != ref.token[m]:
+            assert ref.margin[m] < NEAR_TIE, (m, got[m], ref.token[m], ref.margin[m])
+    assert max_rel(lse.cpu().numpy(), ref.lse) < 1e-5
+    assert max_rel(rmax.cpu().numpy(), ref.row_max) < 1e-4
+    print("  exempt:", int((got != ref.token).sum()), "of", M)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_lm_head_sampled_planted_and_stored(dm, dt):
+    H, V = 512, 7001
+    W, hid, g, rows, strided, x = _head_case(11, H, V, dt, M_norm=6, M_rows=24, M_strided=9)
+    M = x.shape[0]
+    td = TD[dt]
+    r = np.random.default_rng(12)
+    tau = np.where(r.random(M) < 0.6, r.choice([1.0, 0.7, 1.3], size=M), 0.0).astype(np.float32)
+    keys = (np.arange(M, dtype=np.uint64) * np.uint64(977) + np.uint64(5)).astype(np.uint64)
+    keys[3] = np.uint64(0xFFFFFFFFFFFFFFFF)           # a no-draw row
+    store = np.arange(M, dtype=np.int32)[::-1].copy()  # every row stored, reversed order
+    plant = np.full(M, -1, np.int32)
+    plant[[1, 7]] = [M - 1, 0]
+    seed = 0x1234_5678_9ABC
+    segs = [dm.head_segment(_t(hid, torch.float32), _t(g, torch.float32)),
+            dm.head_segment(_t(rows, td)),
+            dm.head_segment(_t(strided, td), n=strided.shape[0], ld=2 * H)]
+    tok = torch.empty(M, dtype=torch.int32, device="cuda")
+    lse = torch.empty(M, dtype=torch.float32, device="cuda")
+    logits = torch.full((M, V), float("nan"), dtype=torch.float32, device="cuda")
+    dm.lm_head(_t(W, td), segs, tok, temperature=_t(tau, torch.float32),
+               draw_key=_t(keys.view(np.int64), torch.int64), seed=seed,
+               plant_row=_t(plant, torch.int32), store_row=_t(store, torch.int32), logits=logits,
+               lse=lse)
+    L = W.astype(np.float64)
+    ref_logits = x @ L.T
+    got_logits = logits.cpu().numpy()[store]
+    assert max_rel(got_logits, ref_logits) < 2e-3
+    t = np.where(tau > 0, tau, 1.0)
+    assert max_rel(lse.cpu().numpy(), onm.logsumexp(ref_logits / t[:, None])) < 1e-4
+    got = tok.cpu().numpy()
+    n_ex = 0
+    for m in range(M):
+        if plant[m] >= 0:
+            src = plant[m]
+            want, margin = int(np.argmax(ref_logits[src])), float(onm.top2_gap(ref_logits[src]))
+        elif tau[m] > 0 and keys[m] != np.uint64(0xFFFFFFFFFFFFFFFF):
+            want, margin = oph.gumbel_argmax(ref_logits[m] / tau[m], seed, int(keys[m]))
+        else:
+            want, margin = int(np.argmax(ref_logits[m])), float(onm.top2_gap(ref_logits[m]))
+        if got[m] != want:
+            assert margin < NEAR_TIE, (m, got[m], want, margin)
+            n_ex += 1
+    print("exempt", n_ex)
+
+
+def test_lm_head_rows_do_not_depend_on_the_batch(dm):
+    H, V = 2048, 20000
+    W, hid, g, rows, strided, x = _head_case(21, H, V, "bf16", M_norm=0, M_rows=100, M_strided=0)
+    Wt = _t(W, torch.bfloat16)
+    X = _t(rows, torch.bfloat16)
+    outs = {}
+    for name, sl in (("all", slice(0, 100)), ("one", slice(37, 38)), ("tail", slice(63, 100))):
+        xs = X[sl].contiguous()
+        n = xs.shape[0]
+        tok = torch.empty(n, dtype=torch.int32, device="cuda")
+        lse = torch.empty(n, dtype=torch.float32, device="cuda")
+        dm.lm_head(Wt, [dm.head_segment(xs)], tok, lse=lse)
+        outs[name] = (tok.cpu().numpy(), lse.cpu().numpy())
+    assert outs["one"][0][0] == outs["all"][0][37] and outs["one"][1][0] == outs["all"][1][37]
+    np.testing.assert_array_equal(outs["tail"][1], outs["all"][1][63:])
+    np.testing.assert_array_equal(outs["tail"][0], outs["all"][0][63:])
+
+
+# ---------------------------------------------------------------- block draft
+
+
+def _draft_case(seed, dt, B, H, Hq, Hkv, d, F, NL, K, n_anchor, ctx_lens, V=500, window=0):
+    r = np.random.default_rng(seed)
+    cu = np.concatenate([[0], np.cumsum(ctx_lens)]).astype(np.int32)
+    tot = int(cu[-1])
+    emb = _store(0.02 * r.standard_normal((V, H)), dt)
+    layers = []
+    for _ in range(NL):
+        layers.append(dict(
+            g_attn=(1 + 0.1 * r.standard_normal(H)).astype(np.float32),
+            wqkv=_store(0.02 * r.standard_normal(((Hq + 2 * Hkv) * d, H)), dt),
+            wo=_store(0.02 * r.standard_normal((H, Hq * d)), dt),
+            g_ffn=(1 + 0.1 * r.standard_normal(H)).astype(np.float32),
+            wg=_store(0.02 * r.standard_normal((F, H)), dt),
+            wu=_store(0.02 * r.standard_normal((F, H)), dt),
+            wd=_store(0.02 * r.standard_normal((H, F)), dt),
+            ctx_k=_store(r.standard_normal((max(tot, 1), Hkv, d)), dt),
+            ctx_v=_store(r.standard_normal((max(tot, 1), Hkv, d)), dt)))
+    anchor = r.integers(0, V - 1, size=B).astype(np.int32)
+    x_t1 = (emb[r.integers(0, V - 1, size=B)] + 0.01 * r.standard_normal((B, H))).astype(np.float32)
+    g_final = (1 + 0.1 * r.standard_normal(H)).astype(np.float32)
+    return dict(cu=cu, emb=emb, layers=layers, anchor=anchor, x_t1=x_t1, g_final=g_final,
+                ctx_lens=np.asarray(ctx_lens))
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [
+    dict(B=3, H=256, Hq=4, Hkv=2, d=64, F=512, NL=2, K=7, n_anchor=2, ctx_lens=[0, 70, 200]),
+    dict(B=2, H=512, Hq=8, Hkv=2, d=128, F=768, NL=1, K=7, n_anchor=1, ctx_lens=[130, 1]),
+    dict(B=4, H=256, Hq=4, Hkv=4, d=64, F=256, NL=1, K=5, n_anchor=2, ctx_lens=[300, 64, 65, 5],
+         window=100),
+    dict(B=2, H=512, Hq=10, Hkv=2, d=128, F=512, NL=1, K=16, n_anchor=2, ctx_lens=[777, 2100]),
+])
+def test_block_draft(dm, dt, shape):
+    shape = dict(shape)
+    window = shape.pop("window", 0)
+    print(f"block_draft dt={dt} {shape} window={window}", flush=True)
+    c = _draft_case(sum(shape["ctx_lens"]) + shape["H"], dt, window=window, **shape)
+    B, H, K, na = shape["B"], shape["H"], shape["K"], shape["n_anchor"]
+    td = TD[dt]
+    f32 = torch.float32
+    lt = [{k: _t(v, f32 if k.startswith("g_") else td) for k, v in L.items()} for L in c["layers"]]
+    Ls = [dm.layer_arg(**L) for L in lt]
+    out = torch.empty(B * (K - 1), H, dtype=td, device="cuda")
+    V = c["emb"].shape[0]
+    dm.block_draft(out, B=B, H=H, Hq=shape["Hq"], Hkv=shape["Hkv"], d=shape["d"], F=shape["F"], K=K,
+                   n_anchor=na, layers=Ls, anchor_ids=_t(c["anchor"], torch.int32),
+                   x_t1=_t(c["x_t1"], f32), mask_id=V - 1, emb=_t(c["emb"], td),
+                   cu_ctx=_t(c["cu"], torch.int32), max_ctx=int(max(c["ctx_lens"])),
+                   ctx_rows=int(c["cu"][-1]), g_final=_t(c["g_final"], f32), window=window)
+    got = out.float().cpu().numpy().reshape(B, K - 1, H)
+    slots = [odm.block_slots(c["emb"][c["anchor"][b]], c["x_t1"][b], c["emb"][V - 1], K, na)
+             for b in range(B)]
+    L64 = [odm.Layer64(*(np.asarray(L[k], np.float64) for k in
+                         ("g_attn", "wqkv", "wo", "g_ffn", "wg", "wu", "wd"))) for L in c["layers"]]
+    ref = odm.block_draft(slots, c["ctx_lens"], L64, [L["ctx_k"] for L in c["layers"]],
+                          [L["ctx_v"] for L in c["layers"]], c["cu"], list(range(B)), c["g_final"],
+                          onm.round_to(dt), Hq=shape["Hq"], Hkv=shape["Hkv"], d=shape["d"], eps=1e-6,
+                          rope_base=1e6, window=window)
+    ref = np.stack(ref)[:, na:, :]
+    err = max_rel(got, ref)
+    print("  max rel", err)
+    assert err < (1e-4 if dt == "f32" else 2e-2)
+    if dt == "bf16":
+        # rounding flips only: almost every element is the same bf16 value
+        assert np.mean(got != ref) < 0.02
+
+
+# ---------------------------------------------------------------- verify
+
+
+def _softmax_lse(l, tau):
+    return onm.logsumexp(l / tau, axis=-1)
+
+
+@pytest.mark.parametrize("V", [3001, 151936])
+def test_verify_greedy_and_sampled(dm, V):
+    B, K = 24, 7
+    r = np.random.default_rng(V)
+    tau = np.where(np.arange(B) % 2 == 0, 0.0, 1.0).astype(np.float32)
+    tau[5] = 0.8
+    logits = (1.5 * r.standard_normal((B, 2 * K + 1, V))).astype(np.float32)
+    # candidates: from the q rows, with target rows made to agree on a planted prefix
+    target = logits[:, K:, :].argmax(-1).astype(np.int32)
+    drafts = r.integers(0, V, size=(B, K)).astype(np.int32)
+    for b in range(B):
+        k = (b // 2) % (K + 1)                # force acceptance up to row k (greedy rows)
+        drafts[b, :k] = target[b, :k]
+        if k < K and drafts[b, k] == target[b, k]:
+            drafts[b, k] = (target[b, k] + 1) % V
+    u = (r.integers(0, 1 << 24, size=(B, K)) * 2.0 ** -24).astype(np.float32)
+    # sampled rows: force accept below row k (u = 0) and a sure rejection at row k
+    for b in range(B):
+        if tau[b] > 0:
+            k = (b // 2) % (K + 1)
+            u[b, :k] = 0.0
+            if k < K:
+                logits[b, K + k, drafts[b, k]] = -30.0
+                u[b, k] = 0.999
+    tt = np.where(tau > 0, tau, 1.0).astype(np.float64)
+    lse = _softmax_lse(logits.astype(np.float64), tt[:, None, None]).astype(np.float32)
+    seed = 77
+    fkeys = np.arange(B, dtype=np.uint64) + np.uint64(1 << 33)
+    acc = torch.empty(B, dtype=torch.int32, device="cuda")
+    out = torch.empty(B, K + 1, dtype=torch.int32, device="cuda")
+    n_out = torch.empty(B, dtype=torch.int32, device="cuda")
+    dm.verify(B=B, K=K, V=V, t1=_t(drafts[:, 0], torch.int32), drafts=_t(drafts[:, 1:], torch.int32),
+              target=_t(target, torch.int32), accept_len=acc, out_tokens=out, n_out=n_out,
+              temperature=_t(tau, torch.float32), logits=_t(logits.reshape(B * (2 * K + 1), V),
+                                                            torch.float32),
+              t1_lse=_t(lse[:, 0], torch.float32), draft_lse=_t(lse[:, 1:K], torch.float32),
+              target_lse=_t(lse[:, K:], torch.float32), u_acc=_t(u, torch.float32), seed=seed,
+              final_key=_t(fkeys.view(np.int64), torch.int64))
+    acc, out, n_out = acc.cpu().numpy(), out.cpu().numpy(), n_out.cpu().numpy()
+    L64 = logits.astype(np.float64)
+    for b in range(B):
+        if tau[b] == 0:
+            L, toks = odm.verify_greedy(drafts[b], target[b])
+            assert acc[b] == L and list(out[b, :L + 1]) == toks and n_out[b] == L + 1
+            assert np.all(out[b, L + 1:] == -1)
+            assert L == (b // 2) % (K + 1)
+            continue
+        q = np.exp(L64[b, :K] / tau[b] - onm.logsumexp(L64[b, :K] / tau[b])[:, None])
+        p = np.exp(L64[b, K:] / tau[b] - onm.logsumexp(L64[b, K:] / tau[b])[:, None])
+        margins = {}
+
+        def accept(i, ratio):
+            margins[("a", i)] = abs(np.log(u[b, i]) - np.log(ratio)) if u[b, i] > 0 else np.inf
+            return bool(u[b, i] < ratio)
+
+        def draw(i, w):
+            with np.errstate(divide="ignore"):
+                j, m = oph.gumbel_argmax(np.log(np.asarray(w)), seed, int(fkeys[b]))
+            margins["final"] = m
+            return j
+
+        L, toks = odm.verify_rejection(drafts[b], p, q, accept, draw)
+        if acc[b] != L:
+            assert margins.get(("a", min(L, acc[b])), np.inf) < NEAR_TIE
+            continue
+        assert list(out[b, :L]) == toks[:L] and n_out[b] == L + 1
+        if out[b, L] != toks[L]:
+            assert margins["final"] < NEAR_TIE, (b, out[b, L], toks[L], margins["final"])
+        k = (b // 2) % (K + 1)
+        assert L == k

@@ -62,12 +62,17 @@ def _layer(r, H, Hq, Hkv, d, F_, scale=0.05, zero=()):
 KW = dict(Hq=4, Hkv=2, d=8, eps=1e-6, rope_base=1e6)
 
 
+def _layer1(X, pos, lw, ck, cv, **kw):
+    """draft_layer on one sequence."""
+    return dmtp.draft_layer(X[None], np.asarray(pos)[None], lw, [ck], [cv], **kw)[0]
+
+
 def test_draft_layer_with_zero_output_projections_is_identity():
     r = _rng(3)
     X = r.standard_normal((5, 32))
     lw = _layer(r, 32, 4, 2, 8, 48, zero=("wo", "wd"))
     ck, cv = r.standard_normal((9, 2, 8)), r.standard_normal((9, 2, 8))
-    np.testing.assert_array_equal(dmtp.draft_layer(X, 9 + np.arange(5), lw, ck, cv, **KW), X)
+    np.testing.assert_array_equal(_layer1(X, 9 + np.arange(5), lw, ck, cv, **KW), X)
 
 
 def test_draft_layer_single_slot_no_context_closed_form():
@@ -75,7 +80,7 @@ def test_draft_layer_single_slot_no_context_closed_form():
     r = _rng(4)
     X = r.standard_normal((1, 32))
     lw = _layer(r, 32, 4, 2, 8, 48, zero=("wg", "wu"))
-    out = dmtp.draft_layer(X, np.array([0]), lw, np.zeros((0, 2, 8)), np.zeros((0, 2, 8)), **KW)
+    out = _layer1(X, np.array([0]), lw, np.zeros((0, 2, 8)), np.zeros((0, 2, 8)), **KW)
     xh = nm.rmsnorm(X, lw.g_attn, 1e-6)
     v = (xh @ lw.wqkv.T)[:, (4 + 2) * 8:].reshape(1, 2, 8)
     o = np.repeat(v, 2, axis=1).reshape(1, 32)       # q heads 0,1 -> kv 0; 2,3 -> kv 1
@@ -88,10 +93,10 @@ def test_draft_attention_is_bidirectional_inside_the_block():
     lw = _layer(r, 32, 4, 2, 8, 48)
     ck, cv = r.standard_normal((7, 2, 8)), r.standard_normal((7, 2, 8))
     pos = 7 + np.arange(6)
-    a = dmtp.draft_layer(X, pos, lw, ck, cv, **KW)
+    a = _layer1(X, pos, lw, ck, cv, **KW)
     X2 = X.copy()
     X2[5] += 1.0                       # perturb the last slot only
-    b = dmtp.draft_layer(X2, pos, lw, ck, cv, **KW)
+    b = _layer1(X2, pos, lw, ck, cv, **KW)
     assert np.all(np.abs(a[0] - b[0]) > 0)   # the first slot sees the last one
 
 
@@ -109,8 +114,8 @@ def test_draft_gqa_equals_mha_with_repeated_kv_heads():
     m = dmtp.Layer64(g.g_attn, np.concatenate([q_rows, rep(k_rows), rep(v_rows)]), g.wo, g.g_ffn,
                      g.wg, g.wu, g.wd)
     pos = 5 + np.arange(4)
-    a = dmtp.draft_layer(X, pos, g, ck, cv, **KW)
-    b = dmtp.draft_layer(X, pos, m, np.repeat(ck, 2, 1), np.repeat(cv, 2, 1),
+    a = _layer1(X, pos, g, ck, cv, **KW)
+    b = _layer1(X, pos, m, np.repeat(ck, 2, 1), np.repeat(cv, 2, 1),
                          **{**KW, "Hkv": 4})
     np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-13)
 
@@ -121,10 +126,10 @@ def test_draft_window_keeps_the_last_positions():
     lw = _layer(r, 32, 4, 2, 8, 48)
     ck, cv = r.standard_normal((20, 2, 8)), r.standard_normal((20, 2, 8))
     pos = 20 + np.arange(3)
-    a = dmtp.draft_layer(X, pos, lw, ck, cv, window=6, **KW)
-    b = dmtp.draft_layer(X, pos, lw, ck[-6:], cv[-6:], **KW)
-    c = dmtp.draft_layer(X, pos, lw, ck, cv, window=20, **KW)
-    d = dmtp.draft_layer(X, pos, lw, ck, cv, **KW)
+    a = _layer1(X, pos, lw, ck, cv, window=6, **KW)
+    b = _layer1(X, pos, lw, ck[-6:], cv[-6:], **KW)
+    c = _layer1(X, pos, lw, ck, cv, window=20, **KW)
+    d = _layer1(X, pos, lw, ck, cv, **KW)
     np.testing.assert_array_equal(a, b)
     np.testing.assert_array_equal(c, d)
     assert not np.allclose(a, d)
