@@ -102,6 +102,7 @@ def fuse(out: torch.Tensor, W: torch.Tensor, g1: torch.Tensor, g2: torch.Tensor,
 
 def layer_arg(g_attn, wqkv, wo, g_ffn, wg, wu, wd, ctx_k, ctx_v) -> Layer:
     L = Layer()
+    L._keep = (g_attn, wqkv, wo, g_ffn, wg, wu, wd, ctx_k, ctx_v)
     L.g_attn, L.wqkv, L.wo, L.g_ffn = _ptr(g_attn), _ptr(wqkv), _ptr(wo), _ptr(g_ffn)
     L.wg, L.wu, L.wd = _ptr(wg), _ptr(wu), _ptr(wd)
     L.ctx_k, L.ctx_v = _ptr(ctx_k), _ptr(ctx_v)
@@ -135,6 +136,7 @@ def block_draft(out: torch.Tensor, *, B: int, H: int, Hq: int, Hkv: int, d: int,
 def head_segment(x: torch.Tensor, g_norm: Optional[torch.Tensor] = None, n: Optional[int] = None,
                  ld: Optional[int] = None) -> HeadSegment:
     s = HeadSegment()
+    s._keep = (x, g_norm)   # the struct holds raw pointers: keep the tensors alive with it
     s.x = _ptr(x)
     s.n = x.shape[0] if n is None else n
     s.ld = x.shape[-1] if ld is None else ld
@@ -157,6 +159,7 @@ def lm_head(W: torch.Tensor, segments: Sequence[HeadSegment], token: torch.Tenso
     D.dtype = dtype_code(W.dtype)
     D.eps = eps
     D.n_seg = len(segments)
+    D._keep = list(segments)
     for i, s in enumerate(segments):
         D.seg[i] = s
     D.W = _ptr(W)

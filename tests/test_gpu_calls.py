@@ -235,6 +235,18 @@ def test_block_draft(dm, dt, shape):
     Ls = [dm.layer_arg(**L) for L in lt]
     out = torch.empty(B * (K - 1), H, dtype=td, device="cuda")
     V = c["emb"].shape[0]
+    S = K - 1 + na
+    if dt == "f32" and S * shape["Hq"] // shape["Hkv"] > 64:
+        # float32 context K/V doubles the LDS tiles: more than 64 query rows per
+        # kv head do not fit one workgroup, and the library refuses the shape
+        with pytest.raises(dm.DmtpError):
+            dm.block_draft(out, B=B, H=H, Hq=shape["Hq"], Hkv=shape["Hkv"], d=shape["d"],
+                           F=shape["F"], K=K, n_anchor=na, layers=Ls,
+                           anchor_ids=_t(c["anchor"], torch.int32), x_t1=_t(c["x_t1"], f32),
+                           mask_id=V - 1, emb=_t(c["emb"], td), cu_ctx=_t(c["cu"], torch.int32),
+                           max_ctx=int(max(c["ctx_lens"])), ctx_rows=int(c["cu"][-1]),
+                           g_final=_t(c["g_final"], f32), window=window)
+        return
     dm.block_draft(out, B=B, H=H, Hq=shape["Hq"], Hkv=shape["Hkv"], d=shape["d"], F=shape["F"], K=K,
                    n_anchor=na, layers=Ls, anchor_ids=_t(c["anchor"], torch.int32),
                    x_t1=_t(c["x_t1"], f32), mask_id=V - 1, emb=_t(c["emb"], td),
