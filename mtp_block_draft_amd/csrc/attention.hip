@@ -236,57 +236,65 @@ __global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(
 }
 
 // Merge the chunk partials and the S block keys; o [B * S, Hq * D].
+// One wave per query row (rows r = 4 blockIdx.y + wave of kv head blockIdx.x);
+// lane l owns dims l, l + 64.  The block-key scores are exact float32 dot
+// products; the chunk weights exp(m_c - M) and the block weights are shared
+// through the wave's slice of LDS.
 __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(
     const float* __restrict__ q, const float* __restrict__ kb, const float* __restrict__ vb,
     const float* __restrict__ part_o, const float* __restrict__ part_ml, int Hkv, int G, int S, int D,
     int NQP, int n_chunks, float scale, float* __restrict__ o) {
-  __shared__ float w_chunk[256];
-  __shared__ float w_blk[64];
-  __shared__ float s_blk[64];
-  __shared__ float inv_l;
+  __shared__ float w_chunk[4][256];
+  __shared__ float w_blk[4][64];
   const int kvh = blockIdx.x % Hkv, b = blockIdx.x / Hkv;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int NQ = S * G;
+  const int r = blockIdx.y * 4 + wave;
+  if (r >= NQ) return;
   const size_t bh = (size_t)b * Hkv + kvh;
-  const float* qg = q + bh * NQ * D;
+  const float* qr = q + (bh * NQ + r) * D;
   const float* kbg = kb + bh * S * D;
   const float* vbg = vb + bh * S * D;
-  for (int r = 0; r < NQ; ++r) {
-    // block-key scores (float32, exact products)
-    for (int j = threadIdx.x; j < S; j += blockDim.x) {
-      float acc = 0.f;
-      for (int k = 0; k < D; ++k) acc = fmaf(qg[(size_t)r * D + k], kbg[(size_t)j * D + k], acc);
-      s_blk[j] = acc * scale;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      float M = -INFINITY;
-      for (int c = 0; c < n_chunks; ++c) M = fmaxf(M, part_ml[(bh * n_chunks + c) * 2 * NQP + r]);
-      for (int j = 0; j < S; ++j) M = fmaxf(M, s_blk[j]);
-      float Lsum = 0.f;
-      for (int c = 0; c < n_chunks; ++c) {
-        const float* ml = part_ml + (bh * n_chunks + c) * 2 * NQP;
-        const float w = ml[r] == -INFINITY ? 0.f : expf(ml[r] - M);
-        w_chunk[c] = w;
-        Lsum += w * ml[NQP + r];
-      }
-      for (int j = 0; j < S; ++j) {
-        const float w = expf(s_blk[j] - M);
-        w_blk[j] = w;
-        Lsum += w;
-      }
-      inv_l = 1.0f / Lsum;
-    }
-    __syncthreads();
-    const int s = r / G, g = r % G;
-    float* orow = o + ((size_t)b * S + s) * ((size_t)Hkv * G * D) + ((size_t)kvh * G + g) * D;
-    for (int k = threadIdx.x; k < D; k += blockDim.x) {
-      float acc = 0.f;
-      for (int c = 0; c < n_chunks; ++c)
-        acc += w_chunk[c] * part_o[((bh * n_chunks + c) * NQP + r) * D + k];
-      for (int j = 0; j < S; ++j) acc += w_blk[j] * vbg[(size_t)j * D + k];
-      orow[k] = acc * inv_l;
-    }
-    __syncthreads();
+  const float q0 = qr[lane], q1 = D > 64 ? qr[lane + 64] : 0.f;
+  float M = -INFINITY;
+  for (int j = 0; j < S; ++j) {
+    float part = q0 * kbg[(size_t)j * D + lane];
+    if (D > 64) part = fmaf(q1, kbg[(size_t)j * D + lane + 64], part);
+    const float sj = wave_sum(part) * scale;
+    if (lane == 0) w_blk[wave][j] = sj;
+    M = fmaxf(M, sj);
+  }
+  const float* ml = part_ml + bh * n_chunks * 2 * NQP;
+  for (int c = lane; c < n_chunks; c += kWave) M = fmaxf(M, ml[(size_t)c * 2 * NQP + r]);
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, shfl_xor(M, off));
+  float Lsum = 0.f;
+  for (int c = lane; c < n_chunks; c += kWave) {
+    const float mc = ml[(size_t)c * 2 * NQP + r];
+    const float w = mc == -INFINITY ? 0.f : expf(mc - M);
+    w_chunk[wave][c] = w;
+    Lsum += w * ml[(size_t)c * 2 * NQP + NQP + r];
+  }
+  Lsum = wave_sum(Lsum);
+  __threadfence_block();
+  __builtin_amdgcn_wave_barrier();
+  float blk = 0.f;
+  for (int j = lane; j < S; j += kWave) {
+    const float w = expf(w_blk[wave][j] - M);
+    w_blk[wave][j] = w;
+    blk += w;
+  }
+  Lsum += wave_sum(blk);
+  __threadfence_block();
+  __builtin_amdgcn_wave_barrier();
+  const float inv_l = 1.0f / Lsum;
+  const int s = r / G, g = r % G;
+  float* orow = o + ((size_t)b * S + s) * ((size_t)Hkv * G * D) + ((size_t)kvh * G + g) * D;
+  for (int k = lane; k < D; k += kWave) {
+    float acc = 0.f;
+    for (int c = 0; c < n_chunks; ++c)
+      acc = fmaf(w_chunk[wave][c], part_o[((bh * n_chunks + c) * NQP + r) * D + k], acc);
+    for (int j = 0; j < S; ++j) acc = fmaf(w_blk[wave][j], vbg[(size_t)j * D + k], acc);
+    orow[k] = acc * inv_l;
   }
 }
 
@@ -405,8 +413,8 @@ hipError_t attention(const AttnPlan& p, const float* q, const float* kb, const f
                    : dispatch_rt<128, 1>(p, q, ctx_k, ctx_v, cu_ctx, cr, po, pml, scale, s);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(p.B * p.Hkv), dim3(kAttnThreads), 0, s, q, kb, vb, po,
-                     pml, p.Hkv, p.G, p.S, p.d, nqp, p.n_chunks, scale, o);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(p.B * p.Hkv, (p.NQ + 3) / 4), dim3(kAttnThreads), 0, s,
+                     q, kb, vb, po, pml, p.Hkv, p.G, p.S, p.d, nqp, p.n_chunks, scale, o);
   return hipGetLastError();
 }
 

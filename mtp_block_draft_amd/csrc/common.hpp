@@ -48,6 +48,16 @@ __device__ __forceinline__ f32x4_t mfma_16x16x32(const uint4& a, const uint4& b,
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// D(32x32, f32) += A(32x16, bf16) * B(16x32, bf16).  Lane l supplies row
+// (l % 32) of A and column (l % 32) of B, eight consecutive k values from the
+// lane half l / 32; it receives D[8 (i / 4) + 4 (l / 32) + (i % 4)][l % 32] in
+// element i (i = 0..15).
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ f32x16_t mfma_32x32x16(const uint4& a, const uint4& b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
 // ----------------------------------------------------------- reductions ----
 template <typename T>
 __device__ __forceinline__ T shfl_xor(T v, int mask) {
