@@ -1104,8 +1104,8 @@ WsLayout ws_layout(const dmtp_head_desc& d, int M) {
 }
 
 // Selects the bf16 head kernel variant from DMTP_HEAD_KERNEL, read once:
-// 0 (default) the 16 x 16 x 32 LDS-DMA kernel, 1 the register-staged pair,
-// 2 the 32 x 32 x 16 LDS-DMA kernel.
+// 0 (default) the 32 x 32 x 16 LDS-DMA kernel, 1 the register-staged pair,
+// 2 the 16 x 16 x 32 LDS-DMA kernel.
 int head_kernel_choice() {
   static int v = [] {
     const char* e = getenv("DMTP_HEAD_KERNEL");
@@ -1168,8 +1168,8 @@ hipError_t lm_head_run(const dmtp_head_desc& d, int M, void* ws, hipStream_t s) 
   }
   if (d.dtype == DMTP_BF16 && d.H % 128 == 0) {
     const int kc = head_kernel_choice();
-    e = kc == 1 ? launch_head_big_any(p, s) : kc == 2 ? launch_head_mf32_any(p, s)
-                                                       : launch_head_lds_any(p, s);
+    e = kc == 1 ? launch_head_big_any(p, s) : kc == 2 ? launch_head_lds_any(p, s)
+                                                       : launch_head_mf32_any(p, s);
     if (e != hipSuccess) return e;
   } else if (d.dtype == DMTP_BF16) {
     dim3 grid(w.n_vtiles, (M + HeadTileBF16::BM - 1) / HeadTileBF16::BM);
