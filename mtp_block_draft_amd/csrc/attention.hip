@@ -235,7 +235,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(
   }
 }
 
-// Merge the chunk partials and the S block keys; o [B * S, Hq * D].
+// Merge the chunk partials and the S block keys; o [B * S, Hq * D] as bf16
+// planes (hi at o, lo at o + o_pst).
 // One wave per query row (rows r = 4 blockIdx.y + wave of kv head blockIdx.x);
 // lane l owns dims l, l + 64.  The block-key scores are exact float32 dot
 // products; the chunk weights exp(m_c - M) and the block weights are shared
@@ -243,7 +244,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(
 __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(
     const float* __restrict__ q, const float* __restrict__ kb, const float* __restrict__ vb,
     const float* __restrict__ part_o, const float* __restrict__ part_ml, int Hkv, int G, int S, int D,
-    int NQP, int n_chunks, float scale, float* __restrict__ o) {
+    int NQP, int n_chunks, float scale, uint16_t* __restrict__ o, size_t o_pst) {
   __shared__ float w_chunk[4][256];
   __shared__ float w_blk[4][64];
   const int kvh = blockIdx.x % Hkv, b = blockIdx.x / Hkv;
@@ -288,13 +289,16 @@ __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(
   __builtin_amdgcn_wave_barrier();
   const float inv_l = 1.0f / Lsum;
   const int s = r / G, g = r % G;
-  float* orow = o + ((size_t)b * S + s) * ((size_t)Hkv * G * D) + ((size_t)kvh * G + g) * D;
+  const size_t orow = ((size_t)b * S + s) * ((size_t)Hkv * G * D) + ((size_t)kvh * G + g) * D;
   for (int k = lane; k < D; k += kWave) {
     float acc = 0.f;
-    for (int c = 0; c < n_chunks; ++c)
-      acc = fmaf(w_chunk[wave][c], part_o[((bh * n_chunks + c) * NQP + r) * D + k], acc);
+    for (int c = 0; c < n_chunks; ++c) {
+      // an empty chunk has weight 0 and never wrote its partial O
+      const float w = w_chunk[wave][c];
+      if (w != 0.f) acc = fmaf(w, part_o[((bh * n_chunks + c) * NQP + r) * D + k], acc);
+    }
     for (int j = 0; j < S; ++j) acc = fmaf(w_blk[wave][j], vbg[(size_t)j * D + k], acc);
-    orow[k] = acc * inv_l;
+    store_planes(o, o_pst, orow + k, acc * inv_l);
   }
 }
 
@@ -396,7 +400,7 @@ size_t attn_ws_bytes(const AttnPlan& p) {
 
 hipError_t attention(const AttnPlan& p, const float* q, const float* kb, const float* vb,
                      const void* ctx_k, const void* ctx_v, const int32_t* cu_ctx, int ctx_rows,
-                     float* ws, float* o, hipStream_t s) {
+                     float* ws, uint16_t* o, hipStream_t s) {
   const int nqp = nqp_of(p.NQ);
   const size_t slots = (size_t)p.B * p.Hkv * (p.n_chunks > 0 ? p.n_chunks : 1);
   float* po = ws;
@@ -414,7 +418,8 @@ hipError_t attention(const AttnPlan& p, const float* q, const float* kb, const f
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(attn_combine_kernel, dim3(p.B * p.Hkv, (p.NQ + 3) / 4), dim3(kAttnThreads), 0, s,
-                     q, kb, vb, po, pml, p.Hkv, p.G, p.S, p.d, nqp, p.n_chunks, scale, o);
+                     q, kb, vb, po, pml, p.Hkv, p.G, p.S, p.d, nqp, p.n_chunks, scale, o,
+                     (size_t)p.B * p.S * p.Hkv * p.G * p.d);
   return hipGetLastError();
 }
 

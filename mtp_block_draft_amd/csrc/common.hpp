@@ -35,6 +35,15 @@ __device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) 
   lo = f32_to_bf16(x - bf16_to_f32(hi));
 }
 
+// Element i of a float32 activation stored as its two bf16 planes: the hi
+// plane at p, the lo plane at p + pst.
+__device__ __forceinline__ void store_planes(uint16_t* p, size_t pst, size_t i, float v) {
+  uint16_t h, l;
+  split_bf16(v, h, l);
+  p[i] = h;
+  p[pst + i] = l;
+}
+
 __device__ __forceinline__ uint32_t pack2(uint16_t a, uint16_t b) {
   return (uint32_t)a | ((uint32_t)b << 16);
 }

@@ -72,7 +72,8 @@ int validate_fuse(const dmtp_fuse_desc* d) {
 }
 
 size_t fuse_ws(const dmtp_fuse_desc* d) {
-  return al((size_t)d->rows * 2 * d->H * 4) + al(gemm_ws_bytes(d->rows, d->H, 2 * d->H));
+  return al((size_t)d->rows * 2 * d->H * 4) +
+         al(gemm_ws_bytes(d->rows, d->H, 2 * d->H, d->w_dtype == DMTP_F32));
 }
 
 // ---------------------------------------------------------- block draft ----
@@ -124,8 +125,9 @@ DraftWs draft_ws(const dmtp_draft_desc* d) {
   const int qkv_n = (d->Hq + 2 * d->Hkv) * d->d;
   w.plan = attn_plan(d->B, d->Hq, d->Hkv, S, d->d, d->max_ctx, d->window, d->dtype == DMTP_F32);
   size_t gemm_max = 0;
+  const int wf32 = d->dtype == DMTP_F32;
   auto upd = [&](int M, int N, int K) {
-    const size_t b = gemm_ws_bytes(M, N, K);
+    const size_t b = gemm_ws_bytes(M, N, K, wf32);
     if (b > gemm_max) gemm_max = b;
   };
   upd((int)R, qkv_n, d->H);
@@ -218,13 +220,14 @@ int dmtp_fuse(const dmtp_fuse_desc* d, void* ws, size_t ws_bytes, hipStream_t st
   CHECK(ws != nullptr, DMTP_E_NULL);
   CHECK(((uintptr_t)ws % kAlign) == 0, DMTP_E_ALIGN);
   if ((e = check_device()) != DMTP_OK) return e;
-  float* cat = (float*)ws;
+  uint16_t* cat = (uint16_t*)ws;   // bf16 planes [2][rows][2H]
   float* part = (float*)((char*)ws + al((size_t)d->rows * 2 * d->H * 4));
   hipError_t h = fuse_prep(*d, cat, stream);
   if (h != hipSuccess) return DMTP_E_LAUNCH;
   const bool has_res = d->res.rows || d->res.ids;
-  GemmArgs g{cat, 1, (size_t)2 * d->H, d->rows, d->W, d->w_dtype == DMTP_F32, (size_t)2 * d->H,
-             d->H, 2 * d->H, d->out, (size_t)d->H, has_res ? d->out : nullptr, (size_t)d->H};
+  GemmArgs g{cat, (size_t)d->rows * 2 * d->H, (size_t)2 * d->H, d->rows, d->W,
+             d->w_dtype == DMTP_F32, (size_t)2 * d->H, d->H, 2 * d->H, d->out, (size_t)d->H,
+             has_res ? d->out : nullptr, (size_t)d->H};
   return launch_status(gemm(g, part, stream));
 }
 
@@ -243,15 +246,15 @@ int dmtp_block_draft(const dmtp_draft_desc* d, void* ws, size_t ws_bytes, hipStr
   if ((e = check_device()) != DMTP_OK) return e;
   char* b = (char*)ws;
   float* X = (float*)(b + w.X);
-  float* xh = (float*)(b + w.xh);
+  uint16_t* xh = (uint16_t*)(b + w.xh);   // bf16 planes [2][R][H]
   float* qkv = (float*)(b + w.qkv);
   float* q = (float*)(b + w.q);
   float* kb = (float*)(b + w.kb);
   float* vb = (float*)(b + w.vb);
-  float* o = (float*)(b + w.o);
+  uint16_t* o = (uint16_t*)(b + w.o);     // bf16 planes [2][R][Hq d]
   float* gate = (float*)(b + w.gate);
   float* up = (float*)(b + w.up);
-  float* act = (float*)(b + w.act);
+  uint16_t* act = (uint16_t*)(b + w.act); // bf16 planes [2][R][F]
   float* gws = (float*)(b + w.gemm);
   float* aws = (float*)(b + w.attn);
   const int S = d->K - 1 + d->n_anchor;
@@ -262,8 +265,9 @@ int dmtp_block_draft(const dmtp_draft_desc* d, void* ws, size_t ws_bytes, hipStr
   for (int l = 0; l < d->n_layers && h == hipSuccess; ++l) {
     const dmtp_layer& L = d->layers[l];
     if ((h = rmsnorm_rows(X, L.g_attn, d->eps, xh, R, d->H, stream)) != hipSuccess) break;
-    GemmArgs g1{xh, 1, (size_t)d->H, R, L.wqkv, wf32, (size_t)d->H, qkv_n, d->H, qkv, (size_t)qkv_n,
-                nullptr, 0};
+    const size_t pst_h = (size_t)R * d->H, pst_o = (size_t)R * d->Hq * d->d, pst_f = (size_t)R * d->F;
+    GemmArgs g1{xh, pst_h, (size_t)d->H, R, L.wqkv, wf32, (size_t)d->H, qkv_n, d->H, qkv,
+                (size_t)qkv_n, nullptr, 0};
     if ((h = gemm(g1, gws, stream)) != hipSuccess) break;
     if ((h = rope_split(qkv, d->cu_ctx, d->ctx_rows, d->B, S, d->Hq, d->Hkv, d->d, d->rope_base, q,
                         kb, vb, stream)) != hipSuccess)
@@ -272,19 +276,19 @@ int dmtp_block_draft(const dmtp_draft_desc* d, void* ws, size_t ws_bytes, hipStr
                        stream)) != hipSuccess)
       break;
     const int od = d->Hq * d->d;
-    GemmArgs g2{o, 1, (size_t)od, R, L.wo, wf32, (size_t)od, d->H, od, X, (size_t)d->H, X,
+    GemmArgs g2{o, pst_o, (size_t)od, R, L.wo, wf32, (size_t)od, d->H, od, X, (size_t)d->H, X,
                 (size_t)d->H};
     if ((h = gemm(g2, gws, stream)) != hipSuccess) break;
     if ((h = rmsnorm_rows(X, L.g_ffn, d->eps, xh, R, d->H, stream)) != hipSuccess) break;
-    GemmArgs g3{xh, 1, (size_t)d->H, R, L.wg, wf32, (size_t)d->H, d->F, d->H, gate, (size_t)d->F,
-                nullptr, 0};
+    GemmArgs g3{xh, pst_h, (size_t)d->H, R, L.wg, wf32, (size_t)d->H, d->F, d->H, gate,
+                (size_t)d->F, nullptr, 0};
     if ((h = gemm(g3, gws, stream)) != hipSuccess) break;
-    GemmArgs g4{xh, 1, (size_t)d->H, R, L.wu, wf32, (size_t)d->H, d->F, d->H, up, (size_t)d->F,
-                nullptr, 0};
+    GemmArgs g4{xh, pst_h, (size_t)d->H, R, L.wu, wf32, (size_t)d->H, d->F, d->H, up,
+                (size_t)d->F, nullptr, 0};
     if ((h = gemm(g4, gws, stream)) != hipSuccess) break;
     if ((h = swiglu(gate, up, act, (size_t)R * d->F, stream)) != hipSuccess) break;
-    GemmArgs g5{act, 1, (size_t)d->F, R, L.wd, wf32, (size_t)d->F, d->H, d->F, X, (size_t)d->H, X,
-                (size_t)d->H};
+    GemmArgs g5{act, pst_f, (size_t)d->F, R, L.wd, wf32, (size_t)d->F, d->H, d->F, X,
+                (size_t)d->H, X, (size_t)d->H};
     h = gemm(g5, gws, stream);
   }
   if (h == hipSuccess)

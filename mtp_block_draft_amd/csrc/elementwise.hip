@@ -33,15 +33,17 @@ __device__ double inv_rms(Load ld, int H, float eps, double* red) {
   return 1.0 / sqrt(ss / H + (double)eps);
 }
 
+// y = RMSNorm(x; g) written as bf16 planes [2][rows][H] (plane stride pst).
 __global__ __launch_bounds__(kRowThreads) void rmsnorm_rows_kernel(const float* __restrict__ x,
                                                                    const float* __restrict__ g,
-                                                                   float eps, float* __restrict__ y,
-                                                                   int H) {
+                                                                   float eps, uint16_t* __restrict__ y,
+                                                                   size_t pst, int H) {
   __shared__ double red[kRowThreads / kWave];
   const float* xr = x + (size_t)blockIdx.x * H;
   const double inv = inv_rms([&](int i) { return (double)xr[i]; }, H, eps, red);
-  float* yr = y + (size_t)blockIdx.x * H;
-  for (int i = threadIdx.x; i < H; i += blockDim.x) yr[i] = (float)((double)xr[i] * inv * g[i]);
+  const size_t r0 = (size_t)blockIdx.x * H;
+  for (int i = threadIdx.x; i < H; i += blockDim.x)
+    store_planes(y, pst, r0 + i, (float)((double)xr[i] * inv * g[i]));
 }
 
 struct RowSrc {
@@ -63,16 +65,17 @@ __device__ __forceinline__ float row_elem(const RowSrc& s, int r, int H, int i) 
 __global__ __launch_bounds__(kRowThreads) void fuse_prep_kernel(RowSrc x1, RowSrc x2, RowSrc res,
                                                                 int has_res, const float* g1,
                                                                 const float* g2, float eps, int H,
-                                                                float* __restrict__ cat,
+                                                                uint16_t* __restrict__ cat,
+                                                                size_t pst,
                                                                 float* __restrict__ out) {
   __shared__ double red[kRowThreads / kWave];
   const int r = blockIdx.x;
   const double i1 = inv_rms([&](int i) { return (double)row_elem(x1, r, H, i); }, H, eps, red);
   const double i2 = inv_rms([&](int i) { return (double)row_elem(x2, r, H, i); }, H, eps, red);
-  float* c = cat + (size_t)r * 2 * H;
+  const size_t c0 = (size_t)r * 2 * H;
   for (int i = threadIdx.x; i < H; i += blockDim.x) {
-    c[i] = (float)((double)row_elem(x1, r, H, i) * i1 * g1[i]);
-    c[H + i] = (float)((double)row_elem(x2, r, H, i) * i2 * g2[i]);
+    store_planes(cat, pst, c0 + i, (float)((double)row_elem(x1, r, H, i) * i1 * g1[i]));
+    store_planes(cat, pst, c0 + H + i, (float)((double)row_elem(x2, r, H, i) * i2 * g2[i]));
     if (has_res) out[(size_t)r * H + i] = row_elem(res, r, H, i);
   }
 }
@@ -128,12 +131,13 @@ __global__ void rope_split_kernel(const float* __restrict__ qkv, const int32_t* 
   }
 }
 
+// a = silu(g) * u, written as bf16 planes [2][n] (plane stride n).
 __global__ void swiglu_kernel(const float* __restrict__ g, const float* __restrict__ u,
-                              float* __restrict__ a, size_t n) {
+                              uint16_t* __restrict__ a, size_t n) {
   for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
        e += (size_t)gridDim.x * blockDim.x) {
     const float x = g[e];
-    a[e] = x / (1.0f + expf(-x)) * u[e];
+    store_planes(a, n, e, x / (1.0f + expf(-x)) * u[e]);
   }
 }
 
@@ -162,17 +166,18 @@ RowSrc src_of(const dmtp_rows& r, int w_dtype) {
 
 }  // namespace
 
-hipError_t rmsnorm_rows(const float* x, const float* g, float eps, float* y, int rows, int H,
+hipError_t rmsnorm_rows(const float* x, const float* g, float eps, uint16_t* y, int rows, int H,
                         hipStream_t s) {
-  hipLaunchKernelGGL(rmsnorm_rows_kernel, dim3(rows), dim3(kRowThreads), 0, s, x, g, eps, y, H);
+  hipLaunchKernelGGL(rmsnorm_rows_kernel, dim3(rows), dim3(kRowThreads), 0, s, x, g, eps, y,
+                     (size_t)rows * H, H);
   return hipGetLastError();
 }
 
-hipError_t fuse_prep(const dmtp_fuse_desc& d, float* cat, hipStream_t s) {
+hipError_t fuse_prep(const dmtp_fuse_desc& d, uint16_t* cat, hipStream_t s) {
   const int has_res = d.res.rows != nullptr || d.res.ids != nullptr;
   hipLaunchKernelGGL(fuse_prep_kernel, dim3(d.rows), dim3(kRowThreads), 0, s,
                      src_of(d.x1, d.w_dtype), src_of(d.x2, d.w_dtype), src_of(d.res, d.w_dtype),
-                     has_res, d.g1, d.g2, d.eps, d.H, cat, d.out);
+                     has_res, d.g1, d.g2, d.eps, d.H, cat, (size_t)d.rows * 2 * d.H, d.out);
   return hipGetLastError();
 }
 
@@ -191,7 +196,7 @@ hipError_t rope_split(const float* qkv, const int32_t* cu_ctx, int ctx_rows, int
   return hipGetLastError();
 }
 
-hipError_t swiglu(const float* g, const float* u, float* a, size_t n, hipStream_t s) {
+hipError_t swiglu(const float* g, const float* u, uint16_t* a, size_t n, hipStream_t s) {
   const size_t blocks = (n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192;
   hipLaunchKernelGGL(swiglu_kernel, dim3((unsigned)blocks), dim3(256), 0, s, g, u, a, n);
   return hipGetLastError();

@@ -1,6 +1,16 @@
-// Generic float32-output GEMM for the fusion projections and the drafter's
-// layer projections: C = R + A B^T, with a deterministic split over K for the
-// small-M, weight-streaming (HBM-bound) shapes of this path.
+// Float32-output GEMMs of the fusion projections and the drafter's layer
+// projections: C = R + A B^T, where A is a float32 activation held as two bf16
+// planes (hi + lo) and B a weight stored [out, in].
+//
+// These are small-M, weight-streaming shapes (M = the 32 fused rows or the
+// B * S draft slots, N and K in the thousands).  A bf16 weight goes through
+// gemm_dma_kernel: 32 x 32 x 16 MFMA tiles fed by a ring of LDS stages that
+// global_load_lds copies fill several k-slices ahead, with K split into
+// contiguous ranges so that about one workgroup per CU is busy; the float32
+// partial sums are added in a fixed order by splitk_reduce4, so results are
+// deterministic.  A float32 weight (the float32 configurations) goes through
+// the plain tiled kernel of gemm_core.hpp.
+#include "dma.hpp"
 #include "gemm_core.hpp"
 #include "kernels.hpp"
 
@@ -10,30 +20,258 @@ namespace {
 
 struct GemmParams {
   const void* A;
+  size_t a_pst;
   size_t lda;
   int M;
   const void* B;
   size_t ldb;
   int N;
-  int k_per_split;
+  int K;
+  int splits;
   float* C;
   size_t ldc;
   const float* R;
   size_t ldr;
-  float* part;   // [splits, M, N] when gridDim.z > 1
+  float* part;   // [splits, M, N] when splits > 1
 };
 
+// ------------------------------------------------- bf16 weight, LDS ring ----
+// Workgroup of four waves, WAVES_N along N times 4 / WAVES_N along M; wave tile
+// 32 UN (weight rows) x 32 UM (activation rows).  One k-slice of 32 is staged
+// as W [BN][32] and the two activation planes [2][BM][32], bf16, 16-byte chunks
+// swizzled by swz_k32.
+template <int UN_, int UM_, int WAVES_N_>
+struct DmaTile {
+  static constexpr int UN = UN_, UM = UM_, WAVES_N = WAVES_N_, WAVES_M = 4 / WAVES_N_;
+  static constexpr int BN = 32 * UN * WAVES_N, BM = 32 * UM * WAVES_M, BK = 32;
+  static constexpr int W_INSTR = BN * BK * 2 / 1024;   // 1 KB copies per slice
+  static constexpr int A_INSTR = 2 * BM * BK * 2 / 1024;
+  static_assert((W_INSTR + A_INSTR) % 4 == 0 && A_INSTR % 2 == 0, "copies per wave");
+  static constexpr int PER_WAVE = (W_INSTR + A_INSTR) / 4;
+  static constexpr int STAGE = (BN + 2 * BM) * BK;     // bf16 elements
+  static constexpr int NBUF_FIT = 147456 / (STAGE * 2);
+  static constexpr int NBUF = NBUF_FIT > 8 ? 8 : NBUF_FIT;
+  static_assert(NBUF >= 2 && PER_WAVE * (NBUF - 2) < 64, "ring");
+  static constexpr size_t LDS_BYTES = (size_t)NBUF * STAGE * 2;
+};
+
+template <class T>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_dma_kernel(GemmParams p, int n_tiles_n, int n_tiles_m) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  const int total = n_tiles_n * n_tiles_m * p.splits;
+  const int per = (total + 7) / 8;   // XCD-contiguous ranges (workgroup i runs on XCD i % 8)
+  const int t = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (t >= total) return;
+  // consecutive t: the splits of one tile, then the tiles along N
+  const int z = t % p.splits;
+  const int tile = t / p.splits;
+  const int n0 = (tile % n_tiles_n) * T::BN, m0 = (tile / n_tiles_n) * T::BM;
+  const int nK = p.K / T::BK;
+  const int s_begin = (int)((long)z * nK / p.splits), s_end = (int)((long)(z + 1) * nK / p.splits);
+  const int ns = s_end - s_begin;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wn = wave % T::WAVES_N, wm = wave / T::WAVES_N;
+  const int lr = lane & 31, lk = lane >> 5;
+  const uint16_t* __restrict__ W = (const uint16_t*)p.B;
+  const uint16_t* __restrict__ A = (const uint16_t*)p.A;
+
+  // sources of this wave's copies: W rows first, then the hi and lo planes of A
+  // (rows clamped into range; their results are never stored)
+  const uint16_t* src[T::PER_WAVE];
+#pragma unroll
+  for (int q = 0; q < T::PER_WAVE; ++q) {
+    const int instr = wave * T::PER_WAVE + q;
+    if (instr < T::W_INSTR) {
+      const int idx = instr * 64 + lane, r = idx >> 2, c = (idx & 3) ^ ((r >> 2) & 3);
+      src[q] = W + (size_t)min(n0 + r, p.N - 1) * p.ldb + 8 * c;
+    } else {
+      const int j = instr - T::W_INSTR, pl = j / (T::A_INSTR / 2);
+      const int idx = (j % (T::A_INSTR / 2)) * 64 + lane, r = idx >> 2, c = (idx & 3) ^ ((r >> 2) & 3);
+      src[q] = A + pl * p.a_pst + (size_t)min(m0 + r, p.M - 1) * p.lda + 8 * c;
+    }
+  }
+  auto issue = [&](int s) __attribute__((always_inline)) {
+    uint16_t* st = smem + (s % T::NBUF) * T::STAGE;
+    const int k0 = (s_begin + s) * T::BK;
+#pragma unroll
+    for (int q = 0; q < T::PER_WAVE; ++q) lds_dma16(src[q] + k0, st + (wave * T::PER_WAVE + q) * 512);
+  };
+  struct Frag {
+    u32x4 w[T::UN];
+    u32x4 a[2][T::UM];
+  };
+  auto read = [&](Frag& f, int s, int ks) __attribute__((always_inline)) {
+    const uint16_t* st = smem + (s % T::NBUF) * T::STAGE;
+    const int c = 2 * ks + lk;
+#pragma unroll
+    for (int u = 0; u < T::UN; ++u) f.w[u] = *(const u32x4*)(st + swz_k32(32 * (T::UN * wn + u) + lr, c));
+#pragma unroll
+    for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+      for (int v = 0; v < T::UM; ++v)
+        f.a[pl][v] = *(const u32x4*)(st + T::BN * T::BK + pl * T::BM * T::BK +
+                                     swz_k32(32 * (T::UM * wm + v) + lr, c));
+  };
+  f32x16_t acc[T::UN][T::UM];
+#pragma unroll
+  for (int u = 0; u < T::UN; ++u)
+#pragma unroll
+    for (int v = 0; v < T::UM; ++v)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[u][v][i] = 0.f;
+  auto compute = [&](const Frag& f) __attribute__((always_inline)) {
+#pragma unroll
+    for (int v = 0; v < T::UM; ++v)
+#pragma unroll
+      for (int u = 0; u < T::UN; ++u) {
+        acc[u][v] = mfma32(f.w[u], f.a[0][v], acc[u][v]);
+        acc[u][v] = mfma32(f.w[u], f.a[1][v], acc[u][v]);
+      }
+  };
+  // Slice s is in LDS once this wave's copies of it have landed (later slices'
+  // copies may stay in flight) and every wave has passed the barrier; the
+  // buffer the next copy refills was read into registers just before.
+  auto wait_slice = [&](int s) __attribute__((always_inline)) {
+    wait_newer<T::PER_WAVE, T::NBUF - 2>(min(ns - 1 - s, T::NBUF - 2));
+    ring_barrier();
+  };
+
+#pragma unroll
+  for (int s0 = 0; s0 < T::NBUF - 1; ++s0)
+    if (s0 < ns) issue(s0);
+  Frag f0, f1;
+  wait_slice(0);
+  if (T::NBUF - 1 < ns) issue(T::NBUF - 1);
+  read(f0, 0, 0);
+  for (int s = 0; s < ns; ++s) {
+    read(f1, s, 1);
+    compute(f0);
+    if (s + 1 < ns) {
+      wait_slice(s + 1);
+      if (s + T::NBUF < ns) issue(s + T::NBUF);
+      read(f0, s + 1, 0);
+    }
+    compute(f1);
+  }
+
+  // element i of acc[u][v]: weight row n = n0 + 32 (UN wn + u) + 8 (i / 4) + 4 lk + i % 4,
+  // activation row m = m0 + 32 (UM wm + v) + lr; four consecutive n per store
+  const bool split = p.splits > 1;
+#pragma unroll
+  for (int v = 0; v < T::UM; ++v) {
+    const int m = m0 + 32 * (T::UM * wm + v) + lr;
+    if (m >= p.M) continue;
+#pragma unroll
+    for (int u = 0; u < T::UN; ++u)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + 32 * (T::UN * wn + u) + 8 * g + 4 * lk;
+        if (n >= p.N) continue;
+        float4 r = make_float4(acc[u][v][4 * g], acc[u][v][4 * g + 1], acc[u][v][4 * g + 2],
+                               acc[u][v][4 * g + 3]);
+        if (split) {
+          *(float4*)(p.part + ((size_t)z * p.M + m) * p.N + n) = r;
+        } else {
+          if (p.R) {
+            const float4 b = *(const float4*)(p.R + (size_t)m * p.ldr + n);
+            r.x += b.x;
+            r.y += b.y;
+            r.z += b.z;
+            r.w += b.w;
+          }
+          *(float4*)(p.C + (size_t)m * p.ldc + n) = r;
+        }
+      }
+  }
+}
+
+// C = R + sum_z part[z] in the order z = 0, 1, ...; four consecutive columns
+// per thread (N % 4 == 0).
+__global__ void splitk_reduce4(const float* __restrict__ part, int splits, int M, int N, float* C,
+                               size_t ldc, const float* R, size_t ldr) {
+  const size_t total4 = (size_t)M * N / 4;
+  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total4;
+       e += (size_t)gridDim.x * blockDim.x) {
+    const int row = (int)(4 * e / N), col = (int)(4 * e % N);
+    float4 s = *(const float4*)(part + 4 * e);
+    for (int z = 1; z < splits; ++z) {
+      const float4 v = *(const float4*)(part + (size_t)z * M * N + 4 * e);
+      s.x += v.x;
+      s.y += v.y;
+      s.z += v.z;
+      s.w += v.w;
+    }
+    if (R) {
+      const float4 b = *(const float4*)(R + (size_t)row * ldr + col);
+      s.x = b.x + s.x;
+      s.y = b.y + s.y;
+      s.z = b.z + s.z;
+      s.w = b.w + s.w;
+    }
+    *(float4*)(C + (size_t)row * ldc + col) = s;
+  }
+}
+
+typedef DmaTile<1, 1, 4> DmaM32;    // 128 x 32
+typedef DmaTile<2, 2, 2> DmaM128;   // 128 x 128
+typedef DmaTile<2, 4, 2> DmaM256;   // 128 x 256
+
+struct DmaPlan {
+  int cfg;   // 0: DmaM32, 1: DmaM128, 2: DmaM256
+  int tn, tm, splits;
+};
+
+DmaPlan dma_plan(int M, int N, int K) {
+  DmaPlan pl;
+  int BM;
+  if (M <= 32) {
+    pl.cfg = 0;
+    BM = DmaM32::BM;
+  } else if (M <= 128) {
+    pl.cfg = 1;
+    BM = DmaM128::BM;
+  } else {
+    pl.cfg = 2;
+    BM = DmaM256::BM;
+  }
+  pl.tn = (N + 127) / 128;
+  pl.tm = (M + BM - 1) / BM;
+  const int tiles = pl.tn * pl.tm;
+  const int nK = K / 32;
+  // about one workgroup per CU, each split at least four k-slices long
+  int sp = (256 + tiles - 1) / tiles;
+  if (sp > nK / 4) sp = nK / 4;
+  pl.splits = sp < 1 ? 1 : sp;
+  return pl;
+}
+
+bool dma_ok(const GemmArgs& a) {
+  return !a.b_f32 && a.K % 32 == 0 && a.N % 4 == 0 && a.ldc % 4 == 0 && (!a.R || a.ldr % 4 == 0) &&
+         a.lda % 8 == 0 && a.ldb % 8 == 0 && a.a_pst % 8 == 0;
+}
+
+template <class T>
+hipError_t launch_dma(const GemmParams& p, const DmaPlan& pl, hipStream_t s) {
+  hipError_t e = hipFuncSetAttribute((const void*)gemm_dma_kernel<T>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)T::LDS_BYTES);
+  if (e != hipSuccess) return e;
+  const int total = pl.tn * pl.tm * pl.splits;
+  hipLaunchKernelGGL(gemm_dma_kernel<T>, dim3(8 * ((total + 7) / 8)), dim3(256), T::LDS_BYTES, s, p,
+                     pl.tn, pl.tm);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------- float32 weight path ----
 template <class T>
 __global__ __launch_bounds__(T::THREADS) void gemm_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[T::LDS_A + T::LDS_B];
   const int n0 = blockIdx.x * T::BN, m0 = blockIdx.y * T::BM;
-  const int z = blockIdx.z;
   Acc<T> acc;
-  gemm_mainloop<T>(acc, lds, p.A, p.lda, p.M, p.B, p.ldb, p.N, m0, n0, z * p.k_per_split,
-                   (z + 1) * p.k_per_split);
+  gemm_mainloop<T>(acc, lds, p.A, p.lda, p.a_pst, p.M, p.B, p.ldb, p.N, m0, n0, 0, p.K);
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int wm0 = (wave / T::WAVES_N) * T::WM, wn0 = (wave % T::WAVES_N) * T::WN;
-  const bool split = gridDim.z > 1;
 #pragma unroll
   for (int i = 0; i < T::TM; ++i)
 #pragma unroll
@@ -43,75 +281,40 @@ __global__ __launch_bounds__(T::THREADS) void gemm_kernel(GemmParams p) {
         const int row = m0 + wm0 + 16 * i + 4 * (lane >> 4) + r;
         const int col = n0 + wn0 + 16 * j + (lane & 15);
         if (row >= p.M || col >= p.N) continue;
-        const float v = acc.v[i][j][r];
-        if (split) {
-          p.part[((size_t)z * p.M + row) * p.N + col] = v;
-        } else {
-          const float base = p.R ? p.R[(size_t)row * p.ldr + col] : 0.f;
-          p.C[(size_t)row * p.ldc + col] = base + v;
-        }
+        const float base = p.R ? p.R[(size_t)row * p.ldr + col] : 0.f;
+        p.C[(size_t)row * p.ldc + col] = base + acc.v[i][j][r];
       }
 }
 
-// C = R + sum_z part[z] in a fixed order.
-__global__ void splitk_reduce(const float* __restrict__ part, int splits, int M, int N, float* C,
-                              size_t ldc, const float* R, size_t ldr) {
-  const size_t total = (size_t)M * N;
-  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
-       e += (size_t)gridDim.x * blockDim.x) {
-    const int row = (int)(e / N), col = (int)(e % N);
-    float s = 0.f;
-    for (int z = 0; z < splits; ++z) s += part[(size_t)z * total + e];
-    const float base = R ? R[(size_t)row * ldr + col] : 0.f;
-    C[(size_t)row * ldc + col] = base + s;
-  }
-}
-
-typedef GemmTile<64, 64, 32, 32, 2, 1> TileF32xBF16;
-typedef GemmTile<64, 64, 32, 32, 2, 2> TileF32xF32;
-typedef GemmTile<64, 64, 32, 32, 1, 1> TileBF16xBF16;
-typedef GemmTile<64, 64, 32, 32, 1, 2> TileBF16xF32;
-
-template <class T>
-hipError_t launch(const GemmParams& p, int splits, hipStream_t s) {
-  dim3 grid((p.N + T::BN - 1) / T::BN, (p.M + T::BM - 1) / T::BM, splits);
-  hipLaunchKernelGGL(gemm_kernel<T>, grid, dim3(T::THREADS), 0, s, p);
-  return hipGetLastError();
-}
+typedef GemmTile<64, 64, 32, 32, 2, 2> TilePlanesF32;
 
 }  // namespace
 
-int gemm_splits(int M, int N, int K) {
-  const int tiles = ((M + 63) / 64) * ((N + 63) / 64);
-  int splits = 1;
-  // aim for >= 1024 workgroups on 256 CUs, keep >= 4 K-stages per split
-  while (tiles * splits < 1024 && K % (2 * splits * 64) == 0 && K / (2 * splits) >= 256)
-    splits *= 2;
-  return splits;
-}
-
-size_t gemm_ws_bytes(int M, int N, int K) {
-  const int sp = gemm_splits(M, N, K);
-  return sp > 1 ? (size_t)sp * M * N * sizeof(float) : 0;
+size_t gemm_ws_bytes(int M, int N, int K, int b_f32) {
+  if (b_f32) return 0;
+  const DmaPlan pl = dma_plan(M, N, K);
+  return pl.splits > 1 ? (size_t)pl.splits * M * N * sizeof(float) : 0;
 }
 
 hipError_t gemm(const GemmArgs& a, float* ws, hipStream_t s) {
-  const int splits = gemm_splits(a.M, a.N, a.K);
-  GemmParams p{a.A, a.lda, a.M, a.B, a.ldb, a.N, a.K / splits, a.C, a.ldc, a.R, a.ldr, ws};
-  hipError_t e;
-  if (a.a_f32 && !a.b_f32)
-    e = launch<TileF32xBF16>(p, splits, s);
-  else if (a.a_f32 && a.b_f32)
-    e = launch<TileF32xF32>(p, splits, s);
-  else if (!a.a_f32 && !a.b_f32)
-    e = launch<TileBF16xBF16>(p, splits, s);
-  else
-    e = launch<TileBF16xF32>(p, splits, s);
-  if (e != hipSuccess || splits == 1) return e;
-  const size_t total = (size_t)a.M * a.N;
-  const int blocks = (int)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
-  hipLaunchKernelGGL(splitk_reduce, dim3(blocks), dim3(256), 0, s, ws, splits, a.M, a.N, a.C,
-                     a.ldc, a.R, a.ldr);
+  GemmParams p{a.A, a.a_pst, a.lda, a.M, a.B, a.ldb, a.N, a.K, 1, a.C, a.ldc, a.R, a.ldr, ws};
+  if (!a.b_f32) {
+    if (!dma_ok(a)) return hipErrorInvalidValue;
+    const DmaPlan pl = dma_plan(a.M, a.N, a.K);
+    p.splits = pl.splits;
+    hipError_t e = pl.cfg == 0   ? launch_dma<DmaM32>(p, pl, s)
+                   : pl.cfg == 1 ? launch_dma<DmaM128>(p, pl, s)
+                                 : launch_dma<DmaM256>(p, pl, s);
+    if (e != hipSuccess || pl.splits == 1) return e;
+    const size_t total4 = (size_t)a.M * a.N / 4;
+    const int blocks = (int)((total4 + 255) / 256 < 4096 ? (total4 + 255) / 256 : 4096);
+    hipLaunchKernelGGL(splitk_reduce4, dim3(blocks), dim3(256), 0, s, ws, pl.splits, a.M, a.N, a.C,
+                       a.ldc, a.R, a.ldr);
+    return hipGetLastError();
+  }
+  dim3 grid((a.N + TilePlanesF32::BN - 1) / TilePlanesF32::BN,
+            (a.M + TilePlanesF32::BM - 1) / TilePlanesF32::BM);
+  hipLaunchKernelGGL(gemm_kernel<TilePlanesF32>, grid, dim3(TilePlanesF32::THREADS), 0, s, p);
   return hipGetLastError();
 }
 

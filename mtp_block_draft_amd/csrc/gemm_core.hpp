@@ -2,10 +2,12 @@
 //
 // Both operands are K-contiguous (row-major A, weights stored [out, in]), so a
 // lane's eight k values of an MFMA fragment are one 16-byte LDS read for A and
-// for B alike.  Operands stored in float32 are split on their way into LDS into
-// two bf16 planes (x = hi + lo to 2^-18), and the tile product accumulates the
-// plane pairs (hi,hi), (hi,lo), (lo,hi): a float32 activation times a bf16
-// weight costs two MFMAs, float32 x float32 three.  Accumulation is float32.
+// for B alike.  A float32 operand enters as two bf16 planes (x = hi + lo to
+// 2^-18): activations arrive already split by the kernel that produced them,
+// float32 weights are split on their way into LDS.  The tile product
+// accumulates the plane pairs (hi,hi), (hi,lo), (lo,hi): a float32 activation
+// times a bf16 weight costs two MFMAs, float32 x float32 three.  Accumulation
+// is float32.
 #pragma once
 
 #include "common.hpp"
@@ -37,12 +39,23 @@ struct Acc {
 };
 
 // Stage one BM x BK (or BN x BK) tile of a row-major K-contiguous operand into
-// LDS: a float32 operand (PLANES == 2) as its hi and lo bf16 planes, a bf16
-// operand (PLANES == 1) as is.  Rows >= nrows are zero-filled.
-template <int ROWS, int BK, int LDK, int THREADS, int PLANES>
+// LDS: a float32 operand (SRC == 2) split into its hi and lo bf16 planes, an
+// operand already held as two bf16 planes (SRC == 3, lo plane at g + pst), or a
+// bf16 operand (SRC == 1) as is.  Rows >= nrows are zero-filled.
+template <int ROWS, int BK, int LDK, int THREADS, int SRC>
 __device__ __forceinline__ void stage_tile(uint16_t* __restrict__ lds, const void* __restrict__ g,
-                                           size_t ld, int row0, int nrows, int k0) {
-  if (PLANES == 2) {
+                                           size_t ld, size_t pst, int row0, int nrows, int k0) {
+  if (SRC == 3) {
+    const uint16_t* src = (const uint16_t*)g;
+    constexpr int V8 = ROWS * BK / 8;
+    for (int idx = threadIdx.x; idx < 2 * V8; idx += THREADS) {
+      const int p = idx / V8, e = idx % V8;
+      const int r = e / (BK / 8), c8 = e % (BK / 8);
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (row0 + r < nrows) v = *(const uint4*)(src + p * pst + (size_t)(row0 + r) * ld + k0 + 8 * c8);
+      *(uint4*)(lds + p * ROWS * LDK + r * LDK + 8 * c8) = v;
+    }
+  } else if (SRC == 2) {
     const float* src = (const float*)g;
     constexpr int V4 = ROWS * BK / 4;
     for (int idx = threadIdx.x; idx < V4; idx += THREADS) {
@@ -70,12 +83,13 @@ __device__ __forceinline__ void stage_tile(uint16_t* __restrict__ lds, const voi
 }
 
 // Main loop over k in [k_begin, k_end) (multiples of BK) for the workgroup tile
-// at (m0, n0).  A is [M, lda], float32 when T::AP == 2 else bf16; B is [N, ldb],
-// float32 when T::BP == 2 else bf16.
-template <class T>
+// at (m0, n0).  A is [M, lda]: bf16 when T::AP == 1; when T::AP == 2 two bf16
+// planes (lo at A + a_pst) if A_F32 is false, else float32 split on the way in.
+// B is [N, ldb], float32 when T::BP == 2 else bf16.
+template <class T, bool A_F32 = false>
 __device__ __forceinline__ void gemm_mainloop(Acc<T>& acc, uint16_t* lds, const void* A, size_t lda,
-                                              int M, const void* B, size_t ldb, int N, int m0,
-                                              int n0, int k_begin, int k_end) {
+                                              size_t a_pst, int M, const void* B, size_t ldb, int N,
+                                              int m0, int n0, int k_begin, int k_end) {
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
   const int wm0 = (wave / T::WAVES_N) * T::WM;
@@ -89,8 +103,9 @@ __device__ __forceinline__ void gemm_mainloop(Acc<T>& acc, uint16_t* lds, const 
 
   const int fr = lane & 15, fk = (lane >> 4) * 8;
   for (int k0 = k_begin; k0 < k_end; k0 += T::BK) {
-    stage_tile<T::BM, T::BK, T::LDK, T::THREADS, T::AP>(As, A, lda, m0, M, k0);
-    stage_tile<T::BN, T::BK, T::LDK, T::THREADS, T::BP>(Bs, B, ldb, n0, N, k0);
+    stage_tile<T::BM, T::BK, T::LDK, T::THREADS, T::AP == 1 ? 1 : (A_F32 ? 2 : 3)>(As, A, lda, a_pst,
+                                                                                   m0, M, k0);
+    stage_tile<T::BN, T::BK, T::LDK, T::THREADS, T::BP>(Bs, B, ldb, 0, n0, N, k0);
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < T::BK; kk += 32) {

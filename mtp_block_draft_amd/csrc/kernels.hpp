@@ -11,9 +11,11 @@ namespace dmtp {
 
 // ------------------------------------------------------------------ GEMM ----
 // C[M, N] (float32, ldc) = R[M, N] (optional, may alias C) + A[M, K] B[N, K]^T.
+// A is a float32 activation held as two bf16 planes (hi at A, lo at A + a_pst,
+// row stride lda); B is a weight stored [out, in], bf16 or float32.
 struct GemmArgs {
-  const void* A;
-  int a_f32;        // A is float32 (split into two bf16 planes) or bf16
+  const uint16_t* A;
+  size_t a_pst;
   size_t lda;
   int M;
   const void* B;
@@ -27,19 +29,19 @@ struct GemmArgs {
   size_t ldr;
 };
 
-// Split-K factor the launcher uses and the float32 workspace it needs.
-int gemm_splits(int M, int N, int K);
-size_t gemm_ws_bytes(int M, int N, int K);
+// float32 workspace the GEMM launcher needs for its split-K partials.
+size_t gemm_ws_bytes(int M, int N, int K, int b_f32);
 hipError_t gemm(const GemmArgs& a, float* ws, hipStream_t s);
 
 // -------------------------------------------------------------- elementwise --
-// y[r] = RMSNorm(x[r]; g) for float32 rows of width H.
-hipError_t rmsnorm_rows(const float* x, const float* g, float eps, float* y, int rows, int H,
+// y[r] = RMSNorm(x[r]; g) for float32 rows of width H, written as bf16 planes
+// [2][rows][H].
+hipError_t rmsnorm_rows(const float* x, const float* g, float eps, uint16_t* y, int rows, int H,
                         hipStream_t s);
 
-// Fusion prologue: cat[r] = [RMSNorm(x1[r]; g1), RMSNorm(x2[r]; g2)] (float32
-// [rows, 2H]) and out[r] = res[r] (float32) when res is present.
-hipError_t fuse_prep(const dmtp_fuse_desc& d, float* cat, hipStream_t s);
+// Fusion prologue: cat[r] = [RMSNorm(x1[r]; g1), RMSNorm(x2[r]; g2)] as bf16
+// planes [2][rows][2H], and out[r] = res[r] (float32) when res is present.
+hipError_t fuse_prep(const dmtp_fuse_desc& d, uint16_t* cat, hipStream_t s);
 
 // Draft slots X [B * S, H] float32 from anchor ids, x_t1 rows and the MASK row.
 hipError_t build_slots(const dmtp_draft_desc& d, float* X, hipStream_t s);
@@ -50,8 +52,8 @@ hipError_t rope_split(const float* qkv, const int32_t* cu_ctx, int ctx_rows, int
                       int Hkv, int d, float rope_base, float* q, float* kb, float* vb,
                       hipStream_t s);
 
-// a = silu(g) * u elementwise ([n] float32)
-hipError_t swiglu(const float* g, const float* u, float* a, size_t n, hipStream_t s);
+// a = silu(g) * u elementwise ([n] float32 in, bf16 planes [2][n] out)
+hipError_t swiglu(const float* g, const float* u, uint16_t* a, size_t n, hipStream_t s);
 
 // out[b, j] = round_dtype(RMSNorm(X[b, n_anchor + j]; g)) for j = 0 .. K-2
 hipError_t final_norm_mask(const float* X, const float* g, float eps, int B, int S, int n_anchor,
@@ -65,10 +67,11 @@ AttnPlan attn_plan(int B, int Hq, int Hkv, int S, int d, int max_ctx, int window
 // Largest number of query rows per kv head (S * Hq / Hkv) the kernels support.
 int attn_max_nq(int d, int kv_f32);
 size_t attn_ws_bytes(const AttnPlan& p);
-// o [B * S, Hq * d] float32 = attention of the block queries over context + block keys.
+// o [B * S, Hq * d] = attention of the block queries over context + block
+// keys, written as bf16 planes [2][B * S][Hq * d].
 hipError_t attention(const AttnPlan& p, const float* q, const float* kb, const float* vb,
                      const void* ctx_k, const void* ctx_v, const int32_t* cu_ctx, int ctx_rows,
-                     float* ws, float* o, hipStream_t s);
+                     float* ws, uint16_t* o, hipStream_t s);
 
 // ---------------------------------------------------------------- LM head --
 size_t lm_head_ws_bytes(const dmtp_head_desc& d, int M);

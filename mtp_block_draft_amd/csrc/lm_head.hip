@@ -14,6 +14,7 @@
 //   finalize  token per row: draw, planted row argmax, or argmax
 #include <cstdlib>
 
+#include "dma.hpp"
 #include "gemm_core.hpp"
 #include "kernels.hpp"
 
@@ -123,7 +124,7 @@ __global__ __launch_bounds__(T::THREADS) void head_gemm_kernel(HeadParams p) {
   __shared__ RowStat wstat[T::WAVES_N][T::BM];
   const int n0 = blockIdx.x * T::BN, m0 = blockIdx.y * T::BM;
   Acc<T> acc;
-  gemm_mainloop<T>(acc, lds, p.A, (size_t)p.H, p.M, p.W, (size_t)p.H, p.V, m0, n0, 0, p.H);
+  gemm_mainloop<T, true>(acc, lds, p.A, (size_t)p.H, 0, p.M, p.W, (size_t)p.H, p.V, m0, n0, 0, p.H);
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int wmi = wave / T::WAVES_N, wni = wave % T::WAVES_N;
   const int wm0 = wmi * T::WM, wn0 = wni * T::WN;
@@ -207,12 +208,7 @@ __device__ __forceinline__ int swz64(int r, int c) { return r * 64 + ((c ^ (r & 
 // row r, 16-byte chunk c of a [rows][128] bf16 tile, chunks XOR-swizzled by row
 __device__ __forceinline__ int swz128(int r, int c) { return r * 128 + ((c ^ (r & 15)) << 3); }
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ f32x16_t mfma32(const u32x4& a, const u32x4& b, f32x16_t c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
 
 template <int NBW>
 __global__ __launch_bounds__(HeadBig<NBW>::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -509,13 +505,6 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// vmcnt(N) and lgkmcnt(0)
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm0() {
-  static_assert(N >= 0 && N < 64, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
-}
-
 template <int T>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void head_gemm_lds_kernel(HeadParams p, int n_mchunks) {
@@ -690,8 +679,6 @@ struct HeadMf32 {
   static constexpr size_t LDS_BYTES = (size_t)NBUF * STAGE * 2;
 };
 
-__device__ __forceinline__ int swz32b(int r, int c) { return r * 32 + ((c ^ ((r >> 2) & 3)) << 3); }
-
 template <int TB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void head_gemm_mf32_kernel(HeadParams p, int n_mchunks) {
@@ -745,10 +732,10 @@ void head_gemm_mf32_kernel(HeadParams p, int n_mchunks) {
   auto read = [&](Frag& f, int slice, int ks) __attribute__((always_inline)) {
     const uint16_t* st = smem + (slice % C::NBUF) * C::STAGE;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) f.a[u] = *(const u32x4*)(st + swz32b(64 * vh + 32 * u + lr, 2 * ks + lk));
+    for (int u = 0; u < 2; ++u) f.a[u] = *(const u32x4*)(st + swz_k32(64 * vh + 32 * u + lr, 2 * ks + lk));
 #pragma unroll
     for (int t = 0; t < TB; ++t)
-      f.b[t] = *(const u32x4*)(st + C::BV * C::BK + swz32b(32 * TB * bh + 32 * t + lr, 2 * ks + lk));
+      f.b[t] = *(const u32x4*)(st + C::BV * C::BK + swz_k32(32 * TB * bh + 32 * t + lr, 2 * ks + lk));
   };
   f32x16_t acc[2][TB];
 #pragma unroll

@@ -41,7 +41,7 @@ TD = {"bf16": torch.bfloat16, "f32": torch.float32}
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-@pytest.mark.parametrize("rows,H", [(1, 256), (37, 256), (32, 2048)])
+@pytest.mark.parametrize("rows,H", [(1, 256), (37, 256), (32, 2048), (144, 320), (300, 2048)])
 @pytest.mark.parametrize("residual", [False, True])
 def test_fuse(dm, dt, rows, H, residual):
     print(f"fuse dt={dt} rows={rows} H={H} res={residual}", flush=True)
@@ -222,6 +222,14 @@ def _draft_case(seed, dt, B, H, Hq, Hkv, d, F, NL, K, n_anchor, ctx_lens, V=500,
     dict(B=4, H=256, Hq=4, Hkv=4, d=64, F=256, NL=1, K=5, n_anchor=2, ctx_lens=[300, 64, 65, 5],
          window=100),
     dict(B=2, H=512, Hq=10, Hkv=2, d=128, F=512, NL=1, K=16, n_anchor=2, ctx_lens=[777, 2100]),
+    # 48 query rows per kv head at d = 64, 32 slot rows
+    dict(B=2, H=256, Hq=6, Hkv=2, d=64, F=512, NL=1, K=15, n_anchor=2, ctx_lens=[100, 300]),
+    # 160 slot rows (one ragged 256-row GEMM tile), 16 query rows per kv head
+    dict(B=20, H=256, Hq=4, Hkv=2, d=64, F=512, NL=1, K=7, n_anchor=2,
+         ctx_lens=[0, 1, 31, 64, 100, 257, 513, 40, 9, 77, 5, 6, 7, 8, 300, 2, 3, 4, 65, 129]),
+    # 144 slot rows, widths that end mid-tile, 48 query rows per kv head
+    dict(B=9, H=320, Hq=6, Hkv=2, d=64, F=576, NL=1, K=15, n_anchor=2,
+         ctx_lens=[0, 1, 31, 64, 100, 257, 513, 40, 9]),
 ])
 def test_block_draft(dm, dt, shape):
     shape = dict(shape)
