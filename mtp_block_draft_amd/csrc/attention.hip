@@ -9,7 +9,16 @@
 // float32 queries and probabilities split into hi/lo bf16 planes.  Each chunk
 // leaves an unnormalised partial (O, running max m, running sum l); a combine
 // kernel merges the chunks exactly and adds the S block keys in float32.
-#include "common.hpp"
+//
+// bf16 context K/V (attn_wave_kernel): one wave per (context chunk, kv head,
+// 32-row query tile, sequence), no workgroup barriers.  32-key K and V tiles
+// stream through a private ring of LDS stages filled by global_load_lds copies;
+// S^T = K Q^T is one 32 x 32 MFMA tile with the query planes held in
+// registers, so every lane owns one query row and its online softmax needs a
+// single exchange with lane l ^ 32; O^T += V^T P^T takes the V^T operand from
+// the transposing LDS read (ds_read_b64_tr_b16) and P^T straight from the
+// softmax registers.  The float32 K/V path keeps the workgroup kernel.
+#include "dma.hpp"
 #include "kernels.hpp"
 
 namespace dmtp {
@@ -235,6 +244,203 @@ __global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(
   }
 }
 
+// ------------------------------------------------------ bf16 K/V, per wave --
+template <int D>
+struct WaveAttn {
+  static constexpr int KT = 32;                  // keys per tile
+  static constexpr int CPR = D / 8;              // 16-byte chunks per key row
+  static constexpr int RPI = 64 / CPR;           // key rows per 1 KB copy
+  static constexpr int INSTR = KT / RPI;         // copies per operand per tile
+  static constexpr int PER_TILE = 2 * INSTR;
+  static constexpr int NBUF = 4;
+  static constexpr int STAGE = 2 * KT * D;       // bf16 elements: K tile, then V tile
+  static constexpr size_t LDS_BYTES = (size_t)NBUF * STAGE * 2;
+  static constexpr int DS = D / 16;              // k-steps of Q K^T
+  static constexpr int DT = D / 32;              // 32-row tiles of O^T
+};
+
+// XOR swizzles of the 16-byte chunks of key row r.  K is read 16 rows x one
+// chunk per pass: distinct chunk positions for any 16 consecutive rows.  V is
+// read by the transposing load as 4 consecutive rows x 2 chunks: 2 (r % 4)
+// keeps those eight chunks apart.
+template <int D>
+__device__ __forceinline__ int swz_key(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+__device__ __forceinline__ int swz_val(int r) { return 2 * (r & 3); }
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+// Four bf16 of the transposing LDS read; see the V^T operand below.
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+  const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16_t*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void attn_wave_kernel(
+    const float* __restrict__ q, const uint16_t* __restrict__ ctx_k,
+    const uint16_t* __restrict__ ctx_v, const int32_t* __restrict__ cu_ctx, int ctx_rows, int Hkv,
+    int NQ, int NQP, int chunk, int n_chunks, int window, float scale, float* __restrict__ part_o,
+    float* __restrict__ part_ml) {
+  typedef WaveAttn<D> C;
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  const int c = blockIdx.x, kvh = blockIdx.y % Hkv, qt = blockIdx.y / Hkv, b = blockIdx.z;
+  const int lane = threadIdx.x, lr = lane & 31, g = lane >> 5;
+  const int L = ctx_len_of(cu_ctx, b, ctx_rows);
+  const int start = (window > 0 && L > window) ? L - window : 0;
+  const int k_lo = start + c * chunk;
+  const int k_hi = min(k_lo + chunk, L);
+  const size_t slot = ((size_t)b * Hkv + kvh) * n_chunks + c;
+  float* po = part_o + slot * NQP * D;
+  float* pml = part_ml + slot * 2 * NQP;
+  const int qrow = 32 * qt + lr;   // this lane's query row
+  if (k_lo >= k_hi) {               // empty chunk: neutral partial
+    if (g == 0) {
+      pml[qrow] = -INFINITY;
+      pml[NQP + qrow] = 0.f;
+    }
+    return;
+  }
+  const int nkeys = k_hi - k_lo;
+  const int nt = (nkeys + C::KT - 1) / C::KT;
+
+  // copies: instruction i of a tile moves key rows RPI i .. RPI i + RPI - 1;
+  // lane supplies row RPI i + lane / CPR, chunk position lane % CPR
+  const size_t row_stride = (size_t)Hkv * D;
+  const size_t seq0 = (size_t)cu_ctx[b];
+  const int rr = lane / C::CPR, pos = lane % C::CPR;
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    uint16_t* st = smem + (t % C::NBUF) * C::STAGE;
+#pragma unroll
+    for (int i = 0; i < C::INSTR; ++i) {
+      const int r = C::RPI * i + rr;
+      const int key = min(k_lo + C::KT * t + r, k_hi - 1);   // rows past the end: masked below
+      const size_t off = (seq0 + key) * row_stride + (size_t)kvh * D;
+      lds_dma16(ctx_k + off + 8 * (pos ^ swz_key<D>(r)), st + i * 512);
+      lds_dma16(ctx_v + off + 8 * (pos ^ swz_val(r)), st + C::KT * D + i * 512);
+    }
+  };
+  // query fragments (B operand of S^T = K Q^T): column = query row, 8 d values;
+  // loaded before the first copies so that waiting for them leaves those in flight
+  const float* qg = q + (((size_t)b * Hkv + kvh) * NQ) * D;
+  u32x4 qh[C::DS], ql[C::DS];
+#pragma unroll
+  for (int ds = 0; ds < C::DS; ++ds) {
+    float v[8];
+    if (qrow < NQ) {
+      const float4 a = *(const float4*)(qg + (size_t)qrow * D + 16 * ds + 8 * g);
+      const float4 e = *(const float4*)(qg + (size_t)qrow * D + 16 * ds + 8 * g + 4);
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = e.x; v[5] = e.y; v[6] = e.z; v[7] = e.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = 0.f;
+    }
+    uint16_t h[8], l[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) split_bf16(v[j], h[j], l[j]);
+    qh[ds] = u32x4{pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7])};
+    ql[ds] = u32x4{pack2(l[0], l[1]), pack2(l[2], l[3]), pack2(l[4], l[5]), pack2(l[6], l[7])};
+  }
+
+#pragma unroll
+  for (int t0 = 0; t0 < C::NBUF - 1; ++t0)
+    if (t0 < nt) issue(t0);
+
+  f32x16_t o[C::DT];
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  for (int t = 0; t < nt; ++t) {
+    wait_newer<C::PER_TILE, C::NBUF - 2>(min(nt - 1 - t, C::NBUF - 2));
+    asm volatile("" ::: "memory");
+    // the buffer refilled here held tile t - 1, whose reads have all returned
+    if (t + C::NBUF - 1 < nt) issue(t + C::NBUF - 1);
+    const uint16_t* Ks = smem + (t % C::NBUF) * C::STAGE;
+    const uint16_t* Vs = Ks + C::KT * D;
+
+    // S^T[key][query]: element i is key 8 (i / 4) + 4 g + i % 4 of this lane's query row
+    f32x16_t s;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = 0.f;
+#pragma unroll
+    for (int ds = 0; ds < C::DS; ++ds) {
+      const int ch = 2 * ds + g;
+      const u32x4 kf = *(const u32x4*)(Ks + lr * D + ((ch ^ swz_key<D>(lr)) << 3));
+      s = mfma32(kf, qh[ds], s);
+      s = mfma32(kf, ql[ds], s);
+    }
+    const int valid = nkeys - C::KT * t;   // keys of this tile inside the chunk
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = 8 * (i >> 2) + 4 * g + (i & 3);
+      s[i] = key < valid ? s[i] * scale : -INFINITY;
+      mx = fmaxf(mx, s[i]);
+    }
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = expf(m_run - m_new);   // 0 on the first tile
+    float ps = 0.f;
+    uint16_t ph[16], pl[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float pv = expf(s[i] - m_new);
+      ps += pv;
+      split_bf16(pv, ph[i], pl[i]);
+    }
+    ps += shfl_xor(ps, 32);
+    l_run = l_run * alpha + ps;
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+
+    // O^T[dd][query] += V^T P^T over the tile's keys in two k-steps; k-step ks
+    // takes this lane group's keys 16 ks + 4 g + (0..3) and 16 ks + 8 + 4 g + (0..3),
+    // which are the P values it holds (i = 8 ks .. 8 ks + 7)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x4 pfh = u32x4{pack2(ph[8 * ks], ph[8 * ks + 1]), pack2(ph[8 * ks + 2], ph[8 * ks + 3]),
+                              pack2(ph[8 * ks + 4], ph[8 * ks + 5]), pack2(ph[8 * ks + 6], ph[8 * ks + 7])};
+      const u32x4 pfl = u32x4{pack2(pl[8 * ks], pl[8 * ks + 1]), pack2(pl[8 * ks + 2], pl[8 * ks + 3]),
+                              pack2(pl[8 * ks + 4], pl[8 * ks + 5]), pack2(pl[8 * ks + 6], pl[8 * ks + 7])};
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) {
+        // transposing read: in each block of 16 lanes, source lane s points at
+        // V[kb + s / 4][dd0 + 4 (s % 4) ..]; lane o of the block receives
+        // V[kb + j][dd0 + o], j = 0..3
+        const int blk = lane >> 4, sl = lane & 15;
+        const int dd = 32 * dt + 16 * (blk & 1) + 4 * (sl & 3);
+        const int ch = dd >> 3, half = (dd >> 2) & 1;
+        const int ka = 16 * ks + 4 * (blk >> 1) + (sl >> 2), kb2 = ka + 8;
+        const uint2 va = lds_read_tr16(Vs + ka * D + ((ch ^ swz_val(ka)) << 3) + 4 * half);
+        const uint2 vb = lds_read_tr16(Vs + kb2 * D + ((ch ^ swz_val(kb2)) << 3) + 4 * half);
+        const u32x4 vf = u32x4{va.x, va.y, vb.x, vb.y};
+        o[dt] = mfma32(vf, pfh, o[dt]);
+        o[dt] = mfma32(vf, pfl, o[dt]);
+      }
+    }
+  }
+
+  // partial: O^T element i of tile dt is dd = 32 dt + 8 (i / 4) + 4 g + i % 4 of query qrow
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int dd = 32 * dt + 8 * gq + 4 * g;
+      *(float4*)(po + (size_t)qrow * D + dd) =
+          make_float4(o[dt][4 * gq], o[dt][4 * gq + 1], o[dt][4 * gq + 2], o[dt][4 * gq + 3]);
+    }
+  if (g == 0) {
+    pml[qrow] = m_run;
+    pml[NQP + qrow] = l_run;
+  }
+}
+
 // Merge the chunk partials and the S block keys; o [B * S, Hq * D] as bf16
 // planes (hi at o, lo at o + o_pst).
 // One wave per query row (rows r = 4 blockIdx.y + wave of kv head blockIdx.x);
@@ -351,10 +557,9 @@ int nqp_of(int NQ) {
 }  // namespace
 
 int attn_max_nq(int d, int kv_f32) {
+  if (!kv_f32) return 256;   // per-wave kernel: any number of 32-row query tiles
   auto fits = [&](int rt) -> bool {
-    if (d == 64)
-      return kv_f32 ? AttnCfg_bytes<64, 2>(rt) <= kLdsLimit : AttnCfg_bytes<64, 1>(rt) <= kLdsLimit;
-    return kv_f32 ? AttnCfg_bytes<128, 2>(rt) <= kLdsLimit : AttnCfg_bytes<128, 1>(rt) <= kLdsLimit;
+    return d == 64 ? AttnCfg_bytes<64, 2>(rt) <= kLdsLimit : AttnCfg_bytes<128, 2>(rt) <= kLdsLimit;
   };
   const int rts[5] = {8, 6, 4, 2, 1};
   for (int rt : rts)
@@ -362,7 +567,8 @@ int attn_max_nq(int d, int kv_f32) {
   return 0;
 }
 
-AttnPlan attn_plan(int B, int Hq, int Hkv, int S, int d, int max_ctx, int window, int kv_f32) {
+AttnPlan attn_plan(int B, int Hq, int Hkv, int S, int d, int max_ctx, int window, int kv_f32,
+                   int ctx_rows) {
   AttnPlan p;
   p.B = B;
   p.Hkv = Hkv;
@@ -372,10 +578,26 @@ AttnPlan attn_plan(int B, int Hq, int Hkv, int S, int d, int max_ctx, int window
   p.NQ = S * p.G;
   p.kv_f32 = kv_f32;
   p.window = window;
+  p.nqp = kv_f32 ? nqp_of(p.NQ) : 32 * ((p.NQ + 31) / 32);
   const int eff = (window > 0 && max_ctx > window) ? window : max_ctx;
   if (eff <= 0) {
     p.chunk = KT;
     p.n_chunks = 0;
+    return p;
+  }
+  if (!kv_f32) {
+    // per-wave kernel: about 1536 waves over the context rows actually present
+    // (ctx_rows / B per sequence on average), at least four 32-key tiles each,
+    // at most 256 chunks per sequence for the combine
+    const long keys = (long)(ctx_rows > 0 ? ctx_rows : (long)B * eff);
+    const long tiles = keys * Hkv * (p.nqp / 32);
+    long per = (tiles + 1536L * 32 - 1) / (1536L * 32);
+    if (per < 4) per = 4;
+    int chunk = (int)(32 * per);
+    const int min_chunk = ((eff + 255) / 256 + 31) / 32 * 32;
+    if (chunk < min_chunk) chunk = min_chunk;
+    p.chunk = chunk;
+    p.n_chunks = (eff + chunk - 1) / chunk;
     return p;
   }
   const int pairs = B * Hkv;
@@ -393,28 +615,43 @@ AttnPlan attn_plan(int B, int Hq, int Hkv, int S, int d, int max_ctx, int window
 }
 
 size_t attn_ws_bytes(const AttnPlan& p) {
-  const size_t nqp = nqp_of(p.NQ);
+  const size_t nqp = p.nqp;
   const size_t slots = (size_t)p.B * p.Hkv * (p.n_chunks > 0 ? p.n_chunks : 1);
   return slots * nqp * p.d * 4 + slots * 2 * nqp * 4 + 256;
+}
+
+template <int D>
+hipError_t launch_wave(const AttnPlan& p, const float* q, const void* ck, const void* cv,
+                       const int32_t* cu, int ctx_rows, float* po, float* pml, float scale,
+                       hipStream_t s) {
+  typedef WaveAttn<D> C;
+  hipError_t e = hipFuncSetAttribute((const void*)attn_wave_kernel<D>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES);
+  if (e != hipSuccess) return e;
+  dim3 grid(p.n_chunks, p.Hkv * (p.nqp / 32), p.B);
+  hipLaunchKernelGGL(attn_wave_kernel<D>, grid, dim3(64), C::LDS_BYTES, s, q, (const uint16_t*)ck,
+                     (const uint16_t*)cv, cu, ctx_rows, p.Hkv, p.NQ, p.nqp, p.chunk, p.n_chunks,
+                     p.window, scale, po, pml);
+  return hipGetLastError();
 }
 
 hipError_t attention(const AttnPlan& p, const float* q, const float* kb, const float* vb,
                      const void* ctx_k, const void* ctx_v, const int32_t* cu_ctx, int ctx_rows,
                      float* ws, uint16_t* o, hipStream_t s) {
-  const int nqp = nqp_of(p.NQ);
+  const int nqp = p.nqp;
   const size_t slots = (size_t)p.B * p.Hkv * (p.n_chunks > 0 ? p.n_chunks : 1);
   float* po = ws;
   float* pml = ws + slots * nqp * p.d;
   const float scale = (float)(1.0 / sqrt((double)p.d));
   hipError_t e = hipSuccess;
-  if (p.n_chunks > 0) {
+  if (p.n_chunks > 0 && !p.kv_f32) {
+    e = p.d == 64 ? launch_wave<64>(p, q, ctx_k, ctx_v, cu_ctx, ctx_rows, po, pml, scale, s)
+                  : launch_wave<128>(p, q, ctx_k, ctx_v, cu_ctx, ctx_rows, po, pml, scale, s);
+    if (e != hipSuccess) return e;
+  } else if (p.n_chunks > 0) {
     const int cr = ctx_rows;
-    if (p.d == 64)
-      e = p.kv_f32 ? dispatch_rt<64, 2>(p, q, ctx_k, ctx_v, cu_ctx, cr, po, pml, scale, s)
-                   : dispatch_rt<64, 1>(p, q, ctx_k, ctx_v, cu_ctx, cr, po, pml, scale, s);
-    else
-      e = p.kv_f32 ? dispatch_rt<128, 2>(p, q, ctx_k, ctx_v, cu_ctx, cr, po, pml, scale, s)
-                   : dispatch_rt<128, 1>(p, q, ctx_k, ctx_v, cu_ctx, cr, po, pml, scale, s);
+    e = p.d == 64 ? dispatch_rt<64, 2>(p, q, ctx_k, ctx_v, cu_ctx, cr, po, pml, scale, s)
+                  : dispatch_rt<128, 2>(p, q, ctx_k, ctx_v, cu_ctx, cr, po, pml, scale, s);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(attn_combine_kernel, dim3(p.B * p.Hkv, (p.NQ + 3) / 4), dim3(kAttnThreads), 0, s,

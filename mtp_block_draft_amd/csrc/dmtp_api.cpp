@@ -123,7 +123,8 @@ DraftWs draft_ws(const dmtp_draft_desc* d) {
   const int S = d->K - 1 + d->n_anchor;
   const size_t R = (size_t)d->B * S;
   const int qkv_n = (d->Hq + 2 * d->Hkv) * d->d;
-  w.plan = attn_plan(d->B, d->Hq, d->Hkv, S, d->d, d->max_ctx, d->window, d->dtype == DMTP_F32);
+  w.plan = attn_plan(d->B, d->Hq, d->Hkv, S, d->d, d->max_ctx, d->window, d->dtype == DMTP_F32,
+                     d->ctx_rows);
   size_t gemm_max = 0;
   const int wf32 = d->dtype == DMTP_F32;
   auto upd = [&](int M, int N, int K) {

@@ -61,9 +61,11 @@ hipError_t final_norm_mask(const float* X, const float* g, float eps, int B, int
 
 // -------------------------------------------------------------- attention --
 struct AttnPlan {
-  int B, Hkv, G, S, d, NQ, chunk, n_chunks, kv_f32, window;
+  int B, Hkv, G, S, d, NQ, nqp, chunk, n_chunks, kv_f32, window;
 };
-AttnPlan attn_plan(int B, int Hq, int Hkv, int S, int d, int max_ctx, int window, int kv_f32);
+// ctx_rows: total context rows of the batch (sizes the chunks for bf16 K/V).
+AttnPlan attn_plan(int B, int Hq, int Hkv, int S, int d, int max_ctx, int window, int kv_f32,
+                   int ctx_rows);
 // Largest number of query rows per kv head (S * Hq / Hkv) the kernels support.
 int attn_max_nq(int d, int kv_f32);
 size_t attn_ws_bytes(const AttnPlan& p);
