@@ -18,12 +18,19 @@
 // single exchange with lane l ^ 32; O^T += V^T P^T takes the V^T operand from
 // the transposing LDS read (ds_read_b64_tr_b16) and P^T straight from the
 // softmax registers.  The float32 K/V path keeps the workgroup kernel.
+#include <cstdlib>
+
 #include "dma.hpp"
 #include "kernels.hpp"
 
 namespace dmtp {
 
 namespace {
+
+int attn_tune(const char* name, int dflt) {
+  const char* e = getenv(name);
+  return e ? atoi(e) : dflt;
+}
 
 constexpr int kAttnThreads = 256;
 constexpr int KT = 64;  // keys per LDS tile
@@ -245,14 +252,14 @@ __global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(
 }
 
 // ------------------------------------------------------ bf16 K/V, per wave --
-template <int D>
+template <int D, int NBUF_>
 struct WaveAttn {
   static constexpr int KT = 32;                  // keys per tile
   static constexpr int CPR = D / 8;              // 16-byte chunks per key row
   static constexpr int RPI = 64 / CPR;           // key rows per 1 KB copy
   static constexpr int INSTR = KT / RPI;         // copies per operand per tile
   static constexpr int PER_TILE = 2 * INSTR;
-  static constexpr int NBUF = 4;
+  static constexpr int NBUF = NBUF_;
   static constexpr int STAGE = 2 * KT * D;       // bf16 elements: K tile, then V tile
   static constexpr size_t LDS_BYTES = (size_t)NBUF * STAGE * 2;
   static constexpr int DS = D / 16;              // k-steps of Q K^T
@@ -276,13 +283,13 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(uint2, v);
 }
 
-template <int D>
+template <int D, int NBUF>
 __global__ __launch_bounds__(64) void attn_wave_kernel(
     const float* __restrict__ q, const uint16_t* __restrict__ ctx_k,
     const uint16_t* __restrict__ ctx_v, const int32_t* __restrict__ cu_ctx, int ctx_rows, int Hkv,
     int NQ, int NQP, int chunk, int n_chunks, int window, float scale, float* __restrict__ part_o,
     float* __restrict__ part_ml) {
-  typedef WaveAttn<D> C;
+  typedef WaveAttn<D, NBUF> C;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   const int c = blockIdx.x, kvh = blockIdx.y % Hkv, qt = blockIdx.y / Hkv, b = blockIdx.z;
   const int lane = threadIdx.x, lr = lane & 31, g = lane >> 5;
@@ -307,39 +314,54 @@ __global__ __launch_bounds__(64) void attn_wave_kernel(
   // copies: instruction i of a tile moves key rows RPI i .. RPI i + RPI - 1;
   // lane supplies row RPI i + lane / CPR, chunk position lane % CPR
   const size_t row_stride = (size_t)Hkv * D;
-  const size_t seq0 = (size_t)cu_ctx[b];
+  const uint16_t* kbase = ctx_k + ((size_t)cu_ctx[b] + k_lo) * row_stride + (size_t)kvh * D;
+  const uint16_t* vbase = ctx_v + ((size_t)cu_ctx[b] + k_lo) * row_stride + (size_t)kvh * D;
   const int rr = lane / C::CPR, pos = lane % C::CPR;
+  uint32_t koff[C::INSTR], voff[C::INSTR];
+#pragma unroll
+  for (int i = 0; i < C::INSTR; ++i) {
+    const int r = C::RPI * i + rr;
+    koff[i] = (uint32_t)(r * row_stride) + 8 * (pos ^ swz_key<D>(r));
+    voff[i] = (uint32_t)(r * row_stride) + 8 * (pos ^ swz_val(r));
+  }
   auto issue = [&](int t) __attribute__((always_inline)) {
     uint16_t* st = smem + (t % C::NBUF) * C::STAGE;
+    const size_t t0 = (size_t)C::KT * t * row_stride;
+    if (C::KT * (t + 1) <= nkeys) {
 #pragma unroll
-    for (int i = 0; i < C::INSTR; ++i) {
-      const int r = C::RPI * i + rr;
-      const int key = min(k_lo + C::KT * t + r, k_hi - 1);   // rows past the end: masked below
-      const size_t off = (seq0 + key) * row_stride + (size_t)kvh * D;
-      lds_dma16(ctx_k + off + 8 * (pos ^ swz_key<D>(r)), st + i * 512);
-      lds_dma16(ctx_v + off + 8 * (pos ^ swz_val(r)), st + C::KT * D + i * 512);
+      for (int i = 0; i < C::INSTR; ++i) {
+        lds_dma16(kbase + t0 + koff[i], st + i * 512);
+        lds_dma16(vbase + t0 + voff[i], st + C::KT * D + i * 512);
+      }
+    } else {   // last tile: rows past the chunk end repeat its last key (masked below)
+#pragma unroll
+      for (int i = 0; i < C::INSTR; ++i) {
+        const int r = C::RPI * i + rr;
+        const size_t row = (size_t)min(C::KT * t + r, nkeys - 1) * row_stride;
+        lds_dma16(kbase + row + 8 * (pos ^ swz_key<D>(r)), st + i * 512);
+        lds_dma16(vbase + row + 8 * (pos ^ swz_val(r)), st + C::KT * D + i * 512);
+      }
     }
   };
+
   // query fragments (B operand of S^T = K Q^T): column = query row, 8 d values;
   // loaded before the first copies so that waiting for them leaves those in flight
   const float* qg = q + (((size_t)b * Hkv + kvh) * NQ) * D;
   u32x4 qh[C::DS], ql[C::DS];
 #pragma unroll
   for (int ds = 0; ds < C::DS; ++ds) {
-    float v[8];
+    float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
     if (qrow < NQ) {
-      const float4 a = *(const float4*)(qg + (size_t)qrow * D + 16 * ds + 8 * g);
-      const float4 e = *(const float4*)(qg + (size_t)qrow * D + 16 * ds + 8 * g + 4);
-      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = e.x; v[5] = e.y; v[6] = e.z; v[7] = e.w;
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = 0.f;
+      x0 = *(const float4*)(qg + (size_t)qrow * D + 16 * ds + 8 * g);
+      x1 = *(const float4*)(qg + (size_t)qrow * D + 16 * ds + 8 * g + 4);
     }
-    uint16_t h[8], l[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) split_bf16(v[j], h[j], l[j]);
-    qh[ds] = u32x4{pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7])};
-    ql[ds] = u32x4{pack2(l[0], l[1]), pack2(l[2], l[3]), pack2(l[4], l[5]), pack2(l[6], l[7])};
+    uint32_t h[4], l[4];
+    split2(x0.x, x0.y, h[0], l[0]);
+    split2(x0.z, x0.w, h[1], l[1]);
+    split2(x1.x, x1.y, h[2], l[2]);
+    split2(x1.z, x1.w, h[3], l[3]);
+    qh[ds] = u32x4{h[0], h[1], h[2], h[3]};
+    ql[ds] = u32x4{l[0], l[1], l[2], l[3]};
   }
 
 #pragma unroll
@@ -351,74 +373,90 @@ __global__ __launch_bounds__(64) void attn_wave_kernel(
   for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
+  // running max in log2 units (scores times scale / ln 2) and running sum
+  const float scale2 = scale * 1.4426950408889634f;
   float m_run = -INFINITY, l_run = 0.f;
+
+  // per-lane LDS offsets of the fragments (elements within a stage)
+  int k_frag[C::DS];
+#pragma unroll
+  for (int ds = 0; ds < C::DS; ++ds) k_frag[ds] = lr * D + (((2 * ds + g) ^ swz_key<D>(lr)) << 3);
+  // transposing read: in each block of 16 lanes, source lane s points at
+  // V[kb + s / 4][dd0 + 4 (s % 4) ..]; lane o of the block receives
+  // V[kb + j][dd0 + o], j = 0..3
+  const int blk = lane >> 4, sl = lane & 15;
+  int v_frag[2][C::DT][2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) {
+      const int dd = 32 * dt + 16 * (blk & 1) + 4 * (sl & 3);
+      const int ch = dd >> 3, half = (dd >> 2) & 1;
+      const int ka = 16 * ks + 4 * (blk >> 1) + (sl >> 2), kb2 = ka + 8;
+      v_frag[ks][dt][0] = C::KT * D + ka * D + ((ch ^ swz_val(ka)) << 3) + 4 * half;
+      v_frag[ks][dt][1] = C::KT * D + kb2 * D + ((ch ^ swz_val(kb2)) << 3) + 4 * half;
+    }
 
   for (int t = 0; t < nt; ++t) {
     wait_newer<C::PER_TILE, C::NBUF - 2>(min(nt - 1 - t, C::NBUF - 2));
     asm volatile("" ::: "memory");
     // the buffer refilled here held tile t - 1, whose reads have all returned
     if (t + C::NBUF - 1 < nt) issue(t + C::NBUF - 1);
-    const uint16_t* Ks = smem + (t % C::NBUF) * C::STAGE;
-    const uint16_t* Vs = Ks + C::KT * D;
+    const uint16_t* st = smem + (t % C::NBUF) * C::STAGE;
 
-    // S^T[key][query]: element i is key 8 (i / 4) + 4 g + i % 4 of this lane's query row
-    f32x16_t s;
+    // S^T[key][query]: element i is key 8 (i / 4) + 4 g + i % 4 of this lane's
+    // query row; the hi and lo query planes accumulate in separate chains
+    f32x16_t s, s2;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s[i] = 0.f;
+    for (int i = 0; i < 16; ++i) s[i] = s2[i] = 0.f;
 #pragma unroll
     for (int ds = 0; ds < C::DS; ++ds) {
-      const int ch = 2 * ds + g;
-      const u32x4 kf = *(const u32x4*)(Ks + lr * D + ((ch ^ swz_key<D>(lr)) << 3));
+      const u32x4 kf = *(const u32x4*)(st + k_frag[ds]);
       s = mfma32(kf, qh[ds], s);
-      s = mfma32(kf, ql[ds], s);
+      s2 = mfma32(kf, ql[ds], s2);
     }
     const int valid = nkeys - C::KT * t;   // keys of this tile inside the chunk
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int key = 8 * (i >> 2) + 4 * g + (i & 3);
-      s[i] = key < valid ? s[i] * scale : -INFINITY;
+      s[i] = key < valid ? (s[i] + s2[i]) * scale2 : -INFINITY;
       mx = fmaxf(mx, s[i]);
     }
     mx = fmaxf(mx, shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx);
-    const float alpha = expf(m_run - m_new);   // 0 on the first tile
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first tile
     float ps = 0.f;
-    uint16_t ph[16], pl[16];
+    uint32_t ph[8], pl[8];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float pv = expf(s[i] - m_new);
-      ps += pv;
-      split_bf16(pv, ph[i], pl[i]);
+    for (int i = 0; i < 16; i += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(s[i] - m_new);
+      const float p1 = __builtin_amdgcn_exp2f(s[i + 1] - m_new);
+      ps += p0 + p1;
+      split2(p0, p1, ph[i / 2], pl[i / 2]);
     }
     ps += shfl_xor(ps, 32);
     l_run = l_run * alpha + ps;
+    // O is rescaled only when some row's running max rose (alpha < 1)
+    if (__ballot(m_new > m_run) != 0) {
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+    }
     m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
 
     // O^T[dd][query] += V^T P^T over the tile's keys in two k-steps; k-step ks
     // takes this lane group's keys 16 ks + 4 g + (0..3) and 16 ks + 8 + 4 g + (0..3),
     // which are the P values it holds (i = 8 ks .. 8 ks + 7)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const u32x4 pfh = u32x4{pack2(ph[8 * ks], ph[8 * ks + 1]), pack2(ph[8 * ks + 2], ph[8 * ks + 3]),
-                              pack2(ph[8 * ks + 4], ph[8 * ks + 5]), pack2(ph[8 * ks + 6], ph[8 * ks + 7])};
-      const u32x4 pfl = u32x4{pack2(pl[8 * ks], pl[8 * ks + 1]), pack2(pl[8 * ks + 2], pl[8 * ks + 3]),
-                              pack2(pl[8 * ks + 4], pl[8 * ks + 5]), pack2(pl[8 * ks + 6], pl[8 * ks + 7])};
+      const u32x4 pfh = u32x4{ph[4 * ks], ph[4 * ks + 1], ph[4 * ks + 2], ph[4 * ks + 3]};
+      const u32x4 pfl = u32x4{pl[4 * ks], pl[4 * ks + 1], pl[4 * ks + 2], pl[4 * ks + 3]};
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) {
-        // transposing read: in each block of 16 lanes, source lane s points at
-        // V[kb + s / 4][dd0 + 4 (s % 4) ..]; lane o of the block receives
-        // V[kb + j][dd0 + o], j = 0..3
-        const int blk = lane >> 4, sl = lane & 15;
-        const int dd = 32 * dt + 16 * (blk & 1) + 4 * (sl & 3);
-        const int ch = dd >> 3, half = (dd >> 2) & 1;
-        const int ka = 16 * ks + 4 * (blk >> 1) + (sl >> 2), kb2 = ka + 8;
-        const uint2 va = lds_read_tr16(Vs + ka * D + ((ch ^ swz_val(ka)) << 3) + 4 * half);
-        const uint2 vb = lds_read_tr16(Vs + kb2 * D + ((ch ^ swz_val(kb2)) << 3) + 4 * half);
+        const uint2 va = lds_read_tr16(st + v_frag[ks][dt][0]);
+        const uint2 vb = lds_read_tr16(st + v_frag[ks][dt][1]);
         const u32x4 vf = u32x4{va.x, va.y, vb.x, vb.y};
         o[dt] = mfma32(vf, pfh, o[dt]);
         o[dt] = mfma32(vf, pfl, o[dt]);
@@ -436,7 +474,7 @@ __global__ __launch_bounds__(64) void attn_wave_kernel(
           make_float4(o[dt][4 * gq], o[dt][4 * gq + 1], o[dt][4 * gq + 2], o[dt][4 * gq + 3]);
     }
   if (g == 0) {
-    pml[qrow] = m_run;
+    pml[qrow] = m_run * 0.6931471805599453f;   // back to natural units
     pml[NQP + qrow] = l_run;
   }
 }
@@ -498,6 +536,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(
   const size_t orow = ((size_t)b * S + s) * ((size_t)Hkv * G * D) + ((size_t)kvh * G + g) * D;
   for (int k = lane; k < D; k += kWave) {
     float acc = 0.f;
+#pragma unroll 4
     for (int c = 0; c < n_chunks; ++c) {
       // an empty chunk has weight 0 and never wrote its partial O
       const float w = w_chunk[wave][c];
@@ -591,7 +630,8 @@ AttnPlan attn_plan(int B, int Hq, int Hkv, int S, int d, int max_ctx, int window
     // at most 256 chunks per sequence for the combine
     const long keys = (long)(ctx_rows > 0 ? ctx_rows : (long)B * eff);
     const long tiles = keys * Hkv * (p.nqp / 32);
-    long per = (tiles + 1536L * 32 - 1) / (1536L * 32);
+    static const long target = attn_tune("DMTP_ATTN_WAVES", 1536);
+    long per = (tiles + target * 32 - 1) / (target * 32);
     if (per < 4) per = 4;
     int chunk = (int)(32 * per);
     const int min_chunk = ((eff + 255) / 256 + 31) / 32 * 32;
@@ -620,19 +660,29 @@ size_t attn_ws_bytes(const AttnPlan& p) {
   return slots * nqp * p.d * 4 + slots * 2 * nqp * 4 + 256;
 }
 
+template <int D, int NBUF>
+hipError_t launch_wave_n(const AttnPlan& p, const float* q, const void* ck, const void* cv,
+                         const int32_t* cu, int ctx_rows, float* po, float* pml, float scale,
+                         hipStream_t s) {
+  typedef WaveAttn<D, NBUF> C;
+  hipError_t e = hipFuncSetAttribute((const void*)attn_wave_kernel<D, NBUF>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES);
+  if (e != hipSuccess) return e;
+  dim3 grid(p.n_chunks, p.Hkv * (p.nqp / 32), p.B);
+  hipLaunchKernelGGL((attn_wave_kernel<D, NBUF>), grid, dim3(64), C::LDS_BYTES, s, q, (const uint16_t*)ck,
+                     (const uint16_t*)cv, cu, ctx_rows, p.Hkv, p.NQ, p.nqp, p.chunk, p.n_chunks,
+                     p.window, scale, po, pml);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_wave(const AttnPlan& p, const float* q, const void* ck, const void* cv,
                        const int32_t* cu, int ctx_rows, float* po, float* pml, float scale,
                        hipStream_t s) {
-  typedef WaveAttn<D> C;
-  hipError_t e = hipFuncSetAttribute((const void*)attn_wave_kernel<D>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES);
-  if (e != hipSuccess) return e;
-  dim3 grid(p.n_chunks, p.Hkv * (p.nqp / 32), p.B);
-  hipLaunchKernelGGL(attn_wave_kernel<D>, grid, dim3(64), C::LDS_BYTES, s, q, (const uint16_t*)ck,
-                     (const uint16_t*)cv, cu, ctx_rows, p.Hkv, p.NQ, p.nqp, p.chunk, p.n_chunks,
-                     p.window, scale, po, pml);
-  return hipGetLastError();
+  static const int nbuf = attn_tune("DMTP_ATTN_NBUF", 2);
+  if (nbuf == 2) return launch_wave_n<D, 2>(p, q, ck, cv, cu, ctx_rows, po, pml, scale, s);
+  if (nbuf == 3) return launch_wave_n<D, 3>(p, q, ck, cv, cu, ctx_rows, po, pml, scale, s);
+  return launch_wave_n<D, 4>(p, q, ck, cv, cu, ctx_rows, po, pml, scale, s);
 }
 
 hipError_t attention(const AttnPlan& p, const float* q, const float* kb, const float* vb,

@@ -35,6 +35,18 @@ __device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) 
   lo = f32_to_bf16(x - bf16_to_f32(hi));
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two-plane split of two floats with the hardware round-to-nearest-even
+// conversion (v_cvt_pk_bf16_f32): hi2 packs bf16(a), bf16(b); lo2 packs the
+// bf16 of the remainders.  Same values as split_bf16 for finite inputs.
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi2, uint32_t& lo2) {
+  const bf16x2_t h = {(__bf16)a, (__bf16)b};
+  hi2 = __builtin_bit_cast(uint32_t, h);
+  const bf16x2_t l = {(__bf16)(a - (float)h[0]), (__bf16)(b - (float)h[1])};
+  lo2 = __builtin_bit_cast(uint32_t, l);
+}
+
 // Element i of a float32 activation stored as its two bf16 planes: the hi
 // plane at p, the lo plane at p + pst.
 __device__ __forceinline__ void store_planes(uint16_t* p, size_t pst, size_t i, float v) {

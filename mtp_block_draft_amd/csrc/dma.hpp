@@ -23,9 +23,11 @@ __device__ __forceinline__ f32x16_t mfma32(const u32x4& a, const u32x4& b, f32x1
 // distinct banks.
 __device__ __forceinline__ int swz_k32(int r, int c) { return r * 32 + ((c ^ ((r >> 2) & 3)) << 3); }
 
-// Copy 16 bytes per lane from src to LDS at dst + 16 * lane.
+// Copy 16 bytes per lane from src to LDS at dst + 16 * lane.  AUX is the
+// cache-policy field of the instruction (2: non-temporal, for data read once).
+template <int AUX = 0>
 __device__ __forceinline__ void lds_dma16(const void* src, uint16_t* dst) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, AUX);
 }
 
 // Wait until at most N vector-memory operations of this wave are outstanding

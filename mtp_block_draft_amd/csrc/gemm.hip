@@ -216,32 +216,34 @@ __global__ void splitk_reduce4(const float* __restrict__ part, int splits, int M
 
 typedef DmaTile<1, 1, 4> DmaM32;    // 128 x 32
 typedef DmaTile<2, 2, 2> DmaM128;   // 128 x 128
-typedef DmaTile<2, 4, 2> DmaM256;   // 128 x 256
 
 struct DmaPlan {
-  int cfg;   // 0: DmaM32, 1: DmaM128, 2: DmaM256
+  int cfg;   // 0: DmaM32, 1: DmaM128
   int tn, tm, splits;
 };
 
+// Tile and split-K choice.  Measured on the drafter shapes (M = 256 slot rows,
+// N and K of 2048 .. 6144): 128 x 128 tiles with about 192 workgroups in total
+// beat larger tiles and a full wave of 256 (fewer float32 partials to write
+// and re-read); the 32 fused rows take the 128 x 32 tile.
 DmaPlan dma_plan(int M, int N, int K) {
   DmaPlan pl;
-  int BM;
+  int BM, target;
   if (M <= 32) {
     pl.cfg = 0;
     BM = DmaM32::BM;
-  } else if (M <= 128) {
+    target = 256;
+  } else {
     pl.cfg = 1;
     BM = DmaM128::BM;
-  } else {
-    pl.cfg = 2;
-    BM = DmaM256::BM;
+    target = 192;
   }
   pl.tn = (N + 127) / 128;
   pl.tm = (M + BM - 1) / BM;
   const int tiles = pl.tn * pl.tm;
   const int nK = K / 32;
-  // about one workgroup per CU, each split at least four k-slices long
-  int sp = (256 + tiles - 1) / tiles;
+  // each split at least four k-slices long
+  int sp = (target + tiles / 2) / tiles;
   if (sp > nK / 4) sp = nK / 4;
   pl.splits = sp < 1 ? 1 : sp;
   return pl;
@@ -302,9 +304,7 @@ hipError_t gemm(const GemmArgs& a, float* ws, hipStream_t s) {
     if (!dma_ok(a)) return hipErrorInvalidValue;
     const DmaPlan pl = dma_plan(a.M, a.N, a.K);
     p.splits = pl.splits;
-    hipError_t e = pl.cfg == 0   ? launch_dma<DmaM32>(p, pl, s)
-                   : pl.cfg == 1 ? launch_dma<DmaM128>(p, pl, s)
-                                 : launch_dma<DmaM256>(p, pl, s);
+    hipError_t e = pl.cfg == 0 ? launch_dma<DmaM32>(p, pl, s) : launch_dma<DmaM128>(p, pl, s);
     if (e != hipSuccess || pl.splits == 1) return e;
     const size_t total4 = (size_t)a.M * a.N / 4;
     const int blocks = (int)((total4 + 255) / 256 < 4096 ? (total4 + 255) / 256 : 4096);
