@@ -38,6 +38,101 @@ def _workload_desc(cfg) -> str:
             f"tau={cfg.tau_mode}")
 
 
+# Sources the LM-head GEMM is compiled from; a counter summary taken on other
+# sources is stale and its traffic figure is not reported.
+HEAD_SOURCES = ("mtp_block_draft_amd/csrc/lm_head.hip", "mtp_block_draft_amd/csrc/dma.hpp",
+                "mtp_block_draft_amd/csrc/common.hpp", "mtp_block_draft_amd/csrc/gemm_core.hpp")
+TRAFFIC_SUMMARY = "profiles/lm_head_gemm_b32_448rows_counters.md"
+
+
+def head_fingerprint() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in HEAD_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the LM-head GEMM from the committed counter summary,
+    or None when there is none or it was taken on different kernel sources."""
+    path = os.path.join(ROOT, TRAFFIC_SUMMARY)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and line.startswith("- "):
+                k, v = line[2:].split(":", 1)
+                vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_fingerprint") != head_fingerprint():
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def rocprof_summary(args) -> int:
+    """Print markdown summary lines from rocprofv3 CSV output (kernel stats, or
+    FETCH_SIZE / WRITE_SIZE counter collections with the copy-probe calibration)."""
+    import csv
+    import re
+
+    def short(name):
+        n = re.sub(r"\(anonymous namespace\)::|dmtp::", "", name)
+        return re.sub(r"\(.*", "", n)
+
+    if args.stats:
+        rows = list(csv.DictReader(open(args.stats)))
+        print("| kernel | calls | avg us | min us | max us | share |")
+        print("|---|---|---|---|---|---|")
+        for r in rows[:args.top]:
+            print(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                  f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                  f"{float(r['Percentage']):.1f}% |")
+        return 0
+
+    def per_kernel(path, counter):
+        out = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            out.setdefault((short(r["Kernel_Name"]), int(r["Grid_Size"])), []).append(
+                float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in out.items()}
+
+    fetch = per_kernel(args.fetch, "FETCH_SIZE")
+    write = per_kernel(args.write, "WRITE_SIZE")
+    copy_bytes = args.copy_mib * 2 ** 20
+
+    def pick(d, pat):
+        cands = [(k, v) for k, v in d.items() if pat in k[0]]
+        if not cands:
+            raise SystemExit(f"no kernel matching {pat!r}")
+        return max(cands, key=lambda kv: kv[1])
+
+    (_, cf) = pick(fetch, args.copy_kernel)
+    (_, cw) = pick(write, args.copy_kernel)
+    f_scale = copy_bytes / (cf * 1024)
+    w_scale = copy_bytes / (cw * 1024)
+    (kk, kf) = pick(fetch, args.kernel)
+    kw = write.get(kk, 0.0)
+    traffic = kf * 1024 * f_scale + kw * 1024 * w_scale
+    print(f"- kernel: `{kk[0]}` (grid {kk[1]})")
+    print(f"- kernel_fingerprint: `{head_fingerprint()}`")
+    print(f"- fetch_kib_per_launch: {kf:.1f}")
+    print(f"- write_kib_per_launch: {kw:.1f}")
+    print(f"- copy_probe_bytes: {copy_bytes}")
+    print(f"- copy_probe_fetch_kib: {cf:.1f}")
+    print(f"- copy_probe_write_kib: {cw:.1f}")
+    print(f"- fetch_scale: {f_scale:.4f}")
+    print(f"- write_scale: {w_scale:.4f}")
+    print(f"- traffic_bytes_per_launch: {traffic:.0f}")
+    return 0
+
+
 def cpu_baseline(inp, n_seq: int):
     from threadpoolctl import threadpool_info
     from oracle import dmtp as odm
@@ -62,7 +157,22 @@ def main() -> int:
     ap.add_argument("--config", default="b32_greedy_bf16")
     ap.add_argument("--cpu-seqs", type=int, default=8, help="sequences in the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="before warm-up, copy this many MiB device-to-device once (a kernel "
+                         "of known traffic, for calibrating FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--rocprof-summary", action="store_true",
+                    help="summarise rocprofv3 CSV output instead of running (see --stats, "
+                         "--fetch, --write)")
+    ap.add_argument("--stats", help="rocprofv3 kernel_stats.csv")
+    ap.add_argument("--top", type=int, default=20)
+    ap.add_argument("--fetch", help="counter_collection.csv of a FETCH_SIZE pass")
+    ap.add_argument("--write", help="counter_collection.csv of a WRITE_SIZE pass")
+    ap.add_argument("--kernel", default="head_gemm_mf32_kernel<7>")
+    ap.add_argument("--copy-kernel", default="elementwise")
+    ap.add_argument("--copy-mib", type=int, default=1024)
     args = ap.parse_args()
+    if args.rocprof_summary:
+        return rocprof_summary(args)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); the round is "
               "data-parallel over sequences and is not sharded here", file=sys.stderr)
@@ -91,6 +201,15 @@ def main() -> int:
                 evs[i][1].record(stream)
             if st != 0:
                 raise RuntimeError(f"call {i} failed with status {st}")
+
+    if args.copy_probe_mib:
+        # one elementwise kernel that reads and writes exactly N MiB
+        src = torch.ones((args.copy_probe_mib << 20) // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         one_round()
@@ -121,9 +240,12 @@ def main() -> int:
     head_us = per_call_us[4]
     achieved = flops / (head_us * 1e-6) / 1e12
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    traffic = recorded_traffic() if args.config == "b32_greedy_bf16" else None
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": None,
-                "kernel": f"dmtp_lm_head over {M} rows (prep + GEMM with fused row statistics + merge)",
+                "frac": round(achieved / peak, 4),
+                "traffic": None if traffic is None else round(traffic),
+                "kernel": f"dmtp_lm_head over {M} rows: the bf16 GEMM with fused row statistics "
+                          f"(head_gemm_mf32_kernel) plus its cross-tile merge",
                 "algorithmic_flops": flops, "algorithmic_bytes": w_bytes + M * cfg.H * 2,
                 "avg_us": round(head_us, 2)}
 

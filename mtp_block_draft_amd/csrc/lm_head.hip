@@ -64,7 +64,7 @@ struct HeadParams {
   int logits_rows;
   void* prepared;        // [M, H] head input
   const void* A;         // rows the GEMM reads: prepared, or the single input segment
-  RowStat* part;         // [n_vtiles, M]
+  RowStat* part;         // [M, n_vtiles]
   int n_vtiles;
   int32_t* amax;         // [M]
   float* gap_greedy;     // [M]
@@ -174,7 +174,7 @@ __global__ __launch_bounds__(T::THREADS) void head_gemm_kernel(HeadParams p) {
     const float it = inv_temp(p.temperature, row);
     RowStat st = wstat[0][lr];
     for (int w = 1; w < T::WAVES_N; ++w) st = stat_merge(st, wstat[w][lr], it);
-    p.part[(size_t)blockIdx.x * p.M + row] = st;
+    p.part[(size_t)row * p.n_vtiles + blockIdx.x] = st;
   }
 }
 
@@ -354,7 +354,7 @@ void head_gemm_big_kernel(HeadParams p, int n_mchunks) {
     o.idx = shfl_xor(st.idx, 32);
     o.v2 = shfl_xor(st.v2, 32);
     st = stat_merge(st, o, it);
-    if (lk == 0 && m_ok) p.part[(size_t)vt * M + m] = st;
+    if (lk == 0 && m_ok) p.part[(size_t)m * p.n_vtiles + vt] = st;
   }
 }
 
@@ -465,7 +465,7 @@ __global__ __launch_bounds__(256) void head_gemm_skinny_kernel(HeadParams p) {
     o.idx = shfl_xor(st.idx, 32);
     o.v2 = shfl_xor(st.v2, 32);
     st = stat_merge(st, o, it);
-    if (lk == 0 && m_ok) p.part[(size_t)vt * M + m] = st;
+    if (lk == 0 && m_ok) p.part[(size_t)m * p.n_vtiles + vt] = st;
   }
 }
 
@@ -639,7 +639,7 @@ void head_gemm_lds_kernel(HeadParams p, int n_mchunks) {
       o.v2 = shfl_xor(st.v2, mask);
       st = stat_merge(st, o, it);
     }
-    if (fq == 0 && m_ok) p.part[(size_t)vt * M + m] = st;
+    if (fq == 0 && m_ok) p.part[(size_t)m * p.n_vtiles + vt] = st;
   }
 }
 
@@ -847,7 +847,7 @@ void head_gemm_mf32_kernel(HeadParams p, int n_mchunks) {
     const int m = m0 + r;
     if (m >= M) continue;
     const float it = inv_temp(p.temperature, m);
-    p.part[(size_t)vt * M + m] = stat_merge(xch[r], xch[C::BB + r], it);
+    p.part[(size_t)m * p.n_vtiles + vt] = stat_merge(xch[r], xch[C::BB + r], it);
   }
 }
 
@@ -941,7 +941,7 @@ __global__ __launch_bounds__(kMergeThreads) void head_merge_kernel(HeadParams p,
   const float it = inv_temp(p.temperature, m);
   RowStat st = stat_empty();
   for (int t = threadIdx.x; t < p.n_vtiles; t += blockDim.x)
-    st = stat_merge(st, p.part[(size_t)t * p.M + m], it);
+    st = stat_merge(st, p.part[(size_t)m * p.n_vtiles + t], it);
 #pragma unroll
   for (int mask = 1; mask < kWave; mask <<= 1) {
     RowStat o;
