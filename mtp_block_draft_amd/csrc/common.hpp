@@ -128,6 +128,34 @@ __device__ __forceinline__ float gumbel_of_word(uint32_t x) {
   return -logf(e);
 }
 
+// Base-2 logarithm and exponential of the hardware transcendental unit
+// (v_log_f32 / v_exp_f32, about one ulp for normal arguments).
+__device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// gumbel_of_word with the hardware logarithm (absolute error below 1e-5 over
+// the whole range).  1 - t is formed from the integer 2^32 - 1 - x, so it keeps
+// full relative precision near t = 1; for t < 2^-7, E = -log(1 - t) is taken
+// from its series t + t^2/2 + t^3/3 + t^4/4 (truncation below 2^-30 relative).
+__device__ __forceinline__ float gumbel_fast(uint32_t x) {
+  const float ln2 = 0.6931471805599453f;
+  const float t = fmaf((float)x, 0x1p-32f, 0x1p-33f);
+  const float om = fmaf((float)(0xFFFFFFFFu - x), 0x1p-32f, 0x1p-33f);
+  const float e_series = t * fmaf(t, fmaf(t, fmaf(t, 0.25f, 0.33333334f), 0.5f), 1.f);
+  const float e = t < 0x1p-7f ? e_series : -hw_log2(om) * ln2;
+  return -hw_log2(e) * ln2;
+}
+
+// log(1 - e^d) for d <= 0 with the hardware log/exp (absolute error about
+// 1e-6): 1 - e^d from the series of -expm1(d) when |d| < 2^-6, where the
+// subtraction would cancel, directly otherwise.
+__device__ __forceinline__ float log1m_exp(float d) {
+  const float ln2 = 0.6931471805599453f, log2e = 1.4426950408889634f;
+  const float em = -d * fmaf(d, fmaf(d, fmaf(d, 1.f / 24.f, 1.f / 6.f), 0.5f), 1.f);
+  const float om = d > -0x1p-6f ? em : 1.f - hw_exp2(d * log2e);
+  return hw_log2(om) * ln2;
+}
+
 // The eight 32-bit words of block (j >> 3) of draw (seed, key).
 __device__ __forceinline__ void philox_words8(uint64_t seed, uint64_t key, uint64_t block,
                                               uint32_t w[8]) {

@@ -36,8 +36,9 @@ __device__ __forceinline__ RowStat stat_merge(const RowStat& a, const RowStat& b
   r.m = t.v1;
   r.idx = t.i1;
   r.v2 = t.v2;
-  const float wa = a.s > 0.f ? a.s * expf((a.m - r.m) * inv_t) : 0.f;
-  const float wb = b.s > 0.f ? b.s * expf((b.m - r.m) * inv_t) : 0.f;
+  const float sc = inv_t * 1.4426950408889634f;
+  const float wa = a.s > 0.f ? a.s * hw_exp2((a.m - r.m) * sc) : 0.f;
+  const float wb = b.s > 0.f ? b.s * hw_exp2((b.m - r.m) * sc) : 0.f;
   r.s = wa + wb;
   return r;
 }
@@ -821,7 +822,7 @@ void head_gemm_mf32_kernel(HeadParams p, int n_mchunks) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int v = v0 + 64 * vh + 32 * u + 8 * (i >> 2) + 4 * lk + (i & 3);
-        if (v < V) sum += exp2f((acc[u][t][i] - v1) * sc);
+        if (v < V) sum += hw_exp2((acc[u][t][i] - v1) * sc);
       }
     if (srow >= 0) {
       float* dst = p.logits + (size_t)srow * V;
@@ -1019,10 +1020,18 @@ __global__ __launch_bounds__(kScanThreads) void head_scan_kernel(HeadParams p) {
     if (j0 < p.V) {
       uint32_t w[8];
       philox_words8(p.seed, p.draw_key[m], (uint64_t)(j0 >> 3), w);
+      float l[8];
+      if (j0 + 8 <= p.V && (p.V & 3) == 0) {
+        const float4 a = *(const float4*)(lr + j0), b = *(const float4*)(lr + j0 + 4);
+        l[0] = a.x; l[1] = a.y; l[2] = a.z; l[3] = a.w; l[4] = b.x; l[5] = b.y; l[6] = b.z; l[7] = b.w;
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) l[k] = j0 + k < p.V ? lr[j0 + k] : 0.f;
+      }
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int j = j0 + k;
-        if (j < p.V) top2_push(t, lr[j] * it + gumbel_of_word(w[k]), j);
+        if (j < p.V) top2_push(t, l[k] * it + gumbel_fast(w[k]), j);
       }
     }
 #pragma unroll
@@ -1037,8 +1046,10 @@ __global__ __launch_bounds__(kScanThreads) void head_scan_kernel(HeadParams p) {
   }
 }
 
-__global__ void head_finalize_kernel(HeadParams p) {
-  const int m = blockIdx.x * blockDim.x + threadIdx.x;
+// One wave per row: the chunk maxima of a drawn row are merged across lanes.
+__global__ __launch_bounds__(256) void head_finalize_kernel(HeadParams p) {
+  const int m = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
   if (m >= p.M) return;
   int tok = p.amax[m];
   float g = p.gap_greedy[m];
@@ -1052,13 +1063,17 @@ __global__ void head_finalize_kernel(HeadParams p) {
       g = 0.f;
     } else {
       Top2 t = top2_empty();
-      for (int c = 0; c < p.n_chunks; ++c) t = top2_merge(t, p.scan_part[(size_t)li * p.n_chunks + c]);
+      for (int c = lane; c < p.n_chunks; c += kWave) t = top2_merge(t, p.scan_part[(size_t)li * p.n_chunks + c]);
+#pragma unroll
+      for (int mask = 1; mask < kWave; mask <<= 1) t = top2_merge(t, top2_shfl_xor(t, mask));
       tok = t.i1;
       g = t.v1 - t.v2;
     }
   }
-  p.token[m] = tok;
-  if (p.gap) p.gap[m] = g;
+  if (lane == 0) {
+    p.token[m] = tok;
+    if (p.gap) p.gap[m] = g;
+  }
 }
 
 typedef GemmTile<64, 64, 32, 32, 2, 2> HeadTileF32;
@@ -1176,7 +1191,7 @@ hipError_t lm_head_run(const dmtp_head_desc& d, int M, void* ws, hipStream_t s) 
     hipLaunchKernelGGL(head_scan_kernel, dim3(2048), dim3(kScanThreads), 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(head_finalize_kernel, dim3((M + 255) / 256), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(head_finalize_kernel, dim3((M + 3) / 4), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

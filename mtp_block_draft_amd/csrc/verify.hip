@@ -137,12 +137,12 @@ __global__ __launch_bounds__(kScanThreads) void verify_scan_kernel(VerifyParams 
       for (int k = 0; k < 8; ++k) {
         const int j = j0 + k;
         if (j >= V) break;
-        const float g = gumbel_of_word(w[k]);
+        const float g = gumbel_fast(w[k]);
         const float a = pr[j] * it - lse_p;          // log p_j
         top2_push(tp, a + g, j);
         if (md == 1) {
           const float c = qr[j] * it - lse_q;        // log q_j
-          const float s = a > c ? a + log1pf(-expf(c - a)) : -INFINITY;   // log(p_j - q_j)
+          const float s = a > c ? a + log1m_exp(c - a) : -INFINITY;   // log(p_j - q_j)
           top2_push(tr, s + g, j);
         }
       }
@@ -169,19 +169,26 @@ __global__ __launch_bounds__(kScanThreads) void verify_scan_kernel(VerifyParams 
   }
 }
 
-__global__ void verify_final_kernel(VerifyParams p) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+// One wave per row: the chunk maxima of the row's draw are merged across lanes.
+__global__ __launch_bounds__(256) void verify_final_kernel(VerifyParams p) {
+  const int b = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
   if (b >= p.B) return;
   const int li = p.list_pos[b];
   if (li < 0) return;
   Top2 tr = top2_empty(), tp = top2_empty();
-  for (int c = 0; c < p.n_chunks; ++c) {
+  for (int c = lane; c < p.n_chunks; c += kWave) {
     tr = top2_merge(tr, p.part[((size_t)li * p.n_chunks + c) * 2 + 0]);
     tp = top2_merge(tp, p.part[((size_t)li * p.n_chunks + c) * 2 + 1]);
   }
+#pragma unroll
+  for (int mask = 1; mask < kWave; mask <<= 1) {
+    tr = top2_merge(tr, top2_shfl_xor(tr, mask));
+    tp = top2_merge(tp, top2_shfl_xor(tp, mask));
+  }
   // residual mode with no positive residual falls back to p
   const int y = (p.mode[b] == 1 && tr.v1 > -INFINITY) ? tr.i1 : tp.i1;
-  p.out_tokens[(size_t)b * (p.K + 1) + p.accept_len[b]] = y;
+  if (lane == 0) p.out_tokens[(size_t)b * (p.K + 1) + p.accept_len[b]] = y;
 }
 
 struct WsL {
@@ -241,7 +248,7 @@ hipError_t verify_run(const dmtp_verify_desc& d, void* ws, hipStream_t s) {
   if (e != hipSuccess || !d.temperature) return e;
   hipLaunchKernelGGL(verify_scan_kernel, dim3(2048), dim3(kScanThreads), 0, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(verify_final_kernel, dim3((d.B + 255) / 256), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(verify_final_kernel, dim3((d.B + 3) / 4), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
