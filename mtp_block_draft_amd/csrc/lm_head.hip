@@ -669,21 +669,42 @@ hipError_t launch_head_lds(const HeadParams& p, int n_mchunks, hipStream_t s) {
 // nor the barrier sits on the matrix-core critical path.  16-byte chunks are
 // XOR-swizzled with (row >> 2) & 3, which keeps the 16 lanes of a read pass on
 // distinct banks.  The two vocabulary halves' row statistics meet in LDS.
-template <int TB>
+// Ring depth: as many stages as fit 144 KB of LDS (at most 12), so that the
+// weight-streaming calls with few rows keep enough copies in flight.
+// Ring depth: as many stages as fit 144 KB of LDS (at most 12).
+constexpr int head_mf32_nbuf(int TB, int BK) {
+  return (147456 / ((128 + 64 * TB) * BK * 2)) > 12 ? 12 : (147456 / ((128 + 64 * TB) * BK * 2));
+}
+
+// Element offset of 16-byte chunk c of row r in a [rows][BK] bf16 tile.  The
+// XOR keeps the 16 rows of one LDS read pass on distinct 16-byte positions of
+// the 256-byte bank window: (r >> 2) & 3 for 64-byte rows, (r >> 1) & 7 for
+// 128-byte rows.
+template <int BK>
+__device__ __forceinline__ int swz_row(int r, int c) {
+  if constexpr (BK == 32) return r * 32 + ((c ^ ((r >> 2) & 3)) << 3);
+  else return r * 64 + ((c ^ ((r >> 1) & 7)) << 3);
+}
+
+template <int TB, int BK_ = 32, int NBUF_ = head_mf32_nbuf(TB, BK_)>
 struct HeadMf32 {
-  static constexpr int BV = 128, BK = 32, NBUF = 4, THREADS = 256;
+  static constexpr int BV = 128, BK = BK_, NBUF = NBUF_, THREADS = 256;
   static constexpr int BB = 64 * TB;
-  static constexpr int W_INSTR = BV * BK / 8 / 64;   // 8
-  static constexpr int X_INSTR = BB * BK / 8 / 64;   // 4 TB
-  static constexpr int PER_WAVE = (W_INSTR + X_INSTR) / 4;
+  static constexpr int CPR = BK / 8;                  // 16-byte chunks per row
+  static constexpr int KS = BK / 16;                  // MFMA k-steps per slice
+  static constexpr int W_INSTR = BV * BK * 2 / 1024;  // 1 KB copies per slice
+  static constexpr int X_INSTR = BB * BK * 2 / 1024;
+  static constexpr int WPW = W_INSTR / 4, XPW = X_INSTR / 4;   // per wave
+  static constexpr int PER_WAVE = WPW + XPW;
   static constexpr int STAGE = (BV + BB) * BK;
   static constexpr size_t LDS_BYTES = (size_t)NBUF * STAGE * 2;
+  static_assert(W_INSTR % 4 == 0 && X_INSTR % 4 == 0 && KS % 2 == 0, "tile");
 };
 
-template <int TB>
+template <int TB, int BK, int NBUF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void head_gemm_mf32_kernel(HeadParams p, int n_mchunks) {
-  typedef HeadMf32<TB> C;
+  typedef HeadMf32<TB, BK, NBUF> C;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   const int total = p.n_vtiles * n_mchunks;
   const int per = (total + 7) / 8;   // XCD-contiguous ranges (workgroup i runs on XCD i % 8)
@@ -698,32 +719,31 @@ void head_gemm_mf32_kernel(HeadParams p, int n_mchunks) {
   const uint16_t* __restrict__ W = (const uint16_t*)p.W;
   const uint16_t* __restrict__ X = (const uint16_t*)p.A;
 
-  const uint16_t* wsrc[2];
+  // lane's source of copy q: row idx / CPR of the tile, the chunk that lands at
+  // position idx % CPR (rows past the end are clamped; their results are unused)
+  auto chunk_of = [](int r, int pos) {
+    return BK == 32 ? (pos ^ ((r >> 2) & 3)) : (pos ^ ((r >> 1) & 7));
+  };
+  const uint16_t* wsrc[C::WPW];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int idx = (wave * 2 + q) * 64 + lane, r = idx >> 2, pos = idx & 3;
-    wsrc[q] = W + (size_t)min(v0 + r, V - 1) * H + 8 * (pos ^ ((r >> 2) & 3));
+  for (int q = 0; q < C::WPW; ++q) {
+    const int idx = (wave * C::WPW + q) * 64 + lane, r = idx / C::CPR;
+    wsrc[q] = W + (size_t)min(v0 + r, V - 1) * H + 8 * chunk_of(r, idx % C::CPR);
   }
-  const uint16_t* xsrc[TB];
+  const uint16_t* xsrc[C::XPW];
 #pragma unroll
-  for (int q = 0; q < TB; ++q) {
-    const int idx = (wave * TB + q) * 64 + lane, r = idx >> 2, pos = idx & 3;
-    xsrc[q] = X + (size_t)min(m0 + r, M - 1) * H + 8 * (pos ^ ((r >> 2) & 3));
+  for (int q = 0; q < C::XPW; ++q) {
+    const int idx = (wave * C::XPW + q) * 64 + lane, r = idx / C::CPR;
+    xsrc[q] = X + (size_t)min(m0 + r, M - 1) * H + 8 * chunk_of(r, idx % C::CPR);
   }
   auto issue = [&](int slice) __attribute__((always_inline)) {
     uint16_t* st = smem + (slice % C::NBUF) * C::STAGE;
     const int k0 = slice * C::BK;
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
-      __builtin_amdgcn_global_load_lds((const void*)(wsrc[q] + k0),
-                                       (__attribute__((address_space(3))) void*)(st + (wave * 2 + q) * 512),
-                                       16, 0, 0);
+    for (int q = 0; q < C::WPW; ++q) lds_dma16(wsrc[q] + k0, st + (wave * C::WPW + q) * 512);
 #pragma unroll
-    for (int q = 0; q < TB; ++q)
-      __builtin_amdgcn_global_load_lds((const void*)(xsrc[q] + k0),
-                                       (__attribute__((address_space(3))) void*)(st + C::BV * C::BK +
-                                                                                  (wave * TB + q) * 512),
-                                       16, 0, 0);
+    for (int q = 0; q < C::XPW; ++q)
+      lds_dma16(xsrc[q] + k0, st + C::BV * C::BK + (wave * C::XPW + q) * 512);
   };
   // fragments of one 16-wide k-step
   struct Frag {
@@ -733,10 +753,10 @@ void head_gemm_mf32_kernel(HeadParams p, int n_mchunks) {
   auto read = [&](Frag& f, int slice, int ks) __attribute__((always_inline)) {
     const uint16_t* st = smem + (slice % C::NBUF) * C::STAGE;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) f.a[u] = *(const u32x4*)(st + swz_k32(64 * vh + 32 * u + lr, 2 * ks + lk));
+    for (int u = 0; u < 2; ++u) f.a[u] = *(const u32x4*)(st + swz_row<BK>(64 * vh + 32 * u + lr, 2 * ks + lk));
 #pragma unroll
     for (int t = 0; t < TB; ++t)
-      f.b[t] = *(const u32x4*)(st + C::BV * C::BK + swz_k32(32 * TB * bh + 32 * t + lr, 2 * ks + lk));
+      f.b[t] = *(const u32x4*)(st + C::BV * C::BK + swz_row<BK>(32 * TB * bh + 32 * t + lr, 2 * ks + lk));
   };
   f32x16_t acc[2][TB];
 #pragma unroll
@@ -756,15 +776,8 @@ void head_gemm_mf32_kernel(HeadParams p, int n_mchunks) {
   // waves passed the barrier.  lgkmcnt(0) first: the buffer that the next DMA
   // refills was read (into registers) just before, by every wave.
   auto wait_slice = [&](int s, int nK) __attribute__((always_inline)) {
-    const int newer = min(nK - 1 - s, C::NBUF - 2);
-    if (newer >= 2)
-      wait_vm_lgkm0<2 * C::PER_WAVE>();
-    else if (newer == 1)
-      wait_vm_lgkm0<C::PER_WAVE>();
-    else
-      wait_vm_lgkm0<0>();
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
+    wait_newer<C::PER_WAVE, C::NBUF - 2>(min(nK - 1 - s, C::NBUF - 2));
+    ring_barrier();
   };
 
   const int nK = H / C::BK;
@@ -775,16 +788,22 @@ void head_gemm_mf32_kernel(HeadParams p, int n_mchunks) {
   wait_slice(0, nK);
   if (C::NBUF - 1 < nK) issue(C::NBUF - 1);
   read(f0, 0, 0);
-  // the next k-step's fragments are read from LDS while this one's MFMAs drain
+  // the next k-step's fragments are read from LDS while this one's MFMAs drain;
+  // the k-steps run in increasing k whatever BK is, so results do not depend on it
   for (int s = 0; s < nK; ++s) {
-    read(f1, s, 1);
-    compute(f0);
-    if (s + 1 < nK) {
-      wait_slice(s + 1, nK);
-      if (s + C::NBUF < nK) issue(s + C::NBUF);
-      read(f0, s + 1, 0);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      Frag& cur = (ks & 1) ? f1 : f0;
+      Frag& nxt = (ks & 1) ? f0 : f1;
+      if (ks + 1 < C::KS) {
+        read(nxt, s, ks + 1);
+      } else if (s + 1 < nK) {
+        wait_slice(s + 1, nK);
+        if (s + C::NBUF < nK) issue(s + C::NBUF);
+        read(nxt, s + 1, 0);
+      }
+      compute(cur);
     }
-    compute(f1);
   }
 
   // ---- epilogue: per input row, 32 logits in the lane; merge the lane pair
@@ -852,31 +871,47 @@ void head_gemm_mf32_kernel(HeadParams p, int n_mchunks) {
   }
 }
 
-template <int TB>
+template <int TB, int BK, int NBUF = head_mf32_nbuf(TB, BK)>
 hipError_t launch_head_mf32(const HeadParams& p, int n_mchunks, hipStream_t s) {
-  typedef HeadMf32<TB> C;
+  typedef HeadMf32<TB, BK, NBUF> C;
   static_assert(C::LDS_BYTES <= 160 * 1024, "head LDS");
-  hipError_t e = hipFuncSetAttribute((const void*)head_gemm_mf32_kernel<TB>,
+  static_assert(C::NBUF >= 2 && C::PER_WAVE * (C::NBUF - 2) < 64, "vmcnt");
+  hipError_t e = hipFuncSetAttribute((const void*)head_gemm_mf32_kernel<TB, BK, NBUF>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES);
   if (e != hipSuccess) return e;
   const int total = p.n_vtiles * n_mchunks;
-  hipLaunchKernelGGL(head_gemm_mf32_kernel<TB>, dim3(8 * ((total + 7) / 8)), dim3(C::THREADS),
-                     C::LDS_BYTES, s, p, n_mchunks);
+  hipLaunchKernelGGL((head_gemm_mf32_kernel<TB, BK, NBUF>), dim3(8 * ((total + 7) / 8)),
+                     dim3(C::THREADS), C::LDS_BYTES, s, p, n_mchunks);
   return hipGetLastError();
 }
 
+int head_tune(const char* name, int dflt) {
+  const char* e = getenv(name);
+  return e ? atoi(e) : dflt;
+}
+
+template <int BK>
+hipError_t launch_head_mf32_bk(const HeadParams& p, int nc, int tb, hipStream_t s) {
+  switch (tb) {
+    case 1: return launch_head_mf32<1, BK>(p, nc, s);
+    case 2: return launch_head_mf32<2, BK>(p, nc, s);
+    case 3: return launch_head_mf32<3, BK>(p, nc, s);
+    case 4: return launch_head_mf32<4, BK>(p, nc, s);
+    case 5: return launch_head_mf32<5, BK>(p, nc, s);
+    case 6: return launch_head_mf32<6, BK>(p, nc, s);
+    default: return launch_head_mf32<7, BK>(p, nc, s);
+  }
+}
+
+// Row chunks of at most 448 rows, split evenly; TB = 64-row tiles per workgroup.
 hipError_t launch_head_mf32_any(const HeadParams& p, hipStream_t s) {
   const int nc = (p.M + 447) / 448;
   const int rows = (p.M + nc - 1) / nc;
-  switch ((rows + 63) / 64) {
-    case 1: return launch_head_mf32<1>(p, nc, s);
-    case 2: return launch_head_mf32<2>(p, nc, s);
-    case 3: return launch_head_mf32<3>(p, nc, s);
-    case 4: return launch_head_mf32<4>(p, nc, s);
-    case 5: return launch_head_mf32<5>(p, nc, s);
-    case 6: return launch_head_mf32<6>(p, nc, s);
-    default: return launch_head_mf32<7>(p, nc, s);
-  }
+  const int tb = (rows + 63) / 64;
+  static const int bk_small = head_tune("DMTP_HEAD_BK_SMALL", 64);
+  static const int bk_big = head_tune("DMTP_HEAD_BK_BIG", 64);
+  const int bk = tb <= 2 ? bk_small : bk_big;
+  return bk == 64 ? launch_head_mf32_bk<64>(p, nc, tb, s) : launch_head_mf32_bk<32>(p, nc, tb, s);
 }
 
 // Row chunks of at most 448 rows, split evenly; T = 16-row tiles per wave.
