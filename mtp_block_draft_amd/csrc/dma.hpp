@@ -18,10 +18,22 @@ __device__ __forceinline__ f32x16_t mfma32(const u32x4& a, const u32x4& b, f32x1
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// Element offset of 16-byte chunk c (0..3) of row r in a [rows][32] bf16 tile.
-// The XOR with (r >> 2) & 3 puts the 16 rows that one LDS read pass touches on
-// distinct banks.
-__device__ __forceinline__ int swz_k32(int r, int c) { return r * 32 + ((c ^ ((r >> 2) & 3)) << 3); }
+// Position of 16-byte chunk c of row r in a [rows][BK] bf16 tile (an
+// involution: it also gives the chunk stored at position c).  The XOR keeps the
+// 16 rows that one LDS read pass touches on distinct 16-byte positions of the
+// 256-byte bank window: (r >> 2) & 3 for 64-byte rows, (r >> 1) & 7 for
+// 128-byte rows.
+template <int BK>
+__device__ __forceinline__ int swz_chunk(int r, int c) {
+  static_assert(BK == 32 || BK == 64, "row width");
+  return BK == 32 ? (c ^ ((r >> 2) & 3)) : (c ^ ((r >> 1) & 7));
+}
+
+// Element offset of 16-byte chunk c of row r in a [rows][BK] bf16 tile.
+template <int BK>
+__device__ __forceinline__ int swz_row(int r, int c) { return r * BK + (swz_chunk<BK>(r, c) << 3); }
+
+__device__ __forceinline__ int swz_k32(int r, int c) { return swz_row<32>(r, c); }
 
 // Copy 16 bytes per lane from src to LDS at dst + 16 * lane.  AUX is the
 // cache-policy field of the instruction (2: non-temporal, for data read once).

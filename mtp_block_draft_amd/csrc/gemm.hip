@@ -37,13 +37,14 @@ struct GemmParams {
 
 // ------------------------------------------------- bf16 weight, LDS ring ----
 // Workgroup of four waves, WAVES_N along N times 4 / WAVES_N along M; wave tile
-// 32 UN (weight rows) x 32 UM (activation rows).  One k-slice of 32 is staged
-// as W [BN][32] and the two activation planes [2][BM][32], bf16, 16-byte chunks
-// swizzled by swz_k32.
-template <int UN_, int UM_, int WAVES_N_>
+// 32 UN (weight rows) x 32 UM (activation rows).  One k-slice of BK is staged
+// as W [BN][BK] and the two activation planes [2][BM][BK], bf16, 16-byte chunks
+// swizzled by swz_row (a 64-wide slice copies whole 128-byte lines).
+template <int UN_, int UM_, int WAVES_N_, int BK_ = 64>
 struct DmaTile {
   static constexpr int UN = UN_, UM = UM_, WAVES_N = WAVES_N_, WAVES_M = 4 / WAVES_N_;
-  static constexpr int BN = 32 * UN * WAVES_N, BM = 32 * UM * WAVES_M, BK = 32;
+  static constexpr int BN = 32 * UN * WAVES_N, BM = 32 * UM * WAVES_M, BK = BK_;
+  static constexpr int CPR = BK / 8, KS = BK / 16;   // 16-byte chunks per row, k-steps per slice
   static constexpr int W_INSTR = BN * BK * 2 / 1024;   // 1 KB copies per slice
   static constexpr int A_INSTR = 2 * BM * BK * 2 / 1024;
   static_assert((W_INSTR + A_INSTR) % 4 == 0 && A_INSTR % 2 == 0, "copies per wave");
@@ -67,7 +68,7 @@ void gemm_dma_kernel(GemmParams p, int n_tiles_n, int n_tiles_m) {
   const int z = t % p.splits;
   const int tile = t / p.splits;
   const int n0 = (tile % n_tiles_n) * T::BN, m0 = (tile / n_tiles_n) * T::BM;
-  const int nK = p.K / T::BK;
+  const int nK = p.K / T::BK;   // K % BK == 0 is checked by the launcher
   const int s_begin = (int)((long)z * nK / p.splits), s_end = (int)((long)(z + 1) * nK / p.splits);
   const int ns = s_end - s_begin;
 
@@ -84,12 +85,13 @@ void gemm_dma_kernel(GemmParams p, int n_tiles_n, int n_tiles_m) {
   for (int q = 0; q < T::PER_WAVE; ++q) {
     const int instr = wave * T::PER_WAVE + q;
     if (instr < T::W_INSTR) {
-      const int idx = instr * 64 + lane, r = idx >> 2, c = (idx & 3) ^ ((r >> 2) & 3);
-      src[q] = W + (size_t)min(n0 + r, p.N - 1) * p.ldb + 8 * c;
+      const int idx = instr * 64 + lane, r = idx / T::CPR;
+      src[q] = W + (size_t)min(n0 + r, p.N - 1) * p.ldb + 8 * swz_chunk<T::BK>(r, idx % T::CPR);
     } else {
       const int j = instr - T::W_INSTR, pl = j / (T::A_INSTR / 2);
-      const int idx = (j % (T::A_INSTR / 2)) * 64 + lane, r = idx >> 2, c = (idx & 3) ^ ((r >> 2) & 3);
-      src[q] = A + pl * p.a_pst + (size_t)min(m0 + r, p.M - 1) * p.lda + 8 * c;
+      const int idx = (j % (T::A_INSTR / 2)) * 64 + lane, r = idx / T::CPR;
+      src[q] = A + pl * p.a_pst + (size_t)min(m0 + r, p.M - 1) * p.lda +
+               8 * swz_chunk<T::BK>(r, idx % T::CPR);
     }
   }
   auto issue = [&](int s) __attribute__((always_inline)) {
@@ -106,13 +108,14 @@ void gemm_dma_kernel(GemmParams p, int n_tiles_n, int n_tiles_m) {
     const uint16_t* st = smem + (s % T::NBUF) * T::STAGE;
     const int c = 2 * ks + lk;
 #pragma unroll
-    for (int u = 0; u < T::UN; ++u) f.w[u] = *(const u32x4*)(st + swz_k32(32 * (T::UN * wn + u) + lr, c));
+    for (int u = 0; u < T::UN; ++u)
+      f.w[u] = *(const u32x4*)(st + swz_row<T::BK>(32 * (T::UN * wn + u) + lr, c));
 #pragma unroll
     for (int pl = 0; pl < 2; ++pl)
 #pragma unroll
       for (int v = 0; v < T::UM; ++v)
         f.a[pl][v] = *(const u32x4*)(st + T::BN * T::BK + pl * T::BM * T::BK +
-                                     swz_k32(32 * (T::UM * wm + v) + lr, c));
+                                     swz_row<T::BK>(32 * (T::UM * wm + v) + lr, c));
   };
   f32x16_t acc[T::UN][T::UM];
 #pragma unroll
@@ -146,14 +149,19 @@ void gemm_dma_kernel(GemmParams p, int n_tiles_n, int n_tiles_m) {
   if (T::NBUF - 1 < ns) issue(T::NBUF - 1);
   read(f0, 0, 0);
   for (int s = 0; s < ns; ++s) {
-    read(f1, s, 1);
-    compute(f0);
-    if (s + 1 < ns) {
-      wait_slice(s + 1);
-      if (s + T::NBUF < ns) issue(s + T::NBUF);
-      read(f0, s + 1, 0);
+#pragma unroll
+    for (int ks = 0; ks < T::KS; ++ks) {
+      Frag& cur = (ks & 1) ? f1 : f0;
+      Frag& nxt = (ks & 1) ? f0 : f1;
+      if (ks + 1 < T::KS) {
+        read(nxt, s, ks + 1);
+      } else if (s + 1 < ns) {
+        wait_slice(s + 1);
+        if (s + T::NBUF < ns) issue(s + T::NBUF);
+        read(nxt, s + 1, 0);
+      }
+      compute(cur);
     }
-    compute(f1);
   }
 
   // element i of acc[u][v]: weight row n = n0 + 32 (UN wn + u) + 8 (i / 4) + 4 lk + i % 4,
@@ -241,7 +249,7 @@ DmaPlan dma_plan(int M, int N, int K) {
   pl.tn = (N + 127) / 128;
   pl.tm = (M + BM - 1) / BM;
   const int tiles = pl.tn * pl.tm;
-  const int nK = K / 32;
+  const int nK = K / 64;
   // each split at least four k-slices long
   int sp = (target + tiles / 2) / tiles;
   if (sp > nK / 4) sp = nK / 4;
@@ -250,7 +258,7 @@ DmaPlan dma_plan(int M, int N, int K) {
 }
 
 bool dma_ok(const GemmArgs& a) {
-  return !a.b_f32 && a.K % 32 == 0 && a.N % 4 == 0 && a.ldc % 4 == 0 && (!a.R || a.ldr % 4 == 0) &&
+  return !a.b_f32 && a.K % 64 == 0 && a.N % 4 == 0 && a.ldc % 4 == 0 && (!a.R || a.ldr % 4 == 0) &&
          a.lda % 8 == 0 && a.ldb % 8 == 0 && a.a_pst % 8 == 0;
 }
 

@@ -676,16 +676,6 @@ constexpr int head_mf32_nbuf(int TB, int BK) {
   return (147456 / ((128 + 64 * TB) * BK * 2)) > 12 ? 12 : (147456 / ((128 + 64 * TB) * BK * 2));
 }
 
-// Element offset of 16-byte chunk c of row r in a [rows][BK] bf16 tile.  The
-// XOR keeps the 16 rows of one LDS read pass on distinct 16-byte positions of
-// the 256-byte bank window: (r >> 2) & 3 for 64-byte rows, (r >> 1) & 7 for
-// 128-byte rows.
-template <int BK>
-__device__ __forceinline__ int swz_row(int r, int c) {
-  if constexpr (BK == 32) return r * 32 + ((c ^ ((r >> 2) & 3)) << 3);
-  else return r * 64 + ((c ^ ((r >> 1) & 7)) << 3);
-}
-
 template <int TB, int BK_ = 32, int NBUF_ = head_mf32_nbuf(TB, BK_)>
 struct HeadMf32 {
   static constexpr int BV = 128, BK = BK_, NBUF = NBUF_, THREADS = 256;
@@ -721,20 +711,17 @@ void head_gemm_mf32_kernel(HeadParams p, int n_mchunks) {
 
   // lane's source of copy q: row idx / CPR of the tile, the chunk that lands at
   // position idx % CPR (rows past the end are clamped; their results are unused)
-  auto chunk_of = [](int r, int pos) {
-    return BK == 32 ? (pos ^ ((r >> 2) & 3)) : (pos ^ ((r >> 1) & 7));
-  };
   const uint16_t* wsrc[C::WPW];
 #pragma unroll
   for (int q = 0; q < C::WPW; ++q) {
     const int idx = (wave * C::WPW + q) * 64 + lane, r = idx / C::CPR;
-    wsrc[q] = W + (size_t)min(v0 + r, V - 1) * H + 8 * chunk_of(r, idx % C::CPR);
+    wsrc[q] = W + (size_t)min(v0 + r, V - 1) * H + 8 * swz_chunk<BK>(r, idx % C::CPR);
   }
   const uint16_t* xsrc[C::XPW];
 #pragma unroll
   for (int q = 0; q < C::XPW; ++q) {
     const int idx = (wave * C::XPW + q) * 64 + lane, r = idx / C::CPR;
-    xsrc[q] = X + (size_t)min(m0 + r, M - 1) * H + 8 * chunk_of(r, idx % C::CPR);
+    xsrc[q] = X + (size_t)min(m0 + r, M - 1) * H + 8 * swz_chunk<BK>(r, idx % C::CPR);
   }
   auto issue = [&](int slice) __attribute__((always_inline)) {
     uint16_t* st = smem + (slice % C::NBUF) * C::STAGE;
