@@ -114,7 +114,7 @@ int validate_draft(const dmtp_draft_desc* d) {
 }
 
 struct DraftWs {
-  size_t X, xh, qkv, q, kb, vb, o, gate, up, act, gemm, attn, total;
+  size_t X, xh, qkv, q, kb, vb, o, gate, up, act, gemm, gemm2, attn, total;
   AttnPlan plan;
 };
 
@@ -147,6 +147,7 @@ DraftWs draft_ws(const dmtp_draft_desc* d) {
   w.up = o; o = al(o + R * d->F * 4);
   w.act = o; o = al(o + R * d->F * 4);
   w.gemm = o; o = al(o + gemm_max);
+  w.gemm2 = o; o = al(o + gemm_max);   // the up projection's partials (live with the gate's)
   w.attn = o; o = al(o + attn_ws_bytes(w.plan));
   w.total = o;
   return w;
@@ -262,39 +263,51 @@ int dmtp_block_draft(const dmtp_draft_desc* d, void* ws, size_t ws_bytes, hipStr
   const int R = d->B * S;
   const int qkv_n = (d->Hq + 2 * d->Hkv) * d->d;
   const int wf32 = d->dtype == DMTP_F32;
+  float* gws2 = (float*)(b + w.gemm2);
+  const size_t pst_h = (size_t)R * d->H, pst_o = (size_t)R * d->Hq * d->d;
+  const int od = d->Hq * d->d;
   hipError_t h = build_slots(*d, X, stream);
+  // RMSNorm of the slots for the first layer; later layers get theirs from the
+  // previous layer's residual update
+  if (h == hipSuccess)
+    h = residual_rmsnorm(split_out_plain(X, (size_t)d->H, R, d->H), X, (size_t)d->H, 0,
+                         d->layers[0].g_attn, d->eps, xh, R, d->H, stream);
   for (int l = 0; l < d->n_layers && h == hipSuccess; ++l) {
     const dmtp_layer& L = d->layers[l];
-    if ((h = rmsnorm_rows(X, L.g_attn, d->eps, xh, R, d->H, stream)) != hipSuccess) break;
-    const size_t pst_h = (size_t)R * d->H, pst_o = (size_t)R * d->Hq * d->d, pst_f = (size_t)R * d->F;
+    SplitOut sq, so, sg, su, sd;
     GemmArgs g1{xh, pst_h, (size_t)d->H, R, L.wqkv, wf32, (size_t)d->H, qkv_n, d->H, qkv,
                 (size_t)qkv_n, nullptr, 0};
-    if ((h = gemm(g1, gws, stream)) != hipSuccess) break;
-    if ((h = rope_split(qkv, d->cu_ctx, d->ctx_rows, d->B, S, d->Hq, d->Hkv, d->d, d->rope_base, q,
-                        kb, vb, stream)) != hipSuccess)
+    if ((h = gemm_deferred(g1, gws, stream, &sq)) != hipSuccess) break;
+    if ((h = rope_split(sq, d->cu_ctx, d->ctx_rows, d->B, S, d->Hq, d->Hkv, d->d, d->rope_base, q, kb,
+                        vb, stream)) != hipSuccess)
       break;
     if ((h = attention(w.plan, q, kb, vb, L.ctx_k, L.ctx_v, d->cu_ctx, d->ctx_rows, aws, o,
                        stream)) != hipSuccess)
       break;
-    const int od = d->Hq * d->d;
     GemmArgs g2{o, pst_o, (size_t)od, R, L.wo, wf32, (size_t)od, d->H, od, X, (size_t)d->H, X,
                 (size_t)d->H};
-    if ((h = gemm(g2, gws, stream)) != hipSuccess) break;
-    if ((h = rmsnorm_rows(X, L.g_ffn, d->eps, xh, R, d->H, stream)) != hipSuccess) break;
+    if ((h = gemm_deferred(g2, gws, stream, &so)) != hipSuccess) break;
+    if ((h = residual_rmsnorm(so, X, (size_t)d->H, 1, L.g_ffn, d->eps, xh, R, d->H, stream)) !=
+        hipSuccess)
+      break;
     GemmArgs g3{xh, pst_h, (size_t)d->H, R, L.wg, wf32, (size_t)d->H, d->F, d->H, gate,
                 (size_t)d->F, nullptr, 0};
-    if ((h = gemm(g3, gws, stream)) != hipSuccess) break;
+    if ((h = gemm_deferred(g3, gws, stream, &sg)) != hipSuccess) break;
     GemmArgs g4{xh, pst_h, (size_t)d->H, R, L.wu, wf32, (size_t)d->H, d->F, d->H, up,
                 (size_t)d->F, nullptr, 0};
-    if ((h = gemm(g4, gws, stream)) != hipSuccess) break;
-    if ((h = swiglu(gate, up, act, (size_t)R * d->F, stream)) != hipSuccess) break;
+    if ((h = gemm_deferred(g4, gws2, stream, &su)) != hipSuccess) break;
+    if ((h = swiglu(sg, su, act, R, d->F, stream)) != hipSuccess) break;
+    const size_t pst_f = (size_t)R * d->F;
     GemmArgs g5{act, pst_f, (size_t)d->F, R, L.wd, wf32, (size_t)d->F, d->H, d->F, X,
                 (size_t)d->H, X, (size_t)d->H};
-    h = gemm(g5, gws, stream);
+    if ((h = gemm_deferred(g5, gws, stream, &sd)) != hipSuccess) break;
+    if (l + 1 < d->n_layers)
+      h = residual_rmsnorm(sd, X, (size_t)d->H, 1, d->layers[l + 1].g_attn, d->eps, xh, R, d->H,
+                           stream);
+    else
+      h = final_norm_mask(sd, d->g_final, d->eps, d->B, S, d->n_anchor, d->K, d->H, d->dtype,
+                          d->out, stream);
   }
-  if (h == hipSuccess)
-    h = final_norm_mask(X, d->g_final, d->eps, d->B, S, d->n_anchor, d->K, d->H, d->dtype, d->out,
-                        stream);
   return launch_status(h);
 }
 

@@ -1,6 +1,9 @@
-// Row-wise kernels of the path: RMSNorm (float64 sum of squares), the fusion
-// prologue, draft-slot assembly, the rotary embedding, SwiGLU and the drafter's
-// final norm.  One workgroup per row; all of them are a few MB of traffic.
+// Row-wise kernels of the path: the fusion prologue, draft-slot assembly,
+// RMSNorm (float64 sum of squares), the rotary embedding, SwiGLU and the
+// drafter's final norm.  One workgroup per row; each reads its row once into
+// registers.  The kernels that follow a drafter GEMM read its result through
+// a SplitOut view, which adds the float32 split-K partials (and the residual)
+// in a fixed order, so no separate reduction pass is needed.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -21,29 +24,116 @@ __device__ double block_sum(double v, double* red) {
   return t;
 }
 
-// 1 / sqrt(mean(x^2) + eps) of a row read through `ld` (float64 accumulation).
-template <class Load>
-__device__ double inv_rms(Load ld, int H, float eps, double* red) {
-  double ss = 0.0;
-  for (int i = threadIdx.x; i < H; i += blockDim.x) {
-    const double v = ld(i);
-    ss += v * v;
+// value(m, n .. n + 3) of a GEMM result: the finished row when it was not split
+// over K, else R + (part[0] + part[1] + ...), the order the reduction uses.
+__device__ __forceinline__ float4 split_load4(const SplitOut& o, int m, int n) {
+  if (o.splits == 1) return *(const float4*)(o.C + (size_t)m * o.ldc + n);
+  const size_t mn = (size_t)m * o.N + n, plane = (size_t)o.M * o.N;
+  float4 s = *(const float4*)(o.part + mn);
+  for (int z = 1; z < o.splits; ++z) {
+    const float4 v = *(const float4*)(o.part + z * plane + mn);
+    s.x += v.x;
+    s.y += v.y;
+    s.z += v.z;
+    s.w += v.w;
   }
-  ss = block_sum(ss, red);
-  return 1.0 / sqrt(ss / H + (double)eps);
+  if (o.R) {
+    const float4 b = *(const float4*)(o.R + (size_t)m * o.ldr + n);
+    s.x = b.x + s.x;
+    s.y = b.y + s.y;
+    s.z = b.z + s.z;
+    s.w = b.w + s.w;
+  }
+  return s;
 }
 
-// y = RMSNorm(x; g) written as bf16 planes [2][rows][H] (plane stride pst).
-__global__ __launch_bounds__(kRowThreads) void rmsnorm_rows_kernel(const float* __restrict__ x,
-                                                                   const float* __restrict__ g,
-                                                                   float eps, uint16_t* __restrict__ y,
-                                                                   size_t pst, int H) {
+__device__ __forceinline__ double sumsq4(const float4& v) {
+  return (double)v.x * v.x + (double)v.y * v.y + (double)v.z * v.z + (double)v.w * v.w;
+}
+
+// Planes of y = x * inv * g for four consecutive elements at index i.
+__device__ __forceinline__ void store_norm4(uint16_t* y, size_t pst, size_t i, const float4& x,
+                                            double inv, const float* g) {
+  const float4 gg = *(const float4*)g;
+  store_planes(y, pst, i + 0, (float)((double)x.x * inv * gg.x));
+  store_planes(y, pst, i + 1, (float)((double)x.y * inv * gg.y));
+  store_planes(y, pst, i + 2, (float)((double)x.z * inv * gg.z));
+  store_planes(y, pst, i + 3, (float)((double)x.w * inv * gg.w));
+}
+
+// X[m] = value(m) (the residual update, when write_x) and y[m] =
+// RMSNorm(value(m); g) as bf16 planes [2][rows][H].  V4 float4 per thread.
+template <int V4>
+__global__ __launch_bounds__(kRowThreads) void residual_rmsnorm_kernel(SplitOut o, float* X, size_t ldx,
+                                                                       int write_x, const float* g,
+                                                                       float eps, uint16_t* y,
+                                                                       size_t pst, int H) {
   __shared__ double red[kRowThreads / kWave];
-  const float* xr = x + (size_t)blockIdx.x * H;
-  const double inv = inv_rms([&](int i) { return (double)xr[i]; }, H, eps, red);
+  const int m = blockIdx.x;
+  float4 v[V4];
+  double ss = 0.0;
+#pragma unroll
+  for (int k = 0; k < V4; ++k) {
+    const int n = 4 * (threadIdx.x + kRowThreads * k);
+    if (n < H) {
+      v[k] = split_load4(o, m, n);
+      ss += sumsq4(v[k]);
+    }
+  }
+  ss = block_sum(ss, red);
+  const double inv = 1.0 / sqrt(ss / H + (double)eps);
+#pragma unroll
+  for (int k = 0; k < V4; ++k) {
+    const int n = 4 * (threadIdx.x + kRowThreads * k);
+    if (n < H) {
+      if (write_x) *(float4*)(X + (size_t)m * ldx + n) = v[k];
+      store_norm4(y, pst, (size_t)m * H + n, v[k], inv, g + n);
+    }
+  }
+}
+
+// out[b, j] = round_dtype(RMSNorm(value(b S + n_anchor + j); g)), j < K - 1.
+template <int V4>
+__global__ __launch_bounds__(kRowThreads) void final_norm_kernel(SplitOut o, const float* g, float eps,
+                                                                 int S, int n_anchor, int Km1, int H,
+                                                                 int dtype, void* out) {
+  __shared__ double red[kRowThreads / kWave];
+  const int b = blockIdx.x / Km1, j = blockIdx.x % Km1;
+  const int m = b * S + n_anchor + j;
+  float4 v[V4];
+  double ss = 0.0;
+#pragma unroll
+  for (int k = 0; k < V4; ++k) {
+    const int n = 4 * (threadIdx.x + kRowThreads * k);
+    if (n < H) {
+      v[k] = split_load4(o, m, n);
+      ss += sumsq4(v[k]);
+    }
+  }
+  ss = block_sum(ss, red);
+  const double inv = 1.0 / sqrt(ss / H + (double)eps);
   const size_t r0 = (size_t)blockIdx.x * H;
-  for (int i = threadIdx.x; i < H; i += blockDim.x)
-    store_planes(y, pst, r0 + i, (float)((double)xr[i] * inv * g[i]));
+#pragma unroll
+  for (int k = 0; k < V4; ++k) {
+    const int n = 4 * (threadIdx.x + kRowThreads * k);
+    if (n < H) {
+      const float4 gg = *(const float4*)(g + n);
+      store_elem(out, dtype, r0 + n + 0, (float)((double)v[k].x * inv * gg.x));
+      store_elem(out, dtype, r0 + n + 1, (float)((double)v[k].y * inv * gg.y));
+      store_elem(out, dtype, r0 + n + 2, (float)((double)v[k].z * inv * gg.z));
+      store_elem(out, dtype, r0 + n + 3, (float)((double)v[k].w * inv * gg.w));
+    }
+  }
+}
+
+// Four consecutive elements (n % 4 == 0) of a row stored in dtype.
+__device__ __forceinline__ float4 load4(const void* base, int dtype, size_t off) {
+  if (dtype == DMTP_BF16) {
+    const uint2 u = *(const uint2*)((const uint16_t*)base + off);
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+  }
+  return *(const float4*)((const float*)base + off);
 }
 
 struct RowSrc {
@@ -54,29 +144,61 @@ struct RowSrc {
   int n_table;
 };
 
-// Element i of row r: the row itself, or table[ids[r]] (zero for an id outside the table).
-__device__ __forceinline__ float row_elem(const RowSrc& s, int r, int H, int i) {
-  if (s.rows) return load_elem(s.rows, s.dtype, (size_t)r * H + i);
+// Elements n .. n + 3 of row r: the row itself, or table[ids[r]] (zero for an
+// id outside the table).
+__device__ __forceinline__ float4 row_elem4(const RowSrc& s, int r, int H, int n) {
+  if (s.rows) return load4(s.rows, s.dtype, (size_t)r * H + n);
   const int id = s.ids[r];
-  if (id < 0 || id >= s.n_table) return 0.f;
-  return load_elem(s.table, s.dtype, (size_t)id * H + i);
+  if (id < 0 || id >= s.n_table) return make_float4(0.f, 0.f, 0.f, 0.f);
+  return load4(s.table, s.dtype, (size_t)id * H + n);
 }
 
+// cat[r] = [RMSNorm(x1[r]; g1), RMSNorm(x2[r]; g2)] as bf16 planes, and
+// out[r] = res[r] when has_res.
+template <int V4>
 __global__ __launch_bounds__(kRowThreads) void fuse_prep_kernel(RowSrc x1, RowSrc x2, RowSrc res,
                                                                 int has_res, const float* g1,
                                                                 const float* g2, float eps, int H,
                                                                 uint16_t* __restrict__ cat,
                                                                 size_t pst,
                                                                 float* __restrict__ out) {
-  __shared__ double red[kRowThreads / kWave];
+  __shared__ double red[2][kRowThreads / kWave];
   const int r = blockIdx.x;
-  const double i1 = inv_rms([&](int i) { return (double)row_elem(x1, r, H, i); }, H, eps, red);
-  const double i2 = inv_rms([&](int i) { return (double)row_elem(x2, r, H, i); }, H, eps, red);
+  float4 a[V4], c[V4];
+  double s1 = 0.0, s2 = 0.0;
+#pragma unroll
+  for (int k = 0; k < V4; ++k) {
+    const int n = 4 * (threadIdx.x + kRowThreads * k);
+    if (n < H) {
+      a[k] = row_elem4(x1, r, H, n);
+      c[k] = row_elem4(x2, r, H, n);
+      s1 += sumsq4(a[k]);
+      s2 += sumsq4(c[k]);
+    }
+  }
+  s1 = wave_sum(s1);
+  s2 = wave_sum(s2);
+  const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
+  if (l == 0) {
+    red[0][w] = s1;
+    red[1][w] = s2;
+  }
+  __syncthreads();
+  s1 = s2 = 0.0;
+  for (int i = 0; i < kRowThreads / kWave; ++i) {
+    s1 += red[0][i];
+    s2 += red[1][i];
+  }
+  const double i1 = 1.0 / sqrt(s1 / H + (double)eps), i2 = 1.0 / sqrt(s2 / H + (double)eps);
   const size_t c0 = (size_t)r * 2 * H;
-  for (int i = threadIdx.x; i < H; i += blockDim.x) {
-    store_planes(cat, pst, c0 + i, (float)((double)row_elem(x1, r, H, i) * i1 * g1[i]));
-    store_planes(cat, pst, c0 + H + i, (float)((double)row_elem(x2, r, H, i) * i2 * g2[i]));
-    if (has_res) out[(size_t)r * H + i] = row_elem(res, r, H, i);
+#pragma unroll
+  for (int k = 0; k < V4; ++k) {
+    const int n = 4 * (threadIdx.x + kRowThreads * k);
+    if (n < H) {
+      store_norm4(cat, pst, c0 + n, a[k], i1, g1 + n);
+      store_norm4(cat, pst, c0 + H + n, c[k], i2, g2 + n);
+      if (has_res) *(float4*)(out + (size_t)r * H + n) = row_elem4(res, r, H, n);
+    }
   }
 }
 
@@ -87,71 +209,76 @@ __global__ void build_slots_kernel(const int32_t* __restrict__ anchor, const flo
   float* xr = X + (size_t)blockIdx.x * H;
   if (s == n_anchor - 1) {
     const float* src = x_t1 + (size_t)b * H;
-    for (int i = threadIdx.x; i < H; i += blockDim.x) xr[i] = src[i];
+    for (int i = 4 * threadIdx.x; i < H; i += 4 * blockDim.x)
+      *(float4*)(xr + i) = *(const float4*)(src + i);
     return;
   }
   const int tok = (n_anchor == 2 && s == 0) ? anchor[b] : mask_id;
   const bool ok = tok >= 0 && tok < V;
-  for (int i = threadIdx.x; i < H; i += blockDim.x)
-    xr[i] = ok ? load_elem(emb, dtype, (size_t)tok * H + i) : 0.f;
+  for (int i = 4 * threadIdx.x; i < H; i += 4 * blockDim.x)
+    *(float4*)(xr + i) = ok ? load4(emb, dtype, (size_t)tok * H + i) : make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
-// Rotary embedding, rotate-half form: dims i and i + d/2 turn by pos * base^(-2i/d).
-// Angles and their sines in float64 so that positions up to 32K keep full accuracy.
-__global__ void rope_split_kernel(const float* __restrict__ qkv, const int32_t* __restrict__ cu_ctx,
-                                  int ctx_rows, int S, int Hq, int Hkv, int d, float rope_base,
-                                  float* __restrict__ q, float* __restrict__ kb,
-                                  float* __restrict__ vb) {
-  const int b = blockIdx.x / S, s = blockIdx.x % S;
+// q/k/v split of the QKV projection with the rotary embedding at the slot's
+// position: pair (i, i + d/2) of every query and key head is rotated by
+// pos * base^(-2i/d).  The angles depend only on (pos, i), so their cosines and
+// sines are computed once per row (float64) into LDS.
+__global__ __launch_bounds__(256) void rope_split_kernel(SplitOut o, const int32_t* __restrict__ cu_ctx,
+                                                         int ctx_rows, int S, int Hq, int Hkv, int d,
+                                                         float rope_base, float* __restrict__ q,
+                                                         float* __restrict__ kb,
+                                                         float* __restrict__ vb) {
+  __shared__ double cs[64], sn[64];
+  const int m = blockIdx.x;
+  const int b = m / S, s = m % S;
   const int G = Hq / Hkv, NQ = S * G, half = d / 2;
   const int pos = ctx_len_of(cu_ctx, b, ctx_rows) + s;
-  const float* row = qkv + (size_t)blockIdx.x * (Hq + 2 * Hkv) * d;
   const double lnb = log((double)rope_base);
-  // rotated heads: Hq query heads then Hkv key heads, pairs (i, i + d/2)
-  for (int e = threadIdx.x; e < (Hq + Hkv) * half; e += blockDim.x) {
-    const int h = e / half, i = e % half;
+  for (int i = threadIdx.x; i < half; i += blockDim.x) {
     const double ang = (double)pos * exp(-(2.0 * i / d) * lnb);
-    double sn, cs;
-    sincos(ang, &sn, &cs);
-    const double x1 = row[h * d + i], x2 = row[h * d + i + half];
-    const float o1 = (float)(x1 * cs - x2 * sn), o2 = (float)(x2 * cs + x1 * sn);
-    if (h < Hq) {
-      float* dst = q + (((size_t)b * Hkv + h / G) * NQ + s * G + h % G) * d;
-      dst[i] = o1;
-      dst[i + half] = o2;
-    } else {
-      float* dst = kb + (((size_t)b * Hkv + (h - Hq)) * S + s) * d;
-      dst[i] = o1;
-      dst[i + half] = o2;
+    double sv, cv;
+    sincos(ang, &sv, &cv);
+    sn[i] = sv;
+    cs[i] = cv;
+  }
+  __syncthreads();
+  // rotated heads: Hq query heads then Hkv key heads; four pairs per thread
+  const int quads = (Hq + Hkv) * half / 4;
+  for (int e = threadIdx.x; e < quads; e += blockDim.x) {
+    const int h = (4 * e) / half, i0 = (4 * e) % half;
+    const float4 x1 = split_load4(o, m, h * d + i0), x2 = split_load4(o, m, h * d + i0 + half);
+    const float a1[4] = {x1.x, x1.y, x1.z, x1.w}, a2[4] = {x2.x, x2.y, x2.z, x2.w};
+    float r1[4], r2[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const double c = cs[i0 + t], sv = sn[i0 + t];
+      r1[t] = (float)((double)a1[t] * c - (double)a2[t] * sv);
+      r2[t] = (float)((double)a2[t] * c + (double)a1[t] * sv);
     }
+    float* dst = h < Hq ? q + (((size_t)b * Hkv + h / G) * NQ + s * G + h % G) * d
+                        : kb + (((size_t)b * Hkv + (h - Hq)) * S + s) * d;
+    *(float4*)(dst + i0) = make_float4(r1[0], r1[1], r1[2], r1[3]);
+    *(float4*)(dst + i0 + half) = make_float4(r2[0], r2[1], r2[2], r2[3]);
   }
-  for (int e = threadIdx.x; e < Hkv * d; e += blockDim.x) {
-    const int h = e / d, i = e % d;
-    vb[(((size_t)b * Hkv + h) * S + s) * d + i] = row[(Hq + Hkv) * d + e];
+  for (int e = threadIdx.x; e < Hkv * d / 4; e += blockDim.x) {
+    const int h = (4 * e) / d, i = (4 * e) % d;
+    *(float4*)(vb + (((size_t)b * Hkv + h) * S + s) * d + i) = split_load4(o, m, (Hq + Hkv) * d + 4 * e);
   }
 }
 
-// a = silu(g) * u, written as bf16 planes [2][n] (plane stride n).
-__global__ void swiglu_kernel(const float* __restrict__ g, const float* __restrict__ u,
-                              uint16_t* __restrict__ a, size_t n) {
-  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
+// a = silu(g) * u over [rows, F], written as bf16 planes [2][rows][F].
+__global__ void swiglu_kernel(SplitOut gs, SplitOut us, uint16_t* __restrict__ a, int rows, int F) {
+  const size_t n4 = (size_t)rows * F / 4, pst = (size_t)rows * F;
+  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n4;
        e += (size_t)gridDim.x * blockDim.x) {
-    const float x = g[e];
-    store_planes(a, n, e, x / (1.0f + expf(-x)) * u[e]);
+    const int m = (int)(4 * e / F), n = (int)(4 * e % F);
+    const float4 g = split_load4(gs, m, n), u = split_load4(us, m, n);
+    const size_t i = 4 * e;
+    store_planes(a, pst, i + 0, g.x / (1.0f + expf(-g.x)) * u.x);
+    store_planes(a, pst, i + 1, g.y / (1.0f + expf(-g.y)) * u.y);
+    store_planes(a, pst, i + 2, g.z / (1.0f + expf(-g.z)) * u.z);
+    store_planes(a, pst, i + 3, g.w / (1.0f + expf(-g.w)) * u.w);
   }
-}
-
-__global__ __launch_bounds__(kRowThreads) void final_norm_kernel(const float* __restrict__ X,
-                                                                 const float* __restrict__ g,
-                                                                 float eps, int S, int n_anchor,
-                                                                 int Km1, int H, int dtype,
-                                                                 void* __restrict__ out) {
-  __shared__ double red[kRowThreads / kWave];
-  const int b = blockIdx.x / Km1, j = blockIdx.x % Km1;
-  const float* xr = X + ((size_t)b * S + n_anchor + j) * H;
-  const double inv = inv_rms([&](int i) { return (double)xr[i]; }, H, eps, red);
-  for (int i = threadIdx.x; i < H; i += blockDim.x)
-    store_elem(out, dtype, (size_t)blockIdx.x * H + i, (float)((double)xr[i] * inv * g[i]));
 }
 
 RowSrc src_of(const dmtp_rows& r, int w_dtype) {
@@ -164,20 +291,52 @@ RowSrc src_of(const dmtp_rows& r, int w_dtype) {
   return s;
 }
 
+// float4 groups per thread for a row of H elements (H % 4 == 0, H <= 16384).
+int v4_of(int H) {
+  const int g = (H / 4 + kRowThreads - 1) / kRowThreads;
+  return g <= 1 ? 1 : g <= 2 ? 2 : g <= 4 ? 4 : g <= 8 ? 8 : 16;
+}
+
 }  // namespace
 
-hipError_t rmsnorm_rows(const float* x, const float* g, float eps, uint16_t* y, int rows, int H,
-                        hipStream_t s) {
-  hipLaunchKernelGGL(rmsnorm_rows_kernel, dim3(rows), dim3(kRowThreads), 0, s, x, g, eps, y,
-                     (size_t)rows * H, H);
+SplitOut split_out_plain(const float* C, size_t ldc, int M, int N) {
+  SplitOut o{};
+  o.C = C;
+  o.ldc = ldc;
+  o.splits = 1;
+  o.M = M;
+  o.N = N;
+  return o;
+}
+
+hipError_t residual_rmsnorm(const SplitOut& x, float* X, size_t ldx, int write_x, const float* g,
+                            float eps, uint16_t* y, int rows, int H, hipStream_t s) {
+  const size_t pst = (size_t)rows * H;
+  switch (v4_of(H)) {
+#define DMTP_CASE(n)                                                                               \
+  case n:                                                                                          \
+    hipLaunchKernelGGL(residual_rmsnorm_kernel<n>, dim3(rows), dim3(kRowThreads), 0, s, x, X, ldx,  \
+                       write_x, g, eps, y, pst, H);                                                \
+    break;
+    DMTP_CASE(1) DMTP_CASE(2) DMTP_CASE(4) DMTP_CASE(8) DMTP_CASE(16)
+#undef DMTP_CASE
+  }
   return hipGetLastError();
 }
 
 hipError_t fuse_prep(const dmtp_fuse_desc& d, uint16_t* cat, hipStream_t s) {
   const int has_res = d.res.rows != nullptr || d.res.ids != nullptr;
-  hipLaunchKernelGGL(fuse_prep_kernel, dim3(d.rows), dim3(kRowThreads), 0, s,
-                     src_of(d.x1, d.w_dtype), src_of(d.x2, d.w_dtype), src_of(d.res, d.w_dtype),
-                     has_res, d.g1, d.g2, d.eps, d.H, cat, (size_t)d.rows * 2 * d.H, d.out);
+  const RowSrc a = src_of(d.x1, d.w_dtype), b = src_of(d.x2, d.w_dtype), r = src_of(d.res, d.w_dtype);
+  const size_t pst = (size_t)d.rows * 2 * d.H;
+  switch (v4_of(d.H)) {
+#define DMTP_CASE(n)                                                                               \
+  case n:                                                                                          \
+    hipLaunchKernelGGL(fuse_prep_kernel<n>, dim3(d.rows), dim3(kRowThreads), 0, s, a, b, r,         \
+                       has_res, d.g1, d.g2, d.eps, d.H, cat, pst, d.out);                          \
+    break;
+    DMTP_CASE(1) DMTP_CASE(2) DMTP_CASE(4) DMTP_CASE(8) DMTP_CASE(16)
+#undef DMTP_CASE
+  }
   return hipGetLastError();
 }
 
@@ -188,7 +347,7 @@ hipError_t build_slots(const dmtp_draft_desc& d, float* X, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t rope_split(const float* qkv, const int32_t* cu_ctx, int ctx_rows, int B, int S, int Hq,
+hipError_t rope_split(const SplitOut& qkv, const int32_t* cu_ctx, int ctx_rows, int B, int S, int Hq,
                       int Hkv, int d, float rope_base, float* q, float* kb, float* vb,
                       hipStream_t s) {
   hipLaunchKernelGGL(rope_split_kernel, dim3(B * S), dim3(256), 0, s, qkv, cu_ctx, ctx_rows, S, Hq,
@@ -196,16 +355,24 @@ hipError_t rope_split(const float* qkv, const int32_t* cu_ctx, int ctx_rows, int
   return hipGetLastError();
 }
 
-hipError_t swiglu(const float* g, const float* u, uint16_t* a, size_t n, hipStream_t s) {
-  const size_t blocks = (n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192;
-  hipLaunchKernelGGL(swiglu_kernel, dim3((unsigned)blocks), dim3(256), 0, s, g, u, a, n);
+hipError_t swiglu(const SplitOut& g, const SplitOut& u, uint16_t* a, int rows, int F, hipStream_t s) {
+  const size_t n4 = (size_t)rows * F / 4;
+  const size_t blocks = (n4 + 255) / 256 < 8192 ? (n4 + 255) / 256 : 8192;
+  hipLaunchKernelGGL(swiglu_kernel, dim3((unsigned)blocks), dim3(256), 0, s, g, u, a, rows, F);
   return hipGetLastError();
 }
 
-hipError_t final_norm_mask(const float* X, const float* g, float eps, int B, int S, int n_anchor,
+hipError_t final_norm_mask(const SplitOut& x, const float* g, float eps, int B, int S, int n_anchor,
                            int K, int H, int dtype, void* out, hipStream_t s) {
-  hipLaunchKernelGGL(final_norm_kernel, dim3(B * (K - 1)), dim3(kRowThreads), 0, s, X, g, eps, S,
-                     n_anchor, K - 1, H, dtype, out);
+  switch (v4_of(H)) {
+#define DMTP_CASE(n)                                                                               \
+  case n:                                                                                          \
+    hipLaunchKernelGGL(final_norm_kernel<n>, dim3(B * (K - 1)), dim3(kRowThreads), 0, s, x, g, eps,  \
+                       S, n_anchor, K - 1, H, dtype, out);                                         \
+    break;
+    DMTP_CASE(1) DMTP_CASE(2) DMTP_CASE(4) DMTP_CASE(8) DMTP_CASE(16)
+#undef DMTP_CASE
+  }
   return hipGetLastError();
 }
 

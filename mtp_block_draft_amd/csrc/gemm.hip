@@ -306,6 +306,22 @@ size_t gemm_ws_bytes(int M, int N, int K, int b_f32) {
   return pl.splits > 1 ? (size_t)pl.splits * M * N * sizeof(float) : 0;
 }
 
+hipError_t gemm_deferred(const GemmArgs& a, float* ws, hipStream_t s, SplitOut* out) {
+  GemmParams p{a.A, a.a_pst, a.lda, a.M, a.B, a.ldb, a.N, a.K, 1, a.C, a.ldc, a.R, a.ldr, ws};
+  *out = SplitOut{a.C, a.ldc, ws, 1, a.M, a.N, a.R, a.ldr};
+  if (!a.b_f32) {
+    if (!dma_ok(a)) return hipErrorInvalidValue;
+    const DmaPlan pl = dma_plan(a.M, a.N, a.K);
+    p.splits = pl.splits;
+    out->splits = pl.splits;
+    return pl.cfg == 0 ? launch_dma<DmaM32>(p, pl, s) : launch_dma<DmaM128>(p, pl, s);
+  }
+  dim3 grid((a.N + TilePlanesF32::BN - 1) / TilePlanesF32::BN,
+            (a.M + TilePlanesF32::BM - 1) / TilePlanesF32::BM);
+  hipLaunchKernelGGL(gemm_kernel<TilePlanesF32>, grid, dim3(TilePlanesF32::THREADS), 0, s, p);
+  return hipGetLastError();
+}
+
 hipError_t gemm(const GemmArgs& a, float* ws, hipStream_t s) {
   GemmParams p{a.A, a.a_pst, a.lda, a.M, a.B, a.ldb, a.N, a.K, 1, a.C, a.ldc, a.R, a.ldr, ws};
   if (!a.b_f32) {

@@ -33,11 +33,26 @@ struct GemmArgs {
 size_t gemm_ws_bytes(int M, int N, int K, int b_f32);
 hipError_t gemm(const GemmArgs& a, float* ws, hipStream_t s);
 
+// A GEMM result that may still be split over K.  splits == 1: the finished C
+// [M, ldc] (R already added).  splits > 1: value(m, n) = R[m, n] (if R) +
+// sum_z part[z][m][n], summed in z order by the kernel that reads it.
+struct SplitOut {
+  const float* C;
+  size_t ldc;
+  const float* part;   // [splits][M][N]
+  int splits, M, N;
+  const float* R;
+  size_t ldr;
+};
+SplitOut split_out_plain(const float* C, size_t ldc, int M, int N);
+// The GEMM without its reduction pass: the reader of *out adds the partials.
+hipError_t gemm_deferred(const GemmArgs& a, float* ws, hipStream_t s, SplitOut* out);
+
 // -------------------------------------------------------------- elementwise --
-// y[r] = RMSNorm(x[r]; g) for float32 rows of width H, written as bf16 planes
-// [2][rows][H].
-hipError_t rmsnorm_rows(const float* x, const float* g, float eps, uint16_t* y, int rows, int H,
-                        hipStream_t s);
+// X[r] = value(r) (when write_x; the residual stream update) and y[r] =
+// RMSNorm(value(r); g) as bf16 planes [2][rows][H], for the rows of x.
+hipError_t residual_rmsnorm(const SplitOut& x, float* X, size_t ldx, int write_x, const float* g,
+                            float eps, uint16_t* y, int rows, int H, hipStream_t s);
 
 // Fusion prologue: cat[r] = [RMSNorm(x1[r]; g1), RMSNorm(x2[r]; g2)] as bf16
 // planes [2][rows][2H], and out[r] = res[r] (float32) when res is present.
@@ -48,15 +63,15 @@ hipError_t build_slots(const dmtp_draft_desc& d, float* X, hipStream_t s);
 
 // q/k/v split of the QKV projection with the rotary embedding at slot
 // positions: q [B, Hkv, S * G, d], kb and vb [B, Hkv, S, d] (float32).
-hipError_t rope_split(const float* qkv, const int32_t* cu_ctx, int ctx_rows, int B, int S, int Hq,
+hipError_t rope_split(const SplitOut& qkv, const int32_t* cu_ctx, int ctx_rows, int B, int S, int Hq,
                       int Hkv, int d, float rope_base, float* q, float* kb, float* vb,
                       hipStream_t s);
 
-// a = silu(g) * u elementwise ([n] float32 in, bf16 planes [2][n] out)
-hipError_t swiglu(const float* g, const float* u, uint16_t* a, size_t n, hipStream_t s);
+// a = silu(g) * u elementwise over [rows, F] (bf16 planes [2][rows][F] out)
+hipError_t swiglu(const SplitOut& g, const SplitOut& u, uint16_t* a, int rows, int F, hipStream_t s);
 
-// out[b, j] = round_dtype(RMSNorm(X[b, n_anchor + j]; g)) for j = 0 .. K-2
-hipError_t final_norm_mask(const float* X, const float* g, float eps, int B, int S, int n_anchor,
+// out[b, j] = round_dtype(RMSNorm(value(b S + n_anchor + j); g)) for j = 0 .. K-2
+hipError_t final_norm_mask(const SplitOut& x, const float* g, float eps, int B, int S, int n_anchor,
                            int K, int H, int dtype, void* out, hipStream_t s);
 
 // -------------------------------------------------------------- attention --
