@@ -167,7 +167,7 @@ def main() -> int:
     ap.add_argument("--top", type=int, default=20)
     ap.add_argument("--fetch", help="counter_collection.csv of a FETCH_SIZE pass")
     ap.add_argument("--write", help="counter_collection.csv of a WRITE_SIZE pass")
-    ap.add_argument("--kernel", default="head_gemm_mf32_kernel<7>")
+    ap.add_argument("--kernel", default="head_gemm_mf32_kernel<7,")
     ap.add_argument("--copy-kernel", default="elementwise")
     ap.add_argument("--copy-mib", type=int, default=1024)
     args = ap.parse_args()
