@@ -63,6 +63,19 @@ __device__ __forceinline__ void wait_newer(int newer) {
   }
 }
 
+// wait_vm_lgkm0<n>() for a run-time n in [0, N].
+template <int N>
+__device__ __forceinline__ void wait_vm_dyn(int n) {
+  if constexpr (N <= 0) {
+    wait_vm_lgkm0<0>();
+  } else {
+    if (n >= N)
+      wait_vm_lgkm0<N>();
+    else
+      wait_vm_dyn<N - 1>(n);
+  }
+}
+
 // Workgroup barrier for the LDS ring: no memory fence (the waits above order
 // this wave's own copies), and a compiler barrier so that no LDS access moves
 // across it.

@@ -13,6 +13,7 @@
 //             stored logits rows of sampled rows, in vocabulary chunks
 //   finalize  token per row: draw, planted row argmax, or argmax
 #include <cstdlib>
+#include <type_traits>
 
 #include "dma.hpp"
 #include "gemm_core.hpp"
@@ -40,6 +41,26 @@ __device__ __forceinline__ RowStat stat_merge(const RowStat& a, const RowStat& b
   const float wa = a.s > 0.f ? a.s * hw_exp2((a.m - r.m) * sc) : 0.f;
   const float wb = b.s > 0.f ? b.s * hw_exp2((b.m - r.m) * sc) : 0.f;
   r.s = wa + wb;
+  return r;
+}
+
+// v_max / v_min / v_max3 as the hardware executes them.  fmaxf on a value of
+// unknown origin (here: accumulators read from AGPRs) is compiled with an
+// extra quieting instruction per input; the row statistics never see
+// signalling NaNs, so that step is skipped.
+__device__ __forceinline__ float hw_max(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float hw_min(float a, float b) {
+  float r;
+  asm("v_min_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float hw_max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
   return r;
 }
 
@@ -663,15 +684,14 @@ hipError_t launch_head_lds(const HeadParams& p, int n_mchunks, hipStream_t s) {
 // takes vocabulary half (w & 1) (64 rows) against input half (w >> 1) (32 TB
 // rows): 2 x TB accumulator tiles of 32 x 32 held in AGPRs (TB = 7: 448 rows,
 // the draft + target rows of a batch-32 round, in one pass over W).  K runs in
-// 32-wide slices through four LDS stages filled by global_load_lds_dwordx4 as
-// in the 16 x 16 version; in addition each wave reads the fragments of slice
-// s + 1 from LDS while the MFMAs of slice s drain, so neither the LDS latency
-// nor the barrier sits on the matrix-core critical path.  16-byte chunks are
-// XOR-swizzled with (row >> 2) & 3, which keeps the 16 lanes of a read pass on
-// distinct banks.  The two vocabulary halves' row statistics meet in LDS.
-// Ring depth: as many stages as fit 144 KB of LDS (at most 12), so that the
-// weight-streaming calls with few rows keep enough copies in flight.
-// Ring depth: as many stages as fit 144 KB of LDS (at most 12).
+// BK-wide slices through an LDS ring filled by global_load_lds_dwordx4; each
+// wave reads the fragments of the next 16-wide k-step from LDS while the MFMAs
+// of the current one drain, so neither the LDS latency nor the barrier sits on
+// the matrix-core critical path.  16-byte chunks are XOR-swizzled per row
+// (swz_chunk), which keeps the lanes of a read pass on distinct banks.  The two
+// vocabulary halves' row statistics meet in LDS.
+// Default ring depth: as many stages as fit 144 KB of LDS (at most 12), so that
+// the weight-streaming calls with few rows keep enough copies in flight.
 constexpr int head_mf32_nbuf(int TB, int BK) {
   return (147456 / ((128 + 64 * TB) * BK * 2)) > 12 ? 12 : (147456 / ((128 + 64 * TB) * BK * 2));
 }
@@ -709,28 +729,46 @@ void head_gemm_mf32_kernel(HeadParams p, int n_mchunks) {
   const uint16_t* __restrict__ W = (const uint16_t*)p.W;
   const uint16_t* __restrict__ X = (const uint16_t*)p.A;
 
-  // lane's source of copy q: row idx / CPR of the tile, the chunk that lands at
-  // position idx % CPR (rows past the end are clamped; their results are unused)
-  const uint16_t* wsrc[C::WPW];
+  // Raw per-row inputs of the epilogue, loaded ahead of the main loop so that
+  // their memory latency is spent under it rather than once per row group at
+  // the end (one wave per SIMD leaves nothing else to hide it).
+  float t_in[TB];   // temperature of the lane's row in tile t (1 when none given)
+  int s_in[TB];     // logits store index of that row (-1: none)
 #pragma unroll
-  for (int q = 0; q < C::WPW; ++q) {
-    const int idx = (wave * C::WPW + q) * 64 + lane, r = idx / C::CPR;
-    wsrc[q] = W + (size_t)min(v0 + r, V - 1) * H + 8 * swz_chunk<BK>(r, idx % C::CPR);
+  for (int t = 0; t < TB; ++t) {
+    const int m = m0 + 32 * TB * bh + 32 * t + lr;
+    const bool ok = m < M;
+    t_in[t] = (ok && p.temperature) ? p.temperature[m] : 1.f;
+    s_in[t] = (ok && p.store_row) ? p.store_row[m] : -1;
   }
-  const uint16_t* xsrc[C::XPW];
+  constexpr int NFIN = (C::BB + C::THREADS - 1) / C::THREADS;
+  float tf_in[NFIN];   // temperatures of the rows this thread writes partials for
 #pragma unroll
-  for (int q = 0; q < C::XPW; ++q) {
-    const int idx = (wave * C::XPW + q) * 64 + lane, r = idx / C::CPR;
-    xsrc[q] = X + (size_t)min(m0 + r, M - 1) * H + 8 * swz_chunk<BK>(r, idx % C::CPR);
+  for (int j = 0; j < NFIN; ++j) {
+    const int r = threadIdx.x + j * C::THREADS;
+    tf_in[j] = (r < C::BB && m0 + r < M && p.temperature) ? p.temperature[m0 + r] : 1.f;
   }
-  auto issue = [&](int slice) __attribute__((always_inline)) {
-    uint16_t* st = smem + (slice % C::NBUF) * C::STAGE;
-    const int k0 = slice * C::BK;
+
+  // Copy q of a slice (q < WPW: W rows, then input rows): lane's source is row
+  // idx / CPR of the tile, the chunk that lands at position idx % CPR (rows past
+  // the end are clamped; their results are unused); dst its 1 KB block.
+  const uint16_t* src[C::PER_WAVE];
+  int dst[C::PER_WAVE];
 #pragma unroll
-    for (int q = 0; q < C::WPW; ++q) lds_dma16(wsrc[q] + k0, st + (wave * C::WPW + q) * 512);
-#pragma unroll
-    for (int q = 0; q < C::XPW; ++q)
-      lds_dma16(xsrc[q] + k0, st + C::BV * C::BK + (wave * C::XPW + q) * 512);
+  for (int q = 0; q < C::PER_WAVE; ++q) {
+    if (q < C::WPW) {
+      const int idx = (wave * C::WPW + q) * 64 + lane, r = idx / C::CPR;
+      src[q] = W + (size_t)min(v0 + r, V - 1) * H + 8 * swz_chunk<BK>(r, idx % C::CPR);
+      dst[q] = (wave * C::WPW + q) * 512;
+    } else {
+      const int qq = q - C::WPW;
+      const int idx = (wave * C::XPW + qq) * 64 + lane, r = idx / C::CPR;
+      src[q] = X + (size_t)min(m0 + r, M - 1) * H + 8 * swz_chunk<BK>(r, idx % C::CPR);
+      dst[q] = C::BV * C::BK + (wave * C::XPW + qq) * 512;
+    }
+  }
+  auto issue_one = [&](int slice, int q) __attribute__((always_inline)) {
+    lds_dma16(src[q] + slice * C::BK, smem + (slice % C::NBUF) * C::STAGE + dst[q]);
   };
   // fragments of one 16-wide k-step
   struct Frag {
@@ -752,32 +790,72 @@ void head_gemm_mf32_kernel(HeadParams p, int n_mchunks) {
     for (int t = 0; t < TB; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[u][t][i] = 0.f;
-  auto compute = [&](const Frag& f) __attribute__((always_inline)) {
+  const int nK = H / C::BK;
+  // With three or more stages the copies of slice s + NBUF - 1 are spread over
+  // the MFMA pairs of slice s (copy q after pair q * PAIRS / PER_WAVE), so the
+  // wave never stalls on a burst of copies while the matrix unit idles.  With
+  // two stages every copy of the next slice must be issued before the wait for
+  // it, so they go out in one burst after the barrier.
+  constexpr bool INTER = C::NBUF >= 3;
+  constexpr int PAIRS = C::KS * TB;
+  auto compute = [&](const Frag& f, int ks, int s_fill) __attribute__((always_inline)) {
 #pragma unroll
-    for (int t = 0; t < TB; ++t)
+    for (int t = 0; t < TB; ++t) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) acc[u][t] = mfma32(f.a[u], f.b[t], acc[u][t]);
+      if constexpr (INTER) {
+#pragma unroll
+        for (int q = 0; q < C::PER_WAVE; ++q)
+          if ((q * PAIRS) / C::PER_WAVE == ks * TB + t && s_fill < nK) issue_one(s_fill, q);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   };
-  // Slice s is in LDS for every wave once this wave's own copies have landed
-  // (vmcnt counts the later slices' requests still allowed in flight) and all
-  // waves passed the barrier.  lgkmcnt(0) first: the buffer that the next DMA
-  // refills was read (into registers) just before, by every wave.
-  auto wait_slice = [&](int s, int nK) __attribute__((always_inline)) {
-    wait_newer<C::PER_WAVE, C::NBUF - 2>(min(nK - 1 - s, C::NBUF - 2));
+  // copies of the slice being filled that go out before the wait at the last k-step
+  constexpr int Q_BEFORE = [] {
+    int c = 0;
+    for (int q = 0; q < C::PER_WAVE; ++q)
+      if ((q * PAIRS) / C::PER_WAVE < (C::KS - 1) * TB) ++c;
+    return c;
+  }();
+  // Slice s is in LDS for every wave once this wave's own copies of it have
+  // landed -- vmcnt allows exactly the copies issued after them to stay in
+  // flight -- and all waves passed the barrier.  lgkmcnt(0) first: the buffer
+  // the next copies refill was read into registers just before, by every wave.
+  auto wait_slice = [&](int s) __attribute__((always_inline)) {
+    if constexpr (!INTER) {
+      wait_newer<C::PER_WAVE, C::NBUF - 2>(min(nK - 1 - s, C::NBUF - 2));
+    } else {
+      // issued after slice s: slices s+1 .. s+NBUF-3 whole (those that exist) and
+      // Q_BEFORE copies of slice s+NBUF-2 (the one being filled, if it exists).
+      // In the prologue slice NBUF-2 is already whole, so this waits longer than
+      // needed there, never shorter.
+      constexpr int STEADY = (C::NBUF - 3) * C::PER_WAVE + Q_BEFORE;
+      if (s + C::NBUF - 2 < nK) {
+        wait_vm_lgkm0<STEADY>();
+      } else {
+        const int full = nK - 1 - s > C::NBUF - 3 ? C::NBUF - 3 : (nK - 1 - s < 0 ? 0 : nK - 1 - s);
+        wait_vm_dyn<STEADY>(full * C::PER_WAVE);
+      }
+    }
     ring_barrier();
   };
 
-  const int nK = H / C::BK;
 #pragma unroll
   for (int s0 = 0; s0 < C::NBUF - 1; ++s0)
-    if (s0 < nK) issue(s0);
+    if (s0 < nK)
+#pragma unroll
+      for (int q = 0; q < C::PER_WAVE; ++q) issue_one(s0, q);
   Frag f0, f1;
-  wait_slice(0, nK);
-  if (C::NBUF - 1 < nK) issue(C::NBUF - 1);
+  wait_slice(0);
+  if (!INTER && C::NBUF - 1 < nK)
+#pragma unroll
+    for (int q = 0; q < C::PER_WAVE; ++q) issue_one(C::NBUF - 1, q);
   read(f0, 0, 0);
   // the next k-step's fragments are read from LDS while this one's MFMAs drain;
   // the k-steps run in increasing k whatever BK is, so results do not depend on it
   for (int s = 0; s < nK; ++s) {
+    const int s_fill = s + C::NBUF - 1;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       Frag& cur = (ks & 1) ? f1 : f0;
@@ -785,75 +863,95 @@ void head_gemm_mf32_kernel(HeadParams p, int n_mchunks) {
       if (ks + 1 < C::KS) {
         read(nxt, s, ks + 1);
       } else if (s + 1 < nK) {
-        wait_slice(s + 1, nK);
-        if (s + C::NBUF < nK) issue(s + C::NBUF);
+        wait_slice(s + 1);
+        if (!INTER && s + C::NBUF < nK)
+#pragma unroll
+          for (int q = 0; q < C::PER_WAVE; ++q) issue_one(s + C::NBUF, q);
         read(nxt, s + 1, 0);
       }
-      compute(cur);
+      compute(cur, ks, s_fill);
     }
   }
 
-  // ---- epilogue: per input row, 32 logits in the lane; merge the lane pair
-  // (xor 32), then the two vocabulary halves through LDS.
+  // ---- epilogue: per input row, 32 logits in the lane (element e = 16 u + i
+  // sits at vocabulary offset off(e) from the lane's first column, rising with
+  // e); merge the lane pair (xor 32), then the two vocabulary halves in LDS.
   __syncthreads();
   RowStat* xch = (RowStat*)smem;   // [2 vocabulary halves][BB rows]
+  const int vl = v0 + 64 * vh + 4 * lk;
+  auto off = [](int e) { return 32 * (e >> 4) + 8 * ((e & 15) >> 2) + (e & 3); };
+  // TAIL: the last vocabulary tile, whose columns past V hold clamped rows and
+  // are masked out; every other tile takes the path without the checks.
+  auto row_stats = [&](auto TAIL) __attribute__((always_inline)) {
 #pragma unroll
-  for (int t = 0; t < TB; ++t) {
-    // Pin this tile's accumulators in AGPRs up to here, so that the copies to
-    // VGPRs are made one tile at a time rather than all at the loop exit.
-    asm volatile("" : "+a"(acc[0][t]), "+a"(acc[1][t])::"memory");
-    const int lrow = 32 * TB * bh + 32 * t + lr;
-    const int m = m0 + lrow;
-    const bool m_ok = m < M;
-    const float it = m_ok ? inv_temp(p.temperature, m) : 1.f;
-    int srow = (m_ok && p.store_row) ? p.store_row[m] : -1;
-    if (srow >= p.logits_rows) srow = -1;
-    float v1 = -INFINITY, v2 = -INFINITY;
-    int i1 = 0x7FFFFFFF;
+    for (int t = 0; t < TB; ++t) {
+      // Pin this tile's accumulators in AGPRs up to here, so that the copies to
+      // VGPRs are made one tile at a time rather than all at the loop exit.
+      asm volatile("" : "+a"(acc[0][t]), "+a"(acc[1][t])::"memory");
+      const int lrow = 32 * TB * bh + 32 * t + lr;
+      const float it = t_in[t] > 0.f ? 1.f / t_in[t] : 1.f;
+      const int srow = s_in[t] < p.logits_rows ? s_in[t] : -1;
+      float x[32];
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+      for (int e = 0; e < 32; ++e)
+        x[e] = (!decltype(TAIL)::value || vl + off(e) < V) ? acc[e >> 4][t][e & 15] : -INFINITY;
+      // largest and second largest (a repeated maximum counts twice) by a
+      // pairwise tree, then the lowest element holding the largest
+      float h[16], l[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int v = v0 + 64 * vh + 32 * u + 8 * (i >> 2) + 4 * lk + (i & 3);
-        const float x = v < V ? acc[u][t][i] : -INFINITY;
-        const bool gt = x > v1;              // indices rise with (u, i): ties keep the lowest
-        v2 = gt ? v1 : fmaxf(v2, x);
-        i1 = gt ? v : i1;
-        v1 = gt ? x : v1;
+      for (int j = 0; j < 16; ++j) {
+        h[j] = hw_max(x[2 * j], x[2 * j + 1]);
+        l[j] = hw_min(x[2 * j], x[2 * j + 1]);
       }
-    const float sc = it * 1.4426950408889634f;   // exp(y) = exp2(y log2 e)
-    float sum = 0.f;
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+      for (int w = 16; w > 1; w >>= 1)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int v = v0 + 64 * vh + 32 * u + 8 * (i >> 2) + 4 * lk + (i & 3);
-        if (v < V) sum += hw_exp2((acc[u][t][i] - v1) * sc);
-      }
-    if (srow >= 0) {
-      float* dst = p.logits + (size_t)srow * V;
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int v = v0 + 64 * vh + 32 * u + 8 * (i >> 2) + 4 * lk + (i & 3);
-          if (v < V) dst[v] = acc[u][t][i];
+        for (int j = 0; j < w / 2; ++j) {
+          const float hh = hw_max(h[2 * j], h[2 * j + 1]);
+          l[j] = hw_max3(hw_min(h[2 * j], h[2 * j + 1]), l[2 * j], l[2 * j + 1]);
+          h[j] = hh;
         }
+      const float v1 = h[0], v2 = l[0];
+      int e1 = 31;
+#pragma unroll
+      for (int e = 30; e >= 0; --e) e1 = x[e] == v1 ? e : e1;
+      // exp((x - v1) t^-1) as exp2(x sc - v1 sc)
+      const float sc = it * 1.4426950408889634f, bias = -v1 * sc;
+      float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 32; ++e) ps[e & 3] += hw_exp2(fmaf(x[e], sc, bias));
+      float sum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+      int i1 = vl + off(e1);
+      if (decltype(TAIL)::value && !(v1 > -INFINITY)) {   // lane wholly past V
+        sum = 0.f;
+        i1 = 0x7FFFFFFF;
+      }
+      if (srow >= 0) {
+        float* dst = p.logits + (size_t)srow * V + vl;
+#pragma unroll
+        for (int e = 0; e < 32; ++e)
+          if (!decltype(TAIL)::value || vl + off(e) < V) dst[off(e)] = x[e];
+      }
+      RowStat st{v1, sum, i1, v2};
+      RowStat o;
+      o.m = shfl_xor(st.m, 32);
+      o.s = shfl_xor(st.s, 32);
+      o.idx = shfl_xor(st.idx, 32);
+      o.v2 = shfl_xor(st.v2, 32);
+      st = stat_merge(st, o, it);
+      if (lk == 0) xch[vh * C::BB + lrow] = st;
     }
-    RowStat st{v1, sum, i1, v2};
-    RowStat o;
-    o.m = shfl_xor(st.m, 32);
-    o.s = shfl_xor(st.s, 32);
-    o.idx = shfl_xor(st.idx, 32);
-    o.v2 = shfl_xor(st.v2, 32);
-    st = stat_merge(st, o, it);
-    if (lk == 0) xch[vh * C::BB + lrow] = st;
-  }
+  };
+  if (v0 + C::BV > V)
+    row_stats(std::true_type{});
+  else
+    row_stats(std::false_type{});
   __syncthreads();
-  for (int r = threadIdx.x; r < C::BB; r += C::THREADS) {
-    const int m = m0 + r;
-    if (m >= M) continue;
-    const float it = inv_temp(p.temperature, m);
+#pragma unroll
+  for (int j = 0; j < NFIN; ++j) {
+    const int r = threadIdx.x + j * C::THREADS, m = m0 + r;
+    if (r >= C::BB || m >= M) continue;
+    const float it = tf_in[j] > 0.f ? 1.f / tf_in[j] : 1.f;
     p.part[(size_t)m * p.n_vtiles + vt] = stat_merge(xch[r], xch[C::BB + r], it);
   }
 }
@@ -877,28 +975,26 @@ int head_tune(const char* name, int dflt) {
   return e ? atoi(e) : dflt;
 }
 
-template <int BK>
-hipError_t launch_head_mf32_bk(const HeadParams& p, int nc, int tb, hipStream_t s) {
-  switch (tb) {
-    case 1: return launch_head_mf32<1, BK>(p, nc, s);
-    case 2: return launch_head_mf32<2, BK>(p, nc, s);
-    case 3: return launch_head_mf32<3, BK>(p, nc, s);
-    case 4: return launch_head_mf32<4, BK>(p, nc, s);
-    case 5: return launch_head_mf32<5, BK>(p, nc, s);
-    case 6: return launch_head_mf32<6, BK>(p, nc, s);
-    default: return launch_head_mf32<7, BK>(p, nc, s);
-  }
-}
-
-// Row chunks of at most 448 rows, split evenly; TB = 64-row tiles per workgroup.
+// Row chunks of at most 448 rows, split evenly; TB = 64-row tiles per
+// workgroup.  One or two tiles (weight streaming): 64-wide slices, deep ring.
+// More: 32-wide slices, three stages, copies spread over the MFMAs.
 hipError_t launch_head_mf32_any(const HeadParams& p, hipStream_t s) {
   const int nc = (p.M + 447) / 448;
   const int rows = (p.M + nc - 1) / nc;
   const int tb = (rows + 63) / 64;
-  static const int bk_small = head_tune("DMTP_HEAD_BK_SMALL", 64);
-  static const int bk_big = head_tune("DMTP_HEAD_BK_BIG", 64);
-  const int bk = tb <= 2 ? bk_small : bk_big;
-  return bk == 64 ? launch_head_mf32_bk<64>(p, nc, tb, s) : launch_head_mf32_bk<32>(p, nc, tb, s);
+  static const int big = head_tune("DMTP_HEAD_BIG", 0);
+  switch (tb) {
+    case 1: return launch_head_mf32<1, 64>(p, nc, s);
+    case 2: return launch_head_mf32<2, 64>(p, nc, s);
+    case 3: return launch_head_mf32<3, 32, 3>(p, nc, s);
+    case 4: return launch_head_mf32<4, 32, 3>(p, nc, s);
+    case 5: return launch_head_mf32<5, 32, 3>(p, nc, s);
+    case 6: return launch_head_mf32<6, 32, 3>(p, nc, s);
+    default:
+      if (big == 1) return launch_head_mf32<7, 32, 4>(p, nc, s);
+      if (big == 2) return launch_head_mf32<7, 64, 2>(p, nc, s);
+      return launch_head_mf32<7, 32, 3>(p, nc, s);
+  }
 }
 
 // Row chunks of at most 448 rows, split evenly; T = 16-row tiles per wave.

@@ -170,13 +170,38 @@ def test_lm_head_sampled_planted_and_stored(dm, dt):
     print("exempt", n_ex)
 
 
+@pytest.mark.parametrize("M", [200, 448, 901])
+def test_lm_head_many_rows(dm, M):
+    # 64-row tiles per workgroup from 4 to 7, one and several row chunks, a
+    # ragged vocabulary tile (7001 = 54 * 128 + 89)
+    H, V = 512, 7001
+    print(f"lm_head many rows M={M}", flush=True)
+    W, hid, g, rows, strided, x = _head_case(31 + M, H, V, "bf16", M_norm=0, M_rows=M, M_strided=0)
+    tok = torch.empty(M, dtype=torch.int32, device="cuda")
+    lse = torch.empty(M, dtype=torch.float32, device="cuda")
+    rmax = torch.empty(M, dtype=torch.float32, device="cuda")
+    gap = torch.empty(M, dtype=torch.float32, device="cuda")
+    dm.lm_head(_t(W, torch.bfloat16), [dm.head_segment(_t(rows, torch.bfloat16))], tok, lse=lse,
+               row_max=rmax, gap=gap)
+    ref = odm.lm_head(x, W.astype(np.float64), np.zeros(M))
+    got = tok.cpu().numpy()
+    bad = np.nonzero(got != ref.token)[0]
+    assert all(ref.margin[m] < NEAR_TIE for m in bad), [(m, got[m], ref.token[m]) for m in bad[:5]]
+    assert max_rel(lse.cpu().numpy(), ref.lse) < 1e-5
+    assert max_rel(rmax.cpu().numpy(), ref.row_max) < 1e-4
+    print("  exempt:", len(bad), "of", M)
+
+
 def test_lm_head_rows_do_not_depend_on_the_batch(dm):
+    # 448 rows run 7 tiles per workgroup; 1, 200 and 385 rows take other tile
+    # counts and slice widths, which must not change any row's result
     H, V = 2048, 20000
-    W, hid, g, rows, strided, x = _head_case(21, H, V, "bf16", M_norm=0, M_rows=100, M_strided=0)
+    W, hid, g, rows, strided, x = _head_case(21, H, V, "bf16", M_norm=0, M_rows=448, M_strided=0)
     Wt = _t(W, torch.bfloat16)
     X = _t(rows, torch.bfloat16)
     outs = {}
-    for name, sl in (("all", slice(0, 100)), ("one", slice(37, 38)), ("tail", slice(63, 100))):
+    for name, sl in (("all", slice(0, 448)), ("one", slice(37, 38)), ("tail", slice(63, 448)),
+                     ("mid", slice(100, 300))):
         xs = X[sl].contiguous()
         n = xs.shape[0]
         tok = torch.empty(n, dtype=torch.int32, device="cuda")
@@ -186,6 +211,8 @@ def test_lm_head_rows_do_not_depend_on_the_batch(dm):
     assert outs["one"][0][0] == outs["all"][0][37] and outs["one"][1][0] == outs["all"][1][37]
     np.testing.assert_array_equal(outs["tail"][1], outs["all"][1][63:])
     np.testing.assert_array_equal(outs["tail"][0], outs["all"][0][63:])
+    np.testing.assert_array_equal(outs["mid"][1], outs["all"][1][100:300])
+    np.testing.assert_array_equal(outs["mid"][0], outs["all"][0][100:300])
 
 
 # ---------------------------------------------------------------- block draft
