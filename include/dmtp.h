@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define DMTP_ABI_VERSION 1
+#define DMTP_ABI_VERSION 2
 
 enum dmtp_status {
   DMTP_OK = 0,
@@ -208,6 +208,14 @@ typedef struct {
   float* row_max;             /* [M] or NULL */
   float* lse;                 /* [M] or NULL */
   float* gap;                 /* [M] or NULL */
+  /* Optional profiling hook: when both are set (hipEvent_t handles created
+   * with timing enabled), the bf16 vocabulary GEMM kernel of this call is
+   * launched with them as its start and stop events, taken from that
+   * kernel's own dispatch, so hipEventElapsedTime(start, stop) is its
+   * duration and no extra command enters the stream.  Ignored by the float32
+   * path (which then records neither). */
+  void* gemm_start_event;
+  void* gemm_stop_event;
 } dmtp_head_desc;
 
 size_t dmtp_lm_head_ws(const dmtp_head_desc* d);

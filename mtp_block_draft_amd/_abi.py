@@ -61,7 +61,8 @@ class HeadDesc(ctypes.Structure):
                 ("temperature", c_void_p), ("draw_key", c_void_p), ("seed", c_uint64),
                 ("plant_row", c_void_p), ("store_row", c_void_p), ("logits", c_void_p),
                 ("logits_rows", c_int32), ("prepared", c_void_p), ("token", c_void_p),
-                ("row_max", c_void_p), ("lse", c_void_p), ("gap", c_void_p)]
+                ("row_max", c_void_p), ("lse", c_void_p), ("gap", c_void_p),
+                ("gemm_start_event", c_void_p), ("gemm_stop_event", c_void_p)]
 
 
 class VerifyDesc(ctypes.Structure):

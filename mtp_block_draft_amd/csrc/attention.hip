@@ -18,19 +18,12 @@
 // single exchange with lane l ^ 32; O^T += V^T P^T takes the V^T operand from
 // the transposing LDS read (ds_read_b64_tr_b16) and P^T straight from the
 // softmax registers.  The float32 K/V path keeps the workgroup kernel.
-#include <cstdlib>
-
 #include "dma.hpp"
 #include "kernels.hpp"
 
 namespace dmtp {
 
 namespace {
-
-int attn_tune(const char* name, int dflt) {
-  const char* e = getenv(name);
-  return e ? atoi(e) : dflt;
-}
 
 constexpr int kAttnThreads = 256;
 constexpr int KT = 64;  // keys per LDS tile
@@ -482,69 +475,114 @@ __global__ __launch_bounds__(64) void attn_wave_kernel(
 // Merge the chunk partials and the S block keys; o [B * S, Hq * D] as bf16
 // planes (hi at o, lo at o + o_pst).
 // One wave per query row (rows r = 4 blockIdx.y + wave of kv head blockIdx.x);
-// lane l owns dims l, l + 64.  The block-key scores are exact float32 dot
-// products; the chunk weights exp(m_c - M) and the block weights are shared
-// through the wave's slice of LDS.
+// lane l owns dims l (and l + 64 when D = 128).  Every global load that does
+// not depend on another one -- the query row, the chunk maxima and sums, the
+// first CB chunk partials, and the block keys and values (staged once in LDS
+// for the workgroup's four rows) -- is issued up front, so that a row costs
+// about one memory latency instead of one per step.  The block-key scores are
+// exact float32 dot products; chunk weights exp(m_c - M) are shared through
+// the wave's slice of LDS, block weights by lane reads.
+template <int D>
 __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(
     const float* __restrict__ q, const float* __restrict__ kb, const float* __restrict__ vb,
-    const float* __restrict__ part_o, const float* __restrict__ part_ml, int Hkv, int G, int S, int D,
+    const float* __restrict__ part_o, const float* __restrict__ part_ml, int Hkv, int G, int S,
     int NQP, int n_chunks, float scale, uint16_t* __restrict__ o, size_t o_pst) {
+  constexpr int DL = D / kWave;   // dims per lane
+  constexpr int CB = 16;          // chunk partials in flight per batch
+  extern __shared__ __attribute__((aligned(16))) float kvs[];   // [2][S][D] block keys, values
   __shared__ float w_chunk[4][256];
-  __shared__ float w_blk[4][64];
   const int kvh = blockIdx.x % Hkv, b = blockIdx.x / Hkv;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int NQ = S * G;
   const int r = blockIdx.y * 4 + wave;
-  if (r >= NQ) return;
+  const bool live = r < NQ;
+  const int rr = live ? r : NQ - 1;   // a wave past the last row loads in range and stores nothing
   const size_t bh = (size_t)b * Hkv + kvh;
-  const float* qr = q + (bh * NQ + r) * D;
-  const float* kbg = kb + bh * S * D;
-  const float* vbg = vb + bh * S * D;
-  const float q0 = qr[lane], q1 = D > 64 ? qr[lane + 64] : 0.f;
-  float M = -INFINITY;
-  for (int j = 0; j < S; ++j) {
-    float part = q0 * kbg[(size_t)j * D + lane];
-    if (D > 64) part = fmaf(q1, kbg[(size_t)j * D + lane + 64], part);
-    const float sj = wave_sum(part) * scale;
-    if (lane == 0) w_blk[wave][j] = sj;
-    M = fmaxf(M, sj);
-  }
+
+  float qv[DL];
+#pragma unroll
+  for (int i = 0; i < DL; ++i) qv[i] = q[(bh * NQ + rr) * D + lane + kWave * i];
   const float* ml = part_ml + bh * n_chunks * 2 * NQP;
-  for (int c = lane; c < n_chunks; c += kWave) M = fmaxf(M, ml[(size_t)c * 2 * NQP + r]);
+  float mc[4], lc[4];   // chunks lane + 64 i (at most 256)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = lane + kWave * i;
+    mc[i] = c < n_chunks ? ml[(size_t)c * 2 * NQP + rr] : -INFINITY;
+    lc[i] = c < n_chunks ? ml[(size_t)c * 2 * NQP + NQP + rr] : 0.f;
+  }
+  // chunk c of this row at po + c * NQP * D; an empty chunk never wrote its
+  // partial, which is read here but weighted out below
+  const float* po = part_o + (bh * n_chunks * NQP + rr) * D + lane;
+  const size_t cstride = (size_t)NQP * D;
+  float pv[CB][DL];
+#pragma unroll
+  for (int c = 0; c < CB; ++c)
+#pragma unroll
+    for (int i = 0; i < DL; ++i) pv[c][i] = c < n_chunks ? po[c * cstride + kWave * i] : 0.f;
+  {
+    const float4* k4 = (const float4*)(kb + bh * S * D);
+    const float4* v4 = (const float4*)(vb + bh * S * D);
+    float4* s4 = (float4*)kvs;
+    const int n4 = S * D / 4;
+    for (int e = threadIdx.x; e < n4; e += kAttnThreads) {
+      s4[e] = k4[e];
+      s4[n4 + e] = v4[e];
+    }
+  }
+  __syncthreads();
+  if (!live) return;
+
+  float M = fmaxf(fmaxf(mc[0], mc[1]), fmaxf(mc[2], mc[3]));
+  float s_lane = -INFINITY;   // lane j < S: score of block key j
+  for (int j = 0; j < S; ++j) {
+    float part = 0.f;
+#pragma unroll
+    for (int i = 0; i < DL; ++i) part = fmaf(qv[i], kvs[j * D + lane + kWave * i], part);
+    const float sj = wave_sum(part) * scale;
+    s_lane = lane == j ? sj : s_lane;
+  }
+  M = fmaxf(M, s_lane);
+#pragma unroll
   for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, shfl_xor(M, off));
   float Lsum = 0.f;
-  for (int c = lane; c < n_chunks; c += kWave) {
-    const float mc = ml[(size_t)c * 2 * NQP + r];
-    const float w = mc == -INFINITY ? 0.f : expf(mc - M);
-    w_chunk[wave][c] = w;
-    Lsum += w * ml[(size_t)c * 2 * NQP + NQP + r];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float w = mc[i] == -INFINITY ? 0.f : expf(mc[i] - M);
+    w_chunk[wave][lane + kWave * i] = w;
+    Lsum = fmaf(w, lc[i], Lsum);
   }
-  Lsum = wave_sum(Lsum);
+  const float wb = lane < S ? expf(s_lane - M) : 0.f;
+  Lsum = wave_sum(Lsum + wb);
   __threadfence_block();
   __builtin_amdgcn_wave_barrier();
-  float blk = 0.f;
-  for (int j = lane; j < S; j += kWave) {
-    const float w = expf(w_blk[wave][j] - M);
-    w_blk[wave][j] = w;
-    blk += w;
-  }
-  Lsum += wave_sum(blk);
-  __threadfence_block();
-  __builtin_amdgcn_wave_barrier();
-  const float inv_l = 1.0f / Lsum;
-  const int s = r / G, g = r % G;
-  const size_t orow = ((size_t)b * S + s) * ((size_t)Hkv * G * D) + ((size_t)kvh * G + g) * D;
-  for (int k = lane; k < D; k += kWave) {
-    float acc = 0.f;
-#pragma unroll 4
-    for (int c = 0; c < n_chunks; ++c) {
-      // an empty chunk has weight 0 and never wrote its partial O
-      const float w = w_chunk[wave][c];
-      if (w != 0.f) acc = fmaf(w, part_o[((bh * n_chunks + c) * NQP + r) * D + k], acc);
+
+  float acc[DL];
+#pragma unroll
+  for (int i = 0; i < DL; ++i) acc[i] = 0.f;
+  for (int c0 = 0; c0 < n_chunks; c0 += CB) {
+    if (c0 > 0)
+#pragma unroll
+      for (int c = 0; c < CB; ++c)
+#pragma unroll
+        for (int i = 0; i < DL; ++i)
+          pv[c][i] = c0 + c < n_chunks ? po[(c0 + c) * cstride + kWave * i] : 0.f;
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+      const float w = c0 + c < n_chunks ? w_chunk[wave][c0 + c] : 0.f;
+#pragma unroll
+      for (int i = 0; i < DL; ++i) acc[i] = w != 0.f ? fmaf(w, pv[c][i], acc[i]) : acc[i];
     }
-    for (int j = 0; j < S; ++j) acc = fmaf(w_blk[wave][j], vbg[(size_t)j * D + k], acc);
-    store_planes(o, o_pst, orow + k, acc * inv_l);
   }
+  for (int j = 0; j < S; ++j) {
+    const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wb), j));
+#pragma unroll
+    for (int i = 0; i < DL; ++i) acc[i] = fmaf(w, kvs[S * D + j * D + lane + kWave * i], acc[i]);
+  }
+  const float inv_l = 1.0f / Lsum;
+  const int sl = r / G, g = r % G;
+  const size_t orow = ((size_t)b * S + sl) * ((size_t)Hkv * G * D) + ((size_t)kvh * G + g) * D;
+#pragma unroll
+  for (int i = 0; i < DL; ++i) store_planes(o, o_pst, orow + lane + kWave * i, acc[i] * inv_l);
 }
 
 template <int RT, int D, int KVP>
@@ -630,7 +668,7 @@ AttnPlan attn_plan(int B, int Hq, int Hkv, int S, int d, int max_ctx, int window
     // at most 256 chunks per sequence for the combine
     const long keys = (long)(ctx_rows > 0 ? ctx_rows : (long)B * eff);
     const long tiles = keys * Hkv * (p.nqp / 32);
-    static const long target = attn_tune("DMTP_ATTN_WAVES", 1536);
+    constexpr long target = 1536;
     long per = (tiles + target * 32 - 1) / (target * 32);
     if (per < 4) per = 4;
     int chunk = (int)(32 * per);
@@ -679,10 +717,7 @@ template <int D>
 hipError_t launch_wave(const AttnPlan& p, const float* q, const void* ck, const void* cv,
                        const int32_t* cu, int ctx_rows, float* po, float* pml, float scale,
                        hipStream_t s) {
-  static const int nbuf = attn_tune("DMTP_ATTN_NBUF", 2);
-  if (nbuf == 2) return launch_wave_n<D, 2>(p, q, ck, cv, cu, ctx_rows, po, pml, scale, s);
-  if (nbuf == 3) return launch_wave_n<D, 3>(p, q, ck, cv, cu, ctx_rows, po, pml, scale, s);
-  return launch_wave_n<D, 4>(p, q, ck, cv, cu, ctx_rows, po, pml, scale, s);
+  return launch_wave_n<D, 2>(p, q, ck, cv, cu, ctx_rows, po, pml, scale, s);
 }
 
 hipError_t attention(const AttnPlan& p, const float* q, const float* kb, const float* vb,
@@ -704,9 +739,15 @@ hipError_t attention(const AttnPlan& p, const float* q, const float* kb, const f
                   : dispatch_rt<128, 2>(p, q, ctx_k, ctx_v, cu_ctx, cr, po, pml, scale, s);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(p.B * p.Hkv, (p.NQ + 3) / 4), dim3(kAttnThreads), 0, s,
-                     q, kb, vb, po, pml, p.Hkv, p.G, p.S, p.d, nqp, p.n_chunks, scale, o,
-                     (size_t)p.B * p.S * p.Hkv * p.G * p.d);
+  const dim3 cgrid(p.B * p.Hkv, (p.NQ + 3) / 4);
+  const size_t clds = (size_t)2 * p.S * p.d * sizeof(float);
+  const size_t o_pst = (size_t)p.B * p.S * p.Hkv * p.G * p.d;
+  if (p.d == 64)
+    hipLaunchKernelGGL(attn_combine_kernel<64>, cgrid, dim3(kAttnThreads), clds, s, q, kb, vb, po, pml,
+                       p.Hkv, p.G, p.S, nqp, p.n_chunks, scale, o, o_pst);
+  else
+    hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, dim3(kAttnThreads), clds, s, q, kb, vb, po,
+                       pml, p.Hkv, p.G, p.S, nqp, p.n_chunks, scale, o, o_pst);
   return hipGetLastError();
 }
 

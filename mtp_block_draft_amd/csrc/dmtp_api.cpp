@@ -358,7 +358,7 @@ const char* dmtp_status_str(int s) {
   }
 }
 
-const char* dmtp_version(void) { return "dmtp 0.1.0 (gfx950, ABI 1)"; }
+const char* dmtp_version(void) { return "dmtp 0.2.0 (gfx950, ABI 2)"; }
 
 size_t dmtp_struct_size(int which) {
   switch (which) {

@@ -26,25 +26,55 @@ __device__ double block_sum(double v, double* red) {
 
 // value(m, n .. n + 3) of a GEMM result: the finished row when it was not split
 // over K, else R + (part[0] + part[1] + ...), the order the reduction uses.
-__device__ __forceinline__ float4 split_load4(const SplitOut& o, int m, int n) {
-  if (o.splits == 1) return *(const float4*)(o.C + (size_t)m * o.ldc + n);
+// split_issue4 starts the loads of the first Z partials (and of R) without
+// waiting for them; split_finish4 adds them in that order, loading any splits
+// past Z itself.  Issuing every load of a row before the first sum keeps one
+// memory latency per row instead of one per split.
+template <int Z>
+struct SplitAcc {
+  float4 t[Z];
+  float4 r;
+};
+
+template <int Z>
+__device__ __forceinline__ void split_issue4(const SplitOut& o, int m, int n, SplitAcc<Z>& a) {
+  if (o.splits == 1) {
+    a.t[0] = *(const float4*)(o.C + (size_t)m * o.ldc + n);
+    return;
+  }
   const size_t mn = (size_t)m * o.N + n, plane = (size_t)o.M * o.N;
-  float4 s = *(const float4*)(o.part + mn);
-  for (int z = 1; z < o.splits; ++z) {
-    const float4 v = *(const float4*)(o.part + z * plane + mn);
-    s.x += v.x;
-    s.y += v.y;
-    s.z += v.z;
-    s.w += v.w;
+#pragma unroll
+  for (int z = 0; z < Z; ++z)
+    if (z < o.splits) a.t[z] = *(const float4*)(o.part + z * plane + mn);
+  if (o.R) a.r = *(const float4*)(o.R + (size_t)m * o.ldr + n);
+}
+
+__device__ __forceinline__ void add4(float4& s, const float4& v) {
+  s.x += v.x;
+  s.y += v.y;
+  s.z += v.z;
+  s.w += v.w;
+}
+
+template <int Z>
+__device__ __forceinline__ float4 split_finish4(const SplitOut& o, int m, int n, const SplitAcc<Z>& a) {
+  if (o.splits == 1) return a.t[0];
+  float4 s = a.t[0];
+#pragma unroll
+  for (int z = 1; z < Z; ++z)
+    if (z < o.splits) add4(s, a.t[z]);
+  if (o.splits > Z) {
+    const size_t mn = (size_t)m * o.N + n, plane = (size_t)o.M * o.N;
+    for (int z = Z; z < o.splits; ++z) add4(s, *(const float4*)(o.part + z * plane + mn));
   }
-  if (o.R) {
-    const float4 b = *(const float4*)(o.R + (size_t)m * o.ldr + n);
-    s.x = b.x + s.x;
-    s.y = b.y + s.y;
-    s.z = b.z + s.z;
-    s.w = b.w + s.w;
-  }
+  if (o.R) s = make_float4(a.r.x + s.x, a.r.y + s.y, a.r.z + s.z, a.r.w + s.w);
   return s;
+}
+
+// splits held in flight per float4 for a thread that fetches V4 of them
+template <int V4>
+constexpr int zb_of() {
+  return V4 >= 8 ? 1 : 8 / V4;
 }
 
 __device__ __forceinline__ double sumsq4(const float4& v) {
@@ -53,8 +83,7 @@ __device__ __forceinline__ double sumsq4(const float4& v) {
 
 // Planes of y = x * inv * g for four consecutive elements at index i.
 __device__ __forceinline__ void store_norm4(uint16_t* y, size_t pst, size_t i, const float4& x,
-                                            double inv, const float* g) {
-  const float4 gg = *(const float4*)g;
+                                            double inv, const float4& gg) {
   store_planes(y, pst, i + 0, (float)((double)x.x * inv * gg.x));
   store_planes(y, pst, i + 1, (float)((double)x.y * inv * gg.y));
   store_planes(y, pst, i + 2, (float)((double)x.z * inv * gg.z));
@@ -70,13 +99,22 @@ __global__ __launch_bounds__(kRowThreads) void residual_rmsnorm_kernel(SplitOut 
                                                                        size_t pst, int H) {
   __shared__ double red[kRowThreads / kWave];
   const int m = blockIdx.x;
-  float4 v[V4];
+  float4 v[V4], gv[V4];
+  SplitAcc<zb_of<V4>()> acc[V4];
+#pragma unroll
+  for (int k = 0; k < V4; ++k) {
+    const int n = 4 * (threadIdx.x + kRowThreads * k);
+    if (n < H) {
+      split_issue4(o, m, n, acc[k]);
+      gv[k] = *(const float4*)(g + n);
+    }
+  }
   double ss = 0.0;
 #pragma unroll
   for (int k = 0; k < V4; ++k) {
     const int n = 4 * (threadIdx.x + kRowThreads * k);
     if (n < H) {
-      v[k] = split_load4(o, m, n);
+      v[k] = split_finish4(o, m, n, acc[k]);
       ss += sumsq4(v[k]);
     }
   }
@@ -87,7 +125,7 @@ __global__ __launch_bounds__(kRowThreads) void residual_rmsnorm_kernel(SplitOut 
     const int n = 4 * (threadIdx.x + kRowThreads * k);
     if (n < H) {
       if (write_x) *(float4*)(X + (size_t)m * ldx + n) = v[k];
-      store_norm4(y, pst, (size_t)m * H + n, v[k], inv, g + n);
+      store_norm4(y, pst, (size_t)m * H + n, v[k], inv, gv[k]);
     }
   }
 }
@@ -100,13 +138,22 @@ __global__ __launch_bounds__(kRowThreads) void final_norm_kernel(SplitOut o, con
   __shared__ double red[kRowThreads / kWave];
   const int b = blockIdx.x / Km1, j = blockIdx.x % Km1;
   const int m = b * S + n_anchor + j;
-  float4 v[V4];
+  float4 v[V4], gv[V4];
+  SplitAcc<zb_of<V4>()> acc[V4];
+#pragma unroll
+  for (int k = 0; k < V4; ++k) {
+    const int n = 4 * (threadIdx.x + kRowThreads * k);
+    if (n < H) {
+      split_issue4(o, m, n, acc[k]);
+      gv[k] = *(const float4*)(g + n);
+    }
+  }
   double ss = 0.0;
 #pragma unroll
   for (int k = 0; k < V4; ++k) {
     const int n = 4 * (threadIdx.x + kRowThreads * k);
     if (n < H) {
-      v[k] = split_load4(o, m, n);
+      v[k] = split_finish4(o, m, n, acc[k]);
       ss += sumsq4(v[k]);
     }
   }
@@ -117,7 +164,7 @@ __global__ __launch_bounds__(kRowThreads) void final_norm_kernel(SplitOut o, con
   for (int k = 0; k < V4; ++k) {
     const int n = 4 * (threadIdx.x + kRowThreads * k);
     if (n < H) {
-      const float4 gg = *(const float4*)(g + n);
+      const float4 gg = gv[k];
       store_elem(out, dtype, r0 + n + 0, (float)((double)v[k].x * inv * gg.x));
       store_elem(out, dtype, r0 + n + 1, (float)((double)v[k].y * inv * gg.y));
       store_elem(out, dtype, r0 + n + 2, (float)((double)v[k].z * inv * gg.z));
@@ -164,14 +211,29 @@ __global__ __launch_bounds__(kRowThreads) void fuse_prep_kernel(RowSrc x1, RowSr
                                                                 float* __restrict__ out) {
   __shared__ double red[2][kRowThreads / kWave];
   const int r = blockIdx.x;
-  float4 a[V4], c[V4];
-  double s1 = 0.0, s2 = 0.0;
+  // up to 8 float4 per thread, the residual and the gains are loaded with the
+  // rows; longer rows load them in the store loop to stay within registers
+  constexpr bool PRE = V4 <= 8;
+  constexpr int VP = PRE ? V4 : 1;
+  float4 a[V4], c[V4], e[VP], ga[VP], gc[VP];
 #pragma unroll
   for (int k = 0; k < V4; ++k) {
     const int n = 4 * (threadIdx.x + kRowThreads * k);
     if (n < H) {
       a[k] = row_elem4(x1, r, H, n);
       c[k] = row_elem4(x2, r, H, n);
+      if (PRE) {
+        if (has_res) e[k % VP] = row_elem4(res, r, H, n);
+        ga[k % VP] = *(const float4*)(g1 + n);
+        gc[k % VP] = *(const float4*)(g2 + n);
+      }
+    }
+  }
+  double s1 = 0.0, s2 = 0.0;
+#pragma unroll
+  for (int k = 0; k < V4; ++k) {
+    const int n = 4 * (threadIdx.x + kRowThreads * k);
+    if (n < H) {
       s1 += sumsq4(a[k]);
       s2 += sumsq4(c[k]);
     }
@@ -195,9 +257,15 @@ __global__ __launch_bounds__(kRowThreads) void fuse_prep_kernel(RowSrc x1, RowSr
   for (int k = 0; k < V4; ++k) {
     const int n = 4 * (threadIdx.x + kRowThreads * k);
     if (n < H) {
-      store_norm4(cat, pst, c0 + n, a[k], i1, g1 + n);
-      store_norm4(cat, pst, c0 + H + n, c[k], i2, g2 + n);
-      if (has_res) *(float4*)(out + (size_t)r * H + n) = row_elem4(res, r, H, n);
+      if (PRE) {
+        store_norm4(cat, pst, c0 + n, a[k], i1, ga[k % VP]);
+        store_norm4(cat, pst, c0 + H + n, c[k], i2, gc[k % VP]);
+        if (has_res) *(float4*)(out + (size_t)r * H + n) = e[k % VP];
+      } else {
+        store_norm4(cat, pst, c0 + n, a[k], i1, *(const float4*)(g1 + n));
+        store_norm4(cat, pst, c0 + H + n, c[k], i2, *(const float4*)(g2 + n));
+        if (has_res) *(float4*)(out + (size_t)r * H + n) = row_elem4(res, r, H, n);
+      }
     }
   }
 }
@@ -246,7 +314,10 @@ __global__ __launch_bounds__(256) void rope_split_kernel(SplitOut o, const int32
   const int quads = (Hq + Hkv) * half / 4;
   for (int e = threadIdx.x; e < quads; e += blockDim.x) {
     const int h = (4 * e) / half, i0 = (4 * e) % half;
-    const float4 x1 = split_load4(o, m, h * d + i0), x2 = split_load4(o, m, h * d + i0 + half);
+    SplitAcc<4> p1, p2;
+    split_issue4(o, m, h * d + i0, p1);
+    split_issue4(o, m, h * d + i0 + half, p2);
+    const float4 x1 = split_finish4(o, m, h * d + i0, p1), x2 = split_finish4(o, m, h * d + i0 + half, p2);
     const float a1[4] = {x1.x, x1.y, x1.z, x1.w}, a2[4] = {x2.x, x2.y, x2.z, x2.w};
     float r1[4], r2[4];
 #pragma unroll
@@ -262,7 +333,9 @@ __global__ __launch_bounds__(256) void rope_split_kernel(SplitOut o, const int32
   }
   for (int e = threadIdx.x; e < Hkv * d / 4; e += blockDim.x) {
     const int h = (4 * e) / d, i = (4 * e) % d;
-    *(float4*)(vb + (((size_t)b * Hkv + h) * S + s) * d + i) = split_load4(o, m, (Hq + Hkv) * d + 4 * e);
+    SplitAcc<8> pv;
+    split_issue4(o, m, (Hq + Hkv) * d + 4 * e, pv);
+    *(float4*)(vb + (((size_t)b * Hkv + h) * S + s) * d + i) = split_finish4(o, m, (Hq + Hkv) * d + 4 * e, pv);
   }
 }
 
@@ -272,7 +345,10 @@ __global__ void swiglu_kernel(SplitOut gs, SplitOut us, uint16_t* __restrict__ a
   for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n4;
        e += (size_t)gridDim.x * blockDim.x) {
     const int m = (int)(4 * e / F), n = (int)(4 * e % F);
-    const float4 g = split_load4(gs, m, n), u = split_load4(us, m, n);
+    SplitAcc<4> pg, pu;
+    split_issue4(gs, m, n, pg);
+    split_issue4(us, m, n, pu);
+    const float4 g = split_finish4(gs, m, n, pg), u = split_finish4(us, m, n, pu);
     const size_t i = 4 * e;
     store_planes(a, pst, i + 0, g.x / (1.0f + expf(-g.x)) * u.x);
     store_planes(a, pst, i + 1, g.y / (1.0f + expf(-g.y)) * u.y);

@@ -196,23 +196,37 @@ void gemm_dma_kernel(GemmParams p, int n_tiles_n, int n_tiles_m) {
 }
 
 // C = R + sum_z part[z] in the order z = 0, 1, ...; four consecutive columns
-// per thread (N % 4 == 0).
+// per thread (N % 4 == 0).  The partials are loaded sixteen splits at a time,
+// all in flight together, before they are added.
 __global__ void splitk_reduce4(const float* __restrict__ part, int splits, int M, int N, float* C,
                                size_t ldc, const float* R, size_t ldr) {
+  constexpr int ZB = 16;
   const size_t total4 = (size_t)M * N / 4;
+  const size_t zs = (size_t)M * N;
   for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total4;
        e += (size_t)gridDim.x * blockDim.x) {
     const int row = (int)(4 * e / N), col = (int)(4 * e % N);
-    float4 s = *(const float4*)(part + 4 * e);
-    for (int z = 1; z < splits; ++z) {
-      const float4 v = *(const float4*)(part + (size_t)z * M * N + 4 * e);
-      s.x += v.x;
-      s.y += v.y;
-      s.z += v.z;
-      s.w += v.w;
+    const float4 b = R ? *(const float4*)(R + (size_t)row * ldr + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int z0 = 0; z0 < splits; z0 += ZB) {
+      float4 v[ZB];
+#pragma unroll
+      for (int z = 0; z < ZB; ++z)
+        if (z0 + z < splits) v[z] = *(const float4*)(part + (size_t)(z0 + z) * zs + 4 * e);
+#pragma unroll
+      for (int z = 0; z < ZB; ++z)
+        if (z0 + z < splits) {
+          if (z0 + z == 0) {
+            s = v[0];
+          } else {
+            s.x += v[z].x;
+            s.y += v[z].y;
+            s.z += v[z].z;
+            s.w += v[z].w;
+          }
+        }
     }
     if (R) {
-      const float4 b = *(const float4*)(R + (size_t)row * ldr + col);
       s.x = b.x + s.x;
       s.y = b.y + s.y;
       s.z = b.z + s.z;

@@ -12,8 +12,9 @@
 //   plan/scan (only when temperatures are given) Gumbel-max draws over the
 //             stored logits rows of sampled rows, in vocabulary chunks
 //   finalize  token per row: draw, planted row argmax, or argmax
-#include <cstdlib>
 #include <type_traits>
+
+#include <hip/hip_ext.h>
 
 #include "dma.hpp"
 #include "gemm_core.hpp"
@@ -113,7 +114,41 @@ __global__ __launch_bounds__(kPrepThreads) void head_prep_kernel(HeadParams p) {
   const Seg sg = p.seg[si];
   const int H = p.H;
   const size_t orow = (size_t)blockIdx.x * H;
-  if (sg.g) {
+  if (sg.g && H % 4 == 0 && H <= 8 * 4 * kPrepThreads) {
+    // the row and its gains in registers: every load issued before the first use
+    const float* xr = (const float*)sg.x + (size_t)m * sg.ld;
+    float4 xv[8], gv[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int i = 4 * (threadIdx.x + kPrepThreads * k);
+      if (i < H) {
+        xv[k] = *(const float4*)(xr + i);
+        gv[k] = *(const float4*)(sg.g + i);
+      }
+    }
+    double ss = 0.0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (4 * (threadIdx.x + kPrepThreads * k) < H)
+        ss += (double)xv[k].x * xv[k].x + (double)xv[k].y * xv[k].y + (double)xv[k].z * xv[k].z +
+              (double)xv[k].w * xv[k].w;
+    ss = wave_sum(ss);
+    if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = ss;
+    __syncthreads();
+    double t = 0.0;
+    for (int w = 0; w < kPrepThreads / kWave; ++w) t += red[w];
+    const double inv = 1.0 / sqrt(t / H + (double)p.eps);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int i = 4 * (threadIdx.x + kPrepThreads * k);
+      if (i < H) {
+        store_elem(p.prepared, p.dtype, orow + i + 0, (float)((double)xv[k].x * inv * gv[k].x));
+        store_elem(p.prepared, p.dtype, orow + i + 1, (float)((double)xv[k].y * inv * gv[k].y));
+        store_elem(p.prepared, p.dtype, orow + i + 2, (float)((double)xv[k].z * inv * gv[k].z));
+        store_elem(p.prepared, p.dtype, orow + i + 3, (float)((double)xv[k].w * inv * gv[k].w));
+      }
+    }
+  } else if (sg.g) {
     const float* xr = (const float*)sg.x + (size_t)m * sg.ld;
     double ss = 0.0;
     for (int i = threadIdx.x; i < H; i += blockDim.x) ss += (double)xr[i] * xr[i];
@@ -198,484 +233,6 @@ __global__ __launch_bounds__(T::THREADS) void head_gemm_kernel(HeadParams p) {
     for (int w = 1; w < T::WAVES_N; ++w) st = stat_merge(st, wstat[w][lr], it);
     p.part[(size_t)row * p.n_vtiles + blockIdx.x] = st;
   }
-}
-
-// ---- bf16 head GEMM: vocabulary rows on the MFMA row side.
-//
-// Workgroup tile: 128 vocabulary rows x (64 * NBW) head-input rows; wave w owns
-// input rows 64 w .. 64 w + 63 against all 128 vocabulary rows (4 x 2 tiles of
-// 32 x 32).  With the vocabulary on the row side, a lane's accumulators hold
-// 64 logits of each of its two input rows, so the per-row statistics reduce
-// inside the lane and across one lane pair only.  All input rows of a chunk
-// (up to 448) share one pass over W, which is read from HBM once per chunk.
-//
-// Data movement per 128-wide K slice: the W slice (128 x 128, shared by every
-// wave) goes through registers into one of two LDS buffers, 16-byte chunks
-// XOR-swizzled by row, and is fetched two slices ahead; each wave's input-row
-// fragments come straight from L2 into registers one slice ahead (no LDS: no
-// other wave reads them).  Inside a slice, lane half h supplies k = 64 h + 8 kk
-// .. + 7 at step kk, so a lane's eight input-row fragments are 128 contiguous
-// bytes; the W fragments read from LDS use the same k assignment.
-template <int NBW>
-struct HeadBig {
-  static constexpr int BV = 128, BK = 128, BB = 64 * NBW, THREADS = 64 * NBW;
-  static constexpr int KSTEPS = BK / 16;                    // MFMA k-steps per slice
-  static constexpr int W_CH = BV * BK / 8;                  // 16-byte chunks per W slice
-  static constexpr int WPT = (W_CH + THREADS - 1) / THREADS;
-  static constexpr int STAGE = BV * BK;                     // bf16 elements per W buffer
-  static constexpr size_t LDS_BYTES = (size_t)2 * STAGE * 2;
-};
-
-__device__ __forceinline__ int swz64(int r, int c) { return r * 64 + ((c ^ (r & 7)) << 3); }
-// row r, 16-byte chunk c of a [rows][128] bf16 tile, chunks XOR-swizzled by row
-__device__ __forceinline__ int swz128(int r, int c) { return r * 128 + ((c ^ (r & 15)) << 3); }
-
-
-
-template <int NBW>
-__global__ __launch_bounds__(HeadBig<NBW>::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void head_gemm_big_kernel(HeadParams p, int n_mchunks) {
-  typedef HeadBig<NBW> C;
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  const int total = p.n_vtiles * n_mchunks;
-  // Workgroup i runs on XCD i % 8: each XCD gets a contiguous range of
-  // (vocabulary tile, row chunk) pairs, so the row chunks of one vocabulary
-  // tile meet in the same L2.
-  const int per = (total + 7) / 8;
-  const int t = (blockIdx.x % 8) * per + blockIdx.x / 8;
-  if (t >= total) return;
-  const int vt = t / n_mchunks, mc = t % n_mchunks;
-  const int v0 = vt * C::BV, m0 = mc * C::BB;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lr = lane & 31, lk = lane >> 5;
-  const int H = p.H, V = p.V, M = p.M;
-  const uint16_t* __restrict__ W = (const uint16_t*)p.W;
-  const uint16_t* __restrict__ X = (const uint16_t*)p.A;
-  // Loads clamp their row into range instead of branching: rows past V or M
-  // only feed accumulators that the epilogue never reads.
-  const uint16_t* wsrc[C::WPT];
-  int wdst[C::WPT];
-#pragma unroll
-  for (int s = 0; s < C::WPT; ++s) {
-    const int idx = min(tid + s * C::THREADS, C::W_CH - 1);
-    const int r = idx >> 4, c = idx & 15;
-    wsrc[s] = W + (size_t)min(v0 + r, V - 1) * H + 8 * c;
-    wdst[s] = swz128(r, c);
-  }
-  // lane half lk supplies k = 64 lk + 8 kk .. + 7 at step kk of a slice
-  const uint16_t* xp0 = X + (size_t)min(m0 + 64 * wave + lr, M - 1) * H + 64 * lk;
-  const uint16_t* xp1 = X + (size_t)min(m0 + 64 * wave + 32 + lr, M - 1) * H + 64 * lk;
-
-  f32x16_t acc[4][2];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
-
-  auto gload_w = [&](u32x4* wr, int k0) __attribute__((always_inline)) {
-#pragma unroll
-    for (int s = 0; s < C::WPT; ++s) wr[s] = *(const u32x4*)(wsrc[s] + k0);
-  };
-  auto store_w = [&](const u32x4* wr, uint16_t* buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int s = 0; s < C::WPT; ++s) *(u32x4*)(buf + wdst[s]) = wr[s];
-  };
-  auto gload_x = [&](u32x4* x0, u32x4* x1, int k0) __attribute__((always_inline)) {
-#pragma unroll
-    for (int kk = 0; kk < C::KSTEPS; ++kk) {
-      x0[kk] = *(const u32x4*)(xp0 + k0 + 8 * kk);
-      x1[kk] = *(const u32x4*)(xp1 + k0 + 8 * kk);
-    }
-  };
-  auto compute = [&](const uint16_t* cur, const u32x4* x0, const u32x4* x1)
-                     __attribute__((always_inline)) {
-#pragma unroll
-    for (int kk = 0; kk < C::KSTEPS; ++kk) {
-      u32x4 a_[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        a_[u] = *(const u32x4*)(cur + swz128(32 * u + lr, C::KSTEPS * lk + kk));
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        acc[u][0] = mfma32(a_[u], x0[kk], acc[u][0]);
-        acc[u][1] = mfma32(a_[u], x1[kk], acc[u][1]);
-      }
-    }
-  };
-
-  const int nK = H / C::BK;
-  const int last = (nK - 1) * C::BK;
-  uint16_t* buf0 = smem;
-  uint16_t* buf1 = smem + C::STAGE;
-  u32x4 wA[C::WPT], wB[C::WPT];
-  u32x4 xa0[C::KSTEPS], xa1[C::KSTEPS], xb0[C::KSTEPS], xb1[C::KSTEPS];
-  gload_w(wA, 0);
-  gload_w(wB, min(C::BK, last));
-  gload_x(xa0, xa1, 0);
-  store_w(wA, buf0);
-  __syncthreads();
-  // Two K slices per trip keep every register ring index static.  Slice kt
-  // computes from buf0 / xa while W of slice kt + 1 (in wB) and kt + 2 (into
-  // wA) are in flight.  Past the end the loads repeat the last slice, which
-  // nothing reads.
-  int kt = 0;
-  for (; kt + 1 < nK; kt += 2) {
-    gload_w(wA, min((kt + 2) * C::BK, last));
-    gload_x(xb0, xb1, (kt + 1) * C::BK);
-    compute(buf0, xa0, xa1);
-    store_w(wB, buf1);
-    __syncthreads();
-    gload_w(wB, min((kt + 3) * C::BK, last));
-    gload_x(xa0, xa1, min((kt + 2) * C::BK, last));
-    compute(buf1, xb0, xb1);
-    store_w(wA, buf0);
-    __syncthreads();
-  }
-  if (kt < nK) compute(buf0, xa0, xa1);   // odd slice count: the last sits in buf0 / xa
-
-  // ---- epilogue: statistics of each of the lane's two input rows
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int m = m0 + 64 * wave + 32 * j + lr;
-    const bool m_ok = m < M;
-    const float it = m_ok ? inv_temp(p.temperature, m) : 1.f;
-    int srow = (m_ok && p.store_row) ? p.store_row[m] : -1;
-    if (srow >= p.logits_rows) srow = -1;
-    Top2 tp = top2_empty();
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int v = v0 + 32 * u + 8 * (i >> 2) + 4 * lk + (i & 3);
-        if (v < V) top2_push(tp, acc[u][j][i], v);
-      }
-    float sum = 0.f;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int v = v0 + 32 * u + 8 * (i >> 2) + 4 * lk + (i & 3);
-        if (v < V) sum += expf((acc[u][j][i] - tp.v1) * it);
-      }
-    if (srow >= 0) {
-      float* dst = p.logits + (size_t)srow * V;
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int v = v0 + 32 * u + 8 * (i >> 2) + 4 * lk + (i & 3);
-          if (v < V) dst[v] = acc[u][j][i];
-        }
-    }
-    RowStat st{tp.v1, sum, tp.i1, tp.v2};
-    RowStat o;
-    o.m = shfl_xor(st.m, 32);
-    o.s = shfl_xor(st.s, 32);
-    o.idx = shfl_xor(st.idx, 32);
-    o.v2 = shfl_xor(st.v2, 32);
-    st = stat_merge(st, o, it);
-    if (lk == 0 && m_ok) p.part[(size_t)m * p.n_vtiles + vt] = st;
-  }
-}
-
-// ---- bf16 head GEMM for at most 64 head-input rows (the MTP candidate rows).
-//
-// Weight-streaming and HBM-bound: every wave owns 128 vocabulary rows and
-// reads them straight from HBM into registers in MFMA fragment order (64
-// contiguous bytes per lane and row per half K slice, two in flight); the few input rows are fragments read from L2.  No LDS and no
-// barriers, so all ~1200 waves of a 151936-row vocabulary are resident at once
-// and keep enough bytes in flight to cover HBM latency.  The epilogue is the
-// one of the big kernel (same partial layout).
-template <int NB>   // 32-row input tiles: 1 (M <= 32) or 2 (M <= 64)
-__global__ __launch_bounds__(256) void head_gemm_skinny_kernel(HeadParams p) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int vt = blockIdx.x * 4 + wave;
-  if (vt >= p.n_vtiles) return;
-  const int lr = lane & 31, lk = lane >> 5;
-  const int H = p.H, V = p.V, M = p.M;
-  const int v0 = vt * 128;
-  const uint16_t* __restrict__ W = (const uint16_t*)p.W;
-  const uint16_t* __restrict__ X = (const uint16_t*)p.A;
-  // Same k grouping per MFMA as the big kernel (lane half lk supplies
-  // k = 128 s + 64 lk + 8 kk .. + 7 at step kk of slice s), issued in two
-  // half-slices of four steps, so every row gets bit-identical logits
-  // whichever kernel its launch size selects.
-  const uint16_t* wp[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) wp[u] = W + (size_t)min(v0 + 32 * u + lr, V - 1) * H + 64 * lk;
-  const uint16_t* xp[NB];
-#pragma unroll
-  for (int j = 0; j < NB; ++j) xp[j] = X + (size_t)min(32 * j + lr, M - 1) * H + 64 * lk;
-
-  f32x16_t acc[4][NB];
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[u][j][i] = 0.f;
-
-  auto load = [&](u32x4 (&w)[4][4], u32x4 (&x)[NB][4], int k0) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) w[u][kk] = *(const u32x4*)(wp[u] + k0 + 8 * kk);
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) x[j][kk] = *(const u32x4*)(xp[j] + k0 + 8 * kk);
-  };
-  auto compute = [&](const u32x4 (&w)[4][4], const u32x4 (&x)[NB][4]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int j = 0; j < NB; ++j) acc[u][j] = mfma32(w[u][kk], x[j][kk], acc[u][j]);
-  };
-  // half-slice hs covers steps 4 (hs & 1) .. + 3 of slice hs / 2
-  auto k_of = [](int hs) { return 128 * (hs >> 1) + 32 * (hs & 1); };
-  const int nH = H / 64;            // half-slices (H is a multiple of 128)
-  u32x4 wa[4][4], wb[4][4], xa[NB][4], xb[NB][4];
-  load(wa, xa, 0);
-  for (int hs = 0; hs < nH; hs += 2) {
-    load(wb, xb, k_of(hs + 1));
-    compute(wa, xa);
-    load(wa, xa, k_of(min(hs + 2, nH - 1)));
-    compute(wb, xb);
-  }
-
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    const int m = 32 * j + lr;
-    const bool m_ok = m < M;
-    const float it = m_ok ? inv_temp(p.temperature, m) : 1.f;
-    int srow = (m_ok && p.store_row) ? p.store_row[m] : -1;
-    if (srow >= p.logits_rows) srow = -1;
-    Top2 tp = top2_empty();
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int v = v0 + 32 * u + 8 * (i >> 2) + 4 * lk + (i & 3);
-        if (v < V) top2_push(tp, acc[u][j][i], v);
-      }
-    float sum = 0.f;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int v = v0 + 32 * u + 8 * (i >> 2) + 4 * lk + (i & 3);
-        if (v < V) sum += expf((acc[u][j][i] - tp.v1) * it);
-      }
-    if (srow >= 0) {
-      float* dst = p.logits + (size_t)srow * V;
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int v = v0 + 32 * u + 8 * (i >> 2) + 4 * lk + (i & 3);
-          if (v < V) dst[v] = acc[u][j][i];
-        }
-    }
-    RowStat st{tp.v1, sum, tp.i1, tp.v2};
-    RowStat o;
-    o.m = shfl_xor(st.m, 32);
-    o.s = shfl_xor(st.s, 32);
-    o.idx = shfl_xor(st.idx, 32);
-    o.v2 = shfl_xor(st.v2, 32);
-    st = stat_merge(st, o, it);
-    if (lk == 0 && m_ok) p.part[(size_t)m * p.n_vtiles + vt] = st;
-  }
-}
-
-// ---- bf16 head GEMM, LDS-DMA version.
-//
-// Workgroup: 4 waves, 128 vocabulary rows x 64 T head-input rows (a row chunk);
-// wave w computes the 128 vocabulary rows against its own 16 T input rows with
-// 16 x 16 x 32 MFMAs (8 x T accumulator tiles, held in AGPRs).  T = 7 covers
-// 448 rows, the draft + target rows of a batch-32 round, without padding.
-//
-// K runs in 32-wide slices through a ring of four LDS stages filled by
-// global_load_lds_dwordx4 (no register staging): each instruction moves 64 x 16
-// bytes, and lane i fetches the 16-byte chunk that belongs at LDS position i of
-// the XOR-swizzled tile, so every instruction reads whole 64-byte row segments
-// from memory.  Slice s + 3 is requested while slice s is computed; a wave waits
-// only for its own requests of slice s (s_waitcnt vmcnt) and a barrier makes the
-// other waves' parts visible.  Vocabulary rows are on the MFMA row side, so the
-// per-row statistics reduce inside a lane (32 logits per input row and lane)
-// and across the four lanes that share an input row.
-template <int T>
-struct HeadLds {
-  static constexpr int BV = 128, BK = 32, NBUF = 4, WAVES = 4, THREADS = 256;
-  static constexpr int BB = 64 * T;                 // input rows per chunk
-  static constexpr int W_INSTR = BV * BK / 8 / 64;  // 16-byte DMA instructions per slice (8)
-  static constexpr int X_INSTR = BB * BK / 8 / 64;  // (4 T)
-  static constexpr int PER_WAVE = (W_INSTR + X_INSTR) / WAVES;   // 2 + T
-  static constexpr int STAGE = (BV + BB) * BK;      // bf16 elements per stage
-  static constexpr size_t LDS_BYTES = (size_t)NBUF * STAGE * 2;
-};
-
-// position of 16-byte chunk c (0..3) of row r in a [rows][32] bf16 tile
-__device__ __forceinline__ int swz32(int r, int c) { return r * 32 + ((c ^ ((r >> 1) & 3)) << 3); }
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-template <int T>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2)))
-void head_gemm_lds_kernel(HeadParams p, int n_mchunks) {
-  typedef HeadLds<T> C;
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  const int total = p.n_vtiles * n_mchunks;
-  const int per = (total + 7) / 8;   // XCD-contiguous ranges (workgroup i runs on XCD i % 8)
-  const int tt = (blockIdx.x % 8) * per + blockIdx.x / 8;
-  if (tt >= total) return;
-  const int vt = tt / n_mchunks, mc = tt % n_mchunks;
-  const int v0 = vt * C::BV, m0 = mc * C::BB;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int H = p.H, V = p.V, M = p.M;
-  const uint16_t* __restrict__ W = (const uint16_t*)p.W;
-  const uint16_t* __restrict__ X = (const uint16_t*)p.A;
-
-  // DMA sources of this lane (rows clamped into range: their results are unused)
-  const uint16_t* wsrc[C::W_INSTR / C::WAVES];
-#pragma unroll
-  for (int q = 0; q < C::W_INSTR / C::WAVES; ++q) {
-    const int instr = wave * (C::W_INSTR / C::WAVES) + q;
-    const int idx = instr * 64 + lane, r = idx >> 2, pos = idx & 3;
-    const int c = pos ^ ((r >> 1) & 3);
-    wsrc[q] = W + (size_t)min(v0 + r, V - 1) * H + 8 * c;
-  }
-  const uint16_t* xsrc[T];
-#pragma unroll
-  for (int q = 0; q < T; ++q) {
-    const int instr = wave * T + q;
-    const int idx = instr * 64 + lane, r = idx >> 2, pos = idx & 3;
-    const int c = pos ^ ((r >> 1) & 3);
-    xsrc[q] = X + (size_t)min(m0 + r, M - 1) * H + 8 * c;
-  }
-  auto issue = [&](int slice) __attribute__((always_inline)) {
-    uint16_t* st = smem + (slice % C::NBUF) * C::STAGE;
-    const int k0 = slice * C::BK;
-#pragma unroll
-    for (int q = 0; q < C::W_INSTR / C::WAVES; ++q) {
-      const int instr = wave * (C::W_INSTR / C::WAVES) + q;
-      __builtin_amdgcn_global_load_lds((const void*)(wsrc[q] + k0),
-                                       (__attribute__((address_space(3))) void*)(st + instr * 512),
-                                       16, 0, 0);
-    }
-#pragma unroll
-    for (int q = 0; q < T; ++q) {
-      const int instr = wave * T + q;
-      __builtin_amdgcn_global_load_lds((const void*)(xsrc[q] + k0),
-                                       (__attribute__((address_space(3))) void*)(st + C::BV * C::BK +
-                                                                                  instr * 512),
-                                       16, 0, 0);
-    }
-  };
-
-  f32x4_t acc[8][T];
-#pragma unroll
-  for (int u = 0; u < 8; ++u)
-#pragma unroll
-    for (int t = 0; t < T; ++t) acc[u][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  const int fr = lane & 15, fq = lane >> 4;
-  const int nK = H / C::BK;
-#pragma unroll
-  for (int s0 = 0; s0 < C::NBUF - 1; ++s0)
-    if (s0 < nK) issue(s0);
-  for (int ks = 0; ks < nK; ++ks) {
-    const int newer = nK - 1 - ks;   // slices requested after ks and still possibly in flight
-    if (newer >= 2)
-      wait_vmcnt<2 * C::PER_WAVE>();
-    else if (newer == 1)
-      wait_vmcnt<C::PER_WAVE>();
-    else
-      wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-    if (ks + C::NBUF - 1 < nK) issue(ks + C::NBUF - 1);
-    const uint16_t* st = smem + (ks % C::NBUF) * C::STAGE;
-    u32x4 a[8], b[T];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) a[u] = *(const u32x4*)(st + swz32(16 * u + fr, fq));
-#pragma unroll
-    for (int t = 0; t < T; ++t)
-      b[t] = *(const u32x4*)(st + C::BV * C::BK + swz32(16 * T * wave + 16 * t + fr, fq));
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-#pragma unroll
-      for (int t = 0; t < T; ++t)
-        acc[u][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[u]),
-                                                            __builtin_bit_cast(bf16x8_t, b[t]),
-                                                            acc[u][t], 0, 0, 0);
-  }
-
-  // ---- epilogue: lane holds, for each of its T input rows, 32 vocabulary logits
-#pragma unroll
-  for (int t = 0; t < T; ++t) {
-    const int m = m0 + 16 * T * wave + 16 * t + fr;
-    const bool m_ok = m < M;
-    const float it = m_ok ? inv_temp(p.temperature, m) : 1.f;
-    int srow = (m_ok && p.store_row) ? p.store_row[m] : -1;
-    if (srow >= p.logits_rows) srow = -1;
-    Top2 tp = top2_empty();
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int v = v0 + 16 * u + 4 * fq + i;
-        if (v < V) top2_push(tp, acc[u][t][i], v);
-      }
-    float sum = 0.f;
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int v = v0 + 16 * u + 4 * fq + i;
-        if (v < V) sum += expf((acc[u][t][i] - tp.v1) * it);
-      }
-    if (srow >= 0) {
-      float* dst = p.logits + (size_t)srow * V;
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int v = v0 + 16 * u + 4 * fq + i;
-          if (v < V) dst[v] = acc[u][t][i];
-        }
-    }
-    RowStat st{tp.v1, sum, tp.i1, tp.v2};
-#pragma unroll
-    for (int mask = 16; mask < 64; mask <<= 1) {
-      RowStat o;
-      o.m = shfl_xor(st.m, mask);
-      o.s = shfl_xor(st.s, mask);
-      o.idx = shfl_xor(st.idx, mask);
-      o.v2 = shfl_xor(st.v2, mask);
-      st = stat_merge(st, o, it);
-    }
-    if (fq == 0 && m_ok) p.part[(size_t)m * p.n_vtiles + vt] = st;
-  }
-}
-
-template <int T>
-hipError_t launch_head_lds(const HeadParams& p, int n_mchunks, hipStream_t s) {
-  typedef HeadLds<T> C;
-  static_assert(C::LDS_BYTES <= 160 * 1024, "head LDS");
-  hipError_t e = hipFuncSetAttribute((const void*)head_gemm_lds_kernel<T>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES);
-  if (e != hipSuccess) return e;
-  const int total = p.n_vtiles * n_mchunks;
-  hipLaunchKernelGGL(head_gemm_lds_kernel<T>, dim3(8 * ((total + 7) / 8)), dim3(C::THREADS),
-                     C::LDS_BYTES, s, p, n_mchunks);
-  return hipGetLastError();
 }
 
 // ---- bf16 head GEMM, 32 x 32 x 16 MFMA version.
@@ -956,8 +513,13 @@ void head_gemm_mf32_kernel(HeadParams p, int n_mchunks) {
   }
 }
 
+// Optional start/stop events of the vocabulary GEMM launch (both or neither).
+struct GemmEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
 template <int TB, int BK, int NBUF = head_mf32_nbuf(TB, BK)>
-hipError_t launch_head_mf32(const HeadParams& p, int n_mchunks, hipStream_t s) {
+hipError_t launch_head_mf32(const HeadParams& p, int n_mchunks, const GemmEvents& ev, hipStream_t s) {
   typedef HeadMf32<TB, BK, NBUF> C;
   static_assert(C::LDS_BYTES <= 160 * 1024, "head LDS");
   static_assert(C::NBUF >= 2 && C::PER_WAVE * (C::NBUF - 2) < 64, "vmcnt");
@@ -965,90 +527,32 @@ hipError_t launch_head_mf32(const HeadParams& p, int n_mchunks, hipStream_t s) {
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES);
   if (e != hipSuccess) return e;
   const int total = p.n_vtiles * n_mchunks;
-  hipLaunchKernelGGL((head_gemm_mf32_kernel<TB, BK, NBUF>), dim3(8 * ((total + 7) / 8)),
-                     dim3(C::THREADS), C::LDS_BYTES, s, p, n_mchunks);
+  const dim3 grid(8 * ((total + 7) / 8));
+  if (ev.start && ev.stop)
+    hipExtLaunchKernelGGL((head_gemm_mf32_kernel<TB, BK, NBUF>), grid, dim3(C::THREADS),
+                          (uint32_t)C::LDS_BYTES, s, ev.start, ev.stop, 0u, p, n_mchunks);
+  else
+    hipLaunchKernelGGL((head_gemm_mf32_kernel<TB, BK, NBUF>), grid, dim3(C::THREADS), C::LDS_BYTES,
+                       s, p, n_mchunks);
   return hipGetLastError();
 }
 
-int head_tune(const char* name, int dflt) {
-  const char* e = getenv(name);
-  return e ? atoi(e) : dflt;
-}
 
 // Row chunks of at most 448 rows, split evenly; TB = 64-row tiles per
 // workgroup.  One or two tiles (weight streaming): 64-wide slices, deep ring.
 // More: 32-wide slices, three stages, copies spread over the MFMAs.
-hipError_t launch_head_mf32_any(const HeadParams& p, hipStream_t s) {
+hipError_t launch_head_mf32_any(const HeadParams& p, const GemmEvents& ev, hipStream_t s) {
   const int nc = (p.M + 447) / 448;
   const int rows = (p.M + nc - 1) / nc;
   const int tb = (rows + 63) / 64;
-  static const int big = head_tune("DMTP_HEAD_BIG", 0);
   switch (tb) {
-    case 1: return launch_head_mf32<1, 64>(p, nc, s);
-    case 2: return launch_head_mf32<2, 64>(p, nc, s);
-    case 3: return launch_head_mf32<3, 32, 3>(p, nc, s);
-    case 4: return launch_head_mf32<4, 32, 3>(p, nc, s);
-    case 5: return launch_head_mf32<5, 32, 3>(p, nc, s);
-    case 6: return launch_head_mf32<6, 32, 3>(p, nc, s);
-    default:
-      if (big == 1) return launch_head_mf32<7, 32, 4>(p, nc, s);
-      if (big == 2) return launch_head_mf32<7, 64, 2>(p, nc, s);
-      return launch_head_mf32<7, 32, 3>(p, nc, s);
-  }
-}
-
-// Row chunks of at most 448 rows, split evenly; T = 16-row tiles per wave.
-hipError_t launch_head_lds_any(const HeadParams& p, hipStream_t s) {
-  const int nc = (p.M + 447) / 448;
-  const int rows = (p.M + nc - 1) / nc;
-  switch ((rows + 63) / 64) {
-    case 1: return launch_head_lds<1>(p, nc, s);
-    case 2: return launch_head_lds<2>(p, nc, s);
-    case 3: return launch_head_lds<3>(p, nc, s);
-    case 4: return launch_head_lds<4>(p, nc, s);
-    case 5: return launch_head_lds<5>(p, nc, s);
-    case 6: return launch_head_lds<6>(p, nc, s);
-    default: return launch_head_lds<7>(p, nc, s);
-  }
-}
-
-template <int NBW>
-hipError_t launch_head_big(const HeadParams& p, int n_mchunks, hipStream_t s) {
-  typedef HeadBig<NBW> C;
-  static_assert(C::LDS_BYTES <= 160 * 1024, "head LDS");
-  hipError_t e = hipFuncSetAttribute((const void*)head_gemm_big_kernel<NBW>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES);
-  if (e != hipSuccess) return e;
-  const int total = p.n_vtiles * n_mchunks;
-  const int grid = 8 * ((total + 7) / 8);
-  hipLaunchKernelGGL(head_gemm_big_kernel<NBW>, dim3(grid), dim3(C::THREADS), C::LDS_BYTES, s, p,
-                     n_mchunks);
-  return hipGetLastError();
-}
-
-// Row chunks of at most 256 rows (four waves, one per SIMD, so that each wave
-// may hold 512 registers), split evenly.
-void head_chunks(int M, int& n_mchunks, int& nbw) {
-  n_mchunks = (M + 255) / 256;
-  const int rows = (M + n_mchunks - 1) / n_mchunks;
-  nbw = (rows + 63) / 64;
-}
-
-hipError_t launch_head_big_any(const HeadParams& p, hipStream_t s) {
-  if (p.M <= 64) {
-    const dim3 grid((p.n_vtiles + 3) / 4);
-    if (p.M <= 32)
-      hipLaunchKernelGGL(head_gemm_skinny_kernel<1>, grid, dim3(256), 0, s, p);
-    else
-      hipLaunchKernelGGL(head_gemm_skinny_kernel<2>, grid, dim3(256), 0, s, p);
-    return hipGetLastError();
-  }
-  int nc, nbw;
-  head_chunks(p.M, nc, nbw);
-  switch (nbw) {   // rows per chunk > 64 here, so nbw >= 2
-    case 2: return launch_head_big<2>(p, nc, s);
-    case 3: return launch_head_big<3>(p, nc, s);
-    default: return launch_head_big<4>(p, nc, s);
+    case 1: return launch_head_mf32<1, 64>(p, nc, ev, s);
+    case 2: return launch_head_mf32<2, 64>(p, nc, ev, s);
+    case 3: return launch_head_mf32<3, 32, 3>(p, nc, ev, s);
+    case 4: return launch_head_mf32<4, 32, 3>(p, nc, ev, s);
+    case 5: return launch_head_mf32<5, 32, 3>(p, nc, ev, s);
+    case 6: return launch_head_mf32<6, 32, 3>(p, nc, ev, s);
+    default: return launch_head_mf32<7, 32, 3>(p, nc, ev, s);
   }
 }
 
@@ -1059,8 +563,21 @@ __global__ __launch_bounds__(kMergeThreads) void head_merge_kernel(HeadParams p,
   const int m = blockIdx.x;
   const float it = inv_temp(p.temperature, m);
   RowStat st = stat_empty();
-  for (int t = threadIdx.x; t < p.n_vtiles; t += blockDim.x)
-    st = stat_merge(st, p.part[(size_t)m * p.n_vtiles + t], it);
+  // tiles t = threadIdx.x + kMergeThreads j, merged in increasing j; eight
+  // partials are loaded together before they are merged
+  constexpr int PB = 8;
+  const RowStat* pr = p.part + (size_t)m * p.n_vtiles;
+  for (int t0 = threadIdx.x; t0 < p.n_vtiles; t0 += PB * kMergeThreads) {
+    RowStat v[PB];
+#pragma unroll
+    for (int j = 0; j < PB; ++j) {
+      const int t = t0 + j * kMergeThreads;
+      v[j] = t < p.n_vtiles ? pr[t] : stat_empty();
+    }
+#pragma unroll
+    for (int j = 0; j < PB; ++j)
+      if (t0 + j * kMergeThreads < p.n_vtiles) st = stat_merge(st, v[j], it);
+  }
 #pragma unroll
   for (int mask = 1; mask < kWave; mask <<= 1) {
     RowStat o;
@@ -1223,17 +740,6 @@ WsLayout ws_layout(const dmtp_head_desc& d, int M) {
   return w;
 }
 
-// Selects the bf16 head kernel variant from DMTP_HEAD_KERNEL, read once:
-// 0 (default) the 32 x 32 x 16 LDS-DMA kernel, 1 the register-staged pair,
-// 2 the 16 x 16 x 32 LDS-DMA kernel.
-int head_kernel_choice() {
-  static int v = [] {
-    const char* e = getenv("DMTP_HEAD_KERNEL");
-    return e ? atoi(e) : 0;
-  }();
-  return v;
-}
-
 }  // namespace
 
 size_t lm_head_ws_bytes(const dmtp_head_desc& d, int M) { return ws_layout(d, M).total; }
@@ -1287,9 +793,10 @@ hipError_t lm_head_run(const dmtp_head_desc& d, int M, void* ws, hipStream_t s) 
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (d.dtype == DMTP_BF16 && d.H % 128 == 0) {
-    const int kc = head_kernel_choice();
-    e = kc == 1 ? launch_head_big_any(p, s) : kc == 2 ? launch_head_lds_any(p, s)
-                                                       : launch_head_mf32_any(p, s);
+    GemmEvents ev;
+    ev.start = (hipEvent_t)d.gemm_start_event;
+    ev.stop = (hipEvent_t)d.gemm_stop_event;
+    e = launch_head_mf32_any(p, ev, s);
     if (e != hipSuccess) return e;
   } else if (d.dtype == DMTP_BF16) {
     dim3 grid(w.n_vtiles, (M + HeadTileBF16::BM - 1) / HeadTileBF16::BM);
