@@ -5,7 +5,8 @@
 // These are small-M, weight-streaming shapes (M = the 32 fused rows or the
 // B * S draft slots, N and K in the thousands).  A bf16 weight goes through
 // gemm_dma_kernel: 32 x 32 x 16 MFMA tiles fed by a ring of LDS stages that
-// global_load_lds copies fill several k-slices ahead, with K split into
+// global_load_lds copies fill several k-slices ahead (spread over the MFMAs of
+// the slice before, with three or more stages), with K split into
 // contiguous ranges so that about one workgroup per CU is busy; the float32
 // partial sums are added in a fixed order by splitk_reduce4, so results are
 // deterministic.  A float32 weight (the float32 configurations) goes through
@@ -94,11 +95,13 @@ void gemm_dma_kernel(GemmParams p, int n_tiles_n, int n_tiles_m) {
                8 * swz_chunk<T::BK>(r, idx % T::CPR);
     }
   }
+  auto issue_one = [&](int s, int q) __attribute__((always_inline)) {
+    lds_dma16(src[q] + (s_begin + s) * T::BK,
+              smem + (s % T::NBUF) * T::STAGE + (wave * T::PER_WAVE + q) * 512);
+  };
   auto issue = [&](int s) __attribute__((always_inline)) {
-    uint16_t* st = smem + (s % T::NBUF) * T::STAGE;
-    const int k0 = (s_begin + s) * T::BK;
 #pragma unroll
-    for (int q = 0; q < T::PER_WAVE; ++q) lds_dma16(src[q] + k0, st + (wave * T::PER_WAVE + q) * 512);
+    for (int q = 0; q < T::PER_WAVE; ++q) issue_one(s, q);
   };
   struct Frag {
     u32x4 w[T::UN];
@@ -124,20 +127,54 @@ void gemm_dma_kernel(GemmParams p, int n_tiles_n, int n_tiles_m) {
     for (int v = 0; v < T::UM; ++v)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[u][v][i] = 0.f;
-  auto compute = [&](const Frag& f) __attribute__((always_inline)) {
+  // With three or more stages the copies of slice s + NBUF - 1 are spread over
+  // the MFMA units (pairs of plane products) of slice s, copy q after unit
+  // q * UNITS / PER_WAVE; with two stages they go out in one burst after the
+  // barrier, since all of them must land before the next wait.
+  constexpr bool INTER = T::NBUF >= 3;
+  constexpr int UNITS = T::KS * T::UM * T::UN;   // per slice
+  auto compute = [&](const Frag& f, int ks, int s_fill) __attribute__((always_inline)) {
 #pragma unroll
     for (int v = 0; v < T::UM; ++v)
 #pragma unroll
       for (int u = 0; u < T::UN; ++u) {
         acc[u][v] = mfma32(f.w[u], f.a[0][v], acc[u][v]);
         acc[u][v] = mfma32(f.w[u], f.a[1][v], acc[u][v]);
+        if constexpr (INTER) {
+          const int unit = (ks * T::UM + v) * T::UN + u;
+#pragma unroll
+          for (int q = 0; q < T::PER_WAVE; ++q)
+            if ((q * UNITS) / T::PER_WAVE == unit && s_fill < ns) issue_one(s_fill, q);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
   };
-  // Slice s is in LDS once this wave's copies of it have landed (later slices'
-  // copies may stay in flight) and every wave has passed the barrier; the
-  // buffer the next copy refills was read into registers just before.
+  // copies of the slice being filled that go out before the wait at the last k-step
+  constexpr int Q_BEFORE = [] {
+    int c = 0;
+    for (int q = 0; q < T::PER_WAVE; ++q)
+      if ((q * UNITS) / T::PER_WAVE < (T::KS - 1) * T::UM * T::UN) ++c;
+    return c;
+  }();
+  // Slice s is in LDS once this wave's copies of it have landed -- vmcnt lets
+  // exactly the copies issued after them stay in flight -- and every wave has
+  // passed the barrier; the buffer the next copies refill was read into
+  // registers just before, by every wave.
   auto wait_slice = [&](int s) __attribute__((always_inline)) {
-    wait_newer<T::PER_WAVE, T::NBUF - 2>(min(ns - 1 - s, T::NBUF - 2));
+    if constexpr (!INTER) {
+      wait_newer<T::PER_WAVE, T::NBUF - 2>(min(ns - 1 - s, T::NBUF - 2));
+    } else {
+      // issued after slice s: slices s+1 .. s+NBUF-3 whole (those that exist)
+      // and Q_BEFORE copies of slice s+NBUF-2 when it exists.  In the prologue
+      // that slice is already whole, so the wait there is longer than needed.
+      constexpr int STEADY = (T::NBUF - 3) * T::PER_WAVE + Q_BEFORE;
+      if (s + T::NBUF - 2 < ns) {
+        wait_vm_lgkm0<STEADY>();
+      } else {
+        const int full = ns - 1 - s > T::NBUF - 3 ? T::NBUF - 3 : (ns - 1 - s < 0 ? 0 : ns - 1 - s);
+        wait_vm_dyn<STEADY>(full * T::PER_WAVE);
+      }
+    }
     ring_barrier();
   };
 
@@ -146,9 +183,10 @@ void gemm_dma_kernel(GemmParams p, int n_tiles_n, int n_tiles_m) {
     if (s0 < ns) issue(s0);
   Frag f0, f1;
   wait_slice(0);
-  if (T::NBUF - 1 < ns) issue(T::NBUF - 1);
+  if (!INTER && T::NBUF - 1 < ns) issue(T::NBUF - 1);
   read(f0, 0, 0);
   for (int s = 0; s < ns; ++s) {
+    const int s_fill = s + T::NBUF - 1;
 #pragma unroll
     for (int ks = 0; ks < T::KS; ++ks) {
       Frag& cur = (ks & 1) ? f1 : f0;
@@ -157,10 +195,10 @@ void gemm_dma_kernel(GemmParams p, int n_tiles_n, int n_tiles_m) {
         read(nxt, s, ks + 1);
       } else if (s + 1 < ns) {
         wait_slice(s + 1);
-        if (s + T::NBUF < ns) issue(s + T::NBUF);
+        if (!INTER && s + T::NBUF < ns) issue(s + T::NBUF);
         read(nxt, s + 1, 0);
       }
-      compute(cur);
+      compute(cur, ks, s_fill);
     }
   }
 
@@ -287,6 +325,10 @@ hipError_t launch_dma(const GemmParams& p, const DmaPlan& pl, hipStream_t s) {
   return hipGetLastError();
 }
 
+hipError_t launch_dma_any(const GemmParams& p, const DmaPlan& pl, hipStream_t s) {
+  return pl.cfg == 0 ? launch_dma<DmaM32>(p, pl, s) : launch_dma<DmaM128>(p, pl, s);
+}
+
 // ---------------------------------------------------- float32 weight path ----
 template <class T>
 __global__ __launch_bounds__(T::THREADS) void gemm_kernel(GemmParams p) {
@@ -328,7 +370,7 @@ hipError_t gemm_deferred(const GemmArgs& a, float* ws, hipStream_t s, SplitOut* 
     const DmaPlan pl = dma_plan(a.M, a.N, a.K);
     p.splits = pl.splits;
     out->splits = pl.splits;
-    return pl.cfg == 0 ? launch_dma<DmaM32>(p, pl, s) : launch_dma<DmaM128>(p, pl, s);
+    return launch_dma_any(p, pl, s);
   }
   dim3 grid((a.N + TilePlanesF32::BN - 1) / TilePlanesF32::BN,
             (a.M + TilePlanesF32::BM - 1) / TilePlanesF32::BM);
@@ -342,7 +384,7 @@ hipError_t gemm(const GemmArgs& a, float* ws, hipStream_t s) {
     if (!dma_ok(a)) return hipErrorInvalidValue;
     const DmaPlan pl = dma_plan(a.M, a.N, a.K);
     p.splits = pl.splits;
-    hipError_t e = pl.cfg == 0 ? launch_dma<DmaM32>(p, pl, s) : launch_dma<DmaM128>(p, pl, s);
+    hipError_t e = launch_dma_any(p, pl, s);
     if (e != hipSuccess || pl.splits == 1) return e;
     const size_t total4 = (size_t)a.M * a.N / 4;
     const int blocks = (int)((total4 + 255) / 256 < 4096 ? (total4 + 255) / 256 : 4096);
