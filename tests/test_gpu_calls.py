@@ -170,9 +170,9 @@ def test_lm_head_sampled_planted_and_stored(dm, dt):
     print("exempt", n_ex)
 
 
-@pytest.mark.parametrize("M", [200, 448, 901])
+@pytest.mark.parametrize("M", [32, 64, 200, 448, 901])
 def test_lm_head_many_rows(dm, M):
-    # 64-row tiles per workgroup from 4 to 7, one and several row chunks, a
+    # 1 to 7 row tiles of 64 per workgroup, one and several row chunks, a
     # ragged vocabulary tile (7001 = 54 * 128 + 89)
     H, V = 512, 7001
     print(f"lm_head many rows M={M}", flush=True)
