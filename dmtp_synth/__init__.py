@@ -60,6 +60,7 @@ class RoundConfig:
     plant_frac: float = 0.0      # fraction of rows whose T1 is set to the target argmax
     w_zero: bool = False         # DMTP residual projection W zero-initialised
     n_anchor: int = 2
+    verify: str = "rejection"    # "rejection" | "target_only" (rows with tau > 0)
     window: int = 0              # 0 = every context position, else the last `window`
     rope_base: float = 1.0e6
     eps: float = 1.0e-6
@@ -126,6 +127,7 @@ _TID = {
 # Purposes of the counter-based random draws (upper 32 bits of a draw key).
 DRAW_DRAFT = 1   # sampling of candidate i of sequence b from the draft distribution
 DRAW_FINAL = 2   # the correction/bonus draw of sequence b during verification
+DRAW_TARGET = 3  # the target's own pick at verify row i of sequence b (target-only verify)
 
 
 def draft_draw_key(b: int, i: int) -> int:
@@ -136,6 +138,11 @@ def draft_draw_key(b: int, i: int) -> int:
 def final_draw_key(b: int) -> int:
     """Key of the correction/bonus draw of sequence b."""
     return (DRAW_FINAL << 32) | int(b)
+
+
+def target_pick_key(b: int, i: int) -> int:
+    """Key of the draw that picks the target's token at verify row i of sequence b."""
+    return (DRAW_TARGET << 32) | (int(b) << 8) | int(i)
 
 
 def _rng(cfg: RoundConfig, tid: int) -> np.random.Generator:
@@ -244,6 +251,7 @@ class RoundInputs:
     philox_seed: int       # key of the counter-based generator
     draft_keys: np.ndarray  # [B, K] uint64 draw keys for candidate sampling
     final_keys: np.ndarray  # [B] uint64 draw keys for correction/bonus draws
+    target_keys: np.ndarray  # [B, K + 1] uint64 draw keys of the target's picks
 
 
 def make_inputs(cfg: RoundConfig, *, with_layers: bool = True) -> RoundInputs:
@@ -308,6 +316,8 @@ def make_inputs(cfg: RoundConfig, *, with_layers: bool = True) -> RoundInputs:
     draft_keys = np.array([[draft_draw_key(b, i) for i in range(K)] for b in range(B)],
                           dtype=np.uint64)
     final_keys = np.array([final_draw_key(b) for b in range(B)], dtype=np.uint64)
+    target_keys = np.array([[target_pick_key(b, i) for i in range(K + 1)] for b in range(B)],
+                           dtype=np.uint64)
 
     return RoundInputs(
         cfg=cfg, emb=emb, w_head=w_head, fuse_M=fuse_M, fuse_W=fuse_W,
@@ -316,10 +326,12 @@ def make_inputs(cfg: RoundConfig, *, with_layers: bool = True) -> RoundInputs:
         g_f=_gain(cfg, _TID["g_f"], H), g_final=_gain(cfg, _TID["g_final"], H),
         layers=layers, ctx_len=ctx_len, cu_ctx=cu_ctx, anchor=anchor,
         h_prev=h_prev, h_target=h_target, tau=tau, u_acc=u_acc, plant=plant,
-        philox_seed=philox_seed, draft_keys=draft_keys, final_keys=final_keys)
+        philox_seed=philox_seed, draft_keys=draft_keys, final_keys=final_keys,
+        target_keys=target_keys)
 
 
 __all__ = [
     "RoundConfig", "CONFIGS", "RoundInputs", "LayerInputs", "make_inputs",
-    "draft_draw_key", "final_draw_key", "DRAW_DRAFT", "DRAW_FINAL",
+    "draft_draw_key", "final_draw_key", "target_pick_key", "DRAW_DRAFT", "DRAW_FINAL",
+    "DRAW_TARGET",
 ]

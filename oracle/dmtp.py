@@ -30,6 +30,11 @@ One round for a sequence whose last emitted-but-unprocessed token is A:
      normalize(max(0, p - q)), all accepted draws the bonus from p ([DvM]
      reference 8, Leviathan et al.; [DvM] "DFlash's Lossless Guarantee Breaks at
      Non-Zero Temperature": the draft sampler uses the same tau as the target).
+     Target-only verification, the verifier the pages' experiments use ([DMTP]
+     section 5, the note after step 3; [colibri]: a sampled pick that equals the
+     next draft accepts it), instead compares each candidate with the target's
+     own pick y_i ~ softmax(lt_i / tau): the accepted prefix runs to the first
+     mismatch and the pick there (or y_K) is committed.
 
 Precision reading (the pages fix none beyond bf16 weights): weights, embeddings,
 context K/V and target rows are inputs in the configuration's dtype; every
@@ -235,6 +240,24 @@ def verify_greedy(drafts: Sequence[int], target_argmax: Sequence[int]) -> Tuple[
     return L, [int(t) for t in drafts[:L]] + [int(target_argmax[L])]
 
 
+def verify_target_only(drafts: Sequence[int], pick: Callable[[int], int]) -> Tuple[int, List[int]]:
+    """Target-only block verification ([DMTP] section 5, the note after step 3).
+
+    pick(i) is the target's own token at row i (row i follows the prefix and
+    d_0..d_{i-1}): a draw from its distribution at temperature tau, or its
+    argmax at tau = 0.  Candidate d_i is accepted while it equals that pick; the
+    first pick that differs is committed in its place as the correction, and
+    when all K match the pick of row K is the bonus.  Picks of rows past the
+    first mismatch are never needed (pick is called in increasing i).
+    """
+    K = len(drafts)
+    for i in range(K):
+        y = int(pick(i))
+        if y != int(drafts[i]):
+            return i, [int(t) for t in drafts[:i]] + [y]
+    return K, [int(t) for t in drafts] + [int(pick(K))]
+
+
 class VerifyOps:
     """Arithmetic used by the rejection verifier, float64 NumPy version."""
 
@@ -287,7 +310,7 @@ class RoundResult:
     hd: np.ndarray           # [n, S, H] rounded final-normed drafter output, all slots
     t1: np.ndarray           # [n]
     drafts: np.ndarray       # [n, K]  d_0 = T1, d_i from MASK slot i + n_anchor - 1
-    target_argmax: np.ndarray  # [n, K + 1]
+    target_argmax: np.ndarray  # [n, K + 1] the target's pick per row: argmax, or a draw (target-only, tau > 0)
     q_lse: np.ndarray        # [n, K]   lse(l / tau) of the candidate rows
     p_lse: np.ndarray        # [n, K + 1]
     q_max: np.ndarray
@@ -397,10 +420,19 @@ def run_round(inp, seqs: Optional[Sequence[int]] = None,
     accept_len = np.empty(n, dtype=np.int64)
     out_tokens = np.full((n, K + 1), -1, dtype=np.int64)
     y_final = np.empty((n, K + 1), dtype=np.int64)
+    target_only = getattr(cfg, "verify", "rejection") == "target_only"
     for r, b in enumerate(seqs):
         for i in range(K + 1):
-            y_final[r, i] = decide(("y", b, i), tgt_argmax[r, i], tgt_gap[r, i])
-        if tau[r] > 0:
+            if target_only and tau[r] > 0:
+                # the target's own pick: a draw from softmax(lt_i / tau)
+                v, m = gumbel_argmax(p_logits[r, i] / tau[r], seed, int(inp.target_keys[b, i]))
+            else:
+                v, m = tgt_argmax[r, i], tgt_gap[r, i]
+            y_final[r, i] = decide(("y", b, i), v, m)
+        if target_only:
+            # at tau = 0 the picks are the argmax and this is greedy verification
+            L, toks = verify_target_only(drafts[r], lambda i, r=r: y_final[r, i])
+        elif tau[r] > 0:
             p_rows = np.exp(p_logits[r] / tau[r] - p_lse[r][:, None])
             q_rows = np.exp(q_logits[r] / tau[r] - q_lse[r][:, None])
             u = inp.u_acc[b].astype(np.float64)

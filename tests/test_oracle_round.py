@@ -216,6 +216,37 @@ def test_sampled_round_uses_draws_and_accept_tests():
     assert np.all(res_hot.p_lse > np.log(cfg.V) - 0.05)
 
 
+def test_target_only_round_at_tau_zero_is_the_greedy_round():
+    cfg = TINY.with_(B=3, ctx_min=20, ctx_max=60, seed=91)
+    a = dmtp.run_round(synth.make_inputs(cfg))
+    b = dmtp.run_round(synth.make_inputs(cfg.with_(verify="target_only")))
+    for name in ("t1", "drafts", "target_argmax", "accept_len", "out_tokens", "n_out"):
+        np.testing.assert_array_equal(getattr(a, name), getattr(b, name))
+
+
+def test_target_only_sampled_round_commits_the_target_picks():
+    cfg = TINY.with_(B=4, tau_mode="sample", verify="target_only", ctx_min=20, ctx_max=60, seed=92)
+    inp = synth.make_inputs(cfg)
+    res = dmtp.run_round(inp)
+    kinds = {k[0] for k, _, _ in res.decisions}
+    assert "accept" not in kinds and "final" not in kinds     # no accept tests, no residual draws
+    from oracle.philox import gumbel_argmax
+    full = dmtp.run_round(inp, keep_logits=True)
+    for r in range(cfg.B):
+        y = res.target_argmax[r]
+        # every pick is the Gumbel-max draw of its row at the row's temperature
+        for i in range(cfg.K + 1):
+            want, _ = gumbel_argmax(full.p_logits[r, i] / inp.tau[r], int(inp.philox_seed),
+                                    int(inp.target_keys[r, i]))
+            assert y[i] == want
+        L = int(res.accept_len[r])
+        assert np.array_equal(res.drafts[r, :L], y[:L])
+        assert L == cfg.K or res.drafts[r, L] != y[L]
+        assert res.out_tokens[r, L] == y[L] and np.all(res.out_tokens[r, L + 1:] == -1)
+    # the picks are draws, not the argmax: at tau = 1 over V = 1024 some differ
+    assert np.any(res.target_argmax != np.argmax(full.p_logits, axis=-1))
+
+
 def test_single_anchor_layout():
     cfg = TINY.with_(n_anchor=1)
     inp = synth.make_inputs(cfg)

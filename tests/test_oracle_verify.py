@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 
 from oracle import dmtp
-from oracle.dmtp import verify_greedy, verify_rejection
+from oracle.dmtp import verify_greedy, verify_rejection, verify_target_only
 
 
 def test_verify_greedy_longest_prefix_bruteforce():
@@ -214,3 +214,100 @@ def test_enumeration_detects_a_planted_mistake():
     for prob, t in _enumerate(run):
         dist[t] = dist.get(t, Fr(0)) + prob
     assert any(dist.get(t, Fr(0)) != p([])[t] for t in range(V))
+
+
+# ---------------------------------------------------------------------------
+# target-only verification
+# ---------------------------------------------------------------------------
+
+
+def test_target_only_with_argmax_picks_is_greedy():
+    rng = np.random.default_rng(4)
+    for _ in range(3000):
+        K = int(rng.integers(1, 9))
+        y = rng.integers(0, 3, size=K + 1)
+        d = rng.integers(0, 3, size=K)
+        called = []
+
+        def pick(i):
+            called.append(i)
+            return int(y[i])
+
+        assert verify_target_only(d, pick) == verify_greedy(d, y)
+        # picks are taken in order and stop at the first mismatch (or the bonus row)
+        assert called == list(range(len(called)))
+        assert len(called) == verify_greedy(d, y)[0] + 1
+
+
+def _target_only_committed(V, K, N, p, q, commit_rejected_draft=False):
+    """Distribution of the first N committed tokens of repeated target-only rounds."""
+
+    def run(path):
+        seq = []
+        while len(seq) < N:
+            drafts = []
+            for _ in range(K):
+                drafts.append(path.draw(-1, q(seq + drafts)))
+
+            def pick(i, seq=seq, drafts=drafts):
+                return path.draw(i, p(seq + drafts[:i]))
+
+            L, toks = verify_target_only(drafts, pick)
+            if commit_rejected_draft and L < K:
+                toks[L] = drafts[L]
+            seq += toks
+        return tuple(seq[:N])
+
+    dist = {}
+    for prob, s in _enumerate(run):
+        dist[s] = dist.get(s, Fr(0)) + prob
+    return dist
+
+
+@pytest.mark.parametrize("V,K,N", [(3, 2, 3), (4, 1, 3), (3, 3, 2)])
+def test_target_only_is_lossless_exact_enumeration(V, K, N):
+    p = lambda pre: _toy_dist(pre, V, "p")  # noqa: E731
+    q = lambda pre: _toy_dist(pre, V, "q")  # noqa: E731
+    dist = _target_only_committed(V, K, N, p, q)
+    assert sum(dist.values()) == 1
+    for s in itertools.product(range(V), repeat=N):
+        want = Fr(1)
+        for t in range(N):
+            want *= p(list(s[:t]))[s[t]]
+        assert dist.get(s, Fr(0)) == want, (s, dist.get(s), want)
+
+
+def test_target_only_acceptance_closed_form():
+    """For fixed drafts, P(L >= k) = prod_{i<k} p_i(d_i) with p_i after d_0..d_{i-1}."""
+    V, K = 4, 3
+    p = lambda pre: _toy_dist(pre, V, "p")  # noqa: E731
+    for d in itertools.product(range(V), repeat=K):
+        d = list(d)
+
+        def run(path):
+            return verify_target_only(d, lambda i: path.draw(i, p(d[:i])))[0]
+
+        hist = {}
+        for prob, L in _enumerate(run):
+            hist[L] = hist.get(L, Fr(0)) + prob
+        for k in range(K + 1):
+            want = Fr(1)
+            for i in range(k):
+                want *= p(d[:i])[d[i]]
+            got = sum((v for L, v in hist.items() if L >= k), Fr(0))
+            assert got == want, (d, k, got, want)
+
+
+def test_target_only_enumeration_detects_a_planted_mistake():
+    """Sensitivity: committing the rejected draft instead of the target's pick is not lossless."""
+    V, K, N = 3, 2, 2
+    p = lambda pre: _toy_dist(pre, V, "p")  # noqa: E731
+    q = lambda pre: _toy_dist(pre, V, "q")  # noqa: E731
+    dist = _target_only_committed(V, K, N, p, q, commit_rejected_draft=True)
+    wrong = 0
+    for s in itertools.product(range(V), repeat=N):
+        want = Fr(1)
+        for t in range(N):
+            want *= p(list(s[:t]))[s[t]]
+        wrong += dist.get(s, Fr(0)) != want
+    assert wrong > 0
