@@ -38,7 +38,7 @@ def _workload_desc(cfg) -> str:
     return (f"{cfg.name}: B={cfg.B}, H={cfg.H}, V={cfg.V}, {cfg.n_layers} draft layer(s) "
             f"{cfg.Hq}q/{cfg.Hkv}kv x{cfg.d}, F={cfg.F}, K={cfg.K} candidates "
             f"({cfg.S} slots, {cfg.R} verify rows), ctx U[{cfg.ctx_min},{cfg.ctx_max}], "
-            f"tau={cfg.tau_mode}")
+            f"tau={cfg.tau_mode}, verify={cfg.verify}")
 
 
 # Sources the LM-head GEMM is compiled from; a counter summary taken on other
@@ -158,6 +158,11 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--config", default="b32_greedy_bf16")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of the round captured as one HIP graph (the LM-head "
+                         "GEMM is still timed by its dispatch events in an eager pass)")
+    ap.add_argument("--verify", choices=["rejection", "target_only"], default=None,
+                    help="verification of sampled rows (default: the workload's)")
     ap.add_argument("--cpu-seqs", type=int, default=8, help="sequences in the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -187,6 +192,8 @@ def main() -> int:
     from mtp_block_draft_amd.round import Round
 
     cfg = synth.CONFIGS[args.config]
+    if args.verify:
+        cfg = cfg.with_(verify=args.verify)
     inp = synth.make_inputs(cfg)
     R = Round(inp)
     stream = torch.cuda.current_stream()
@@ -259,6 +266,21 @@ def main() -> int:
         hip.hipEventDestroy(b)
     one_round()   # leaves the descriptor without events
 
+    graph_ms_step = None
+    if args.graph:
+        R.capture()
+        for _ in range(args.warmup):
+            R.replay()
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(args.steps):
+            R.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms_step = g0.elapsed_time(g1) / args.steps
+
     # per-call durations, from a separate pass after the timed loop (stream
     # events between calls add a few microseconds each, so they stay out of it)
     n_diag = min(args.steps, 50)
@@ -271,6 +293,9 @@ def main() -> int:
                                            for k in range(n_diag)])) for i in range(n_calls)]
     res = R.results()
     committed = int(res["n_out"].sum())
+    eager_ms_step = ms_step
+    if graph_ms_step is not None:
+        ms_step = graph_ms_step
     rounds_s = 1000.0 / ms_step
 
     # dominant kernel: the LM-head call over draft (B(K-1)) and target (B(K+1)) rows
@@ -295,13 +320,16 @@ def main() -> int:
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": cfg.dtype, "data": "synthetic (seeded random-init weights and inputs)",
         "config": {"workload": _workload_desc(cfg), "global_batch": cfg.B,
-                   "candidates": cfg.K, "parallelism": "single GPU"},
+                   "candidates": cfg.K, "verify": cfg.verify, "parallelism": "single GPU",
+                   "submission": "one HIP graph per round" if args.graph else "six calls per round"},
         "accepted_tokens_per_s": round(rounds_s * committed, 1),
         "committed_tokens_per_round": committed,
         "phases_us": dict(zip(["fuse_mtp", "lm_head_t1", "fuse_delta", "block_draft",
                                "lm_head_draft_target", "verify"], [round(x, 2) for x in per_call_us])),
         "roofline": roofline,
     }
+    if graph_ms_step is not None:
+        out["eager_rounds_per_s"] = round(1000.0 / eager_ms_step, 2)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seqs)
     print(json.dumps(out), flush=True)

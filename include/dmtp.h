@@ -7,12 +7,14 @@
  * hidden is added to T1's embedding slot, one parallel block-draft forward over
  * [E(A), E(T1)+Delta, E(MASK)...] proposes the remaining candidates, and the
  * target verifies all of them, committing the accepted prefix plus one
- * correction or bonus token.  Four calls cover it:
+ * correction or bonus token.  Four calls cover it, and a fifth summarises
+ * acceptance over rounds:
  *
  *   dmtp_fuse         RMSNorm-concat-projection (MTP input fusion; DMTP residual)
  *   dmtp_block_draft  the block drafter's layers and final norm
  *   dmtp_lm_head      the shared vocabulary head with argmax / sampling
- *   dmtp_verify       greedy or rejection-sampling block verification
+ *   dmtp_verify       greedy, rejection-sampling or target-only block verification
+ *   dmtp_accept_stats acceptance histogram and statistics of verify rounds
  *
  * Conventions (all calls)
  *   - Tensor pointers are DEVICE pointers to row-major, contiguous data,
@@ -47,7 +49,7 @@
 extern "C" {
 #endif
 
-#define DMTP_ABI_VERSION 2
+#define DMTP_ABI_VERSION 3
 
 enum dmtp_status {
   DMTP_OK = 0,
@@ -236,6 +238,14 @@ int dmtp_lm_head(const dmtp_head_desc* d, void* ws, size_t ws_bytes, hipStream_t
  *       zero); if all K are accepted draw the bonus from p_K.  Draws are
  *       Gumbel-max over Philox draw (seed, final_key[b]), the layout of
  *       dmtp_lm_head.  Needs the lse of every row (lse of logits / t).
+ *   target_only != 0 (DMTP blog section 5, the note on target-only
+ *       verification; colibri: a sampled pick equal to the next draft
+ *       accepts it): every sequence, whatever its temperature, is verified
+ *       against target[b][i], which then holds the target's own pick at row
+ *       i -- a draw from softmax(lp_i / t) (dmtp_lm_head with a draw key), or
+ *       the argmax at t = 0.  L = first i < K with d_i != target[b][i] (else
+ *       K); commit d_0 .. d_{L-1}, target[b][L].  temperature, logits, lse,
+ *       u_acc and final_key are not read.
  * out_tokens [B, K+1] is -1 padded, n_out = accept_len + 1. */
 typedef struct {
   int32_t B, K, V;
@@ -253,16 +263,45 @@ typedef struct {
   int32_t* accept_len;        /* [B] */
   int32_t* out_tokens;        /* [B, K + 1] */
   int32_t* n_out;             /* [B] */
+  int32_t target_only;        /* 0: greedy (t = 0) / rejection (t > 0); 1: target-only */
 } dmtp_verify_desc;
 
 size_t dmtp_verify_ws(const dmtp_verify_desc* d);
 int dmtp_verify(const dmtp_verify_desc* d, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ----------------------------------------------------- acceptance stats ----
+ * Acceptance statistics of verify rounds (DMTP blog section 7: per-verify
+ * acceptance length and its histogram; section 7 "Position-Wise Acceptance":
+ * cumulative P(L >= k) and conditional acceptance).  Adds the B accepted
+ * lengths to a running histogram and, optionally, summarises it:
+ *   hist[k] += #{b : accept_len[b] == k}, k = 0..K   (lengths outside [0, K]
+ *       are not counted; hist is caller-owned device memory, accumulated
+ *       across calls -- zero it before the first)
+ *   summary (NULL to skip), from the updated histogram, N = sum_k hist[k]:
+ *     [0]         per-verify length 1 + sum_k k hist[k] / N (the committed
+ *                 correction/bonus token included)
+ *     [1]         first-candidate acceptance 1 - hist[0] / N
+ *     [2 + k - 1] cumulative P(L >= k), k = 1..K
+ *     [2 + K + k - 1] conditional P(L >= k | L >= k-1), k = 1..K
+ *                 (NaN where the condition has no rounds; all NaN when N = 0)
+ * Needs no workspace.  Integer counts make the histogram exact and the result
+ * independent of the order of rows. */
+typedef struct {
+  int32_t B;                  /* >= 0 rows in this call */
+  int32_t K;                  /* 1 .. 64 candidates per round */
+  const int32_t* accept_len;  /* [B] */
+  int64_t* hist;              /* [K + 1], accumulated */
+  double* summary;            /* [2 + 2K] or NULL */
+} dmtp_stats_desc;
+
+int dmtp_accept_stats(const dmtp_stats_desc* d, hipStream_t stream);
+
 /* ------------------------------------------------------------- helpers ---- */
 const char* dmtp_status_str(int status);
 const char* dmtp_version(void);
 /* sizeof of the descriptor structs, for bindings to check their layout:
- * which = 0 rows, 1 fuse, 2 layer, 3 draft, 4 head segment, 5 head, 6 verify */
+ * which = 0 rows, 1 fuse, 2 layer, 3 draft, 4 head segment, 5 head, 6 verify,
+ * 7 stats */
 size_t dmtp_struct_size(int which);
 
 #ifdef __cplusplus

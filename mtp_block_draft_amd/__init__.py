@@ -15,11 +15,12 @@ import torch
 
 from . import _abi
 from ._abi import (DMTP_BF16, DMTP_F32, DMTP_NO_DRAW, DmtpError, DraftDesc, FuseDesc, HeadDesc,
-                   HeadSegment, Layer, Rows, VerifyDesc)
+                   HeadSegment, Layer, Rows, StatsDesc, VerifyDesc)
 
 lib = _abi.load()
 
-__all__ = ["lib", "fuse", "block_draft", "lm_head", "verify", "call", "workspace_bytes",
+__all__ = ["lib", "fuse", "block_draft", "lm_head", "verify", "accept_stats", "call",
+           "workspace_bytes",
            "DMTP_F32", "DMTP_BF16", "DMTP_NO_DRAW", "DmtpError", "version"]
 
 
@@ -179,9 +180,9 @@ def verify(*, B: int, K: int, V: int, t1: torch.Tensor, drafts: Optional[torch.T
            logits: Optional[torch.Tensor] = None, t1_lse: Optional[torch.Tensor] = None,
            draft_lse: Optional[torch.Tensor] = None, target_lse: Optional[torch.Tensor] = None,
            u_acc: Optional[torch.Tensor] = None, seed: int = 0,
-           final_key: Optional[torch.Tensor] = None,
+           final_key: Optional[torch.Tensor] = None, target_only: bool = False,
            ws: Optional[torch.Tensor] = None, run: bool = True) -> VerifyDesc:
-    """Greedy or rejection-sampling block verification (dmtp_verify)."""
+    """Greedy, rejection-sampling or target-only block verification (dmtp_verify)."""
     D = VerifyDesc()
     D.B, D.K, D.V = B, K, V
     D.t1, D.drafts, D.target = _ptr(t1), _ptr(drafts), _ptr(target)
@@ -189,6 +190,25 @@ def verify(*, B: int, K: int, V: int, t1: torch.Tensor, drafts: Optional[torch.T
     D.t1_lse, D.draft_lse, D.target_lse = _ptr(t1_lse), _ptr(draft_lse), _ptr(target_lse)
     D.u_acc, D.seed, D.final_key = _ptr(u_acc), seed, _ptr(final_key)
     D.accept_len, D.out_tokens, D.n_out = _ptr(accept_len), _ptr(out_tokens), _ptr(n_out)
+    D.target_only = 1 if target_only else 0
     if run:
         call("verify", D, ws)
+    return D
+
+
+def accept_stats(accept_len: torch.Tensor, K: int, hist: torch.Tensor,
+                 summary: Optional[torch.Tensor] = None, run: bool = True) -> StatsDesc:
+    """Add accept_len's histogram to hist (int64 [K+1]); summary float64 [2+2K] (dmtp_accept_stats)."""
+    if accept_len.dtype != torch.int32 or hist.dtype != torch.int64:
+        raise ValueError("accept_len must be int32 and hist int64")
+    if summary is not None and summary.dtype != torch.float64:
+        raise ValueError("summary must be float64")
+    D = StatsDesc()
+    D.B, D.K = accept_len.numel(), K
+    D.accept_len, D.hist, D.summary = _ptr(accept_len), _ptr(hist), _ptr(summary)
+    D._keep = (accept_len, hist, summary)
+    if run:
+        st = lib.dmtp_accept_stats(ctypes.byref(D), ctypes.c_void_p(_stream()))
+        if st != 0:
+            raise DmtpError("dmtp_accept_stats", st, lib.dmtp_status_str(st).decode())
     return D

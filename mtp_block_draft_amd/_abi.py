@@ -71,15 +71,20 @@ class VerifyDesc(ctypes.Structure):
                 ("logits", c_void_p), ("t1_lse", c_void_p), ("draft_lse", c_void_p),
                 ("target_lse", c_void_p), ("u_acc", c_void_p), ("seed", c_uint64),
                 ("final_key", c_void_p), ("accept_len", c_void_p), ("out_tokens", c_void_p),
-                ("n_out", c_void_p)]
+                ("n_out", c_void_p), ("target_only", c_int32)]
 
 
-_STRUCTS = [Rows, FuseDesc, Layer, DraftDesc, HeadSegment, HeadDesc, VerifyDesc]
+class StatsDesc(ctypes.Structure):
+    _fields_ = [("B", c_int32), ("K", c_int32), ("accept_len", c_void_p), ("hist", c_void_p),
+                ("summary", c_void_p)]
+
+
+_STRUCTS = [Rows, FuseDesc, Layer, DraftDesc, HeadSegment, HeadDesc, VerifyDesc, StatsDesc]
 
 # exported symbols of include/dmtp.h
 SYMBOLS = ["dmtp_fuse", "dmtp_fuse_ws", "dmtp_block_draft", "dmtp_block_draft_ws", "dmtp_lm_head",
-           "dmtp_lm_head_ws", "dmtp_verify", "dmtp_verify_ws", "dmtp_status_str", "dmtp_version",
-           "dmtp_struct_size"]
+           "dmtp_lm_head_ws", "dmtp_verify", "dmtp_verify_ws", "dmtp_accept_stats",
+           "dmtp_status_str", "dmtp_version", "dmtp_struct_size"]
 
 
 class DmtpError(RuntimeError):
@@ -101,6 +106,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         q = getattr(lib, name + "_ws")
         q.argtypes = [POINTER(desc)]
         q.restype = c_size_t
+    lib.dmtp_accept_stats.argtypes = [POINTER(StatsDesc), c_void_p]
+    lib.dmtp_accept_stats.restype = c_int
     lib.dmtp_status_str.argtypes = [c_int]
     lib.dmtp_status_str.restype = ctypes.c_char_p
     lib.dmtp_version.argtypes = []

@@ -196,10 +196,21 @@ int validate_verify(const dmtp_verify_desc* d) {
   CHECK(d->V >= 2 && d->V <= (1 << 26), DMTP_E_SHAPE);
   CHECK(d->t1 && d->target && d->accept_len && d->out_tokens && d->n_out, DMTP_E_NULL);
   if (d->K > 1) CHECK(d->drafts != nullptr, DMTP_E_NULL);
-  if (d->temperature) {
+  CHECK(d->target_only == 0 || d->target_only == 1, DMTP_E_ARG);
+  if (d->temperature && !d->target_only) {
     CHECK(d->logits && d->t1_lse && d->target_lse && d->u_acc && d->final_key, DMTP_E_NULL);
     if (d->K > 1) CHECK(d->draft_lse != nullptr, DMTP_E_NULL);
   }
+  return DMTP_OK;
+}
+
+int validate_stats(const dmtp_stats_desc* d) {
+  CHECK(d != nullptr, DMTP_E_NULL);
+  CHECK(d->B >= 0 && d->B <= (1 << 30), DMTP_E_SHAPE);
+  CHECK(d->K >= 1 && d->K <= accept_stats_max_k(), DMTP_E_SHAPE);
+  CHECK(d->hist != nullptr, DMTP_E_NULL);
+  if (d->B > 0) CHECK(d->accept_len != nullptr, DMTP_E_NULL);
+  CHECK(((uintptr_t)d->hist & 7u) == 0 && ((uintptr_t)d->summary & 7u) == 0, DMTP_E_ALIGN);
   return DMTP_OK;
 }
 
@@ -343,6 +354,13 @@ int dmtp_verify(const dmtp_verify_desc* d, void* ws, size_t ws_bytes, hipStream_
   return launch_status(verify_run(*d, ws, stream));
 }
 
+int dmtp_accept_stats(const dmtp_stats_desc* d, hipStream_t stream) {
+  int e = validate_stats(d);
+  if (e != DMTP_OK) return e;
+  if ((e = check_device()) != DMTP_OK) return e;
+  return launch_status(accept_stats_run(*d, stream));
+}
+
 const char* dmtp_status_str(int s) {
   switch (s) {
     case DMTP_OK: return "ok";
@@ -358,7 +376,7 @@ const char* dmtp_status_str(int s) {
   }
 }
 
-const char* dmtp_version(void) { return "dmtp 0.2.0 (gfx950, ABI 2)"; }
+const char* dmtp_version(void) { return "dmtp 0.3.0 (gfx950, ABI 3)"; }
 
 size_t dmtp_struct_size(int which) {
   switch (which) {
@@ -369,6 +387,7 @@ size_t dmtp_struct_size(int which) {
     case 4: return sizeof(dmtp_head_segment);
     case 5: return sizeof(dmtp_head_desc);
     case 6: return sizeof(dmtp_verify_desc);
+    case 7: return sizeof(dmtp_stats_desc);
     default: return 0;
   }
 }

@@ -97,5 +97,8 @@ hipError_t lm_head_run(const dmtp_head_desc& d, int M, void* ws, hipStream_t s);
 // ----------------------------------------------------------------- verify --
 size_t verify_ws_bytes(const dmtp_verify_desc& d);
 hipError_t verify_run(const dmtp_verify_desc& d, void* ws, hipStream_t s);
+// Largest K the acceptance-statistics kernel supports.
+int accept_stats_max_k();
+hipError_t accept_stats_run(const dmtp_stats_desc& d, hipStream_t s);
 
 }  // namespace dmtp

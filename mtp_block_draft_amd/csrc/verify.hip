@@ -9,6 +9,8 @@
 //          vocabulary chunks, Gumbel-max over log(max(0, p - q)) (and over log p
 //          for the zero-residual fallback) with the same Philox noise
 //   final  merges the chunk maxima and writes the correction/bonus token
+//   stats  acceptance histogram of a batch of verify rounds, added to a running
+//          histogram, and the statistics derived from it
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -35,6 +37,7 @@ struct VerifyParams {
   int32_t* accept_len;
   int32_t* out_tokens;
   int32_t* n_out;
+  int target_only;
   // workspace
   int32_t* list;       // [B]
   int32_t* list_pos;   // [B]
@@ -58,7 +61,8 @@ __global__ void verify_main_kernel(VerifyParams p) {
     const int b = c0 + threadIdx.x;
     int flag = 0;
     if (b < p.B) {
-      const float t = p.temperature ? p.temperature[b] : 0.f;
+      // target-only verification compares with the target's picks at any temperature
+      const float t = (p.temperature && !p.target_only) ? p.temperature[b] : 0.f;
       int L = 0, md = 0;
       if (t > 0.f) {
         const float it = 1.f / t;
@@ -191,6 +195,50 @@ __global__ __launch_bounds__(256) void verify_final_kernel(VerifyParams p) {
   if (lane == 0) p.out_tokens[(size_t)b * (p.K + 1) + p.accept_len[b]] = y;
 }
 
+constexpr int kStatsThreads = 256;
+constexpr int kStatsMaxK = 64;
+
+// One workgroup: LDS histogram of the batch, added to the running histogram
+// bin by bin (a single writer per bin), then the summary from the result.
+__global__ __launch_bounds__(kStatsThreads) void accept_stats_kernel(int B, int K,
+                                                                     const int32_t* accept_len,
+                                                                     int64_t* hist, double* summary) {
+  __shared__ int32_t h[kStatsMaxK + 1];
+  __shared__ int64_t tot[kStatsMaxK + 1];
+  for (int k = threadIdx.x; k <= K; k += blockDim.x) h[k] = 0;
+  __syncthreads();
+  for (int b = threadIdx.x; b < B; b += blockDim.x) {
+    const int L = accept_len[b];
+    if (L >= 0 && L <= K) atomicAdd(&h[L], 1);
+  }
+  __syncthreads();
+  for (int k = threadIdx.x; k <= K; k += blockDim.x) {
+    const int64_t v = hist[k] + h[k];
+    hist[k] = v;
+    tot[k] = v;
+  }
+  __syncthreads();
+  if (summary == nullptr || threadIdx.x != 0) return;
+  int64_t n = 0, wsum = 0;
+  for (int k = 0; k <= K; ++k) {
+    n += tot[k];
+    wsum += (int64_t)k * tot[k];
+  }
+  const double nan = __longlong_as_double(0x7FF8000000000000ll);
+  const double N = (double)n;
+  summary[0] = n ? 1.0 + (double)wsum / N : nan;
+  summary[1] = n ? 1.0 - (double)tot[0] / N : nan;
+  // P(L >= k) from the tail sums; conditional = P(L >= k) / P(L >= k - 1)
+  int64_t geq_prev = n;
+  int64_t tail = n;
+  for (int k = 1; k <= K; ++k) {
+    tail -= tot[k - 1];   // rounds with L >= k
+    summary[2 + k - 1] = n ? (double)tail / N : nan;
+    summary[2 + K + k - 1] = geq_prev ? (double)tail / (double)geq_prev : nan;
+    geq_prev = tail;
+  }
+}
+
 struct WsL {
   size_t list, list_pos, count, mode, part, total;
   int n_chunks;
@@ -207,7 +255,7 @@ WsL layout(const dmtp_verify_desc& d) {
   w.count = o; o = al(o + 4);
   w.mode = o; o = al(o + (size_t)d.B * 4);
   w.part = o;
-  if (d.temperature) o = al(o + (size_t)d.B * w.n_chunks * 2 * sizeof(Top2));
+  if (d.temperature && !d.target_only) o = al(o + (size_t)d.B * w.n_chunks * 2 * sizeof(Top2));
   w.total = o;
   return w;
 }
@@ -237,6 +285,7 @@ hipError_t verify_run(const dmtp_verify_desc& d, void* ws, hipStream_t s) {
   p.accept_len = d.accept_len;
   p.out_tokens = d.out_tokens;
   p.n_out = d.n_out;
+  p.target_only = d.target_only != 0;
   p.list = (int32_t*)(base + w.list);
   p.list_pos = (int32_t*)(base + w.list_pos);
   p.count = (int32_t*)(base + w.count);
@@ -245,10 +294,18 @@ hipError_t verify_run(const dmtp_verify_desc& d, void* ws, hipStream_t s) {
   p.n_chunks = w.n_chunks;
   hipLaunchKernelGGL(verify_main_kernel, dim3(1), dim3(1024), 0, s, p);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !d.temperature) return e;
+  if (e != hipSuccess || !d.temperature || d.target_only) return e;
   hipLaunchKernelGGL(verify_scan_kernel, dim3(2048), dim3(kScanThreads), 0, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(verify_final_kernel, dim3((d.B + 3) / 4), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+int accept_stats_max_k() { return kStatsMaxK; }
+
+hipError_t accept_stats_run(const dmtp_stats_desc& d, hipStream_t s) {
+  hipLaunchKernelGGL(accept_stats_kernel, dim3(1), dim3(kStatsThreads), 0, s, d.B, d.K,
+                     d.accept_len, d.hist, d.summary);
   return hipGetLastError();
 }
 

@@ -18,6 +18,18 @@ so step 5 reads one contiguous matrix.  Sampled sequences keep their float32
 logits rows in a [B, 2K+1, V] buffer: candidate rows 0..K-1, target rows
 K..2K.  The planted workload (T1 set to the target argmax) adds the B target
 rows of position 0 to step 2 as a second, strided segment.
+
+Verification follows the configuration: "rejection" (greedy at temperature 0,
+rejection sampling above it) or "target_only", where step 5 draws the
+target's own pick at each target row of a sampled sequence (its draw keys)
+and step 6 compares the candidates with those picks.  accept_stats() adds
+the round's accepted lengths to a running histogram on the device.
+
+capture() records the six calls once into a HIP graph (through torch's graph
+capture of the stream they are enqueued on); replay() then submits the whole
+round -- T1 head, candidate write, embedding gather, residual, drafter, head
+and verification -- as one launch.  The calls allocate nothing and record no
+memset, so the captured round reads and writes the same buffers as run().
 """
 from __future__ import annotations
 
@@ -27,8 +39,8 @@ from typing import Dict, Optional
 import numpy as np
 import torch
 
-from . import (DMTP_NO_DRAW, block_draft, call, fuse, head_segment, layer_arg, lib, lm_head,
-               verify, workspace_bytes)
+from . import (DMTP_NO_DRAW, accept_stats, block_draft, call, fuse, head_segment, layer_arg, lib,
+               lm_head, verify, workspace_bytes)
 
 
 def _dev(a: np.ndarray, dtype: torch.dtype, device) -> torch.Tensor:
@@ -69,6 +81,7 @@ class Round:
         tau = inp.tau.astype(np.float32)
         sampled = tau > 0
         self.any_sampled = bool(sampled.any())
+        self.target_only = getattr(cfg, "verify", "rejection") == "target_only"
         plant = inp.plant.astype(bool)
         self.any_plant = bool(plant.any())
         self.seed = int(inp.philox_seed)
@@ -107,6 +120,10 @@ class Round:
             c_temp = np.concatenate([tm, tt]).astype(np.float32)
             c_key = np.full(M2, DMTP_NO_DRAW, dtype=np.uint64)
             c_key[:nd] = inp.draft_keys[:, 1:].reshape(-1)
+            if self.target_only:
+                # the target's own picks at the rows of sampled sequences
+                c_key[nd:] = np.where(np.repeat(sampled, K + 1), inp.target_keys.reshape(-1),
+                                      DMTP_NO_DRAW).astype(np.uint64)
             bb = np.repeat(np.arange(B), K - 1)
             jj = np.tile(np.arange(K - 1), B)
             s_mask = np.where(sampled[bb], bb * R2 + 1 + jj, -1)
@@ -167,7 +184,10 @@ class Round:
                                temperature=self.v_temp, logits=self.logits,
                                t1_lse=self.t1_lse[:B], draft_lse=self.lse[:nd],
                                target_lse=self.lse[nd:], u_acc=self.u_acc, seed=self.seed,
-                               final_key=self.final_key, run=False)
+                               final_key=self.final_key, target_only=self.target_only,
+                               run=False)
+        self.hist = torch.zeros(K + 1, dtype=torch.int64, device=dv)
+        self.summary = torch.zeros(2 + 2 * K, dtype=torch.float64, device=dv)
         self.steps = [("fuse", self.d_fuse_mtp), ("lm_head", self.d_head_t1),
                       ("fuse", self.d_fuse_delta), ("block_draft", self.d_draft),
                       ("lm_head", self.d_head_c), ("verify", self.d_verify)]
@@ -188,6 +208,28 @@ class Round:
             st = fn(ref, self._ws_ptr, self._ws_bytes, s)
             if st != 0:
                 raise RuntimeError(f"dmtp_{name}: {lib.dmtp_status_str(st).decode()}")
+
+    def capture(self) -> None:
+        """Record one round into a HIP graph for replay()."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.run()           # first calls outside capture: kernel attributes, device checks
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.run()
+        torch.cuda.synchronize()
+        self.graph = g
+
+    def replay(self) -> None:
+        """Submit the captured round on the current stream."""
+        self.graph.replay()
+
+    def accept_stats(self) -> None:
+        """Add this round's accepted lengths to self.hist and refresh self.summary."""
+        accept_stats(self.accept_len, self.cfg.K, self.hist, self.summary)
 
     def results(self) -> Dict[str, np.ndarray]:
         torch.cuda.synchronize()

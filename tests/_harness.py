@@ -39,8 +39,12 @@ def _margins(res: odm.RoundResult) -> Dict[tuple, float]:
     return m
 
 
-def _first_mismatch(res: odm.RoundResult, g: Dict[str, np.ndarray], tau: np.ndarray):
-    """(key, gpu_value) of the first decision where the two sides differ, or None."""
+def _first_mismatch(res: odm.RoundResult, g: Dict[str, np.ndarray], tau: np.ndarray,
+                    target_only: bool = False):
+    """(key, gpu_value) of the first decision where the two sides differ, or None.
+
+    Under target-only verification the accepted length has no decision of its
+    own: it follows from the candidates and the picks, compared before it."""
     K = res.drafts.shape[1]
     for r, b in enumerate(res.seqs):
         if g["t1"][b] != res.t1[r]:
@@ -53,7 +57,7 @@ def _first_mismatch(res: odm.RoundResult, g: Dict[str, np.ndarray], tau: np.ndar
                 return ("y", b, i), int(g["target_argmax"][b, i])
         Lg, Lo = int(g["accept_len"][b]), int(res.accept_len[r])
         if Lg != Lo:
-            if tau[b] > 0:
+            if tau[b] > 0 and not target_only:
                 i = min(Lg, Lo)
                 return ("accept", b, i), int(Lg > i)
             return ("accept_len", b), Lg          # greedy: no decision of its own
@@ -81,7 +85,7 @@ def compare_round(inp, g: Dict[str, np.ndarray], seqs: Optional[Sequence[int]] =
     overrides: Dict[tuple, int] = {}
     exempt: List[Tuple[tuple, float]] = []
     for _ in range(max_replays):
-        mm = _first_mismatch(res, g, inp.tau)
+        mm = _first_mismatch(res, g, inp.tau, getattr(cfg, "verify", "") == "target_only")
         if mm is None:
             break
         key, gv = mm

@@ -144,6 +144,41 @@ def test_verify_argument_errors(lib):
     d.drafts = FAKE
     need = lib.dmtp_verify_ws(ctypes.byref(d))
     assert need > 0 and _call(lib, "dmtp_verify", d, ws_bytes=need - 1) == -4
+    d.target_only = 2                 # a flag: 0 or 1
+    assert _call(lib, "dmtp_verify", d, ws_bytes=need) == -8
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="needs a machine without a GPU")
+def test_target_only_verify_needs_no_logits(lib):
+    """Target-only verification reads only the picks: with temperatures but no
+    logits, lse or uniforms it passes validation and reaches the device check."""
+    d = abi.VerifyDesc()
+    d.B, d.K, d.V = 3, 7, 1000
+    d.t1 = d.drafts = d.target = d.accept_len = d.out_tokens = d.n_out = FAKE
+    d.temperature = FAKE
+    d.target_only = 1
+    need = lib.dmtp_verify_ws(ctypes.byref(d))
+    assert need > 0 and _call(lib, "dmtp_verify", d, ws_bytes=need) == -6
+
+
+def test_accept_stats_argument_errors(lib):
+    def st(**over):
+        d = abi.StatsDesc()
+        d.B, d.K, d.accept_len, d.hist, d.summary = 10, 7, FAKE, FAKE, FAKE
+        for k, v in over.items():
+            setattr(d, k, v)
+        return lib.dmtp_accept_stats(ctypes.byref(d), None)
+
+    assert lib.dmtp_accept_stats(None, None) == -1
+    assert st(K=0) == -2
+    assert st(K=65) == -2
+    assert st(B=-1) == -2
+    assert st(hist=None) == -1
+    assert st(accept_len=None) == -1
+    assert st(hist=FAKE + 4) == -5
+    if torch.cuda.device_count() == 0:
+        assert st(B=0, accept_len=None) == -6      # valid: only the device check is left
+        assert st(summary=None) == -6
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="needs a machine without a GPU")

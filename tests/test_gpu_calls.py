@@ -382,3 +382,67 @@ def test_verify_greedy_and_sampled(dm, V):
             assert margins["final"] < NEAR_TIE, (b, out[b, L], toks[L], margins["final"])
         k = (b // 2) % (K + 1)
         assert L == k
+
+
+def test_verify_target_only_compares_with_the_picks(dm):
+    """Target-only: every sequence, sampled or not, commits the matching prefix of
+    its candidates and the target's pick at the first mismatch (or the bonus);
+    nothing but the picks is read."""
+    B, K, V = 40, 7, 1000
+    r = np.random.default_rng(9)
+    picks = r.integers(0, V, size=(B, K + 1)).astype(np.int32)
+    drafts = r.integers(0, V, size=(B, K)).astype(np.int32)
+    for b in range(B):
+        k = b % (K + 1)
+        drafts[b, :k] = picks[b, :k]
+        if k < K and drafts[b, k] == picks[b, k]:
+            drafts[b, k] = (picks[b, k] + 1) % V
+    tau = np.where(np.arange(B) % 3 == 0, 0.0, 1.0).astype(np.float32)
+    acc = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    out = torch.full((B, K + 1), -7, dtype=torch.int32, device="cuda")
+    n_out = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    dm.verify(B=B, K=K, V=V, t1=_t(drafts[:, 0], torch.int32), drafts=_t(drafts[:, 1:], torch.int32),
+              target=_t(picks, torch.int32), accept_len=acc, out_tokens=out, n_out=n_out,
+              temperature=_t(tau, torch.float32), target_only=True)
+    acc, out, n_out = acc.cpu().numpy(), out.cpu().numpy(), n_out.cpu().numpy()
+    for b in range(B):
+        L, toks = odm.verify_target_only(drafts[b], lambda i: picks[b, i])
+        assert acc[b] == L == b % (K + 1)
+        assert list(out[b, :L + 1]) == toks and n_out[b] == L + 1
+        assert np.all(out[b, L + 1:] == -1)
+
+
+# ------------------------------------------------------------- acceptance stats
+
+
+def _stats_summary(st, K):
+    return np.array([st["per_verify"], st["first_candidate"]] + list(st["cumulative"]) +
+                    list(st["conditional"]), dtype=np.float64)
+
+
+@pytest.mark.parametrize("K", [1, 7, 16, 64])
+def test_accept_stats_match_the_oracle(dm, K):
+    r = np.random.default_rng(K)
+    hist = torch.zeros(K + 1, dtype=torch.int64, device="cuda")
+    summ = torch.zeros(2 + 2 * K, dtype=torch.float64, device="cuda")
+    seen = []
+    for B in (1, 300, 4097, 0):
+        # skewed lengths, plus out-of-range values that are not counted
+        L = np.minimum(r.geometric(0.35, size=B) - 1, K).astype(np.int32)
+        if B > 10:
+            L[:3] = [-1, K + 1, 1 << 20]
+        dm.accept_stats(_t(L, torch.int32) if B else torch.empty(0, dtype=torch.int32, device="cuda"),
+                        K, hist, summ)
+        seen.extend(int(x) for x in L if 0 <= x <= K)
+        st = odm.acceptance_stats(np.array(seen, dtype=np.int64), K)
+        assert hist.cpu().numpy().tolist() == st["hist"]
+        got = summ.cpu().numpy()
+        np.testing.assert_allclose(got, _stats_summary(st, K), rtol=1e-14, equal_nan=True)
+
+
+def test_accept_stats_of_an_empty_histogram_are_nan(dm):
+    K = 5
+    hist = torch.zeros(K + 1, dtype=torch.int64, device="cuda")
+    summ = torch.zeros(2 + 2 * K, dtype=torch.float64, device="cuda")
+    dm.accept_stats(torch.empty(0, dtype=torch.int32, device="cuda"), K, hist, summ)
+    assert np.all(hist.cpu().numpy() == 0) and np.all(np.isnan(summ.cpu().numpy()))

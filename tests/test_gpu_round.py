@@ -61,6 +61,32 @@ def test_tiny_sampled_f32(rnd):
         _report(f"{cfg.name}/{seed}", rep)
 
 
+def test_tiny_sampled_target_only_f32(rnd):
+    cfg = synth.CONFIGS["tiny_sampled_f32"].with_(verify="target_only")
+    for seed in (303, 304, 305, 306):
+        inp = synth.make_inputs(cfg.with_(seed=seed))
+        ht = correlated_targets(inp, cfg.rho)
+        R, g = _run(rnd, inp, h_target=ht)
+        res, rep = compare_round(inp, g, h_target=ht)
+        _report(f"{cfg.name}/target_only/{seed}", rep)
+
+
+def test_ragged_mixed_target_only_bf16(rnd):
+    cfg = synth.RoundConfig(name="ragged_mixed_target_only", B=6, H=512, V=3001, Hq=8, Hkv=2,
+                            d=64, F=768, n_layers=2, K=7, ctx_min=0, ctx_max=700, dtype="bf16",
+                            tau_mode="mixed", plant_frac=0.5, gain_std=0.1, verify="target_only",
+                            seed=12)
+    inp = synth.make_inputs(cfg)
+    R, g = _run(rnd, inp)
+    res, rep = compare_round(inp, g)
+    _report(cfg.name, rep)
+    # the device histogram of the round equals the oracle's statistics
+    R.accept_stats()
+    from oracle import dmtp as odm
+    st = odm.acceptance_stats(res.accept_len, cfg.K)
+    assert R.hist.cpu().numpy().tolist() == st["hist"]
+
+
 def test_ragged_mixed_bf16(rnd):
     """Several tiles, ragged contexts (including empty), mixed greedy/sampled, planted T1."""
     cfg = synth.RoundConfig(name="ragged_mixed", B=6, H=512, V=3001, Hq=8, Hkv=2, d=64, F=768,
@@ -114,9 +140,47 @@ def test_chat_b128_mixed_full_size(rnd):
 
 
 @pytest.mark.timeout(900)
+def test_chat_b128_target_only_full_size(rnd):
+    cfg = synth.CONFIGS["chat_b128_mixed_bf16"].with_(verify="target_only")
+    inp = synth.make_inputs(cfg)
+    R, g = _run(rnd, inp)
+    seqs = list(range(1, cfg.B, 5))
+    res, rep = compare_round(inp, g, seqs=seqs)
+    _report(f"{cfg.name}/target_only", rep)
+    assert inp.tau[seqs].min() == 0 and inp.tau[seqs].max() > 0
+
+
+@pytest.mark.timeout(900)
 def test_long_block16_full_size(rnd):
     cfg = synth.CONFIGS["long_block16_bf16"]
     inp = synth.make_inputs(cfg)
     R, g = _run(rnd, inp)
     res, rep = compare_round(inp, g, seqs=[0, 5])
     _report(cfg.name, rep)
+
+
+@pytest.mark.timeout(900)
+def test_whole_round_graph_replays_match_eager(rnd):
+    """The round captured as one graph gives, on every replay, the eager round's
+    results bit for bit; eager work and synchronisations sit between replays."""
+    for name in ("tiny_sampled_f32", "chat_b128_mixed_bf16"):
+        cfg = synth.CONFIGS[name]
+        inp = synth.make_inputs(cfg)
+        R = rnd(inp)
+        R.run()
+        want = R.results()
+        R.capture()
+        keys = ("t1", "x_t1", "hd_mask", "drafts", "target_argmax", "target_lse", "accept_len",
+                "out_tokens", "n_out")
+        for rep in range(4):
+            # clobber the outputs eagerly, then replay into them
+            R.out_tokens.fill_(-9)
+            R.accept_len.fill_(-9)
+            R.head_in[: R.n_draft_rows].zero_()
+            torch.cuda.synchronize()
+            R.replay()
+            got = R.results()
+            for k in keys:
+                np.testing.assert_array_equal(got[k], want[k], err_msg=f"{name} replay {rep} {k}")
+        if name == "tiny_sampled_f32":
+            res, rep_ = compare_round(inp, want)
