@@ -104,6 +104,20 @@ struct u64x4 {
   uint64_t x, y, z, w;
 };
 
+// hi:lo = a * m, the full 128-bit product, from four 32 x 32 -> 64 partial
+// products (each a single multiply-add on the vector unit):
+//   a m = p00 + 2^32 (a0 m1 + a1 m0) + 2^64 a1 m1, with the middle terms folded
+//   one at a time so that no partial sum exceeds 64 bits.
+__device__ __forceinline__ void mulhilo64(uint64_t a, uint64_t m, uint64_t& hi, uint64_t& lo) {
+  const uint32_t a0 = (uint32_t)a, a1 = (uint32_t)(a >> 32);
+  const uint32_t m0 = (uint32_t)m, m1 = (uint32_t)(m >> 32);
+  const uint64_t p00 = (uint64_t)a0 * m0;
+  const uint64_t p01 = (uint64_t)a0 * m1 + (p00 >> 32);
+  const uint64_t p10 = (uint64_t)a1 * m0 + (uint32_t)p01;
+  hi = (uint64_t)a1 * m1 + (p01 >> 32) + (p10 >> 32);
+  lo = (p10 << 32) | (uint32_t)p00;
+}
+
 __device__ __forceinline__ u64x4 philox4x64_10(u64x4 c, uint64_t k0, uint64_t k1) {
   const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
   const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
@@ -113,8 +127,9 @@ __device__ __forceinline__ u64x4 philox4x64_10(u64x4 c, uint64_t k0, uint64_t k1
       k0 += W0;
       k1 += W1;
     }
-    const uint64_t hi0 = __umul64hi(M0, c.x), lo0 = M0 * c.x;
-    const uint64_t hi1 = __umul64hi(M1, c.z), lo1 = M1 * c.z;
+    uint64_t hi0, lo0, hi1, lo1;
+    mulhilo64(c.x, M0, hi0, lo0);
+    mulhilo64(c.z, M1, hi1, lo1);
     c = u64x4{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
   }
   return c;
@@ -199,6 +214,15 @@ __device__ __forceinline__ Top2 top2_merge(const Top2& a, const Top2& b) {
     r.v2 = fmaxf(a.v2, b.v1);
   }
   return r;
+}
+
+// Running top-2 of a lane that sees its indices in increasing order: an equal
+// value never displaces the earlier (lower) index, so no index compare is needed.
+__device__ __forceinline__ void top2_push_inc(Top2& t, float v, int i) {
+  const bool gt = v > t.v1;
+  t.v2 = fmaxf(t.v2, fminf(v, t.v1));
+  t.i1 = gt ? i : t.i1;
+  t.v1 = gt ? v : t.v1;
 }
 
 __device__ __forceinline__ Top2 top2_shfl_xor(const Top2& t, int mask) {

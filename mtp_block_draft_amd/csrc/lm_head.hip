@@ -637,47 +637,65 @@ __global__ void head_plan_kernel(HeadParams p) {
   if (threadIdx.x == 0) p.list_count[0] = base;
 }
 
-constexpr int kScanThreads = 256;
-constexpr int kScanChunk = kScanThreads * 8;  // vocabulary entries per work item
+// Gumbel-max scan.  A work item is (list index, vocabulary chunk of kScanChunk
+// entries) and belongs to one wave: lane l takes the 8-entry blocks
+// l, l + 64, ... of the chunk (kScanU of them), issues all of their loads
+// first, then the Philox words of each block, score_j = l_j / t + g_j and a
+// running top-2 in increasing j; one butterfly merge per item gives the
+// chunk's partial.  Waves stride over the items, so the grid is sized to the
+// machine, not to the batch.
+constexpr int kScanWaves = 4;
+constexpr int kScanU = 4;
+constexpr int kScanChunk = kWave * 8 * kScanU;   // 2048 vocabulary entries per item
 
-// Gumbel-max scan: item = (list index, chunk); score_j = l_j / t + g_j.
-__global__ __launch_bounds__(kScanThreads) void head_scan_kernel(HeadParams p) {
-  __shared__ Top2 red[kScanThreads / kWave];
-  const int count = p.list_count[0];
-  const int items = count * p.n_chunks;
-  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+__device__ __forceinline__ Top2 wave_top2(Top2 t) {
+#pragma unroll
+  for (int mask = 1; mask < kWave; mask <<= 1) t = top2_merge(t, top2_shfl_xor(t, mask));
+  return t;
+}
+
+__global__ __launch_bounds__(kScanWaves * kWave) void head_scan_kernel(HeadParams p) {
+  const int lane = threadIdx.x % kWave;
+  const int nw = gridDim.x * kScanWaves;
+  const int items = p.list_count[0] * p.n_chunks;
+  const bool vec = (p.V & 3) == 0;
+  for (int item = blockIdx.x * kScanWaves + threadIdx.x / kWave; item < items; item += nw) {
     const int li = item / p.n_chunks, ch = item % p.n_chunks;
     const int m = p.list[li];
     const float it = 1.f / p.temperature[m];
+    const uint64_t key = p.draw_key[m];
     const float* lr = p.logits + (size_t)p.store_row[m] * p.V;
-    const int j0 = ch * kScanChunk + 8 * threadIdx.x;
+    const int base = ch * kScanChunk + 8 * lane;
     Top2 t = top2_empty();
-    if (j0 < p.V) {
-      uint32_t w[8];
-      philox_words8(p.seed, p.draw_key[m], (uint64_t)(j0 >> 3), w);
-      float l[8];
-      if (j0 + 8 <= p.V && (p.V & 3) == 0) {
-        const float4 a = *(const float4*)(lr + j0), b = *(const float4*)(lr + j0 + 4);
-        l[0] = a.x; l[1] = a.y; l[2] = a.z; l[3] = a.w; l[4] = b.x; l[5] = b.y; l[6] = b.z; l[7] = b.w;
-      } else {
+    if (vec && ch * kScanChunk + kScanChunk <= p.V) {
+      float4 a[kScanU], b[kScanU];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) l[k] = j0 + k < p.V ? lr[j0 + k] : 0.f;
+      for (int u = 0; u < kScanU; ++u) {
+        a[u] = *(const float4*)(lr + base + 512 * u);
+        b[u] = *(const float4*)(lr + base + 512 * u + 4);
       }
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int j = j0 + k;
-        if (j < p.V) top2_push(t, l[k] * it + gumbel_fast(w[k]), j);
+      for (int u = 0; u < kScanU; ++u) {
+        const int j0 = base + 512 * u;
+        uint32_t w[8];
+        philox_words8(p.seed, key, (uint64_t)(j0 >> 3), w);
+        const float l[8] = {a[u].x, a[u].y, a[u].z, a[u].w, b[u].x, b[u].y, b[u].z, b[u].w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) top2_push_inc(t, fmaf(l[k], it, gumbel_fast(w[k])), j0 + k);
+      }
+    } else {
+      // the last chunk (or rows that are not 16-byte aligned): entry by entry
+      for (int u = 0; u < kScanU; ++u) {
+        const int j0 = base + 512 * u;
+        if (j0 >= p.V) break;
+        uint32_t w[8];
+        philox_words8(p.seed, key, (uint64_t)(j0 >> 3), w);
+        for (int k = 0; k < 8 && j0 + k < p.V; ++k)
+          top2_push_inc(t, fmaf(lr[j0 + k], it, gumbel_fast(w[k])), j0 + k);
       }
     }
-#pragma unroll
-    for (int mask = 1; mask < kWave; mask <<= 1) t = top2_merge(t, top2_shfl_xor(t, mask));
-    if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = t;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      for (int w2 = 1; w2 < kScanThreads / kWave; ++w2) t = top2_merge(t, red[w2]);
-      p.scan_part[(size_t)li * p.n_chunks + ch] = t;
-    }
-    __syncthreads();
+    t = wave_top2(t);
+    if (lane == 0) p.scan_part[(size_t)li * p.n_chunks + ch] = t;
   }
 }
 
@@ -813,7 +831,7 @@ hipError_t lm_head_run(const dmtp_head_desc& d, int M, void* ws, hipStream_t s) 
   if (d.temperature) {
     hipLaunchKernelGGL(head_plan_kernel, dim3(1), dim3(1024), 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(head_scan_kernel, dim3(2048), dim3(kScanThreads), 0, s, p);
+    hipLaunchKernelGGL(head_scan_kernel, dim3(2048), dim3(kScanWaves * kWave), 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   hipLaunchKernelGGL(head_finalize_kernel, dim3((M + 3) / 4), dim3(256), 0, s, p);

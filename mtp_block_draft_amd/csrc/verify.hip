@@ -18,8 +18,13 @@ namespace dmtp {
 
 namespace {
 
-constexpr int kScanThreads = 256;
-constexpr int kChunk = kScanThreads * 8;
+// Scan work items are (sequence in the draw list, vocabulary chunk of kChunk
+// entries), one wave each: lane l takes the 8-entry blocks l, l + 64, ...
+// (kScanU of them), loads them all before any arithmetic and keeps running
+// top-2s in increasing index; one butterfly merge per item.
+constexpr int kScanWaves = 4;
+constexpr int kScanU = 4;
+constexpr int kChunk = kWave * 8 * kScanU;
 
 struct VerifyParams {
   int B, K, V;
@@ -116,39 +121,78 @@ __global__ void verify_main_kernel(VerifyParams p) {
   if (threadIdx.x == 0) p.count[0] = base;
 }
 
-__global__ __launch_bounds__(kScanThreads) void verify_scan_kernel(VerifyParams p) {
-  __shared__ Top2 red[2][kScanThreads / kWave];
+// Per entry j of the scanned rows: a = log p_j = lp_j / t - lse_p; the bonus /
+// fallback score a + g_j; in residual mode c = log q_j and the residual score
+// log(p_j - q_j) + g_j where p_j > q_j (the same Gumbel noise g_j).
+__device__ __forceinline__ void verify_entry(float lp, float lq, float it, float lse_p, float lse_q,
+                                             bool resid, uint32_t word, int j, Top2& tr, Top2& tp) {
+  const float g = gumbel_fast(word);
+  const float a = fmaf(lp, it, -lse_p);
+  top2_push_inc(tp, a + g, j);
+  if (resid) {
+    const float c = fmaf(lq, it, -lse_q);
+    const float sres = a > c ? a + log1m_exp(c - a) : -INFINITY;
+    top2_push_inc(tr, sres + g, j);
+  }
+}
+
+__global__ __launch_bounds__(kScanWaves * kWave) void verify_scan_kernel(VerifyParams p) {
+  const int lane = threadIdx.x % kWave;
+  const int nw = gridDim.x * kScanWaves;
   const int items = p.count[0] * p.n_chunks;
   const int K = p.K, V = p.V;
-  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+  const bool vec = (V & 3) == 0;
+  for (int item = blockIdx.x * kScanWaves + threadIdx.x / kWave; item < items; item += nw) {
     const int li = item / p.n_chunks, ch = item % p.n_chunks;
     const int b = p.list[li];
     const int L = p.accept_len[b];
-    const int md = p.mode[b];
+    const bool resid = p.mode[b] == 1;
     const float it = 1.f / p.temperature[b];
     const float* rows = p.logits + (size_t)b * (2 * K + 1) * V;
     // residual at row L: p row K + L, q row L; bonus: p row 2K
     const float* pr = rows + (size_t)(K + L) * V;
     const float* qr = rows + (size_t)L * V;
     const float lse_p = p.target_lse[(size_t)b * (K + 1) + L];
-    const float lse_q = md == 1 ? (L == 0 ? p.t1_lse[b] : p.draft_lse[(size_t)b * (K - 1) + L - 1]) : 0.f;
+    const float lse_q = resid ? (L == 0 ? p.t1_lse[b] : p.draft_lse[(size_t)b * (K - 1) + L - 1]) : 0.f;
+    const uint64_t key = p.final_key[b];
+    const int base = ch * kChunk + 8 * lane;
     Top2 tr = top2_empty(), tp = top2_empty();
-    const int j0 = ch * kChunk + 8 * threadIdx.x;
-    if (j0 < V) {
-      uint32_t w[8];
-      philox_words8(p.seed, p.final_key[b], (uint64_t)(j0 >> 3), w);
+    if (vec && ch * kChunk + kChunk <= V) {
+      float4 pa[kScanU], pb[kScanU], qa[kScanU], qb[kScanU];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int j = j0 + k;
-        if (j >= V) break;
-        const float g = gumbel_fast(w[k]);
-        const float a = pr[j] * it - lse_p;          // log p_j
-        top2_push(tp, a + g, j);
-        if (md == 1) {
-          const float c = qr[j] * it - lse_q;        // log q_j
-          const float s = a > c ? a + log1m_exp(c - a) : -INFINITY;   // log(p_j - q_j)
-          top2_push(tr, s + g, j);
+      for (int u = 0; u < kScanU; ++u) {
+        pa[u] = *(const float4*)(pr + base + 512 * u);
+        pb[u] = *(const float4*)(pr + base + 512 * u + 4);
+      }
+      if (resid) {
+#pragma unroll
+        for (int u = 0; u < kScanU; ++u) {
+          qa[u] = *(const float4*)(qr + base + 512 * u);
+          qb[u] = *(const float4*)(qr + base + 512 * u + 4);
         }
+      } else {
+#pragma unroll
+        for (int u = 0; u < kScanU; ++u) qa[u] = qb[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < kScanU; ++u) {
+        const int j0 = base + 512 * u;
+        uint32_t w[8];
+        philox_words8(p.seed, key, (uint64_t)(j0 >> 3), w);
+        const float lp[8] = {pa[u].x, pa[u].y, pa[u].z, pa[u].w, pb[u].x, pb[u].y, pb[u].z, pb[u].w};
+        const float lq[8] = {qa[u].x, qa[u].y, qa[u].z, qa[u].w, qb[u].x, qb[u].y, qb[u].z, qb[u].w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) verify_entry(lp[k], lq[k], it, lse_p, lse_q, resid, w[k], j0 + k, tr, tp);
+      }
+    } else {
+      for (int u = 0; u < kScanU; ++u) {
+        const int j0 = base + 512 * u;
+        if (j0 >= V) break;
+        uint32_t w[8];
+        philox_words8(p.seed, key, (uint64_t)(j0 >> 3), w);
+        for (int k = 0; k < 8 && j0 + k < V; ++k)
+          verify_entry(pr[j0 + k], resid ? qr[j0 + k] : 0.f, it, lse_p, lse_q, resid, w[k], j0 + k,
+                       tr, tp);
       }
     }
 #pragma unroll
@@ -156,20 +200,10 @@ __global__ __launch_bounds__(kScanThreads) void verify_scan_kernel(VerifyParams 
       tr = top2_merge(tr, top2_shfl_xor(tr, mask));
       tp = top2_merge(tp, top2_shfl_xor(tp, mask));
     }
-    if (threadIdx.x % kWave == 0) {
-      red[0][threadIdx.x / kWave] = tr;
-      red[1][threadIdx.x / kWave] = tp;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      for (int w2 = 1; w2 < kScanThreads / kWave; ++w2) {
-        tr = top2_merge(tr, red[0][w2]);
-        tp = top2_merge(tp, red[1][w2]);
-      }
+    if (lane == 0) {
       p.part[((size_t)li * p.n_chunks + ch) * 2 + 0] = tr;
       p.part[((size_t)li * p.n_chunks + ch) * 2 + 1] = tp;
     }
-    __syncthreads();
   }
 }
 
@@ -295,7 +329,7 @@ hipError_t verify_run(const dmtp_verify_desc& d, void* ws, hipStream_t s) {
   hipLaunchKernelGGL(verify_main_kernel, dim3(1), dim3(1024), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !d.temperature || d.target_only) return e;
-  hipLaunchKernelGGL(verify_scan_kernel, dim3(2048), dim3(kScanThreads), 0, s, p);
+  hipLaunchKernelGGL(verify_scan_kernel, dim3(2048), dim3(kScanWaves * kWave), 0, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(verify_final_kernel, dim3((d.B + 3) / 4), dim3(256), 0, s, p);
   return hipGetLastError();
