@@ -61,6 +61,7 @@ class RoundConfig:
     w_zero: bool = False         # DMTP residual projection W zero-initialised
     n_anchor: int = 2
     verify: str = "rejection"    # "rejection" | "target_only" (rows with tau > 0)
+    mtp_block: bool = False      # h_MTP from an MTP decoder block over h' (else h_MTP = h')
     window: int = 0              # 0 = every context position, else the last `window`
     rope_base: float = 1.0e6
     eps: float = 1.0e-6
@@ -153,6 +154,10 @@ def _layer_tid(layer: int, name: str) -> int:
     return 100 + 16 * layer + _TID[name]
 
 
+def _mtp_tid(name: str) -> int:
+    return 2000 + _TID[name]
+
+
 _CHUNK = 1 << 22  # elements per independent random stream of a large tensor
 _POOL: Optional[ThreadPoolExecutor] = None
 
@@ -240,6 +245,9 @@ class RoundInputs:
     g_f: np.ndarray        # [H] final norm before the LM head, MTP rows
     g_final: np.ndarray    # [H] final norm of the block drafter
     layers: List[LayerInputs]
+    mtp_layers: List[LayerInputs]  # the MTP decoder block (empty unless cfg.mtp_block); its
+    #                                ctx_k / ctx_v are the block's own causal KV cache, one row
+    #                                per context position (lengths ctx_len, offsets cu_ctx)
     ctx_len: np.ndarray    # [B] int32
     cu_ctx: np.ndarray     # [B + 1] int32 prefix sums of ctx_len
     anchor: np.ndarray     # [B] int32   A: emitted, not yet processed by the target
@@ -289,6 +297,22 @@ def make_inputs(cfg: RoundConfig, *, with_layers: bool = True) -> RoundInputs:
                 ctx_v=t("ctx_v", (total, cfg.Hkv, cfg.d), 1.0),
             ))
 
+    mtp_layers: List[LayerInputs] = []
+    if with_layers and cfg.mtp_block:
+        def tm(name, shape, sd):
+            return _normal_t(cfg, _mtp_tid(name), shape, sd, dt)
+        mtp_layers.append(LayerInputs(
+            g_attn=_gain(cfg, _mtp_tid("g_attn"), H),
+            wqkv=tm("wqkv", (cfg.qkv_dim, H), std),
+            wo=tm("wo", (H, cfg.Hq * cfg.d), std),
+            g_ffn=_gain(cfg, _mtp_tid("g_ffn"), H),
+            wg=tm("wg", (cfg.F, H), std),
+            wu=tm("wu", (cfg.F, H), std),
+            wd=tm("wd", (H, cfg.F), std),
+            ctx_k=tm("ctx_k", (total, cfg.Hkv, cfg.d), 1.0),
+            ctx_v=tm("ctx_v", (total, cfg.Hkv, cfg.d), 1.0),
+        ))
+
     anchor = _rng(cfg, _TID["anchor"]).integers(0, V - 1, size=B).astype(np.int32)
     h_prev = _normal_t(cfg, _TID["h_prev"], (B, H), 1.0, dt)
     h_target = _normal_t(cfg, _TID["h_target"], (B, K + 1, H), 1.0, dt)
@@ -324,7 +348,7 @@ def make_inputs(cfg: RoundConfig, *, with_layers: bool = True) -> RoundInputs:
         g_h=_gain(cfg, _TID["g_h"], H), g_e=_gain(cfg, _TID["g_e"], H),
         g_e2=_gain(cfg, _TID["g_e2"], H), g_m=_gain(cfg, _TID["g_m"], H),
         g_f=_gain(cfg, _TID["g_f"], H), g_final=_gain(cfg, _TID["g_final"], H),
-        layers=layers, ctx_len=ctx_len, cu_ctx=cu_ctx, anchor=anchor,
+        layers=layers, mtp_layers=mtp_layers, ctx_len=ctx_len, cu_ctx=cu_ctx, anchor=anchor,
         h_prev=h_prev, h_target=h_target, tau=tau, u_acc=u_acc, plant=plant,
         philox_seed=philox_seed, draft_keys=draft_keys, final_keys=final_keys,
         target_keys=target_keys)

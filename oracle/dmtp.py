@@ -10,7 +10,10 @@ One round for a sequence whose last emitted-but-unprocessed token is A:
   1. MTP input fusion  h' = M [RMSNorm(h); RMSNorm(Emb(A))]      ([DvM] "MTP:
      Sequential Prediction Heads ...", module-input equation; [colibri]: the
      head input pairs the backbone's post-final-norm output with the next
-     token's embedding).  No MTP decoder block is in scope: h_MTP := h'.
+     token's embedding).  h_MTP is the output of the MTP decoder block over h'
+     (a pre-norm Transformer block with its own causal KV cache: [DvM] the
+     same section; [DMTP] section 6.5; [colibri]) when the workload has one,
+     else h' itself.
   2. T1 = the MTP candidate: LM head on RMSNorm(h_MTP), argmax or a draw
      ([DMTP] section 5, step 1; section 6.4 keeps highest-probability selection).
   3. DMTP residual  Delta = W [RMS_e(e_T1); RMS_m(h_MTP)],  e~ = e_T1 + Delta
@@ -157,46 +160,91 @@ def layer64(lw) -> Layer64:
     return Layer64(lw.g_attn, lw.wqkv, lw.wo, lw.g_ffn, lw.wg, lw.wu, lw.wd)
 
 
-def draft_layer(X: np.ndarray, positions: np.ndarray, lw: Layer64,
-                ctx_k: Sequence[np.ndarray], ctx_v: Sequence[np.ndarray], *, Hq: int, Hkv: int,
-                d: int, eps: float, rope_base: float, window: int = 0) -> np.ndarray:
-    """One pre-norm decoder layer of the block drafter for n sequences.
+def decoder_layer(X: np.ndarray, positions: np.ndarray, lw: Layer64,
+                  ctx_k: Sequence[np.ndarray], ctx_v: Sequence[np.ndarray], *, Hq: int, Hkv: int,
+                  d: int, eps: float, rope_base: float, window: int = 0, causal: bool = False):
+    """One pre-norm decoder layer over n sequences of S new rows each.
 
-    X is [n, S, H] (the S slots of each sequence), positions [n, S];
-    ctx_k[i] / ctx_v[i] are the context keys / values [L_i, Hkv, d] of sequence i.
-    Attention: every slot's query reads its own sequence's context keys (the
-    last `window` of them when window > 0) and all S block keys, with no mask
-    -- the block-diagonal (bidirectional) part plus the offset block-causal
-    part of the DFlash mask, which for one block is "see everything" ([DvM]
-    "DFlash: Block Diffusion ...", three-component mask; [DMTP] section 6.2
-    window).  GQA: query head h reads kv head h // (Hq / Hkv).  Context keys
-    arrive already rotated; block q and k are rotated at the slot positions.
-    The projections are row-wise, so they are taken for all sequences at once.
+    X is [n, S, H], positions [n, S]; ctx_k[i] / ctx_v[i] are the keys /
+    values [L_i, Hkv, d] that row i's sequence already holds (already rotated).
+    x^ = RMSNorm(X; g_attn); q, k, v = x^ Wqkv^T; q and k rotated at the row
+    positions; each query reads the held keys (the last `window` when
+    window > 0) and the new rows' keys -- all S of them, or, when causal, rows
+    0..j for row j; GQA maps query head h to kv head h // (Hq / Hkv);
+    X1 = X + o Wo^T; X2 = X1 + (silu(x^2 Wg^T) * (x^2 Wu^T)) Wd^T with
+    x^2 = RMSNorm(X1; g_ffn).  Returns (X2, k, v), k rotated, both [n, S, Hkv, d]:
+    the rows a cache appends.  The projections are row-wise, so they are
+    taken for all sequences at once.
     """
     n, S, H = X.shape
     xh = nm.rmsnorm(X, lw.g_attn, eps)
     qkv = nm.matmul_nt(xh.reshape(n * S, H), lw.wqkv).reshape(n, S, -1)
     group = Hq // Hkv
     o = np.empty((n, S, Hq, d))
+    k_all = np.empty((n, S, Hkv, d))
+    v_all = np.empty((n, S, Hkv, d))
     for i in range(n):
         q = nm.rope(qkv[i, :, : Hq * d].reshape(S, Hq, d), positions[i], rope_base)
         k = nm.rope(qkv[i, :, Hq * d: (Hq + Hkv) * d].reshape(S, Hkv, d), positions[i], rope_base)
         v = qkv[i, :, (Hq + Hkv) * d:].reshape(S, Hkv, d)
+        k_all[i], v_all[i] = k, v
         ck = np.asarray(ctx_k[i], dtype=np.float64)
         cv = np.asarray(ctx_v[i], dtype=np.float64)
         if window > 0 and ck.shape[0] > window:
             ck, cv = ck[-window:], cv[-window:]
         keys = np.concatenate([ck, k], axis=0)     # [n_ctx + S, Hkv, d]
         vals = np.concatenate([cv, v], axis=0)
+        n_ctx = ck.shape[0]
         for kv in range(Hkv):
             kk = np.ascontiguousarray(keys[:, kv])
             vv = np.ascontiguousarray(vals[:, kv])
             for h in range(kv * group, (kv + 1) * group):
-                o[i, :, h] = nm.attention(q[:, h], kk, vv)
+                if not causal:
+                    o[i, :, h] = nm.attention(q[:, h], kk, vv)
+                else:
+                    for j in range(S):
+                        o[i, j, h] = nm.attention(q[j: j + 1, h], kk[: n_ctx + j + 1],
+                                                  vv[: n_ctx + j + 1])[0]
     X1 = X + nm.matmul_nt(o.reshape(n * S, Hq * d), lw.wo).reshape(n, S, H)
     xh2 = nm.rmsnorm(X1, lw.g_ffn, eps).reshape(n * S, H)
     a = nm.silu(nm.matmul_nt(xh2, lw.wg)) * nm.matmul_nt(xh2, lw.wu)
-    return X1 + nm.matmul_nt(a, lw.wd).reshape(n, S, H)
+    return X1 + nm.matmul_nt(a, lw.wd).reshape(n, S, H), k_all, v_all
+
+
+def draft_layer(X: np.ndarray, positions: np.ndarray, lw: Layer64,
+                ctx_k: Sequence[np.ndarray], ctx_v: Sequence[np.ndarray], *, Hq: int, Hkv: int,
+                d: int, eps: float, rope_base: float, window: int = 0) -> np.ndarray:
+    """One layer of the block drafter: decoder_layer over the S draft slots with
+    no mask -- every slot's query reads its sequence's context keys and all S
+    block keys, the block-diagonal (bidirectional) part plus the offset
+    block-causal part of the DFlash mask, which for one block is "see
+    everything" ([DvM] "DFlash: Block Diffusion ...", three-component mask;
+    [DMTP] section 6.2 window)."""
+    return decoder_layer(X, positions, lw, ctx_k, ctx_v, Hq=Hq, Hkv=Hkv, d=d, eps=eps,
+                         rope_base=rope_base, window=window)[0]
+
+
+def mtp_block(X: np.ndarray, positions: np.ndarray, layers64: Sequence[Layer64],
+              cache_k: Sequence[Sequence[np.ndarray]], cache_v: Sequence[Sequence[np.ndarray]], *,
+              Hq: int, Hkv: int, d: int, eps: float, rope_base: float):
+    """The MTP decoder block over S new rows per sequence ([DvM] "MTP: Sequential
+    Prediction Heads ...": a dedicated Transformer block after the input
+    projection; [DMTP] section 6.5: full-history causal attention, projections,
+    normalisation and a feed-forward network; [colibri]: the head keeps its own
+    causal KV cache, to which every completed pair contributes its K/V).
+
+    X [n, S, H] holds the fused inputs h' of the new rows, at positions
+    [n, S]; cache_k[l][i] / cache_v[l][i] are layer l's cached keys / values of
+    sequence i (the whole history: no window).  Row j attends to the cache and
+    to new rows 0..j.  Returns (h_MTP [n, S, H] -- the block output, with no
+    final norm -- and per layer the (k, v) rows [n, S, Hkv, d] to append).
+    """
+    kv = []
+    for l, lw in enumerate(layers64):
+        X, k, v = decoder_layer(X, positions, lw, cache_k[l], cache_v[l], Hq=Hq, Hkv=Hkv, d=d,
+                                eps=eps, rope_base=rope_base, window=0, causal=True)
+        kv.append((k, v))
+    return X, kv
 
 
 def block_draft(slots: Sequence[np.ndarray], ctx_len: np.ndarray, layers64: Sequence[Layer64],
@@ -304,7 +352,8 @@ def verify_rejection(drafts: Sequence[int], p_rows, q_rows, accept: Callable, dr
 @dataclass
 class RoundResult:
     seqs: List[int]
-    h_mtp: np.ndarray        # [n, H]
+    h_fused: np.ndarray      # [n, H] h' = M [RMSNorm(h); RMSNorm(E(A))]
+    h_mtp: np.ndarray        # [n, H] h' or the MTP block's output
     z1: np.ndarray           # [n, H] rounded LM-head input of the T1 rows
     x_t1: np.ndarray         # [n, H] E(T1) + Delta
     hd: np.ndarray           # [n, S, H] rounded final-normed drafter output, all slots
@@ -319,6 +368,7 @@ class RoundResult:
     out_tokens: np.ndarray   # [n, K + 1], -1 padded
     n_out: np.ndarray        # [n]
     decisions: List[Tuple[tuple, int, float]] = field(default_factory=list)
+    mtp_kv: Optional[list] = None            # per MTP layer (k, v) [n, 1, Hkv, d] to append
     q_logits: Optional[np.ndarray] = None   # [n, K, V] when keep_logits
     p_logits: Optional[np.ndarray] = None   # [n, K + 1, V]
 
@@ -366,8 +416,21 @@ def run_round(inp, seqs: Optional[Sequence[int]] = None,
     tgt_gap = nm.top2_gap(p_logits)
     tt = np.where(tau > 0, tau, 1.0)
 
-    # -- 1. MTP input fusion (the MTP block itself is out of scope: h_MTP = h') --
-    h_mtp = fuse(inp.h_prev[seqs], E[inp.anchor[seqs]], inp.g_h, inp.g_e, inp.fuse_M, eps)
+    # -- 1. MTP input fusion, then the MTP decoder block when the workload has one
+    #       (otherwise h_MTP = h') --
+    h_fused = fuse(inp.h_prev[seqs], E[inp.anchor[seqs]], inp.g_h, inp.g_e, inp.fuse_M, eps)
+    mtp_kv = None
+    if getattr(cfg, "mtp_block", False):
+        spans = [(int(inp.cu_ctx[b]), int(inp.cu_ctx[b + 1])) for b in seqs]
+        ml = inp.mtp_layers
+        out, mtp_kv = mtp_block(h_fused[:, None, :], inp.ctx_len[seqs][:, None].astype(np.int64),
+                                [layer64(lw) for lw in ml],
+                                [[lw.ctx_k[lo:hi] for lo, hi in spans] for lw in ml],
+                                [[lw.ctx_v[lo:hi] for lo, hi in spans] for lw in ml],
+                                Hq=cfg.Hq, Hkv=cfg.Hkv, d=cfg.d, eps=eps, rope_base=cfg.rope_base)
+        h_mtp = out[:, 0]
+    else:
+        h_mtp = h_fused
 
     # -- 2. T1 from the shared head on RMSNorm(h_MTP; g_f), rounded to the head dtype --
     z1 = rf(nm.rmsnorm(h_mtp, inp.g_f, eps))
@@ -454,11 +517,11 @@ def run_round(inp, seqs: Optional[Sequence[int]] = None,
         out_tokens[r, : len(toks)] = toks
 
     return RoundResult(
-        seqs=seqs, h_mtp=h_mtp, z1=z1, x_t1=x_t1, hd=hd, t1=t1, drafts=drafts,
+        seqs=seqs, h_fused=h_fused, h_mtp=h_mtp, z1=z1, x_t1=x_t1, hd=hd, t1=t1, drafts=drafts,
         target_argmax=y_final, q_lse=q_lse, p_lse=p_lse,
         q_max=q_logits.max(axis=-1), p_max=p_logits.max(axis=-1),
         accept_len=accept_len, out_tokens=out_tokens, n_out=accept_len + 1,
-        decisions=decisions,
+        decisions=decisions, mtp_kv=mtp_kv,
         q_logits=q_logits if keep_logits else None,
         p_logits=p_logits if keep_logits else None)
 
