@@ -38,7 +38,8 @@ def _workload_desc(cfg) -> str:
     return (f"{cfg.name}: B={cfg.B}, H={cfg.H}, V={cfg.V}, {cfg.n_layers} draft layer(s) "
             f"{cfg.Hq}q/{cfg.Hkv}kv x{cfg.d}, F={cfg.F}, K={cfg.K} candidates "
             f"({cfg.S} slots, {cfg.R} verify rows), ctx U[{cfg.ctx_min},{cfg.ctx_max}], "
-            f"tau={cfg.tau_mode}, verify={cfg.verify}")
+            f"tau={cfg.tau_mode}, verify={cfg.verify}"
+            + (", MTP decoder block" if cfg.mtp_block else ""))
 
 
 # Sources the LM-head GEMM is compiled from; a counter summary taken on other
@@ -163,6 +164,9 @@ def main() -> int:
                          "GEMM is still timed by its dispatch events in an eager pass)")
     ap.add_argument("--verify", choices=["rejection", "target_only"], default=None,
                     help="verification of sampled rows (default: the workload's)")
+    ap.add_argument("--mtp-block", action="store_true",
+                    help="h_MTP from an MTP decoder block (drafter layer shapes, causal over its "
+                         "own KV cache) instead of h_MTP = h'")
     ap.add_argument("--cpu-seqs", type=int, default=8, help="sequences in the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -194,6 +198,8 @@ def main() -> int:
     cfg = synth.CONFIGS[args.config]
     if args.verify:
         cfg = cfg.with_(verify=args.verify)
+    if args.mtp_block:
+        cfg = cfg.with_(mtp_block=True)
     inp = synth.make_inputs(cfg)
     R = Round(inp)
     stream = torch.cuda.current_stream()
@@ -324,8 +330,7 @@ def main() -> int:
                    "submission": "one HIP graph per round" if args.graph else "six calls per round"},
         "accepted_tokens_per_s": round(rounds_s * committed, 1),
         "committed_tokens_per_round": committed,
-        "phases_us": dict(zip(["fuse_mtp", "lm_head_t1", "fuse_delta", "block_draft",
-                               "lm_head_draft_target", "verify"], [round(x, 2) for x in per_call_us])),
+        "phases_us": dict(zip(R.step_names, [round(x, 2) for x in per_call_us])),
         "roofline": roofline,
     }
     if graph_ms_step is not None:

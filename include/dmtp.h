@@ -7,10 +7,11 @@
  * hidden is added to T1's embedding slot, one parallel block-draft forward over
  * [E(A), E(T1)+Delta, E(MASK)...] proposes the remaining candidates, and the
  * target verifies all of them, committing the accepted prefix plus one
- * correction or bonus token.  Four calls cover it, and a fifth summarises
- * acceptance over rounds:
+ * correction or bonus token.  Four calls cover it; the MTP decoder block and a
+ * summary of acceptance over rounds complete the set:
  *
  *   dmtp_fuse         RMSNorm-concat-projection (MTP input fusion; DMTP residual)
+ *   dmtp_mtp_block    the MTP decoder block (causal, with its own KV cache)
  *   dmtp_block_draft  the block drafter's layers and final norm
  *   dmtp_lm_head      the shared vocabulary head with argmax / sampling
  *   dmtp_verify       greedy, rejection-sampling or target-only block verification
@@ -49,7 +50,7 @@
 extern "C" {
 #endif
 
-#define DMTP_ABI_VERSION 3
+#define DMTP_ABI_VERSION 4
 
 enum dmtp_status {
   DMTP_OK = 0,
@@ -154,6 +155,42 @@ typedef struct {
 
 size_t dmtp_block_draft_ws(const dmtp_draft_desc* d);
 int dmtp_block_draft(const dmtp_draft_desc* d, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------ MTP block ----
+ * The MTP decoder block ("DFlash vs MTP", "MTP: Sequential Prediction Heads
+ * Trained With the Model": a dedicated Transformer block after the input
+ * projection h' = M[RMSNorm(h); RMSNorm(Emb(t))]; DMTP blog section 6.5:
+ * full-history causal attention, projections, normalisation and a
+ * feed-forward network; colibri: the head keeps its own causal KV cache, to
+ * which every completed pair contributes its K/V).  Per sequence b, S new rows
+ * x[b, j] (the fused inputs h' produced by dmtp_fuse) at positions
+ * ctx_len[b] + j, where ctx_len[b] = cu_ctx[b+1] - cu_ctx[b] is the length of
+ * the block's cache.  Each of the n_layers layers is the decoder layer of
+ * dmtp_block_draft, except that row j attends to the whole cache (no window)
+ * and to new rows 0..j only (causal); layers[l].ctx_k / ctx_v are layer l's
+ * cache [sum ctx_len, Hkv, d] in dtype, keys already rotated.
+ *   out [B, S, H] float32: h_MTP of each new row, the residual stream after the
+ *       last layer (no final norm; the LM head applies its own).
+ *   k_new[l] / v_new[l] (HOST array of n_layers device pointers, or NULL):
+ *       [B, S, Hkv, d] in dtype, layer l's rotated keys and values of the new
+ *       rows -- what the caller appends to the cache once the rows are
+ *       committed.  A NULL entry skips that output. */
+typedef struct {
+  int32_t B, S, H, Hq, Hkv, d, F, n_layers, dtype;
+  float eps;
+  float rope_base;
+  int32_t max_ctx;        /* host-side upper bound of ctx_len[b] */
+  int32_t ctx_rows;       /* rows of each layer's cache; sequences are clamped to them */
+  const float* x;         /* [B, S, H] float32 */
+  const int32_t* cu_ctx;  /* [B + 1] prefix sums of the cache lengths */
+  const dmtp_layer* layers;   /* HOST array of n_layers entries */
+  float* out;             /* [B, S, H] float32 */
+  void* const* k_new;     /* HOST array of n_layers pointers, or NULL */
+  void* const* v_new;     /* HOST array of n_layers pointers, or NULL */
+} dmtp_mtp_desc;
+
+size_t dmtp_mtp_block_ws(const dmtp_mtp_desc* d);
+int dmtp_mtp_block(const dmtp_mtp_desc* d, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* -------------------------------------------------------------- LM head ----
  * The shared vocabulary head ("DFlash vs MTP": shared output head; DMTP blog
@@ -301,7 +338,7 @@ const char* dmtp_status_str(int status);
 const char* dmtp_version(void);
 /* sizeof of the descriptor structs, for bindings to check their layout:
  * which = 0 rows, 1 fuse, 2 layer, 3 draft, 4 head segment, 5 head, 6 verify,
- * 7 stats */
+ * 7 stats, 8 MTP block */
 size_t dmtp_struct_size(int which);
 
 #ifdef __cplusplus

@@ -15,11 +15,11 @@ import torch
 
 from . import _abi
 from ._abi import (DMTP_BF16, DMTP_F32, DMTP_NO_DRAW, DmtpError, DraftDesc, FuseDesc, HeadDesc,
-                   HeadSegment, Layer, Rows, StatsDesc, VerifyDesc)
+                   HeadSegment, Layer, MtpDesc, Rows, StatsDesc, VerifyDesc)
 
 lib = _abi.load()
 
-__all__ = ["lib", "fuse", "block_draft", "lm_head", "verify", "accept_stats", "call",
+__all__ = ["lib", "fuse", "mtp_block", "block_draft", "lm_head", "verify", "accept_stats", "call",
            "workspace_bytes",
            "DMTP_F32", "DMTP_BF16", "DMTP_NO_DRAW", "DmtpError", "version"]
 
@@ -131,6 +131,32 @@ def block_draft(out: torch.Tensor, *, B: int, H: int, Hq: int, Hkv: int, d: int,
     D.g_final, D.out = _ptr(g_final), _ptr(out)
     if run:
         call("block_draft", D, ws)
+    return D
+
+
+def mtp_block(out: torch.Tensor, x: torch.Tensor, *, Hq: int, Hkv: int, d: int, F: int,
+              layers: Sequence[Layer], cu_ctx: torch.Tensor, max_ctx: int, ctx_rows: int,
+              dtype: int, k_new: Optional[Sequence[torch.Tensor]] = None,
+              v_new: Optional[Sequence[torch.Tensor]] = None, eps: float = 1e-6,
+              rope_base: float = 1e6, ws: Optional[torch.Tensor] = None,
+              run: bool = True) -> MtpDesc:
+    """The MTP decoder block over x [B, S, H] float32 (dmtp_mtp_block)."""
+    D = MtpDesc()
+    D.B, D.S, D.H = x.shape
+    D.Hq, D.Hkv, D.d, D.F, D.n_layers, D.dtype = Hq, Hkv, d, F, len(layers), dtype
+    D.eps, D.rope_base, D.max_ctx, D.ctx_rows = eps, rope_base, max_ctx, ctx_rows
+    arr = (Layer * len(layers))(*layers)
+    D.layers = ctypes.cast(arr, ctypes.POINTER(Layer))
+    keep = [arr, x, out, cu_ctx]
+    D.x, D.cu_ctx, D.out = _ptr(x), _ptr(cu_ctx), _ptr(out)
+    for name, ts in (("k_new", k_new), ("v_new", v_new)):
+        if ts is not None:
+            ptrs = (ctypes.c_void_p * len(layers))(*[_ptr(t) for t in ts])
+            setattr(D, name, ctypes.cast(ptrs, ctypes.POINTER(ctypes.c_void_p)))
+            keep += [ptrs, list(ts)]
+    D._keep = keep
+    if run:
+        call("mtp_block", D, ws)
     return D
 
 

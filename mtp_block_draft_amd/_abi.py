@@ -79,10 +79,21 @@ class StatsDesc(ctypes.Structure):
                 ("summary", c_void_p)]
 
 
-_STRUCTS = [Rows, FuseDesc, Layer, DraftDesc, HeadSegment, HeadDesc, VerifyDesc, StatsDesc]
+class MtpDesc(ctypes.Structure):
+    _fields_ = [("B", c_int32), ("S", c_int32), ("H", c_int32), ("Hq", c_int32), ("Hkv", c_int32),
+                ("d", c_int32), ("F", c_int32), ("n_layers", c_int32), ("dtype", c_int32),
+                ("eps", c_float), ("rope_base", c_float), ("max_ctx", c_int32),
+                ("ctx_rows", c_int32), ("x", c_void_p), ("cu_ctx", c_void_p),
+                ("layers", POINTER(Layer)), ("out", c_void_p), ("k_new", POINTER(c_void_p)),
+                ("v_new", POINTER(c_void_p))]
+
+
+_STRUCTS = [Rows, FuseDesc, Layer, DraftDesc, HeadSegment, HeadDesc, VerifyDesc, StatsDesc,
+            MtpDesc]
 
 # exported symbols of include/dmtp.h
-SYMBOLS = ["dmtp_fuse", "dmtp_fuse_ws", "dmtp_block_draft", "dmtp_block_draft_ws", "dmtp_lm_head",
+SYMBOLS = ["dmtp_fuse", "dmtp_fuse_ws", "dmtp_mtp_block", "dmtp_mtp_block_ws", "dmtp_block_draft",
+           "dmtp_block_draft_ws", "dmtp_lm_head",
            "dmtp_lm_head_ws", "dmtp_verify", "dmtp_verify_ws", "dmtp_accept_stats",
            "dmtp_status_str", "dmtp_version", "dmtp_struct_size"]
 
@@ -98,7 +109,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         raise ImportError(f"{path} is not built; run `python -m mtp_block_draft_amd.build` "
                           "(the DMTP path has no fallback)")
     lib = ctypes.CDLL(path)
-    for name, desc in (("dmtp_fuse", FuseDesc), ("dmtp_block_draft", DraftDesc),
+    for name, desc in (("dmtp_fuse", FuseDesc), ("dmtp_mtp_block", MtpDesc),
+                       ("dmtp_block_draft", DraftDesc),
                        ("dmtp_lm_head", HeadDesc), ("dmtp_verify", VerifyDesc)):
         f = getattr(lib, name)
         f.argtypes = [POINTER(desc), c_void_p, c_size_t, c_void_p]

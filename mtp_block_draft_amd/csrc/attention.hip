@@ -473,7 +473,8 @@ __global__ __launch_bounds__(64) void attn_wave_kernel(
 }
 
 // Merge the chunk partials and the S block keys; o [B * S, Hq * D] as bf16
-// planes (hi at o, lo at o + o_pst).
+// planes (hi at o, lo at o + o_pst).  causal != 0: the query of slot s reads
+// block keys 0..s only (the context keys in full).
 // One wave per query row (rows r = 4 blockIdx.y + wave of kv head blockIdx.x);
 // lane l owns dims l (and l + 64 when D = 128).  Every global load that does
 // not depend on another one -- the query row, the chunk maxima and sums, the
@@ -486,7 +487,7 @@ template <int D>
 __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(
     const float* __restrict__ q, const float* __restrict__ kb, const float* __restrict__ vb,
     const float* __restrict__ part_o, const float* __restrict__ part_ml, int Hkv, int G, int S,
-    int NQP, int n_chunks, float scale, uint16_t* __restrict__ o, size_t o_pst) {
+    int NQP, int n_chunks, float scale, int causal, uint16_t* __restrict__ o, size_t o_pst) {
   constexpr int DL = D / kWave;   // dims per lane
   constexpr int CB = 16;          // chunk partials in flight per batch
   extern __shared__ __attribute__((aligned(16))) float kvs[];   // [2][S][D] block keys, values
@@ -533,8 +534,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(
   if (!live) return;
 
   float M = fmaxf(fmaxf(mc[0], mc[1]), fmaxf(mc[2], mc[3]));
-  float s_lane = -INFINITY;   // lane j < S: score of block key j
-  for (int j = 0; j < S; ++j) {
+  float s_lane = -INFINITY;   // lane j < S: score of block key j (-inf where hidden)
+  const int nvis = causal ? r / G + 1 : S;   // block keys this row sees (its own slot included)
+  for (int j = 0; j < nvis; ++j) {
     float part = 0.f;
 #pragma unroll
     for (int i = 0; i < DL; ++i) part = fmaf(qv[i], kvs[j * D + lane + kWave * i], part);
@@ -551,7 +553,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(
     w_chunk[wave][lane + kWave * i] = w;
     Lsum = fmaf(w, lc[i], Lsum);
   }
-  const float wb = lane < S ? expf(s_lane - M) : 0.f;
+  const float wb = lane < nvis ? expf(s_lane - M) : 0.f;
   Lsum = wave_sum(Lsum + wb);
   __threadfence_block();
   __builtin_amdgcn_wave_barrier();
@@ -573,7 +575,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(
       for (int i = 0; i < DL; ++i) acc[i] = w != 0.f ? fmaf(w, pv[c][i], acc[i]) : acc[i];
     }
   }
-  for (int j = 0; j < S; ++j) {
+  for (int j = 0; j < nvis; ++j) {
     const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wb), j));
 #pragma unroll
     for (int i = 0; i < DL; ++i) acc[i] = fmaf(w, kvs[S * D + j * D + lane + kWave * i], acc[i]);
@@ -655,6 +657,7 @@ AttnPlan attn_plan(int B, int Hq, int Hkv, int S, int d, int max_ctx, int window
   p.NQ = S * p.G;
   p.kv_f32 = kv_f32;
   p.window = window;
+  p.causal = 0;
   p.nqp = kv_f32 ? nqp_of(p.NQ) : 32 * ((p.NQ + 31) / 32);
   const int eff = (window > 0 && max_ctx > window) ? window : max_ctx;
   if (eff <= 0) {
@@ -744,10 +747,10 @@ hipError_t attention(const AttnPlan& p, const float* q, const float* kb, const f
   const size_t o_pst = (size_t)p.B * p.S * p.Hkv * p.G * p.d;
   if (p.d == 64)
     hipLaunchKernelGGL(attn_combine_kernel<64>, cgrid, dim3(kAttnThreads), clds, s, q, kb, vb, po, pml,
-                       p.Hkv, p.G, p.S, nqp, p.n_chunks, scale, o, o_pst);
+                       p.Hkv, p.G, p.S, nqp, p.n_chunks, scale, p.causal, o, o_pst);
   else
     hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, dim3(kAttnThreads), clds, s, q, kb, vb, po,
-                       pml, p.Hkv, p.G, p.S, nqp, p.n_chunks, scale, o, o_pst);
+                       pml, p.Hkv, p.G, p.S, nqp, p.n_chunks, scale, p.causal, o, o_pst);
   return hipGetLastError();
 }
 

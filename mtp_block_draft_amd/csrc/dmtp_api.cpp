@@ -77,6 +77,8 @@ size_t fuse_ws(const dmtp_fuse_desc* d) {
 }
 
 // ---------------------------------------------------------- block draft ----
+int check_layers(const dmtp_layer* layers, int n_layers, bool has_ctx);
+
 int validate_draft(const dmtp_draft_desc* d) {
   CHECK(d != nullptr, DMTP_E_NULL);
   CHECK(d->B >= 1 && d->B <= 4096, DMTP_E_SHAPE);
@@ -99,18 +101,29 @@ int validate_draft(const dmtp_draft_desc* d) {
   if (d->n_anchor == 2) CHECK(d->anchor_ids != nullptr, DMTP_E_NULL);
   CHECK(aligned16(d->x_t1) && aligned16(d->emb) && aligned16(d->g_final) && aligned16(d->out),
         DMTP_E_ALIGN);
-  for (int l = 0; l < d->n_layers; ++l) {
-    const dmtp_layer& L = d->layers[l];
-    CHECK(L.g_attn && L.wqkv && L.wo && L.g_ffn && L.wg && L.wu && L.wd, DMTP_E_NULL);
-    CHECK(aligned16(L.g_attn) && aligned16(L.wqkv) && aligned16(L.wo) && aligned16(L.g_ffn) &&
-              aligned16(L.wg) && aligned16(L.wu) && aligned16(L.wd),
-          DMTP_E_ALIGN);
-    if (d->max_ctx > 0 && d->ctx_rows > 0) {
-      CHECK(L.ctx_k && L.ctx_v, DMTP_E_NULL);
-      CHECK(aligned16(L.ctx_k) && aligned16(L.ctx_v), DMTP_E_ALIGN);
-    }
-  }
-  return DMTP_OK;
+  return check_layers(d->layers, d->n_layers, d->max_ctx > 0 && d->ctx_rows > 0);
+}
+
+// Shapes of a stack of decoder layers over B sequences of S rows (the drafter's
+// slots, or the MTP block's new rows).
+struct Stack {
+  int B, S, H, Hq, Hkv, d, F, n_layers, dtype;
+  float eps, rope_base;
+  int window, max_ctx, ctx_rows;
+  const dmtp_layer* layers;
+  const int32_t* cu_ctx;
+  int causal;
+};
+
+Stack stack_of(const dmtp_draft_desc* d) {
+  return Stack{d->B, d->K - 1 + d->n_anchor, d->H, d->Hq, d->Hkv, d->d, d->F, d->n_layers,
+               d->dtype, d->eps, d->rope_base, d->window, d->max_ctx, d->ctx_rows, d->layers,
+               d->cu_ctx, 0};
+}
+
+Stack stack_of(const dmtp_mtp_desc* d) {
+  return Stack{d->B, d->S, d->H, d->Hq, d->Hkv, d->d, d->F, d->n_layers, d->dtype, d->eps,
+               d->rope_base, 0, d->max_ctx, d->ctx_rows, d->layers, d->cu_ctx, 1};
 }
 
 struct DraftWs {
@@ -118,39 +131,147 @@ struct DraftWs {
   AttnPlan plan;
 };
 
-DraftWs draft_ws(const dmtp_draft_desc* d) {
+DraftWs stack_ws(const Stack& d) {
   DraftWs w;
-  const int S = d->K - 1 + d->n_anchor;
-  const size_t R = (size_t)d->B * S;
-  const int qkv_n = (d->Hq + 2 * d->Hkv) * d->d;
-  w.plan = attn_plan(d->B, d->Hq, d->Hkv, S, d->d, d->max_ctx, d->window, d->dtype == DMTP_F32,
-                     d->ctx_rows);
+  const int S = d.S;
+  const size_t R = (size_t)d.B * S;
+  const int qkv_n = (d.Hq + 2 * d.Hkv) * d.d;
+  w.plan = attn_plan(d.B, d.Hq, d.Hkv, S, d.d, d.max_ctx, d.window, d.dtype == DMTP_F32, d.ctx_rows);
+  w.plan.causal = d.causal;
   size_t gemm_max = 0;
-  const int wf32 = d->dtype == DMTP_F32;
+  const int wf32 = d.dtype == DMTP_F32;
   auto upd = [&](int M, int N, int K) {
     const size_t b = gemm_ws_bytes(M, N, K, wf32);
     if (b > gemm_max) gemm_max = b;
   };
-  upd((int)R, qkv_n, d->H);
-  upd((int)R, d->H, d->Hq * d->d);
-  upd((int)R, d->F, d->H);
-  upd((int)R, d->H, d->F);
+  upd((int)R, qkv_n, d.H);
+  upd((int)R, d.H, d.Hq * d.d);
+  upd((int)R, d.F, d.H);
+  upd((int)R, d.H, d.F);
   size_t o = 0;
-  w.X = o; o = al(o + R * d->H * 4);
-  w.xh = o; o = al(o + R * d->H * 4);
+  w.X = o; o = al(o + R * d.H * 4);
+  w.xh = o; o = al(o + R * d.H * 4);
   w.qkv = o; o = al(o + R * qkv_n * 4);
-  w.q = o; o = al(o + R * d->Hq * d->d * 4);
-  w.kb = o; o = al(o + R * d->Hkv * d->d * 4);
-  w.vb = o; o = al(o + R * d->Hkv * d->d * 4);
-  w.o = o; o = al(o + R * d->Hq * d->d * 4);
-  w.gate = o; o = al(o + R * d->F * 4);
-  w.up = o; o = al(o + R * d->F * 4);
-  w.act = o; o = al(o + R * d->F * 4);
+  w.q = o; o = al(o + R * d.Hq * d.d * 4);
+  w.kb = o; o = al(o + R * d.Hkv * d.d * 4);
+  w.vb = o; o = al(o + R * d.Hkv * d.d * 4);
+  w.o = o; o = al(o + R * d.Hq * d.d * 4);
+  w.gate = o; o = al(o + R * d.F * 4);
+  w.up = o; o = al(o + R * d.F * 4);
+  w.act = o; o = al(o + R * d.F * 4);
   w.gemm = o; o = al(o + gemm_max);
   w.gemm2 = o; o = al(o + gemm_max);   // the up projection's partials (live with the gate's)
   w.attn = o; o = al(o + attn_ws_bytes(w.plan));
   w.total = o;
   return w;
+}
+
+DraftWs draft_ws(const dmtp_draft_desc* d) { return stack_ws(stack_of(d)); }
+
+// The layers of a stack over X [B S, H] (float32, in the workspace), whose
+// first-layer norm planes are already in xh.  Layer l's rotated block keys and
+// values go to k_new[l] / v_new[l] when those are given.  On return *last is
+// the residual stream after the last layer, as a split result not yet summed.
+hipError_t run_stack(const Stack& d, const DraftWs& w, char* b, void* const* k_new,
+                     void* const* v_new, SplitOut* last, hipStream_t stream) {
+  float* X = (float*)(b + w.X);
+  uint16_t* xh = (uint16_t*)(b + w.xh);   // bf16 planes [2][R][H]
+  float* qkv = (float*)(b + w.qkv);
+  float* q = (float*)(b + w.q);
+  float* kb = (float*)(b + w.kb);
+  float* vb = (float*)(b + w.vb);
+  uint16_t* o = (uint16_t*)(b + w.o);     // bf16 planes [2][R][Hq d]
+  float* gate = (float*)(b + w.gate);
+  float* up = (float*)(b + w.up);
+  uint16_t* act = (uint16_t*)(b + w.act); // bf16 planes [2][R][F]
+  float* gws = (float*)(b + w.gemm);
+  float* gws2 = (float*)(b + w.gemm2);
+  float* aws = (float*)(b + w.attn);
+  const int S = d.S;
+  const int R = d.B * S;
+  const int qkv_n = (d.Hq + 2 * d.Hkv) * d.d;
+  const int wf32 = d.dtype == DMTP_F32;
+  const size_t pst_h = (size_t)R * d.H, pst_o = (size_t)R * d.Hq * d.d;
+  const int od = d.Hq * d.d;
+  hipError_t h = hipSuccess;
+  for (int l = 0; l < d.n_layers && h == hipSuccess; ++l) {
+    const dmtp_layer& L = d.layers[l];
+    SplitOut sq, so, sg, su, sd;
+    GemmArgs g1{xh, pst_h, (size_t)d.H, R, L.wqkv, wf32, (size_t)d.H, qkv_n, d.H, qkv,
+                (size_t)qkv_n, nullptr, 0};
+    if ((h = gemm_deferred(g1, gws, stream, &sq)) != hipSuccess) break;
+    if ((h = rope_split(sq, d.cu_ctx, d.ctx_rows, d.B, S, d.Hq, d.Hkv, d.d, d.rope_base, q, kb, vb,
+                        stream)) != hipSuccess)
+      break;
+    if ((k_new || v_new) &&
+        (h = export_kv(kb, vb, d.B, S, d.Hkv, d.d, d.dtype, k_new ? k_new[l] : nullptr,
+                       v_new ? v_new[l] : nullptr, stream)) != hipSuccess)
+      break;
+    if ((h = attention(w.plan, q, kb, vb, L.ctx_k, L.ctx_v, d.cu_ctx, d.ctx_rows, aws, o,
+                       stream)) != hipSuccess)
+      break;
+    GemmArgs g2{o, pst_o, (size_t)od, R, L.wo, wf32, (size_t)od, d.H, od, X, (size_t)d.H, X,
+                (size_t)d.H};
+    if ((h = gemm_deferred(g2, gws, stream, &so)) != hipSuccess) break;
+    if ((h = residual_rmsnorm(so, X, (size_t)d.H, 1, L.g_ffn, d.eps, xh, R, d.H, stream)) !=
+        hipSuccess)
+      break;
+    GemmArgs g3{xh, pst_h, (size_t)d.H, R, L.wg, wf32, (size_t)d.H, d.F, d.H, gate,
+                (size_t)d.F, nullptr, 0};
+    if ((h = gemm_deferred(g3, gws, stream, &sg)) != hipSuccess) break;
+    GemmArgs g4{xh, pst_h, (size_t)d.H, R, L.wu, wf32, (size_t)d.H, d.F, d.H, up,
+                (size_t)d.F, nullptr, 0};
+    if ((h = gemm_deferred(g4, gws2, stream, &su)) != hipSuccess) break;
+    if ((h = swiglu(sg, su, act, R, d.F, stream)) != hipSuccess) break;
+    const size_t pst_f = (size_t)R * d.F;
+    GemmArgs g5{act, pst_f, (size_t)d.F, R, L.wd, wf32, (size_t)d.F, d.H, d.F, X,
+                (size_t)d.H, X, (size_t)d.H};
+    if ((h = gemm_deferred(g5, gws, stream, &sd)) != hipSuccess) break;
+    if (l + 1 < d.n_layers)
+      h = residual_rmsnorm(sd, X, (size_t)d.H, 1, d.layers[l + 1].g_attn, d.eps, xh, R, d.H, stream);
+    else
+      *last = sd;
+  }
+  return h;
+}
+
+int check_layers(const dmtp_layer* layers, int n_layers, bool has_ctx) {
+  for (int l = 0; l < n_layers; ++l) {
+    const dmtp_layer& L = layers[l];
+    CHECK(L.g_attn && L.wqkv && L.wo && L.g_ffn && L.wg && L.wu && L.wd, DMTP_E_NULL);
+    CHECK(aligned16(L.g_attn) && aligned16(L.wqkv) && aligned16(L.wo) && aligned16(L.g_ffn) &&
+              aligned16(L.wg) && aligned16(L.wu) && aligned16(L.wd),
+          DMTP_E_ALIGN);
+    if (has_ctx) {
+      CHECK(L.ctx_k && L.ctx_v, DMTP_E_NULL);
+      CHECK(aligned16(L.ctx_k) && aligned16(L.ctx_v), DMTP_E_ALIGN);
+    }
+  }
+  return DMTP_OK;
+}
+
+// ------------------------------------------------------------ MTP block ----
+int validate_mtp(const dmtp_mtp_desc* d) {
+  CHECK(d != nullptr, DMTP_E_NULL);
+  CHECK(d->B >= 1 && d->B <= 4096, DMTP_E_SHAPE);
+  CHECK(d->S >= 1 && d->S <= 64, DMTP_E_SHAPE);
+  CHECK(d->H >= 64 && d->H <= 16384 && d->H % 64 == 0, DMTP_E_SHAPE);
+  CHECK(d->d == 64 || d->d == 128, DMTP_E_SHAPE);
+  CHECK(d->Hkv >= 1 && d->Hq >= d->Hkv && d->Hq % d->Hkv == 0 && d->Hq <= 256, DMTP_E_SHAPE);
+  CHECK((d->Hq * d->d) % 64 == 0, DMTP_E_SHAPE);
+  CHECK(d->F >= 64 && d->F % 64 == 0 && d->F <= 65536, DMTP_E_SHAPE);
+  CHECK(d->n_layers >= 1 && d->n_layers <= 64, DMTP_E_SHAPE);
+  CHECK(valid_dtype(d->dtype), DMTP_E_DTYPE);
+  CHECK(d->S * (d->Hq / d->Hkv) <= attn_max_nq(d->d, d->dtype == DMTP_F32), DMTP_E_SHAPE);
+  CHECK(d->eps >= 0.f && d->rope_base > 1.f, DMTP_E_ARG);
+  CHECK(d->max_ctx >= 0 && d->ctx_rows >= 0, DMTP_E_SHAPE);
+  CHECK(d->x && d->cu_ctx && d->layers && d->out, DMTP_E_NULL);
+  CHECK(aligned16(d->x) && aligned16(d->out), DMTP_E_ALIGN);
+  for (int l = 0; l < d->n_layers; ++l) {
+    if (d->k_new && d->k_new[l]) CHECK(aligned16(d->k_new[l]), DMTP_E_ALIGN);
+    if (d->v_new && d->v_new[l]) CHECK(aligned16(d->v_new[l]), DMTP_E_ALIGN);
+  }
+  return check_layers(d->layers, d->n_layers, d->max_ctx > 0 && d->ctx_rows > 0);
 }
 
 // -------------------------------------------------------------- LM head ----
@@ -252,73 +373,54 @@ size_t dmtp_block_draft_ws(const dmtp_draft_desc* d) {
 int dmtp_block_draft(const dmtp_draft_desc* d, void* ws, size_t ws_bytes, hipStream_t stream) {
   int e = validate_draft(d);
   if (e != DMTP_OK) return e;
-  const DraftWs w = draft_ws(d);
+  const Stack st = stack_of(d);
+  const DraftWs w = stack_ws(st);
   CHECK(ws_bytes >= w.total, DMTP_E_WORKSPACE);
   CHECK(ws != nullptr, DMTP_E_NULL);
   CHECK(((uintptr_t)ws % kAlign) == 0, DMTP_E_ALIGN);
   if ((e = check_device()) != DMTP_OK) return e;
   char* b = (char*)ws;
   float* X = (float*)(b + w.X);
-  uint16_t* xh = (uint16_t*)(b + w.xh);   // bf16 planes [2][R][H]
-  float* qkv = (float*)(b + w.qkv);
-  float* q = (float*)(b + w.q);
-  float* kb = (float*)(b + w.kb);
-  float* vb = (float*)(b + w.vb);
-  uint16_t* o = (uint16_t*)(b + w.o);     // bf16 planes [2][R][Hq d]
-  float* gate = (float*)(b + w.gate);
-  float* up = (float*)(b + w.up);
-  uint16_t* act = (uint16_t*)(b + w.act); // bf16 planes [2][R][F]
-  float* gws = (float*)(b + w.gemm);
-  float* aws = (float*)(b + w.attn);
-  const int S = d->K - 1 + d->n_anchor;
-  const int R = d->B * S;
-  const int qkv_n = (d->Hq + 2 * d->Hkv) * d->d;
-  const int wf32 = d->dtype == DMTP_F32;
-  float* gws2 = (float*)(b + w.gemm2);
-  const size_t pst_h = (size_t)R * d->H, pst_o = (size_t)R * d->Hq * d->d;
-  const int od = d->Hq * d->d;
+  uint16_t* xh = (uint16_t*)(b + w.xh);
+  const int R = d->B * st.S;
   hipError_t h = build_slots(*d, X, stream);
   // RMSNorm of the slots for the first layer; later layers get theirs from the
   // previous layer's residual update
   if (h == hipSuccess)
     h = residual_rmsnorm(split_out_plain(X, (size_t)d->H, R, d->H), X, (size_t)d->H, 0,
                          d->layers[0].g_attn, d->eps, xh, R, d->H, stream);
-  for (int l = 0; l < d->n_layers && h == hipSuccess; ++l) {
-    const dmtp_layer& L = d->layers[l];
-    SplitOut sq, so, sg, su, sd;
-    GemmArgs g1{xh, pst_h, (size_t)d->H, R, L.wqkv, wf32, (size_t)d->H, qkv_n, d->H, qkv,
-                (size_t)qkv_n, nullptr, 0};
-    if ((h = gemm_deferred(g1, gws, stream, &sq)) != hipSuccess) break;
-    if ((h = rope_split(sq, d->cu_ctx, d->ctx_rows, d->B, S, d->Hq, d->Hkv, d->d, d->rope_base, q, kb,
-                        vb, stream)) != hipSuccess)
-      break;
-    if ((h = attention(w.plan, q, kb, vb, L.ctx_k, L.ctx_v, d->cu_ctx, d->ctx_rows, aws, o,
-                       stream)) != hipSuccess)
-      break;
-    GemmArgs g2{o, pst_o, (size_t)od, R, L.wo, wf32, (size_t)od, d->H, od, X, (size_t)d->H, X,
-                (size_t)d->H};
-    if ((h = gemm_deferred(g2, gws, stream, &so)) != hipSuccess) break;
-    if ((h = residual_rmsnorm(so, X, (size_t)d->H, 1, L.g_ffn, d->eps, xh, R, d->H, stream)) !=
-        hipSuccess)
-      break;
-    GemmArgs g3{xh, pst_h, (size_t)d->H, R, L.wg, wf32, (size_t)d->H, d->F, d->H, gate,
-                (size_t)d->F, nullptr, 0};
-    if ((h = gemm_deferred(g3, gws, stream, &sg)) != hipSuccess) break;
-    GemmArgs g4{xh, pst_h, (size_t)d->H, R, L.wu, wf32, (size_t)d->H, d->F, d->H, up,
-                (size_t)d->F, nullptr, 0};
-    if ((h = gemm_deferred(g4, gws2, stream, &su)) != hipSuccess) break;
-    if ((h = swiglu(sg, su, act, R, d->F, stream)) != hipSuccess) break;
-    const size_t pst_f = (size_t)R * d->F;
-    GemmArgs g5{act, pst_f, (size_t)d->F, R, L.wd, wf32, (size_t)d->F, d->H, d->F, X,
-                (size_t)d->H, X, (size_t)d->H};
-    if ((h = gemm_deferred(g5, gws, stream, &sd)) != hipSuccess) break;
-    if (l + 1 < d->n_layers)
-      h = residual_rmsnorm(sd, X, (size_t)d->H, 1, d->layers[l + 1].g_attn, d->eps, xh, R, d->H,
-                           stream);
-    else
-      h = final_norm_mask(sd, d->g_final, d->eps, d->B, S, d->n_anchor, d->K, d->H, d->dtype,
-                          d->out, stream);
-  }
+  SplitOut last{};
+  if (h == hipSuccess) h = run_stack(st, w, b, nullptr, nullptr, &last, stream);
+  if (h == hipSuccess)
+    h = final_norm_mask(last, d->g_final, d->eps, d->B, st.S, d->n_anchor, d->K, d->H, d->dtype,
+                        d->out, stream);
+  return launch_status(h);
+}
+
+size_t dmtp_mtp_block_ws(const dmtp_mtp_desc* d) {
+  if (validate_mtp(d) != DMTP_OK) return 0;
+  return stack_ws(stack_of(d)).total;
+}
+
+int dmtp_mtp_block(const dmtp_mtp_desc* d, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int e = validate_mtp(d);
+  if (e != DMTP_OK) return e;
+  const Stack st = stack_of(d);
+  const DraftWs w = stack_ws(st);
+  CHECK(ws_bytes >= w.total, DMTP_E_WORKSPACE);
+  CHECK(ws != nullptr, DMTP_E_NULL);
+  CHECK(((uintptr_t)ws % kAlign) == 0, DMTP_E_ALIGN);
+  if ((e = check_device()) != DMTP_OK) return e;
+  char* b = (char*)ws;
+  float* X = (float*)(b + w.X);
+  uint16_t* xh = (uint16_t*)(b + w.xh);
+  const int R = d->B * d->S;
+  // X = x and the first layer's norm planes in one pass
+  hipError_t h = residual_rmsnorm(split_out_plain(d->x, (size_t)d->H, R, d->H), X, (size_t)d->H, 1,
+                                  d->layers[0].g_attn, d->eps, xh, R, d->H, stream);
+  SplitOut last{};
+  if (h == hipSuccess) h = run_stack(st, w, b, d->k_new, d->v_new, &last, stream);
+  if (h == hipSuccess) h = finish_rows(last, d->out, (size_t)d->H, R, d->H, stream);
   return launch_status(h);
 }
 
@@ -376,7 +478,7 @@ const char* dmtp_status_str(int s) {
   }
 }
 
-const char* dmtp_version(void) { return "dmtp 0.3.0 (gfx950, ABI 3)"; }
+const char* dmtp_version(void) { return "dmtp 0.4.0 (gfx950, ABI 4)"; }
 
 size_t dmtp_struct_size(int which) {
   switch (which) {
@@ -388,6 +490,7 @@ size_t dmtp_struct_size(int which) {
     case 5: return sizeof(dmtp_head_desc);
     case 6: return sizeof(dmtp_verify_desc);
     case 7: return sizeof(dmtp_stats_desc);
+    case 8: return sizeof(dmtp_mtp_desc);
     default: return 0;
   }
 }

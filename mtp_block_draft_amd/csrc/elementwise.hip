@@ -339,6 +339,40 @@ __global__ __launch_bounds__(256) void rope_split_kernel(SplitOut o, const int32
   }
 }
 
+// out[m] = value(m) in float32: the finished rows of a split GEMM result.
+template <int V4>
+__global__ __launch_bounds__(kRowThreads) void finish_rows_kernel(SplitOut o, float* __restrict__ out,
+                                                                  size_t ldo, int H) {
+  const int m = blockIdx.x;
+  SplitAcc<zb_of<V4>()> acc[V4];
+#pragma unroll
+  for (int k = 0; k < V4; ++k) {
+    const int n = 4 * (threadIdx.x + kRowThreads * k);
+    if (n < H) split_issue4(o, m, n, acc[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < V4; ++k) {
+    const int n = 4 * (threadIdx.x + kRowThreads * k);
+    if (n < H) *(float4*)(out + (size_t)m * ldo + n) = split_finish4(o, m, n, acc[k]);
+  }
+}
+
+// Block keys / values [B, Hkv, S, d] (float32) -> rows [B, S, Hkv, d] in dtype:
+// the rows a key/value cache appends.  One workgroup per (b, s).
+__global__ void export_kv_kernel(const float* __restrict__ kb, const float* __restrict__ vb, int S,
+                                 int Hkv, int d, int dtype, void* __restrict__ k_new,
+                                 void* __restrict__ v_new) {
+  const int b = blockIdx.x / S, sl = blockIdx.x % S;
+  const int n = Hkv * d;
+  for (int e = threadIdx.x; e < n; e += blockDim.x) {
+    const int h = e / d, i = e % d;
+    const size_t src = (((size_t)b * Hkv + h) * S + sl) * d + i;
+    const size_t dst = (size_t)blockIdx.x * n + e;
+    if (k_new) store_elem(k_new, dtype, dst, kb[src]);
+    if (v_new) store_elem(v_new, dtype, dst, vb[src]);
+  }
+}
+
 // a = silu(g) * u over [rows, F], written as bf16 planes [2][rows][F].
 __global__ void swiglu_kernel(SplitOut gs, SplitOut us, uint16_t* __restrict__ a, int rows, int F) {
   const size_t n4 = (size_t)rows * F / 4, pst = (size_t)rows * F;
@@ -435,6 +469,26 @@ hipError_t swiglu(const SplitOut& g, const SplitOut& u, uint16_t* a, int rows, i
   const size_t n4 = (size_t)rows * F / 4;
   const size_t blocks = (n4 + 255) / 256 < 8192 ? (n4 + 255) / 256 : 8192;
   hipLaunchKernelGGL(swiglu_kernel, dim3((unsigned)blocks), dim3(256), 0, s, g, u, a, rows, F);
+  return hipGetLastError();
+}
+
+hipError_t finish_rows(const SplitOut& x, float* out, size_t ldo, int rows, int H, hipStream_t s) {
+  switch (v4_of(H)) {
+#define DMTP_CASE(n)                                                                               \
+  case n:                                                                                          \
+    hipLaunchKernelGGL(finish_rows_kernel<n>, dim3(rows), dim3(kRowThreads), 0, s, x, out, ldo, H);  \
+    break;
+    DMTP_CASE(1) DMTP_CASE(2) DMTP_CASE(4) DMTP_CASE(8) DMTP_CASE(16)
+#undef DMTP_CASE
+  }
+  return hipGetLastError();
+}
+
+hipError_t export_kv(const float* kb, const float* vb, int B, int S, int Hkv, int d, int dtype,
+                     void* k_new, void* v_new, hipStream_t s) {
+  if (!k_new && !v_new) return hipSuccess;
+  hipLaunchKernelGGL(export_kv_kernel, dim3(B * S), dim3(256), 0, s, kb, vb, S, Hkv, d, dtype, k_new,
+                     v_new);
   return hipGetLastError();
 }
 

@@ -70,6 +70,14 @@ hipError_t rope_split(const SplitOut& qkv, const int32_t* cu_ctx, int ctx_rows, 
 // a = silu(g) * u elementwise over [rows, F] (bf16 planes [2][rows][F] out)
 hipError_t swiglu(const SplitOut& g, const SplitOut& u, uint16_t* a, int rows, int F, hipStream_t s);
 
+// out[m] = value(m) (float32, row stride ldo) for the rows of x
+hipError_t finish_rows(const SplitOut& x, float* out, size_t ldo, int rows, int H, hipStream_t s);
+
+// k_new / v_new [B, S, Hkv, d] in dtype from the block keys / values kb, vb
+// [B, Hkv, S, d] (float32; rounded to bf16 for DMTP_BF16).  Either may be NULL.
+hipError_t export_kv(const float* kb, const float* vb, int B, int S, int Hkv, int d, int dtype,
+                     void* k_new, void* v_new, hipStream_t s);
+
 // out[b, j] = round_dtype(RMSNorm(value(b S + n_anchor + j); g)) for j = 0 .. K-2
 hipError_t final_norm_mask(const SplitOut& x, const float* g, float eps, int B, int S, int n_anchor,
                            int K, int H, int dtype, void* out, hipStream_t s);
@@ -77,6 +85,7 @@ hipError_t final_norm_mask(const SplitOut& x, const float* g, float eps, int B, 
 // -------------------------------------------------------------- attention --
 struct AttnPlan {
   int B, Hkv, G, S, d, NQ, nqp, chunk, n_chunks, kv_f32, window;
+  int causal;   // block keys: slot s sees slots 0..s only (0 from attn_plan)
 };
 // ctx_rows: total context rows of the batch (sizes the chunks for bf16 K/V).
 AttnPlan attn_plan(int B, int Hq, int Hkv, int S, int d, int max_ctx, int window, int kv_f32,

@@ -4,7 +4,10 @@ Round(inputs) uploads the seeded inputs once, allocates every output and one
 shared workspace, and prebuilds the call descriptors; run() then enqueues,
 on the current stream:
 
-  1. dmtp_fuse        h_MTP = M [RMSNorm(h); RMSNorm(E(A))]          (MTP fusion)
+  1. dmtp_fuse        h' = M [RMSNorm(h); RMSNorm(E(A))]             (MTP fusion)
+     dmtp_mtp_block   h_MTP = the MTP decoder block over h' (workloads with
+                      one; it also returns the K/V rows its cache appends),
+                      else h_MTP = h'
   2. dmtp_lm_head     T1 from RMSNorm(h_MTP; g_f)                       (MTP candidate)
   3. dmtp_fuse        x_T1 = E(T1) + W [RMS_e(E(T1)); RMS_m(h_MTP)]     (DMTP residual)
   4. dmtp_block_draft MASK-slot rows of the drafter                    (block draft)
@@ -40,7 +43,7 @@ import numpy as np
 import torch
 
 from . import (DMTP_NO_DRAW, accept_stats, block_draft, call, fuse, head_segment, layer_arg, lib,
-               lm_head, verify, workspace_bytes)
+               lm_head, mtp_block, verify, workspace_bytes)
 
 
 def _dev(a: np.ndarray, dtype: torch.dtype, device) -> torch.Tensor:
@@ -64,11 +67,12 @@ class Round:
         self.fuse_W = up(inp.fuse_W)
         g = {k: up(getattr(inp, k), f32) for k in ("g_h", "g_e", "g_e2", "g_m", "g_f", "g_final")}
         self.gains = g
-        self.layers_t = []
-        for lw in inp.layers:
-            self.layers_t.append({k: up(getattr(lw, k), f32 if k.startswith("g_") else tdt)
-                                  for k in ("g_attn", "wqkv", "wo", "g_ffn", "wg", "wu", "wd",
-                                            "ctx_k", "ctx_v")})
+        def layer_t(lw):
+            return {k: up(getattr(lw, k), f32 if k.startswith("g_") else tdt)
+                    for k in ("g_attn", "wqkv", "wo", "g_ffn", "wg", "wu", "wd", "ctx_k", "ctx_v")}
+        self.layers_t = [layer_t(lw) for lw in inp.layers]
+        self.has_mtp = bool(getattr(cfg, "mtp_block", False))
+        self.mtp_layers_t = [layer_t(lw) for lw in inp.mtp_layers] if self.has_mtp else []
         self.cu_ctx = up(inp.cu_ctx, i32)
         self.anchor = up(inp.anchor, i32)
         self.h_prev = up(inp.h_prev)
@@ -88,6 +92,11 @@ class Round:
 
         # outputs
         self.h_mtp = torch.empty(B, H, dtype=f32, device=dv)
+        self.h_fused = torch.empty(B, H, dtype=f32, device=dv) if self.has_mtp else self.h_mtp
+        self.mtp_k_new = [torch.empty(B, 1, cfg.Hkv, cfg.d, dtype=tdt, device=dv)
+                          for _ in self.mtp_layers_t]
+        self.mtp_v_new = [torch.empty(B, 1, cfg.Hkv, cfg.d, dtype=tdt, device=dv)
+                          for _ in self.mtp_layers_t]
         self.x_t1 = torch.empty(B, H, dtype=f32, device=dv)
         M1 = 2 * B if self.any_plant else B
         self.M1 = M1
@@ -153,8 +162,17 @@ class Round:
 
         # descriptors
         eps = cfg.eps
-        self.d_fuse_mtp = fuse(self.h_mtp, self.fuse_M, g["g_h"], g["g_e"], x1=self.h_prev,
+        self.d_fuse_mtp = fuse(self.h_fused, self.fuse_M, g["g_h"], g["g_e"], x1=self.h_prev,
                                x2_ids=self.anchor, table=self.emb, eps=eps, run=False)
+        if self.has_mtp:
+            self._mtp_layers = [layer_arg(**lt) for lt in self.mtp_layers_t]
+            self.d_mtp = mtp_block(self.h_mtp.view(B, 1, H), self.h_fused.view(B, 1, H), Hq=cfg.Hq,
+                                   Hkv=cfg.Hkv, d=cfg.d, F=cfg.F, layers=self._mtp_layers,
+                                   cu_ctx=self.cu_ctx, max_ctx=int(inp.ctx_len.max()),
+                                   ctx_rows=int(inp.cu_ctx[-1]),
+                                   dtype=1 if cfg.dtype == "bf16" else 0, k_new=self.mtp_k_new,
+                                   v_new=self.mtp_v_new, eps=eps, rope_base=cfg.rope_base,
+                                   run=False)
         segs = [head_segment(self.h_mtp, g["g_f"])]
         if self.any_plant:
             segs.append(head_segment(self.head_in[nd:], None, n=B, ld=(K + 1) * H))
@@ -188,7 +206,14 @@ class Round:
                                run=False)
         self.hist = torch.zeros(K + 1, dtype=torch.int64, device=dv)
         self.summary = torch.zeros(2 + 2 * K, dtype=torch.float64, device=dv)
-        self.steps = [("fuse", self.d_fuse_mtp), ("lm_head", self.d_head_t1),
+        self.steps = [("fuse", self.d_fuse_mtp)]
+        self.step_names = ["fuse_mtp"]
+        if self.has_mtp:
+            self.steps.append(("mtp_block", self.d_mtp))
+            self.step_names.append("mtp_block")
+        self.step_names += ["lm_head_t1", "fuse_delta", "block_draft", "lm_head_draft_target",
+                            "verify"]
+        self.steps += [("lm_head", self.d_head_t1),
                       ("fuse", self.d_fuse_delta), ("block_draft", self.d_draft),
                       ("lm_head", self.d_head_c), ("verify", self.d_verify)]
         need = max(workspace_bytes(n, d) for n, d in self.steps)
@@ -238,7 +263,7 @@ class Round:
         f = lambda t: t.detach().float().cpu().numpy()  # noqa: E731
         i = lambda t: t.detach().cpu().numpy().astype(np.int64)  # noqa: E731
         out = {
-            "h_mtp": f(self.h_mtp), "z1": f(self.t1_prep[:B]), "t1": i(self.t1_token[:B]),
+            "h_mtp": f(self.h_mtp), "h_fused": f(self.h_fused), "z1": f(self.t1_prep[:B]), "t1": i(self.t1_token[:B]),
             "t1_lse": f(self.t1_lse[:B]), "t1_max": f(self.t1_max[:B]), "t1_gap": f(self.t1_gap[:B]),
             "x_t1": f(self.x_t1), "hd_mask": f(self.head_in[:nd]).reshape(B, K - 1, cfg.H),
             "drafts_rest": i(self.tok[:nd]).reshape(B, K - 1),
@@ -251,4 +276,5 @@ class Round:
             "out_tokens": i(self.out_tokens), "n_out": i(self.n_out),
         }
         out["drafts"] = np.concatenate([out["t1"][:, None], out["drafts_rest"]], axis=1)
+        out["mtp_kv"] = [(f(k), f(v)) for k, v in zip(self.mtp_k_new, self.mtp_v_new)]
         return out

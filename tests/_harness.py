@@ -69,7 +69,7 @@ def _first_mismatch(res: odm.RoundResult, g: Dict[str, np.ndarray], tau: np.ndar
 
 
 def _splice(res: odm.RoundResult, sub: odm.RoundResult, r: int) -> None:
-    for name in ("h_mtp", "z1", "x_t1", "hd", "t1", "drafts", "target_argmax", "q_lse", "p_lse",
+    for name in ("h_fused", "h_mtp", "z1", "x_t1", "hd", "t1", "drafts", "target_argmax", "q_lse", "p_lse",
                  "q_max", "p_max", "accept_len", "out_tokens", "n_out"):
         getattr(res, name)[r] = getattr(sub, name)[0]
     b = sub.seqs[0]
@@ -104,6 +104,7 @@ def compare_round(inp, g: Dict[str, np.ndarray], seqs: Optional[Sequence[int]] =
     idx = np.array(seqs)
     K, first = cfg.K, cfg.n_anchor
     rep = {
+        "h_fused": max_rel(g["h_fused"][idx], res.h_fused),
         "h_mtp": max_rel(g["h_mtp"][idx], res.h_mtp),
         "x_t1": max_rel(g["x_t1"][idx], res.x_t1),
         "z1": max_rel(g["z1"][idx], res.z1),
@@ -118,7 +119,7 @@ def compare_round(inp, g: Dict[str, np.ndarray], seqs: Optional[Sequence[int]] =
     }
     for k in ("z1", "hd_mask", "draft_max", "target_max"):
         assert rep[k] <= VALUE_TOL, (k, rep[k])
-    for k in ("h_mtp", "x_t1", "t1_lse", "draft_lse", "target_lse"):
+    for k in ("h_fused", "h_mtp", "x_t1", "t1_lse", "draft_lse", "target_lse"):
         assert rep[k] <= F32_TOL, (k, rep[k])
     return res, rep
 

@@ -191,3 +191,35 @@ def test_valid_call_without_gfx950_is_refused(lib):
 def test_binding_refuses_to_load_a_missing_library(tmp_path):
     with pytest.raises(ImportError):
         abi.load(str(tmp_path / "libdmtp.so"))
+
+
+def test_mtp_block_argument_errors(lib):
+    L = abi.Layer(*([FAKE] * 9))
+    arr = (abi.Layer * 1)(L)
+
+    def desc(**over):
+        d = abi.MtpDesc()
+        d.B, d.S, d.H, d.Hq, d.Hkv, d.d, d.F, d.n_layers, d.dtype = 4, 1, 256, 4, 2, 64, 512, 1, 1
+        d.eps, d.rope_base, d.max_ctx, d.ctx_rows = 1e-6, 1e6, 100, 300
+        d.x = d.cu_ctx = d.out = FAKE
+        d.layers = ctypes.cast(arr, ctypes.POINTER(abi.Layer))
+        for k, v in over.items():
+            setattr(d, k, v)
+        return d
+
+    assert lib.dmtp_mtp_block(None, None, 0, None) == -1
+    assert _call(lib, "dmtp_mtp_block", desc(S=0)) == -2
+    assert _call(lib, "dmtp_mtp_block", desc(d=96)) == -2
+    assert _call(lib, "dmtp_mtp_block", desc(Hq=6, Hkv=4)) == -2
+    assert _call(lib, "dmtp_mtp_block", desc(dtype=5)) == -3
+    assert _call(lib, "dmtp_mtp_block", desc(x=None)) == -1
+    assert _call(lib, "dmtp_mtp_block", desc(out=FAKE + 8)) == -5
+    bad = (abi.Layer * 1)(abi.Layer(*([FAKE] * 7 + [None, FAKE])))   # cache keys missing
+    assert _call(lib, "dmtp_mtp_block", desc(layers=ctypes.cast(bad, ctypes.POINTER(abi.Layer)))) == -1
+    mis = (ctypes.c_void_p * 1)(FAKE + 4)                              # misaligned K/V output
+    assert _call(lib, "dmtp_mtp_block", desc(k_new=ctypes.cast(mis, ctypes.POINTER(ctypes.c_void_p)))) == -5
+    d = desc()
+    need = lib.dmtp_mtp_block_ws(ctypes.byref(d))
+    assert need > 0 and _call(lib, "dmtp_mtp_block", d, ws_bytes=need - 1) == -4
+    if torch.cuda.device_count() == 0:
+        assert _call(lib, "dmtp_mtp_block", d, ws_bytes=need) == -6

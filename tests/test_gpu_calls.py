@@ -305,6 +305,62 @@ def test_block_draft(dm, dt, shape):
         assert np.mean(got != ref) < 0.02
 
 
+# ---------------------------------------------------------------- MTP block
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [
+    dict(B=3, S=1, H=256, Hq=4, Hkv=2, d=64, F=512, NL=1, ctx_lens=[0, 5, 300]),
+    dict(B=2, S=4, H=512, Hq=8, Hkv=2, d=128, F=768, NL=2, ctx_lens=[130, 1]),
+    dict(B=5, S=3, H=256, Hq=4, Hkv=4, d=64, F=256, NL=1, ctx_lens=[64, 65, 0, 1000, 7]),
+    dict(B=32, S=1, H=512, Hq=16, Hkv=4, d=128, F=512, NL=1,
+         ctx_lens=list(range(40, 40 + 32 * 37, 37))),
+])
+def test_mtp_block(dm, dt, shape):
+    """The causal MTP block and the K/V rows it returns, against the oracle."""
+    shape = dict(shape)
+    print(f"mtp_block dt={dt} {shape}", flush=True)
+    S = shape.pop("S")
+    c = _draft_case(sum(shape["ctx_lens"]) + 7 * S, dt, K=2, n_anchor=1, **shape)
+    B, H, Hq, Hkv, d, F = (shape[k] for k in ("B", "H", "Hq", "Hkv", "d", "F"))
+    r = np.random.default_rng(B * 100 + S)
+    x = r.standard_normal((B, S, H)).astype(np.float32)
+    td = TD[dt]
+    f32 = torch.float32
+    lt = [{k: _t(v, f32 if k.startswith("g_") else td) for k, v in L.items()} for L in c["layers"]]
+    Ls = [dm.layer_arg(**L) for L in lt]
+    out = torch.empty(B, S, H, dtype=f32, device="cuda")
+    k_new = [torch.empty(B, S, Hkv, d, dtype=td, device="cuda") for _ in Ls]
+    v_new = [torch.empty(B, S, Hkv, d, dtype=td, device="cuda") for _ in Ls]
+    dm.mtp_block(out, _t(x, f32), Hq=Hq, Hkv=Hkv, d=d, F=F, layers=Ls,
+                 cu_ctx=_t(c["cu"], torch.int32), max_ctx=int(max(c["ctx_lens"])),
+                 ctx_rows=int(c["cu"][-1]), dtype=1 if dt == "bf16" else 0, k_new=k_new,
+                 v_new=v_new)
+    L64 = [odm.Layer64(*(np.asarray(L[k], np.float64) for k in
+                         ("g_attn", "wqkv", "wo", "g_ffn", "wg", "wu", "wd"))) for L in c["layers"]]
+    cu = c["cu"]
+    spans = [(int(cu[b]), int(cu[b + 1])) for b in range(B)]
+    pos = np.asarray(c["ctx_lens"])[:, None] + np.arange(S)
+    ref, kv = odm.mtp_block(x.astype(np.float64), pos, L64,
+                            [[L["ctx_k"][lo:hi] for lo, hi in spans] for L in c["layers"]],
+                            [[L["ctx_v"][lo:hi] for lo, hi in spans] for L in c["layers"]],
+                            Hq=Hq, Hkv=Hkv, d=d, eps=1e-6, rope_base=1e6)
+    err = max_rel(out.cpu().numpy(), ref)
+    print("  max rel out", err)
+    assert err < 1e-4
+    rf = onm.round_to(dt)
+    for l in range(len(Ls)):
+        for got_t, want in ((k_new[l], kv[l][0]), (v_new[l], kv[l][1])):
+            got = got_t.float().cpu().numpy()
+            want_r = rf(want)
+            e = max_rel(got, want_r)
+            print("  max rel kv", e)
+            # float32: accumulation error only; bf16: at most a rounding flip of one ulp
+            assert e < (1e-4 if dt == "f32" else 1e-2)
+            if dt == "bf16":
+                assert np.mean(got != want_r) < 0.02
+
+
 # ---------------------------------------------------------------- verify
 
 

@@ -16,7 +16,7 @@ torch = pytest.importorskip("torch")
 
 import dmtp_synth as synth  # noqa: E402
 
-from tests._harness import compare_round, correlated_targets  # noqa: E402
+from tests._harness import compare_round, correlated_targets, max_rel  # noqa: E402
 
 
 @pytest.fixture(scope="module")
@@ -87,6 +87,18 @@ def test_ragged_mixed_target_only_bf16(rnd):
     assert R.hist.cpu().numpy().tolist() == st["hist"]
 
 
+def test_tiny_rounds_with_the_mtp_block(rnd):
+    for name in ("tiny_greedy_f32", "tiny_sampled_f32"):
+        cfg = synth.CONFIGS[name].with_(mtp_block=True, B=3, ctx_min=0, ctx_max=200, gain_std=0.1)
+        inp = synth.make_inputs(cfg)
+        R, g = _run(rnd, inp)
+        res, rep = compare_round(inp, g)
+        _report(f"{name}/mtp_block", rep)
+        for l, (k, v) in enumerate(g["mtp_kv"]):
+            assert max_rel(k[:, 0], res.mtp_kv[l][0][:, 0]) < 1e-4
+            assert max_rel(v[:, 0], res.mtp_kv[l][1][:, 0]) < 1e-4
+
+
 def test_ragged_mixed_bf16(rnd):
     """Several tiles, ragged contexts (including empty), mixed greedy/sampled, planted T1."""
     cfg = synth.RoundConfig(name="ragged_mixed", B=6, H=512, V=3001, Hq=8, Hkv=2, d=64, F=768,
@@ -118,6 +130,15 @@ def test_b32_greedy_bf16_full_size(rnd):
     g2 = R.results()
     for k in ("hd_mask", "out_tokens", "target_lse", "x_t1"):
         np.testing.assert_array_equal(g[k], g2[k])
+
+
+@pytest.mark.timeout(900)
+def test_b32_greedy_with_the_mtp_block_full_size(rnd):
+    cfg = synth.CONFIGS["b32_greedy_bf16"].with_(mtp_block=True)
+    inp = synth.make_inputs(cfg)
+    R, g = _run(rnd, inp)
+    res, rep = compare_round(inp, g, seqs=[0, 9, 31])
+    _report(f"{cfg.name}/mtp_block", rep)
 
 
 @pytest.mark.timeout(900)
