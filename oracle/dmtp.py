@@ -247,6 +247,34 @@ def mtp_block(X: np.ndarray, positions: np.ndarray, layers64: Sequence[Layer64],
     return X, kv
 
 
+def ctx_kv(feats: np.ndarray, positions: np.ndarray, w_fc: np.ndarray, layers64: Sequence[Layer64],
+           *, Hq: int, Hkv: int, d: int, eps: float, rope_base: float):
+    """The drafter's context K/V of new target rows ([DvM] "DFlash: Block
+    Diffusion ...": KV injection -- hidden features from a few target layers go
+    into the key/value cache of every draft layer; [DMTP] section 3, ablation
+    notes: context fusion concatenates five target feature streams and projects
+    them back to the hidden size).
+
+    feats [N, n_feat, H] are the target features of N committed rows at
+    `positions` [N]; c = W_fc [f_1; ...; f_n] (W_fc [H, n_feat H]).  Reading
+    where the pages stop: c enters every drafter layer the way a block row does,
+    so layer l's cache rows are k = RoPE(RMSNorm(c; g_attn) Wk^T, pos) and
+    v = RMSNorm(c; g_attn) Wv^T with Wk, Wv the key and value rows of Wqkv.
+    Returns c [N, H] and per layer (k, v) [N, Hkv, d].
+    """
+    N, nf, H = feats.shape
+    c = nm.matmul_nt(np.asarray(feats, dtype=np.float64).reshape(N, nf * H), w_fc)
+    out = []
+    for lw in layers64:
+        xh = nm.rmsnorm(c, lw.g_attn, eps)
+        kvw = np.asarray(lw.wqkv, dtype=np.float64)[Hq * d:]
+        kv = nm.matmul_nt(xh, kvw)
+        k = nm.rope(kv[:, : Hkv * d].reshape(N, Hkv, d), np.asarray(positions), rope_base)
+        v = kv[:, Hkv * d:].reshape(N, Hkv, d)
+        out.append((k, v))
+    return c, out
+
+
 def block_draft(slots: Sequence[np.ndarray], ctx_len: np.ndarray, layers64: Sequence[Layer64],
                 ctx_k: Sequence[np.ndarray], ctx_v: Sequence[np.ndarray], cu_ctx: np.ndarray,
                 seqs: Sequence[int], g_final: np.ndarray, rf: Callable, *, Hq: int, Hkv: int,
