@@ -12,6 +12,7 @@
  *
  *   dmtp_fuse         RMSNorm-concat-projection (MTP input fusion; DMTP residual)
  *   dmtp_mtp_block    the MTP decoder block (causal, with its own KV cache)
+ *   dmtp_ctx_kv       the drafter's context K/V rows from target features
  *   dmtp_block_draft  the block drafter's layers and final norm
  *   dmtp_lm_head      the shared vocabulary head with argmax / sampling
  *   dmtp_verify       greedy, rejection-sampling or target-only block verification
@@ -50,7 +51,7 @@
 extern "C" {
 #endif
 
-#define DMTP_ABI_VERSION 4
+#define DMTP_ABI_VERSION 5
 
 enum dmtp_status {
   DMTP_OK = 0,
@@ -191,6 +192,41 @@ typedef struct {
 
 size_t dmtp_mtp_block_ws(const dmtp_mtp_desc* d);
 int dmtp_mtp_block(const dmtp_mtp_desc* d, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* --------------------------------------------------------- context K/V ----
+ * The drafter's context key/value rows of newly committed target rows
+ * ("DFlash vs MTP", "DFlash: Block Diffusion as a Draft Model": KV injection
+ * of hidden features from a few target layers into the cache of every draft
+ * layer; DMTP blog section 3, ablation notes: context fusion concatenates
+ * five target feature streams and projects them back to the hidden size).
+ * Per new row n: c = W_fc [f_1; ...; f_n_feat] (feats[n] holds the streams),
+ * then for every drafter layer l, with x^ = RMSNorm(c; layers[l].g_attn) and
+ * the key / value rows of layers[l].wqkv:
+ *     k = RoPE(x^ Wk^T, positions[n]) (rotate-half, base rope_base),
+ *     v = x^ Wv^T,
+ * written in dtype to k_cache[l][dst_rows[n]] and v_cache[l][dst_rows[n]]
+ * ([ctx_rows, Hkv, d] each) -- the rows dmtp_block_draft then reads as
+ * context.  A dst_rows entry outside [0, ctx_rows) writes nothing.  ctx_out,
+ * when given, receives c [N, H] float32. */
+typedef struct {
+  int32_t N;              /* new rows, 1 .. 65536 */
+  int32_t n_feat;         /* feature streams per row, 1 .. 8 */
+  int32_t H, Hq, Hkv, d, n_layers, dtype;
+  float eps;
+  float rope_base;
+  const void* feats;      /* [N, n_feat, H] in dtype */
+  const int32_t* positions;   /* [N] */
+  const int32_t* dst_rows;    /* [N] */
+  const void* w_fc;       /* [H, n_feat H] in dtype */
+  const dmtp_layer* layers;   /* HOST array: g_attn and wqkv of each drafter layer */
+  int32_t ctx_rows;       /* rows of every cache */
+  void* const* k_cache;   /* HOST array of n_layers device pointers [ctx_rows, Hkv, d] */
+  void* const* v_cache;   /* HOST array of n_layers device pointers [ctx_rows, Hkv, d] */
+  float* ctx_out;         /* [N, H] or NULL */
+} dmtp_ctx_desc;
+
+size_t dmtp_ctx_kv_ws(const dmtp_ctx_desc* d);
+int dmtp_ctx_kv(const dmtp_ctx_desc* d, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* -------------------------------------------------------------- LM head ----
  * The shared vocabulary head ("DFlash vs MTP": shared output head; DMTP blog
@@ -338,7 +374,7 @@ const char* dmtp_status_str(int status);
 const char* dmtp_version(void);
 /* sizeof of the descriptor structs, for bindings to check their layout:
  * which = 0 rows, 1 fuse, 2 layer, 3 draft, 4 head segment, 5 head, 6 verify,
- * 7 stats, 8 MTP block */
+ * 7 stats, 8 MTP block, 9 context K/V */
 size_t dmtp_struct_size(int which);
 
 #ifdef __cplusplus

@@ -15,11 +15,11 @@ import torch
 
 from . import _abi
 from ._abi import (DMTP_BF16, DMTP_F32, DMTP_NO_DRAW, DmtpError, DraftDesc, FuseDesc, HeadDesc,
-                   HeadSegment, Layer, MtpDesc, Rows, StatsDesc, VerifyDesc)
+                   CtxDesc, HeadSegment, Layer, MtpDesc, Rows, StatsDesc, VerifyDesc)
 
 lib = _abi.load()
 
-__all__ = ["lib", "fuse", "mtp_block", "block_draft", "lm_head", "verify", "accept_stats", "call",
+__all__ = ["lib", "fuse", "mtp_block", "ctx_kv", "block_draft", "lm_head", "verify", "accept_stats", "call",
            "workspace_bytes",
            "DMTP_F32", "DMTP_BF16", "DMTP_NO_DRAW", "DmtpError", "version"]
 
@@ -157,6 +157,34 @@ def mtp_block(out: torch.Tensor, x: torch.Tensor, *, Hq: int, Hkv: int, d: int, 
     D._keep = keep
     if run:
         call("mtp_block", D, ws)
+    return D
+
+
+def ctx_kv(feats: torch.Tensor, positions: torch.Tensor, dst_rows: torch.Tensor,
+           w_fc: torch.Tensor, *, Hq: int, Hkv: int, d: int, layers: Sequence[Layer],
+           k_cache: Sequence[torch.Tensor], v_cache: Sequence[torch.Tensor],
+           ctx_out: Optional[torch.Tensor] = None, eps: float = 1e-6, rope_base: float = 1e6,
+           ws: Optional[torch.Tensor] = None, run: bool = True) -> CtxDesc:
+    """Drafter context K/V rows from target features [N, n_feat, H] (dmtp_ctx_kv)."""
+    if positions.dtype != torch.int32 or dst_rows.dtype != torch.int32:
+        raise ValueError("positions and dst_rows must be int32")
+    D = CtxDesc()
+    D.N, D.n_feat, D.H = feats.shape
+    D.Hq, D.Hkv, D.d, D.n_layers = Hq, Hkv, d, len(layers)
+    D.dtype = dtype_code(feats.dtype)
+    D.eps, D.rope_base = eps, rope_base
+    D.feats, D.positions, D.dst_rows, D.w_fc = _ptr(feats), _ptr(positions), _ptr(dst_rows), _ptr(w_fc)
+    arr = (Layer * len(layers))(*layers)
+    D.layers = ctypes.cast(arr, ctypes.POINTER(Layer))
+    D.ctx_rows = k_cache[0].shape[0]
+    kp = (ctypes.c_void_p * len(layers))(*[_ptr(t) for t in k_cache])
+    vp = (ctypes.c_void_p * len(layers))(*[_ptr(t) for t in v_cache])
+    D.k_cache = ctypes.cast(kp, ctypes.POINTER(ctypes.c_void_p))
+    D.v_cache = ctypes.cast(vp, ctypes.POINTER(ctypes.c_void_p))
+    D.ctx_out = _ptr(ctx_out)
+    D._keep = (arr, kp, vp, feats, positions, dst_rows, w_fc, list(k_cache), list(v_cache), ctx_out)
+    if run:
+        call("ctx_kv", D, ws)
     return D
 
 

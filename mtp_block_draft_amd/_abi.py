@@ -88,11 +88,21 @@ class MtpDesc(ctypes.Structure):
                 ("v_new", POINTER(c_void_p))]
 
 
+class CtxDesc(ctypes.Structure):
+    _fields_ = [("N", c_int32), ("n_feat", c_int32), ("H", c_int32), ("Hq", c_int32),
+                ("Hkv", c_int32), ("d", c_int32), ("n_layers", c_int32), ("dtype", c_int32),
+                ("eps", c_float), ("rope_base", c_float), ("feats", c_void_p),
+                ("positions", c_void_p), ("dst_rows", c_void_p), ("w_fc", c_void_p),
+                ("layers", POINTER(Layer)), ("ctx_rows", c_int32), ("k_cache", POINTER(c_void_p)),
+                ("v_cache", POINTER(c_void_p)), ("ctx_out", c_void_p)]
+
+
 _STRUCTS = [Rows, FuseDesc, Layer, DraftDesc, HeadSegment, HeadDesc, VerifyDesc, StatsDesc,
-            MtpDesc]
+            MtpDesc, CtxDesc]
 
 # exported symbols of include/dmtp.h
-SYMBOLS = ["dmtp_fuse", "dmtp_fuse_ws", "dmtp_mtp_block", "dmtp_mtp_block_ws", "dmtp_block_draft",
+SYMBOLS = ["dmtp_fuse", "dmtp_fuse_ws", "dmtp_mtp_block", "dmtp_mtp_block_ws", "dmtp_ctx_kv",
+           "dmtp_ctx_kv_ws", "dmtp_block_draft",
            "dmtp_block_draft_ws", "dmtp_lm_head",
            "dmtp_lm_head_ws", "dmtp_verify", "dmtp_verify_ws", "dmtp_accept_stats",
            "dmtp_status_str", "dmtp_version", "dmtp_struct_size"]
@@ -109,7 +119,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         raise ImportError(f"{path} is not built; run `python -m mtp_block_draft_amd.build` "
                           "(the DMTP path has no fallback)")
     lib = ctypes.CDLL(path)
-    for name, desc in (("dmtp_fuse", FuseDesc), ("dmtp_mtp_block", MtpDesc),
+    for name, desc in (("dmtp_fuse", FuseDesc), ("dmtp_mtp_block", MtpDesc), ("dmtp_ctx_kv", CtxDesc),
                        ("dmtp_block_draft", DraftDesc),
                        ("dmtp_lm_head", HeadDesc), ("dmtp_verify", VerifyDesc)):
         f = getattr(lib, name)

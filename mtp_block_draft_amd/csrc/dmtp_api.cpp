@@ -274,6 +274,52 @@ int validate_mtp(const dmtp_mtp_desc* d) {
   return check_layers(d->layers, d->n_layers, d->max_ctx > 0 && d->ctx_rows > 0);
 }
 
+// ---------------------------------------------------------- context K/V ----
+int validate_ctx(const dmtp_ctx_desc* d) {
+  CHECK(d != nullptr, DMTP_E_NULL);
+  CHECK(d->N >= 1 && d->N <= 65536, DMTP_E_SHAPE);
+  CHECK(d->n_feat >= 1 && d->n_feat <= 8, DMTP_E_SHAPE);
+  CHECK(d->H >= 64 && d->H <= 16384 && d->H % 64 == 0, DMTP_E_SHAPE);
+  CHECK(d->d == 64 || d->d == 128, DMTP_E_SHAPE);
+  CHECK(d->Hkv >= 1 && d->Hq >= d->Hkv && d->Hq % d->Hkv == 0 && d->Hq <= 256, DMTP_E_SHAPE);
+  CHECK(d->n_layers >= 1 && d->n_layers <= 64, DMTP_E_SHAPE);
+  CHECK(valid_dtype(d->dtype), DMTP_E_DTYPE);
+  CHECK(d->eps >= 0.f && d->rope_base > 1.f, DMTP_E_ARG);
+  CHECK(d->ctx_rows >= 0, DMTP_E_SHAPE);
+  CHECK(d->feats && d->positions && d->dst_rows && d->w_fc && d->layers && d->k_cache &&
+            d->v_cache,
+        DMTP_E_NULL);
+  CHECK(aligned16(d->feats) && aligned16(d->w_fc), DMTP_E_ALIGN);
+  if (d->ctx_out) CHECK(aligned16(d->ctx_out), DMTP_E_ALIGN);
+  for (int l = 0; l < d->n_layers; ++l) {
+    const dmtp_layer& L = d->layers[l];
+    CHECK(L.g_attn && L.wqkv && d->k_cache[l] && d->v_cache[l], DMTP_E_NULL);
+    CHECK(aligned16(L.g_attn) && aligned16(L.wqkv), DMTP_E_ALIGN);
+  }
+  return DMTP_OK;
+}
+
+struct CtxWs {
+  size_t planes, c, xh, kv, gemm, total;
+};
+
+CtxWs ctx_ws(const dmtp_ctx_desc* d) {
+  CtxWs w;
+  const size_t N = d->N, H = d->H, KF = (size_t)d->n_feat * d->H, nkv = (size_t)2 * d->Hkv * d->d;
+  const int wf32 = d->dtype == DMTP_F32;
+  size_t g = gemm_ws_bytes(d->N, d->H, (int)KF, wf32);
+  const size_t g2 = gemm_ws_bytes(d->N, (int)nkv, d->H, wf32);
+  if (g2 > g) g = g2;
+  size_t o = 0;
+  w.planes = o; o = al(o + 2 * N * KF * 2);
+  w.c = o; o = al(o + N * H * 4);
+  w.xh = o; o = al(o + 2 * N * H * 2);
+  w.kv = o; o = al(o + N * nkv * 4);
+  w.gemm = o; o = al(o + g);
+  w.total = o;
+  return w;
+}
+
 // -------------------------------------------------------------- LM head ----
 int validate_head(const dmtp_head_desc* d, int* M_out) {
   CHECK(d != nullptr, DMTP_E_NULL);
@@ -424,6 +470,49 @@ int dmtp_mtp_block(const dmtp_mtp_desc* d, void* ws, size_t ws_bytes, hipStream_
   return launch_status(h);
 }
 
+size_t dmtp_ctx_kv_ws(const dmtp_ctx_desc* d) {
+  if (validate_ctx(d) != DMTP_OK) return 0;
+  return ctx_ws(d).total;
+}
+
+int dmtp_ctx_kv(const dmtp_ctx_desc* d, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int e = validate_ctx(d);
+  if (e != DMTP_OK) return e;
+  const CtxWs w = ctx_ws(d);
+  CHECK(ws_bytes >= w.total, DMTP_E_WORKSPACE);
+  CHECK(ws != nullptr, DMTP_E_NULL);
+  CHECK(((uintptr_t)ws % kAlign) == 0, DMTP_E_ALIGN);
+  if ((e = check_device()) != DMTP_OK) return e;
+  char* b = (char*)ws;
+  uint16_t* planes = (uint16_t*)(b + w.planes);
+  float* c = d->ctx_out ? d->ctx_out : (float*)(b + w.c);
+  uint16_t* xh = (uint16_t*)(b + w.xh);
+  float* kv = (float*)(b + w.kv);
+  float* gws = (float*)(b + w.gemm);
+  const int N = d->N, H = d->H, KF = d->n_feat * d->H, nkv = 2 * d->Hkv * d->d;
+  const int wf32 = d->dtype == DMTP_F32;
+  hipError_t h = to_planes(d->feats, d->dtype, (size_t)N * KF, planes, stream);
+  if (h == hipSuccess) {
+    GemmArgs g{planes, (size_t)N * KF, (size_t)KF, N, d->w_fc, wf32, (size_t)KF, H, KF, c,
+               (size_t)H, nullptr, 0};
+    h = gemm(g, gws, stream);
+  }
+  for (int l = 0; l < d->n_layers && h == hipSuccess; ++l) {
+    const dmtp_layer& L = d->layers[l];
+    // RMSNorm(c; g_attn) as planes (the X output is not written)
+    if ((h = residual_rmsnorm(split_out_plain(c, (size_t)H, N, H), nullptr, (size_t)H, 0, L.g_attn,
+                              d->eps, xh, N, H, stream)) != hipSuccess)
+      break;
+    const char* wkv = (const char*)L.wqkv + (size_t)d->Hq * d->d * H * esize(d->dtype);
+    GemmArgs g{xh, (size_t)N * H, (size_t)H, N, wkv, wf32, (size_t)H, nkv, H, kv, (size_t)nkv,
+               nullptr, 0};
+    if ((h = gemm(g, gws, stream)) != hipSuccess) break;
+    h = rope_scatter(kv, d->positions, d->dst_rows, N, d->Hkv, d->d, d->rope_base, d->dtype,
+                     d->ctx_rows, d->k_cache[l], d->v_cache[l], stream);
+  }
+  return launch_status(h);
+}
+
 size_t dmtp_lm_head_ws(const dmtp_head_desc* d) {
   int M = 0;
   if (validate_head(d, &M) != DMTP_OK) return 0;
@@ -478,7 +567,7 @@ const char* dmtp_status_str(int s) {
   }
 }
 
-const char* dmtp_version(void) { return "dmtp 0.4.0 (gfx950, ABI 4)"; }
+const char* dmtp_version(void) { return "dmtp 0.5.0 (gfx950, ABI 5)"; }
 
 size_t dmtp_struct_size(int which) {
   switch (which) {
@@ -491,6 +580,7 @@ size_t dmtp_struct_size(int which) {
     case 6: return sizeof(dmtp_verify_desc);
     case 7: return sizeof(dmtp_stats_desc);
     case 8: return sizeof(dmtp_mtp_desc);
+    case 9: return sizeof(dmtp_ctx_desc);
     default: return 0;
   }
 }

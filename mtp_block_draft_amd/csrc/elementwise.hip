@@ -339,6 +339,48 @@ __global__ __launch_bounds__(256) void rope_split_kernel(SplitOut o, const int32
   }
 }
 
+// Two bf16 planes of n elements (x = hi + lo to 2^-18; lo = 0 for bf16 input).
+__global__ void to_planes_kernel(const void* __restrict__ x, int dtype, size_t n,
+                                 uint16_t* __restrict__ planes) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    store_planes(planes, n, i, load_elem(x, dtype, i));
+}
+
+// One workgroup per row: keys rotated at the row's position (angles in
+// float64, as in rope_split_kernel), keys and values stored in dtype at the
+// row's cache slot.
+__global__ __launch_bounds__(256) void rope_scatter_kernel(const float* __restrict__ kv,
+                                                           const int32_t* __restrict__ positions,
+                                                           const int32_t* __restrict__ dst_rows,
+                                                           int Hkv, int d, float rope_base, int dtype,
+                                                           int ctx_rows, void* __restrict__ k_cache,
+                                                           void* __restrict__ v_cache) {
+  __shared__ double cs[64], sn[64];
+  const int r = blockIdx.x;
+  const int dst = dst_rows[r];
+  if (dst < 0 || dst >= ctx_rows) return;
+  const int half = d / 2, pos = positions[r];
+  const double lnb = log((double)rope_base);
+  for (int i = threadIdx.x; i < half; i += blockDim.x) {
+    const double ang = (double)pos * exp(-(2.0 * i / d) * lnb);
+    double sv, cv;
+    sincos(ang, &sv, &cv);
+    sn[i] = sv;
+    cs[i] = cv;
+  }
+  __syncthreads();
+  const float* kr = kv + (size_t)r * 2 * Hkv * d;
+  const size_t o = (size_t)dst * Hkv * d;
+  for (int e = threadIdx.x; e < Hkv * half; e += blockDim.x) {
+    const int h = e / half, i = e % half;
+    const double a1 = kr[h * d + i], a2 = kr[h * d + i + half];
+    store_elem(k_cache, dtype, o + h * d + i, (float)(a1 * cs[i] - a2 * sn[i]));
+    store_elem(k_cache, dtype, o + h * d + i + half, (float)(a2 * cs[i] + a1 * sn[i]));
+  }
+  for (int e = threadIdx.x; e < Hkv * d; e += blockDim.x) store_elem(v_cache, dtype, o + e, kr[Hkv * d + e]);
+}
+
 // out[m] = value(m) in float32: the finished rows of a split GEMM result.
 template <int V4>
 __global__ __launch_bounds__(kRowThreads) void finish_rows_kernel(SplitOut o, float* __restrict__ out,
@@ -469,6 +511,20 @@ hipError_t swiglu(const SplitOut& g, const SplitOut& u, uint16_t* a, int rows, i
   const size_t n4 = (size_t)rows * F / 4;
   const size_t blocks = (n4 + 255) / 256 < 8192 ? (n4 + 255) / 256 : 8192;
   hipLaunchKernelGGL(swiglu_kernel, dim3((unsigned)blocks), dim3(256), 0, s, g, u, a, rows, F);
+  return hipGetLastError();
+}
+
+hipError_t to_planes(const void* x, int dtype, size_t n, uint16_t* planes, hipStream_t s) {
+  const size_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
+  hipLaunchKernelGGL(to_planes_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, dtype, n, planes);
+  return hipGetLastError();
+}
+
+hipError_t rope_scatter(const float* kv, const int32_t* positions, const int32_t* dst_rows, int N,
+                        int Hkv, int d, float rope_base, int dtype, int ctx_rows, void* k_cache,
+                        void* v_cache, hipStream_t s) {
+  hipLaunchKernelGGL(rope_scatter_kernel, dim3(N), dim3(256), 0, s, kv, positions, dst_rows, Hkv, d,
+                     rope_base, dtype, ctx_rows, k_cache, v_cache);
   return hipGetLastError();
 }
 

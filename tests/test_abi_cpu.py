@@ -223,3 +223,35 @@ def test_mtp_block_argument_errors(lib):
     assert need > 0 and _call(lib, "dmtp_mtp_block", d, ws_bytes=need - 1) == -4
     if torch.cuda.device_count() == 0:
         assert _call(lib, "dmtp_mtp_block", d, ws_bytes=need) == -6
+
+
+def test_ctx_kv_argument_errors(lib):
+    L = abi.Layer(*([FAKE] * 9))
+    arr = (abi.Layer * 1)(L)
+    caches = (ctypes.c_void_p * 1)(FAKE)
+
+    def desc(**over):
+        d = abi.CtxDesc()
+        d.N, d.n_feat, d.H, d.Hq, d.Hkv, d.d, d.n_layers, d.dtype = 10, 5, 256, 4, 2, 64, 1, 1
+        d.eps, d.rope_base, d.ctx_rows = 1e-6, 1e6, 100
+        d.feats = d.positions = d.dst_rows = d.w_fc = FAKE
+        d.layers = ctypes.cast(arr, ctypes.POINTER(abi.Layer))
+        d.k_cache = ctypes.cast(caches, ctypes.POINTER(ctypes.c_void_p))
+        d.v_cache = ctypes.cast(caches, ctypes.POINTER(ctypes.c_void_p))
+        for k, v in over.items():
+            setattr(d, k, v)
+        return d
+
+    assert lib.dmtp_ctx_kv(None, None, 0, None) == -1
+    assert _call(lib, "dmtp_ctx_kv", desc(N=0)) == -2
+    assert _call(lib, "dmtp_ctx_kv", desc(n_feat=9)) == -2
+    assert _call(lib, "dmtp_ctx_kv", desc(H=100)) == -2
+    assert _call(lib, "dmtp_ctx_kv", desc(dtype=3)) == -3
+    assert _call(lib, "dmtp_ctx_kv", desc(dst_rows=None)) == -1
+    assert _call(lib, "dmtp_ctx_kv", desc(k_cache=None)) == -1
+    assert _call(lib, "dmtp_ctx_kv", desc(w_fc=FAKE + 2)) == -5
+    d = desc()
+    need = lib.dmtp_ctx_kv_ws(ctypes.byref(d))
+    assert need > 0 and _call(lib, "dmtp_ctx_kv", d, ws_bytes=need - 1) == -4
+    if torch.cuda.device_count() == 0:
+        assert _call(lib, "dmtp_ctx_kv", d, ws_bytes=need) == -6

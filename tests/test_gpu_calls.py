@@ -361,6 +361,55 @@ def test_mtp_block(dm, dt, shape):
                 assert np.mean(got != want_r) < 0.02
 
 
+# ---------------------------------------------------------------- context K/V
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("N,NF,H,Hq,Hkv,d,NL", [(1, 5, 256, 4, 2, 64, 1), (37, 5, 512, 8, 2, 128, 2),
+                                                (300, 3, 2048, 16, 4, 128, 1)])
+def test_ctx_kv(dm, dt, N, NF, H, Hq, Hkv, d, NL):
+    """Context K/V rows from target features, written into the named cache rows."""
+    print(f"ctx_kv dt={dt} N={N} NF={NF} H={H} {Hq}/{Hkv}x{d} NL={NL}", flush=True)
+    r = np.random.default_rng(N + H)
+    rows = 2 * N + 5
+    feats = _store(r.standard_normal((N, NF, H)), dt)
+    w_fc = _store(0.02 * r.standard_normal((H, NF * H)), dt)
+    pos = r.integers(0, 40000, size=N).astype(np.int32)
+    dst = r.permutation(rows)[:N].astype(np.int32)
+    if N > 2:
+        dst[1], dst[2] = -1, rows + 3          # out of range: nothing written
+    layers = [dict(g_attn=(1 + 0.1 * r.standard_normal(H)).astype(np.float32),
+                   wqkv=_store(0.02 * r.standard_normal(((Hq + 2 * Hkv) * d, H)), dt))
+              for _ in range(NL)]
+    td, f32 = TD[dt], torch.float32
+    z = lambda *sh: torch.zeros(*sh, dtype=td, device="cuda")   # noqa: E731
+    Ls = [dm.layer_arg(g_attn=_t(L["g_attn"], f32), wqkv=_t(L["wqkv"], td), wo=z(64), g_ffn=z(64),
+                       wg=z(64), wu=z(64), wd=z(64), ctx_k=z(64), ctx_v=z(64)) for L in layers]
+    sentinel = 3.0
+    kc = [torch.full((rows, Hkv, d), sentinel, dtype=td, device="cuda") for _ in range(NL)]
+    vc = [torch.full((rows, Hkv, d), sentinel, dtype=td, device="cuda") for _ in range(NL)]
+    c_out = torch.empty(N, H, dtype=f32, device="cuda")
+    dm.ctx_kv(_t(feats, td), _t(pos, torch.int32), _t(dst, torch.int32), _t(w_fc, td), Hq=Hq,
+              Hkv=Hkv, d=d, layers=Ls, k_cache=kc, v_cache=vc, ctx_out=c_out)
+    L64 = [odm.Layer64(np.asarray(L["g_attn"], np.float64), np.asarray(L["wqkv"], np.float64),
+                       None, None, None, None, None) for L in layers]
+    c_ref, kv = odm.ctx_kv(feats.astype(np.float64), pos, w_fc.astype(np.float64), L64, Hq=Hq,
+                           Hkv=Hkv, d=d, eps=1e-6, rope_base=1e6)
+    assert max_rel(c_out.cpu().numpy(), c_ref) < 1e-5
+    rf = onm.round_to(dt)
+    ok = (dst >= 0) & (dst < rows)
+    untouched = np.setdiff1d(np.arange(rows), dst[ok])
+    for l in range(NL):
+        for cache, want in ((kc[l], kv[l][0]), (vc[l], kv[l][1])):
+            got = cache.float().cpu().numpy()
+            e = max_rel(got[dst[ok]], rf(want[ok]))
+            print("  max rel", e)
+            assert e < (1e-4 if dt == "f32" else 1e-2)
+            if dt == "bf16":
+                assert np.mean(got[dst[ok]] != rf(want[ok])) < 0.02
+            assert np.all(got[untouched] == sentinel)
+
+
 # ---------------------------------------------------------------- verify
 
 
