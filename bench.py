@@ -37,7 +37,8 @@ METRIC = "draft+verify rounds/s and accepted tokens/s at B32; % MFMA / HBM peak"
 def _workload_desc(cfg) -> str:
     return (f"{cfg.name}: B={cfg.B}, H={cfg.H}, V={cfg.V}, {cfg.n_layers} draft layer(s) "
             f"{cfg.Hq}q/{cfg.Hkv}kv x{cfg.d}, F={cfg.F}, K={cfg.K} candidates "
-            f"({cfg.S} slots, {cfg.R} verify rows), ctx U[{cfg.ctx_min},{cfg.ctx_max}], "
+            f"({cfg.S} slots, {cfg.R} verify rows), ctx U[{cfg.ctx_min},{cfg.ctx_max}] "
+            f"(drafter window {cfg.window or 'all'}), "
             f"tau={cfg.tau_mode}, verify={cfg.verify}"
             + (", MTP decoder block" if cfg.mtp_block else ""))
 

@@ -62,7 +62,8 @@ class RoundConfig:
     n_anchor: int = 2
     verify: str = "rejection"    # "rejection" | "target_only" (rows with tau > 0)
     mtp_block: bool = False      # h_MTP from an MTP decoder block over h' (else h_MTP = h')
-    window: int = 0              # 0 = every context position, else the last `window`
+    window: int = 4096           # the drafter reads the last `window` context positions before
+    #                              the anchor (0 = all of them)
     rope_base: float = 1.0e6
     eps: float = 1.0e-6
     weight_std: float = 0.02
@@ -107,7 +108,7 @@ CONFIGS: Dict[str, RoundConfig] = {
     "long_block16_bf16": RoundConfig(
         name="long_block16_bf16", B=8, H=5120, V=151936, Hq=40, Hkv=8, d=128,
         F=13824, n_layers=2, K=16, ctx_min=32768, ctx_max=32768, dtype="bf16",
-        seed=404),
+        window=0, seed=404),
     "chat_b128_mixed_bf16": RoundConfig(
         name="chat_b128_mixed_bf16", B=128, H=2048, V=151936, Hq=16, Hkv=4,
         d=128, F=6144, n_layers=1, K=7, ctx_min=64, ctx_max=512, dtype="bf16",

@@ -181,6 +181,16 @@ def test_long_block16_full_size(rnd):
 
 
 @pytest.mark.timeout(900)
+def test_long_block16_anchor_window_full_size(rnd):
+    """The pages' default visibility: the last 4096 context positions before the anchor."""
+    cfg = synth.CONFIGS["long_block16_bf16"].with_(window=4096)
+    inp = synth.make_inputs(cfg)
+    R, g = _run(rnd, inp)
+    res, rep = compare_round(inp, g, seqs=[3])
+    _report(f"{cfg.name}/window4096", rep)
+
+
+@pytest.mark.timeout(900)
 def test_whole_round_graph_replays_match_eager(rnd):
     """The round captured as one graph gives, on every replay, the eager round's
     results bit for bit; eager work and synchronisations sit between replays."""
