@@ -138,19 +138,26 @@ def rocprof_summary(args) -> int:
     return 0
 
 
-def cpu_baseline(inp, n_seq: int):
+def cpu_baseline(inp, n_seq: int, min_seconds: float = 10.0):
+    """The oracle as it stands, on the host cores: whole rounds (or the first
+    n_seq sequences of one, scaled) repeated until min_seconds have passed."""
     from threadpoolctl import threadpool_info
     from oracle import dmtp as odm
 
     seqs = list(range(min(n_seq, inp.cfg.B)))
-    t0 = time.perf_counter()
-    odm.run_round(inp, seqs=seqs)
-    dt = time.perf_counter() - t0
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        odm.run_round(inp, seqs=seqs)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
     scale = inp.cfg.B / len(seqs)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": 1.0 / (dt * scale), "unit": "rounds/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"float64 NumPy oracle on {len(seqs)} of {inp.cfg.B} sequences of one round "
-                      f"({dt:.1f} s), scaled x{scale:g} to a whole round",
+    return {"value": reps / (dt * scale), "unit": "rounds/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"float64 NumPy oracle, {reps} repetitions of {len(seqs)} of {inp.cfg.B} "
+                      f"sequences of one round ({dt:.1f} s)"
+                      + (f", scaled x{scale:g} to a whole round" if scale != 1 else ""),
             "seconds": dt}
 
 
@@ -168,7 +175,9 @@ def main() -> int:
     ap.add_argument("--mtp-block", action="store_true",
                     help="h_MTP from an MTP decoder block (drafter layer shapes, causal over its "
                          "own KV cache) instead of h_MTP = h'")
-    ap.add_argument("--cpu-seqs", type=int, default=8, help="sequences in the oracle sample")
+    ap.add_argument("--cpu-seqs", type=int, default=32, help="sequences in the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="repeat the oracle sample until this much time has passed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before warm-up, copy this many MiB device-to-device once (a kernel "
@@ -273,6 +282,22 @@ def main() -> int:
         hip.hipEventDestroy(b)
     one_round()   # leaves the descriptor without events
 
+    # Rounds with a cold last-level cache: 512 MB written before each round
+    # evicts the 256 MB cache that back-to-back rounds partly share (drafter
+    # weights, context K/V); each such round is timed alone by its own events.
+    n_flush = min(args.steps, 50)
+    flush = torch.empty((512 << 20) // 4, dtype=torch.float32, device="cuda")
+    fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_flush)]
+    for k in range(n_flush):
+        flush.fill_(float(k))
+        fev[k][0].record(stream)
+        one_round()
+        fev[k][1].record(stream)
+    torch.cuda.synchronize()
+    flushed_us = 1000.0 * float(np.median([a.elapsed_time(b) for a, b in fev]))
+    del flush
+
     graph_ms_step = None
     if args.graph:
         R.capture()
@@ -333,11 +358,15 @@ def main() -> int:
         "committed_tokens_per_round": committed,
         "phases_us": dict(zip(R.step_names, [round(x, 2) for x in per_call_us])),
         "roofline": roofline,
+        "cold_cache_round": {"us": round(flushed_us, 2), "rounds_per_s": round(1e6 / flushed_us, 2),
+                             "rounds": n_flush,
+                             "note": "median of single rounds, each after 512 MB of writes that "
+                                     "evict the 256 MB last-level cache"},
     }
     if graph_ms_step is not None:
         out["eager_rounds_per_s"] = round(1000.0 / eager_ms_step, 2)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seqs)
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seqs, args.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0
 

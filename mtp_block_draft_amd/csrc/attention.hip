@@ -317,22 +317,23 @@ __global__ __launch_bounds__(64) void attn_wave_kernel(
     koff[i] = (uint32_t)(r * row_stride) + 8 * (pos ^ swz_key<D>(r));
     voff[i] = (uint32_t)(r * row_stride) + 8 * (pos ^ swz_val(r));
   }
+  // context K/V is read once per call: non-temporal copies
   auto issue = [&](int t) __attribute__((always_inline)) {
     uint16_t* st = smem + (t % C::NBUF) * C::STAGE;
     const size_t t0 = (size_t)C::KT * t * row_stride;
     if (C::KT * (t + 1) <= nkeys) {
 #pragma unroll
       for (int i = 0; i < C::INSTR; ++i) {
-        lds_dma16(kbase + t0 + koff[i], st + i * 512);
-        lds_dma16(vbase + t0 + voff[i], st + C::KT * D + i * 512);
+        lds_dma16<2>(kbase + t0 + koff[i], st + i * 512);
+        lds_dma16<2>(vbase + t0 + voff[i], st + C::KT * D + i * 512);
       }
     } else {   // last tile: rows past the chunk end repeat its last key (masked below)
 #pragma unroll
       for (int i = 0; i < C::INSTR; ++i) {
         const int r = C::RPI * i + rr;
         const size_t row = (size_t)min(C::KT * t + r, nkeys - 1) * row_stride;
-        lds_dma16(kbase + row + 8 * (pos ^ swz_key<D>(r)), st + i * 512);
-        lds_dma16(vbase + row + 8 * (pos ^ swz_val(r)), st + C::KT * D + i * 512);
+        lds_dma16<2>(kbase + row + 8 * (pos ^ swz_key<D>(r)), st + i * 512);
+        lds_dma16<2>(vbase + row + 8 * (pos ^ swz_val(r)), st + C::KT * D + i * 512);
       }
     }
   };

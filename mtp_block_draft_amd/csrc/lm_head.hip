@@ -324,8 +324,14 @@ void head_gemm_mf32_kernel(HeadParams p, int n_mchunks) {
       dst[q] = C::BV * C::BK + (wave * C::XPW + qq) * 512;
     }
   }
+  // The weight rows are read once per call and the matrix is larger than the
+  // 256 MB last-level cache: their copies are non-temporal, which keeps them
+  // from evicting the input rows every workgroup re-reads.
   auto issue_one = [&](int slice, int q) __attribute__((always_inline)) {
-    lds_dma16(src[q] + slice * C::BK, smem + (slice % C::NBUF) * C::STAGE + dst[q]);
+    if (q < C::WPW)
+      lds_dma16<2>(src[q] + slice * C::BK, smem + (slice % C::NBUF) * C::STAGE + dst[q]);
+    else
+      lds_dma16(src[q] + slice * C::BK, smem + (slice % C::NBUF) * C::STAGE + dst[q]);
   };
   // fragments of one 16-wide k-step
   struct Frag {
