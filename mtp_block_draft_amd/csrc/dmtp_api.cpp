@@ -146,6 +146,7 @@ DraftWs stack_ws(const Stack& d) {
   };
   upd((int)R, qkv_n, d.H);
   upd((int)R, d.H, d.Hq * d.d);
+  upd((int)R, 2 * d.F, d.H);   // gate and up as one GEMM (bf16 weights)
   upd((int)R, d.F, d.H);
   upd((int)R, d.H, d.F);
   size_t o = 0;
@@ -156,7 +157,7 @@ DraftWs stack_ws(const Stack& d) {
   w.kb = o; o = al(o + R * d.Hkv * d.d * 4);
   w.vb = o; o = al(o + R * d.Hkv * d.d * 4);
   w.o = o; o = al(o + R * d.Hq * d.d * 4);
-  w.gate = o; o = al(o + R * d.F * 4);
+  w.gate = o; o = al(o + R * 2 * d.F * 4);   // [R, 2F]: gate columns, then up columns
   w.up = o; o = al(o + R * d.F * 4);
   w.act = o; o = al(o + R * d.F * 4);
   w.gemm = o; o = al(o + gemm_max);
@@ -216,12 +217,27 @@ hipError_t run_stack(const Stack& d, const DraftWs& w, char* b, void* const* k_n
     if ((h = residual_rmsnorm(so, X, (size_t)d.H, 1, L.g_ffn, d.eps, xh, R, d.H, stream)) !=
         hipSuccess)
       break;
-    GemmArgs g3{xh, pst_h, (size_t)d.H, R, L.wg, wf32, (size_t)d.H, d.F, d.H, gate,
-                (size_t)d.F, nullptr, 0};
-    if ((h = gemm_deferred(g3, gws, stream, &sg)) != hipSuccess) break;
-    GemmArgs g4{xh, pst_h, (size_t)d.H, R, L.wu, wf32, (size_t)d.H, d.F, d.H, up,
-                (size_t)d.F, nullptr, 0};
-    if ((h = gemm_deferred(g4, gws2, stream, &su)) != hipSuccess) break;
+    if (!wf32) {
+      // gate and up projections of the same rows as one GEMM over [Wg; Wu]:
+      // columns [0, F) are the gate, [F, 2F) the up projection
+      GemmArgs g3{xh, pst_h, (size_t)d.H, R, L.wg, wf32, (size_t)d.H, 2 * d.F, d.H, gate,
+                  (size_t)2 * d.F, nullptr, 0};
+      g3.B2 = L.wu;
+      g3.N1 = d.F;
+      SplitOut sgu;
+      if ((h = gemm_deferred(g3, gws, stream, &sgu)) != hipSuccess) break;
+      sg = sgu;
+      su = sgu;
+      su.C = sgu.C + d.F;
+      if (su.splits > 1) su.part = sgu.part + d.F;
+    } else {
+      GemmArgs g3{xh, pst_h, (size_t)d.H, R, L.wg, wf32, (size_t)d.H, d.F, d.H, gate,
+                  (size_t)d.F, nullptr, 0};
+      if ((h = gemm_deferred(g3, gws, stream, &sg)) != hipSuccess) break;
+      GemmArgs g4{xh, pst_h, (size_t)d.H, R, L.wu, wf32, (size_t)d.H, d.F, d.H, up,
+                  (size_t)d.F, nullptr, 0};
+      if ((h = gemm_deferred(g4, gws2, stream, &su)) != hipSuccess) break;
+    }
     if ((h = swiglu(sg, su, act, R, d.F, stream)) != hipSuccess) break;
     const size_t pst_f = (size_t)R * d.F;
     GemmArgs g5{act, pst_f, (size_t)d.F, R, L.wd, wf32, (size_t)d.F, d.H, d.F, X,

@@ -34,6 +34,8 @@ struct GemmParams {
   const float* R;
   size_t ldr;
   float* part;   // [splits, M, N] when splits > 1
+  const void* B2;  // rows n >= N1 of the weight come from B2 (NULL: B only)
+  int N1;
 };
 
 // ------------------------------------------------- bf16 weight, LDS ring ----
@@ -77,6 +79,7 @@ void gemm_dma_kernel(GemmParams p, int n_tiles_n, int n_tiles_m) {
   const int wn = wave % T::WAVES_N, wm = wave / T::WAVES_N;
   const int lr = lane & 31, lk = lane >> 5;
   const uint16_t* __restrict__ W = (const uint16_t*)p.B;
+  const uint16_t* __restrict__ W2 = (const uint16_t*)p.B2;
   const uint16_t* __restrict__ A = (const uint16_t*)p.A;
 
   // sources of this wave's copies: W rows first, then the hi and lo planes of A
@@ -87,7 +90,9 @@ void gemm_dma_kernel(GemmParams p, int n_tiles_n, int n_tiles_m) {
     const int instr = wave * T::PER_WAVE + q;
     if (instr < T::W_INSTR) {
       const int idx = instr * 64 + lane, r = idx / T::CPR;
-      src[q] = W + (size_t)min(n0 + r, p.N - 1) * p.ldb + 8 * swz_chunk<T::BK>(r, idx % T::CPR);
+      const int wr = min(n0 + r, p.N - 1);
+      const uint16_t* wrow = (W2 && wr >= p.N1) ? W2 + (size_t)(wr - p.N1) * p.ldb : W + (size_t)wr * p.ldb;
+      src[q] = wrow + 8 * swz_chunk<T::BK>(r, idx % T::CPR);
     } else {
       const int j = instr - T::W_INSTR, pl = j / (T::A_INSTR / 2);
       const int idx = (j % (T::A_INSTR / 2)) * 64 + lane, r = idx / T::CPR;
@@ -310,7 +315,7 @@ DmaPlan dma_plan(int M, int N, int K) {
 }
 
 bool dma_ok(const GemmArgs& a) {
-  return !a.b_f32 && a.K % 64 == 0 && a.N % 4 == 0 && a.ldc % 4 == 0 && (!a.R || a.ldr % 4 == 0) &&
+  return !a.b_f32 && (!a.B2 || (a.N1 > 0 && a.N1 < a.N)) && a.K % 64 == 0 && a.N % 4 == 0 && a.ldc % 4 == 0 && (!a.R || a.ldr % 4 == 0) &&
          a.lda % 8 == 0 && a.ldb % 8 == 0 && a.a_pst % 8 == 0;
 }
 
@@ -363,7 +368,8 @@ size_t gemm_ws_bytes(int M, int N, int K, int b_f32) {
 }
 
 hipError_t gemm_deferred(const GemmArgs& a, float* ws, hipStream_t s, SplitOut* out) {
-  GemmParams p{a.A, a.a_pst, a.lda, a.M, a.B, a.ldb, a.N, a.K, 1, a.C, a.ldc, a.R, a.ldr, ws};
+  GemmParams p{a.A, a.a_pst, a.lda, a.M, a.B, a.ldb, a.N, a.K, 1, a.C, a.ldc, a.R, a.ldr, ws,
+               a.B2, a.B2 ? a.N1 : a.N};
   *out = SplitOut{a.C, a.ldc, ws, 1, a.M, a.N, a.R, a.ldr};
   if (!a.b_f32) {
     if (!dma_ok(a)) return hipErrorInvalidValue;
@@ -379,7 +385,8 @@ hipError_t gemm_deferred(const GemmArgs& a, float* ws, hipStream_t s, SplitOut* 
 }
 
 hipError_t gemm(const GemmArgs& a, float* ws, hipStream_t s) {
-  GemmParams p{a.A, a.a_pst, a.lda, a.M, a.B, a.ldb, a.N, a.K, 1, a.C, a.ldc, a.R, a.ldr, ws};
+  GemmParams p{a.A, a.a_pst, a.lda, a.M, a.B, a.ldb, a.N, a.K, 1, a.C, a.ldc, a.R, a.ldr, ws,
+               a.B2, a.B2 ? a.N1 : a.N};
   if (!a.b_f32) {
     if (!dma_ok(a)) return hipErrorInvalidValue;
     const DmaPlan pl = dma_plan(a.M, a.N, a.K);

@@ -27,6 +27,10 @@ struct GemmArgs {
   size_t ldc;
   const float* R;   // residual or NULL
   size_t ldr;
+  // Optional second weight matrix: output columns n >= N1 use row n - N1 of B2
+  // (same ldb and dtype), so two projections of one input run as one GEMM.
+  const void* B2 = nullptr;
+  int N1 = 0;
 };
 
 // float32 workspace the GEMM launcher needs for its split-K partials.
