@@ -276,16 +276,27 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(uint2, v);
 }
 
+// Workgroup: the waves of up to kAttnQtw 32-row query tiles of one (context
+// chunk, kv head, sequence).  They share one LDS ring of K/V tiles, so a chunk
+// is read once for all of them: wave 0 issues every copy and waits for it, a
+// workgroup barrier per tile hands the tile to the others.  With more query
+// tiles than that, blockIdx.y also selects the group of tiles.
+constexpr int kAttnQtw = 4;
+
 template <int D, int NBUF>
-__global__ __launch_bounds__(64) void attn_wave_kernel(
+__global__ __launch_bounds__(64 * kAttnQtw) void attn_wave_kernel(
     const float* __restrict__ q, const uint16_t* __restrict__ ctx_k,
     const uint16_t* __restrict__ ctx_v, const int32_t* __restrict__ cu_ctx, int ctx_rows, int Hkv,
     int NQ, int NQP, int chunk, int n_chunks, int window, float scale, float* __restrict__ part_o,
     float* __restrict__ part_ml) {
   typedef WaveAttn<D, NBUF> C;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  const int c = blockIdx.x, kvh = blockIdx.y % Hkv, qt = blockIdx.y / Hkv, b = blockIdx.z;
-  const int lane = threadIdx.x, lr = lane & 31, g = lane >> 5;
+  const int c = blockIdx.x, kvh = blockIdx.y % Hkv, b = blockIdx.z;
+  const int wave = threadIdx.x >> 6, waves = blockDim.x >> 6;
+  const int qt = (blockIdx.y / Hkv) * waves + wave;
+  const bool live = 32 * qt < NQP;     // a wave past the last query tile only joins the barriers
+  const bool issuer = wave == 0;
+  const int lane = threadIdx.x & 63, lr = lane & 31, g = lane >> 5;
   const int L = ctx_len_of(cu_ctx, b, ctx_rows);
   const int start = (window > 0 && L > window) ? L - window : 0;
   const int k_lo = start + c * chunk;
@@ -295,7 +306,7 @@ __global__ __launch_bounds__(64) void attn_wave_kernel(
   float* pml = part_ml + slot * 2 * NQP;
   const int qrow = 32 * qt + lr;   // this lane's query row
   if (k_lo >= k_hi) {               // empty chunk: neutral partial
-    if (g == 0) {
+    if (g == 0 && live) {
       pml[qrow] = -INFINITY;
       pml[NQP + qrow] = 0.f;
     }
@@ -358,9 +369,10 @@ __global__ __launch_bounds__(64) void attn_wave_kernel(
     ql[ds] = u32x4{l[0], l[1], l[2], l[3]};
   }
 
+  if (issuer)
 #pragma unroll
-  for (int t0 = 0; t0 < C::NBUF - 1; ++t0)
-    if (t0 < nt) issue(t0);
+    for (int t0 = 0; t0 < C::NBUF - 1; ++t0)
+      if (t0 < nt) issue(t0);
 
   f32x16_t o[C::DT];
 #pragma unroll
@@ -392,10 +404,11 @@ __global__ __launch_bounds__(64) void attn_wave_kernel(
     }
 
   for (int t = 0; t < nt; ++t) {
-    wait_newer<C::PER_TILE, C::NBUF - 2>(min(nt - 1 - t, C::NBUF - 2));
-    asm volatile("" ::: "memory");
-    // the buffer refilled here held tile t - 1, whose reads have all returned
-    if (t + C::NBUF - 1 < nt) issue(t + C::NBUF - 1);
+    if (issuer) wait_newer<C::PER_TILE, C::NBUF - 2>(min(nt - 1 - t, C::NBUF - 2));
+    // tile t is in LDS for every wave; every wave has consumed tile t - 1 (its
+    // MFMAs used the fragments read from it), whose buffer is refilled next
+    ring_barrier();
+    if (issuer && t + C::NBUF - 1 < nt) issue(t + C::NBUF - 1);
     const uint16_t* st = smem + (t % C::NBUF) * C::STAGE;
 
     // S^T[key][query]: element i is key 8 (i / 4) + 4 g + i % 4 of this lane's
@@ -459,6 +472,7 @@ __global__ __launch_bounds__(64) void attn_wave_kernel(
   }
 
   // partial: O^T element i of tile dt is dd = 32 dt + 8 (i / 4) + 4 g + i % 4 of query qrow
+  if (!live) return;
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
@@ -710,8 +724,10 @@ hipError_t launch_wave_n(const AttnPlan& p, const float* q, const void* ck, cons
   hipError_t e = hipFuncSetAttribute((const void*)attn_wave_kernel<D, NBUF>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES);
   if (e != hipSuccess) return e;
-  dim3 grid(p.n_chunks, p.Hkv * (p.nqp / 32), p.B);
-  hipLaunchKernelGGL((attn_wave_kernel<D, NBUF>), grid, dim3(64), C::LDS_BYTES, s, q, (const uint16_t*)ck,
+  const int qtiles = p.nqp / 32;
+  const int qtw = qtiles < kAttnQtw ? qtiles : kAttnQtw;
+  dim3 grid(p.n_chunks, p.Hkv * ((qtiles + qtw - 1) / qtw), p.B);
+  hipLaunchKernelGGL((attn_wave_kernel<D, NBUF>), grid, dim3(64 * qtw), C::LDS_BYTES, s, q, (const uint16_t*)ck,
                      (const uint16_t*)cv, cu, ctx_rows, p.Hkv, p.NQ, p.nqp, p.chunk, p.n_chunks,
                      p.window, scale, po, pml);
   return hipGetLastError();
