@@ -97,7 +97,7 @@ def _head_case(seed, H, V, dt, M_norm=5, M_rows=20, M_strided=12):
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
-@pytest.mark.parametrize("H,V", [(256, 5003), (2048, 151936)])
+@pytest.mark.parametrize("H,V", [(256, 5003), (2048, 151936), (256, 2), (192, 130)])
 def test_lm_head_greedy(dm, dt, H, V):
     print(f"lm_head greedy dt={dt} H={H} V={V}", flush=True)
     W, hid, g, rows, strided, x = _head_case(H + V, H, V, dt)
@@ -257,6 +257,12 @@ def _draft_case(seed, dt, B, H, Hq, Hkv, d, F, NL, K, n_anchor, ctx_lens, V=500,
     # 144 slot rows, widths that end mid-tile, 48 query rows per kv head
     dict(B=9, H=320, Hq=6, Hkv=2, d=64, F=576, NL=1, K=15, n_anchor=2,
          ctx_lens=[0, 1, 31, 64, 100, 257, 513, 40, 9]),
+    # the largest block (32 candidates, 33 slots): three query tiles share a chunk's K/V
+    dict(B=2, H=256, Hq=2, Hkv=1, d=64, F=256, NL=1, K=32, n_anchor=2, ctx_lens=[50, 0]),
+    # 170 query rows per kv head: six query tiles, two workgroups of four (two waves idle)
+    dict(B=2, H=256, Hq=10, Hkv=1, d=64, F=256, NL=1, K=16, n_anchor=2, ctx_lens=[300, 40]),
+    # the smallest block: one MASK slot
+    dict(B=3, H=256, Hq=4, Hkv=2, d=64, F=256, NL=1, K=2, n_anchor=2, ctx_lens=[17, 0, 64]),
 ])
 def test_block_draft(dm, dt, shape):
     shape = dict(shape)
@@ -271,9 +277,11 @@ def test_block_draft(dm, dt, shape):
     out = torch.empty(B * (K - 1), H, dtype=td, device="cuda")
     V = c["emb"].shape[0]
     S = K - 1 + na
-    if dt == "f32" and S * shape["Hq"] // shape["Hkv"] > 64:
-        # float32 context K/V doubles the LDS tiles: more than 64 query rows per
-        # kv head do not fit one workgroup, and the library refuses the shape
+    f32_rows = 128 if shape["d"] == 64 else 64
+    if dt == "f32" and S * shape["Hq"] // shape["Hkv"] > f32_rows:
+        # float32 context K/V doubles the LDS tiles: more than 128 (d = 64) or
+        # 64 (d = 128) query rows per kv head do not fit one workgroup, and the
+        # library refuses the shape
         with pytest.raises(dm.DmtpError):
             dm.block_draft(out, B=B, H=H, Hq=shape["Hq"], Hkv=shape["Hkv"], d=shape["d"],
                            F=shape["F"], K=K, n_anchor=na, layers=Ls,
@@ -551,3 +559,57 @@ def test_accept_stats_of_an_empty_histogram_are_nan(dm):
     summ = torch.zeros(2 + 2 * K, dtype=torch.float64, device="cuda")
     dm.accept_stats(torch.empty(0, dtype=torch.int32, device="cuda"), K, hist, summ)
     assert np.all(hist.cpu().numpy() == 0) and np.all(np.isnan(summ.cpu().numpy()))
+
+
+def test_verify_one_candidate(dm):
+    """K = 1: the MTP candidate alone, greedy, sampled and target-only."""
+    B, K, V = 12, 1, 500
+    r = np.random.default_rng(21)
+    tau = np.where(np.arange(B) % 2 == 0, 0.0, 1.0).astype(np.float32)
+    logits = (1.5 * r.standard_normal((B, 2 * K + 1, V))).astype(np.float32)
+    target = logits[:, K:, :].argmax(-1).astype(np.int32)
+    t1 = r.integers(0, V, size=B).astype(np.int32)
+    t1[::3] = target[::3, 0]                 # some accepted, some rejected
+    u = (r.integers(0, 1 << 24, size=(B, K)) * 2.0 ** -24).astype(np.float32)
+    tt = np.where(tau > 0, tau, 1.0).astype(np.float64)
+    lse = _softmax_lse(logits.astype(np.float64), tt[:, None, None]).astype(np.float32)
+    fkeys = np.arange(B, dtype=np.uint64) + np.uint64(5 << 32)
+    seed = 5
+    L64 = logits.astype(np.float64)
+    for target_only in (False, True):
+        acc = torch.empty(B, dtype=torch.int32, device="cuda")
+        out = torch.empty(B, K + 1, dtype=torch.int32, device="cuda")
+        n_out = torch.empty(B, dtype=torch.int32, device="cuda")
+        dm.verify(B=B, K=K, V=V, t1=_t(t1, torch.int32), drafts=None, target=_t(target, torch.int32),
+                  accept_len=acc, out_tokens=out, n_out=n_out, temperature=_t(tau, torch.float32),
+                  logits=_t(logits.reshape(B * 3, V), torch.float32),
+                  t1_lse=_t(lse[:, 0], torch.float32), draft_lse=None,
+                  target_lse=_t(lse[:, K:], torch.float32), u_acc=_t(u, torch.float32), seed=seed,
+                  final_key=_t(fkeys.view(np.int64), torch.int64), target_only=target_only)
+        acc, out, n_out = acc.cpu().numpy(), out.cpu().numpy(), n_out.cpu().numpy()
+        for b in range(B):
+            if target_only or tau[b] == 0:
+                L, toks = odm.verify_greedy([t1[b]], target[b])
+                assert acc[b] == L and list(out[b, :L + 1]) == toks and n_out[b] == L + 1
+                assert np.all(out[b, L + 1:] == -1)
+                continue
+            q = np.exp(L64[b, :K] / tau[b] - onm.logsumexp(L64[b, :K] / tau[b])[:, None])
+            p = np.exp(L64[b, K:] / tau[b] - onm.logsumexp(L64[b, K:] / tau[b])[:, None])
+            m = {}
+
+            def accept(i, ratio):
+                m["a"] = abs(np.log(u[b, i]) - np.log(ratio)) if u[b, i] > 0 else np.inf
+                return bool(u[b, i] < ratio)
+
+            def draw(i, w):
+                with np.errstate(divide="ignore"):
+                    j, mg = oph.gumbel_argmax(np.log(np.asarray(w)), seed, int(fkeys[b]))
+                m["final"] = mg
+                return j
+
+            L, toks = odm.verify_rejection([t1[b]], p, q, accept, draw)
+            if acc[b] != L:
+                assert m["a"] < NEAR_TIE
+                continue
+            assert list(out[b, :L]) == toks[:L] and n_out[b] == L + 1
+            assert out[b, L] == toks[L] or m["final"] < NEAR_TIE

@@ -110,6 +110,16 @@ def test_ragged_mixed_bf16(rnd):
     _report(cfg.name, rep)
 
 
+@pytest.mark.parametrize("K", [2, 6])
+def test_tiny_round_block_sizes(rnd, K):
+    """K = 2 (a single MASK slot) and K = 6 (the literal five-MASK layout)."""
+    cfg = synth.CONFIGS["tiny_greedy_f32"].with_(K=K, B=3, ctx_min=0, ctx_max=150, gain_std=0.1)
+    inp = synth.make_inputs(cfg)
+    R, g = _run(rnd, inp)
+    res, rep = compare_round(inp, g)
+    _report(f"tiny K={K}", rep)
+
+
 def test_single_anchor_layout(rnd):
     cfg = synth.CONFIGS["tiny_greedy_f32"].with_(n_anchor=1, B=3, ctx_min=10, ctx_max=90)
     inp = synth.make_inputs(cfg)
