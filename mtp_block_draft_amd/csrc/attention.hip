@@ -681,12 +681,15 @@ AttnPlan attn_plan(int B, int Hq, int Hkv, int S, int d, int max_ctx, int window
     return p;
   }
   if (!kv_f32) {
-    // per-wave kernel: about 1536 waves over the context rows actually present
-    // (ctx_rows / B per sequence on average), at least four 32-key tiles each,
-    // at most 256 chunks per sequence for the combine
+    // per-wave kernel: about 768 query-tile waves over the context rows
+    // actually present (ctx_rows / B per sequence on average), at least four
+    // 32-key tiles each, at most 256 chunks per sequence for the combine.
+    // Measured against 384 .. 3072: fewer, longer chunks keep each wave's copy
+    // pipeline full for longer; below 768 the long-context workload runs out
+    // of parallelism.
     const long keys = (long)(ctx_rows > 0 ? ctx_rows : (long)B * eff);
     const long tiles = keys * Hkv * (p.nqp / 32);
-    constexpr long target = 1536;
+    constexpr long target = 768;
     long per = (tiles + target * 32 - 1) / (target * 32);
     if (per < 4) per = 4;
     int chunk = (int)(32 * per);
