@@ -162,6 +162,49 @@ def cpu_baseline(inp, n_seq: int, min_seconds: float = 10.0):
             "seconds": dt}
 
 
+def ctx_kv_bench(R, cfg, stream, steps: int, warmup: int):
+    """Time dmtp_ctx_kv on the rows one round can commit (B (K + 1)), five bf16
+    feature streams per row, into fresh caches of the drafter layers' shapes."""
+    import torch
+    from mtp_block_draft_amd import call, ctx_kv, layer_arg, lib, workspace_bytes
+
+    N, H, nf = cfg.B * (cfg.K + 1), cfg.H, 5
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    gen = torch.Generator(device="cuda").manual_seed(cfg.seed + 7)
+    feats = torch.randn(N, nf, H, generator=gen, device="cuda").to(tdt)
+    w_fc = (0.02 * torch.randn(H, nf * H, generator=gen, device="cuda")).to(tdt)
+    pos = torch.arange(N, dtype=torch.int32, device="cuda") + 4096
+    dst = torch.arange(N, dtype=torch.int32, device="cuda")
+    layers = [layer_arg(**lt) for lt in R.layers_t]
+    kc = [torch.empty(N, cfg.Hkv, cfg.d, dtype=tdt, device="cuda") for _ in layers]
+    vc = [torch.empty(N, cfg.Hkv, cfg.d, dtype=tdt, device="cuda") for _ in layers]
+    desc = ctx_kv(feats, pos, dst, w_fc, Hq=cfg.Hq, Hkv=cfg.Hkv, d=cfg.d, layers=layers, k_cache=kc,
+                  v_cache=vc, eps=cfg.eps, rope_base=cfg.rope_base, run=False)
+    ws = torch.empty(max(workspace_bytes("ctx_kv", desc), 256), dtype=torch.uint8, device="cuda")
+    call("ctx_kv", desc, ws)
+    # the entry point itself, as the round loop calls it (no per-call query)
+    import ctypes
+    fn, ref = lib.dmtp_ctx_kv, ctypes.byref(desc)
+    wsp, wsn, sp = ctypes.c_void_p(ws.data_ptr()), ws.numel(), ctypes.c_void_p(stream.cuda_stream)
+    for _ in range(warmup):
+        fn(ref, wsp, wsn, sp)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(steps):
+        if fn(ref, wsp, wsn, sp) != 0:
+            raise RuntimeError("dmtp_ctx_kv failed")
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = 1000.0 * a.elapsed_time(b) / steps
+    esz = 2 if cfg.dtype == "bf16" else 4
+    nbytes = (H * nf * H + len(layers) * 2 * cfg.Hkv * cfg.d * H + N * nf * H
+              + len(layers) * 2 * N * cfg.Hkv * cfg.d) * esz
+    return {"rows": N, "feature_streams": nf, "layers": len(layers), "us": round(us, 2),
+            "algorithmic_bytes": nbytes, "gb_s": round(nbytes / us / 1e3, 1),
+            "hbm_frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -173,6 +216,8 @@ def main() -> int:
                          "GEMM is still timed by its dispatch events in an eager pass)")
     ap.add_argument("--verify", choices=["rejection", "target_only"], default=None,
                     help="verification of sampled rows (default: the workload's)")
+    ap.add_argument("--ctx-kv", action="store_true",
+                    help="also time dmtp_ctx_kv on the rows one round can commit")
     ap.add_argument("--mtp-block", action="store_true",
                     help="h_MTP from an MTP decoder block (drafter layer shapes, causal over its "
                          "own KV cache) instead of h_MTP = h'")
@@ -370,6 +415,8 @@ def main() -> int:
     }
     if graph_ms_step is not None:
         out["eager_rounds_per_s"] = round(1000.0 / eager_ms_step, 2)
+    if args.ctx_kv:
+        out["ctx_kv"] = ctx_kv_bench(R, cfg, stream, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seqs, args.cpu_seconds)
     print(json.dumps(out), flush=True)

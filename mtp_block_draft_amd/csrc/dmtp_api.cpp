@@ -507,10 +507,20 @@ int dmtp_ctx_kv(const dmtp_ctx_desc* d, void* ws, size_t ws_bytes, hipStream_t s
   float* gws = (float*)(b + w.gemm);
   const int N = d->N, H = d->H, KF = d->n_feat * d->H, nkv = 2 * d->Hkv * d->d;
   const int wf32 = d->dtype == DMTP_F32;
-  hipError_t h = to_planes(d->feats, d->dtype, (size_t)N * KF, planes, stream);
-  if (h == hipSuccess) {
-    GemmArgs g{planes, (size_t)N * KF, (size_t)KF, N, d->w_fc, wf32, (size_t)KF, H, KF, c,
+  hipError_t h = hipSuccess;
+  if (wf32) {
+    // float32 features and weights: the two-plane product
+    h = to_planes(d->feats, d->dtype, (size_t)N * KF, planes, stream);
+    if (h == hipSuccess) {
+      GemmArgs g{planes, (size_t)N * KF, (size_t)KF, N, d->w_fc, wf32, (size_t)KF, H, KF, c,
+                 (size_t)H, nullptr, 0};
+      h = gemm(g, gws, stream);
+    }
+  } else {
+    // bf16 features enter the projection as they are (one plane)
+    GemmArgs g{(const uint16_t*)d->feats, 0, (size_t)KF, N, d->w_fc, wf32, (size_t)KF, H, KF, c,
                (size_t)H, nullptr, 0};
+    g.a_planes = 1;
     h = gemm(g, gws, stream);
   }
   for (int l = 0; l < d->n_layers && h == hipSuccess; ++l) {

@@ -41,18 +41,19 @@ struct GemmParams {
 // ------------------------------------------------- bf16 weight, LDS ring ----
 // Workgroup of four waves, WAVES_N along N times 4 / WAVES_N along M; wave tile
 // 32 UN (weight rows) x 32 UM (activation rows).  One k-slice of BK is staged
-// as W [BN][BK] and the two activation planes [2][BM][BK], bf16, 16-byte chunks
-// swizzled by swz_row (a 64-wide slice copies whole 128-byte lines).
-template <int UN_, int UM_, int WAVES_N_, int BK_ = 64>
+// as W [BN][BK] and the AP activation planes [AP][BM][BK], bf16, 16-byte chunks
+// swizzled by swz_row (a 64-wide slice copies whole 128-byte lines).  AP = 2:
+// a float32 activation as hi + lo planes; AP = 1: a bf16 activation as is.
+template <int UN_, int UM_, int WAVES_N_, int BK_ = 64, int AP_ = 2>
 struct DmaTile {
   static constexpr int UN = UN_, UM = UM_, WAVES_N = WAVES_N_, WAVES_M = 4 / WAVES_N_;
-  static constexpr int BN = 32 * UN * WAVES_N, BM = 32 * UM * WAVES_M, BK = BK_;
+  static constexpr int BN = 32 * UN * WAVES_N, BM = 32 * UM * WAVES_M, BK = BK_, AP = AP_;
   static constexpr int CPR = BK / 8, KS = BK / 16;   // 16-byte chunks per row, k-steps per slice
   static constexpr int W_INSTR = BN * BK * 2 / 1024;   // 1 KB copies per slice
-  static constexpr int A_INSTR = 2 * BM * BK * 2 / 1024;
-  static_assert((W_INSTR + A_INSTR) % 4 == 0 && A_INSTR % 2 == 0, "copies per wave");
+  static constexpr int A_INSTR = AP * BM * BK * 2 / 1024;
+  static_assert((W_INSTR + A_INSTR) % 4 == 0 && A_INSTR % AP == 0, "copies per wave");
   static constexpr int PER_WAVE = (W_INSTR + A_INSTR) / 4;
-  static constexpr int STAGE = (BN + 2 * BM) * BK;     // bf16 elements
+  static constexpr int STAGE = (BN + AP * BM) * BK;    // bf16 elements
   static constexpr int NBUF_FIT = 147456 / (STAGE * 2);
   static constexpr int NBUF = NBUF_FIT > 8 ? 8 : NBUF_FIT;
   static_assert(NBUF >= 2 && PER_WAVE * (NBUF - 2) < 64, "ring");
@@ -94,8 +95,8 @@ void gemm_dma_kernel(GemmParams p, int n_tiles_n, int n_tiles_m) {
       const uint16_t* wrow = (W2 && wr >= p.N1) ? W2 + (size_t)(wr - p.N1) * p.ldb : W + (size_t)wr * p.ldb;
       src[q] = wrow + 8 * swz_chunk<T::BK>(r, idx % T::CPR);
     } else {
-      const int j = instr - T::W_INSTR, pl = j / (T::A_INSTR / 2);
-      const int idx = (j % (T::A_INSTR / 2)) * 64 + lane, r = idx / T::CPR;
+      const int j = instr - T::W_INSTR, pl = j / (T::A_INSTR / T::AP);
+      const int idx = (j % (T::A_INSTR / T::AP)) * 64 + lane, r = idx / T::CPR;
       src[q] = A + pl * p.a_pst + (size_t)min(m0 + r, p.M - 1) * p.lda +
                8 * swz_chunk<T::BK>(r, idx % T::CPR);
     }
@@ -110,7 +111,7 @@ void gemm_dma_kernel(GemmParams p, int n_tiles_n, int n_tiles_m) {
   };
   struct Frag {
     u32x4 w[T::UN];
-    u32x4 a[2][T::UM];
+    u32x4 a[T::AP][T::UM];
   };
   auto read = [&](Frag& f, int s, int ks) __attribute__((always_inline)) {
     const uint16_t* st = smem + (s % T::NBUF) * T::STAGE;
@@ -119,7 +120,7 @@ void gemm_dma_kernel(GemmParams p, int n_tiles_n, int n_tiles_m) {
     for (int u = 0; u < T::UN; ++u)
       f.w[u] = *(const u32x4*)(st + swz_row<T::BK>(32 * (T::UN * wn + u) + lr, c));
 #pragma unroll
-    for (int pl = 0; pl < 2; ++pl)
+    for (int pl = 0; pl < T::AP; ++pl)
 #pragma unroll
       for (int v = 0; v < T::UM; ++v)
         f.a[pl][v] = *(const u32x4*)(st + T::BN * T::BK + pl * T::BM * T::BK +
@@ -144,7 +145,7 @@ void gemm_dma_kernel(GemmParams p, int n_tiles_n, int n_tiles_m) {
 #pragma unroll
       for (int u = 0; u < T::UN; ++u) {
         acc[u][v] = mfma32(f.w[u], f.a[0][v], acc[u][v]);
-        acc[u][v] = mfma32(f.w[u], f.a[1][v], acc[u][v]);
+        if constexpr (T::AP == 2) acc[u][v] = mfma32(f.w[u], f.a[1][v], acc[u][v]);
         if constexpr (INTER) {
           const int unit = (ks * T::UM + v) * T::UN + u;
 #pragma unroll
@@ -281,6 +282,8 @@ __global__ void splitk_reduce4(const float* __restrict__ part, int splits, int M
 
 typedef DmaTile<1, 1, 4> DmaM32;    // 128 x 32
 typedef DmaTile<2, 2, 2> DmaM128;   // 128 x 128
+typedef DmaTile<1, 1, 4, 64, 1> DmaM32Bf16;    // the same tiles for a bf16 activation
+typedef DmaTile<2, 2, 2, 64, 1> DmaM128Bf16;
 
 struct DmaPlan {
   int cfg;   // 0: DmaM32, 1: DmaM128
@@ -315,7 +318,7 @@ DmaPlan dma_plan(int M, int N, int K) {
 }
 
 bool dma_ok(const GemmArgs& a) {
-  return !a.b_f32 && (!a.B2 || (a.N1 > 0 && a.N1 < a.N)) && a.K % 64 == 0 && a.N % 4 == 0 && a.ldc % 4 == 0 && (!a.R || a.ldr % 4 == 0) &&
+  return !a.b_f32 && (a.a_planes == 1 || a.a_planes == 2) && (!a.B2 || (a.N1 > 0 && a.N1 < a.N)) && a.K % 64 == 0 && a.N % 4 == 0 && a.ldc % 4 == 0 && (!a.R || a.ldr % 4 == 0) &&
          a.lda % 8 == 0 && a.ldb % 8 == 0 && a.a_pst % 8 == 0;
 }
 
@@ -330,7 +333,8 @@ hipError_t launch_dma(const GemmParams& p, const DmaPlan& pl, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_dma_any(const GemmParams& p, const DmaPlan& pl, hipStream_t s) {
+hipError_t launch_dma_any(const GemmParams& p, const DmaPlan& pl, int a_planes, hipStream_t s) {
+  if (a_planes == 1) return pl.cfg == 0 ? launch_dma<DmaM32Bf16>(p, pl, s) : launch_dma<DmaM128Bf16>(p, pl, s);
   return pl.cfg == 0 ? launch_dma<DmaM32>(p, pl, s) : launch_dma<DmaM128>(p, pl, s);
 }
 
@@ -376,7 +380,7 @@ hipError_t gemm_deferred(const GemmArgs& a, float* ws, hipStream_t s, SplitOut* 
     const DmaPlan pl = dma_plan(a.M, a.N, a.K);
     p.splits = pl.splits;
     out->splits = pl.splits;
-    return launch_dma_any(p, pl, s);
+    return launch_dma_any(p, pl, a.a_planes, s);
   }
   dim3 grid((a.N + TilePlanesF32::BN - 1) / TilePlanesF32::BN,
             (a.M + TilePlanesF32::BM - 1) / TilePlanesF32::BM);
@@ -391,7 +395,7 @@ hipError_t gemm(const GemmArgs& a, float* ws, hipStream_t s) {
     if (!dma_ok(a)) return hipErrorInvalidValue;
     const DmaPlan pl = dma_plan(a.M, a.N, a.K);
     p.splits = pl.splits;
-    hipError_t e = launch_dma_any(p, pl, s);
+    hipError_t e = launch_dma_any(p, pl, a.a_planes, s);
     if (e != hipSuccess || pl.splits == 1) return e;
     const size_t total4 = (size_t)a.M * a.N / 4;
     const int blocks = (int)((total4 + 255) / 256 < 4096 ? (total4 + 255) / 256 : 4096);

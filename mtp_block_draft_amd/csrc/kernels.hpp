@@ -12,7 +12,8 @@ namespace dmtp {
 // ------------------------------------------------------------------ GEMM ----
 // C[M, N] (float32, ldc) = R[M, N] (optional, may alias C) + A[M, K] B[N, K]^T.
 // A is a float32 activation held as two bf16 planes (hi at A, lo at A + a_pst,
-// row stride lda); B is a weight stored [out, in], bf16 or float32.
+// row stride lda), or, with a_planes = 1 and a bf16 weight, a bf16 activation;
+// B is a weight stored [out, in], bf16 or float32.
 struct GemmArgs {
   const uint16_t* A;
   size_t a_pst;
@@ -31,6 +32,7 @@ struct GemmArgs {
   // (same ldb and dtype), so two projections of one input run as one GEMM.
   const void* B2 = nullptr;
   int N1 = 0;
+  int a_planes = 2;
 };
 
 // float32 workspace the GEMM launcher needs for its split-K partials.
