@@ -85,7 +85,8 @@ struct HeadParams {
   const int32_t* store_row;
   float* logits;
   int logits_rows;
-  void* prepared;        // [M, H] head input
+  void* prepared;        // head input: [M, H], or [H / a_sl][M][a_sl] when a_sl > 0
+  int a_sl;              // k-slice width of a slice-major prepared layout (0: row-major)
   const void* A;         // rows the GEMM reads: prepared, or the single input segment
   RowStat* part;         // [M, n_vtiles]
   int n_vtiles;
@@ -113,7 +114,12 @@ __global__ __launch_bounds__(kPrepThreads) void head_prep_kernel(HeadParams p) {
   }
   const Seg sg = p.seg[si];
   const int H = p.H;
-  const size_t orow = (size_t)blockIdx.x * H;
+  // element i of this row: row-major, or inside k-slice i / a_sl of a
+  // slice-major layout (a_sl a multiple of 4, so a group of four stays whole)
+  const size_t orow = p.a_sl ? (size_t)blockIdx.x * p.a_sl : (size_t)blockIdx.x * H;
+  auto oidx = [&](int i) -> size_t {
+    return p.a_sl ? (size_t)(i / p.a_sl) * p.M * p.a_sl + orow + (i % p.a_sl) : orow + i;
+  };
   if (sg.g && H % 4 == 0 && H <= 8 * 4 * kPrepThreads) {
     // the row and its gains in registers: every load issued before the first use
     const float* xr = (const float*)sg.x + (size_t)m * sg.ld;
@@ -142,10 +148,11 @@ __global__ __launch_bounds__(kPrepThreads) void head_prep_kernel(HeadParams p) {
     for (int k = 0; k < 8; ++k) {
       const int i = 4 * (threadIdx.x + kPrepThreads * k);
       if (i < H) {
-        store_elem(p.prepared, p.dtype, orow + i + 0, (float)((double)xv[k].x * inv * gv[k].x));
-        store_elem(p.prepared, p.dtype, orow + i + 1, (float)((double)xv[k].y * inv * gv[k].y));
-        store_elem(p.prepared, p.dtype, orow + i + 2, (float)((double)xv[k].z * inv * gv[k].z));
-        store_elem(p.prepared, p.dtype, orow + i + 3, (float)((double)xv[k].w * inv * gv[k].w));
+        const size_t o = oidx(i);
+        store_elem(p.prepared, p.dtype, o + 0, (float)((double)xv[k].x * inv * gv[k].x));
+        store_elem(p.prepared, p.dtype, o + 1, (float)((double)xv[k].y * inv * gv[k].y));
+        store_elem(p.prepared, p.dtype, o + 2, (float)((double)xv[k].z * inv * gv[k].z));
+        store_elem(p.prepared, p.dtype, o + 3, (float)((double)xv[k].w * inv * gv[k].w));
       }
     }
   } else if (sg.g) {
@@ -159,13 +166,13 @@ __global__ __launch_bounds__(kPrepThreads) void head_prep_kernel(HeadParams p) {
     for (int w = 0; w < kPrepThreads / kWave; ++w) t += red[w];
     const double inv = 1.0 / sqrt(t / H + (double)p.eps);
     for (int i = threadIdx.x; i < H; i += blockDim.x)
-      store_elem(p.prepared, p.dtype, orow + i, (float)((double)xr[i] * inv * sg.g[i]));
+      store_elem(p.prepared, p.dtype, oidx(i), (float)((double)xr[i] * inv * sg.g[i]));
   } else if (p.dtype == DMTP_BF16) {
     const uint16_t* xr = (const uint16_t*)sg.x + (size_t)m * sg.ld;
-    for (int i = threadIdx.x; i < H; i += blockDim.x) ((uint16_t*)p.prepared)[orow + i] = xr[i];
+    for (int i = threadIdx.x; i < H; i += blockDim.x) ((uint16_t*)p.prepared)[oidx(i)] = xr[i];
   } else {
     const float* xr = (const float*)sg.x + (size_t)m * sg.ld;
-    for (int i = threadIdx.x; i < H; i += blockDim.x) ((float*)p.prepared)[orow + i] = xr[i];
+    for (int i = threadIdx.x; i < H; i += blockDim.x) ((float*)p.prepared)[oidx(i)] = xr[i];
   }
 }
 
@@ -285,6 +292,9 @@ void head_gemm_mf32_kernel(HeadParams p, int n_mchunks) {
   const int H = p.H, V = p.V, M = p.M;
   const uint16_t* __restrict__ W = (const uint16_t*)p.W;
   const uint16_t* __restrict__ X = (const uint16_t*)p.A;
+  // input rows: row-major [M, H], or slice-major with k-slices of width BK
+  const size_t x_rs = p.a_sl ? (size_t)BK : (size_t)H;
+  const size_t x_ss = p.a_sl ? (size_t)M * BK : (size_t)BK;
 
   // Raw per-row inputs of the epilogue, loaded ahead of the main loop so that
   // their memory latency is spent under it rather than once per row group at
@@ -320,7 +330,7 @@ void head_gemm_mf32_kernel(HeadParams p, int n_mchunks) {
     } else {
       const int qq = q - C::WPW;
       const int idx = (wave * C::XPW + qq) * 64 + lane, r = idx / C::CPR;
-      src[q] = X + (size_t)min(m0 + r, M - 1) * H + 8 * swz_chunk<BK>(r, idx % C::CPR);
+      src[q] = X + (size_t)min(m0 + r, M - 1) * x_rs + 8 * swz_chunk<BK>(r, idx % C::CPR);
       dst[q] = C::BV * C::BK + (wave * C::XPW + qq) * 512;
     }
   }
@@ -331,7 +341,7 @@ void head_gemm_mf32_kernel(HeadParams p, int n_mchunks) {
     if (q < C::WPW)
       lds_dma16<2>(src[q] + slice * C::BK, smem + (slice % C::NBUF) * C::STAGE + dst[q]);
     else
-      lds_dma16(src[q] + slice * C::BK, smem + (slice % C::NBUF) * C::STAGE + dst[q]);
+      lds_dma16(src[q] + (size_t)slice * x_ss, smem + (slice % C::NBUF) * C::STAGE + dst[q]);
   };
   // fragments of one 16-wide k-step
   struct Frag {
@@ -547,11 +557,16 @@ hipError_t launch_head_mf32(const HeadParams& p, int n_mchunks, const GemmEvents
 // Row chunks of at most 448 rows, split evenly; TB = 64-row tiles per
 // workgroup.  One or two tiles (weight streaming): 64-wide slices, deep ring.
 // More: 32-wide slices, three stages, copies spread over the MFMAs.
+int head_mf32_tb(int M) {
+  const int nc = (M + 447) / 448;
+  return ((M + nc - 1) / nc + 63) / 64;
+}
+// k-slice width of the kernel launch_head_mf32_any picks for M rows
+int head_mf32_bk(int M) { return head_mf32_tb(M) <= 2 ? 64 : 32; }
+
 hipError_t launch_head_mf32_any(const HeadParams& p, const GemmEvents& ev, hipStream_t s) {
   const int nc = (p.M + 447) / 448;
-  const int rows = (p.M + nc - 1) / nc;
-  const int tb = (rows + 63) / 64;
-  switch (tb) {
+  switch (head_mf32_tb(p.M)) {
     case 1: return launch_head_mf32<1, 64>(p, nc, ev, s);
     case 2: return launch_head_mf32<2, 64>(p, nc, ev, s);
     case 3: return launch_head_mf32<3, 32, 3>(p, nc, ev, s);
@@ -808,15 +823,21 @@ hipError_t lm_head_run(const dmtp_head_desc& d, int M, void* ws, hipStream_t s) 
   p.lse = d.lse;
   p.gap = d.gap;
 
-  // a single segment of ready head-input rows is read in place
-  const bool direct = d.n_seg == 1 && !d.seg[0].g_norm && d.seg[0].ld == d.H && !d.prepared;
+  // The 32-wide-slice kernels read their input rows slice-major (each k-slice
+  // of all rows one contiguous block) unless the caller asked for the
+  // row-major prepared rows; otherwise a single segment of ready head-input
+  // rows is read in place.
+  const bool mf32 = d.dtype == DMTP_BF16 && d.H % 128 == 0;
+  p.a_sl = (mf32 && !d.prepared && head_mf32_bk(M) == 32) ? 32 : 0;
+  const bool direct =
+      !p.a_sl && d.n_seg == 1 && !d.seg[0].g_norm && d.seg[0].ld == d.H && !d.prepared;
   p.A = direct ? d.seg[0].x : p.prepared;
   hipError_t e = hipSuccess;
   if (!direct) {
     hipLaunchKernelGGL(head_prep_kernel, dim3(M), dim3(kPrepThreads), 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (d.dtype == DMTP_BF16 && d.H % 128 == 0) {
+  if (mf32) {
     GemmEvents ev;
     ev.start = (hipEvent_t)d.gemm_start_event;
     ev.stop = (hipEvent_t)d.gemm_stop_event;
