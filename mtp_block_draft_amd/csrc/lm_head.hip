@@ -12,6 +12,7 @@
 //   plan/scan (only when temperatures are given) Gumbel-max draws over the
 //             stored logits rows of sampled rows, in vocabulary chunks
 //   finalize  token per row: draw, planted row argmax, or argmax
+#include <algorithm>
 #include <type_traits>
 
 #include <hip/hip_ext.h>
@@ -577,6 +578,213 @@ hipError_t launch_head_mf32_any(const HeadParams& p, const GemmEvents& ev, hipSt
   }
 }
 
+// ---- bf16 head GEMM for calls of at most 32 input rows (weight streaming).
+//
+// Such a call is bound by one read of the [V, H] weight matrix, so the design
+// serves the read pattern.  Persistent workgroups (one per CU) take 32-row
+// vocabulary tiles in turn.  Stream wave w (of four) covers k-quarter w of
+// every tile through a ring of its own: stages of 32 rows x 128 k, each copy
+// instruction reading 256 contiguous bytes of four weight rows, so a tile's
+// 128 KB are read as four long runs.  The input rows' k-quarter stays in the
+// stream wave's registers for the whole kernel (no input copies at all).  A
+// fifth wave adds the four partial 32 x 32 tiles in wave order and computes
+// the row statistics, one partial per 32 vocabulary rows, while the stream
+// waves go on to the next tile.  Splitting k changes the float32 summation
+// order against the kernels above, which sum over k in one sequence: the two
+// agree to rounding, not bit for bit; each is batch invariant on its own.
+constexpr int kT1Stream = 4;                       // stream waves
+constexpr int kT1Threads = (kT1Stream + 1) * kWave;
+constexpr int kT1BK = 128;                         // stage width in k
+constexpr int kT1NB = 3;                           // stages per stream wave
+constexpr int kT1Stage = 32 * kT1BK;               // elements per stage
+constexpr int kT1Copies = kT1Stage * 2 / 1024;     // 1 KB copies per stage
+constexpr int kT1Red = kT1Stream * 16 * kWave;     // floats of one partial set
+constexpr size_t kT1Lds = (size_t)kT1Stream * kT1NB * kT1Stage * 2 + 2 * (size_t)kT1Red * 4;
+
+// Position of 16-byte chunk c of row r in a [32][128] stage (an involution):
+// the 16 lanes of one read pass land on the 16 positions of the bank window.
+__device__ __forceinline__ int t1_swz(int r, int c) { return c ^ (r & 15); }
+
+// Wait until this wave has at most N vector-memory operations outstanding,
+// leaving the LDS counter alone.
+template <int N>
+__device__ __forceinline__ void wait_vm_only() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <int KQ>   // 16-wide k-steps per quarter: H = 64 KQ
+__global__ __launch_bounds__(kT1Threads) void head_t1_kernel(HeadParams p, int n_tiles) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  constexpr int KPS = kT1BK / 16;                  // k-steps per stage
+  constexpr int SUB = KQ / KPS;                    // stages per tile and stream wave
+  static_assert(KQ % KPS == 0, "quarter");
+  static_assert(kT1Copies * (kT1NB - 2) < 64, "vmcnt");
+  float* red = (float*)(smem + kT1Stream * kT1NB * kT1Stage);   // [2][stream wave][16][64]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 31, lk = lane >> 5;
+  const int H = p.H, V = p.V, M = p.M;
+  const int G = gridDim.x;
+  const int my_tiles = (n_tiles - (int)blockIdx.x + G - 1) / G;   // blockIdx.x < n_tiles
+
+  if (wave < kT1Stream) {
+    const uint16_t* __restrict__ W = (const uint16_t*)p.W;
+    const uint16_t* __restrict__ X = (const uint16_t*)p.A;
+    const int kq0 = wave * KQ * 16;
+    // MFMA B operands of the quarter: input row lr (rows past M repeat row
+    // M - 1; their results are never written), k = kq0 + 16 j + 8 lk ..
+    u32x4 xf[KQ];
+    const uint16_t* xr = X + (size_t)min(lr, M - 1) * H + kq0 + 8 * lk;
+#pragma unroll
+    for (int j = 0; j < KQ; ++j) xf[j] = *(const u32x4*)(xr + 16 * j);
+    // these loads complete before the first copy is issued, so no later wait
+    // for them drains the ring
+    wait_vm_only<0>();
+    uint16_t* ring = smem + wave * kT1NB * kT1Stage;
+    const int nseq = my_tiles * SUB;
+    // stage q: tile blockIdx.x + (q / SUB) G, k from kq0 + 128 (q % SUB); copy i
+    // covers rows 4 i .. 4 i + 3 (lane / 16), chunk position lane % 16
+    auto issue = [&](int q) __attribute__((always_inline)) {
+      const int t = blockIdx.x + (q / SUB) * G;
+      const int k0 = kq0 + kT1BK * (q % SUB);
+      uint16_t* st = ring + (q % kT1NB) * kT1Stage;
+#pragma unroll
+      for (int i = 0; i < kT1Copies; ++i) {
+        const int r = 4 * i + (lane >> 4);
+        lds_dma16<2>(W + (size_t)min(32 * t + r, V - 1) * H + k0 + 8 * t1_swz(r, lane & 15), st + 512 * i);
+      }
+    };
+    for (int q = 0; q < kT1NB - 1 && q < nseq; ++q) issue(q);
+    for (int tile = 0; tile < my_tiles; ++tile) {
+      f32x16_t acc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+      for (int s = 0; s < SUB; ++s) {
+        const int q = tile * SUB + s;
+        // stage q has landed once only the copies of the stages issued after
+        // it may be outstanding; lgkmcnt(0) as well, since the stage refilled
+        // below was read just before
+        wait_vm_dyn<kT1Copies * (kT1NB - 2)>(kT1Copies * min(nseq - 1 - q, kT1NB - 2));
+        const uint16_t* st = ring + (q % kT1NB) * kT1Stage;
+        u32x4 wf[KPS];
+#pragma unroll
+        for (int j = 0; j < KPS; ++j) wf[j] = *(const u32x4*)(st + lr * kT1BK + 8 * t1_swz(lr, 2 * j + lk));
+#pragma unroll
+        for (int j = 0; j < KPS; ++j) acc = mfma32(wf[j], xf[s * KPS + j], acc);
+        if (q + kT1NB - 1 < nseq) issue(q + kT1NB - 1);
+      }
+      float* rb = red + (size_t)(tile & 1) * kT1Red + wave * 16 * kWave;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) rb[i * kWave + lane] = acc[i];
+      // the partials are in LDS before the barrier; the copies stay in flight
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0) only
+      ring_barrier();
+    }
+    return;
+  }
+
+  // statistics wave: lane (lr, lk) holds input row lr and the 16 vocabulary
+  // rows 32 t + 8 (i / 4) + 4 lk + (i % 4), i = 0 .. 15, of tile t
+  const bool ok = lr < M;
+  const float tin = (ok && p.temperature) ? p.temperature[lr] : 1.f;
+  const int sin = (ok && p.store_row) ? p.store_row[lr] : -1;
+  const float it = tin > 0.f ? 1.f / tin : 1.f;
+  const int srow = sin < p.logits_rows ? sin : -1;
+  const float sc = it * 1.4426950408889634f;
+  auto off = [](int i) { return 8 * (i >> 2) + (i & 3); };
+  for (int tile = 0; tile < my_tiles; ++tile) {
+    ring_barrier();
+    const int t = blockIdx.x + tile * G;
+    const int vl = 32 * t + 4 * lk;
+    const float* rb = red + (size_t)(tile & 1) * kT1Red + lane;
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float v = rb[i * kWave];
+#pragma unroll
+      for (int w = 1; w < kT1Stream; ++w) v += rb[(w * 16 + i) * kWave];
+      x[i] = vl + off(i) < V ? v : -INFINITY;
+    }
+    float h[8], l[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      h[j] = hw_max(x[2 * j], x[2 * j + 1]);
+      l[j] = hw_min(x[2 * j], x[2 * j + 1]);
+    }
+#pragma unroll
+    for (int w = 8; w > 1; w >>= 1)
+#pragma unroll
+      for (int j = 0; j < w / 2; ++j) {
+        const float hh = hw_max(h[2 * j], h[2 * j + 1]);
+        l[j] = hw_max3(hw_min(h[2 * j], h[2 * j + 1]), l[2 * j], l[2 * j + 1]);
+        h[j] = hh;
+      }
+    const float v1 = h[0], v2 = l[0];
+    int e1 = 15;
+#pragma unroll
+    for (int e = 14; e >= 0; --e) e1 = x[e] == v1 ? e : e1;
+    const float bias = -v1 * sc;
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) ps[e & 3] += hw_exp2(fmaf(x[e], sc, bias));
+    float sum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    int i1 = vl + off(e1);
+    if (!(v1 > -INFINITY)) {   // lane wholly past V
+      sum = 0.f;
+      i1 = 0x7FFFFFFF;
+    }
+    if (srow >= 0) {
+      float* dst = p.logits + (size_t)srow * V + vl;
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (vl + off(e) < V) dst[off(e)] = x[e];
+    }
+    RowStat st{v1, sum, i1, v2};
+    RowStat o;
+    o.m = shfl_xor(st.m, 32);
+    o.s = shfl_xor(st.s, 32);
+    o.idx = shfl_xor(st.idx, 32);
+    o.v2 = shfl_xor(st.v2, 32);
+    st = stat_merge(st, o, it);
+    if (lk == 0 && ok) p.part[(size_t)lr * p.n_vtiles + t] = st;
+  }
+}
+
+// The weight-streaming kernel serves bf16 calls of at most 32 rows whose
+// k-quarter fits the stream waves' registers (H = 512 .. 2048, a multiple of 512).
+bool head_t1_fits(const dmtp_head_desc& d, int M) {
+  return d.dtype == DMTP_BF16 && M <= 32 && d.H % 512 == 0 && d.H <= 2048;
+}
+
+template <int KQ>
+hipError_t launch_head_t1_kq(const HeadParams& p, int grid, const GemmEvents& ev, hipStream_t s) {
+  static_assert(kT1Lds <= 160 * 1024, "head LDS");
+  hipError_t e = hipFuncSetAttribute((const void*)head_t1_kernel<KQ>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kT1Lds);
+  if (e != hipSuccess) return e;
+  if (ev.start && ev.stop)
+    hipExtLaunchKernelGGL((head_t1_kernel<KQ>), dim3(grid), dim3(kT1Threads), (uint32_t)kT1Lds, s, ev.start,
+                          ev.stop, 0u, p, p.n_vtiles);
+  else
+    hipLaunchKernelGGL((head_t1_kernel<KQ>), dim3(grid), dim3(kT1Threads), kT1Lds, s, p, p.n_vtiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_head_t1(const HeadParams& p, const GemmEvents& ev, hipStream_t s) {
+  int dev = 0, n_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int grid = std::min(p.n_vtiles, std::max(n_cu, 1));
+  switch (p.H / 64) {
+    case 8: return launch_head_t1_kq<8>(p, grid, ev, s);
+    case 16: return launch_head_t1_kq<16>(p, grid, ev, s);
+    case 24: return launch_head_t1_kq<24>(p, grid, ev, s);
+    default: return launch_head_t1_kq<32>(p, grid, ev, s);
+  }
+}
+
 constexpr int kMergeThreads = 256;
 
 __global__ __launch_bounds__(kMergeThreads) void head_merge_kernel(HeadParams p, int final_greedy) {
@@ -762,7 +970,10 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 WsLayout ws_layout(const dmtp_head_desc& d, int M) {
   WsLayout w;
-  w.n_vtiles = (d.dtype == DMTP_BF16 && d.H % 128 == 0) ? (d.V + 127) / 128 : (d.V + 63) / 64;
+  // partials per row: one per 32 (streaming kernel), 128 (MFMA kernel) or 64 vocabulary rows
+  w.n_vtiles = head_t1_fits(d, M)                        ? (d.V + 31) / 32
+               : (d.dtype == DMTP_BF16 && d.H % 128 == 0) ? (d.V + 127) / 128
+                                                          : (d.V + 63) / 64;
   w.n_chunks = (d.V + kScanChunk - 1) / kScanChunk;
   const size_t esz = d.dtype == DMTP_BF16 ? 2 : 4;
   size_t o = 0;
@@ -841,7 +1052,7 @@ hipError_t lm_head_run(const dmtp_head_desc& d, int M, void* ws, hipStream_t s) 
     GemmEvents ev;
     ev.start = (hipEvent_t)d.gemm_start_event;
     ev.stop = (hipEvent_t)d.gemm_stop_event;
-    e = launch_head_mf32_any(p, ev, s);
+    e = head_t1_fits(d, M) ? launch_head_t1(p, ev, s) : launch_head_mf32_any(p, ev, s);
     if (e != hipSuccess) return e;
   } else if (d.dtype == DMTP_BF16) {
     dim3 grid(w.n_vtiles, (M + HeadTileBF16::BM - 1) / HeadTileBF16::BM);

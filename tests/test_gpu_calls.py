@@ -193,26 +193,85 @@ def test_lm_head_many_rows(dm, M):
 
 
 def test_lm_head_rows_do_not_depend_on_the_batch(dm):
-    # 448 rows run 7 tiles per workgroup; 1, 200 and 385 rows take other tile
-    # counts and slice widths, which must not change any row's result
+    # Calls of 33 rows and more: 448 rows run 7 tiles per workgroup; 200 and
+    # 385 rows take other tile counts and slice widths, which must not change
+    # any row's result.  Calls of at most 32 rows take the weight-streaming
+    # kernel, bit for bit the same among themselves; its k-split sums in
+    # another order, so against the larger calls the rows agree to rounding.
     H, V = 2048, 20000
     W, hid, g, rows, strided, x = _head_case(21, H, V, "bf16", M_norm=0, M_rows=448, M_strided=0)
     Wt = _t(W, torch.bfloat16)
     X = _t(rows, torch.bfloat16)
     outs = {}
-    for name, sl in (("all", slice(0, 448)), ("one", slice(37, 38)), ("tail", slice(63, 448)),
-                     ("mid", slice(100, 300))):
+    for name, sl in (("all", slice(0, 448)), ("tail", slice(63, 448)), ("mid", slice(100, 300)),
+                     ("one", slice(37, 38)), ("s20", slice(30, 50)), ("s32", slice(37, 69))):
         xs = X[sl].contiguous()
         n = xs.shape[0]
         tok = torch.empty(n, dtype=torch.int32, device="cuda")
         lse = torch.empty(n, dtype=torch.float32, device="cuda")
-        dm.lm_head(Wt, [dm.head_segment(xs)], tok, lse=lse)
-        outs[name] = (tok.cpu().numpy(), lse.cpu().numpy())
-    assert outs["one"][0][0] == outs["all"][0][37] and outs["one"][1][0] == outs["all"][1][37]
-    np.testing.assert_array_equal(outs["tail"][1], outs["all"][1][63:])
-    np.testing.assert_array_equal(outs["tail"][0], outs["all"][0][63:])
-    np.testing.assert_array_equal(outs["mid"][1], outs["all"][1][100:300])
-    np.testing.assert_array_equal(outs["mid"][0], outs["all"][0][100:300])
+        gap = torch.empty(n, dtype=torch.float32, device="cuda")
+        dm.lm_head(Wt, [dm.head_segment(xs)], tok, lse=lse, gap=gap)
+        outs[name] = (tok.cpu().numpy(), lse.cpu().numpy(), gap.cpu().numpy())
+    for j in (0, 1):
+        np.testing.assert_array_equal(outs["tail"][j], outs["all"][j][63:])
+        np.testing.assert_array_equal(outs["mid"][j], outs["all"][j][100:300])
+        np.testing.assert_array_equal(outs["one"][j], outs["s32"][j][:1])
+        np.testing.assert_array_equal(outs["s20"][j][7:], outs["s32"][j][:13])
+    tok_s, lse_s, _ = outs["s32"]
+    tok_a, lse_a, gap_a = (v[37:69] for v in outs["all"])
+    assert max_rel(lse_s, lse_a) < 1e-6
+    assert all(tok_s[i] == tok_a[i] or gap_a[i] < 1e-4 for i in range(32))
+
+
+@pytest.mark.parametrize("H", [512, 1024, 1536, 2048])
+@pytest.mark.parametrize("M", [1, 9, 32])
+def test_lm_head_at_most_32_rows(dm, H, M):
+    # the weight-streaming kernel: normed, plain and strided segments, greedy,
+    # sampled, planted and no-draw rows, stored logits, a ragged last
+    # vocabulary tile (8191 = 255 * 32 + 31)
+    V = 8191
+    print(f"lm_head streaming H={H} M={M}", flush=True)
+    n_norm, n_rows = (M + 2) // 3, M // 3
+    W, hid, g, rows, strided, x = _head_case(7 * H + M, H, V, "bf16", M_norm=n_norm,
+                                             M_rows=n_rows, M_strided=M - n_norm - n_rows)
+    r = np.random.default_rng(H + M)
+    tau = np.where(r.random(M) < 0.5, r.choice([1.0, 0.7], size=M), 0.0).astype(np.float32)
+    keys = (np.arange(M, dtype=np.uint64) * np.uint64(131) + np.uint64(9)).astype(np.uint64)
+    if M > 2:
+        keys[2] = np.uint64(0xFFFFFFFFFFFFFFFF)
+    plant = np.full(M, -1, np.int32)
+    if M > 4:
+        plant[4] = 0
+    store = np.arange(M, dtype=np.int32)[::-1].copy()
+    segs = [dm.head_segment(_t(hid, torch.float32), _t(g, torch.float32)),
+            dm.head_segment(_t(rows, torch.bfloat16)),
+            dm.head_segment(_t(strided, torch.bfloat16), n=strided.shape[0], ld=2 * H)]
+    segs = [sg for sg, n in zip(segs, (n_norm, n_rows, M - n_norm - n_rows)) if n > 0]
+    tok = torch.empty(M, dtype=torch.int32, device="cuda")
+    lse = torch.empty(M, dtype=torch.float32, device="cuda")
+    rmax = torch.empty(M, dtype=torch.float32, device="cuda")
+    logits = torch.full((M, V), float("nan"), dtype=torch.float32, device="cuda")
+    seed = 0xDEC0DE
+    dm.lm_head(_t(W, torch.bfloat16), segs, tok, eps=1e-6, temperature=_t(tau, torch.float32),
+               draw_key=_t(keys.view(np.int64), torch.int64), seed=seed,
+               plant_row=_t(plant, torch.int32), store_row=_t(store, torch.int32), logits=logits,
+               lse=lse, row_max=rmax)
+    ref_logits = x @ W.astype(np.float64).T
+    assert max_rel(logits.cpu().numpy()[store], ref_logits) < 2e-3
+    t = np.where(tau > 0, tau, 1.0)
+    assert max_rel(lse.cpu().numpy(), onm.logsumexp(ref_logits / t[:, None])) < 1e-5
+    assert max_rel(rmax.cpu().numpy(), ref_logits.max(axis=1)) < 1e-4
+    got = tok.cpu().numpy()
+    for m in range(M):
+        if plant[m] >= 0:
+            src = plant[m]
+            want, margin = int(np.argmax(ref_logits[src])), float(onm.top2_gap(ref_logits[src]))
+        elif tau[m] > 0 and keys[m] != np.uint64(0xFFFFFFFFFFFFFFFF):
+            want, margin = oph.gumbel_argmax(ref_logits[m] / tau[m], seed, int(keys[m]))
+        else:
+            want, margin = int(np.argmax(ref_logits[m])), float(onm.top2_gap(ref_logits[m]))
+        if got[m] != want:
+            assert margin < NEAR_TIE, (m, got[m], want, margin)
 
 
 # ---------------------------------------------------------------- block draft
