@@ -581,15 +581,15 @@ hipError_t launch_head_mf32_any(const HeadParams& p, const GemmEvents& ev, hipSt
 // ---- bf16 head GEMM for calls of at most 32 input rows (weight streaming).
 //
 // Such a call is bound by one read of the [V, H] weight matrix, so the design
-// serves the read pattern.  Persistent workgroups (one per CU) take 32-row
-// vocabulary tiles in turn.  Stream wave w (of four) covers k-quarter w of
+// serves the read pattern.  Persistent workgroups (one per CU) each take a
+// contiguous run of 32-row vocabulary tiles.  Stream wave w (of four) covers k-quarter w of
 // every tile through a ring of its own: stages of 32 rows x 128 k, each copy
 // instruction reading 256 contiguous bytes of four weight rows, so a tile's
 // 128 KB are read as four long runs.  The input rows' k-quarter stays in the
 // stream wave's registers for the whole kernel (no input copies at all).  A
-// fifth wave adds the four partial 32 x 32 tiles in wave order and computes
-// the row statistics, one partial per 32 vocabulary rows, while the stream
-// waves go on to the next tile.  Splitting k changes the float32 summation
+// fifth wave adds the four partial 32 x 32 tiles in wave order and folds
+// each tile's row statistics into one partial per row and workgroup, in tile
+// order, while the stream waves go on to the next tile.  Splitting k changes the float32 summation
 // order against the kernels above, which sum over k in one sequence: the two
 // agree to rounding, not bit for bit; each is batch invariant on its own.
 constexpr int kT1Stream = 4;                       // stream waves
@@ -599,6 +599,7 @@ constexpr int kT1NB = 3;                           // stages per stream wave
 constexpr int kT1Stage = 32 * kT1BK;               // elements per stage
 constexpr int kT1Copies = kT1Stage * 2 / 1024;     // 1 KB copies per stage
 constexpr int kT1Red = kT1Stream * 16 * kWave;     // floats of one partial set
+constexpr int kT1Grid = 256;                       // workgroups (at most; one per CU)
 constexpr size_t kT1Lds = (size_t)kT1Stream * kT1NB * kT1Stage * 2 + 2 * (size_t)kT1Red * 4;
 
 // Position of 16-byte chunk c of row r in a [32][128] stage (an involution):
@@ -624,8 +625,11 @@ __global__ __launch_bounds__(kT1Threads) void head_t1_kernel(HeadParams p, int n
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 31, lk = lane >> 5;
   const int H = p.H, V = p.V, M = p.M;
-  const int G = gridDim.x;
-  const int my_tiles = (n_tiles - (int)blockIdx.x + G - 1) / G;   // blockIdx.x < n_tiles
+  // tiles t0 .. t0 + my_tiles - 1: n_tiles split into gridDim.x runs whose
+  // lengths differ by at most one (gridDim.x <= n_tiles, so none is empty)
+  const int G = gridDim.x, b = blockIdx.x;
+  const int my_tiles = n_tiles / G + (b < n_tiles % G ? 1 : 0);
+  const int t0 = b * (n_tiles / G) + min(b, n_tiles % G);
 
   if (wave < kT1Stream) {
     const uint16_t* __restrict__ W = (const uint16_t*)p.W;
@@ -642,10 +646,10 @@ __global__ __launch_bounds__(kT1Threads) void head_t1_kernel(HeadParams p, int n
     wait_vm_only<0>();
     uint16_t* ring = smem + wave * kT1NB * kT1Stage;
     const int nseq = my_tiles * SUB;
-    // stage q: tile blockIdx.x + (q / SUB) G, k from kq0 + 128 (q % SUB); copy i
-    // covers rows 4 i .. 4 i + 3 (lane / 16), chunk position lane % 16
+    // stage q: tile t0 + q / SUB, k from kq0 + 128 (q % SUB); copy i covers
+    // rows 4 i .. 4 i + 3 (lane / 16), chunk position lane % 16
     auto issue = [&](int q) __attribute__((always_inline)) {
-      const int t = blockIdx.x + (q / SUB) * G;
+      const int t = t0 + q / SUB;
       const int k0 = kq0 + kT1BK * (q % SUB);
       uint16_t* st = ring + (q % kT1NB) * kT1Stage;
 #pragma unroll
@@ -693,9 +697,10 @@ __global__ __launch_bounds__(kT1Threads) void head_t1_kernel(HeadParams p, int n
   const int srow = sin < p.logits_rows ? sin : -1;
   const float sc = it * 1.4426950408889634f;
   auto off = [](int i) { return 8 * (i >> 2) + (i & 3); };
+  RowStat run = stat_empty();   // the row's statistics over this workgroup's tiles so far
   for (int tile = 0; tile < my_tiles; ++tile) {
     ring_barrier();
-    const int t = blockIdx.x + tile * G;
+    const int t = t0 + tile;
     const int vl = 32 * t + 4 * lk;
     const float* rb = red + (size_t)(tile & 1) * kT1Red + lane;
     float x[16];
@@ -746,9 +751,9 @@ __global__ __launch_bounds__(kT1Threads) void head_t1_kernel(HeadParams p, int n
     o.s = shfl_xor(st.s, 32);
     o.idx = shfl_xor(st.idx, 32);
     o.v2 = shfl_xor(st.v2, 32);
-    st = stat_merge(st, o, it);
-    if (lk == 0 && ok) p.part[(size_t)lr * p.n_vtiles + t] = st;
+    run = stat_merge(run, stat_merge(st, o, it), it);
   }
+  if (lk == 0 && ok) p.part[(size_t)lr * p.n_vtiles + b] = run;
 }
 
 // The weight-streaming kernel serves bf16 calls of at most 32 rows whose
@@ -758,30 +763,30 @@ bool head_t1_fits(const dmtp_head_desc& d, int M) {
 }
 
 template <int KQ>
-hipError_t launch_head_t1_kq(const HeadParams& p, int grid, const GemmEvents& ev, hipStream_t s) {
+hipError_t launch_head_t1_kq(const HeadParams& p, int n_tiles, const GemmEvents& ev, hipStream_t s) {
   static_assert(kT1Lds <= 160 * 1024, "head LDS");
   hipError_t e = hipFuncSetAttribute((const void*)head_t1_kernel<KQ>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kT1Lds);
   if (e != hipSuccess) return e;
+  // one workgroup per partial (p.n_vtiles of them)
   if (ev.start && ev.stop)
-    hipExtLaunchKernelGGL((head_t1_kernel<KQ>), dim3(grid), dim3(kT1Threads), (uint32_t)kT1Lds, s, ev.start,
-                          ev.stop, 0u, p, p.n_vtiles);
+    hipExtLaunchKernelGGL((head_t1_kernel<KQ>), dim3(p.n_vtiles), dim3(kT1Threads), (uint32_t)kT1Lds, s,
+                          ev.start, ev.stop, 0u, p, n_tiles);
   else
-    hipLaunchKernelGGL((head_t1_kernel<KQ>), dim3(grid), dim3(kT1Threads), kT1Lds, s, p, p.n_vtiles);
+    hipLaunchKernelGGL((head_t1_kernel<KQ>), dim3(p.n_vtiles), dim3(kT1Threads), kT1Lds, s, p, n_tiles);
   return hipGetLastError();
 }
 
+// partials per row of the streaming kernel: one per workgroup
+int head_t1_grid(int V) { return std::min((V + 31) / 32, kT1Grid); }
+
 hipError_t launch_head_t1(const HeadParams& p, const GemmEvents& ev, hipStream_t s) {
-  int dev = 0, n_cu = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return e;
-  const int grid = std::min(p.n_vtiles, std::max(n_cu, 1));
+  const int n_tiles = (p.V + 31) / 32;
   switch (p.H / 64) {
-    case 8: return launch_head_t1_kq<8>(p, grid, ev, s);
-    case 16: return launch_head_t1_kq<16>(p, grid, ev, s);
-    case 24: return launch_head_t1_kq<24>(p, grid, ev, s);
-    default: return launch_head_t1_kq<32>(p, grid, ev, s);
+    case 8: return launch_head_t1_kq<8>(p, n_tiles, ev, s);
+    case 16: return launch_head_t1_kq<16>(p, n_tiles, ev, s);
+    case 24: return launch_head_t1_kq<24>(p, n_tiles, ev, s);
+    default: return launch_head_t1_kq<32>(p, n_tiles, ev, s);
   }
 }
 
@@ -970,8 +975,9 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 WsLayout ws_layout(const dmtp_head_desc& d, int M) {
   WsLayout w;
-  // partials per row: one per 32 (streaming kernel), 128 (MFMA kernel) or 64 vocabulary rows
-  w.n_vtiles = head_t1_fits(d, M)                        ? (d.V + 31) / 32
+  // partials per row: one per workgroup (streaming kernel), per 128 (MFMA
+  // kernel) or per 64 vocabulary rows
+  w.n_vtiles = head_t1_fits(d, M)                        ? head_t1_grid(d.V)
                : (d.dtype == DMTP_BF16 && d.H % 128 == 0) ? (d.V + 127) / 128
                                                           : (d.V + 63) / 64;
   w.n_chunks = (d.V + kScanChunk - 1) / kScanChunk;
