@@ -444,13 +444,9 @@ int dmtp_block_draft(const dmtp_draft_desc* d, void* ws, size_t ws_bytes, hipStr
   char* b = (char*)ws;
   float* X = (float*)(b + w.X);
   uint16_t* xh = (uint16_t*)(b + w.xh);
-  const int R = d->B * st.S;
-  hipError_t h = build_slots(*d, X, stream);
-  // RMSNorm of the slots for the first layer; later layers get theirs from the
-  // previous layer's residual update
-  if (h == hipSuccess)
-    h = residual_rmsnorm(split_out_plain(X, (size_t)d->H, R, d->H), X, (size_t)d->H, 0,
-                         d->layers[0].g_attn, d->eps, xh, R, d->H, stream);
+  // the slots and their RMSNorm for the first layer; later layers get theirs
+  // from the previous layer's residual update
+  hipError_t h = build_slots(*d, X, d->layers[0].g_attn, xh, stream);
   SplitOut last{};
   if (h == hipSuccess) h = run_stack(st, w, b, nullptr, nullptr, &last, stream);
   if (h == hipSuccess)

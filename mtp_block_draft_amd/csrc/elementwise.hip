@@ -270,21 +270,44 @@ __global__ __launch_bounds__(kRowThreads) void fuse_prep_kernel(RowSrc x1, RowSr
   }
 }
 
-__global__ void build_slots_kernel(const int32_t* __restrict__ anchor, const float* __restrict__ x_t1,
-                                   const void* __restrict__ emb, int dtype, int mask_id, int V, int S,
-                                   int n_anchor, int H, float* __restrict__ X) {
-  const int b = blockIdx.x / S, s = blockIdx.x % S;
-  float* xr = X + (size_t)blockIdx.x * H;
-  if (s == n_anchor - 1) {
-    const float* src = x_t1 + (size_t)b * H;
-    for (int i = 4 * threadIdx.x; i < H; i += 4 * blockDim.x)
-      *(float4*)(xr + i) = *(const float4*)(src + i);
-    return;
-  }
+// Draft slot rows X [B * S, H] (float32): slot n_anchor - 1 is x_t1[b], slot
+// 0 of a dual-anchor block the anchor's embedding, every other slot the MASK
+// embedding (zeros for an id outside the table); and, as residual_rmsnorm_kernel
+// computes it from X, their RMSNorm with gains g as bf16 planes y [2][rows][H].
+template <int V4>
+__global__ __launch_bounds__(kRowThreads) void build_slots_kernel(
+    const int32_t* __restrict__ anchor, const float* __restrict__ x_t1, const void* __restrict__ emb,
+    int dtype, int mask_id, int V, int S, int n_anchor, int H, float* __restrict__ X,
+    const float* __restrict__ g, float eps, uint16_t* __restrict__ y, size_t pst) {
+  __shared__ double red[kRowThreads / kWave];
+  const int m = blockIdx.x, b = m / S, s = m % S;
+  const bool from_t1 = s == n_anchor - 1;
   const int tok = (n_anchor == 2 && s == 0) ? anchor[b] : mask_id;
   const bool ok = tok >= 0 && tok < V;
-  for (int i = 4 * threadIdx.x; i < H; i += 4 * blockDim.x)
-    *(float4*)(xr + i) = ok ? load4(emb, dtype, (size_t)tok * H + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 v[V4], gv[V4];
+#pragma unroll
+  for (int k = 0; k < V4; ++k) {
+    const int n = 4 * (threadIdx.x + kRowThreads * k);
+    if (n < H) {
+      v[k] = from_t1 ? *(const float4*)(x_t1 + (size_t)b * H + n)
+                     : (ok ? load4(emb, dtype, (size_t)tok * H + n) : make_float4(0.f, 0.f, 0.f, 0.f));
+      gv[k] = *(const float4*)(g + n);
+    }
+  }
+  double ss = 0.0;
+#pragma unroll
+  for (int k = 0; k < V4; ++k)
+    if (4 * (threadIdx.x + kRowThreads * k) < H) ss += sumsq4(v[k]);
+  ss = block_sum(ss, red);
+  const double inv = 1.0 / sqrt(ss / H + (double)eps);
+#pragma unroll
+  for (int k = 0; k < V4; ++k) {
+    const int n = 4 * (threadIdx.x + kRowThreads * k);
+    if (n < H) {
+      *(float4*)(X + (size_t)m * H + n) = v[k];
+      store_norm4(y, pst, (size_t)m * H + n, v[k], inv, gv[k]);
+    }
+  }
 }
 
 // q/k/v split of the QKV projection with the rotary embedding at the slot's
@@ -492,10 +515,20 @@ hipError_t fuse_prep(const dmtp_fuse_desc& d, uint16_t* cat, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t build_slots(const dmtp_draft_desc& d, float* X, hipStream_t s) {
+hipError_t build_slots(const dmtp_draft_desc& d, float* X, const float* g, uint16_t* y, hipStream_t s) {
   const int S = d.K - 1 + d.n_anchor;
-  hipLaunchKernelGGL(build_slots_kernel, dim3(d.B * S), dim3(256), 0, s, d.anchor_ids, d.x_t1,
-                     d.emb, d.dtype, d.mask_id, d.V, S, d.n_anchor, d.H, X);
+  const int rows = d.B * S;
+  const size_t pst = (size_t)rows * d.H;
+  switch (v4_of(d.H)) {
+#define DMTP_CASE(n)                                                                               \
+  case n:                                                                                          \
+    hipLaunchKernelGGL(build_slots_kernel<n>, dim3(rows), dim3(kRowThreads), 0, s, d.anchor_ids,    \
+                       d.x_t1, d.emb, d.dtype, d.mask_id, d.V, S, d.n_anchor, d.H, X, g, d.eps, y, \
+                       pst);                                                                       \
+    break;
+    DMTP_CASE(1) DMTP_CASE(2) DMTP_CASE(4) DMTP_CASE(8) DMTP_CASE(16)
+#undef DMTP_CASE
+  }
   return hipGetLastError();
 }
 

@@ -64,8 +64,9 @@ hipError_t residual_rmsnorm(const SplitOut& x, float* X, size_t ldx, int write_x
 // planes [2][rows][2H], and out[r] = res[r] (float32) when res is present.
 hipError_t fuse_prep(const dmtp_fuse_desc& d, uint16_t* cat, hipStream_t s);
 
-// Draft slots X [B * S, H] float32 from anchor ids, x_t1 rows and the MASK row.
-hipError_t build_slots(const dmtp_draft_desc& d, float* X, hipStream_t s);
+// Draft slots X [B * S, H] float32 from anchor ids, x_t1 rows and the MASK row,
+// and y [2][B * S][H] = their RMSNorm with gains g as bf16 planes.
+hipError_t build_slots(const dmtp_draft_desc& d, float* X, const float* g, uint16_t* y, hipStream_t s);
 
 // q/k/v split of the QKV projection with the rotary embedding at slot
 // positions: q [B, Hkv, S * G, d], kb and vb [B, Hkv, S, d] (float32).
