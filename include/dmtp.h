@@ -254,7 +254,13 @@ int dmtp_ctx_kv(const dmtp_ctx_desc* d, void* ws, size_t ws_bytes, hipStream_t s
  * the kernels: an out-of-range embedding id reads a zero row, an
  * out-of-range store or plant index is ignored, so bad data never leads to
  * an out-of-bounds access.
- * Results do not depend on M or on the other rows (row-wise arithmetic). */
+ * A row's results do not depend on the other rows.  With bf16, H a multiple
+ * of 512 and at most 2048, a call of at most 32 rows streams the weights with
+ * H split into four quarters whose partial sums are added in order, while
+ * larger calls sum over H in one sequence: a row's logit statistics then
+ * agree between the two to float32 rounding, and tokens agree unless the
+ * top-2 gap is within that rounding.  Within either case they do not depend
+ * on M. */
 typedef struct {
   const void* x;          /* [n, ld] rows */
   int32_t n;              /* rows in this segment (may be 0) */
