@@ -338,6 +338,152 @@ hipError_t launch_dma_any(const GemmParams& p, const DmaPlan& pl, int a_planes, 
   return pl.cfg == 0 ? launch_dma<DmaM32>(p, pl, s) : launch_dma<DmaM128>(p, pl, s);
 }
 
+// ------------------------------------- at most 32 rows: weight streaming ----
+// The fusion projections and the MTP block's projections multiply at most 32
+// activation rows by a weight matrix that is read once: the call is a weight
+// stream.  K is split into 512-wide ranges.  Persistent workgroups (at most
+// kSkGrid, about equally many per range) each keep one range of the
+// activation planes in registers -- stream wave w of four holds k 128 w ..
+// 128 w + 127 of the range -- and take a contiguous run of 32-row weight tiles
+// (32 output columns each).  A stream wave copies its 32 x 128 piece of every
+// tile through a three-stage LDS ring of its own, four weight rows x 256
+// contiguous bytes per copy, and accumulates the planes in turn.  A fifth
+// wave adds the four partial tiles in wave order and stores the range's sum
+// as split z of the [splits][M][N] partials, which the readers of a split-K
+// result add in split order.
+constexpr int kSkStream = 4;
+constexpr int kSkThreads = (kSkStream + 1) * kWave;
+constexpr int kSkBK = 128;                       // k per stream wave and tile
+constexpr int kSkRange = kSkStream * kSkBK;      // k per split
+constexpr int kSkNB = 3;                         // ring stages per stream wave
+constexpr int kSkStage = 32 * kSkBK;             // bf16 elements per stage
+constexpr int kSkCopies = kSkStage * 2 / 1024;   // 1 KB copies per stage
+constexpr int kSkRed = kSkStream * 16 * kWave;   // floats of one set of partial tiles
+constexpr size_t kSkLds = (size_t)kSkStream * kSkNB * kSkStage * 2 + 2 * (size_t)kSkRed * 4;
+constexpr int kSkGrid = 256;
+
+// Position of 16-byte chunk c of row r in a [32][128] stage (an involution):
+// the 16 lanes of one read pass land on the 16 positions of the bank window.
+__device__ __forceinline__ int sk_swz(int r, int c) { return c ^ (r & 15); }
+
+// blockIdx.x = z per_split + j: split z, run j of the n_tiles weight tiles.
+template <int AP>
+__global__ __launch_bounds__(kSkThreads) void gemm_skinny_kernel(GemmParams p, int n_tiles, int per_split) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  static_assert(kSkCopies * (kSkNB - 2) < 64, "vmcnt");
+  constexpr int KPS = kSkBK / 16;                // k-steps per stage
+  float* red = (float*)(smem + kSkStream * kSkNB * kSkStage);   // [2][stream wave][16][64]
+  const int z = blockIdx.x / per_split, j = blockIdx.x % per_split;
+  const int my = n_tiles / per_split + (j < n_tiles % per_split ? 1 : 0);
+  const int t0 = j * (n_tiles / per_split) + min(j, n_tiles % per_split);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 31, lk = lane >> 5;
+  const int M = p.M, N = p.N;
+  if (my == 0) return;   // the whole workgroup, before any barrier
+
+  if (wave < kSkStream) {
+    const uint16_t* __restrict__ W = (const uint16_t*)p.B;
+    const uint16_t* __restrict__ W2 = (const uint16_t*)p.B2;
+    const uint16_t* __restrict__ A = (const uint16_t*)p.A;
+    const int k0 = z * kSkRange + wave * kSkBK;
+    // MFMA B operands of the range: activation row lr (rows past M repeat row
+    // M - 1; their results are never stored), k = k0 + 16 j + 8 lk ..
+    u32x4 xf[AP][KPS];
+    const uint16_t* xr = A + (size_t)min(lr, M - 1) * p.lda + k0 + 8 * lk;
+#pragma unroll
+    for (int pl = 0; pl < AP; ++pl)
+#pragma unroll
+      for (int jj = 0; jj < KPS; ++jj) xf[pl][jj] = *(const u32x4*)(xr + pl * p.a_pst + 16 * jj);
+    // complete before the first copy, so no later wait for them drains the ring
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+    uint16_t* ring = smem + wave * kSkNB * kSkStage;
+    // tile q of the run: weight rows 32 (t0 + q) .. + 31; copy i covers rows
+    // 4 i .. 4 i + 3 (lane / 16), chunk position lane % 16
+    auto issue = [&](int q) __attribute__((always_inline)) {
+      const int n0 = 32 * (t0 + q);
+      uint16_t* st = ring + (q % kSkNB) * kSkStage;
+#pragma unroll
+      for (int i = 0; i < kSkCopies; ++i) {
+        const int r = 4 * i + (lane >> 4);
+        const int n = min(n0 + r, N - 1);
+        const uint16_t* wrow = (W2 && n >= p.N1) ? W2 + (size_t)(n - p.N1) * p.ldb : W + (size_t)n * p.ldb;
+        lds_dma16(wrow + k0 + 8 * sk_swz(r, lane & 15), st + 512 * i);
+      }
+    };
+    for (int q = 0; q < kSkNB - 1 && q < my; ++q) issue(q);
+    for (int tile = 0; tile < my; ++tile) {
+      // tile has landed once only the copies issued after it may be
+      // outstanding; lgkmcnt(0) too, since the stage refilled below was read
+      // just before
+      wait_vm_dyn<kSkCopies * (kSkNB - 2)>(kSkCopies * min(my - 1 - tile, kSkNB - 2));
+      const uint16_t* st = ring + (tile % kSkNB) * kSkStage;
+      u32x4 wf[KPS];
+#pragma unroll
+      for (int jj = 0; jj < KPS; ++jj) wf[jj] = *(const u32x4*)(st + lr * kSkBK + 8 * sk_swz(lr, 2 * jj + lk));
+      f32x16_t acc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < KPS; ++jj)
+#pragma unroll
+        for (int pl = 0; pl < AP; ++pl) acc = mfma32(wf[jj], xf[pl][jj], acc);
+      if (tile + kSkNB - 1 < my) issue(tile + kSkNB - 1);
+      float* rb = red + (size_t)(tile & 1) * kSkRed + wave * 16 * kWave;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) rb[i * kWave + lane] = acc[i];
+      // the partial tile is in LDS before the barrier; the copies stay in flight
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0) only
+      ring_barrier();
+    }
+    return;
+  }
+
+  // sum wave: lane (lr, lk) holds activation row lr and output columns
+  // 32 t + 8 (i / 4) + 4 lk + (i % 4), i = 0 .. 15, of tile t
+  for (int tile = 0; tile < my; ++tile) {
+    ring_barrier();
+    const int n0 = 32 * (t0 + tile);
+    const float* rb = red + (size_t)(tile & 1) * kSkRed + lane;
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float a = rb[i * kWave];
+#pragma unroll
+      for (int w = 1; w < kSkStream; ++w) a += rb[(w * 16 + i) * kWave];
+      v[i] = a;
+    }
+    if (lr < M) {
+      float* dst = p.part + ((size_t)z * M + lr) * N;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + 8 * g + 4 * lk;
+        if (n < N) *(float4*)(dst + n) = make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+      }
+    }
+  }
+}
+
+// Calls of at most 32 rows whose K is a multiple of the split range, with
+// at least two ranges (the kernel writes partials only: readers of a result
+// of one split read C instead).
+bool skinny_fits(int M, int K) { return M <= 32 && K % kSkRange == 0 && K >= 2 * kSkRange; }
+
+hipError_t launch_skinny(const GemmParams& p, int a_planes, hipStream_t s) {
+  static_assert(kSkLds <= 160 * 1024, "skinny LDS");
+  const int splits = p.K / kSkRange;
+  const int n_tiles = (p.N + 31) / 32;
+  int per = kSkGrid / splits;
+  per = per < 1 ? 1 : (per > n_tiles ? n_tiles : per);
+  const void* fn = a_planes == 1 ? (const void*)gemm_skinny_kernel<1> : (const void*)gemm_skinny_kernel<2>;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSkLds);
+  if (e != hipSuccess) return e;
+  if (a_planes == 1)
+    hipLaunchKernelGGL(gemm_skinny_kernel<1>, dim3(splits * per), dim3(kSkThreads), kSkLds, s, p, n_tiles, per);
+  else
+    hipLaunchKernelGGL(gemm_skinny_kernel<2>, dim3(splits * per), dim3(kSkThreads), kSkLds, s, p, n_tiles, per);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------- float32 weight path ----
 template <class T>
 __global__ __launch_bounds__(T::THREADS) void gemm_kernel(GemmParams p) {
@@ -367,6 +513,7 @@ typedef GemmTile<64, 64, 32, 32, 2, 2> TilePlanesF32;
 
 size_t gemm_ws_bytes(int M, int N, int K, int b_f32) {
   if (b_f32) return 0;
+  if (skinny_fits(M, K)) return (size_t)(K / kSkRange) * M * N * sizeof(float);
   const DmaPlan pl = dma_plan(M, N, K);
   return pl.splits > 1 ? (size_t)pl.splits * M * N * sizeof(float) : 0;
 }
@@ -377,6 +524,11 @@ hipError_t gemm_deferred(const GemmArgs& a, float* ws, hipStream_t s, SplitOut* 
   *out = SplitOut{a.C, a.ldc, ws, 1, a.M, a.N, a.R, a.ldr};
   if (!a.b_f32) {
     if (!dma_ok(a)) return hipErrorInvalidValue;
+    if (skinny_fits(a.M, a.K)) {
+      p.splits = a.K / kSkRange;
+      out->splits = p.splits;
+      return launch_skinny(p, a.a_planes, s);
+    }
     const DmaPlan pl = dma_plan(a.M, a.N, a.K);
     p.splits = pl.splits;
     out->splits = pl.splits;
@@ -393,13 +545,19 @@ hipError_t gemm(const GemmArgs& a, float* ws, hipStream_t s) {
                a.B2, a.B2 ? a.N1 : a.N};
   if (!a.b_f32) {
     if (!dma_ok(a)) return hipErrorInvalidValue;
-    const DmaPlan pl = dma_plan(a.M, a.N, a.K);
-    p.splits = pl.splits;
-    hipError_t e = launch_dma_any(p, pl, a.a_planes, s);
-    if (e != hipSuccess || pl.splits == 1) return e;
+    hipError_t e;
+    if (skinny_fits(a.M, a.K)) {
+      p.splits = a.K / kSkRange;
+      e = launch_skinny(p, a.a_planes, s);
+    } else {
+      const DmaPlan pl = dma_plan(a.M, a.N, a.K);
+      p.splits = pl.splits;
+      e = launch_dma_any(p, pl, a.a_planes, s);
+    }
+    if (e != hipSuccess || p.splits == 1) return e;
     const size_t total4 = (size_t)a.M * a.N / 4;
     const int blocks = (int)((total4 + 255) / 256 < 4096 ? (total4 + 255) / 256 : 4096);
-    hipLaunchKernelGGL(splitk_reduce4, dim3(blocks), dim3(256), 0, s, ws, pl.splits, a.M, a.N, a.C,
+    hipLaunchKernelGGL(splitk_reduce4, dim3(blocks), dim3(256), 0, s, ws, p.splits, a.M, a.N, a.C,
                        a.ldc, a.R, a.ldr);
     return hipGetLastError();
   }

@@ -41,7 +41,8 @@ TD = {"bf16": torch.bfloat16, "f32": torch.float32}
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-@pytest.mark.parametrize("rows,H", [(1, 256), (37, 256), (32, 2048), (144, 320), (300, 2048)])
+@pytest.mark.parametrize("rows,H", [(1, 256), (37, 256), (32, 2048), (5, 1024), (32, 1536), (144, 320),
+                                    (300, 2048)])
 @pytest.mark.parametrize("residual", [False, True])
 def test_fuse(dm, dt, rows, H, residual):
     print(f"fuse dt={dt} rows={rows} H={H} res={residual}", flush=True)
