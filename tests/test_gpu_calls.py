@@ -383,6 +383,9 @@ def test_block_draft(dm, dt, shape):
     dict(B=5, S=3, H=256, Hq=4, Hkv=4, d=64, F=256, NL=1, ctx_lens=[64, 65, 0, 1000, 7]),
     dict(B=32, S=1, H=512, Hq=16, Hkv=4, d=128, F=512, NL=1,
          ctx_lens=list(range(40, 40 + 32 * 37, 37))),
+    # 12 rows with K >= 1024: the weight-streaming projections (2 and 3 splits,
+    # the gate/up pair as one call), two layers
+    dict(B=6, S=2, H=1024, Hq=8, Hkv=2, d=128, F=1536, NL=2, ctx_lens=[0, 17, 300, 64, 1, 900]),
 ])
 def test_mtp_block(dm, dt, shape):
     """The causal MTP block and the K/V rows it returns, against the oracle."""
