@@ -284,16 +284,21 @@ typedef DmaTile<1, 1, 4> DmaM32;    // 128 x 32
 typedef DmaTile<2, 2, 2> DmaM128;   // 128 x 128
 typedef DmaTile<1, 1, 4, 64, 1> DmaM32Bf16;    // the same tiles for a bf16 activation
 typedef DmaTile<2, 2, 2, 64, 1> DmaM128Bf16;
+typedef DmaTile<3, 1, 1> DmaM128N96;            // 96 x 128
+typedef DmaTile<3, 1, 1, 64, 1> DmaM128N96Bf16;
 
 struct DmaPlan {
-  int cfg;   // 0: DmaM32, 1: DmaM128
+  int cfg;   // 0: DmaM32, 1: DmaM128, 2: DmaM128N96
   int tn, tm, splits;
 };
 
 // Tile and split-K choice.  Measured on the drafter shapes (M = 256 slot rows,
 // N and K of 2048 .. 6144): 128 x 128 tiles with about 192 workgroups in total
 // beat larger tiles and a full wave of 256 (fewer float32 partials to write
-// and re-read); the 32 fused rows take the 128 x 32 tile.
+// and re-read).  Where N is a multiple of 96 and 96-wide tiles fit one pass
+// over 256 CUs (the QKV and the fused gate/up projections of the batch-32
+// drafter), those fill the machine instead: 64 tiles x 4 splits and 256
+// tiles, against 192 workgroups.  The 32 fused rows take the 128 x 32 tile.
 DmaPlan dma_plan(int M, int N, int K) {
   DmaPlan pl;
   int BM, target;
@@ -308,6 +313,11 @@ DmaPlan dma_plan(int M, int N, int K) {
   }
   pl.tn = (N + 127) / 128;
   pl.tm = (M + BM - 1) / BM;
+  if (M > 32 && N % 96 == 0 && (N / 96) * pl.tm <= 256) {
+    pl.cfg = 2;
+    pl.tn = N / 96;
+    target = 256;
+  }
   const int tiles = pl.tn * pl.tm;
   const int nK = K / 64;
   // each split at least four k-slices long
@@ -334,6 +344,7 @@ hipError_t launch_dma(const GemmParams& p, const DmaPlan& pl, hipStream_t s) {
 }
 
 hipError_t launch_dma_any(const GemmParams& p, const DmaPlan& pl, int a_planes, hipStream_t s) {
+  if (pl.cfg == 2) return a_planes == 1 ? launch_dma<DmaM128N96Bf16>(p, pl, s) : launch_dma<DmaM128N96>(p, pl, s);
   if (a_planes == 1) return pl.cfg == 0 ? launch_dma<DmaM32Bf16>(p, pl, s) : launch_dma<DmaM128Bf16>(p, pl, s);
   return pl.cfg == 0 ? launch_dma<DmaM32>(p, pl, s) : launch_dma<DmaM128>(p, pl, s);
 }
