@@ -238,6 +238,9 @@ def main() -> int:
     ap.add_argument("--kernel", default="head_gemm_mf32_kernel<7,")
     ap.add_argument("--copy-kernel", default="elementwise")
     ap.add_argument("--copy-mib", type=int, default=1024)
+    ap.add_argument("--sustain", type=float, default=0.0,
+                    help="repeat each LM-head call of the round alone for this many seconds "
+                         "(for power and clock readings taken alongside), then exit")
     args = ap.parse_args()
     if args.rocprof_summary:
         return rocprof_summary(args)
@@ -288,6 +291,26 @@ def main() -> int:
                 call_evs[i][1].record(stream)
             if st != 0:
                 raise RuntimeError(f"call {i} failed with status {st}")
+
+    if args.sustain > 0:
+        # each head call of the round on its own, back to back, for a few
+        # seconds: a steady load for readings of power and clocks
+        one_round()
+        torch.cuda.synchronize()
+        for name in ("lm_head_draft_target", "lm_head_t1"):
+            fn, ref = R._fns[R.step_names.index(name)]
+            t0 = time.time()
+            n = 0
+            while time.time() - t0 < args.sustain:
+                for _ in range(20):
+                    if fn(ref, R._ws_ptr, R._ws_bytes, sp) != 0:
+                        raise RuntimeError(f"{name} failed")
+                torch.cuda.synchronize()
+                n += 20
+            t1 = time.time()
+            print(json.dumps({"sustain": name, "start": round(t0, 3), "end": round(t1, 3), "calls": n,
+                              "us_per_call": round((t1 - t0) / n * 1e6, 2)}), flush=True)
+        return 0
 
     if args.copy_probe_mib:
         # one elementwise kernel that reads and writes exactly N MiB
