@@ -68,10 +68,12 @@ void gemm_dma_kernel(GemmParams p, int n_tiles_n, int n_tiles_m) {
   const int per = (total + 7) / 8;   // XCD-contiguous ranges (workgroup i runs on XCD i % 8)
   const int t = (blockIdx.x % 8) * per + blockIdx.x / 8;
   if (t >= total) return;
-  // consecutive t: the splits of one tile, then the tiles along N
-  const int z = t % p.splits;
-  const int tile = t / p.splits;
-  const int n0 = (tile % n_tiles_n) * T::BN, m0 = (tile / n_tiles_n) * T::BM;
+  // consecutive t: the row tiles that share one weight tile (and split), so
+  // that they run together on one XCD and its L2 serves the second read of
+  // the weights; then the splits, then the tiles along N
+  const int m0 = (t % n_tiles_m) * T::BM;
+  const int z = (t / n_tiles_m) % p.splits;
+  const int n0 = (t / n_tiles_m / p.splits) * T::BN;
   const int nK = p.K / T::BK;   // K % BK == 0 is checked by the launcher
   const int s_begin = (int)((long)z * nK / p.splits), s_end = (int)((long)(z + 1) * nK / p.splits);
   const int ns = s_end - s_begin;
@@ -286,9 +288,10 @@ typedef DmaTile<1, 1, 4, 64, 1> DmaM32Bf16;    // the same tiles for a bf16 acti
 typedef DmaTile<2, 2, 2, 64, 1> DmaM128Bf16;
 typedef DmaTile<3, 1, 1> DmaM128N96;            // 96 x 128
 typedef DmaTile<3, 1, 1, 64, 1> DmaM128N96Bf16;
+typedef DmaTile<1, 5, 4, 32> DmaM160;             // 160 x 128, 32-wide slices
 
 struct DmaPlan {
-  int cfg;   // 0: DmaM32, 1: DmaM128, 2: DmaM128N96
+  int cfg;   // 0: DmaM32, 1: DmaM128, 2: DmaM128N96, 3: DmaM160 (two planes only)
   int tn, tm, splits;
 };
 
@@ -299,7 +302,11 @@ struct DmaPlan {
 // over 256 CUs (the QKV and the fused gate/up projections of the batch-32
 // drafter), those fill the machine instead: 64 tiles x 4 splits and 256
 // tiles, against 192 workgroups.  The 32 fused rows take the 128 x 32 tile.
-DmaPlan dma_plan(int M, int N, int K) {
+// 129 .. 160 rows of a two-plane activation (136 slot rows of the long-block
+// drafter) take one 160-row tile instead of two 128-row tiles, the second
+// nearly empty: 160 x 128 with 32-wide slices and five stages measured faster
+// than both that and 160 x 256 tiles.
+DmaPlan dma_plan(int M, int N, int K, int a_planes) {
   DmaPlan pl;
   int BM, target;
   if (M <= 32) {
@@ -313,13 +320,20 @@ DmaPlan dma_plan(int M, int N, int K) {
   }
   pl.tn = (N + 127) / 128;
   pl.tm = (M + BM - 1) / BM;
-  if (M > 32 && N % 96 == 0 && (N / 96) * pl.tm <= 256) {
+  int BK = 64;
+  if (M > 128 && M <= 160 && a_planes == 2) {
+    pl.cfg = 3;
+    pl.tn = (N + DmaM160::BN - 1) / DmaM160::BN;
+    pl.tm = 1;
+    target = 256;
+    BK = 32;
+  } else if (M > 32 && N % 96 == 0 && (N / 96) * pl.tm <= 256) {
     pl.cfg = 2;
     pl.tn = N / 96;
     target = 256;
   }
   const int tiles = pl.tn * pl.tm;
-  const int nK = K / 64;
+  const int nK = K / BK;
   // each split at least four k-slices long
   int sp = (target + tiles / 2) / tiles;
   if (sp > nK / 4) sp = nK / 4;
@@ -344,6 +358,7 @@ hipError_t launch_dma(const GemmParams& p, const DmaPlan& pl, hipStream_t s) {
 }
 
 hipError_t launch_dma_any(const GemmParams& p, const DmaPlan& pl, int a_planes, hipStream_t s) {
+  if (pl.cfg == 3) return launch_dma<DmaM160>(p, pl, s);
   if (pl.cfg == 2) return a_planes == 1 ? launch_dma<DmaM128N96Bf16>(p, pl, s) : launch_dma<DmaM128N96>(p, pl, s);
   if (a_planes == 1) return pl.cfg == 0 ? launch_dma<DmaM32Bf16>(p, pl, s) : launch_dma<DmaM128Bf16>(p, pl, s);
   return pl.cfg == 0 ? launch_dma<DmaM32>(p, pl, s) : launch_dma<DmaM128>(p, pl, s);
@@ -525,8 +540,9 @@ typedef GemmTile<64, 64, 32, 32, 2, 2> TilePlanesF32;
 size_t gemm_ws_bytes(int M, int N, int K, int b_f32) {
   if (b_f32) return 0;
   if (skinny_fits(M, K)) return (size_t)(K / kSkRange) * M * N * sizeof(float);
-  const DmaPlan pl = dma_plan(M, N, K);
-  return pl.splits > 1 ? (size_t)pl.splits * M * N * sizeof(float) : 0;
+  // either activation form: the larger of the two plans
+  const int splits = max(dma_plan(M, N, K, 1).splits, dma_plan(M, N, K, 2).splits);
+  return splits > 1 ? (size_t)splits * M * N * sizeof(float) : 0;
 }
 
 hipError_t gemm_deferred(const GemmArgs& a, float* ws, hipStream_t s, SplitOut* out) {
@@ -540,7 +556,7 @@ hipError_t gemm_deferred(const GemmArgs& a, float* ws, hipStream_t s, SplitOut* 
       out->splits = p.splits;
       return launch_skinny(p, a.a_planes, s);
     }
-    const DmaPlan pl = dma_plan(a.M, a.N, a.K);
+    const DmaPlan pl = dma_plan(a.M, a.N, a.K, a.a_planes);
     p.splits = pl.splits;
     out->splits = pl.splits;
     return launch_dma_any(p, pl, a.a_planes, s);
@@ -561,7 +577,7 @@ hipError_t gemm(const GemmArgs& a, float* ws, hipStream_t s) {
       p.splits = a.K / kSkRange;
       e = launch_skinny(p, a.a_planes, s);
     } else {
-      const DmaPlan pl = dma_plan(a.M, a.N, a.K);
+      const DmaPlan pl = dma_plan(a.M, a.N, a.K, a.a_planes);
       p.splits = pl.splits;
       e = launch_dma_any(p, pl, a.a_planes, s);
     }
