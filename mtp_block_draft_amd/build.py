@@ -25,11 +25,16 @@ SOURCES = ["dmtp_api.cpp", "gemm.hip", "elementwise.hip", "attention.hip", "lm_h
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", f"-I{INCLUDE}", f"-I{CSRC}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-result"]
+# The attention kernels keep their MFMA accumulators in ordinary VGPRs: the
+# online softmax reads the scores and rescales the output accumulators with
+# vector ALU instructions, which cannot address AGPRs, so AGPR accumulators
+# cost a move out and back per element and tile.  Their registers fit either way.
+EXTRA = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + FLAGS
+    cmd = [HIPCC, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + FLAGS + EXTRA.get(src, [])
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

@@ -349,8 +349,10 @@ __global__ __launch_bounds__(64 * kAttnQtw) void attn_wave_kernel(
     }
   };
 
-  // query fragments (B operand of S^T = K Q^T): column = query row, 8 d values;
-  // loaded before the first copies so that waiting for them leaves those in flight
+  // query fragments (B operand of S^T = K Q^T): column = query row, 8 d values,
+  // times scale / ln 2 so that the scores come out in log2 units; loaded
+  // before the first copies so that waiting for them leaves those in flight
+  const float scale2 = scale * 1.4426950408889634f;
   const float* qg = q + (((size_t)b * Hkv + kvh) * NQ) * D;
   u32x4 qh[C::DS], ql[C::DS];
 #pragma unroll
@@ -359,6 +361,8 @@ __global__ __launch_bounds__(64 * kAttnQtw) void attn_wave_kernel(
     if (qrow < NQ) {
       x0 = *(const float4*)(qg + (size_t)qrow * D + 16 * ds + 8 * g);
       x1 = *(const float4*)(qg + (size_t)qrow * D + 16 * ds + 8 * g + 4);
+      x0 = make_float4(x0.x * scale2, x0.y * scale2, x0.z * scale2, x0.w * scale2);
+      x1 = make_float4(x1.x * scale2, x1.y * scale2, x1.z * scale2, x1.w * scale2);
     }
     uint32_t h[4], l[4];
     split2(x0.x, x0.y, h[0], l[0]);
@@ -379,8 +383,7 @@ __global__ __launch_bounds__(64 * kAttnQtw) void attn_wave_kernel(
   for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
-  // running max in log2 units (scores times scale / ln 2) and running sum
-  const float scale2 = scale * 1.4426950408889634f;
+  // reference max of the exponentials, in log2 units, and running sum
   float m_run = -INFINITY, l_run = 0.f;
 
   // per-lane LDS offsets of the fragments (elements within a stage)
@@ -411,47 +414,52 @@ __global__ __launch_bounds__(64 * kAttnQtw) void attn_wave_kernel(
     if (issuer && t + C::NBUF - 1 < nt) issue(t + C::NBUF - 1);
     const uint16_t* st = smem + (t % C::NBUF) * C::STAGE;
 
-    // S^T[key][query]: element i is key 8 (i / 4) + 4 g + i % 4 of this lane's
-    // query row; the hi and lo query planes accumulate in separate chains
-    f32x16_t s, s2;
+    // S^T[key][query] in log2 units: element i is key 8 (i / 4) + 4 g + i % 4
+    // of this lane's query row; both query planes accumulate in one chain
+    f32x16_t s;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s[i] = s2[i] = 0.f;
+    for (int i = 0; i < 16; ++i) s[i] = 0.f;
 #pragma unroll
     for (int ds = 0; ds < C::DS; ++ds) {
       const u32x4 kf = *(const u32x4*)(st + k_frag[ds]);
       s = mfma32(kf, qh[ds], s);
-      s2 = mfma32(kf, ql[ds], s2);
+      s = mfma32(kf, ql[ds], s);
     }
     const int valid = nkeys - C::KT * t;   // keys of this tile inside the chunk
-    float mx = -INFINITY;
+    if (valid < C::KT) {                   // the chunk's last tile: mask the repeated keys
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = 8 * (i >> 2) + 4 * g + (i & 3);
-      s[i] = key < valid ? (s[i] + s2[i]) * scale2 : -INFINITY;
-      mx = fmaxf(mx, s[i]);
+      for (int i = 0; i < 16; ++i)
+        if (8 * (i >> 2) + 4 * g + (i & 3) >= valid) s[i] = -INFINITY;
     }
+    float mx = s[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
     mx = fmaxf(mx, shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first tile
-    float ps = 0.f;
-    uint32_t ph[8], pl[8];
-#pragma unroll
-    for (int i = 0; i < 16; i += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(s[i] - m_new);
-      const float p1 = __builtin_amdgcn_exp2f(s[i + 1] - m_new);
-      ps += p0 + p1;
-      split2(p0, p1, ph[i / 2], pl[i / 2]);
-    }
-    ps += shfl_xor(ps, 32);
-    l_run = l_run * alpha + ps;
-    // O is rescaled only when some row's running max rose (alpha < 1)
-    if (__ballot(m_new > m_run) != 0) {
+    // The exponentials are taken against a reference max m_run, moved (and O
+    // and l rescaled) only when some row's max exceeds it by more than 2^8:
+    // the (m, l, O) triple stays exact for any reference, and a stale one
+    // keeps every weight at most 2^8.
+    if (__ballot(mx > m_run + 8.f) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first tile
+      l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+      m_run = m_new;
     }
-    m_run = m_new;
+    float ps = 0.f;
+    uint32_t ph[8], pl[8];
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(s[i] - m_run);
+      const float p1 = __builtin_amdgcn_exp2f(s[i + 1] - m_run);
+      ps += p0 + p1;
+      split2(p0, p1, ph[i / 2], pl[i / 2]);
+    }
+    ps += shfl_xor(ps, 32);
+    l_run += ps;
 
     // O^T[dd][query] += V^T P^T over the tile's keys in two k-steps; k-step ks
     // takes this lane group's keys 16 ks + 4 g + (0..3) and 16 ks + 8 + 4 g + (0..3),
@@ -684,12 +692,15 @@ AttnPlan attn_plan(int B, int Hq, int Hkv, int S, int d, int max_ctx, int window
     // per-wave kernel: about 768 query-tile waves over the context rows
     // actually present (ctx_rows / B per sequence on average), at least four
     // 32-key tiles each, at most 256 chunks per sequence for the combine.
-    // Measured against 384 .. 3072: fewer, longer chunks keep each wave's copy
-    // pipeline full for longer; below 768 the long-context workload runs out
-    // of parallelism.
+    // Measured against 384 .. 3072 with one-wave workgroups (32 query rows
+    // per kv head): fewer, longer chunks keep each wave's copy pipeline full
+    // for longer.  When a kv head has several query tiles, their waves share
+    // one workgroup and its ring, and 1536 waves (two such workgroups per CU,
+    // so that one's softmax overlaps the other's matrix products) measured
+    // faster than 768 and 3072.
     const long keys = (long)(ctx_rows > 0 ? ctx_rows : (long)B * eff);
     const long tiles = keys * Hkv * (p.nqp / 32);
-    constexpr long target = 768;
+    const long target = p.nqp > 32 ? 1536 : 768;
     long per = (tiles + target * 32 - 1) / (target * 32);
     if (per < 4) per = 4;
     int chunk = (int)(32 * per);
