@@ -334,8 +334,9 @@ DmaPlan dma_plan(int M, int N, int K, int a_planes) {
   }
   const int tiles = pl.tn * pl.tm;
   const int nK = K / BK;
-  // each split at least four k-slices long
-  int sp = (target + tiles / 2) / tiles;
+  // each split at least four k-slices long; the 160-row tiles stay within one
+  // pass over the CUs (56 QKV tiles of the long-block drafter: 4 splits, not 5)
+  int sp = pl.cfg == 3 ? target / tiles : (target + tiles / 2) / tiles;
   if (sp > nK / 4) sp = nK / 4;
   pl.splits = sp < 1 ? 1 : sp;
   return pl;
