@@ -278,7 +278,16 @@ def test_lm_head_at_most_32_rows(dm, H, M):
 # ---------------------------------------------------------------- block draft
 
 
-def _draft_case(seed, dt, B, H, Hq, Hkv, d, F, NL, K, n_anchor, ctx_lens, V=500, window=0):
+def _spiked(k, ctx_lens, spike):
+    """Keys of the context rows at position 50 mod 97 of each sequence times
+    spike: their scores jump far above the rest in the middle of a chunk."""
+    if spike:
+        pos = np.concatenate([np.arange(n) for n in ctx_lens] + [np.zeros(0, np.int64)])
+        k[:len(pos)][pos % 97 == 50] *= spike
+    return k
+
+
+def _draft_case(seed, dt, B, H, Hq, Hkv, d, F, NL, K, n_anchor, ctx_lens, V=500, window=0, spike=0.0):
     r = np.random.default_rng(seed)
     cu = np.concatenate([[0], np.cumsum(ctx_lens)]).astype(np.int32)
     tot = int(cu[-1])
@@ -293,7 +302,7 @@ def _draft_case(seed, dt, B, H, Hq, Hkv, d, F, NL, K, n_anchor, ctx_lens, V=500,
             wg=_store(0.02 * r.standard_normal((F, H)), dt),
             wu=_store(0.02 * r.standard_normal((F, H)), dt),
             wd=_store(0.02 * r.standard_normal((H, F)), dt),
-            ctx_k=_store(r.standard_normal((max(tot, 1), Hkv, d)), dt),
+            ctx_k=_store(_spiked(r.standard_normal((max(tot, 1), Hkv, d)), ctx_lens, spike), dt),
             ctx_v=_store(r.standard_normal((max(tot, 1), Hkv, d)), dt)))
     anchor = r.integers(0, V - 1, size=B).astype(np.int32)
     x_t1 = (emb[r.integers(0, V - 1, size=B)] + 0.01 * r.standard_normal((B, H))).astype(np.float32)
@@ -323,12 +332,21 @@ def _draft_case(seed, dt, B, H, Hq, Hkv, d, F, NL, K, n_anchor, ctx_lens, V=500,
     dict(B=2, H=256, Hq=10, Hkv=1, d=64, F=256, NL=1, K=16, n_anchor=2, ctx_lens=[300, 40]),
     # the smallest block: one MASK slot
     dict(B=3, H=256, Hq=4, Hkv=2, d=64, F=256, NL=1, K=2, n_anchor=2, ctx_lens=[17, 0, 64]),
+    # keys of scattered context rows times 40: a row's max jumps by far more
+    # than 2^8 (log2 units) in the middle of a chunk, so the running reference
+    # max moves and O and l are rescaled there; several query tiles per kv head
+    dict(B=2, H=512, Hq=10, Hkv=2, d=128, F=512, NL=1, K=16, n_anchor=2, ctx_lens=[777, 2100],
+         spike=40.0),
+    # the same with one query tile per kv head
+    dict(B=3, H=256, Hq=4, Hkv=2, d=64, F=512, NL=1, K=7, n_anchor=2, ctx_lens=[1500, 333, 64],
+         spike=40.0),
 ])
 def test_block_draft(dm, dt, shape):
     shape = dict(shape)
     window = shape.pop("window", 0)
-    print(f"block_draft dt={dt} {shape} window={window}", flush=True)
-    c = _draft_case(sum(shape["ctx_lens"]) + shape["H"], dt, window=window, **shape)
+    spike = shape.pop("spike", 0.0)
+    print(f"block_draft dt={dt} {shape} window={window} spike={spike}", flush=True)
+    c = _draft_case(sum(shape["ctx_lens"]) + shape["H"], dt, window=window, spike=spike, **shape)
     B, H, K, na = shape["B"], shape["H"], shape["K"], shape["n_anchor"]
     td = TD[dt]
     f32 = torch.float32
