@@ -404,6 +404,8 @@ def test_block_draft(dm, dt, shape):
     # 12 rows with K >= 1024: the weight-streaming projections (2 and 3 splits,
     # the gate/up pair as one call), two layers
     dict(B=6, S=2, H=1024, Hq=8, Hkv=2, d=128, F=1536, NL=2, ctx_lens=[0, 17, 300, 64, 1, 900]),
+    # spiked context keys: a row's reference max moves in the middle of a chunk
+    dict(B=4, S=3, H=256, Hq=8, Hkv=2, d=64, F=256, NL=1, ctx_lens=[600, 1, 250, 0], spike=40.0),
 ])
 def test_mtp_block(dm, dt, shape):
     """The causal MTP block and the K/V rows it returns, against the oracle."""
