@@ -457,7 +457,10 @@ def test_mtp_block(dm, dt, shape):
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("N,NF,H,Hq,Hkv,d,NL", [(1, 5, 256, 4, 2, 64, 1), (37, 5, 512, 8, 2, 128, 2),
-                                                (300, 3, 2048, 16, 4, 128, 1)])
+                                                (300, 3, 2048, 16, 4, 128, 1),
+                                                # 150 rows: the two-plane layer GEMM on the 160-row
+                                                # tile, the bf16 feature GEMM on 128-row tiles
+                                                (150, 5, 512, 8, 2, 128, 2)])
 def test_ctx_kv(dm, dt, N, NF, H, Hq, Hkv, d, NL):
     """Context K/V rows from target features, written into the named cache rows."""
     print(f"ctx_kv dt={dt} N={N} NF={NF} H={H} {Hq}/{Hkv}x{d} NL={NL}", flush=True)
