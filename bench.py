@@ -8,12 +8,18 @@ hidden 2048, vocabulary 151936, one block-draft layer (16 query / 4 kv heads
 x 128, SwiGLU 6144), 7 candidates (8 draft slots, 8 verify rows), context
 lengths uniform in [1024, 4096], greedy.
 
-Prints one JSON line.  value = rounds/s over the timed steps, which hold
-nothing but the six ABI calls per round; committed tokens/s, the roofline of
-the dominant kernel (the LM-head GEMM over the 448 draft+target rows, timed by
-events attached to its own dispatch) and the CPU oracle timed on a bounded
-sample are extra fields.  Per-call durations (phases_us) come from a separate
-pass after the timed loop.
+Prints one JSON line.  value = rounds/s over the timed steps: W untimed
+rounds, then K rounds back to back between two events, holding nothing but
+the ABI calls of each round.  Extra fields, each from its own pass after the
+timed loop:
+  round_us_warm / round_us_cold  median, p10 and p90 of rounds timed one by one
+      (cold: each after writes that evict the last-level cache);
+  roofline  the dominant kernel (the LM-head GEMM over the 448 draft+target
+      rows), timed by the events attached to its own dispatch on every round
+      of a dedicated pass;
+  phases    per-call medians with each call's algorithmic bytes and its
+      fraction of the HBM (or matrix-core) peak;
+  cpu_baseline  the CPU oracle on a bounded sample, with the host CPU model.
 """
 from __future__ import annotations
 
@@ -32,7 +38,6 @@ PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 METRIC = "draft+verify rounds/s and accepted tokens/s at B32; % MFMA / HBM peak"
-GEMM_EVERY = 4   # timed steps per head-GEMM event sample
 
 
 def _workload_desc(cfg) -> str:
@@ -40,7 +45,8 @@ def _workload_desc(cfg) -> str:
             f"{cfg.Hq}q/{cfg.Hkv}kv x{cfg.d}, F={cfg.F}, K={cfg.K} candidates "
             f"({cfg.S} slots, {cfg.R} verify rows), ctx U[{cfg.ctx_min},{cfg.ctx_max}] "
             f"(drafter window {cfg.window or 'all'}), "
-            f"tau={cfg.tau_mode}, verify={cfg.verify}"
+            f"tau={cfg.tau_mode}"
+            + (f", verify={cfg.verify}" if cfg.tau_mode != "greedy" else ", greedy verify")
             + (", MTP decoder block" if cfg.mtp_block else ""))
 
 
@@ -205,6 +211,66 @@ def ctx_kv_bench(R, cfg, stream, steps: int, warmup: int):
             "hbm_frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4)}
 
 
+def _pct(xs, q):
+    import numpy as np
+    return round(float(np.percentile(np.asarray(xs, dtype=np.float64), q)), 2)
+
+
+def _dist(us):
+    """Median and 10th / 90th percentiles of per-round microseconds."""
+    return {"n": len(us), "median_us": _pct(us, 50), "p10_us": _pct(us, 10), "p90_us": _pct(us, 90)}
+
+
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def phase_model(cfg, inp, n_sampled_rows: int):
+    """Algorithmic bytes (and flops) of each call of one round, and its bound.
+
+    Bytes count what the call must move at least once: weights and tables in
+    the storage dtype, the context keys and values the drafter reads (the last
+    `window` rows of each sequence), input and output rows.  The LM-head call
+    over draft and target rows is a matrix-core bound when it has at least 312
+    rows (the bf16 ridge of 2.5 PFLOP/s over 8 TB/s)."""
+    import numpy as np
+    esz = 2 if cfg.dtype == "bf16" else 4
+    B, H, V, K, S = cfg.B, cfg.H, cfg.V, cfg.K, cfg.S
+    fuse_b = 2 * H * H * esz + 2 * B * H * esz + B * H * 4
+    head_w = V * H * esz
+    L = np.asarray(inp.ctx_len, dtype=np.int64)
+    if cfg.window:
+        L = np.minimum(L, cfg.window)
+    kv_rows = int(L.sum())
+    layer_w = (cfg.qkv_dim * H + H * cfg.Hq * cfg.d + 3 * cfg.F * H) * esz
+    draft_b = cfg.n_layers * (layer_w + 2 * kv_rows * cfg.Hkv * cfg.d * esz) + B * S * H * esz
+    m2 = B * (K - 1) + B * (K + 1)
+    logits_b = n_sampled_rows * V * 4
+    out = {
+        "fuse_mtp": {"bound": "hbm", "bytes": fuse_b},
+        "lm_head_t1": {"bound": "hbm", "bytes": head_w + B * H * 4},
+        "fuse_delta": {"bound": "hbm", "bytes": fuse_b},
+        "block_draft": {"bound": "hbm", "bytes": draft_b},
+        "lm_head_draft_target": {"bound": "mfma" if m2 >= 312 else "hbm",
+                                 "bytes": head_w + m2 * H * esz + logits_b,
+                                 "flops": 2.0 * m2 * V * H},
+        "verify": {"bound": "latency", "bytes": None},
+    }
+    if cfg.mtp_block:
+        # the block reads its whole cache (no window)
+        cache_rows = int(np.asarray(inp.ctx_len, dtype=np.int64).sum())
+        out["mtp_block"] = {"bound": "hbm",
+                            "bytes": layer_w + 2 * cache_rows * cfg.Hkv * cfg.d * esz}
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -221,6 +287,12 @@ def main() -> int:
     ap.add_argument("--mtp-block", action="store_true",
                     help="h_MTP from an MTP decoder block (drafter layer shapes, causal over its "
                          "own KV cache) instead of h_MTP = h'")
+    ap.add_argument("--dist-rounds", type=int, default=200,
+                    help="rounds timed one by one (warm, and after a cache flush) for the "
+                         "median and p10 / p90")
+    ap.add_argument("--kernel-rounds", type=int, default=100,
+                    help="rounds of the pass that times the dominant kernel by its own "
+                         "dispatch events")
     ap.add_argument("--cpu-seqs", type=int, default=32, help="sequences in the oracle sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the oracle sample until this much time has passed")
@@ -267,10 +339,10 @@ def main() -> int:
     sp = ctypes.c_void_p(s_ptr)
     n_calls = len(R._fns)
 
-    # The head GEMM of the draft + target call is timed by its own dispatch:
-    # the descriptor carries a start/stop hipEvent pair per step, which the
-    # library hands to hipExtLaunchKernel, so the timed loop holds no extra
-    # stream commands.  Events come from the HIP runtime torch has loaded.
+    # The head GEMM of the draft + target call can be timed by its own
+    # dispatch: the descriptor carries a start/stop hipEvent pair, which the
+    # library hands to hipExtLaunchKernel, so no extra command enters the
+    # stream.  Events come from the HIP runtime torch has loaded.
     hip_path = next(l.split()[-1] for l in open("/proc/self/maps").read().splitlines()
                     if "libamdhip64" in l)
     hip = ctypes.CDLL(hip_path)
@@ -291,6 +363,9 @@ def main() -> int:
                 call_evs[i][1].record(stream)
             if st != 0:
                 raise RuntimeError(f"call {i} failed with status {st}")
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
 
     if args.sustain > 0:
         # each head call of the round on its own, back to back, for a few
@@ -321,54 +396,83 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
-    for _ in range(args.warmup):
+    # ---- rounds timed one by one: an event pair around each round (warm), and
+    # the same after 512 MB of writes that evict the 256 MB last-level cache
+    # (cold: back-to-back rounds share part of that cache -- drafter weights,
+    # context K/V -- which a target forward pass between rounds would evict)
+    n_dist = max(args.dist_rounds, 1)
+    wev = [(ev(), ev()) for _ in range(n_dist)]
+    for a, b in wev:
+        a.record(stream)
         one_round()
+        b.record(stream)
     torch.cuda.synchronize()
+    warm_us = [1000.0 * a.elapsed_time(b) for a, b in wev]
+    flush = torch.empty((512 << 20) // 4, dtype=torch.float32, device="cuda")
+    fev = [(ev(), ev()) for _ in range(n_dist)]
+    for k, (a, b) in enumerate(fev):
+        flush.fill_(float(k))
+        a.record(stream)
+        one_round()
+        b.record(stream)
+    torch.cuda.synchronize()
+    cold_us = [1000.0 * a.elapsed_time(b) for a, b in fev]
+    del flush
+    print(f"# {n_dist} single rounds: warm median {np.median(warm_us):.1f} us, cold median "
+          f"{np.median(cold_us):.1f} us", file=sys.stderr, flush=True)
 
-    # Every GEMM_EVERY-th timed step carries the head GEMM's dispatch events:
-    # an event-carrying dispatch leaves about 12 us of idle queue around it, so
-    # attaching them to every step would lower the throughput it measures.
+    # ---- the dominant kernel, timed by the events attached to its own
+    # dispatch on every round of a dedicated pass
+    n_k = max(args.kernel_rounds, 1)
     gev = []
-    for _ in range(0, args.steps, GEMM_EVERY):
+    for _ in range(n_k):
         pair = (ctypes.c_void_p(), ctypes.c_void_p())
         if hip.hipEventCreate(ctypes.byref(pair[0])) or hip.hipEventCreate(ctypes.byref(pair[1])):
             raise RuntimeError("hipEventCreate failed")
         gev.append(pair)
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    for k in range(n_k):
+        one_round(gemm_ev=gev[k])
     torch.cuda.synchronize()
-    t_start.record(stream)
-    for k in range(args.steps):
-        one_round(gemm_ev=gev[k // GEMM_EVERY] if k % GEMM_EVERY == 0 else None)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms_total = t_start.elapsed_time(t_end)
-    ms_step = ms_total / args.steps
-    gemm_ms = []
+    gemm_us = []
     for a, b in gev:
         ms = ctypes.c_float()
         if hip.hipEventElapsedTime(ctypes.byref(ms), a, b):
             raise RuntimeError("hipEventElapsedTime failed")
-        gemm_ms.append(ms.value)
+        gemm_us.append(1000.0 * ms.value)
         hip.hipEventDestroy(a)
         hip.hipEventDestroy(b)
     one_round()   # leaves the descriptor without events
-
-    # Rounds with a cold last-level cache: 512 MB written before each round
-    # evicts the 256 MB cache that back-to-back rounds partly share (drafter
-    # weights, context K/V); each such round is timed alone by its own events.
-    n_flush = min(args.steps, 50)
-    flush = torch.empty((512 << 20) // 4, dtype=torch.float32, device="cuda")
-    fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(n_flush)]
-    for k in range(n_flush):
-        flush.fill_(float(k))
-        fev[k][0].record(stream)
-        one_round()
-        fev[k][1].record(stream)
     torch.cuda.synchronize()
-    flushed_us = 1000.0 * float(np.median([a.elapsed_time(b) for a, b in fev]))
-    del flush
+
+    # ---- per-call durations, from a separate pass (events between calls add
+    # a few microseconds each, so they stay out of the passes above)
+    n_diag = 50
+    evs = [[[ev(), ev()] for _ in range(n_calls)] for _ in range(n_diag)]
+    for k in range(n_diag):
+        one_round(call_evs=evs[k])
+    torch.cuda.synchronize()
+    per_call_us = [1000.0 * float(np.median([evs[k][i][0].elapsed_time(evs[k][i][1])
+                                             for k in range(n_diag)])) for i in range(n_calls)]
+    pre_rounds = 2 * n_dist + n_k + 1 + n_diag
+
+    # ---- the headline: W untimed rounds, then exactly K rounds back to back,
+    # with nothing but the round's calls between the two events.  It runs after
+    # the diagnostic passes above, so it measures a GPU in its steady state: on
+    # a GPU fresh from idle the LM-head GEMM runs up to 30 % slower for the
+    # first 20 to 30 rounds while the power controller settles.
+    for _ in range(args.warmup):
+        one_round()
+    torch.cuda.synchronize()
+    t_start, t_end = ev(), ev()
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for _ in range(args.steps):
+        one_round()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    print(f"# headline: {args.steps} rounds, {1000.0 * ms_step:.2f} us per round", file=sys.stderr,
+          flush=True)
 
     graph_ms_step = None
     if args.graph:
@@ -376,8 +480,7 @@ def main() -> int:
         for _ in range(args.warmup):
             R.replay()
         torch.cuda.synchronize()
-        g0 = torch.cuda.Event(enable_timing=True)
-        g1 = torch.cuda.Event(enable_timing=True)
+        g0, g1 = ev(), ev()
         g0.record(stream)
         for _ in range(args.steps):
             R.replay()
@@ -385,16 +488,6 @@ def main() -> int:
         torch.cuda.synchronize()
         graph_ms_step = g0.elapsed_time(g1) / args.steps
 
-    # per-call durations, from a separate pass after the timed loop (stream
-    # events between calls add a few microseconds each, so they stay out of it)
-    n_diag = min(args.steps, 50)
-    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-            for _ in range(n_calls)] for _ in range(n_diag)]
-    for k in range(n_diag):
-        one_round(call_evs=evs[k])
-    torch.cuda.synchronize()
-    per_call_us = [1000.0 * float(np.mean([evs[k][i][0].elapsed_time(evs[k][i][1])
-                                           for k in range(n_diag)])) for i in range(n_calls)]
     res = R.results()
     committed = int(res["n_out"].sum())
     eager_ms_step = ms_step
@@ -402,11 +495,11 @@ def main() -> int:
         ms_step = graph_ms_step
     rounds_s = 1000.0 / ms_step
 
-    # dominant kernel: the LM-head call over draft (B(K-1)) and target (B(K+1)) rows
+    # dominant kernel: the LM-head GEMM over draft (B(K-1)) and target (B(K+1)) rows
     M = R.M2
     flops = 2.0 * M * cfg.V * cfg.H
     w_bytes = cfg.V * cfg.H * (2 if cfg.dtype == "bf16" else 4)
-    head_us = 1000.0 * float(np.mean(gemm_ms))
+    head_us = float(np.mean(gemm_us))
     achieved = flops / (head_us * 1e-6) / 1e12
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
     traffic = recorded_traffic() if args.config == "b32_greedy_bf16" else None
@@ -414,27 +507,45 @@ def main() -> int:
                 "frac": round(achieved / peak, 4),
                 "traffic": None if traffic is None else round(traffic),
                 "kernel": f"head_gemm_mf32_kernel of dmtp_lm_head over {M} rows (bf16 GEMM "
-                          f"with fused row statistics), timed by its dispatch events on "
-                          f"{len(gemm_ms)} of the {args.steps} timed steps",
+                          f"with fused row statistics), timed by the events of its own "
+                          f"dispatch on each of {n_k} rounds of a dedicated pass",
                 "algorithmic_flops": flops, "algorithmic_bytes": w_bytes + M * cfg.H * 2,
-                "avg_us": round(head_us, 2)}
+                "avg_us": round(head_us, 2), "median_us": _pct(gemm_us, 50),
+                "p10_us": _pct(gemm_us, 10), "p90_us": _pct(gemm_us, 90)}
 
+    n_sampled = int((inp.tau > 0).sum()) * (2 * cfg.K + 1)
+    model = phase_model(cfg, inp, n_sampled)
+    phases = {}
+    for name, us in zip(R.step_names, per_call_us):
+        m = model.get(name, {"bound": "latency", "bytes": None})
+        e = {"us": round(us, 2), "bound": m["bound"]}
+        if m.get("bytes"):
+            e["bytes"] = int(m["bytes"])
+            e["hbm_frac"] = round(m["bytes"] / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+        if m.get("flops") and m["bound"] == "mfma":
+            e["mfma_frac"] = round(m["flops"] / (us * 1e-6) / 1e12 / peak, 4)
+        phases[name] = e
+
+    greedy = not bool((inp.tau > 0).any())
     out = {
         "metric": METRIC, "value": round(rounds_s, 2), "unit": "rounds/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": cfg.dtype, "data": "synthetic (seeded random-init weights and inputs)",
         "config": {"workload": _workload_desc(cfg), "global_batch": cfg.B,
-                   "candidates": cfg.K, "verify": cfg.verify, "parallelism": "single GPU",
-                   "submission": "one HIP graph per round" if args.graph else "six calls per round"},
+                   "candidates": cfg.K, "verify": "greedy" if greedy else cfg.verify,
+                   "parallelism": "single GPU",
+                   "submission": "one HIP graph per round" if args.graph else
+                   f"{n_calls} calls per round"},
+        "pre_rounds": pre_rounds,
         "accepted_tokens_per_s": round(rounds_s * committed, 1),
         "committed_tokens_per_round": committed,
-        "phases_us": dict(zip(R.step_names, [round(x, 2) for x in per_call_us])),
+        "round_us_warm": _dist(warm_us),
+        "round_us_cold": dict(_dist(cold_us), note="each round after 512 MB of writes that "
+                              "evict the 256 MB last-level cache"),
+        "phases": phases,
         "roofline": roofline,
-        "cold_cache_round": {"us": round(flushed_us, 2), "rounds_per_s": round(1e6 / flushed_us, 2),
-                             "rounds": n_flush,
-                             "note": "median of single rounds, each after 512 MB of writes that "
-                                     "evict the 256 MB last-level cache"},
+        "host_cpu": host_cpu_model(),
     }
     if graph_ms_step is not None:
         out["eager_rounds_per_s"] = round(1000.0 / eager_ms_step, 2)
