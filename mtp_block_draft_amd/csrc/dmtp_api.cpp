@@ -72,6 +72,7 @@ int validate_fuse(const dmtp_fuse_desc* d) {
 }
 
 size_t fuse_ws(const dmtp_fuse_desc* d) {
+  if (fuse_fits(*d)) return al(fuse_fused_ws(*d));
   return al((size_t)d->rows * 2 * d->H * 4) +
          al(gemm_ws_bytes(d->rows, d->H, 2 * d->H, d->w_dtype == DMTP_F32));
 }
@@ -416,6 +417,9 @@ int dmtp_fuse(const dmtp_fuse_desc* d, void* ws, size_t ws_bytes, hipStream_t st
   CHECK(ws != nullptr, DMTP_E_NULL);
   CHECK(((uintptr_t)ws % kAlign) == 0, DMTP_E_ALIGN);
   if ((e = check_device()) != DMTP_OK) return e;
+  // at most 32 rows with bf16 weights: the norms are folded into the
+  // weight-streaming GEMM (two launches)
+  if (fuse_fits(*d)) return launch_status(fuse_fused(*d, ws, stream));
   uint16_t* cat = (uint16_t*)ws;   // bf16 planes [2][rows][2H]
   float* part = (float*)((char*)ws + al((size_t)d->rows * 2 * d->H * 4));
   hipError_t h = fuse_prep(*d, cat, stream);

@@ -388,85 +388,80 @@ constexpr int kSkCopies = kSkStage * 2 / 1024;   // 1 KB copies per stage
 constexpr int kSkRed = kSkStream * 16 * kWave;   // floats of one set of partial tiles
 constexpr size_t kSkLds = (size_t)kSkStream * kSkNB * kSkStage * 2 + 2 * (size_t)kSkRed * 4;
 constexpr int kSkGrid = 256;
+constexpr int kSkMaxSplits = 32;                 // fused projection: 2 H <= 16384
+
+__device__ __forceinline__ void add4f(float4& s, const float4& v) {
+  s.x += v.x;
+  s.y += v.y;
+  s.z += v.z;
+  s.w += v.w;
+}
 
 // Position of 16-byte chunk c of row r in a [32][128] stage (an involution):
 // the 16 lanes of one read pass land on the 16 positions of the bank window.
 __device__ __forceinline__ int sk_swz(int r, int c) { return c ^ (r & 15); }
 
-// blockIdx.x = z per_split + j: split z, run j of the n_tiles weight tiles.
+// The stream waves' part of a skinny workgroup once their activation
+// registers xf hold k0 .. k0 + 127 of the rows: copy each tile's 32 x 128
+// weight piece through the wave's own ring, multiply, and hand the partial
+// tile to the sum wave through LDS.
 template <int AP>
-__global__ __launch_bounds__(kSkThreads) void gemm_skinny_kernel(GemmParams p, int n_tiles, int per_split) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  static_assert(kSkCopies * (kSkNB - 2) < 64, "vmcnt");
+__device__ __forceinline__ void skinny_stream(const GemmParams& p, const u32x4 (&xf)[AP][kSkBK / 16],
+                                              int k0, int t0, int my, int lane, int wave,
+                                              uint16_t* smem, float* red) {
   constexpr int KPS = kSkBK / 16;                // k-steps per stage
-  float* red = (float*)(smem + kSkStream * kSkNB * kSkStage);   // [2][stream wave][16][64]
-  const int z = blockIdx.x / per_split, j = blockIdx.x % per_split;
-  const int my = n_tiles / per_split + (j < n_tiles % per_split ? 1 : 0);
-  const int t0 = j * (n_tiles / per_split) + min(j, n_tiles % per_split);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 31, lk = lane >> 5;
+  const int N = p.N;
+  const uint16_t* __restrict__ W = (const uint16_t*)p.B;
+  const uint16_t* __restrict__ W2 = (const uint16_t*)p.B2;
+  uint16_t* ring = smem + wave * kSkNB * kSkStage;
+  // tile q of the run: weight rows 32 (t0 + q) .. + 31; copy i covers rows
+  // 4 i .. 4 i + 3 (lane / 16), chunk position lane % 16
+  auto issue = [&](int q) __attribute__((always_inline)) {
+    const int n0 = 32 * (t0 + q);
+    uint16_t* st = ring + (q % kSkNB) * kSkStage;
+#pragma unroll
+    for (int i = 0; i < kSkCopies; ++i) {
+      const int r = 4 * i + (lane >> 4);
+      const int n = min(n0 + r, N - 1);
+      const uint16_t* wrow = (W2 && n >= p.N1) ? W2 + (size_t)(n - p.N1) * p.ldb : W + (size_t)n * p.ldb;
+      lds_dma16(wrow + k0 + 8 * sk_swz(r, lane & 15), st + 512 * i);
+    }
+  };
+  for (int q = 0; q < kSkNB - 1 && q < my; ++q) issue(q);
+  for (int tile = 0; tile < my; ++tile) {
+    // tile has landed once only the copies issued after it may be
+    // outstanding; lgkmcnt(0) too, since the stage refilled below was read
+    // just before
+    wait_vm_dyn<kSkCopies * (kSkNB - 2)>(kSkCopies * min(my - 1 - tile, kSkNB - 2));
+    const uint16_t* st = ring + (tile % kSkNB) * kSkStage;
+    u32x4 wf[KPS];
+#pragma unroll
+    for (int jj = 0; jj < KPS; ++jj) wf[jj] = *(const u32x4*)(st + lr * kSkBK + 8 * sk_swz(lr, 2 * jj + lk));
+    f32x16_t acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < KPS; ++jj)
+#pragma unroll
+      for (int pl = 0; pl < AP; ++pl) acc = mfma32(wf[jj], xf[pl][jj], acc);
+    if (tile + kSkNB - 1 < my) issue(tile + kSkNB - 1);
+    float* rb = red + (size_t)(tile & 1) * kSkRed + wave * 16 * kWave;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) rb[i * kWave + lane] = acc[i];
+    // the partial tile is in LDS before the barrier; the copies stay in flight
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0) only
+    ring_barrier();
+  }
+}
+
+// The sum wave: lane (lr, lk) holds activation row lr and output columns
+// 32 t + 8 (i / 4) + 4 lk + (i % 4), i = 0 .. 15, of tile t; it adds the four
+// partial tiles in wave order and stores split z of the partials.
+__device__ __forceinline__ void skinny_sum(const GemmParams& p, int z, int t0, int my, int lane,
+                                           float* red) {
   const int lr = lane & 31, lk = lane >> 5;
   const int M = p.M, N = p.N;
-  if (my == 0) return;   // the whole workgroup, before any barrier
-
-  if (wave < kSkStream) {
-    const uint16_t* __restrict__ W = (const uint16_t*)p.B;
-    const uint16_t* __restrict__ W2 = (const uint16_t*)p.B2;
-    const uint16_t* __restrict__ A = (const uint16_t*)p.A;
-    const int k0 = z * kSkRange + wave * kSkBK;
-    // MFMA B operands of the range: activation row lr (rows past M repeat row
-    // M - 1; their results are never stored), k = k0 + 16 j + 8 lk ..
-    u32x4 xf[AP][KPS];
-    const uint16_t* xr = A + (size_t)min(lr, M - 1) * p.lda + k0 + 8 * lk;
-#pragma unroll
-    for (int pl = 0; pl < AP; ++pl)
-#pragma unroll
-      for (int jj = 0; jj < KPS; ++jj) xf[pl][jj] = *(const u32x4*)(xr + pl * p.a_pst + 16 * jj);
-    // complete before the first copy, so no later wait for them drains the ring
-    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
-    uint16_t* ring = smem + wave * kSkNB * kSkStage;
-    // tile q of the run: weight rows 32 (t0 + q) .. + 31; copy i covers rows
-    // 4 i .. 4 i + 3 (lane / 16), chunk position lane % 16
-    auto issue = [&](int q) __attribute__((always_inline)) {
-      const int n0 = 32 * (t0 + q);
-      uint16_t* st = ring + (q % kSkNB) * kSkStage;
-#pragma unroll
-      for (int i = 0; i < kSkCopies; ++i) {
-        const int r = 4 * i + (lane >> 4);
-        const int n = min(n0 + r, N - 1);
-        const uint16_t* wrow = (W2 && n >= p.N1) ? W2 + (size_t)(n - p.N1) * p.ldb : W + (size_t)n * p.ldb;
-        lds_dma16(wrow + k0 + 8 * sk_swz(r, lane & 15), st + 512 * i);
-      }
-    };
-    for (int q = 0; q < kSkNB - 1 && q < my; ++q) issue(q);
-    for (int tile = 0; tile < my; ++tile) {
-      // tile has landed once only the copies issued after it may be
-      // outstanding; lgkmcnt(0) too, since the stage refilled below was read
-      // just before
-      wait_vm_dyn<kSkCopies * (kSkNB - 2)>(kSkCopies * min(my - 1 - tile, kSkNB - 2));
-      const uint16_t* st = ring + (tile % kSkNB) * kSkStage;
-      u32x4 wf[KPS];
-#pragma unroll
-      for (int jj = 0; jj < KPS; ++jj) wf[jj] = *(const u32x4*)(st + lr * kSkBK + 8 * sk_swz(lr, 2 * jj + lk));
-      f32x16_t acc;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-#pragma unroll
-      for (int jj = 0; jj < KPS; ++jj)
-#pragma unroll
-        for (int pl = 0; pl < AP; ++pl) acc = mfma32(wf[jj], xf[pl][jj], acc);
-      if (tile + kSkNB - 1 < my) issue(tile + kSkNB - 1);
-      float* rb = red + (size_t)(tile & 1) * kSkRed + wave * 16 * kWave;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) rb[i * kWave + lane] = acc[i];
-      // the partial tile is in LDS before the barrier; the copies stay in flight
-      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0) only
-      ring_barrier();
-    }
-    return;
-  }
-
-  // sum wave: lane (lr, lk) holds activation row lr and output columns
-  // 32 t + 8 (i / 4) + 4 lk + (i % 4), i = 0 .. 15, of tile t
   for (int tile = 0; tile < my; ++tile) {
     ring_barrier();
     const int n0 = 32 * (t0 + tile);
@@ -488,6 +483,211 @@ __global__ __launch_bounds__(kSkThreads) void gemm_skinny_kernel(GemmParams p, i
       }
     }
   }
+}
+
+// blockIdx.x = z per_split + j: split z, run j of the n_tiles weight tiles.
+template <int AP>
+__global__ __launch_bounds__(kSkThreads) void gemm_skinny_kernel(GemmParams p, int n_tiles, int per_split) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  static_assert(kSkCopies * (kSkNB - 2) < 64, "vmcnt");
+  constexpr int KPS = kSkBK / 16;
+  float* red = (float*)(smem + kSkStream * kSkNB * kSkStage);   // [2][stream wave][16][64]
+  const int z = blockIdx.x / per_split, j = blockIdx.x % per_split;
+  const int my = n_tiles / per_split + (j < n_tiles % per_split ? 1 : 0);
+  const int t0 = j * (n_tiles / per_split) + min(j, n_tiles % per_split);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 31, lk = lane >> 5;
+  if (my == 0) return;   // the whole workgroup, before any barrier
+
+  if (wave < kSkStream) {
+    const uint16_t* __restrict__ A = (const uint16_t*)p.A;
+    const int k0 = z * kSkRange + wave * kSkBK;
+    // MFMA B operands of the range: activation row lr (rows past M repeat row
+    // M - 1; their results are never stored), k = k0 + 16 j + 8 lk ..
+    u32x4 xf[AP][KPS];
+    const uint16_t* xr = A + (size_t)min(lr, p.M - 1) * p.lda + k0 + 8 * lk;
+#pragma unroll
+    for (int pl = 0; pl < AP; ++pl)
+#pragma unroll
+      for (int jj = 0; jj < KPS; ++jj) xf[pl][jj] = *(const u32x4*)(xr + pl * p.a_pst + 16 * jj);
+    // complete before the first copy, so no later wait for them drains the ring
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+    skinny_stream<AP>(p, xf, k0, t0, my, lane, wave, smem, red);
+    return;
+  }
+  skinny_sum(p, z, t0, my, lane, red);
+}
+
+// ------------------------------------- fused RMSNorm-concat projection ----
+// out[r] = res[r] + W [RMSNorm(x1[r]; g1); RMSNorm(x2[r]; g2)] for at most 32
+// rows, in two launches.  A row's RMSNorm is its gain-weighted row divided by
+// one scalar, so
+//     W [RMSNorm(x1; g1); RMSNorm(x2; g2)]
+//         = (W1 (x1 * g1)) / rms(x1) + (W2 (x2 * g2)) / rms(x2),
+// W1 / W2 the columns acting on each stream.  fuse_skinny_kernel is the
+// weight-streaming GEMM above whose stream waves load their k-range of the
+// raw rows (rows or embedding ids), multiply by the gains and split the
+// products into the two bf16 planes in registers -- no normalised copy of the
+// rows is written -- and also store the range's sum of squares of the raw
+// rows.  Each split range lies in one stream (H % 512 == 0).  fuse_finish_kernel
+// then adds the partials of each stream in split order, scales each sum by
+// that stream's 1 / rms, and adds the residual.
+struct FuseSrc {
+  const void* rows[2];       // stream rows [M, H] (NULL: gathered by ids)
+  int dtype[2];              // of the rows, or of the table they are gathered from
+  const int32_t* ids[2];
+  const void* table[2];      // [n_table, H]
+  int n_table[2];
+  const float* g[2];
+  int H;
+  float* ssp;                // [splits * kSkStream][M] sums of squares per wave range
+};
+
+// Elements k .. k + 7 of row r of stream s as float (zero for an id outside
+// the table).
+__device__ __forceinline__ void fuse_load8(const FuseSrc& f, int s, int r, int k, float (&x)[8]) {
+  const void* base;
+  int dt;
+  size_t off;
+  if (f.rows[s]) {
+    base = f.rows[s];
+    dt = f.dtype[s];
+    off = (size_t)r * f.H + k;
+  } else {
+    const int id = f.ids[s][r];
+    if (id < 0 || id >= f.n_table[s]) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = 0.f;
+      return;
+    }
+    base = f.table[s];
+    dt = f.dtype[s];
+    off = (size_t)id * f.H + k;
+  }
+  if (dt == DMTP_BF16) {
+    const uint4 u = *(const uint4*)((const uint16_t*)base + off);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = __uint_as_float(w[e] << 16);
+      x[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+    }
+  } else {
+    const float4 a = *(const float4*)((const float*)base + off);
+    const float4 b = *(const float4*)((const float*)base + off + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+}
+
+__global__ __launch_bounds__(kSkThreads) void fuse_skinny_kernel(GemmParams p, FuseSrc f, int n_tiles,
+                                                                 int per_split) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  constexpr int KPS = kSkBK / 16;
+  float* red = (float*)(smem + kSkStream * kSkNB * kSkStage);
+  const int z = blockIdx.x / per_split, j = blockIdx.x % per_split;
+  const int my = n_tiles / per_split + (j < n_tiles % per_split ? 1 : 0);
+  const int t0 = j * (n_tiles / per_split) + min(j, n_tiles % per_split);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 31, lk = lane >> 5;
+  if (my == 0) return;
+
+  if (wave < kSkStream) {
+    const int k0 = z * kSkRange + wave * kSkBK;     // in the concatenated [x1 | x2]
+    const int s = k0 >= f.H ? 1 : 0;
+    const int kk = k0 - s * f.H + 8 * lk;
+    const int r = min(lr, p.M - 1);
+    // all loads first, then the arithmetic: one memory latency
+    float x[KPS][8];
+    float4 g[KPS][2];
+#pragma unroll
+    for (int jj = 0; jj < KPS; ++jj) {
+      fuse_load8(f, s, r, kk + 16 * jj, x[jj]);
+      g[jj][0] = *(const float4*)(f.g[s] + kk + 16 * jj);
+      g[jj][1] = *(const float4*)(f.g[s] + kk + 16 * jj + 4);
+    }
+    u32x4 xf[2][KPS];
+    float ss = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < KPS; ++jj) {
+      const float gg[8] = {g[jj][0].x, g[jj][0].y, g[jj][0].z, g[jj][0].w,
+                           g[jj][1].x, g[jj][1].y, g[jj][1].z, g[jj][1].w};
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ss = fmaf(x[jj][2 * e], x[jj][2 * e], ss);
+        ss = fmaf(x[jj][2 * e + 1], x[jj][2 * e + 1], ss);
+        split2(x[jj][2 * e] * gg[2 * e], x[jj][2 * e + 1] * gg[2 * e + 1], hi[e], lo[e]);
+      }
+      xf[0][jj] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+      xf[1][jj] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+    }
+    // the row's sum of squares over this wave's 128 k (lanes lk = 0, 1 hold
+    // its two halves); one workgroup per split writes it
+    ss += shfl_xor(ss, 32);
+    if (j == 0 && lk == 0 && lr < p.M) f.ssp[(size_t)(z * kSkStream + wave) * p.M + lr] = ss;
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+    skinny_stream<2>(p, xf, k0, t0, my, lane, wave, smem, red);
+    return;
+  }
+  skinny_sum(p, z, t0, my, lane, red);
+}
+
+// out[m, n .. n+3] = res + (sum_{z < z1} part[z]) / rms1 + (sum_{z >= z1} part[z]) / rms2,
+// rms_s = sqrt(sum of the stream's squares / H + eps).  One workgroup of 256
+// threads per (row, 1024 columns); wave 0 turns the per-wave sums of squares
+// into the two scales.
+__global__ __launch_bounds__(256) void fuse_finish_kernel(const float* __restrict__ part, int splits,
+                                                          int z1, const float* __restrict__ ssp,
+                                                          int M, int H, float eps, FuseSrc res,
+                                                          int has_res, float* __restrict__ out) {
+  __shared__ float scale[2];
+  const int m = blockIdx.y;
+  const int n = 4 * (blockIdx.x * 256 + threadIdx.x);
+  const size_t plane = (size_t)M * H;
+  // issue the partial loads before the scales are known
+  float4 v[kSkMaxSplits];
+#pragma unroll
+  for (int z = 0; z < kSkMaxSplits; ++z)
+    if (z < splits && n < H) v[z] = *(const float4*)(part + z * plane + (size_t)m * H + n);
+  float4 rv = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (has_res && n < H) {
+    float x[8];
+    fuse_load8(res, 0, m, n & ~7, x);
+    const int o = n & 7;
+    rv = make_float4(x[o], x[o + 1], x[o + 2], x[o + 3]);
+  }
+  if (threadIdx.x < kWave) {
+    const int nw = splits * kSkStream, w1 = z1 * kSkStream;
+    double a = 0.0, b = 0.0;
+    for (int i = threadIdx.x; i < nw; i += kWave) {
+      const double q = ssp[(size_t)i * M + m];
+      if (i < w1) a += q;
+      else b += q;
+    }
+    a = wave_sum(a);
+    b = wave_sum(b);
+    if (threadIdx.x == 0) {
+      scale[0] = (float)(1.0 / sqrt(a / H + (double)eps));
+      scale[1] = (float)(1.0 / sqrt(b / H + (double)eps));
+    }
+  }
+  __syncthreads();
+  if (n >= H) return;
+  // each stream's partials in split order (register indices fixed at compile time)
+  float4 s1 = make_float4(0.f, 0.f, 0.f, 0.f), s2 = s1;
+#pragma unroll
+  for (int z = 0; z < kSkMaxSplits; ++z) {
+    if (z < z1) add4f(s1, v[z]);
+    else if (z < splits) add4f(s2, v[z]);
+  }
+  const float c1 = scale[0], c2 = scale[1];
+  float4 y;
+  y.x = rv.x + (s1.x * c1 + s2.x * c2);
+  y.y = rv.y + (s1.y * c1 + s2.y * c2);
+  y.z = rv.z + (s1.z * c1 + s2.z * c2);
+  y.w = rv.w + (s1.w * c1 + s2.w * c2);
+  *(float4*)(out + (size_t)m * H + n) = y;
 }
 
 // Calls of at most 32 rows whose K is a multiple of the split range, with
@@ -592,6 +792,63 @@ hipError_t gemm(const GemmArgs& a, float* ws, hipStream_t s) {
   dim3 grid((a.N + TilePlanesF32::BN - 1) / TilePlanesF32::BN,
             (a.M + TilePlanesF32::BM - 1) / TilePlanesF32::BM);
   hipLaunchKernelGGL(gemm_kernel<TilePlanesF32>, grid, dim3(TilePlanesF32::THREADS), 0, s, p);
+  return hipGetLastError();
+}
+
+
+bool fuse_fits(const dmtp_fuse_desc& d) {
+  const int K = 2 * d.H;
+  return d.w_dtype == DMTP_BF16 && d.rows <= 32 && d.H % kSkRange == 0 && skinny_fits(d.rows, K) &&
+         K / kSkRange <= kSkMaxSplits;
+}
+
+size_t fuse_fused_ws(const dmtp_fuse_desc& d) {
+  const int splits = 2 * d.H / kSkRange;
+  const size_t part = (size_t)splits * d.rows * d.H * sizeof(float);
+  return ((part + 255) & ~(size_t)255) + (size_t)splits * kSkStream * d.rows * sizeof(float);
+}
+
+namespace {
+FuseSrc fuse_src_of(const dmtp_rows& a, const dmtp_rows& b, int w_dtype) {
+  FuseSrc f{};
+  const dmtp_rows* r[2] = {&a, &b};
+  for (int s = 0; s < 2; ++s) {
+    f.rows[s] = r[s]->rows;
+    f.dtype[s] = r[s]->rows ? r[s]->dtype : w_dtype;
+    f.ids[s] = r[s]->ids;
+    f.table[s] = r[s]->table;
+    f.n_table[s] = r[s]->table_rows;
+  }
+  return f;
+}
+}  // namespace
+
+hipError_t fuse_fused(const dmtp_fuse_desc& d, void* ws, hipStream_t s) {
+  const int K = 2 * d.H, splits = K / kSkRange;
+  float* part = (float*)ws;
+  const size_t part_bytes = (size_t)splits * d.rows * d.H * sizeof(float);
+  float* ssp = (float*)((char*)ws + ((part_bytes + 255) & ~(size_t)255));
+  FuseSrc f = fuse_src_of(d.x1, d.x2, d.w_dtype);
+  f.g[0] = d.g1;
+  f.g[1] = d.g2;
+  f.H = d.H;
+  f.ssp = ssp;
+  GemmParams p{nullptr, 0, 0, d.rows, d.W, (size_t)K, d.H, K, splits, nullptr, 0, nullptr, 0, part,
+               nullptr, d.H};
+  const int n_tiles = (d.H + 31) / 32;
+  int per = kSkGrid / splits;
+  per = per < 1 ? 1 : (per > n_tiles ? n_tiles : per);
+  hipError_t e = hipFuncSetAttribute((const void*)fuse_skinny_kernel,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSkLds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fuse_skinny_kernel, dim3(splits * per), dim3(kSkThreads), kSkLds, s, p, f,
+                     n_tiles, per);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const bool has_res = d.res.rows || d.res.ids;
+  FuseSrc r = fuse_src_of(d.res, d.res, d.w_dtype);
+  r.H = d.H;
+  hipLaunchKernelGGL(fuse_finish_kernel, dim3((d.H + 1023) / 1024, d.rows), dim3(256), 0, s, part,
+                     splits, splits / 2, ssp, d.rows, d.H, d.eps, r, has_res ? 1 : 0, d.out);
   return hipGetLastError();
 }
 

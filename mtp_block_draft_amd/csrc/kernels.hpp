@@ -54,6 +54,14 @@ SplitOut split_out_plain(const float* C, size_t ldc, int M, int N);
 // The GEMM without its reduction pass: the reader of *out adds the partials.
 hipError_t gemm_deferred(const GemmArgs& a, float* ws, hipStream_t s, SplitOut* out);
 
+// The fusion projection out = res + W [RMSNorm(x1; g1); RMSNorm(x2; g2)] as
+// one weight-streaming GEMM with the norms folded in, plus a pass that adds
+// its split-K partials with each stream's 1 / rms and the residual.  For bf16
+// weights, at most 32 rows and H a multiple of 512 (up to 8192).
+bool fuse_fits(const dmtp_fuse_desc& d);
+size_t fuse_fused_ws(const dmtp_fuse_desc& d);
+hipError_t fuse_fused(const dmtp_fuse_desc& d, void* ws, hipStream_t s);
+
 // -------------------------------------------------------------- elementwise --
 // X[r] = value(r) (when write_x; the residual stream update) and y[r] =
 // RMSNorm(value(r); g) as bf16 planes [2][rows][H], for the rows of x.

@@ -66,6 +66,39 @@ def test_fuse(dm, dt, rows, H, residual):
     assert err < 1e-5
 
 
+@pytest.mark.parametrize("rows,H", [(32, 2048), (7, 512), (1, 4096), (8, 5120), (33, 1024)])
+def test_fuse_residual_layout(dm, rows, H):
+    """The DMTP residual's operand layout: x1 = ids of T1, x2 = float32 MTP rows,
+    res = ids of T1, bf16 weights.  Rows <= 32 with H a multiple of 512 run the
+    projection with the norms folded in; 33 rows take the prologue path.  Two
+    ids fall outside the table and read zero rows."""
+    print(f"fuse residual layout rows={rows} H={H}", flush=True)
+    r = np.random.default_rng(rows * 13 + H)
+    V = 257
+    emb = _store(0.02 * r.standard_normal((V, H)), "bf16")
+    ids = r.integers(0, V, size=rows).astype(np.int32)
+    if rows > 2:
+        ids[1], ids[rows - 1] = -3, V + 5
+    x2 = r.standard_normal((rows, H)).astype(np.float32)
+    g1 = (1 + 0.1 * r.standard_normal(H)).astype(np.float32)
+    g2 = (1 + 0.1 * r.standard_normal(H)).astype(np.float32)
+    W = _store(0.02 * r.standard_normal((H, 2 * H)), "bf16")
+    out = torch.empty(rows, H, dtype=torch.float32, device="cuda")
+    I = _t(ids, torch.int32)
+    dm.fuse(out, _t(W, torch.bfloat16), _t(g1, torch.float32), _t(g2, torch.float32), x1_ids=I,
+            x2=_t(x2, torch.float32), res_ids=I, table=_t(emb, torch.bfloat16), eps=1e-6)
+    e_rows = np.where(((ids >= 0) & (ids < V))[:, None], emb[np.clip(ids, 0, V - 1)], 0.0)
+    want = odm.fuse(e_rows, x2, g1, g2, W, 1e-6, res=e_rows)
+    got = out.cpu().numpy()
+    err = max_rel(got, want)
+    print("  max rel", err)
+    assert err < 1e-5
+    # a row of the zero embedding normalises to zero: its x1 stream adds nothing
+    if rows > 2:
+        only_h = odm.fuse(np.zeros((1, H)), x2[1:2], g1, g2, W, 1e-6)
+        assert max_rel(got[1:2], only_h) < 1e-5
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_fuse_zero_projection_is_bitwise_residual(dm, dt):
     r = np.random.default_rng(5)
