@@ -11,6 +11,7 @@
  * summary of acceptance over rounds complete the set:
  *
  *   dmtp_fuse         RMSNorm-concat-projection (MTP input fusion; DMTP residual)
+ *   dmtp_fuse_noalloc the same without a caller workspace (static scratch)
  *   dmtp_mtp_block    the MTP decoder block (causal, with its own KV cache)
  *   dmtp_ctx_kv       the drafter's context K/V rows from target features
  *   dmtp_block_draft  the block drafter's layers and final norm
@@ -37,7 +38,8 @@
  *     are refused, never silently degraded.
  *   - The library holds no state across calls and is safe to call from
  *     several host threads on different streams; calls that share output or
- *     workspace buffers must be ordered by the caller.
+ *     workspace buffers must be ordered by the caller.  The one exception is
+ *     dmtp_fuse_noalloc, whose scratch is a static array per GPU.
  */
 #ifndef DMTP_H
 #define DMTP_H
@@ -62,7 +64,8 @@ enum dmtp_status {
   DMTP_E_ALIGN = -5,     /* a pointer is not 16-byte aligned */
   DMTP_E_DEVICE = -6,    /* the current device is not gfx950 */
   DMTP_E_LAUNCH = -7,    /* a kernel launch failed */
-  DMTP_E_ARG = -8        /* an inconsistent combination of arguments */
+  DMTP_E_ARG = -8,       /* an inconsistent combination of arguments */
+  DMTP_E_SCRATCH = -9    /* the call needs more than the static scratch buffer holds */
 };
 
 enum dmtp_dtype { DMTP_F32 = 0, DMTP_BF16 = 1 };
@@ -106,6 +109,27 @@ typedef struct {
 
 size_t dmtp_fuse_ws(const dmtp_fuse_desc* d);
 int dmtp_fuse(const dmtp_fuse_desc* d, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------ fuse without an allocation ----
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Computes
+ * exactly what dmtp_fuse computes, with the same kernels, but takes no
+ * workspace: its scratch (the split-K partials and sums of squares, or the
+ * normalised rows) lives in a static device array of DMTP_SCRATCH_BYTES inside
+ * the library, one per GPU, held until the process ends.  The caller still
+ * owns the input and output buffers.
+ *   - Returns DMTP_E_SCRATCH, before anything is enqueued, when the call
+ *     would need more than DMTP_SCRATCH_BYTES (dmtp_fuse_ws(d) is that need).
+ *   - Allocates nothing: no hipMalloc / hipFree on any call.  The first call
+ *     on a device looks up that device's copy of the array.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents; nothing in it has to start at zero (every call writes
+ *     all the scratch it reads).  Calls that overlap on one GPU -- on
+ *     different streams, or from different host threads -- race on it: the
+ *     caller must order them.
+ * Other errors are those of dmtp_fuse. */
+#define DMTP_SCRATCH_BYTES ((size_t)16 << 20)
+int dmtp_fuse_noalloc(const dmtp_fuse_desc* d, hipStream_t stream);
 
 /* ---------------------------------------------------------- block draft ----
  * The block drafter ("DFlash vs MTP", "DFlash: Block Diffusion as a Draft

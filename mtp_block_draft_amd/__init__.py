@@ -19,7 +19,7 @@ from ._abi import (DMTP_BF16, DMTP_F32, DMTP_NO_DRAW, DmtpError, DraftDesc, Fuse
 
 lib = _abi.load()
 
-__all__ = ["lib", "fuse", "mtp_block", "ctx_kv", "block_draft", "lm_head", "verify", "accept_stats", "call",
+__all__ = ["lib", "fuse", "fuse_noalloc", "mtp_block", "ctx_kv", "block_draft", "lm_head", "verify", "accept_stats", "call",
            "workspace_bytes",
            "DMTP_F32", "DMTP_BF16", "DMTP_NO_DRAW", "DmtpError", "version"]
 
@@ -99,6 +99,15 @@ def fuse(out: torch.Tensor, W: torch.Tensor, g1: torch.Tensor, g2: torch.Tensor,
     if run:
         call("fuse", d, ws)
     return d
+
+
+def fuse_noalloc(desc: FuseDesc, stream: Optional[int] = None) -> None:
+    """dmtp_fuse_noalloc on a prepared fuse descriptor (no workspace: the
+    library's static scratch)."""
+    st = lib.dmtp_fuse_noalloc(ctypes.byref(desc),
+                               ctypes.c_void_p(_stream() if stream is None else stream))
+    if st != 0:
+        raise DmtpError("dmtp_fuse_noalloc", st, lib.dmtp_status_str(st).decode())
 
 
 def layer_arg(g_attn, wqkv, wo, g_ffn, wg, wu, wd, ctx_k, ctx_v) -> Layer:

@@ -19,7 +19,7 @@ DMTP_NO_DRAW = 0xFFFFFFFFFFFFFFFF
 STATUS = {
     0: "DMTP_OK", -1: "DMTP_E_NULL", -2: "DMTP_E_SHAPE", -3: "DMTP_E_DTYPE",
     -4: "DMTP_E_WORKSPACE", -5: "DMTP_E_ALIGN", -6: "DMTP_E_DEVICE", -7: "DMTP_E_LAUNCH",
-    -8: "DMTP_E_ARG",
+    -8: "DMTP_E_ARG", -9: "DMTP_E_SCRATCH",
 }
 
 
@@ -101,7 +101,7 @@ _STRUCTS = [Rows, FuseDesc, Layer, DraftDesc, HeadSegment, HeadDesc, VerifyDesc,
             MtpDesc, CtxDesc]
 
 # exported symbols of include/dmtp.h
-SYMBOLS = ["dmtp_fuse", "dmtp_fuse_ws", "dmtp_mtp_block", "dmtp_mtp_block_ws", "dmtp_ctx_kv",
+SYMBOLS = ["dmtp_fuse", "dmtp_fuse_ws", "dmtp_fuse_noalloc", "dmtp_mtp_block", "dmtp_mtp_block_ws", "dmtp_ctx_kv",
            "dmtp_ctx_kv_ws", "dmtp_block_draft",
            "dmtp_block_draft_ws", "dmtp_lm_head",
            "dmtp_lm_head_ws", "dmtp_verify", "dmtp_verify_ws", "dmtp_accept_stats",
@@ -128,6 +128,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         q = getattr(lib, name + "_ws")
         q.argtypes = [POINTER(desc)]
         q.restype = c_size_t
+    lib.dmtp_fuse_noalloc.argtypes = [POINTER(FuseDesc), c_void_p]
+    lib.dmtp_fuse_noalloc.restype = c_int
     lib.dmtp_accept_stats.argtypes = [POINTER(StatsDesc), c_void_p]
     lib.dmtp_accept_stats.restype = c_int
     lib.dmtp_status_str.argtypes = [c_int]

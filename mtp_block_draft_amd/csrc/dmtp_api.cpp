@@ -4,6 +4,7 @@
 
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include "dmtp.h"
 #include "kernels.hpp"
@@ -400,6 +401,33 @@ int validate_stats(const dmtp_stats_desc* d) {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? DMTP_OK : DMTP_E_LAUNCH; }
 
+// ----------------------------------------------- static scratch buffer ----
+// The workspace of dmtp_fuse_noalloc: one array per GPU (each device holds its
+// own copy at its own address).  In host code `scratch` names a host-side
+// stand-in, never the device memory: every use goes through the device
+// address looked up once per device below.
+static __device__ __align__(256) unsigned char scratch[DMTP_SCRATCH_BYTES];
+
+std::atomic<void*> g_scratch_ptr[64];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch array, or nullptr.
+void* scratch_ptr() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr) return nullptr;
+    g_scratch_ptr[dev].store(q, std::memory_order_release);
+    p = q;
+  }
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -429,6 +457,16 @@ int dmtp_fuse(const dmtp_fuse_desc* d, void* ws, size_t ws_bytes, hipStream_t st
              d->w_dtype == DMTP_F32, (size_t)2 * d->H, d->H, 2 * d->H, d->out, (size_t)d->H,
              has_res ? d->out : nullptr, (size_t)d->H};
   return launch_status(gemm(g, part, stream));
+}
+
+int dmtp_fuse_noalloc(const dmtp_fuse_desc* d, hipStream_t stream) {
+  int e = validate_fuse(d);
+  if (e != DMTP_OK) return e;
+  if (fuse_ws(d) > DMTP_SCRATCH_BYTES) return DMTP_E_SCRATCH;
+  if ((e = check_device()) != DMTP_OK) return e;
+  void* ws = scratch_ptr();
+  if (ws == nullptr) return DMTP_E_DEVICE;
+  return dmtp_fuse(d, ws, DMTP_SCRATCH_BYTES, stream);
 }
 
 size_t dmtp_block_draft_ws(const dmtp_draft_desc* d) {
@@ -589,6 +627,7 @@ const char* dmtp_status_str(int s) {
     case DMTP_E_DEVICE: return "current device is not gfx950";
     case DMTP_E_LAUNCH: return "kernel launch failed";
     case DMTP_E_ARG: return "inconsistent arguments";
+    case DMTP_E_SCRATCH: return "needs more scratch than the library's static buffer holds";
     default: return "unknown status";
   }
 }

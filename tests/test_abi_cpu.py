@@ -71,6 +71,17 @@ def test_fuse_argument_errors(lib):
     assert _call(lib, "dmtp_fuse", d, ws_bytes=need - 1) == -4
 
 
+def test_fuse_noalloc_refuses_a_call_beyond_its_static_scratch(lib):
+    # 32 rows of H = 16384 need about 138 MB of partials; the static array is 16 MiB.
+    d = _fuse_desc(rows=32, H=16384)
+    assert lib.dmtp_fuse_ws(ctypes.byref(d)) > (16 << 20)
+    assert lib.dmtp_fuse_noalloc(ctypes.byref(d), None) == -9
+    assert b"scratch" in lib.dmtp_status_str(-9)
+    # argument errors come first, as in dmtp_fuse
+    assert lib.dmtp_fuse_noalloc(None, None) == -1
+    assert lib.dmtp_fuse_noalloc(ctypes.byref(_fuse_desc(H=100)), None) == -2
+
+
 def _draft_desc(layers, **over):
     d = abi.DraftDesc()
     d.B, d.H, d.Hq, d.Hkv, d.d, d.F, d.n_layers, d.K, d.n_anchor = 2, 256, 4, 4, 64, 512, 1, 7, 2
