@@ -74,6 +74,9 @@ enum dmtp_dtype { DMTP_F32 = 0, DMTP_BF16 = 1 };
  * positive (its lse is still taken at that temperature). */
 #define DMTP_NO_DRAW 0xFFFFFFFFFFFFFFFFull
 
+/* Entries per block of the two-level draws of dmtp_lm_head and dmtp_verify. */
+#define DMTP_DRAW_BLOCK 128
+
 /* Rows of a fusion input: either `rows` [n, H] in `dtype` (row stride H), or,
  * when rows == NULL, the gather table[ids[r]] with table [V, H] in the call's
  * weight dtype.  A dmtp_rows with rows == NULL and ids == NULL is "absent". */
@@ -262,12 +265,18 @@ int dmtp_ctx_kv(const dmtp_ctx_desc* d, void* ws, size_t ws_bytes, hipStream_t s
  *   temperature[m] == 0 (or temperature == NULL): token = argmax (lowest
  *       index among equal maxima), gap = top-1 minus top-2 logit;
  *   temperature[m] > 0 and draw_key[m] != DMTP_NO_DRAW: token is a draw from
- *       softmax(logits / t) taken as
- *       argmax_j (logits_j / t + g_j), g the Gumbel noise of Philox4x64-10
- *       draw (seed, draw_key[m]) -- word j of counter (j >> 3, key, 0, 0)
- *       under key (seed, 0), 64-bit output (j & 7) >> 1, low half if j even;
- *       g = -log(-log1p(-(x + 1/2) 2^-32)).  gap = top-2 gap of that score.
- *       Such rows need store_row[m] >= 0 (else token = -1).
+ *       softmax(logits / t) in two levels: first the block b of
+ *       DMTP_DRAW_BLOCK consecutive entries that maximises log Z_b + g1_b
+ *       (Z_b the block's softmax mass), then the entry j of block b that
+ *       maximises logits_j / t + g0_j.  gL_i is the Gumbel noise of level L of
+ *       Philox4x64-10 draw (seed, draw_key[m]): word i of counter
+ *       (i >> 3, key, L, 0) under key (seed, 0), 64-bit output (i & 7) >> 1,
+ *       low half if i even; g = -log(-log1p(-(x + 1/2) 2^-32)).  The two
+ *       noises are independent, so j is drawn with probability softmax_j
+ *       (Gumbel-max identity, applied to the blocks and within the block).
+ *       gap = the smaller of the two levels' top-2 score gaps.  The block
+ *       masses come from one pass over the stored logits row, so such rows
+ *       need store_row[m] >= 0 (else token = -1).
  *   temperature[m] > 0 and draw_key[m] == DMTP_NO_DRAW: argmax, as greedy.
  *   row_max = max logit; lse = logsumexp(logits / t) (t = 1 when 0).
  *   store_row[m] >= 0 writes the float32 logits row to logits[store_row[m]].
@@ -339,8 +348,10 @@ int dmtp_lm_head(const dmtp_head_desc* d, void* ws, size_t ws_bytes, hipStream_t
  *       iff u_acc[b][i] < p_i(d_i) / q_i(d_i); at the first rejection i draw
  *       the correction from normalize(max(0, p_i - q_i)) (from p_i if that is
  *       zero); if all K are accepted draw the bonus from p_K.  Draws are
- *       Gumbel-max over Philox draw (seed, final_key[b]), the layout of
- *       dmtp_lm_head.  Needs the lse of every row (lse of logits / t).
+ *       the two-level Gumbel-max draws of dmtp_lm_head over these weights
+ *       (block masses of max(0, p_i - q_i) or of p, then an entry of the
+ *       chosen block), with draw (seed, final_key[b]).  Needs the lse of
+ *       every row (lse of logits / t).
  *   target_only != 0 (DMTP blog section 5, the note on target-only
  *       verification; colibri: a sampled pick equal to the next draft
  *       accepts it): every sequence, whatever its temperature, is verified

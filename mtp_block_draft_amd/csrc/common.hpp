@@ -171,14 +171,33 @@ __device__ __forceinline__ float log1m_exp(float d) {
   return hw_log2(om) * ln2;
 }
 
-// The eight 32-bit words of block (j >> 3) of draw (seed, key).
+// The eight 32-bit words of block (j >> 3) of noise level `level` of draw
+// (seed, key): counter (block, key, level, 0), key (seed, 0).  Level 0 noise
+// is indexed by vocabulary entry, level 1 by block of kDrawBlock entries.
 __device__ __forceinline__ void philox_words8(uint64_t seed, uint64_t key, uint64_t block,
-                                              uint32_t w[8]) {
-  const u64x4 o = philox4x64_10(u64x4{block, key, 0, 0}, seed, 0);
+                                              uint32_t w[8], uint64_t level = 0) {
+  const u64x4 o = philox4x64_10(u64x4{block, key, level, 0}, seed, 0);
   w[0] = (uint32_t)o.x; w[1] = (uint32_t)(o.x >> 32);
   w[2] = (uint32_t)o.y; w[3] = (uint32_t)(o.y >> 32);
   w[4] = (uint32_t)o.z; w[5] = (uint32_t)(o.z >> 32);
   w[6] = (uint32_t)o.w; w[7] = (uint32_t)(o.w >> 32);
+}
+
+// Entries per block of a two-level draw: a draw picks a block of kDrawBlock
+// consecutive vocabulary entries by Gumbel-max over the blocks' log masses
+// (level-1 noise), then an entry of that block by Gumbel-max over its log
+// weights (level-0 noise).  The two noises are independent, so the entry is
+// drawn with probability w_j / sum w, as by one Gumbel-max over all entries;
+// only the entries of the chosen block need noise, so a draw over a
+// vocabulary costs one memory-bound pass for the block masses.
+constexpr int kDrawBlock = 128;
+
+// 1 - e^d for d <= 0, accurate where the subtraction would cancel: the series
+// of -expm1(d) when |d| < 2^-6, directly otherwise (hardware exp2).
+__device__ __forceinline__ float one_minus_exp(float d) {
+  const float log2e = 1.4426950408889634f;
+  const float em = -d * fmaf(d, fmaf(d, fmaf(d, 1.f / 24.f, 1.f / 6.f), 0.5f), 1.f);
+  return d > -0x1p-6f ? em : 1.f - hw_exp2(d * log2e);
 }
 
 // ----------------------------------------------------- running maximum ----

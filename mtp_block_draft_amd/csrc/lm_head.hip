@@ -9,9 +9,12 @@
 //             as one 16-byte partial per (row, vocab tile); logits rows with a
 //             store index are written in float32
 //   merge     per row: exact merge of the partials -> max, lse, argmax, gap
-//   plan/scan (only when temperatures are given) Gumbel-max draws over the
-//             stored logits rows of sampled rows, in vocabulary chunks
-//   finalize  token per row: draw, planted row argmax, or argmax
+//   plan/mass (only when temperatures are given) the list of drawn rows, and
+//             one memory-bound pass over their stored logits rows giving the
+//             softmax mass of every block of kDrawBlock entries
+//   finalize  token per row: a two-level Gumbel-max draw (block by its mass,
+//             then an entry of that block), the planted row's argmax, or the
+//             argmax
 #include <algorithm>
 #include <type_traits>
 
@@ -96,8 +99,11 @@ struct HeadParams {
   int32_t* list;         // [M] sampled rows
   int32_t* list_pos;     // [M] position in list or -1
   int32_t* list_count;   // [1]
-  Top2* scan_part;       // [M, n_chunks]
-  int n_chunks;
+  float* rmax;           // [M] row max of the logits (the mass pass's reference)
+  float* mass;           // [M, n_blocks] block masses of drawn rows (list order)
+  int n_blocks;          // blocks of kDrawBlock entries
+  int block_stats;       // the GEMM's per-tile statistics are per block: they give the masses
+  int n_chunks;          // work items of the mass pass per row
   int32_t* token;
   float* row_max;
   float* lse;
@@ -827,6 +833,7 @@ __global__ __launch_bounds__(kMergeThreads) void head_merge_kernel(HeadParams p,
     for (int w = 1; w < kMergeThreads / kWave; ++w) st = stat_merge(st, red[w], it);
     p.amax[m] = st.idx;
     p.gap_greedy[m] = st.m - st.v2;
+    p.rmax[m] = st.m;
     if (p.row_max) p.row_max[m] = st.m;
     if (p.lse) p.lse[m] = st.m * it + logf(st.s);
     if (final_greedy) {
@@ -871,16 +878,24 @@ __global__ void head_plan_kernel(HeadParams p) {
   if (threadIdx.x == 0) p.list_count[0] = base;
 }
 
-// Gumbel-max scan.  A work item is (list index, vocabulary chunk of kScanChunk
-// entries) and belongs to one wave: lane l takes the 8-entry blocks
-// l, l + 64, ... of the chunk (kScanU of them), issues all of their loads
-// first, then the Philox words of each block, score_j = l_j / t + g_j and a
-// running top-2 in increasing j; one butterfly merge per item gives the
-// chunk's partial.  Waves stride over the items, so the grid is sized to the
-// machine, not to the batch.
-constexpr int kScanWaves = 4;
-constexpr int kScanU = 4;
-constexpr int kScanChunk = kWave * 8 * kScanU;   // 2048 vocabulary entries per item
+// Block masses of the drawn rows.  A work item is (list index, chunk of
+// kMassChunk entries) and belongs to one wave: lane l takes the 8-entry groups
+// l, l + 64, ... of the chunk (kMassU of them) and loads them all before any
+// arithmetic.  Group u of lanes 16 q .. 16 q + 15 covers one block of
+// kDrawBlock entries; its mass sum exp((l_j - max) / t) is added lane by lane
+// and then over the 16 lanes in a fixed order.  One exp2 per entry: the pass
+// is bound by the read of the logits.
+#ifndef DMTP_MASS_U
+#define DMTP_MASS_U 4
+#endif
+#ifndef DMTP_MASS_GRID
+#define DMTP_MASS_GRID 8192
+#endif
+constexpr int kMassWaves = 4;
+constexpr int kMassU = DMTP_MASS_U;
+constexpr int kMassChunk = kWave * 8 * kMassU;   // 2048 vocabulary entries per item
+static_assert(kMassChunk % kDrawBlock == 0 && kDrawBlock == 16 * 8, "block layout of a mass item");
+static_assert(512 * kMassU == kMassChunk, "group stride");
 
 __device__ __forceinline__ Top2 wave_top2(Top2 t) {
 #pragma unroll
@@ -888,76 +903,143 @@ __device__ __forceinline__ Top2 wave_top2(Top2 t) {
   return t;
 }
 
-__global__ __launch_bounds__(kScanWaves * kWave) void head_scan_kernel(HeadParams p) {
+__global__ __launch_bounds__(kMassWaves * kWave) void head_mass_kernel(HeadParams p) {
   const int lane = threadIdx.x % kWave;
-  const int nw = gridDim.x * kScanWaves;
+  const int nw = gridDim.x * kMassWaves;
   const int items = p.list_count[0] * p.n_chunks;
   const bool vec = (p.V & 3) == 0;
-  for (int item = blockIdx.x * kScanWaves + threadIdx.x / kWave; item < items; item += nw) {
+  for (int item = blockIdx.x * kMassWaves + threadIdx.x / kWave; item < items; item += nw) {
     const int li = item / p.n_chunks, ch = item % p.n_chunks;
     const int m = p.list[li];
-    const float it = 1.f / p.temperature[m];
-    const uint64_t key = p.draw_key[m];
+    const float sc = 1.4426950408889634f / p.temperature[m];   // log2(e) / t
+    const float ref = p.rmax[m];
     const float* lr = p.logits + (size_t)p.store_row[m] * p.V;
-    const int base = ch * kScanChunk + 8 * lane;
-    Top2 t = top2_empty();
-    if (vec && ch * kScanChunk + kScanChunk <= p.V) {
-      float4 a[kScanU], b[kScanU];
+    const int base = ch * kMassChunk + 8 * lane;
+    float s[kMassU];
+    if (vec && ch * kMassChunk + kMassChunk <= p.V) {
+      float4 a[kMassU], b[kMassU];
 #pragma unroll
-      for (int u = 0; u < kScanU; ++u) {
+      for (int u = 0; u < kMassU; ++u) {
         a[u] = *(const float4*)(lr + base + 512 * u);
         b[u] = *(const float4*)(lr + base + 512 * u + 4);
       }
 #pragma unroll
-      for (int u = 0; u < kScanU; ++u) {
-        const int j0 = base + 512 * u;
-        uint32_t w[8];
-        philox_words8(p.seed, key, (uint64_t)(j0 >> 3), w);
+      for (int u = 0; u < kMassU; ++u) {
         const float l[8] = {a[u].x, a[u].y, a[u].z, a[u].w, b[u].x, b[u].y, b[u].z, b[u].w};
+        float t = 0.f;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) top2_push_inc(t, fmaf(l[k], it, gumbel_fast(w[k])), j0 + k);
+        for (int k = 0; k < 8; ++k) t += hw_exp2((l[k] - ref) * sc);
+        s[u] = t;
       }
     } else {
       // the last chunk (or rows that are not 16-byte aligned): entry by entry
-      for (int u = 0; u < kScanU; ++u) {
+#pragma unroll
+      for (int u = 0; u < kMassU; ++u) {
         const int j0 = base + 512 * u;
-        if (j0 >= p.V) break;
-        uint32_t w[8];
-        philox_words8(p.seed, key, (uint64_t)(j0 >> 3), w);
-        for (int k = 0; k < 8 && j0 + k < p.V; ++k)
-          top2_push_inc(t, fmaf(lr[j0 + k], it, gumbel_fast(w[k])), j0 + k);
+        float t = 0.f;
+        for (int k = 0; k < 8 && j0 + k < p.V; ++k) t += hw_exp2((lr[j0 + k] - ref) * sc);
+        s[u] = t;
       }
     }
-    t = wave_top2(t);
-    if (lane == 0) p.scan_part[(size_t)li * p.n_chunks + ch] = t;
+#pragma unroll
+    for (int u = 0; u < kMassU; ++u) {
+#pragma unroll
+      for (int mask = 1; mask < 16; mask <<= 1) s[u] += shfl_xor(s[u], mask);
+      const int blk = ch * (kMassChunk / kDrawBlock) + 4 * u + (lane >> 4);
+      if ((lane & 15) == 0 && blk < p.n_blocks) p.mass[(size_t)li * p.n_blocks + blk] = s[u];
+    }
   }
 }
 
-// One wave per row: the chunk maxima of a drawn row are merged across lanes.
-__global__ __launch_bounds__(256) void head_finalize_kernel(HeadParams p) {
-  const int m = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+// Level 1 of a two-level draw over the n_blocks block masses of one row, by
+// the kFinThreads threads of one workgroup: thread i takes blocks 8 i .. 8 i + 7
+// (+ 8 kFinThreads r), one Philox call per eight blocks; score log Z_b + g1_b,
+// zero-mass blocks out of the race.  Each wave's best two go through LDS and
+// every thread merges them in wave order, so all threads return the same pick.
+constexpr int kFinThreads = 256;
+
+// Z_b comes from the mass pass (mass != NULL), or from the GEMM epilogue's
+// statistics of the row's vocabulary tiles, which are the blocks: a tile's
+// (max m, sum of exp((l - m) / t)) gives log Z_b = m / t + log s.
+__device__ __forceinline__ Top2 draw_block(const float* mass, const RowStat* tiles, float it,
+                                           int n_blocks, uint64_t seed, uint64_t key, Top2* red) {
+  const float ln2 = 0.6931471805599453f;
+  Top2 t = top2_empty();
+  for (int b0 = 8 * threadIdx.x; b0 < n_blocks; b0 += 8 * kFinThreads) {
+    float lz[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      lz[k] = -INFINITY;
+      if (b0 + k < n_blocks) {
+        if (mass) {
+          const float z = mass[b0 + k];
+          if (z > 0.f) lz[k] = hw_log2(z) * ln2;
+        } else {
+          const RowStat st = tiles[b0 + k];
+          if (st.s > 0.f) lz[k] = fmaf(st.m, it, hw_log2(st.s) * ln2);
+        }
+      }
+    }
+    uint32_t w[8];
+    philox_words8(seed, key, (uint64_t)(b0 >> 3), w, 1);
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (lz[k] > -INFINITY) top2_push_inc(t, lz[k] + gumbel_fast(w[k]), b0 + k);
+  }
+  t = wave_top2(t);
+  if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = t;
+  __syncthreads();
+  Top2 r = red[0];
+#pragma unroll
+  for (int i = 1; i < kFinThreads / kWave; ++i) r = top2_merge(r, red[i]);
+  return r;
+}
+
+// One workgroup per row: the token (a two-level draw, the planted row's
+// argmax, or the argmax) and its decision margin.
+__global__ __launch_bounds__(kFinThreads) void head_finalize_kernel(HeadParams p) {
+  __shared__ Top2 red[kFinThreads / kWave];
+  const int m = blockIdx.x;
   const int lane = threadIdx.x % kWave;
-  if (m >= p.M) return;
   int tok = p.amax[m];
   float g = p.gap_greedy[m];
   if (p.plant_row && p.plant_row[m] >= 0 && p.plant_row[m] < p.M) {
     tok = p.amax[p.plant_row[m]];
     g = p.gap_greedy[p.plant_row[m]];
   } else if (p.temperature && p.temperature[m] > 0.f && p.draw_key[m] != DMTP_NO_DRAW) {
-    const int li = p.list_pos ? p.list_pos[m] : -1;
-    if (li < 0) {
+    const bool stored = p.store_row && p.store_row[m] >= 0 && p.store_row[m] < p.logits_rows;
+    const int li = (stored && !p.block_stats) ? p.list_pos[m] : -1;
+    if (!stored) {
       tok = -1;  // a sampled row without a stored logits row
       g = 0.f;
     } else {
-      Top2 t = top2_empty();
-      for (int c = lane; c < p.n_chunks; c += kWave) t = top2_merge(t, p.scan_part[(size_t)li * p.n_chunks + c]);
+      const uint64_t key = p.draw_key[m];
+      const float it = 1.f / p.temperature[m];
+      const Top2 t1 =
+          draw_block(p.block_stats ? nullptr : p.mass + (size_t)li * p.n_blocks,
+                     p.part + (size_t)m * p.n_vtiles, it, p.n_blocks, p.seed, key, red);
+      if (threadIdx.x >= kWave) return;   // level 2 is wave 0's (no barrier follows)
+      // level 2 over the chosen block: lanes 0..15 take 8 entries each
+      const float* lr = p.logits + (size_t)p.store_row[m] * p.V;
+      Top2 t2 = top2_empty();
+      const bool any = t1.v1 > -INFINITY;
+      const int j0 = (any ? t1.i1 : 0) * kDrawBlock + 8 * lane;
+      if (any && lane < kDrawBlock / 8 && j0 < p.V) {
+        float l[8];
 #pragma unroll
-      for (int mask = 1; mask < kWave; mask <<= 1) t = top2_merge(t, top2_shfl_xor(t, mask));
-      tok = t.i1;
-      g = t.v1 - t.v2;
+        for (int k = 0; k < 8; ++k) l[k] = j0 + k < p.V ? lr[j0 + k] : 0.f;
+        uint32_t w[8];
+        philox_words8(p.seed, key, (uint64_t)(j0 >> 3), w, 0);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (j0 + k < p.V) top2_push_inc(t2, fmaf(l[k], it, gumbel_fast(w[k])), j0 + k);
+      }
+      t2 = wave_top2(t2);
+      tok = (any && t2.i1 != 0x7FFFFFFF) ? t2.i1 : -1;
+      g = tok >= 0 ? fminf(t1.v1 - t1.v2, t2.v1 - t2.v2) : 0.f;
     }
   }
-  if (lane == 0) {
+  if (threadIdx.x == 0) {
     p.token[m] = tok;
     if (p.gap) p.gap[m] = g;
   }
@@ -967,8 +1049,8 @@ typedef GemmTile<64, 64, 32, 32, 2, 2> HeadTileF32;
 typedef GemmTile<128, 64, 64, 32, 1, 1> HeadTileBF16;   // H not a multiple of 128
 
 struct WsLayout {
-  size_t prepared, part, amax, gapg, list, list_pos, list_count, scan, total;
-  int n_vtiles, n_chunks;
+  size_t prepared, part, amax, gapg, rmax, list, list_pos, list_count, mass, total;
+  int n_vtiles, n_blocks, n_chunks;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -980,18 +1062,20 @@ WsLayout ws_layout(const dmtp_head_desc& d, int M) {
   w.n_vtiles = head_t1_fits(d, M)                        ? head_t1_grid(d.V)
                : (d.dtype == DMTP_BF16 && d.H % 128 == 0) ? (d.V + 127) / 128
                                                           : (d.V + 63) / 64;
-  w.n_chunks = (d.V + kScanChunk - 1) / kScanChunk;
+  w.n_blocks = (d.V + kDrawBlock - 1) / kDrawBlock;
+  w.n_chunks = (d.V + kMassChunk - 1) / kMassChunk;
   const size_t esz = d.dtype == DMTP_BF16 ? 2 : 4;
   size_t o = 0;
   w.prepared = o; o = align256(o + (size_t)M * d.H * esz);
   w.part = o; o = align256(o + (size_t)w.n_vtiles * M * sizeof(RowStat));
   w.amax = o; o = align256(o + (size_t)M * 4);
   w.gapg = o; o = align256(o + (size_t)M * 4);
+  w.rmax = o; o = align256(o + (size_t)M * 4);
   w.list = o; o = align256(o + (size_t)M * 4);
   w.list_pos = o; o = align256(o + (size_t)M * 4);
   w.list_count = o; o = align256(o + 4);
-  w.scan = o;
-  if (d.temperature) o = align256(o + (size_t)M * w.n_chunks * sizeof(Top2));
+  w.mass = o;
+  if (d.temperature) o = align256(o + (size_t)M * w.n_blocks * sizeof(float));
   w.total = o;
   return w;
 }
@@ -1033,7 +1117,9 @@ hipError_t lm_head_run(const dmtp_head_desc& d, int M, void* ws, hipStream_t s) 
   p.list = (int32_t*)(base + w.list);
   p.list_pos = d.temperature ? (int32_t*)(base + w.list_pos) : nullptr;
   p.list_count = (int32_t*)(base + w.list_count);
-  p.scan_part = (Top2*)(base + w.scan);
+  p.rmax = (float*)(base + w.rmax);
+  p.mass = (float*)(base + w.mass);
+  p.n_blocks = w.n_blocks;
   p.n_chunks = w.n_chunks;
   p.token = d.token;
   p.row_max = d.row_max;
@@ -1045,6 +1131,7 @@ hipError_t lm_head_run(const dmtp_head_desc& d, int M, void* ws, hipStream_t s) 
   // row-major prepared rows; otherwise a single segment of ready head-input
   // rows is read in place.
   const bool mf32 = d.dtype == DMTP_BF16 && d.H % 128 == 0;
+  p.block_stats = mf32 && !head_t1_fits(d, M) && w.n_vtiles == w.n_blocks;
   p.a_sl = (mf32 && !d.prepared && head_mf32_bk(M) == 32) ? 32 : 0;
   const bool direct =
       !p.a_sl && d.n_seg == 1 && !d.seg[0].g_norm && d.seg[0].ld == d.H && !d.prepared;
@@ -1072,13 +1159,15 @@ hipError_t lm_head_run(const dmtp_head_desc& d, int M, void* ws, hipStream_t s) 
   hipLaunchKernelGGL(head_merge_kernel, dim3(M), dim3(kMergeThreads), 0, s, p, simple);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (simple) return hipSuccess;
-  if (d.temperature) {
+  // The matrix-core GEMM's statistics are per 128-entry vocabulary tile, so
+  // they are the draws' block masses; other GEMMs need the mass pass.
+  if (d.temperature && !p.block_stats) {
     hipLaunchKernelGGL(head_plan_kernel, dim3(1), dim3(1024), 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(head_scan_kernel, dim3(2048), dim3(kScanWaves * kWave), 0, s, p);
+    hipLaunchKernelGGL(head_mass_kernel, dim3(DMTP_MASS_GRID), dim3(kMassWaves * kWave), 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(head_finalize_kernel, dim3((M + 3) / 4), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(head_finalize_kernel, dim3(M), dim3(kFinThreads), 0, s, p);
   return hipGetLastError();
 }
 

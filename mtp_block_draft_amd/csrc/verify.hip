@@ -5,10 +5,13 @@
 //          logits and the row lse values; builds a deterministic list of the
 //          sequences that need a draw (correction from max(0, p - q), or bonus
 //          from p_K)
-//   scan   the draws: HBM-bound pass over the float32 rows, split into
-//          vocabulary chunks, Gumbel-max over log(max(0, p - q)) (and over log p
-//          for the zero-residual fallback) with the same Philox noise
-//   final  merges the chunk maxima and writes the correction/bonus token
+//   mass   the draws' memory-bound pass over the float32 rows, split into
+//          vocabulary chunks: the mass of max(0, p - q) (and of p, for the bonus
+//          and for the zero-residual fallback) in every block of kDrawBlock
+//          entries
+//   final  per drawn sequence, a two-level Gumbel-max draw: a block by its
+//          mass, then an entry of that block by its log weight, and writes the
+//          correction/bonus token
 //   stats  acceptance histogram of a batch of verify rounds, added to a running
 //          histogram, and the statistics derived from it
 #include "common.hpp"
@@ -18,13 +21,20 @@ namespace dmtp {
 
 namespace {
 
-// Scan work items are (sequence in the draw list, vocabulary chunk of kChunk
-// entries), one wave each: lane l takes the 8-entry blocks l, l + 64, ...
-// (kScanU of them), loads them all before any arithmetic and keeps running
-// top-2s in increasing index; one butterfly merge per item.
+// Mass work items are (sequence in the draw list, vocabulary chunk of kChunk
+// entries), one wave each: lane l takes the 8-entry groups l, l + 64, ...
+// (kScanU of them) and loads them all before any arithmetic; group u of lanes
+// 16 q .. 16 q + 15 is one block of kDrawBlock entries.
+#ifndef DMTP_MASS_U
+#define DMTP_MASS_U 2
+#endif
+#ifndef DMTP_MASS_GRID
+#define DMTP_MASS_GRID 4096
+#endif
 constexpr int kScanWaves = 4;
-constexpr int kScanU = 4;
+constexpr int kScanU = DMTP_MASS_U;
 constexpr int kChunk = kWave * 8 * kScanU;
+static_assert(kChunk % kDrawBlock == 0 && kDrawBlock == 16 * 8, "block layout of a mass item");
 
 struct VerifyParams {
   int B, K, V;
@@ -48,8 +58,9 @@ struct VerifyParams {
   int32_t* list_pos;   // [B]
   int32_t* count;      // [1]
   int32_t* mode;       // [B]: 0 greedy/done, 1 residual draw at row L, 2 bonus draw
-  Top2* part;          // [B, n_chunks, 2]
-  int n_chunks;
+  float* mass_r;       // [B, n_blocks] residual block masses (list order)
+  float* mass_p;       // [B, n_blocks] block masses of p
+  int n_blocks, n_chunks;
 };
 
 __device__ __forceinline__ int cand(const VerifyParams& p, int b, int i) {
@@ -121,54 +132,66 @@ __global__ void verify_main_kernel(VerifyParams p) {
   if (threadIdx.x == 0) p.count[0] = base;
 }
 
-// Per entry j of the scanned rows: a = log p_j = lp_j / t - lse_p; the bonus /
-// fallback score a + g_j; in residual mode c = log q_j and the residual score
-// log(p_j - q_j) + g_j where p_j > q_j (the same Gumbel noise g_j).
-__device__ __forceinline__ void verify_entry(float lp, float lq, float it, float lse_p, float lse_q,
-                                             bool resid, uint32_t word, int j, Top2& tr, Top2& tp) {
-  const float g = gumbel_fast(word);
-  const float a = fmaf(lp, it, -lse_p);
-  top2_push_inc(tp, a + g, j);
-  if (resid) {
-    const float c = fmaf(lq, it, -lse_q);
-    const float sres = a > c ? a + log1m_exp(c - a) : -INFINITY;
-    top2_push_inc(tr, sres + g, j);
+// Row pointers and lse values of a drawn sequence: the residual at row L
+// (p: target row K + L, q: candidate row L), or the bonus from target row 2K.
+struct DrawRows {
+  const float* pr;
+  const float* qr;
+  float lse_p, lse_q, it;
+  bool resid;
+};
+
+__device__ __forceinline__ DrawRows draw_rows(const VerifyParams& p, int b) {
+  const int K = p.K, V = p.V, L = p.accept_len[b];
+  const float* rows = p.logits + (size_t)b * (2 * K + 1) * V;
+  DrawRows r;
+  r.resid = p.mode[b] == 1;
+  r.it = 1.f / p.temperature[b];
+  r.pr = rows + (size_t)(K + L) * V;
+  r.qr = rows + (size_t)L * V;
+  r.lse_p = p.target_lse[(size_t)b * (K + 1) + L];
+  r.lse_q = r.resid ? (L == 0 ? p.t1_lse[b] : p.draft_lse[(size_t)b * (K - 1) + L - 1]) : 0.f;
+  return r;
+}
+
+// p_j and the residual max(0, p_j - q_j) of one entry from its logits: with
+// a = log p_j and c = log q_j, the residual is p_j (1 - e^(c - a)) where a > c,
+// the difference taken without cancelling.
+__device__ __forceinline__ void entry_mass(float lp, float lq, const DrawRows& r, float& pm,
+                                           float& rm) {
+  const float log2e = 1.4426950408889634f;
+  const float a = fmaf(lp, r.it, -r.lse_p);
+  pm = hw_exp2(a * log2e);
+  rm = 0.f;
+  if (r.resid) {
+    const float c = fmaf(lq, r.it, -r.lse_q);
+    rm = a > c ? pm * one_minus_exp(c - a) : 0.f;
   }
 }
 
-__global__ __launch_bounds__(kScanWaves * kWave) void verify_scan_kernel(VerifyParams p) {
+__global__ __launch_bounds__(kScanWaves * kWave) void verify_mass_kernel(VerifyParams p) {
   const int lane = threadIdx.x % kWave;
   const int nw = gridDim.x * kScanWaves;
   const int items = p.count[0] * p.n_chunks;
-  const int K = p.K, V = p.V;
+  const int V = p.V;
   const bool vec = (V & 3) == 0;
   for (int item = blockIdx.x * kScanWaves + threadIdx.x / kWave; item < items; item += nw) {
     const int li = item / p.n_chunks, ch = item % p.n_chunks;
-    const int b = p.list[li];
-    const int L = p.accept_len[b];
-    const bool resid = p.mode[b] == 1;
-    const float it = 1.f / p.temperature[b];
-    const float* rows = p.logits + (size_t)b * (2 * K + 1) * V;
-    // residual at row L: p row K + L, q row L; bonus: p row 2K
-    const float* pr = rows + (size_t)(K + L) * V;
-    const float* qr = rows + (size_t)L * V;
-    const float lse_p = p.target_lse[(size_t)b * (K + 1) + L];
-    const float lse_q = resid ? (L == 0 ? p.t1_lse[b] : p.draft_lse[(size_t)b * (K - 1) + L - 1]) : 0.f;
-    const uint64_t key = p.final_key[b];
+    const DrawRows r = draw_rows(p, p.list[li]);
     const int base = ch * kChunk + 8 * lane;
-    Top2 tr = top2_empty(), tp = top2_empty();
+    float sp[kScanU], sr[kScanU];
     if (vec && ch * kChunk + kChunk <= V) {
       float4 pa[kScanU], pb[kScanU], qa[kScanU], qb[kScanU];
 #pragma unroll
       for (int u = 0; u < kScanU; ++u) {
-        pa[u] = *(const float4*)(pr + base + 512 * u);
-        pb[u] = *(const float4*)(pr + base + 512 * u + 4);
+        pa[u] = *(const float4*)(r.pr + base + 512 * u);
+        pb[u] = *(const float4*)(r.pr + base + 512 * u + 4);
       }
-      if (resid) {
+      if (r.resid) {
 #pragma unroll
         for (int u = 0; u < kScanU; ++u) {
-          qa[u] = *(const float4*)(qr + base + 512 * u);
-          qb[u] = *(const float4*)(qr + base + 512 * u + 4);
+          qa[u] = *(const float4*)(r.qr + base + 512 * u);
+          qb[u] = *(const float4*)(r.qr + base + 512 * u + 4);
         }
       } else {
 #pragma unroll
@@ -176,56 +199,137 @@ __global__ __launch_bounds__(kScanWaves * kWave) void verify_scan_kernel(VerifyP
       }
 #pragma unroll
       for (int u = 0; u < kScanU; ++u) {
-        const int j0 = base + 512 * u;
-        uint32_t w[8];
-        philox_words8(p.seed, key, (uint64_t)(j0 >> 3), w);
         const float lp[8] = {pa[u].x, pa[u].y, pa[u].z, pa[u].w, pb[u].x, pb[u].y, pb[u].z, pb[u].w};
         const float lq[8] = {qa[u].x, qa[u].y, qa[u].z, qa[u].w, qb[u].x, qb[u].y, qb[u].z, qb[u].w};
+        float tp = 0.f, tr = 0.f;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) verify_entry(lp[k], lq[k], it, lse_p, lse_q, resid, w[k], j0 + k, tr, tp);
+        for (int k = 0; k < 8; ++k) {
+          float pm, rm;
+          entry_mass(lp[k], lq[k], r, pm, rm);
+          tp += pm;
+          tr += rm;
+        }
+        sp[u] = tp;
+        sr[u] = tr;
       }
     } else {
+#pragma unroll
       for (int u = 0; u < kScanU; ++u) {
         const int j0 = base + 512 * u;
-        if (j0 >= V) break;
-        uint32_t w[8];
-        philox_words8(p.seed, key, (uint64_t)(j0 >> 3), w);
-        for (int k = 0; k < 8 && j0 + k < V; ++k)
-          verify_entry(pr[j0 + k], resid ? qr[j0 + k] : 0.f, it, lse_p, lse_q, resid, w[k], j0 + k,
-                       tr, tp);
+        float tp = 0.f, tr = 0.f;
+        for (int k = 0; k < 8 && j0 + k < V; ++k) {
+          float pm, rm;
+          entry_mass(r.pr[j0 + k], r.resid ? r.qr[j0 + k] : 0.f, r, pm, rm);
+          tp += pm;
+          tr += rm;
+        }
+        sp[u] = tp;
+        sr[u] = tr;
       }
     }
 #pragma unroll
-    for (int mask = 1; mask < kWave; mask <<= 1) {
-      tr = top2_merge(tr, top2_shfl_xor(tr, mask));
-      tp = top2_merge(tp, top2_shfl_xor(tp, mask));
-    }
-    if (lane == 0) {
-      p.part[((size_t)li * p.n_chunks + ch) * 2 + 0] = tr;
-      p.part[((size_t)li * p.n_chunks + ch) * 2 + 1] = tp;
+    for (int u = 0; u < kScanU; ++u) {
+#pragma unroll
+      for (int mask = 1; mask < 16; mask <<= 1) {
+        sp[u] += shfl_xor(sp[u], mask);
+        sr[u] += shfl_xor(sr[u], mask);
+      }
+      const int blk = ch * (kChunk / kDrawBlock) + 4 * u + (lane >> 4);
+      if ((lane & 15) == 0 && blk < p.n_blocks) {
+        p.mass_p[(size_t)li * p.n_blocks + blk] = sp[u];
+        if (r.resid) p.mass_r[(size_t)li * p.n_blocks + blk] = sr[u];
+      }
     }
   }
 }
 
-// One wave per row: the chunk maxima of the row's draw are merged across lanes.
-__global__ __launch_bounds__(256) void verify_final_kernel(VerifyParams p) {
-  const int b = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-  const int lane = threadIdx.x % kWave;
-  if (b >= p.B) return;
-  const int li = p.list_pos[b];
-  if (li < 0) return;
-  Top2 tr = top2_empty(), tp = top2_empty();
-  for (int c = lane; c < p.n_chunks; c += kWave) {
-    tr = top2_merge(tr, p.part[((size_t)li * p.n_chunks + c) * 2 + 0]);
-    tp = top2_merge(tp, p.part[((size_t)li * p.n_chunks + c) * 2 + 1]);
-  }
+__device__ __forceinline__ Top2 wave_top2(Top2 t) {
 #pragma unroll
-  for (int mask = 1; mask < kWave; mask <<= 1) {
-    tr = top2_merge(tr, top2_shfl_xor(tr, mask));
-    tp = top2_merge(tp, top2_shfl_xor(tp, mask));
+  for (int mask = 1; mask < kWave; mask <<= 1) t = top2_merge(t, top2_shfl_xor(t, mask));
+  return t;
+}
+
+// One workgroup per drawn sequence: the residual draw (or, when the residual
+// has no mass, the fallback draw from p), or the bonus draw from p_K.  Level 1
+// picks a block by log Z_b + g1_b -- thread i takes blocks 8 i .. 8 i + 7, one
+// Philox call per eight blocks, and the waves' best two are merged through
+// LDS in wave order -- and level 2 (wave 0) an entry of that block by its log
+// weight plus g0_j, the log residual log p_j + log(1 - e^(c - a)) taken
+// without cancelling.
+constexpr int kFinThreads = 256;
+
+__global__ __launch_bounds__(kFinThreads) void verify_final_kernel(VerifyParams p) {
+  __shared__ Top2 red[kFinThreads / kWave];
+  __shared__ int any_resid;
+  const float ln2 = 0.6931471805599453f;
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x % kWave;
+  const int li = p.list_pos[b];
+  if (li < 0) return;   // the whole workgroup, before any barrier
+  DrawRows r = draw_rows(p, b);
+  const uint64_t key = p.final_key[b];
+  const int nb = p.n_blocks;
+  const float* mr = p.mass_r + (size_t)li * nb;
+  const float* mp = p.mass_p + (size_t)li * nb;
+  // both mass rows are loaded before the choice between them is known
+  float zr[8], zp[8];
+  Top2 tr = top2_empty(), tp = top2_empty();
+  if (threadIdx.x == 0) any_resid = 0;
+  __syncthreads();
+  for (int b0 = 8 * threadIdx.x; b0 < nb; b0 += 8 * kFinThreads) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      zp[k] = b0 + k < nb ? mp[b0 + k] : 0.f;
+      zr[k] = (r.resid && b0 + k < nb) ? mr[b0 + k] : 0.f;
+    }
+    uint32_t w[8];
+    philox_words8(p.seed, key, (uint64_t)(b0 >> 3), w, 1);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float g = gumbel_fast(w[k]);
+      if (zp[k] > 0.f) top2_push_inc(tp, fmaf(hw_log2(zp[k]), ln2, g), b0 + k);
+      if (zr[k] > 0.f) top2_push_inc(tr, fmaf(hw_log2(zr[k]), ln2, g), b0 + k);
+    }
   }
-  // residual mode with no positive residual falls back to p
-  const int y = (p.mode[b] == 1 && tr.v1 > -INFINITY) ? tr.i1 : tp.i1;
+  // no positive residual mass in any block: the draw falls back to p
+  if (r.resid && tr.v1 > -INFINITY) any_resid = 1;   // benign race: every writer stores 1
+  __syncthreads();
+  r.resid = r.resid && any_resid;
+  Top2 t1 = wave_top2(r.resid ? tr : tp);
+  if (lane == 0) red[threadIdx.x / kWave] = t1;
+  __syncthreads();
+  if (threadIdx.x >= kWave) return;   // level 2 is wave 0's (no barrier follows)
+  t1 = red[0];
+#pragma unroll
+  for (int i = 1; i < kFinThreads / kWave; ++i) t1 = top2_merge(t1, red[i]);
+  const bool found = t1.v1 > -INFINITY;
+  Top2 t2 = top2_empty();
+  const int j0 = (found ? t1.i1 : 0) * kDrawBlock + 8 * lane;
+  if (found && lane < kDrawBlock / 8 && j0 < p.V) {
+    float lp[8], lq[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      lp[k] = j0 + k < p.V ? r.pr[j0 + k] : 0.f;
+      lq[k] = (r.resid && j0 + k < p.V) ? r.qr[j0 + k] : 0.f;
+    }
+    uint32_t w[8];
+    philox_words8(p.seed, key, (uint64_t)(j0 >> 3), w, 0);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int j = j0 + k;
+      if (j < p.V) {
+        const float a = fmaf(lp[k], r.it, -r.lse_p);
+        float lw = a;
+        if (r.resid) {
+          const float c = fmaf(lq[k], r.it, -r.lse_q);
+          lw = a > c ? a + log1m_exp(c - a) : -INFINITY;
+        }
+        if (lw > -INFINITY) top2_push_inc(t2, lw + gumbel_fast(w[k]), j);
+      }
+    }
+  }
+  t2 = wave_top2(t2);
+  const int y = (found && t2.i1 != 0x7FFFFFFF) ? t2.i1 : -1;
   if (lane == 0) p.out_tokens[(size_t)b * (p.K + 1) + p.accept_len[b]] = y;
 }
 
@@ -274,22 +378,26 @@ __global__ __launch_bounds__(kStatsThreads) void accept_stats_kernel(int B, int 
 }
 
 struct WsL {
-  size_t list, list_pos, count, mode, part, total;
-  int n_chunks;
+  size_t list, list_pos, count, mode, mass_r, mass_p, total;
+  int n_blocks, n_chunks;
 };
 
 size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 
 WsL layout(const dmtp_verify_desc& d) {
   WsL w;
+  w.n_blocks = (d.V + kDrawBlock - 1) / kDrawBlock;
   w.n_chunks = (d.V + kChunk - 1) / kChunk;
   size_t o = 0;
   w.list = o; o = al(o + (size_t)d.B * 4);
   w.list_pos = o; o = al(o + (size_t)d.B * 4);
   w.count = o; o = al(o + 4);
   w.mode = o; o = al(o + (size_t)d.B * 4);
-  w.part = o;
-  if (d.temperature && !d.target_only) o = al(o + (size_t)d.B * w.n_chunks * 2 * sizeof(Top2));
+  const bool draws = d.temperature && !d.target_only;
+  w.mass_r = o;
+  if (draws) o = al(o + (size_t)d.B * w.n_blocks * sizeof(float));
+  w.mass_p = o;
+  if (draws) o = al(o + (size_t)d.B * w.n_blocks * sizeof(float));
   w.total = o;
   return w;
 }
@@ -324,14 +432,16 @@ hipError_t verify_run(const dmtp_verify_desc& d, void* ws, hipStream_t s) {
   p.list_pos = (int32_t*)(base + w.list_pos);
   p.count = (int32_t*)(base + w.count);
   p.mode = (int32_t*)(base + w.mode);
-  p.part = (Top2*)(base + w.part);
+  p.mass_r = (float*)(base + w.mass_r);
+  p.mass_p = (float*)(base + w.mass_p);
+  p.n_blocks = w.n_blocks;
   p.n_chunks = w.n_chunks;
   hipLaunchKernelGGL(verify_main_kernel, dim3(1), dim3(1024), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !d.temperature || d.target_only) return e;
-  hipLaunchKernelGGL(verify_scan_kernel, dim3(2048), dim3(kScanWaves * kWave), 0, s, p);
+  hipLaunchKernelGGL(verify_mass_kernel, dim3(DMTP_MASS_GRID), dim3(kScanWaves * kWave), 0, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(verify_final_kernel, dim3((d.B + 3) / 4), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(verify_final_kernel, dim3(d.B), dim3(kFinThreads), 0, s, p);
   return hipGetLastError();
 }
 

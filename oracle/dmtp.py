@@ -54,7 +54,7 @@ from typing import Callable, Dict, List, Optional, Sequence, Tuple
 import numpy as np
 
 from . import numerics as nm
-from .philox import gumbel_argmax
+from .philox import grouped_gumbel_argmax
 
 # ---------------------------------------------------------------------------
 # step 1 and 3: fusion projections
@@ -101,15 +101,16 @@ def select_tokens(logits: np.ndarray, tau: np.ndarray, seed: int,
                   keys: Optional[np.ndarray]) -> Tuple[np.ndarray, np.ndarray]:
     """Per row: argmax when tau = 0, else a draw from softmax(l / tau).
 
-    The draw is the Gumbel-max form of sampling: argmax_j (l_j / tau + g_j) with
-    g the Gumbel noise of the row's draw key.  Lowest index on exact ties.
+    The draw is the two-level Gumbel-max form of sampling of
+    philox.grouped_gumbel_argmax over l / tau with the row's draw key.  Lowest
+    index on exact ties.
     """
     M = logits.shape[0]
     tok = np.empty(M, dtype=np.int64)
     mar = np.empty(M, dtype=np.float64)
     for m in range(M):
         if tau[m] > 0.0:
-            tok[m], mar[m] = gumbel_argmax(logits[m] / tau[m], seed, int(keys[m]))
+            tok[m], mar[m] = grouped_gumbel_argmax(logits[m] / tau[m], seed, int(keys[m]))
         else:
             tok[m] = nm.argmax_first(logits[m])
             mar[m] = nm.top2_gap(logits[m])
@@ -470,7 +471,7 @@ def run_round(inp, seqs: Optional[Sequence[int]] = None,
             # stand-in for an MTP head that agrees with the target)
             v, m = tgt_argmax[r, 0], tgt_gap[r, 0]
         elif tau[r] > 0:
-            v, m = gumbel_argmax(l1[r] / tau[r], seed, int(inp.draft_keys[b, 0]))
+            v, m = grouped_gumbel_argmax(l1[r] / tau[r], seed, int(inp.draft_keys[b, 0]))
         else:
             v, m = nm.argmax_first(l1[r]), nm.top2_gap(l1[r])
         t1[r] = decide(("T1", b), v, m)
@@ -499,7 +500,7 @@ def run_round(inp, seqs: Optional[Sequence[int]] = None,
         for i in range(1, K):
             row = q_logits[r, i]
             if tau[r] > 0:
-                v, m = gumbel_argmax(row / tau[r], seed, int(inp.draft_keys[b, i]))
+                v, m = grouped_gumbel_argmax(row / tau[r], seed, int(inp.draft_keys[b, i]))
             else:
                 v, m = nm.argmax_first(row), nm.top2_gap(row)
             drafts[r, i] = decide(("draft", b, i), v, m)
@@ -516,7 +517,7 @@ def run_round(inp, seqs: Optional[Sequence[int]] = None,
         for i in range(K + 1):
             if target_only and tau[r] > 0:
                 # the target's own pick: a draw from softmax(lt_i / tau)
-                v, m = gumbel_argmax(p_logits[r, i] / tau[r], seed, int(inp.target_keys[b, i]))
+                v, m = grouped_gumbel_argmax(p_logits[r, i] / tau[r], seed, int(inp.target_keys[b, i]))
             else:
                 v, m = tgt_argmax[r, i], tgt_gap[r, i]
             y_final[r, i] = decide(("y", b, i), v, m)
@@ -535,7 +536,7 @@ def run_round(inp, seqs: Optional[Sequence[int]] = None,
             def draw(i, w, b=b):
                 with np.errstate(divide="ignore"):
                     lw = np.log(np.asarray(w, dtype=np.float64))
-                v, m = gumbel_argmax(lw, seed, int(inp.final_keys[b]))
+                v, m = grouped_gumbel_argmax(lw, seed, int(inp.final_keys[b]))
                 return decide(("final", b), v, m)
 
             L, toks = verify_rejection(drafts[r], p_rows, q_rows, accept, draw)

@@ -11,14 +11,23 @@ against NumPy's independent ``numpy.random.Philox``.
 
 Draw layout (shared definition with the HIP sampler, each side implementing
 it on its own): a draw is named by ``(seed, draw_key)``; the 32-bit word for
-vocabulary index j comes from counter ``(j >> 3, draw_key, 0, 0)`` under key
-``(seed, 0)``, output word ``(j & 7) >> 1``, low half when ``j & 1 == 0``.
+index j of noise level L comes from counter ``(j >> 3, draw_key, L, 0)`` under
+key ``(seed, 0)``, output word ``(j & 7) >> 1``, low half when ``j & 1 == 0``.
+Level 0 indexes vocabulary entries, level 1 blocks of entries.
 
 Gumbel variate of word x: t = (x + 1/2) / 2^32, E = -log(1 - t) (an Exp(1)
 variate), g = -log(E).  Taking E through log1p keeps full relative precision
 for the small E that decide the maximum.  Sampling index j with probability
 proportional to w_j is then argmax_j (log w_j + g_j) (the Gumbel-max
-identity).  Test infrastructure only.
+identity).
+
+A draw over a vocabulary is taken in two levels (grouped_gumbel_argmax):
+first a block of DRAW_BLOCK consecutive entries by Gumbel-max over the
+blocks' log masses (level-1 noise), then an entry of that block by
+Gumbel-max over its log weights (level-0 noise).  The two noises are
+independent, so P(j) = P(block of j) P(j | block) = (Z_b / Z)(w_j / Z_b) =
+w_j / Z: the same distribution as one Gumbel-max over all entries.  Test
+infrastructure only.
 """
 from __future__ import annotations
 
@@ -28,6 +37,7 @@ M0 = 0xD2E7470EE14C6C93
 M1 = 0xCA5A826395121157
 W0 = 0x9E3779B97F4A7C15
 W1 = 0xBB67AE8584CAA73B
+DRAW_BLOCK = 128
 _M32 = np.uint64(0xFFFFFFFF)
 _S32 = np.uint64(32)
 
@@ -63,11 +73,12 @@ def philox4x64_10(c0, c1, c2, c3, k0: int, k1: int):
     return c
 
 
-def words32(seed: int, draw_key: int, n: int) -> np.ndarray:
-    """The n 32-bit words of draw (seed, draw_key), index j = 0..n-1 (uint64)."""
+def words32(seed: int, draw_key: int, n: int, level: int = 0) -> np.ndarray:
+    """The n 32-bit words of noise level `level` of draw (seed, draw_key),
+    index j = 0..n-1 (uint64)."""
     j = np.arange(n, dtype=np.uint64)
     blocks = np.arange((n + 7) // 8, dtype=np.uint64)
-    out = philox4x64_10(blocks, np.uint64(draw_key), 0, 0, int(seed), 0)
+    out = philox4x64_10(blocks, np.uint64(draw_key), np.uint64(level), 0, int(seed), 0)
     o = np.stack(out, axis=1)                 # [n_blocks, 4]
     w = j & np.uint64(7)
     word64 = o[(j >> np.uint64(3)).astype(np.int64), (w >> np.uint64(1)).astype(np.int64)]
@@ -75,23 +86,55 @@ def words32(seed: int, draw_key: int, n: int) -> np.ndarray:
     return np.where(half, word64 >> _S32, word64 & _M32)
 
 
-def gumbel(seed: int, draw_key: int, n: int) -> np.ndarray:
-    """Gumbel(0, 1) noise of draw (seed, draw_key) for indices 0..n-1 (float64)."""
-    x = words32(seed, draw_key, n).astype(np.float64)
+def gumbel(seed: int, draw_key: int, n: int, level: int = 0) -> np.ndarray:
+    """Gumbel(0, 1) noise of draw (seed, draw_key), level `level`, for indices 0..n-1."""
+    x = words32(seed, draw_key, n, level).astype(np.float64)
     t = (x + 0.5) * 2.0 ** -32
     e = -np.log1p(-t)
     return -np.log(e)
 
 
-def gumbel_argmax(log_w: np.ndarray, seed: int, draw_key: int):
-    """Sample index j with probability exp(log_w_j) / sum exp(log_w) (Gumbel max).
-
-    Entries with log_w = -inf never win.  Returns (index, margin) where the
-    margin is the gap between the best and second-best perturbed score.
-    """
-    s = np.asarray(log_w, dtype=np.float64) + gumbel(seed, draw_key, log_w.shape[-1])
+def _argmax_gap(s: np.ndarray):
+    """Index of the maximum (lowest among equals) and the top-2 gap."""
     j = int(np.argmax(s))
     if s.shape[-1] < 2:
         return j, np.inf
     part = np.partition(s, -2)
     return j, float(part[-1] - part[-2])
+
+
+def gumbel_argmax(log_w: np.ndarray, seed: int, draw_key: int, level: int = 0):
+    """Sample index j with probability exp(log_w_j) / sum exp(log_w) (Gumbel max)
+    with the noise of level `level`.
+
+    Entries with log_w = -inf never win.  Returns (index, margin) where the
+    margin is the gap between the best and second-best perturbed score.
+    """
+    lw = np.asarray(log_w, dtype=np.float64)
+    return _argmax_gap(lw + gumbel(seed, draw_key, lw.shape[-1], level))
+
+
+def grouped_gumbel_argmax(log_w: np.ndarray, seed: int, draw_key: int, block: int = DRAW_BLOCK):
+    """Sample index j with probability w_j / sum(w), w = exp(log_w), in two levels.
+
+    The entries are cut into blocks of `block` consecutive indices (the last
+    one may be shorter).  Level 1: block b = argmax_b (log Z_b + g1_b), Z_b
+    the block's mass and g1 the level-1 noise of the draw, indexed by block.
+    Level 2: j = argmax over the entries of block b of (log_w_j + g0_j), g0 the
+    level-0 noise indexed by entry.  Blocks of zero mass, and entries with
+    log_w = -inf, never win.  Returns (index, margin): the margin is the
+    smaller of the two levels' top-2 score gaps, so a decision whose margin is
+    large stays the same under a small change of any weight.
+    """
+    lw = np.asarray(log_w, dtype=np.float64)
+    V = lw.shape[-1]
+    top = np.max(lw)
+    w = np.exp(lw - top)                       # the common shift leaves both levels unchanged
+    starts = np.arange(0, V, block)
+    Z = np.add.reduceat(w, starts)
+    with np.errstate(divide="ignore"):
+        logZ = np.log(Z)
+    b, gap1 = _argmax_gap(logZ + gumbel(seed, draw_key, len(starts), level=1))
+    lo, hi = b * block, min(V, (b + 1) * block)
+    j, gap2 = _argmax_gap(lw[lo:hi] + gumbel(seed, draw_key, V, level=0)[lo:hi])
+    return lo + j, min(gap1, gap2)

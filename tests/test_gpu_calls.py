@@ -195,7 +195,7 @@ def test_lm_head_sampled_planted_and_stored(dm, dt):
             src = plant[m]
             want, margin = int(np.argmax(ref_logits[src])), float(onm.top2_gap(ref_logits[src]))
         elif tau[m] > 0 and keys[m] != np.uint64(0xFFFFFFFFFFFFFFFF):
-            want, margin = oph.gumbel_argmax(ref_logits[m] / tau[m], seed, int(keys[m]))
+            want, margin = oph.grouped_gumbel_argmax(ref_logits[m] / tau[m], seed, int(keys[m]))
         else:
             want, margin = int(np.argmax(ref_logits[m])), float(onm.top2_gap(ref_logits[m]))
         if got[m] != want:
@@ -301,7 +301,7 @@ def test_lm_head_at_most_32_rows(dm, H, M):
             src = plant[m]
             want, margin = int(np.argmax(ref_logits[src])), float(onm.top2_gap(ref_logits[src]))
         elif tau[m] > 0 and keys[m] != np.uint64(0xFFFFFFFFFFFFFFFF):
-            want, margin = oph.gumbel_argmax(ref_logits[m] / tau[m], seed, int(keys[m]))
+            want, margin = oph.grouped_gumbel_argmax(ref_logits[m] / tau[m], seed, int(keys[m]))
         else:
             want, margin = int(np.argmax(ref_logits[m])), float(onm.top2_gap(ref_logits[m]))
         if got[m] != want:
@@ -601,7 +601,7 @@ def test_verify_greedy_and_sampled(dm, V):
 
         def draw(i, w):
             with np.errstate(divide="ignore"):
-                j, m = oph.gumbel_argmax(np.log(np.asarray(w)), seed, int(fkeys[b]))
+                j, m = oph.grouped_gumbel_argmax(np.log(np.asarray(w)), seed, int(fkeys[b]))
             margins["final"] = m
             return j
 
@@ -722,7 +722,7 @@ def test_verify_one_candidate(dm):
 
             def draw(i, w):
                 with np.errstate(divide="ignore"):
-                    j, mg = oph.gumbel_argmax(np.log(np.asarray(w)), seed, int(fkeys[b]))
+                    j, mg = oph.grouped_gumbel_argmax(np.log(np.asarray(w)), seed, int(fkeys[b]))
                 m["final"] = mg
                 return j
 

@@ -119,11 +119,14 @@ def test_philox4x64_matches_numpy():
 
 def test_words32_layout():
     seed, dk = 99, (1 << 32) | 5
-    w = philox.words32(seed, dk, 20)
-    for j in (0, 1, 7, 8, 13, 19):
-        o = philox.philox4x64_10(np.uint64(j >> 3), np.uint64(dk), 0, 0, seed, 0)
-        v = int(o[(j & 7) >> 1])
-        assert int(w[j]) == ((v >> 32) if (j & 1) else (v & 0xFFFFFFFF))
+    for level in (0, 1):
+        w = philox.words32(seed, dk, 20, level)
+        for j in (0, 1, 7, 8, 13, 19):
+            o = philox.philox4x64_10(np.uint64(j >> 3), np.uint64(dk), np.uint64(level), 0, seed, 0)
+            v = int(o[(j & 7) >> 1])
+            assert int(w[j]) == ((v >> 32) if (j & 1) else (v & 0xFFFFFFFF))
+    # the two levels are different streams
+    assert not np.array_equal(philox.words32(seed, dk, 64, 0), philox.words32(seed, dk, 64, 1))
 
 
 def test_gumbel_moments_and_gumbel_max_frequencies():
@@ -144,3 +147,74 @@ def test_gumbel_moments_and_gumbel_max_frequencies():
     lw = np.log(np.array([0.0, 1.0, 0.0, 2.0]))
     for key in range(200):
         assert philox.gumbel_argmax(lw, 5, key)[0] in (1, 3)
+
+
+# ------------------------------------------------- two-level Gumbel-max draw
+
+
+def _chi2(counts, expect):
+    return float(((counts - expect) ** 2 / expect).sum())
+
+
+@pytest.mark.parametrize("block", [4, 5, 16])
+def test_grouped_draw_frequencies_match_the_weights(block):
+    # 16 entries in blocks of 4 (even), 5 (ragged last block) and 16 (one block)
+    w = np.arange(1, 17, dtype=np.float64)
+    w[3] = 0.0                                  # a zero weight never wins
+    counts = np.zeros(16)
+    n = 16000
+    for key in range(n):
+        j, _ = philox.grouped_gumbel_argmax(np.log(np.where(w > 0, w, 1.0)) + np.where(w > 0, 0, -np.inf),
+                                            11, key, block=block)
+        counts[j] += 1
+    assert counts[3] == 0
+    keep = w > 0
+    expect = n * w[keep] / w.sum()
+    # 14 degrees of freedom: P(chi2 > 36.1) = 1e-3
+    assert _chi2(counts[keep], expect) < 36.1
+
+
+def test_grouped_draw_with_one_block_is_the_level0_gumbel_max():
+    r = np.random.default_rng(21)
+    for key in range(50):
+        lw = r.standard_normal(37) * 2
+        assert philox.grouped_gumbel_argmax(lw, 7, key, block=64) == philox.gumbel_argmax(lw, 7, key, 0)
+
+
+def test_grouped_draw_with_unit_blocks_is_the_level1_gumbel_max():
+    r = np.random.default_rng(22)
+    for key in range(50):
+        lw = r.standard_normal(29)
+        j, m = philox.grouped_gumbel_argmax(lw, 5, key, block=1)
+        j1, m1 = philox.gumbel_argmax(lw, 5, key, 1)
+        assert j == j1 and math.isclose(m, m1, rel_tol=1e-9, abs_tol=1e-12)
+
+
+def test_grouped_draw_block_choice_follows_block_masses():
+    # two blocks of two entries; block masses 1 : 3 -> P(block 1) = 3/4, and
+    # within block 1 entries in ratio 1 : 2
+    lw = np.log(np.array([0.5, 0.5, 1.0, 2.0]))
+    n = 12000
+    counts = np.zeros(4)
+    for key in range(n):
+        counts[philox.grouped_gumbel_argmax(lw, 3, key, block=2)[0]] += 1
+    expect = n * np.array([0.125, 0.125, 0.25, 0.5])
+    assert _chi2(counts, expect) < 16.3    # 3 degrees of freedom, P = 1e-3
+
+
+def test_grouped_draw_ignores_empty_blocks_and_reports_the_smaller_gap():
+    lw = np.full(12, -np.inf)
+    lw[9] = 0.0
+    for key in range(100):
+        assert philox.grouped_gumbel_argmax(lw, 1, key, block=4)[0] == 9
+    # margin: the smaller of the block-level and entry-level gaps
+    r = np.random.default_rng(23)
+    lw = r.standard_normal(10)
+    seed, key, blk = 4, 77, 4
+    j, m = philox.grouped_gumbel_argmax(lw, seed, key, block=blk)
+    Z = np.add.reduceat(np.exp(lw), np.arange(0, 10, blk))
+    s1 = np.log(Z) + philox.gumbel(seed, key, len(Z), level=1)
+    b = int(np.argmax(s1))
+    s2 = lw[b * blk:(b + 1) * blk] + philox.gumbel(seed, key, 10, level=0)[b * blk:(b + 1) * blk]
+    gaps = [np.sort(s1)[-1] - np.sort(s1)[-2], np.sort(s2)[-1] - np.sort(s2)[-2]]
+    assert j == b * blk + int(np.argmax(s2)) and math.isclose(m, min(gaps), rel_tol=1e-12)

@@ -230,14 +230,14 @@ def test_target_only_sampled_round_commits_the_target_picks():
     res = dmtp.run_round(inp)
     kinds = {k[0] for k, _, _ in res.decisions}
     assert "accept" not in kinds and "final" not in kinds     # no accept tests, no residual draws
-    from oracle.philox import gumbel_argmax
+    from oracle.philox import grouped_gumbel_argmax
     full = dmtp.run_round(inp, keep_logits=True)
     for r in range(cfg.B):
         y = res.target_argmax[r]
-        # every pick is the Gumbel-max draw of its row at the row's temperature
+        # every pick is the two-level Gumbel-max draw of its row at the row's temperature
         for i in range(cfg.K + 1):
-            want, _ = gumbel_argmax(full.p_logits[r, i] / inp.tau[r], int(inp.philox_seed),
-                                    int(inp.target_keys[r, i]))
+            want, _ = grouped_gumbel_argmax(full.p_logits[r, i] / inp.tau[r], int(inp.philox_seed),
+                                            int(inp.target_keys[r, i]))
             assert y[i] == want
         L = int(res.accept_len[r])
         assert np.array_equal(res.drafts[r, :L], y[:L])
