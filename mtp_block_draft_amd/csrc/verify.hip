@@ -25,16 +25,40 @@ namespace {
 // entries), one wave each: lane l takes the 8-entry groups l, l + 64, ...
 // (kScanU of them) and loads them all before any arithmetic; group u of lanes
 // 16 q .. 16 q + 15 is one block of kDrawBlock entries.
+// 512 entries of each row per work item and a grid that covers every item of
+// a batch-128 draw in one pass: measured faster than longer items (the pass is
+// short, so its memory latency chain dominates)
 #ifndef DMTP_MASS_U
-#define DMTP_MASS_U 2
+#define DMTP_MASS_U 1
 #endif
 #ifndef DMTP_MASS_GRID
-#define DMTP_MASS_GRID 4096
+#define DMTP_MASS_GRID 8192
+#endif
+#ifndef DMTP_MASS_NT
+#define DMTP_MASS_NT 0
 #endif
 constexpr int kScanWaves = 4;
 constexpr int kScanU = DMTP_MASS_U;
+
+// 16 bytes of a logits row that is read once (non-temporal when DMTP_MASS_NT)
+__device__ __forceinline__ float4 ld_row4(const float* q) {
+  if constexpr (DMTP_MASS_NT) {
+    const f32x4_t v = __builtin_nontemporal_load((const f32x4_t*)q);
+    return make_float4(v[0], v[1], v[2], v[3]);
+  }
+  return *(const float4*)q;
+}
 constexpr int kChunk = kWave * 8 * kScanU;
 static_assert(kChunk % kDrawBlock == 0 && kDrawBlock == 16 * 8, "block layout of a mass item");
+
+// Row pointers and lse values of a drawn sequence: the residual at row L
+// (p: target row K + L, q: candidate row L), or the bonus from target row 2K.
+struct DrawRows {
+  const float* pr;
+  const float* qr;
+  float lse_p, lse_q, it;
+  bool resid;
+};
 
 struct VerifyParams {
   int B, K, V;
@@ -60,86 +84,13 @@ struct VerifyParams {
   int32_t* mode;       // [B]: 0 greedy/done, 1 residual draw at row L, 2 bonus draw
   float* mass_r;       // [B, n_blocks] residual block masses (list order)
   float* mass_p;       // [B, n_blocks] block masses of p
+  DrawRows* draws;     // [B] rows and lse values of each listed draw (list order)
   int n_blocks, n_chunks;
 };
 
 __device__ __forceinline__ int cand(const VerifyParams& p, int b, int i) {
   return i == 0 ? p.t1[b] : p.drafts[(size_t)b * (p.K - 1) + i - 1];
 }
-
-__global__ void verify_main_kernel(VerifyParams p) {
-  __shared__ int32_t sc[1024];
-  __shared__ int32_t base;
-  if (threadIdx.x == 0) base = 0;
-  __syncthreads();
-  const int K = p.K, V = p.V;
-  for (int c0 = 0; c0 < p.B; c0 += blockDim.x) {
-    const int b = c0 + threadIdx.x;
-    int flag = 0;
-    if (b < p.B) {
-      // target-only verification compares with the target's picks at any temperature
-      const float t = (p.temperature && !p.target_only) ? p.temperature[b] : 0.f;
-      int L = 0, md = 0;
-      if (t > 0.f) {
-        const float it = 1.f / t;
-        const float* rows = p.logits + (size_t)b * (2 * K + 1) * V;
-        L = K;
-        for (int i = 0; i < K; ++i) {
-          const int d = cand(p, b, i);
-          bool acc = false;
-          if (d >= 0 && d < V) {
-            const float lq = rows[(size_t)i * V + d] * it -
-                             (i == 0 ? p.t1_lse[b] : p.draft_lse[(size_t)b * (K - 1) + i - 1]);
-            const float lp = rows[(size_t)(K + i) * V + d] * it - p.target_lse[(size_t)b * (K + 1) + i];
-            const float u = p.u_acc[(size_t)b * K + i];
-            acc = (u <= 0.f) || (logf(u) < lp - lq);
-          }
-          if (!acc) {
-            L = i;
-            break;
-          }
-        }
-        md = L < K ? 1 : 2;
-        flag = 1;
-      } else {
-        while (L < K && cand(p, b, L) == p.target[(size_t)b * (K + 1) + L]) ++L;
-      }
-      int32_t* out = p.out_tokens + (size_t)b * (K + 1);
-      for (int i = 0; i < L; ++i) out[i] = cand(p, b, i);
-      out[L] = md ? -1 : p.target[(size_t)b * (K + 1) + L];
-      for (int i = L + 1; i <= K; ++i) out[i] = -1;
-      p.accept_len[b] = L;
-      p.n_out[b] = L + 1;
-      p.mode[b] = md;
-    }
-    sc[threadIdx.x] = flag;
-    __syncthreads();
-    for (int o = 1; o < (int)blockDim.x; o <<= 1) {
-      const int v = threadIdx.x >= (unsigned)o ? sc[threadIdx.x - o] : 0;
-      __syncthreads();
-      sc[threadIdx.x] += v;
-      __syncthreads();
-    }
-    if (b < p.B) {
-      const int pos = base + sc[threadIdx.x] - flag;
-      p.list_pos[b] = flag ? pos : -1;
-      if (flag) p.list[pos] = b;
-    }
-    __syncthreads();
-    if (threadIdx.x == blockDim.x - 1) base += sc[threadIdx.x];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) p.count[0] = base;
-}
-
-// Row pointers and lse values of a drawn sequence: the residual at row L
-// (p: target row K + L, q: candidate row L), or the bonus from target row 2K.
-struct DrawRows {
-  const float* pr;
-  const float* qr;
-  float lse_p, lse_q, it;
-  bool resid;
-};
 
 __device__ __forceinline__ DrawRows draw_rows(const VerifyParams& p, int b) {
   const int K = p.K, V = p.V, L = p.accept_len[b];
@@ -153,6 +104,102 @@ __device__ __forceinline__ DrawRows draw_rows(const VerifyParams& p, int b) {
   r.lse_q = r.resid ? (L == 0 ? p.t1_lse[b] : p.draft_lse[(size_t)b * (K - 1) + L - 1]) : 0.f;
   return r;
 }
+
+__global__ __launch_bounds__(1024) void verify_main_kernel(VerifyParams p) {
+  __shared__ int32_t sc[1024 / kWave];
+  __shared__ int32_t base;
+  if (threadIdx.x == 0) base = 0;
+  __syncthreads();
+  const int K = p.K, V = p.V;
+  for (int c0 = 0; c0 < p.B; c0 += blockDim.x) {
+    const int b = c0 + threadIdx.x;
+    int flag = 0;
+    if (b < p.B) {
+      // target-only verification compares with the target's picks at any temperature
+      const float t = (p.temperature && !p.target_only) ? p.temperature[b] : 0.f;
+      int L = 0, md = 0;
+      // the candidates, their gathered logits and lse values and the uniforms
+      // of eight rows at a time are loaded before any test, so a sequence
+      // costs one memory latency per eight rows instead of one per row
+      constexpr int G = 8;
+      if (t > 0.f) {
+        const float it = 1.f / t;
+        const float* rows = p.logits + (size_t)b * (2 * K + 1) * V;
+        L = K;
+        for (int i0 = 0; i0 < K && L == K; i0 += G) {
+          int d[G];
+          float lq[G], lp[G], u[G];
+#pragma unroll
+          for (int g = 0; g < G; ++g) d[g] = i0 + g < K ? cand(p, b, i0 + g) : -1;
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            const int i = i0 + g;
+            lq[g] = lp[g] = 0.f;
+            u[g] = 1.f;
+            if (i < K && d[g] >= 0 && d[g] < V) {
+              lq[g] = rows[(size_t)i * V + d[g]] * it -
+                      (i == 0 ? p.t1_lse[b] : p.draft_lse[(size_t)b * (K - 1) + i - 1]);
+              lp[g] = rows[(size_t)(K + i) * V + d[g]] * it - p.target_lse[(size_t)b * (K + 1) + i];
+              u[g] = p.u_acc[(size_t)b * K + i];
+            }
+          }
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            const int i = i0 + g;
+            if (i >= K || L < K) continue;
+            const bool acc = d[g] >= 0 && d[g] < V && ((u[g] <= 0.f) || (logf(u[g]) < lp[g] - lq[g]));
+            if (!acc) L = i;
+          }
+        }
+        md = L < K ? 1 : 2;
+        flag = 1;
+      } else {
+        for (int i0 = 0; i0 < K && L == i0; i0 += G) {
+          int d[G], y[G];
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            d[g] = i0 + g < K ? cand(p, b, i0 + g) : -1;
+            y[g] = i0 + g < K ? p.target[(size_t)b * (K + 1) + i0 + g] : -2;
+          }
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+            if (L == i0 + g && i0 + g < K && d[g] == y[g]) ++L;
+        }
+      }
+      int32_t* out = p.out_tokens + (size_t)b * (K + 1);
+      for (int i = 0; i < L; ++i) out[i] = cand(p, b, i);
+      out[L] = md ? -1 : p.target[(size_t)b * (K + 1) + L];
+      for (int i = L + 1; i <= K; ++i) out[i] = -1;
+      p.accept_len[b] = L;
+      p.n_out[b] = L + 1;
+      p.mode[b] = md;
+    }
+    // exclusive prefix of the flags: within a wave by ballot, across waves
+    // through LDS (one barrier per pass over the batch)
+    const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
+    const uint64_t bal = __ballot(flag);
+    const int before = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) sc[wv] = __popcll(bal);
+    __syncthreads();
+    int off = base;
+    for (int w = 0; w < wv; ++w) off += sc[w];
+    int total = 0;
+    for (int w = 0; w < (int)(blockDim.x / kWave); ++w) total += sc[w];
+    if (b < p.B) {
+      const int pos = off + before;
+      p.list_pos[b] = flag ? pos : -1;
+      if (flag) {
+        p.list[pos] = b;
+        p.draws[pos] = draw_rows(p, b);
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) base += total;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) p.count[0] = base;
+}
+
 
 // p_j and the residual max(0, p_j - q_j) of one entry from its logits: with
 // a = log p_j and c = log q_j, the residual is p_j (1 - e^(c - a)) where a > c,
@@ -177,21 +224,21 @@ __global__ __launch_bounds__(kScanWaves * kWave) void verify_mass_kernel(VerifyP
   const bool vec = (V & 3) == 0;
   for (int item = blockIdx.x * kScanWaves + threadIdx.x / kWave; item < items; item += nw) {
     const int li = item / p.n_chunks, ch = item % p.n_chunks;
-    const DrawRows r = draw_rows(p, p.list[li]);
+    const DrawRows r = p.draws[li];
     const int base = ch * kChunk + 8 * lane;
     float sp[kScanU], sr[kScanU];
     if (vec && ch * kChunk + kChunk <= V) {
       float4 pa[kScanU], pb[kScanU], qa[kScanU], qb[kScanU];
 #pragma unroll
       for (int u = 0; u < kScanU; ++u) {
-        pa[u] = *(const float4*)(r.pr + base + 512 * u);
-        pb[u] = *(const float4*)(r.pr + base + 512 * u + 4);
+        pa[u] = ld_row4(r.pr + base + 512 * u);
+        pb[u] = ld_row4(r.pr + base + 512 * u + 4);
       }
       if (r.resid) {
 #pragma unroll
         for (int u = 0; u < kScanU; ++u) {
-          qa[u] = *(const float4*)(r.qr + base + 512 * u);
-          qb[u] = *(const float4*)(r.qr + base + 512 * u + 4);
+          qa[u] = ld_row4(r.qr + base + 512 * u);
+          qb[u] = ld_row4(r.qr + base + 512 * u + 4);
         }
       } else {
 #pragma unroll
@@ -266,7 +313,7 @@ __global__ __launch_bounds__(kFinThreads) void verify_final_kernel(VerifyParams 
   const int lane = threadIdx.x % kWave;
   const int li = p.list_pos[b];
   if (li < 0) return;   // the whole workgroup, before any barrier
-  DrawRows r = draw_rows(p, b);
+  DrawRows r = p.draws[li];
   const uint64_t key = p.final_key[b];
   const int nb = p.n_blocks;
   const float* mr = p.mass_r + (size_t)li * nb;
@@ -378,7 +425,7 @@ __global__ __launch_bounds__(kStatsThreads) void accept_stats_kernel(int B, int 
 }
 
 struct WsL {
-  size_t list, list_pos, count, mode, mass_r, mass_p, total;
+  size_t list, list_pos, count, mode, mass_r, mass_p, draws, total;
   int n_blocks, n_chunks;
 };
 
@@ -398,6 +445,8 @@ WsL layout(const dmtp_verify_desc& d) {
   if (draws) o = al(o + (size_t)d.B * w.n_blocks * sizeof(float));
   w.mass_p = o;
   if (draws) o = al(o + (size_t)d.B * w.n_blocks * sizeof(float));
+  w.draws = o;
+  if (draws) o = al(o + (size_t)d.B * sizeof(DrawRows));
   w.total = o;
   return w;
 }
@@ -434,9 +483,12 @@ hipError_t verify_run(const dmtp_verify_desc& d, void* ws, hipStream_t s) {
   p.mode = (int32_t*)(base + w.mode);
   p.mass_r = (float*)(base + w.mass_r);
   p.mass_p = (float*)(base + w.mass_p);
+  p.draws = (DrawRows*)(base + w.draws);
   p.n_blocks = w.n_blocks;
   p.n_chunks = w.n_chunks;
-  hipLaunchKernelGGL(verify_main_kernel, dim3(1), dim3(1024), 0, s, p);
+  // one workgroup; up to 1024 threads, whole waves, as many as the batch needs
+  const int vthreads = d.B >= 1024 ? 1024 : ((d.B + kWave - 1) / kWave) * kWave;
+  hipLaunchKernelGGL(verify_main_kernel, dim3(1), dim3(vthreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !d.temperature || d.target_only) return e;
   hipLaunchKernelGGL(verify_mass_kernel, dim3(DMTP_MASS_GRID), dim3(kScanWaves * kWave), 0, s, p);
