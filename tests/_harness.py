@@ -14,6 +14,8 @@ Tolerances
 """
 from __future__ import annotations
 
+import json
+import os
 from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
@@ -103,6 +105,7 @@ def compare_round(inp, g: Dict[str, np.ndarray], seqs: Optional[Sequence[int]] =
 
     idx = np.array(seqs)
     K, first = cfg.K, cfg.n_anchor
+    margins = [m for _, _, m in res.decisions]
     rep = {
         "h_fused": max_rel(g["h_fused"][idx], res.h_fused),
         "h_mtp": max_rel(g["h_mtp"][idx], res.h_mtp),
@@ -115,13 +118,33 @@ def compare_round(inp, g: Dict[str, np.ndarray], seqs: Optional[Sequence[int]] =
         "draft_max": max_rel(g["draft_max"][idx], res.q_max[:, 1:]),
         "target_max": max_rel(g["target_max"][idx], res.p_max),
         "exempt": exempt,
+        "overrides": overrides,
         "n_decisions": len(res.decisions),
+        "near_ties": int(sum(1 for m in margins if m < NEAR_TIE)),
+        "min_margin": float(min(margins)) if margins else float("inf"),
     }
+    # every exemption was a near-tie of the oracle when it was taken (checked
+    # above, decision by decision)
+    assert all(m < NEAR_TIE for _, m in exempt)
     for k in ("z1", "hd_mask", "draft_max", "target_max"):
         assert rep[k] <= VALUE_TOL, (k, rep[k])
     for k in ("h_fused", "h_mtp", "x_t1", "t1_lse", "draft_lse", "target_lse"):
         assert rep[k] <= F32_TOL, (k, rep[k])
     return res, rep
+
+
+def record(name: str, rep: dict) -> None:
+    """Append a parity summary of one comparison to the JSON-lines file named by
+    $DMTP_PARITY_RECORD (nothing when it is not set)."""
+    path = os.environ.get("DMTP_PARITY_RECORD")
+    line = {"case": name, "decisions": rep["n_decisions"], "near_ties": rep["near_ties"],
+            "exempt": len(rep["exempt"]), "exempt_keys": [list(map(str, k)) for k, _ in rep["exempt"]],
+            "min_margin": rep["min_margin"]}
+    line.update({k: v for k, v in rep.items() if isinstance(v, float) and k != "min_margin"})
+    print("PARITY " + json.dumps(line), flush=True)
+    if path:
+        with open(path, "a") as fh:
+            fh.write(json.dumps(line) + "\n")
 
 
 def correlated_targets(inp, rho: float) -> np.ndarray:

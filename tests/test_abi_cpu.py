@@ -16,7 +16,10 @@ abi = pytest.importorskip("mtp_block_draft_amd._abi")
 
 @pytest.fixture(scope="module")
 def lib():
-    return abi.load()
+    # DMTP_ABI_TEST_LIB: another build of the library to run these checks on
+    # (the host-sanitized one; see test_abi_sanitized.py)
+    path = os.environ.get("DMTP_ABI_TEST_LIB")
+    return abi.load(path) if path else abi.load()
 
 
 def test_exports_every_declared_function(lib):

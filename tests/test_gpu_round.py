@@ -16,7 +16,7 @@ torch = pytest.importorskip("torch")
 
 import dmtp_synth as synth  # noqa: E402
 
-from tests._harness import compare_round, correlated_targets, max_rel  # noqa: E402
+from tests._harness import compare_round, correlated_targets, max_rel, record  # noqa: E402
 
 
 @pytest.fixture(scope="module")
@@ -34,8 +34,10 @@ def _run(Round, inp, h_target=None):
 
 
 def _report(name, rep):
-    print(f"{name}: " + ", ".join(f"{k}={v:.2e}" for k, v in rep.items() if isinstance(v, float)),
-          f"exempt={rep['exempt']}", flush=True)
+    """Print and record the comparison; an exemption is only ever granted for a
+    near-tie of the oracle, so there are never more of them than near-ties."""
+    record(name, rep)
+    assert len(rep["exempt"]) <= rep["near_ties"], (name, rep["exempt"], rep["near_ties"])
 
 
 @pytest.mark.parametrize("w_zero", [False, True])
@@ -168,6 +170,22 @@ def test_chat_b128_mixed_full_size(rnd):
     res, rep = compare_round(inp, g, seqs=seqs)
     _report(cfg.name, rep)
     assert inp.tau[seqs].min() == 0 and inp.tau[seqs].max() > 0
+    # the float32 logits rows the head stores for sampled sequences, element by
+    # element against the oracle at the full vocabulary, for three sampled
+    # sequences (candidate rows 0..K-1, then target rows 0..K)
+    from oracle import dmtp as odm
+    logits = R.logits.view(cfg.B, 2 * cfg.K + 1, cfg.V)
+    sampled = [b for b in seqs if inp.tau[b] > 0][:3]
+    assert sampled
+    for b in sampled:
+        ov = {k: v for k, v in rep["overrides"].items() if k[1] == b}
+        ref = odm.run_round(inp, seqs=[b], overrides=ov, keep_logits=True)
+        want = np.concatenate([ref.q_logits[0], ref.p_logits[0]])        # [2K + 1, V]
+        got = logits[b].cpu().numpy().astype(np.float64)
+        scale = np.max(np.abs(want), axis=1, keepdims=True)
+        err = np.max(np.abs(got - want) / scale)
+        print(f"chat logits seq {b}: max |gpu - oracle| / row max = {err:.2e}", flush=True)
+        assert err < 2e-3, (b, err)
 
 
 @pytest.mark.timeout(900)
@@ -186,7 +204,7 @@ def test_long_block16_full_size(rnd):
     cfg = synth.CONFIGS["long_block16_bf16"]
     inp = synth.make_inputs(cfg)
     R, g = _run(rnd, inp)
-    res, rep = compare_round(inp, g, seqs=[0, 5])
+    res, rep = compare_round(inp, g, seqs=[0, 2, 5, 7])
     _report(cfg.name, rep)
 
 
@@ -196,7 +214,7 @@ def test_long_block16_anchor_window_full_size(rnd):
     cfg = synth.CONFIGS["long_block16_bf16"].with_(window=4096)
     inp = synth.make_inputs(cfg)
     R, g = _run(rnd, inp)
-    res, rep = compare_round(inp, g, seqs=[3])
+    res, rep = compare_round(inp, g, seqs=[3, 6])
     _report(f"{cfg.name}/window4096", rep)
 
 
