@@ -269,6 +269,31 @@ __device__ __forceinline__ int swz_val(int r) { return 2 * (r & 3); }
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
+// bf16 hi/lo planes of the pair (a, b), packed two to a word: the hi floats
+// are read back from the packed word by a byte permute (low half to the top,
+// zeros below) and a mask, instead of converting each value again.
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi2, uint32_t& lo2) {
+  const bf16x2_t h = {(__bf16)a, (__bf16)b};
+  hi2 = __builtin_bit_cast(uint32_t, h);
+  const float ha = __uint_as_float(__builtin_amdgcn_perm(0u, hi2, 0x01000c0cu));
+  const float hb = __uint_as_float(hi2 & 0xffff0000u);
+  const bf16x2_t l = {(__bf16)(a - ha), (__bf16)(b - hb)};
+  lo2 = __builtin_bit_cast(uint32_t, l);
+}
+
+// Buffer descriptor over `bytes` bytes from `base` (raw, dword data format):
+// the copies below address one K or V tile through it.
+typedef __amdgpu_buffer_rsrc_t buf_rsrc;
+__device__ __forceinline__ buf_rsrc make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// 16 bytes per lane from descriptor r at byte offset vo (this lane) + so
+// (uniform) to LDS at dst + 16 lane; non-temporal (the context is read once).
+__device__ __forceinline__ void buf_dma16(buf_rsrc r, uint32_t vo, uint32_t so, uint16_t* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, vo, so, 0, 2);
+}
+
 // Four bf16 of the transposing LDS read; see the V^T operand below.
 __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
   const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -283,8 +308,10 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
 // tiles than that, blockIdx.y also selects the group of tiles.
 constexpr int kAttnQtw = 4;
 
+// At most 256 registers, so that two waves share a SIMD (two multi-wave
+// workgroups a CU).
 template <int D, int NBUF>
-__global__ __launch_bounds__(64 * kAttnQtw) void attn_wave_kernel(
+__global__ __launch_bounds__(64 * kAttnQtw) __attribute__((amdgpu_waves_per_eu(2))) void attn_wave_kernel(
     const float* __restrict__ q, const uint16_t* __restrict__ ctx_k,
     const uint16_t* __restrict__ ctx_v, const int32_t* __restrict__ cu_ctx, int ctx_rows, int Hkv,
     int NQ, int NQP, int chunk, int n_chunks, int window, float scale, float* __restrict__ part_o,
@@ -316,35 +343,43 @@ __global__ __launch_bounds__(64 * kAttnQtw) void attn_wave_kernel(
   const int nt = (nkeys + C::KT - 1) / C::KT;
 
   // copies: instruction i of a tile moves key rows RPI i .. RPI i + RPI - 1;
-  // lane supplies row RPI i + lane / CPR, chunk position lane % CPR
-  const size_t row_stride = (size_t)Hkv * D;
-  const uint16_t* kbase = ctx_k + ((size_t)cu_ctx[b] + k_lo) * row_stride + (size_t)kvh * D;
-  const uint16_t* vbase = ctx_v + ((size_t)cu_ctx[b] + k_lo) * row_stride + (size_t)kvh * D;
+  // lane supplies row RPI i + lane / CPR, chunk position lane % CPR.  They are
+  // buffer copies over one tile's rows: the tile's first row is the
+  // descriptor's base, instruction i's first row a scalar offset, and the lane
+  // part a vector offset that depends on i only through the key swizzle, which
+  // repeats every KPER instructions (RPI KPER = 16 rows); the value swizzle
+  // reads r % 4 = lane row % 4 and does not depend on i.
+  constexpr int KPER = 16 / C::RPI;
+  static_assert(C::RPI % 4 == 0 && C::INSTR % KPER == 0, "copy layout");
+  const uint32_t row_bytes = (uint32_t)(Hkv * D * 2);
+  const size_t head0 = ((size_t)cu_ctx[b] + k_lo) * row_bytes + (size_t)kvh * D * 2;
+  const char* kbase = (const char*)ctx_k + head0;
+  const char* vbase = (const char*)ctx_v + head0;
   const int rr = lane / C::CPR, pos = lane % C::CPR;
-  uint32_t koff[C::INSTR], voff[C::INSTR];
+  uint32_t koff[KPER];
 #pragma unroll
-  for (int i = 0; i < C::INSTR; ++i) {
-    const int r = C::RPI * i + rr;
-    koff[i] = (uint32_t)(r * row_stride) + 8 * (pos ^ swz_key<D>(r));
-    voff[i] = (uint32_t)(r * row_stride) + 8 * (pos ^ swz_val(r));
-  }
+  for (int i = 0; i < KPER; ++i) koff[i] = rr * row_bytes + 16 * (pos ^ swz_key<D>(C::RPI * i + rr));
+  const uint32_t voff = rr * row_bytes + 16 * (pos ^ swz_val(rr));
   // context K/V is read once per call: non-temporal copies
   auto issue = [&](int t) __attribute__((always_inline)) {
     uint16_t* st = smem + (t % C::NBUF) * C::STAGE;
-    const size_t t0 = (size_t)C::KT * t * row_stride;
+    const size_t t0 = (size_t)C::KT * t * row_bytes;
+    const int tile_bytes = C::KT * (int)row_bytes;
+    const buf_rsrc kr = make_rsrc(kbase + t0, tile_bytes), vr = make_rsrc(vbase + t0, tile_bytes);
     if (C::KT * (t + 1) <= nkeys) {
 #pragma unroll
       for (int i = 0; i < C::INSTR; ++i) {
-        lds_dma16<2>(kbase + t0 + koff[i], st + i * 512);
-        lds_dma16<2>(vbase + t0 + voff[i], st + C::KT * D + i * 512);
+        const uint32_t r0 = (uint32_t)(C::RPI * i) * row_bytes;
+        buf_dma16(kr, koff[i % KPER], r0, st + i * 512);
+        buf_dma16(vr, voff, r0, st + C::KT * D + i * 512);
       }
     } else {   // last tile: rows past the chunk end repeat its last key (masked below)
 #pragma unroll
       for (int i = 0; i < C::INSTR; ++i) {
         const int r = C::RPI * i + rr;
-        const size_t row = (size_t)min(C::KT * t + r, nkeys - 1) * row_stride;
-        lds_dma16<2>(kbase + row + 8 * (pos ^ swz_key<D>(r)), st + i * 512);
-        lds_dma16<2>(vbase + row + 8 * (pos ^ swz_val(r)), st + C::KT * D + i * 512);
+        const uint32_t row = (uint32_t)min(r, nkeys - 1 - C::KT * t) * row_bytes;
+        buf_dma16(kr, row + 16 * (pos ^ swz_key<D>(r)), 0, st + i * 512);
+        buf_dma16(vr, row + 16 * (pos ^ swz_val(r)), 0, st + C::KT * D + i * 512);
       }
     }
   };
@@ -392,19 +427,19 @@ __global__ __launch_bounds__(64 * kAttnQtw) void attn_wave_kernel(
   for (int ds = 0; ds < C::DS; ++ds) k_frag[ds] = lr * D + (((2 * ds + g) ^ swz_key<D>(lr)) << 3);
   // transposing read: in each block of 16 lanes, source lane s points at
   // V[kb + s / 4][dd0 + 4 (s % 4) ..]; lane o of the block receives
-  // V[kb + j][dd0 + o], j = 0..3
+  // V[kb + j][dd0 + o], j = 0..3.  Key rows kb = 16 ks + 4 (blk / 2) + s / 4
+  // (and kb + 8) only add whole rows, since the value swizzle reads kb % 4; the
+  // chunk of column dd0 = 32 dt + .. is 4 dt + (0..3), and the swizzle (bits 1
+  // and 2) can flip bit 0 of dt only, so dt = 2, 3 sit 8 chunks after dt = 0, 1.
   const int blk = lane >> 4, sl = lane & 15;
-  int v_frag[2][C::DT][2];
+  int v_frag[2];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) {
-      const int dd = 32 * dt + 16 * (blk & 1) + 4 * (sl & 3);
-      const int ch = dd >> 3, half = (dd >> 2) & 1;
-      const int ka = 16 * ks + 4 * (blk >> 1) + (sl >> 2), kb2 = ka + 8;
-      v_frag[ks][dt][0] = C::KT * D + ka * D + ((ch ^ swz_val(ka)) << 3) + 4 * half;
-      v_frag[ks][dt][1] = C::KT * D + kb2 * D + ((ch ^ swz_val(kb2)) << 3) + 4 * half;
-    }
+  for (int e = 0; e < 2; ++e) {
+    const int dd = 32 * e + 16 * (blk & 1) + 4 * (sl & 3);
+    const int ch = dd >> 3, half = (dd >> 2) & 1;
+    const int ka = 4 * (blk >> 1) + (sl >> 2);
+    v_frag[e] = C::KT * D + ka * D + ((ch ^ swz_val(ka)) << 3) + 4 * half;
+  }
 
   for (int t = 0; t < nt; ++t) {
     if (issuer) wait_newer<C::PER_TILE, C::NBUF - 2>(min(nt - 1 - t, C::NBUF - 2));
@@ -456,7 +491,7 @@ __global__ __launch_bounds__(64 * kAttnQtw) void attn_wave_kernel(
       const float p0 = __builtin_amdgcn_exp2f(s[i] - m_run);
       const float p1 = __builtin_amdgcn_exp2f(s[i + 1] - m_run);
       ps += p0 + p1;
-      split2(p0, p1, ph[i / 2], pl[i / 2]);
+      split_pair(p0, p1, ph[i / 2], pl[i / 2]);
     }
     ps += shfl_xor(ps, 32);
     l_run += ps;
@@ -470,8 +505,9 @@ __global__ __launch_bounds__(64 * kAttnQtw) void attn_wave_kernel(
       const u32x4 pfl = u32x4{pl[4 * ks], pl[4 * ks + 1], pl[4 * ks + 2], pl[4 * ks + 3]};
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) {
-        const uint2 va = lds_read_tr16(st + v_frag[ks][dt][0]);
-        const uint2 vb = lds_read_tr16(st + v_frag[ks][dt][1]);
+        const uint16_t* vp = st + v_frag[dt & 1] + 64 * (dt >> 1) + 16 * ks * D;
+        const uint2 va = lds_read_tr16(vp);
+        const uint2 vb = lds_read_tr16(vp + 8 * D);
         const u32x4 vf = u32x4{va.x, va.y, vb.x, vb.y};
         o[dt] = mfma32(vf, pfh, o[dt]);
         o[dt] = mfma32(vf, pfl, o[dt]);
