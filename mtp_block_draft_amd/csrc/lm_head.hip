@@ -536,6 +536,273 @@ void head_gemm_mf32_kernel(HeadParams p, int n_mchunks) {
   }
 }
 
+// Buffer descriptor over `bytes` bytes from `base` (raw, dword data format).
+typedef __amdgpu_buffer_rsrc_t buf_rsrc;
+__device__ __forceinline__ buf_rsrc make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// 16 bytes per lane from descriptor r at byte offset vo (this lane) + so
+// (uniform) to LDS at dst + 16 lane; non-temporal (the weights are read once).
+__device__ __forceinline__ void buf_dma16(buf_rsrc r, uint32_t vo, uint32_t so, uint16_t* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, vo, so, 0, 2);
+}
+
+// 16 x 16 x 32 bf16 MFMA on fragments held as four words per lane
+__device__ __forceinline__ f32x4_t mfma16(const u32x4& a, const u32x4& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// ---- bf16 head GEMM, 16 x 16 x 32 MFMA, input fragments in registers.
+//
+// Workgroup: 4 waves on 128 vocabulary rows x 64 TQ input rows; wave w takes
+// all 128 vocabulary rows against 16 TQ input rows of its own (8 x TQ
+// accumulator tiles of 16 x 16).  Only the weight tile goes through LDS: a
+// ring of four 32-wide k-slices (8 KB each) filled by buffer loads with an LDS
+// destination and read by all four waves.  Each wave loads its input rows'
+// fragments of the next slice straight into registers (with the slice-major
+// input layout a 16-row fragment is one contiguous 1 KB read), so no input row
+// passes through LDS.  Per slice and workgroup, LDS takes 8 KB of copies and
+// 32 KB of fragment reads, against 36 KB and 72 KB for the 32 x 32 x 16
+// kernel above, whose waves share their input rows through LDS.
+template <int TQ, int NBUF_ = 4>
+struct HeadXr {
+  static constexpr int BV = 128, BK = 32, THREADS = 256;
+  static constexpr int NBUF = NBUF_;                   // weight stages
+  static constexpr int NU = BV / 16;                   // vocabulary tiles of 16 rows
+  static constexpr int RW = 16 * TQ;                   // input rows per wave
+  static constexpr int BB = 4 * RW;                    // input rows per workgroup
+  static constexpr int CPR = BK / 8;                   // 16-byte chunks per weight row
+  static constexpr int W_INSTR = BV * BK * 2 / 1024;   // 1 KB weight copies per slice
+  static constexpr int WPW = W_INSTR / 4;              // per wave
+  static constexpr int PER_WAVE = WPW + TQ;            // vector-memory instructions per wave and slice
+  static constexpr int STAGE = BV * BK;                // bf16 elements
+  static constexpr size_t LDS_BYTES = (size_t)NBUF * STAGE * 2;
+  static_assert(W_INSTR % 4 == 0 && NBUF >= 3 && PER_WAVE * (NBUF - 2) < 64, "copies");
+};
+
+template <int TQ>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void head_gemm_xr_kernel(HeadParams p, int n_mchunks) {
+  typedef HeadXr<TQ> C;
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  const int total = p.n_vtiles * n_mchunks;
+  const int per = (total + 7) / 8;   // XCD-contiguous ranges (workgroup i runs on XCD i % 8)
+  const int tt = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (tt >= total) return;
+  const int vt = tt / n_mchunks, mc = tt % n_mchunks;
+  const int v0 = vt * C::BV;
+  // the wave index is uniform across the wave: read from lane 0, so that the
+  // offsets derived from it stay in scalar registers
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int fr = lane & 15, fg = lane >> 4;
+  const int H = p.H, V = p.V, M = p.M;
+  const int rw0 = mc * C::BB + C::RW * wave;   // first input row of this wave
+
+  // Both operands are read through buffer descriptors, so that every address
+  // is a lane offset fixed for the whole kernel plus a scalar offset.
+  // Weight copy q of this wave: rows 16 (WPW wave + q) .. + 15 of the tile,
+  // lane idx = 64 (WPW wave + q) + lane supplying row idx / CPR, the chunk
+  // that lands at position idx % CPR.  The descriptor ends at row V, so the
+  // rows of the last tile past V read as zeros (their columns are masked).
+  const buf_rsrc wr = make_rsrc((const uint16_t*)p.W + (size_t)v0 * H, min(C::BV, V - v0) * H * 2);
+  uint32_t woff[C::WPW];
+  int wdst[C::WPW];
+#pragma unroll
+  for (int q = 0; q < C::WPW; ++q) {
+    const int idx = (wave * C::WPW + q) * 64 + lane, r = idx / C::CPR;
+    woff[q] = (uint32_t)(r * H * 2 + 16 * swz_chunk<C::BK>(r, idx % C::CPR));
+    wdst[q] = (wave * C::WPW + q) * 512;
+  }
+  // Input fragment t (B operand): row rw0 + 16 t + fr (clamped to M - 1; the
+  // results of rows past M are never written), k chunk fg of the slice; rows
+  // are row-major [M, H] or slice-major with k-slices of width BK.  The host
+  // keeps M H 2 below 2^31.
+  const buf_rsrc xr = make_rsrc(p.A, M * H * 2);
+  const uint32_t x_rs = p.a_sl ? C::BK : H;                     // elements between rows
+  const uint32_t x_ss = p.a_sl ? (uint32_t)M * C::BK : C::BK;   // elements between slices
+  uint32_t xoff[TQ];
+#pragma unroll
+  for (int t = 0; t < TQ; ++t) xoff[t] = ((uint32_t)min(rw0 + 16 * t + fr, M - 1) * x_rs + 8 * fg) * 2;
+
+  // Input fragments are loaded one slice ahead; three slices ahead (four
+  // register sets) measured slower, with three times the input loads in
+  // flight on the vector memory path beside the weight copies.
+  constexpr int XD = 1;                     // input slices loaded ahead
+  constexpr int XS = XD + 1;                // input register sets
+  constexpr int UF = 2;                     // steps per loop iteration (register sets static)
+  u32x4 xf[XS][TQ];   // input fragments, set = slice % XS
+  auto load_x = [&](int slice, int set) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < TQ; ++t)
+      xf[set][t] = __builtin_amdgcn_raw_buffer_load_b128(xr, xoff[t], (uint32_t)slice * x_ss * 2, 0);
+  };
+  auto issue_w = [&](int slice, int stage) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < C::WPW; ++q)
+      buf_dma16(wr, woff[q], (uint32_t)slice * C::BK * 2, smem + stage * C::STAGE + wdst[q]);
+  };
+  u32x4 wf[2][C::NU];   // weight fragments (A operand), double-buffered over slices
+  auto read_w = [&](int stage, int b) __attribute__((always_inline)) {
+    const uint16_t* st = smem + stage * C::STAGE;
+#pragma unroll
+    for (int u = 0; u < C::NU; ++u) wf[b][u] = *(const u32x4*)(st + swz_row<C::BK>(16 * u + fr, fg));
+  };
+
+  f32x4_t acc[C::NU][TQ];
+
+  // Per step k (slice k) the vector-memory instructions go out in one fixed
+  // order: the input loads of slice k + 1, then, after the barrier, the weight
+  // copies of slice k + NBUF into slice k's stage (read by every wave before
+  // that barrier).  Past the last slice the same instructions are issued again
+  // for the last slice (into a stage and an input set nobody reads), so that
+  // the order never changes.  At the wait of step k for slice k + 1's weights,
+  // copied at step k + 1 - NBUF, the (NBUF - 2) PER_WAVE most recent
+  // instructions are the input loads of slices k + 4 - NBUF .. k + 1 and the
+  // weight copies of slices k + 2 .. k + NBUF - 1: vmcnt of that many means
+  // slice k + 1's copies have landed (and older input loads, already
+  // consumed).  The first NBUF - 1 slices' copies land at the prologue's full
+  // wait.  The input loads of slice k + 1 are waited for by the compiler
+  // before the MFMAs that use them.
+  constexpr int WAIT_N = (C::NBUF - 2) * C::PER_WAVE;
+  const int nK = H / C::BK;   // even (H % 128 == 0)
+#pragma unroll
+  for (int s = 0; s < C::NBUF - 1; ++s) issue_w(min(s, nK - 1), s);
+#pragma unroll
+  for (int s = 0; s < XD; ++s) load_x(min(s, nK - 1), s);
+  wait_vm_lgkm0<0>();
+  ring_barrier();
+  read_w(0, 0);
+  issue_w(min(C::NBUF - 1, nK - 1), C::NBUF - 1);
+  // step k with register sets J (k = J modulo the set counts); FIRST: slice 0,
+  // whose MFMAs start from zero accumulators (an inline zero operand:
+  // accumulators that enter the loop as constants make the compiler move them
+  // between registers on every MFMA); NEXT: a slice k + 1 exists.  No MFMA
+  // sits under a run-time branch, so the accumulators stay in place from step
+  // to step.
+  auto step = [&](int k, auto J, auto FIRST, auto NEXT) __attribute__((always_inline)) {
+    constexpr int pb = decltype(J)::value % 2, xs = decltype(J)::value % XS;
+    constexpr bool first = decltype(FIRST)::value, next = decltype(NEXT)::value;
+    auto mfmas = [&](int u0, int u1) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = u0; u < u1; ++u)
+#pragma unroll
+        for (int t = 0; t < TQ; ++t)
+          acc[u][t] = mfma16(wf[pb][u], xf[xs][t], first ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc[u][t]);
+    };
+    // the scheduling barriers keep this order: left to itself the compiler
+    // sinks the input loads below the MFMAs, which undoes the prefetch
+    load_x(min(k + XD, nK - 1), (xs + XD) % XS);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(0, C::NU / 2);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (next) {
+      wait_vm_lgkm0<WAIT_N>();
+      ring_barrier();
+      read_w((k + 1) % C::NBUF, pb ^ 1);
+    }
+    issue_w(min(k + C::NBUF, nK - 1), k % C::NBUF);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(C::NU / 2, C::NU);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  const std::true_type Y;
+  const std::false_type N;
+  step(0, std::integral_constant<int, 0>{}, Y, Y);   // nK >= 4
+  // steps k0 + 1, k0 + 2 per iteration (nK is even), then the last step,
+  // without a next slice
+  int k0 = 0;
+  for (; k0 + UF < nK; k0 += UF) {
+    step(k0 + 1, std::integral_constant<int, 1>{}, N, Y);
+    step(k0 + 2, std::integral_constant<int, 2>{}, N, Y);
+  }
+  step(k0 + 1, std::integral_constant<int, 1>{}, N, N);
+  // the repeated copies of the last steps land before the workgroup ends
+  wait_vm_lgkm0<0>();
+
+  // per-row inputs of the epilogue
+  float t_in[TQ];   // temperature of the lane's row in tile t (1 when none given)
+  int s_in[TQ];     // logits store index of that row (-1: none)
+#pragma unroll
+  for (int t = 0; t < TQ; ++t) {
+    const int m = rw0 + 16 * t + fr;
+    const bool ok = m < M;
+    t_in[t] = (ok && p.temperature) ? p.temperature[m] : 1.f;
+    s_in[t] = (ok && p.store_row) ? p.store_row[m] : -1;
+  }
+
+  // ---- epilogue: per input row tile t, the lane holds 32 logits of its row
+  // (element e = 4 u + i at vocabulary column v0 + 16 u + 4 fg + i, rising with
+  // e); the four lane groups that share the row merge by two exchanges.
+  const int vl = v0 + 4 * fg;
+  auto off = [](int e) { return 16 * (e >> 2) + (e & 3); };
+  auto row_stats = [&](auto TAIL) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < TQ; ++t) {
+      const int row = rw0 + 16 * t + fr;
+      const float it = t_in[t] > 0.f ? 1.f / t_in[t] : 1.f;
+      const int srow = s_in[t] < p.logits_rows ? s_in[t] : -1;
+      float x[32];
+#pragma unroll
+      for (int e = 0; e < 32; ++e)
+        x[e] = (!decltype(TAIL)::value || vl + off(e) < V) ? acc[e >> 2][t][e & 3] : -INFINITY;
+      // largest and second largest (a repeated maximum counts twice) by a
+      // pairwise tree, then the lowest element holding the largest
+      float h[16], l[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        h[j] = hw_max(x[2 * j], x[2 * j + 1]);
+        l[j] = hw_min(x[2 * j], x[2 * j + 1]);
+      }
+#pragma unroll
+      for (int w = 16; w > 1; w >>= 1)
+#pragma unroll
+        for (int j = 0; j < w / 2; ++j) {
+          const float hh = hw_max(h[2 * j], h[2 * j + 1]);
+          l[j] = hw_max3(hw_min(h[2 * j], h[2 * j + 1]), l[2 * j], l[2 * j + 1]);
+          h[j] = hh;
+        }
+      const float v1 = h[0], v2 = l[0];
+      int e1 = 31;
+#pragma unroll
+      for (int e = 30; e >= 0; --e) e1 = x[e] == v1 ? e : e1;
+      // exp((x - v1) t^-1) as exp2(x sc - v1 sc)
+      const float sc = it * 1.4426950408889634f, bias = -v1 * sc;
+      float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 32; ++e) ps[e & 3] += hw_exp2(fmaf(x[e], sc, bias));
+      float sum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+      int i1 = vl + off(e1);
+      if (decltype(TAIL)::value && !(v1 > -INFINITY)) {   // lane wholly past V
+        sum = 0.f;
+        i1 = 0x7FFFFFFF;
+      }
+      if (srow >= 0) {
+        float* dst = p.logits + (size_t)srow * V + vl;
+#pragma unroll
+        for (int e = 0; e < 32; ++e)
+          if (!decltype(TAIL)::value || vl + off(e) < V) dst[off(e)] = x[e];
+      }
+      RowStat st{v1, sum, i1, v2};
+#pragma unroll
+      for (int mask = 16; mask < 64; mask <<= 1) {
+        RowStat o;
+        o.m = shfl_xor(st.m, mask);
+        o.s = shfl_xor(st.s, mask);
+        o.idx = shfl_xor(st.idx, mask);
+        o.v2 = shfl_xor(st.v2, mask);
+        st = stat_merge(st, o, it);
+      }
+      if (fg == 0 && row < M) p.part[(size_t)row * p.n_vtiles + vt] = st;
+    }
+  };
+  if (v0 + C::BV > V)
+    row_stats(std::true_type{});
+  else
+    row_stats(std::false_type{});
+}
+
 // Optional start/stop events of the vocabulary GEMM launch (both or neither).
 struct GemmEvents {
   hipEvent_t start = nullptr, stop = nullptr;
@@ -561,6 +828,20 @@ hipError_t launch_head_mf32(const HeadParams& p, int n_mchunks, const GemmEvents
 }
 
 
+template <int TQ>
+hipError_t launch_head_xr(const HeadParams& p, int n_mchunks, const GemmEvents& ev, hipStream_t s) {
+  typedef HeadXr<TQ> C;
+  static_assert(C::LDS_BYTES <= 160 * 1024, "head LDS");
+  const int total = p.n_vtiles * n_mchunks;
+  const dim3 grid(8 * ((total + 7) / 8));
+  if (ev.start && ev.stop)
+    hipExtLaunchKernelGGL((head_gemm_xr_kernel<TQ>), grid, dim3(C::THREADS), (uint32_t)C::LDS_BYTES, s,
+                          ev.start, ev.stop, 0u, p, n_mchunks);
+  else
+    hipLaunchKernelGGL((head_gemm_xr_kernel<TQ>), grid, dim3(C::THREADS), C::LDS_BYTES, s, p, n_mchunks);
+  return hipGetLastError();
+}
+
 // Row chunks of at most 448 rows, split evenly; TB = 64-row tiles per
 // workgroup.  One or two tiles (weight streaming): 64-wide slices, deep ring.
 // More: 32-wide slices, three stages, copies spread over the MFMAs.
@@ -573,7 +854,19 @@ int head_mf32_bk(int M) { return head_mf32_tb(M) <= 2 ? 64 : 32; }
 
 hipError_t launch_head_mf32_any(const HeadParams& p, const GemmEvents& ev, hipStream_t s) {
   const int nc = (p.M + 447) / 448;
-  switch (head_mf32_tb(p.M)) {
+  const int tb = head_mf32_tb(p.M);
+  // three or more 64-row tiles: the register-input kernel, which addresses the
+  // input rows through one buffer descriptor (byte offsets below 2^31)
+  if (tb >= 3 && (size_t)p.M * p.H * 2 < ((size_t)1 << 31)) {
+    switch (tb) {
+      case 3: return launch_head_xr<3>(p, nc, ev, s);
+      case 4: return launch_head_xr<4>(p, nc, ev, s);
+      case 5: return launch_head_xr<5>(p, nc, ev, s);
+      case 6: return launch_head_xr<6>(p, nc, ev, s);
+      default: return launch_head_xr<7>(p, nc, ev, s);
+    }
+  }
+  switch (tb) {
     case 1: return launch_head_mf32<1, 64>(p, nc, ev, s);
     case 2: return launch_head_mf32<2, 64>(p, nc, ev, s);
     case 3: return launch_head_mf32<3, 32, 3>(p, nc, ev, s);
