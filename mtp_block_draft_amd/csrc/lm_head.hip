@@ -91,6 +91,7 @@ struct HeadParams {
   int logits_rows;
   void* prepared;        // head input: [M, H], or [H / a_sl][M][a_sl] when a_sl > 0
   int a_sl;              // k-slice width of a slice-major prepared layout (0: row-major)
+  int a_frag;            // prepared rows in the fragment layout of the register-input GEMM
   const void* A;         // rows the GEMM reads: prepared, or the single input segment
   RowStat* part;         // [M, n_vtiles]
   int n_vtiles;
@@ -122,9 +123,15 @@ __global__ __launch_bounds__(kPrepThreads) void head_prep_kernel(HeadParams p) {
   const Seg sg = p.seg[si];
   const int H = p.H;
   // element i of this row: row-major, or inside k-slice i / a_sl of a
-  // slice-major layout (a_sl a multiple of 4, so a group of four stays whole)
+  // slice-major layout (a_sl a multiple of 4, so a group of four stays whole),
+  // or in the fragment layout: k-slices of 32 over the rows padded to a
+  // multiple of 16, each slice a run of 16-row tiles, each tile its four
+  // 8-element chunks in turn, each chunk the tile's 16 rows in turn
   const size_t orow = p.a_sl ? (size_t)blockIdx.x * p.a_sl : (size_t)blockIdx.x * H;
+  const size_t mp = ((size_t)p.M + 15) & ~(size_t)15;
+  const size_t ftile = (size_t)(blockIdx.x >> 4) * 512 + (blockIdx.x & 15) * 8;
   auto oidx = [&](int i) -> size_t {
+    if (p.a_frag) return (size_t)(i >> 5) * mp * 32 + ftile + ((i & 31) >> 3) * 128 + (i & 7);
     return p.a_sl ? (size_t)(i / p.a_sl) * p.M * p.a_sl + orow + (i % p.a_sl) : orow + i;
   };
   if (sg.g && H % 4 == 0 && H <= 8 * 4 * kPrepThreads) {
@@ -582,10 +589,10 @@ struct HeadXr {
   static_assert(W_INSTR % 4 == 0 && NBUF >= 3 && PER_WAVE * (NBUF - 2) < 64, "copies");
 };
 
-template <int TQ>
+template <int TQ, int NBUF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void head_gemm_xr_kernel(HeadParams p, int n_mchunks) {
-  typedef HeadXr<TQ> C;
+  typedef HeadXr<TQ, NBUF> C;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   const int total = p.n_vtiles * n_mchunks;
   const int per = (total + 7) / 8;   // XCD-contiguous ranges (workgroup i runs on XCD i % 8)
@@ -615,16 +622,21 @@ void head_gemm_xr_kernel(HeadParams p, int n_mchunks) {
     woff[q] = (uint32_t)(r * H * 2 + 16 * swz_chunk<C::BK>(r, idx % C::CPR));
     wdst[q] = (wave * C::WPW + q) * 512;
   }
-  // Input fragment t (B operand): row rw0 + 16 t + fr (clamped to M - 1; the
-  // results of rows past M are never written), k chunk fg of the slice; rows
-  // are row-major [M, H] or slice-major with k-slices of width BK.  The host
-  // keeps M H 2 below 2^31.
-  const buf_rsrc xr = make_rsrc(p.A, M * H * 2);
-  const uint32_t x_rs = p.a_sl ? C::BK : H;                     // elements between rows
-  const uint32_t x_ss = p.a_sl ? (uint32_t)M * C::BK : C::BK;   // elements between slices
+  // Input fragment t (B operand): row rw0 + 16 t + fr, k chunk fg of the
+  // slice.  In the fragment layout (the prep pass's, rows padded to Mp, a
+  // multiple of 16) lane l's 16 bytes sit at 16 l of the tile's 1 KB, so a
+  // load is one run in lane order; tiles past Mp are clamped to the last one.
+  // Row-major [M, H] input (the caller's prepared rows) clamps the row to
+  // M - 1.  Results of rows past M are never written.  The host keeps the
+  // input's bytes below 2^31.
+  const int Mp = (M + 15) & ~15;
+  const buf_rsrc xr = make_rsrc(p.A, (p.a_frag ? Mp : M) * H * 2);
+  const uint32_t x_ss = p.a_frag ? (uint32_t)Mp * C::BK : C::BK;   // elements between slices
   uint32_t xoff[TQ];
 #pragma unroll
-  for (int t = 0; t < TQ; ++t) xoff[t] = ((uint32_t)min(rw0 + 16 * t + fr, M - 1) * x_rs + 8 * fg) * 2;
+  for (int t = 0; t < TQ; ++t)
+    xoff[t] = p.a_frag ? ((uint32_t)min((rw0 >> 4) + t, (Mp >> 4) - 1) * 512 + 8 * lane) * 2
+                       : ((uint32_t)min(rw0 + 16 * t + fr, M - 1) * H + 8 * fg) * 2;
 
   // Input fragments are loaded one slice ahead; three slices ahead (four
   // register sets) measured slower, with three times the input loads in
@@ -835,10 +847,10 @@ hipError_t launch_head_xr(const HeadParams& p, int n_mchunks, const GemmEvents& 
   const int total = p.n_vtiles * n_mchunks;
   const dim3 grid(8 * ((total + 7) / 8));
   if (ev.start && ev.stop)
-    hipExtLaunchKernelGGL((head_gemm_xr_kernel<TQ>), grid, dim3(C::THREADS), (uint32_t)C::LDS_BYTES, s,
+    hipExtLaunchKernelGGL((head_gemm_xr_kernel<TQ, C::NBUF>), grid, dim3(C::THREADS), (uint32_t)C::LDS_BYTES, s,
                           ev.start, ev.stop, 0u, p, n_mchunks);
   else
-    hipLaunchKernelGGL((head_gemm_xr_kernel<TQ>), grid, dim3(C::THREADS), C::LDS_BYTES, s, p, n_mchunks);
+    hipLaunchKernelGGL((head_gemm_xr_kernel<TQ, C::NBUF>), grid, dim3(C::THREADS), C::LDS_BYTES, s, p, n_mchunks);
   return hipGetLastError();
 }
 
@@ -851,13 +863,16 @@ int head_mf32_tb(int M) {
 }
 // k-slice width of the kernel launch_head_mf32_any picks for M rows
 int head_mf32_bk(int M) { return head_mf32_tb(M) <= 2 ? 64 : 32; }
+// calls the register-input kernel takes: three or more 64-row tiles, input
+// rows (padded to a multiple of 16) addressed through one buffer descriptor
+bool head_xr_fits(int M, int H) {
+  return head_mf32_tb(M) >= 3 && ((size_t)(M + 15) & ~(size_t)15) * H * 2 < ((size_t)1 << 31);
+}
 
 hipError_t launch_head_mf32_any(const HeadParams& p, const GemmEvents& ev, hipStream_t s) {
   const int nc = (p.M + 447) / 448;
   const int tb = head_mf32_tb(p.M);
-  // three or more 64-row tiles: the register-input kernel, which addresses the
-  // input rows through one buffer descriptor (byte offsets below 2^31)
-  if (tb >= 3 && (size_t)p.M * p.H * 2 < ((size_t)1 << 31)) {
+  if (head_xr_fits(p.M, p.H)) {
     switch (tb) {
       case 3: return launch_head_xr<3>(p, nc, ev, s);
       case 4: return launch_head_xr<4>(p, nc, ev, s);
@@ -1359,7 +1374,7 @@ WsLayout ws_layout(const dmtp_head_desc& d, int M) {
   w.n_chunks = (d.V + kMassChunk - 1) / kMassChunk;
   const size_t esz = d.dtype == DMTP_BF16 ? 2 : 4;
   size_t o = 0;
-  w.prepared = o; o = align256(o + (size_t)M * d.H * esz);
+  w.prepared = o; o = align256(o + (size_t)(M + 15) * d.H * esz);   // rows padded for the fragment layout
   w.part = o; o = align256(o + (size_t)w.n_vtiles * M * sizeof(RowStat));
   w.amax = o; o = align256(o + (size_t)M * 4);
   w.gapg = o; o = align256(o + (size_t)M * 4);
@@ -1425,6 +1440,7 @@ hipError_t lm_head_run(const dmtp_head_desc& d, int M, void* ws, hipStream_t s) 
   // rows is read in place.
   const bool mf32 = d.dtype == DMTP_BF16 && d.H % 128 == 0;
   p.block_stats = mf32 && !head_t1_fits(d, M) && w.n_vtiles == w.n_blocks;
+  p.a_frag = mf32 && !d.prepared && !head_t1_fits(d, M) && head_xr_fits(M, d.H);
   p.a_sl = (mf32 && !d.prepared && head_mf32_bk(M) == 32) ? 32 : 0;
   const bool direct =
       !p.a_sl && d.n_seg == 1 && !d.seg[0].g_norm && d.seg[0].ld == d.H && !d.prepared;
