@@ -573,26 +573,28 @@ __device__ __forceinline__ f32x4_t mfma16(const u32x4& a, const u32x4& b, f32x4_
 // passes through LDS.  Per slice and workgroup, LDS takes 8 KB of copies and
 // 32 KB of fragment reads, against 36 KB and 72 KB for the 32 x 32 x 16
 // kernel above, whose waves share their input rows through LDS.
-template <int TQ, int NBUF_ = 4>
+template <int TQ, int NW_ = 4>
 struct HeadXr {
   static constexpr int BV = 128, BK = 32, THREADS = 256;
-  static constexpr int NBUF = NBUF_;                   // weight stages
+  static constexpr int WK = 64;                        // k-width of a weight stage (whole 128-byte lines)
+  static constexpr int NW = NW_;                       // weight stages
   static constexpr int NU = BV / 16;                   // vocabulary tiles of 16 rows
   static constexpr int RW = 16 * TQ;                   // input rows per wave
   static constexpr int BB = 4 * RW;                    // input rows per workgroup
-  static constexpr int CPR = BK / 8;                   // 16-byte chunks per weight row
-  static constexpr int W_INSTR = BV * BK * 2 / 1024;   // 1 KB weight copies per slice
+  static constexpr int CPR = WK / 8;                   // 16-byte chunks per weight row of a stage
+  static constexpr int W_INSTR = BV * WK * 2 / 1024;   // 1 KB weight copies per stage
   static constexpr int WPW = W_INSTR / 4;              // per wave
-  static constexpr int PER_WAVE = WPW + TQ;            // vector-memory instructions per wave and slice
-  static constexpr int STAGE = BV * BK;                // bf16 elements
-  static constexpr size_t LDS_BYTES = (size_t)NBUF * STAGE * 2;
-  static_assert(W_INSTR % 4 == 0 && NBUF >= 3 && PER_WAVE * (NBUF - 2) < 64, "copies");
+  static constexpr int STAGE = BV * WK;                // bf16 elements
+  static constexpr size_t LDS_BYTES = (size_t)NW * STAGE * 2;
+  // vector-memory instructions after a stage's copies at the wait for them
+  static constexpr int WAIT_N = (2 * NW - 2) * TQ + (NW - 2) * WPW;
+  static_assert(W_INSTR % 4 == 0 && NW >= 2 && WAIT_N < 64, "copies");
 };
 
-template <int TQ, int NBUF>
+template <int TQ, int NW>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void head_gemm_xr_kernel(HeadParams p, int n_mchunks) {
-  typedef HeadXr<TQ, NBUF> C;
+  typedef HeadXr<TQ, NW> C;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   const int total = p.n_vtiles * n_mchunks;
   const int per = (total + 7) / 8;   // XCD-contiguous ranges (workgroup i runs on XCD i % 8)
@@ -609,25 +611,27 @@ void head_gemm_xr_kernel(HeadParams p, int n_mchunks) {
 
   // Both operands are read through buffer descriptors, so that every address
   // is a lane offset fixed for the whole kernel plus a scalar offset.
-  // Weight copy q of this wave: rows 16 (WPW wave + q) .. + 15 of the tile,
-  // lane idx = 64 (WPW wave + q) + lane supplying row idx / CPR, the chunk
-  // that lands at position idx % CPR.  The descriptor ends at row V, so the
-  // rows of the last tile past V read as zeros (their columns are masked).
+  // A weight stage holds 64 k-values (one whole 128-byte line) of each of the
+  // tile's 128 rows.  Weight copy q of this wave: rows 8 (WPW wave + q) .. + 7
+  // of the tile, lane idx = 64 (WPW wave + q) + lane supplying row idx / CPR,
+  // the chunk that lands at position idx % CPR.  The descriptor ends at row V,
+  // so the rows of the last tile past V read as zeros (their columns are
+  // masked).
   const buf_rsrc wr = make_rsrc((const uint16_t*)p.W + (size_t)v0 * H, min(C::BV, V - v0) * H * 2);
   uint32_t woff[C::WPW];
   int wdst[C::WPW];
 #pragma unroll
   for (int q = 0; q < C::WPW; ++q) {
     const int idx = (wave * C::WPW + q) * 64 + lane, r = idx / C::CPR;
-    woff[q] = (uint32_t)(r * H * 2 + 16 * swz_chunk<C::BK>(r, idx % C::CPR));
+    woff[q] = (uint32_t)(r * H * 2 + 16 * swz_chunk<C::WK>(r, idx % C::CPR));
     wdst[q] = (wave * C::WPW + q) * 512;
   }
   // Input fragment t (B operand): row rw0 + 16 t + fr, k chunk fg of the
-  // slice.  In the fragment layout (the prep pass's, rows padded to Mp, a
-  // multiple of 16) lane l's 16 bytes sit at 16 l of the tile's 1 KB, so a
-  // load is one run in lane order; tiles past Mp are clamped to the last one.
-  // Row-major [M, H] input (the caller's prepared rows) clamps the row to
-  // M - 1.  Results of rows past M are never written.  The host keeps the
+  // 32-wide slice.  In the fragment layout (the prep pass's, rows padded to
+  // Mp, a multiple of 16) lane l's 16 bytes sit at 16 l of the tile's 1 KB, so
+  // a load is one run in lane order; tiles past Mp are clamped to the last
+  // one.  Row-major [M, H] input (the caller's prepared rows) clamps the row
+  // to M - 1.  Results of rows past M are never written.  The host keeps the
   // input's bytes below 2^31.
   const int Mp = (M + 15) & ~15;
   const buf_rsrc xr = make_rsrc(p.A, (p.a_frag ? Mp : M) * H * 2);
@@ -641,80 +645,83 @@ void head_gemm_xr_kernel(HeadParams p, int n_mchunks) {
   // Input fragments are loaded one slice ahead; three slices ahead (four
   // register sets) measured slower, with three times the input loads in
   // flight on the vector memory path beside the weight copies.
-  constexpr int XD = 1;                     // input slices loaded ahead
-  constexpr int XS = XD + 1;                // input register sets
-  constexpr int UF = 2;                     // steps per loop iteration (register sets static)
-  u32x4 xf[XS][TQ];   // input fragments, set = slice % XS
+  u32x4 xf[2][TQ];   // input fragments, set = slice % 2
   auto load_x = [&](int slice, int set) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < TQ; ++t)
       xf[set][t] = __builtin_amdgcn_raw_buffer_load_b128(xr, xoff[t], (uint32_t)slice * x_ss * 2, 0);
   };
-  auto issue_w = [&](int slice, int stage) __attribute__((always_inline)) {
+  auto issue_w = [&](int stage, int slot) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < C::WPW; ++q)
-      buf_dma16(wr, woff[q], (uint32_t)slice * C::BK * 2, smem + stage * C::STAGE + wdst[q]);
+      buf_dma16(wr, woff[q], (uint32_t)stage * C::WK * 2, smem + slot * C::STAGE + wdst[q]);
   };
-  u32x4 wf[2][C::NU];   // weight fragments (A operand), double-buffered over slices
-  auto read_w = [&](int stage, int b) __attribute__((always_inline)) {
-    const uint16_t* st = smem + stage * C::STAGE;
+  u32x4 wf[2][C::NU];   // weight fragments (A operand) of a 32-wide slice, double-buffered
+  // fragments of slice k: stage k / 2 (in slot (k / 2) % NW), chunks 4 (k % 2) + fg
+  auto read_w = [&](int k, int b) __attribute__((always_inline)) {
+    const uint16_t* st = smem + ((k >> 1) % C::NW) * C::STAGE;
 #pragma unroll
-    for (int u = 0; u < C::NU; ++u) wf[b][u] = *(const u32x4*)(st + swz_row<C::BK>(16 * u + fr, fg));
+    for (int u = 0; u < C::NU; ++u)
+      wf[b][u] = *(const u32x4*)(st + swz_row<C::WK>(16 * u + fr, 4 * (k & 1) + fg));
   };
 
   f32x4_t acc[C::NU][TQ];
 
-  // Per step k (slice k) the vector-memory instructions go out in one fixed
-  // order: the input loads of slice k + 1, then, after the barrier, the weight
-  // copies of slice k + NBUF into slice k's stage (read by every wave before
-  // that barrier).  Past the last slice the same instructions are issued again
-  // for the last slice (into a stage and an input set nobody reads), so that
-  // the order never changes.  At the wait of step k for slice k + 1's weights,
-  // copied at step k + 1 - NBUF, the (NBUF - 2) PER_WAVE most recent
-  // instructions are the input loads of slices k + 4 - NBUF .. k + 1 and the
-  // weight copies of slices k + 2 .. k + NBUF - 1: vmcnt of that many means
-  // slice k + 1's copies have landed (and older input loads, already
-  // consumed).  The first NBUF - 1 slices' copies land at the prologue's full
-  // wait.  The input loads of slice k + 1 are waited for by the compiler
-  // before the MFMAs that use them.
-  constexpr int WAIT_N = (C::NBUF - 2) * C::PER_WAVE;
-  const int nK = H / C::BK;   // even (H % 128 == 0)
+  // Per step k (32-wide slice k) the vector-memory instructions go out in one
+  // fixed order: the input loads of slice k + 1, then, at odd k only and after
+  // the barrier, the copies of stage (k + 1) / 2 + NW - 1 into the slot of
+  // stage (k - 1) / 2, whose last fragments every wave read before that
+  // barrier.  Past the last slice and stage the same instructions are issued
+  // again for the last ones (into a slot and an input set nobody reads), so
+  // the order never changes.  A step's fragments for slice k + 1 come from
+  // the stage of slice k at even k (no wait: that stage was waited for and
+  // shared at step k - 1) and from a new stage at odd k: there the wave waits
+  // until at most WAIT_N newer instructions are in flight -- the input loads
+  // of the 2 NW - 2 slices up to k + 1 and the copies of NW - 2 later stages
+  // -- so that stage (k + 1) / 2 has landed, then meets the others at the
+  // barrier.  The first NW - 1 stages land at the prologue's full wait.  The
+  // compiler waits for the input loads of slice k + 1 before the MFMAs that
+  // use them.
+  const int nK = H / C::BK;    // even (H % 128 == 0)
+  const int nS = nK / 2;       // weight stages
 #pragma unroll
-  for (int s = 0; s < C::NBUF - 1; ++s) issue_w(min(s, nK - 1), s);
-#pragma unroll
-  for (int s = 0; s < XD; ++s) load_x(min(s, nK - 1), s);
+  for (int s = 0; s < C::NW - 1; ++s) issue_w(min(s, nS - 1), s);
+  load_x(0, 0);
   wait_vm_lgkm0<0>();
   ring_barrier();
   read_w(0, 0);
-  issue_w(min(C::NBUF - 1, nK - 1), C::NBUF - 1);
-  // step k with register sets J (k = J modulo the set counts); FIRST: slice 0,
-  // whose MFMAs start from zero accumulators (an inline zero operand:
-  // accumulators that enter the loop as constants make the compiler move them
-  // between registers on every MFMA); NEXT: a slice k + 1 exists.  No MFMA
-  // sits under a run-time branch, so the accumulators stay in place from step
-  // to step.
+  issue_w(min(C::NW - 1, nS - 1), C::NW - 1);
+  // step k with register sets J (= k modulo 2); FIRST: slice 0, whose MFMAs
+  // start from zero accumulators (an inline zero operand: accumulators that
+  // enter the loop as constants make the compiler move them between registers
+  // on every MFMA); NEXT: a slice k + 1 exists.  No MFMA sits under a run-time
+  // branch, so the accumulators stay in place from step to step.
   auto step = [&](int k, auto J, auto FIRST, auto NEXT) __attribute__((always_inline)) {
-    constexpr int pb = decltype(J)::value % 2, xs = decltype(J)::value % XS;
+    constexpr int pb = decltype(J)::value % 2;   // = k % 2
     constexpr bool first = decltype(FIRST)::value, next = decltype(NEXT)::value;
     auto mfmas = [&](int u0, int u1) __attribute__((always_inline)) {
 #pragma unroll
       for (int u = u0; u < u1; ++u)
 #pragma unroll
         for (int t = 0; t < TQ; ++t)
-          acc[u][t] = mfma16(wf[pb][u], xf[xs][t], first ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc[u][t]);
+          acc[u][t] = mfma16(wf[pb][u], xf[pb][t], first ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc[u][t]);
     };
     // the scheduling barriers keep this order: left to itself the compiler
     // sinks the input loads below the MFMAs, which undoes the prefetch
-    load_x(min(k + XD, nK - 1), (xs + XD) % XS);
+    load_x(min(k + 1, nK - 1), pb ^ 1);
     __builtin_amdgcn_sched_barrier(0);
     mfmas(0, C::NU / 2);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (next) {
-      wait_vm_lgkm0<WAIT_N>();
-      ring_barrier();
-      read_w((k + 1) % C::NBUF, pb ^ 1);
+    if constexpr (pb == 0) {
+      if constexpr (next) read_w(k + 1, 1);
+    } else {
+      if constexpr (next) {
+        wait_vm_lgkm0<C::WAIT_N>();
+        ring_barrier();
+        read_w(k + 1, 0);
+      }
+      issue_w(min((k + 1) / 2 + C::NW - 1, nS - 1), ((k - 1) / 2) % C::NW);
     }
-    issue_w(min(k + C::NBUF, nK - 1), k % C::NBUF);
     __builtin_amdgcn_sched_barrier(0);
     mfmas(C::NU / 2, C::NU);
     __builtin_amdgcn_sched_barrier(0);
@@ -725,9 +732,9 @@ void head_gemm_xr_kernel(HeadParams p, int n_mchunks) {
   // steps k0 + 1, k0 + 2 per iteration (nK is even), then the last step,
   // without a next slice
   int k0 = 0;
-  for (; k0 + UF < nK; k0 += UF) {
+  for (; k0 + 2 < nK; k0 += 2) {
     step(k0 + 1, std::integral_constant<int, 1>{}, N, Y);
-    step(k0 + 2, std::integral_constant<int, 2>{}, N, Y);
+    step(k0 + 2, std::integral_constant<int, 0>{}, N, Y);
   }
   step(k0 + 1, std::integral_constant<int, 1>{}, N, N);
   // the repeated copies of the last steps land before the workgroup ends
@@ -847,10 +854,10 @@ hipError_t launch_head_xr(const HeadParams& p, int n_mchunks, const GemmEvents& 
   const int total = p.n_vtiles * n_mchunks;
   const dim3 grid(8 * ((total + 7) / 8));
   if (ev.start && ev.stop)
-    hipExtLaunchKernelGGL((head_gemm_xr_kernel<TQ, C::NBUF>), grid, dim3(C::THREADS), (uint32_t)C::LDS_BYTES, s,
+    hipExtLaunchKernelGGL((head_gemm_xr_kernel<TQ, C::NW>), grid, dim3(C::THREADS), (uint32_t)C::LDS_BYTES, s,
                           ev.start, ev.stop, 0u, p, n_mchunks);
   else
-    hipLaunchKernelGGL((head_gemm_xr_kernel<TQ, C::NBUF>), grid, dim3(C::THREADS), C::LDS_BYTES, s, p, n_mchunks);
+    hipLaunchKernelGGL((head_gemm_xr_kernel<TQ, C::NW>), grid, dim3(C::THREADS), C::LDS_BYTES, s, p, n_mchunks);
   return hipGetLastError();
 }
 
