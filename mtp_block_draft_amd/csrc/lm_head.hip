@@ -573,9 +573,19 @@ __device__ __forceinline__ f32x4_t mfma16(const u32x4& a, const u32x4& b, f32x4_
 // passes through LDS.  Per slice and workgroup, LDS takes 8 KB of copies and
 // 32 KB of fragment reads, against 36 KB and 72 KB for the 32 x 32 x 16
 // kernel above, whose waves share their input rows through LDS.
+// Input slices loaded ahead: one for 6 or 7 tiles per wave, three for fewer
+// (four register sets).  Each input load waits, in vmcnt's issue order, for
+// the weight copies issued before it, so the further ahead, the more of the
+// weights' HBM latency it covers; with 7 tiles three slices ahead measured
+// slower (about three times the input loads in flight on the vector memory
+// path beside the weight copies).
+constexpr int head_xr_xd(int TQ) { return TQ <= 5 ? 3 : 1; }
+
 template <int TQ, int NW_ = 4>
 struct HeadXr {
   static constexpr int BV = 128, BK = 32, THREADS = 256;
+  static constexpr int XD = head_xr_xd(TQ);            // input slices loaded ahead
+  static constexpr int XS = XD + 1;                    // input register sets
   static constexpr int WK = 64;                        // k-width of a weight stage (whole 128-byte lines)
   static constexpr int NW = NW_;                       // weight stages
   static constexpr int NU = BV / 16;                   // vocabulary tiles of 16 rows
@@ -588,6 +598,7 @@ struct HeadXr {
   static constexpr size_t LDS_BYTES = (size_t)NW * STAGE * 2;
   // vector-memory instructions after a stage's copies at the wait for them
   static constexpr int WAIT_N = (2 * NW - 2) * TQ + (NW - 2) * WPW;
+  static_assert(XS == 2 || XS == 4, "register sets");
   static_assert(W_INSTR % 4 == 0 && NW >= 2 && WAIT_N < 64, "copies");
 };
 
@@ -642,10 +653,8 @@ void head_gemm_xr_kernel(HeadParams p, int n_mchunks) {
     xoff[t] = p.a_frag ? ((uint32_t)min((rw0 >> 4) + t, (Mp >> 4) - 1) * 512 + 8 * lane) * 2
                        : ((uint32_t)min(rw0 + 16 * t + fr, M - 1) * H + 8 * fg) * 2;
 
-  // Input fragments are loaded one slice ahead; three slices ahead (four
-  // register sets) measured slower, with three times the input loads in
-  // flight on the vector memory path beside the weight copies.
-  u32x4 xf[2][TQ];   // input fragments, set = slice % 2
+  constexpr int XD = C::XD, XS = C::XS;
+  u32x4 xf[XS][TQ];   // input fragments, set = slice % XS
   auto load_x = [&](int slice, int set) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < TQ; ++t)
@@ -682,33 +691,35 @@ void head_gemm_xr_kernel(HeadParams p, int n_mchunks) {
   // barrier.  The first NW - 1 stages land at the prologue's full wait.  The
   // compiler waits for the input loads of slice k + 1 before the MFMAs that
   // use them.
-  const int nK = H / C::BK;    // even (H % 128 == 0)
+  const int nK = H / C::BK;    // a multiple of 4 (H % 128 == 0)
   const int nS = nK / 2;       // weight stages
 #pragma unroll
   for (int s = 0; s < C::NW - 1; ++s) issue_w(min(s, nS - 1), s);
-  load_x(0, 0);
+#pragma unroll
+  for (int s = 0; s < XD; ++s) load_x(min(s, nK - 1), s);
   wait_vm_lgkm0<0>();
   ring_barrier();
   read_w(0, 0);
   issue_w(min(C::NW - 1, nS - 1), C::NW - 1);
-  // step k with register sets J (= k modulo 2); FIRST: slice 0, whose MFMAs
-  // start from zero accumulators (an inline zero operand: accumulators that
-  // enter the loop as constants make the compiler move them between registers
-  // on every MFMA); NEXT: a slice k + 1 exists.  No MFMA sits under a run-time
-  // branch, so the accumulators stay in place from step to step.
+  // step k with register sets J (= k modulo XS): weight fragments k % 2,
+  // input set k % XS; FIRST: slice 0, whose MFMAs start from zero
+  // accumulators (an inline zero operand: accumulators that enter the loop as
+  // constants make the compiler move them between registers on every MFMA);
+  // NEXT: a slice k + 1 exists.  No MFMA sits under a run-time branch, so the
+  // accumulators stay in place from step to step.
   auto step = [&](int k, auto J, auto FIRST, auto NEXT) __attribute__((always_inline)) {
-    constexpr int pb = decltype(J)::value % 2;   // = k % 2
+    constexpr int pb = decltype(J)::value % 2, xs = decltype(J)::value % XS;
     constexpr bool first = decltype(FIRST)::value, next = decltype(NEXT)::value;
     auto mfmas = [&](int u0, int u1) __attribute__((always_inline)) {
 #pragma unroll
       for (int u = u0; u < u1; ++u)
 #pragma unroll
         for (int t = 0; t < TQ; ++t)
-          acc[u][t] = mfma16(wf[pb][u], xf[pb][t], first ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc[u][t]);
+          acc[u][t] = mfma16(wf[pb][u], xf[xs][t], first ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc[u][t]);
     };
     // the scheduling barriers keep this order: left to itself the compiler
     // sinks the input loads below the MFMAs, which undoes the prefetch
-    load_x(min(k + 1, nK - 1), pb ^ 1);
+    load_x(min(k + XD, nK - 1), (xs + XD) % XS);
     __builtin_amdgcn_sched_barrier(0);
     mfmas(0, C::NU / 2);
     __builtin_amdgcn_sched_barrier(0);
@@ -728,15 +739,33 @@ void head_gemm_xr_kernel(HeadParams p, int n_mchunks) {
   };
   const std::true_type Y;
   const std::false_type N;
+  typedef std::integral_constant<int, 1> J1;
+  typedef std::integral_constant<int, 2> J2;
+  typedef std::integral_constant<int, 3> J3;
+  typedef std::integral_constant<int, 4> J4;
   step(0, std::integral_constant<int, 0>{}, Y, Y);   // nK >= 4
-  // steps k0 + 1, k0 + 2 per iteration (nK is even), then the last step,
-  // without a next slice
+  // steps k0 + 1 .. k0 + XS per iteration (XS register sets; nK is a
+  // multiple of 4), then the last XS - 1 steps, the final one without a next
+  // slice.  (Two steps per iteration where two sets suffice: four measured
+  // slower there.)
   int k0 = 0;
-  for (; k0 + 2 < nK; k0 += 2) {
-    step(k0 + 1, std::integral_constant<int, 1>{}, N, Y);
-    step(k0 + 2, std::integral_constant<int, 0>{}, N, Y);
+  if constexpr (XS == 4) {
+    for (; k0 + 4 < nK; k0 += 4) {
+      step(k0 + 1, J1{}, N, Y);
+      step(k0 + 2, J2{}, N, Y);
+      step(k0 + 3, J3{}, N, Y);
+      step(k0 + 4, J4{}, N, Y);
+    }
+    step(k0 + 1, J1{}, N, Y);
+    step(k0 + 2, J2{}, N, Y);
+    step(k0 + 3, J3{}, N, N);
+  } else {
+    for (; k0 + 2 < nK; k0 += 2) {
+      step(k0 + 1, J1{}, N, Y);
+      step(k0 + 2, J2{}, N, Y);
+    }
+    step(k0 + 1, J1{}, N, N);
   }
-  step(k0 + 1, std::integral_constant<int, 1>{}, N, N);
   // the repeated copies of the last steps land before the workgroup ends
   wait_vm_lgkm0<0>();
 
