@@ -546,32 +546,38 @@ int dmtp_ctx_kv(const dmtp_ctx_desc* d, void* ws, size_t ws_bytes, hipStream_t s
   const int N = d->N, H = d->H, KF = d->n_feat * d->H, nkv = 2 * d->Hkv * d->d;
   const int wf32 = d->dtype == DMTP_F32;
   hipError_t h = hipSuccess;
+  // the projection's split-K partials are added by the first layer's norm,
+  // which also writes the finished rows to c; those of the K/V projection by
+  // the cache scatter
+  SplitOut sc{};
   if (wf32) {
     // float32 features and weights: the two-plane product
     h = to_planes(d->feats, d->dtype, (size_t)N * KF, planes, stream);
     if (h == hipSuccess) {
       GemmArgs g{planes, (size_t)N * KF, (size_t)KF, N, d->w_fc, wf32, (size_t)KF, H, KF, c,
                  (size_t)H, nullptr, 0};
-      h = gemm(g, gws, stream);
+      h = gemm_deferred(g, gws, stream, &sc);
     }
   } else {
     // bf16 features enter the projection as they are (one plane)
     GemmArgs g{(const uint16_t*)d->feats, 0, (size_t)KF, N, d->w_fc, wf32, (size_t)KF, H, KF, c,
                (size_t)H, nullptr, 0};
     g.a_planes = 1;
-    h = gemm(g, gws, stream);
+    h = gemm_deferred(g, gws, stream, &sc);
   }
   for (int l = 0; l < d->n_layers && h == hipSuccess; ++l) {
     const dmtp_layer& L = d->layers[l];
-    // RMSNorm(c; g_attn) as planes (the X output is not written)
-    if ((h = residual_rmsnorm(split_out_plain(c, (size_t)H, N, H), nullptr, (size_t)H, 0, L.g_attn,
-                              d->eps, xh, N, H, stream)) != hipSuccess)
+    // RMSNorm(c; g_attn) as planes; the first layer finishes c itself
+    const int finish_c = l == 0 && sc.splits > 1;
+    if ((h = residual_rmsnorm(l == 0 ? sc : split_out_plain(c, (size_t)H, N, H), finish_c ? c : nullptr,
+                              (size_t)H, finish_c, L.g_attn, d->eps, xh, N, H, stream)) != hipSuccess)
       break;
     const char* wkv = (const char*)L.wqkv + (size_t)d->Hq * d->d * H * esize(d->dtype);
     GemmArgs g{xh, (size_t)N * H, (size_t)H, N, wkv, wf32, (size_t)H, nkv, H, kv, (size_t)nkv,
                nullptr, 0};
-    if ((h = gemm(g, gws, stream)) != hipSuccess) break;
-    h = rope_scatter(kv, d->positions, d->dst_rows, N, d->Hkv, d->d, d->rope_base, d->dtype,
+    SplitOut skv{};
+    if ((h = gemm_deferred(g, gws, stream, &skv)) != hipSuccess) break;
+    h = rope_scatter(skv, d->positions, d->dst_rows, N, d->Hkv, d->d, d->rope_base, d->dtype,
                      d->ctx_rows, d->k_cache[l], d->v_cache[l], stream);
   }
   return launch_status(h);

@@ -375,8 +375,9 @@ __global__ void to_planes_kernel(const void* __restrict__ x, int dtype, size_t n
 
 // One workgroup per row: keys rotated at the row's position (angles in
 // float64, as in rope_split_kernel), keys and values stored in dtype at the
-// row's cache slot.
-__global__ __launch_bounds__(256) void rope_scatter_kernel(const float* __restrict__ kv,
+// row's cache slot.  The row is the split GEMM result's value (partials added
+// in split order, as the other consumers of a deferred GEMM do).
+__global__ __launch_bounds__(256) void rope_scatter_kernel(SplitOut o,
                                                            const int32_t* __restrict__ positions,
                                                            const int32_t* __restrict__ dst_rows,
                                                            int Hkv, int d, float rope_base, int dtype,
@@ -396,15 +397,33 @@ __global__ __launch_bounds__(256) void rope_scatter_kernel(const float* __restri
     cs[i] = cv;
   }
   __syncthreads();
-  const float* kr = kv + (size_t)r * 2 * Hkv * d;
-  const size_t o = (size_t)dst * Hkv * d;
-  for (int e = threadIdx.x; e < Hkv * half; e += blockDim.x) {
-    const int h = e / half, i = e % half;
-    const double a1 = kr[h * d + i], a2 = kr[h * d + i + half];
-    store_elem(k_cache, dtype, o + h * d + i, (float)(a1 * cs[i] - a2 * sn[i]));
-    store_elem(k_cache, dtype, o + h * d + i + half, (float)(a2 * cs[i] + a1 * sn[i]));
+  const size_t ob = (size_t)dst * Hkv * d;
+  // keys: four rotation pairs (i, i + d/2) per thread
+  for (int e = threadIdx.x; e < Hkv * half / 4; e += blockDim.x) {
+    const int h = (4 * e) / half, i0 = (4 * e) % half;
+    SplitAcc<4> p1, p2;
+    split_issue4(o, r, h * d + i0, p1);
+    split_issue4(o, r, h * d + i0 + half, p2);
+    const float4 x1 = split_finish4(o, r, h * d + i0, p1), x2 = split_finish4(o, r, h * d + i0 + half, p2);
+    const float a1[4] = {x1.x, x1.y, x1.z, x1.w}, a2[4] = {x2.x, x2.y, x2.z, x2.w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const double c = cs[i0 + t], sv = sn[i0 + t];
+      store_elem(k_cache, dtype, ob + h * d + i0 + t, (float)((double)a1[t] * c - (double)a2[t] * sv));
+      store_elem(k_cache, dtype, ob + h * d + i0 + half + t,
+                 (float)((double)a2[t] * c + (double)a1[t] * sv));
+    }
   }
-  for (int e = threadIdx.x; e < Hkv * d; e += blockDim.x) store_elem(v_cache, dtype, o + e, kr[Hkv * d + e]);
+  // values as they are
+  for (int e = threadIdx.x; e < Hkv * d / 4; e += blockDim.x) {
+    SplitAcc<8> pv;
+    split_issue4(o, r, Hkv * d + 4 * e, pv);
+    const float4 v = split_finish4(o, r, Hkv * d + 4 * e, pv);
+    store_elem(v_cache, dtype, ob + 4 * e + 0, v.x);
+    store_elem(v_cache, dtype, ob + 4 * e + 1, v.y);
+    store_elem(v_cache, dtype, ob + 4 * e + 2, v.z);
+    store_elem(v_cache, dtype, ob + 4 * e + 3, v.w);
+  }
 }
 
 // out[m] = value(m) in float32: the finished rows of a split GEMM result.
@@ -556,7 +575,7 @@ hipError_t to_planes(const void* x, int dtype, size_t n, uint16_t* planes, hipSt
   return hipGetLastError();
 }
 
-hipError_t rope_scatter(const float* kv, const int32_t* positions, const int32_t* dst_rows, int N,
+hipError_t rope_scatter(const SplitOut& kv, const int32_t* positions, const int32_t* dst_rows, int N,
                         int Hkv, int d, float rope_base, int dtype, int ctx_rows, void* k_cache,
                         void* v_cache, hipStream_t s) {
   hipLaunchKernelGGL(rope_scatter_kernel, dim3(N), dim3(256), 0, s, kv, positions, dst_rows, Hkv, d,

@@ -88,10 +88,11 @@ hipError_t swiglu(const SplitOut& g, const SplitOut& u, uint16_t* a, int rows, i
 // planes [2][n] (hi at planes, lo at planes + n) of n elements of x in dtype
 hipError_t to_planes(const void* x, int dtype, size_t n, uint16_t* planes, hipStream_t s);
 
-// Context cache rows: for row r of kv [N, 2 Hkv d] (keys then values), rotate
-// the keys at positions[r] and write both in dtype to k_cache / v_cache
-// [ctx_rows, Hkv, d] at row dst_rows[r] (skipped when out of range).
-hipError_t rope_scatter(const float* kv, const int32_t* positions, const int32_t* dst_rows, int N,
+// Context cache rows: for row r of kv = value of the split GEMM result [N,
+// 2 Hkv d] (keys then values; its partials are added here), rotate the keys at
+// positions[r] and write both in dtype to k_cache / v_cache [ctx_rows, Hkv, d]
+// at row dst_rows[r] (skipped when out of range).
+hipError_t rope_scatter(const SplitOut& kv, const int32_t* positions, const int32_t* dst_rows, int N,
                         int Hkv, int d, float rope_base, int dtype, int ctx_rows, void* k_cache,
                         void* v_cache, hipStream_t s);
 

@@ -359,6 +359,9 @@ def _draft_case(seed, dt, B, H, Hq, Hkv, d, F, NL, K, n_anchor, ctx_lens, V=500,
     # 144 slot rows, widths that end mid-tile, 48 query rows per kv head
     dict(B=9, H=320, Hq=6, Hkv=2, d=64, F=576, NL=1, K=15, n_anchor=2,
          ctx_lens=[0, 1, 31, 64, 100, 257, 513, 40, 9]),
+    # 200 slot rows: a ragged second 128-row tile in every projection
+    dict(B=25, H=1536, Hq=12, Hkv=4, d=128, F=1024, NL=1, K=7, n_anchor=2,
+         ctx_lens=[(37 * i) % 300 for i in range(25)]),
     # the largest block (32 candidates, 33 slots): three query tiles share a chunk's K/V
     dict(B=2, H=256, Hq=2, Hkv=1, d=64, F=256, NL=1, K=32, n_anchor=2, ctx_lens=[50, 0]),
     # 170 query rows per kv head: six query tiles, two workgroups of four (two waves idle)
@@ -493,7 +496,9 @@ def test_mtp_block(dm, dt, shape):
                                                 (300, 3, 2048, 16, 4, 128, 1),
                                                 # 150 rows: the two-plane layer GEMM on the 160-row
                                                 # tile, the bf16 feature GEMM on 128-row tiles
-                                                (150, 5, 512, 8, 2, 128, 2)])
+                                                (150, 5, 512, 8, 2, 128, 2),
+                                                # 200 rows of 1536: a ragged second 128-row tile
+                                                (200, 2, 1536, 12, 4, 128, 1)])
 def test_ctx_kv(dm, dt, N, NF, H, Hq, Hkv, d, NL):
     """Context K/V rows from target features, written into the named cache rows."""
     print(f"ctx_kv dt={dt} N={N} NF={NF} H={H} {Hq}/{Hkv}x{d} NL={NL}", flush=True)
