@@ -219,19 +219,28 @@ hipError_t run_stack(const Stack& d, const DraftWs& w, char* b, void* const* k_n
     if ((h = residual_rmsnorm(so, X, (size_t)d.H, 1, L.g_ffn, d.eps, xh, R, d.H, stream)) !=
         hipSuccess)
       break;
+    // gate and up projections of the same rows; bf16 weights as one GEMM over
+    // [Wg; Wu] (columns [0, F) the gate, [F, 2F) the up projection), whose
+    // epilogue applies the SwiGLU where the product needs no K split
+    bool act_done = false;
     if (!wf32) {
-      // gate and up projections of the same rows as one GEMM over [Wg; Wu]:
-      // columns [0, F) are the gate, [F, 2F) the up projection
       GemmArgs g3{xh, pst_h, (size_t)d.H, R, L.wg, wf32, (size_t)d.H, 2 * d.F, d.H, gate,
                   (size_t)2 * d.F, nullptr, 0};
       g3.B2 = L.wu;
       g3.N1 = d.F;
-      SplitOut sgu;
-      if ((h = gemm_deferred(g3, gws, stream, &sgu)) != hipSuccess) break;
-      sg = sgu;
-      su = sgu;
-      su.C = sgu.C + d.F;
-      if (su.splits > 1) su.part = sgu.part + d.F;
+      h = gemm_swiglu(g3, act, stream);
+      if (h == hipSuccess) {
+        act_done = true;
+      } else if (h == hipErrorNotSupported) {
+        SplitOut sgu;
+        if ((h = gemm_deferred(g3, gws, stream, &sgu)) != hipSuccess) break;
+        sg = sgu;
+        su = sgu;
+        su.C = sgu.C + d.F;
+        if (su.splits > 1) su.part = sgu.part + d.F;
+      } else {
+        break;
+      }
     } else {
       GemmArgs g3{xh, pst_h, (size_t)d.H, R, L.wg, wf32, (size_t)d.H, d.F, d.H, gate,
                   (size_t)d.F, nullptr, 0};
@@ -240,7 +249,7 @@ hipError_t run_stack(const Stack& d, const DraftWs& w, char* b, void* const* k_n
                   (size_t)d.F, nullptr, 0};
       if ((h = gemm_deferred(g4, gws2, stream, &su)) != hipSuccess) break;
     }
-    if ((h = swiglu(sg, su, act, R, d.F, stream)) != hipSuccess) break;
+    if (!act_done && (h = swiglu(sg, su, act, R, d.F, stream)) != hipSuccess) break;
     const size_t pst_f = (size_t)R * d.F;
     GemmArgs g5{act, pst_f, (size_t)d.F, R, L.wd, wf32, (size_t)d.F, d.H, d.F, X,
                 (size_t)d.H, X, (size_t)d.H};

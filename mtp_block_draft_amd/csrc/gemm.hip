@@ -36,6 +36,13 @@ struct GemmParams {
   float* part;   // [splits, M, N] when splits > 1
   const void* B2;  // rows n >= N1 of the weight come from B2 (NULL: B only)
   int N1;
+  // SwiGLU output (LDS-ring kernel, one split): B holds the gate rows and B2
+  // the up rows of F = N / 2 columns, taken as the interleaved matrix whose
+  // 32-row block b is gate rows 16 b .. 16 b + 15, then up rows 16 b ..
+  // 16 b + 15, so that each lane holds matching gate and up columns; act
+  // [2][M][F] receives the bf16 planes of silu(gate) * up and C is not
+  // written.  NULL: an ordinary product.
+  uint16_t* act = nullptr;
 };
 
 // ------------------------------------------------- bf16 weight, LDS ring ----
@@ -94,7 +101,10 @@ void gemm_dma_kernel(GemmParams p, int n_tiles_n, int n_tiles_m) {
     if (instr < T::W_INSTR) {
       const int idx = instr * 64 + lane, r = idx / T::CPR;
       const int wr = min(n0 + r, p.N - 1);
-      const uint16_t* wrow = (W2 && wr >= p.N1) ? W2 + (size_t)(wr - p.N1) * p.ldb : W + (size_t)wr * p.ldb;
+      const int gi = 16 * (wr >> 5) + (wr & 15);   // SwiGLU: gate / up row of interleaved row wr
+      const uint16_t* wrow = p.act ? ((wr & 16) ? W2 : W) + (size_t)gi * p.ldb
+                           : (W2 && wr >= p.N1) ? W2 + (size_t)(wr - p.N1) * p.ldb
+                                                : W + (size_t)wr * p.ldb;
       src[q] = wrow + 8 * swz_chunk<T::BK>(r, idx % T::CPR);
     } else {
       const int j = instr - T::W_INSTR, pl = j / (T::A_INSTR / T::AP);
@@ -212,6 +222,40 @@ void gemm_dma_kernel(GemmParams p, int n_tiles_n, int n_tiles_m) {
 
   // element i of acc[u][v]: weight row n = n0 + 32 (UN wn + u) + 8 (i / 4) + 4 lk + i % 4,
   // activation row m = m0 + 32 (UM wm + v) + lr; four consecutive n per store
+  if (p.act) {
+    // SwiGLU: elements i < 8 are gate columns 16 b + c (b = the 32-row
+    // block, c = 8 (i / 4) + 4 lk + i % 4), element i + 8 the up column of
+    // the same c; the lane writes four consecutive act columns from i = 0 .. 3
+    // and from 4 .. 7 as bf16 planes
+    const int F = p.N / 2;
+    const size_t pst = (size_t)p.M * F;
+#pragma unroll
+    for (int v = 0; v < T::UM; ++v) {
+      const int m = m0 + 32 * (T::UM * wm + v) + lr;
+      if (m >= p.M) continue;
+#pragma unroll
+      for (int u = 0; u < T::UN; ++u) {
+        const int nb = n0 + 32 * (T::UN * wn + u);
+        if (nb >= p.N) continue;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float a[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float g = acc[u][v][4 * h + i], up = acc[u][v][4 * h + i + 8];
+            a[i] = g / (1.0f + expf(-g)) * up;
+          }
+          uint32_t hi[2], lo[2];
+          split2(a[0], a[1], hi[0], lo[0]);
+          split2(a[2], a[3], hi[1], lo[1]);
+          const size_t j = (size_t)m * F + (nb >> 1) + 8 * h + 4 * lk;
+          *(uint2*)(p.act + j) = make_uint2(hi[0], hi[1]);
+          *(uint2*)(p.act + pst + j) = make_uint2(lo[0], lo[1]);
+        }
+      }
+    }
+    return;
+  }
   const bool split = p.splits > 1;
 #pragma unroll
   for (int v = 0; v < T::UM; ++v) {
@@ -766,6 +810,17 @@ hipError_t gemm_deferred(const GemmArgs& a, float* ws, hipStream_t s, SplitOut* 
             (a.M + TilePlanesF32::BM - 1) / TilePlanesF32::BM);
   hipLaunchKernelGGL(gemm_kernel<TilePlanesF32>, grid, dim3(TilePlanesF32::THREADS), 0, s, p);
   return hipGetLastError();
+}
+
+hipError_t gemm_swiglu(const GemmArgs& a, uint16_t* act, hipStream_t s) {
+  if (a.b_f32 || !a.B2 || a.N != 2 * a.N1 || a.N1 % 16 != 0 || !dma_ok(a) || skinny_fits(a.M, a.K))
+    return hipErrorNotSupported;
+  const DmaPlan pl = dma_plan(a.M, a.N, a.K, a.a_planes);
+  if (pl.splits != 1) return hipErrorNotSupported;
+  GemmParams p{a.A, a.a_pst, a.lda, a.M, a.B, a.ldb, a.N, a.K, 1, nullptr, 0, nullptr, 0, nullptr,
+               a.B2, a.N1};
+  p.act = act;
+  return launch_dma_any(p, pl, a.a_planes, s);
 }
 
 hipError_t gemm(const GemmArgs& a, float* ws, hipStream_t s) {

@@ -54,6 +54,12 @@ SplitOut split_out_plain(const float* C, size_t ldc, int M, int N);
 // The GEMM without its reduction pass: the reader of *out adds the partials.
 hipError_t gemm_deferred(const GemmArgs& a, float* ws, hipStream_t s, SplitOut* out);
 
+// act = silu(x Wgᵀ) * (x Wuᵀ) as bf16 planes [2][M][F] in one launch, for
+// bf16 weights B = Wg and B2 = Wu (N = 2 F, N1 = F, F % 16 == 0) where the
+// LDS-ring kernel takes the product without a K split; hipErrorNotSupported
+// (nothing launched) elsewhere.
+hipError_t gemm_swiglu(const GemmArgs& a, uint16_t* act, hipStream_t s);
+
 // The fusion projection out = res + W [RMSNorm(x1; g1); RMSNorm(x2; g2)] as
 // one weight-streaming GEMM with the norms folded in, plus a pass that adds
 // its split-K partials with each stream's 1 / rms and the residual.  For bf16
