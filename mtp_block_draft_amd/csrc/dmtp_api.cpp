@@ -556,8 +556,9 @@ int dmtp_ctx_kv(const dmtp_ctx_desc* d, void* ws, size_t ws_bytes, hipStream_t s
   const int wf32 = d->dtype == DMTP_F32;
   hipError_t h = hipSuccess;
   // the projection's split-K partials are added by the first layer's norm,
-  // which also writes the finished rows to c; those of the K/V projection by
-  // the cache scatter
+  // which also writes the finished rows to c; the K/V projection rotates and
+  // scatters in its own epilogue (three launches for one layer), or, where it
+  // cannot, the cache scatter adds its partials
   SplitOut sc{};
   if (wf32) {
     // float32 features and weights: the two-plane product
@@ -584,6 +585,11 @@ int dmtp_ctx_kv(const dmtp_ctx_desc* d, void* ws, size_t ws_bytes, hipStream_t s
     const char* wkv = (const char*)L.wqkv + (size_t)d->Hq * d->d * H * esize(d->dtype);
     GemmArgs g{xh, (size_t)N * H, (size_t)H, N, wkv, wf32, (size_t)H, nkv, H, kv, (size_t)nkv,
                nullptr, 0};
+    // bf16 weights: the K/V GEMM's epilogue rotates and scatters (no split);
+    // otherwise the scatter adds the split product's partials itself
+    h = gemm_rope_scatter(g, d->positions, d->dst_rows, d->Hkv, d->d, d->rope_base, d->dtype,
+                          d->ctx_rows, d->k_cache[l], d->v_cache[l], stream);
+    if (h != hipErrorNotSupported) continue;
     SplitOut skv{};
     if ((h = gemm_deferred(g, gws, stream, &skv)) != hipSuccess) break;
     h = rope_scatter(skv, d->positions, d->dst_rows, N, d->Hkv, d->d, d->rope_base, d->dtype,

@@ -67,9 +67,24 @@ struct DmaTile {
   static constexpr size_t LDS_BYTES = (size_t)NBUF * STAGE * 2;
 };
 
-template <class T>
+// Rotary cache scatter of a key/value projection, in place of C (the
+// 128 x 32 tiles, one split): row m of the product is [keys Hkv d | values
+// Hkv d]; its keys are rotated at positions[m] (pair (i, i + d / 2) of each
+// head turned by pos * base^(-2 i / d), angles in float64) and keys and values
+// stored in dtype at cache row dst_rows[m] ([rows, Hkv, d]; rows out of
+// range are skipped).
+struct RopeOut {
+  const int32_t* positions;
+  const int32_t* dst_rows;
+  void* k_cache;
+  void* v_cache;
+  int Hkv, d, dtype, rows;
+  float rope_base;
+};
+
+template <class T, int ROPE = 0>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gemm_dma_kernel(GemmParams p, int n_tiles_n, int n_tiles_m) {
+void gemm_dma_kernel(GemmParams p, int n_tiles_n, int n_tiles_m, RopeOut ro) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   const int total = n_tiles_n * n_tiles_m * p.splits;
   const int per = (total + 7) / 8;   // XCD-contiguous ranges (workgroup i runs on XCD i % 8)
@@ -222,6 +237,52 @@ void gemm_dma_kernel(GemmParams p, int n_tiles_n, int n_tiles_m) {
 
   // element i of acc[u][v]: weight row n = n0 + 32 (UN wn + u) + 8 (i / 4) + 4 lk + i % 4,
   // activation row m = m0 + 32 (UM wm + v) + lr; four consecutive n per store
+  if constexpr (ROPE) {
+    // the 32 x 128 tile through LDS (the ring is idle once every wave is past
+    // its last fragment reads), so that each rotation pair -- both halves of
+    // a head lie in the tile, d dividing 128 -- meets in one thread
+    static_assert(T::UN == 1 && T::UM == 1 && T::BN == 128 && T::BM == 32, "rope tile");
+    constexpr int LD = T::BN + 4;   // padded row of the exchange tile
+    float* xt = (float*)smem;
+    ring_barrier();
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *(float4*)(xt + lr * LD + 32 * wn + 8 * g + 4 * lk) =
+          make_float4(acc[0][0][4 * g], acc[0][0][4 * g + 1], acc[0][0][4 * g + 2], acc[0][0][4 * g + 3]);
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    ring_barrier();
+    const int d = ro.d, half = d / 2, hkd = ro.Hkv * d;
+    if (n0 < hkd) {
+      // keys: items (row, head, i < d / 2)
+      const double lnb = log((double)ro.rope_base);
+      for (int e = threadIdx.x; e < T::BM * 64; e += 256) {
+        const int r = e >> 6, j = e & 63, hl = j / half, i = j % half;
+        const int m = m0 + r;
+        if (m >= p.M) continue;
+        const int dst = ro.dst_rows[m];
+        if (dst < 0 || dst >= ro.rows) continue;
+        const double ang = (double)ro.positions[m] * exp(-(2.0 * i / d) * lnb);
+        double sv, cv;
+        sincos(ang, &sv, &cv);
+        const int c = hl * d + i;
+        const double a1 = xt[r * LD + c], a2 = xt[r * LD + c + half];
+        const size_t o = (size_t)dst * hkd + n0 + c;
+        store_elem(ro.k_cache, ro.dtype, o, (float)(a1 * cv - a2 * sv));
+        store_elem(ro.k_cache, ro.dtype, o + half, (float)(a2 * cv + a1 * sv));
+      }
+    } else {
+      // values as they are
+      for (int e = threadIdx.x; e < T::BM * T::BN; e += 256) {
+        const int r = e >> 7, c = e & 127;
+        const int m = m0 + r;
+        if (m >= p.M) continue;
+        const int dst = ro.dst_rows[m];
+        if (dst < 0 || dst >= ro.rows) continue;
+        store_elem(ro.v_cache, ro.dtype, (size_t)dst * hkd + (n0 - hkd) + c, xt[r * LD + c]);
+      }
+    }
+    return;
+  }
   if (p.act) {
     // SwiGLU: elements i < 8 are gate columns 16 b + c (b = the 32-row
     // block, c = 8 (i / 4) + 4 lk + i % 4), element i + 8 the up column of
@@ -391,14 +452,14 @@ bool dma_ok(const GemmArgs& a) {
          a.lda % 8 == 0 && a.ldb % 8 == 0 && a.a_pst % 8 == 0;
 }
 
-template <class T>
-hipError_t launch_dma(const GemmParams& p, const DmaPlan& pl, hipStream_t s) {
-  hipError_t e = hipFuncSetAttribute((const void*)gemm_dma_kernel<T>,
+template <class T, int ROPE = 0>
+hipError_t launch_dma(const GemmParams& p, const DmaPlan& pl, hipStream_t s, const RopeOut& ro = RopeOut{}) {
+  hipError_t e = hipFuncSetAttribute((const void*)gemm_dma_kernel<T, ROPE>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)T::LDS_BYTES);
   if (e != hipSuccess) return e;
   const int total = pl.tn * pl.tm * pl.splits;
-  hipLaunchKernelGGL(gemm_dma_kernel<T>, dim3(8 * ((total + 7) / 8)), dim3(256), T::LDS_BYTES, s, p,
-                     pl.tn, pl.tm);
+  hipLaunchKernelGGL((gemm_dma_kernel<T, ROPE>), dim3(8 * ((total + 7) / 8)), dim3(256), T::LDS_BYTES, s, p,
+                     pl.tn, pl.tm, ro);
   return hipGetLastError();
 }
 
@@ -810,6 +871,23 @@ hipError_t gemm_deferred(const GemmArgs& a, float* ws, hipStream_t s, SplitOut* 
             (a.M + TilePlanesF32::BM - 1) / TilePlanesF32::BM);
   hipLaunchKernelGGL(gemm_kernel<TilePlanesF32>, grid, dim3(TilePlanesF32::THREADS), 0, s, p);
   return hipGetLastError();
+}
+
+hipError_t gemm_rope_scatter(const GemmArgs& a, const int32_t* positions, const int32_t* dst_rows,
+                             int Hkv, int d, float rope_base, int dtype, int ctx_rows, void* k_cache,
+                             void* v_cache, hipStream_t s) {
+  if (a.b_f32 || a.a_planes != 2 || a.B2 || a.N != 2 * Hkv * d || (Hkv * d) % 128 != 0 || 128 % d != 0 ||
+      !dma_ok(a))
+    return hipErrorNotSupported;
+  DmaPlan pl;
+  pl.cfg = 0;
+  pl.tn = a.N / DmaM32::BN;
+  pl.tm = (a.M + DmaM32::BM - 1) / DmaM32::BM;
+  pl.splits = 1;
+  GemmParams p{a.A, a.a_pst, a.lda, a.M, a.B, a.ldb, a.N, a.K, 1, nullptr, 0, nullptr, 0, nullptr,
+               nullptr, a.N};
+  const RopeOut ro{positions, dst_rows, k_cache, v_cache, Hkv, d, dtype, ctx_rows, rope_base};
+  return launch_dma<DmaM32, 1>(p, pl, s, ro);
 }
 
 hipError_t gemm_swiglu(const GemmArgs& a, uint16_t* act, hipStream_t s) {

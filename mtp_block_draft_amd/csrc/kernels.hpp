@@ -54,6 +54,18 @@ SplitOut split_out_plain(const float* C, size_t ldc, int M, int N);
 // The GEMM without its reduction pass: the reader of *out adds the partials.
 hipError_t gemm_deferred(const GemmArgs& a, float* ws, hipStream_t s, SplitOut* out);
 
+// The key/value rows of a layer for the context cache in one launch: the
+// product of the two-plane rows A [M, K] with the bf16 key/value weight rows
+// B [2 Hkv d, K] (keys, then values), unsplit on 128 x 32 tiles, whose
+// epilogue rotates the keys at positions[m] and stores keys and values in
+// dtype at cache row dst_rows[m] (skipped when out of [0, ctx_rows)), as
+// rope_scatter does with a finished product.  hipErrorNotSupported (nothing
+// launched) for other weights or shapes (d must divide 128 and 128 divide
+// Hkv d).
+hipError_t gemm_rope_scatter(const GemmArgs& a, const int32_t* positions, const int32_t* dst_rows,
+                             int Hkv, int d, float rope_base, int dtype, int ctx_rows, void* k_cache,
+                             void* v_cache, hipStream_t s);
+
 // act = silu(x Wgᵀ) * (x Wuᵀ) as bf16 planes [2][M][F] in one launch, for
 // bf16 weights B = Wg and B2 = Wu (N = 2 F, N1 = F, F % 16 == 0) where the
 // LDS-ring kernel takes the product without a K split; hipErrorNotSupported
