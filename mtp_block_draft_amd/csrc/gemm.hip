@@ -506,34 +506,67 @@ __device__ __forceinline__ void add4f(float4& s, const float4& v) {
 // the 16 lanes of one read pass land on the 16 positions of the bank window.
 __device__ __forceinline__ int sk_swz(int r, int c) { return c ^ (r & 15); }
 
+// Copy of the stream wave's 32 x 128 piece of weight tile t (rows 32 t .. 32 t
+// + 31, k0 .. k0 + 127) into ring stage st: copy i covers rows 4 i .. 4 i + 3
+// (lane / 16), chunk position lane % 16.
+__device__ __forceinline__ void sk_issue(const GemmParams& p, int k0, int t, int lane, uint16_t* st) {
+  const int n0 = 32 * t;
+  const uint16_t* __restrict__ W = (const uint16_t*)p.B;
+  const uint16_t* __restrict__ W2 = (const uint16_t*)p.B2;
+#pragma unroll
+  for (int i = 0; i < kSkCopies; ++i) {
+    const int r = 4 * i + (lane >> 4);
+    const int n = min(n0 + r, p.N - 1);
+    const uint16_t* wrow = (W2 && n >= p.N1) ? W2 + (size_t)(n - p.N1) * p.ldb : W + (size_t)n * p.ldb;
+    lds_dma16(wrow + k0 + 8 * sk_swz(r, lane & 15), st + 512 * i);
+  }
+}
+
+// The copies of a stream wave's first tiles (as many as its ring takes before
+// the loop), issued right after its activation loads: the loads, older, are
+// waited for alone (vmcnt counts in issue order), and the copies' latency
+// passes under the work on the loaded rows.  Returns how many were issued.
+// The same copies through a buffer descriptor over the weight rows (no second
+// matrix), whose offsets the compiler tracks as plain loads.
+__device__ __forceinline__ void sk_issue_buf(__amdgpu_buffer_rsrc_t wr, const GemmParams& p, int k0, int t,
+                                             int lane, uint16_t* st) {
+  const int n0 = 32 * t;
+#pragma unroll
+  for (int i = 0; i < kSkCopies; ++i) {
+    const int r = 4 * i + (lane >> 4);
+    const int n = min(n0 + r, p.N - 1);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        wr, (__attribute__((address_space(3))) void*)(st + 512 * i), 16,
+        (uint32_t)((size_t)n * p.ldb + k0 + 8 * sk_swz(r, lane & 15)) * 2, 0, 0, 0);
+  }
+}
+
+// All of them go out whatever my is (past the run's last tile the rows are
+// clamped into the matrix and the stage is never read; the ring's waits
+// cover them), so that the count of instructions after the loads is known
+// where the loads are waited for: past a branch around some of the copies
+// the compiler would wait for all of them.
+__device__ __forceinline__ int sk_issue_first(const GemmParams& p, int k0, int t0, int lane, int wave,
+                                              uint16_t* smem) {
+  uint16_t* ring = smem + wave * kSkNB * kSkStage;
+#pragma unroll
+  for (int q = 0; q < kSkNB - 1; ++q) sk_issue(p, k0, t0 + q, lane, ring + q * kSkStage);
+  return kSkNB - 1;
+}
+
 // The stream waves' part of a skinny workgroup once their activation
-// registers xf hold k0 .. k0 + 127 of the rows: copy each tile's 32 x 128
-// weight piece through the wave's own ring, multiply, and hand the partial
-// tile to the sum wave through LDS.
+// registers xf hold k0 .. k0 + 127 of the rows and the copies of the first
+// `issued` tiles are on their way: copy each tile's 32 x 128 weight piece
+// through the wave's own ring, multiply, and hand the partial tile to the sum
+// wave through LDS.
 template <int AP>
 __device__ __forceinline__ void skinny_stream(const GemmParams& p, const u32x4 (&xf)[AP][kSkBK / 16],
-                                              int k0, int t0, int my, int lane, int wave,
+                                              int k0, int t0, int my, int issued, int lane, int wave,
                                               uint16_t* smem, float* red) {
   constexpr int KPS = kSkBK / 16;                // k-steps per stage
   const int lr = lane & 31, lk = lane >> 5;
-  const int N = p.N;
-  const uint16_t* __restrict__ W = (const uint16_t*)p.B;
-  const uint16_t* __restrict__ W2 = (const uint16_t*)p.B2;
   uint16_t* ring = smem + wave * kSkNB * kSkStage;
-  // tile q of the run: weight rows 32 (t0 + q) .. + 31; copy i covers rows
-  // 4 i .. 4 i + 3 (lane / 16), chunk position lane % 16
-  auto issue = [&](int q) __attribute__((always_inline)) {
-    const int n0 = 32 * (t0 + q);
-    uint16_t* st = ring + (q % kSkNB) * kSkStage;
-#pragma unroll
-    for (int i = 0; i < kSkCopies; ++i) {
-      const int r = 4 * i + (lane >> 4);
-      const int n = min(n0 + r, N - 1);
-      const uint16_t* wrow = (W2 && n >= p.N1) ? W2 + (size_t)(n - p.N1) * p.ldb : W + (size_t)n * p.ldb;
-      lds_dma16(wrow + k0 + 8 * sk_swz(r, lane & 15), st + 512 * i);
-    }
-  };
-  for (int q = 0; q < kSkNB - 1 && q < my; ++q) issue(q);
+  for (int q = issued; q < kSkNB - 1 && q < my; ++q) sk_issue(p, k0, t0 + q, lane, ring + q * kSkStage);
   for (int tile = 0; tile < my; ++tile) {
     // tile has landed once only the copies issued after it may be
     // outstanding; lgkmcnt(0) too, since the stage refilled below was read
@@ -550,7 +583,8 @@ __device__ __forceinline__ void skinny_stream(const GemmParams& p, const u32x4 (
     for (int jj = 0; jj < KPS; ++jj)
 #pragma unroll
       for (int pl = 0; pl < AP; ++pl) acc = mfma32(wf[jj], xf[pl][jj], acc);
-    if (tile + kSkNB - 1 < my) issue(tile + kSkNB - 1);
+    if (tile + kSkNB - 1 < my)
+      sk_issue(p, k0, t0 + tile + kSkNB - 1, lane, ring + ((tile + kSkNB - 1) % kSkNB) * kSkStage);
     float* rb = red + (size_t)(tile & 1) * kSkRed + wave * 16 * kWave;
 #pragma unroll
     for (int i = 0; i < 16; ++i) rb[i * kWave + lane] = acc[i];
@@ -615,9 +649,10 @@ __global__ __launch_bounds__(kSkThreads) void gemm_skinny_kernel(GemmParams p, i
     for (int pl = 0; pl < AP; ++pl)
 #pragma unroll
       for (int jj = 0; jj < KPS; ++jj) xf[pl][jj] = *(const u32x4*)(xr + pl * p.a_pst + 16 * jj);
-    // complete before the first copy, so no later wait for them drains the ring
-    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
-    skinny_stream<AP>(p, xf, k0, t0, my, lane, wave, smem, red);
+    __builtin_amdgcn_sched_barrier(0);
+    const int issued = sk_issue_first(p, k0, t0, lane, wave, smem);
+    __builtin_amdgcn_sched_barrier(0);
+    skinny_stream<AP>(p, xf, k0, t0, my, issued, lane, wave, smem, red);
     return;
   }
   skinny_sum(p, z, t0, my, lane, red);
@@ -685,6 +720,108 @@ __device__ __forceinline__ void fuse_load8(const FuseSrc& f, int s, int r, int k
   }
 }
 
+// Row r of stream s: where it starts, in what dtype, and whether it reads as
+// zeros (an id outside the table; base then points at row 0).
+// (The stream's fields are picked by selects, not by indexing with s: an
+// array indexed at run time would be read from memory, one more latency.)
+__device__ __forceinline__ void fuse_row(const FuseSrc& f, int s, int r, const void*& base, int& dt,
+                                         bool& zero) {
+  const void* rows = s ? f.rows[1] : f.rows[0];
+  dt = s ? f.dtype[1] : f.dtype[0];
+  zero = false;
+  const size_t esz = dt == DMTP_BF16 ? 2 : 4;
+  if (rows) {
+    base = (const char*)rows + (size_t)r * f.H * esz;
+  } else {
+    const int id = (s ? f.ids[1] : f.ids[0])[r];
+    zero = id < 0 || id >= (s ? f.n_table[1] : f.n_table[0]);
+    base = (const char*)(s ? f.table[1] : f.table[0]) + (size_t)(zero ? 0 : id) * f.H * esz;
+  }
+}
+
+// A stream wave of the fused projection, for rows stored as bf16 (BF) or
+// float32: the row's start first (an id lookup), then all of its loads and
+// the gains' in flight together, then the first weight copies (waited for
+// later, by the ring), then the arithmetic on the rows: two memory latencies,
+// the second beside the copies'.  One straight-line body per dtype, so that
+// the compiler counts the loads still in flight at each use.
+template <bool BF>
+__device__ __forceinline__ void fuse_stream(const GemmParams& p, const FuseSrc& f, int z, int j, int t0,
+                                            int my, int lane, int wave, uint16_t* smem, float* red,
+                                            const void* rb, bool zero) {
+  constexpr int KPS = kSkBK / 16;
+  const int lr = lane & 31, lk = lane >> 5;
+  const int k0 = z * kSkRange + wave * kSkBK;     // in the concatenated [x1 | x2]
+  const int s = k0 >= f.H ? 1 : 0;
+  const int kk = k0 - s * f.H + 8 * lk;
+  const float* gs = s ? f.g[1] : f.g[0];
+  float4 raw[KPS][BF ? 1 : 2];   // bf16: 16 bytes; float32: 32 bytes
+  float4 g[KPS][2];
+#pragma unroll
+  for (int jj = 0; jj < KPS; ++jj) {
+    if constexpr (BF) {
+      raw[jj][0] = *(const float4*)((const uint16_t*)rb + kk + 16 * jj);
+    } else {
+      raw[jj][0] = *(const float4*)((const float*)rb + kk + 16 * jj);
+      raw[jj][1] = *(const float4*)((const float*)rb + kk + 16 * jj + 4);
+    }
+  }
+#pragma unroll
+  for (int jj = 0; jj < KPS; ++jj) {
+    g[jj][0] = *(const float4*)(gs + kk + 16 * jj);
+    g[jj][1] = *(const float4*)(gs + kk + 16 * jj + 4);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(p.B), (short)0, (int)((size_t)p.N * p.ldb * 2), 0x00020000);
+  uint16_t* ring = smem + wave * kSkNB * kSkStage;
+#pragma unroll
+  for (int q = 0; q < kSkNB - 1; ++q) sk_issue_buf(wr, p, k0, t0 + q, lane, ring + q * kSkStage);
+  const int issued = kSkNB - 1;
+  __builtin_amdgcn_sched_barrier(0);
+  float x[KPS][8];
+#pragma unroll
+  for (int jj = 0; jj < KPS; ++jj) {
+    if constexpr (BF) {
+      const uint32_t w[4] = {__float_as_uint(raw[jj][0].x), __float_as_uint(raw[jj][0].y),
+                             __float_as_uint(raw[jj][0].z), __float_as_uint(raw[jj][0].w)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[jj][2 * e] = __uint_as_float(w[e] << 16);
+        x[jj][2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+      }
+    } else {
+      x[jj][0] = raw[jj][0].x; x[jj][1] = raw[jj][0].y; x[jj][2] = raw[jj][0].z; x[jj][3] = raw[jj][0].w;
+      x[jj][4] = raw[jj][1].x; x[jj][5] = raw[jj][1].y; x[jj][6] = raw[jj][1].z; x[jj][7] = raw[jj][1].w;
+    }
+    // an id outside the table reads zeros (a select: a branch here would
+    // make the compiler wait for every load in flight at its join)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[jj][e] = zero ? 0.f : x[jj][e];
+  }
+  u32x4 xf[2][KPS];
+  float ss = 0.f;
+#pragma unroll
+  for (int jj = 0; jj < KPS; ++jj) {
+    const float gg[8] = {g[jj][0].x, g[jj][0].y, g[jj][0].z, g[jj][0].w,
+                         g[jj][1].x, g[jj][1].y, g[jj][1].z, g[jj][1].w};
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ss = fmaf(x[jj][2 * e], x[jj][2 * e], ss);
+      ss = fmaf(x[jj][2 * e + 1], x[jj][2 * e + 1], ss);
+      split2(x[jj][2 * e] * gg[2 * e], x[jj][2 * e + 1] * gg[2 * e + 1], hi[e], lo[e]);
+    }
+    xf[0][jj] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+    xf[1][jj] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+  }
+  // the row's sum of squares over this wave's 128 k (lanes lk = 0, 1 hold
+  // its two halves); one workgroup per split writes it
+  ss += shfl_xor(ss, 32);
+  if (j == 0 && lk == 0 && lr < p.M) f.ssp[(size_t)(z * kSkStream + wave) * p.M + lr] = ss;
+  skinny_stream<2>(p, xf, k0, t0, my, issued, lane, wave, smem, red);
+}
+
 __global__ __launch_bounds__(kSkThreads) void fuse_skinny_kernel(GemmParams p, FuseSrc f, int n_tiles,
                                                                  int per_split) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
@@ -698,41 +835,16 @@ __global__ __launch_bounds__(kSkThreads) void fuse_skinny_kernel(GemmParams p, F
   if (my == 0) return;
 
   if (wave < kSkStream) {
-    const int k0 = z * kSkRange + wave * kSkBK;     // in the concatenated [x1 | x2]
+    const int k0 = z * kSkRange + wave * kSkBK;
     const int s = k0 >= f.H ? 1 : 0;
-    const int kk = k0 - s * f.H + 8 * lk;
-    const int r = min(lr, p.M - 1);
-    // all loads first, then the arithmetic: one memory latency
-    float x[KPS][8];
-    float4 g[KPS][2];
-#pragma unroll
-    for (int jj = 0; jj < KPS; ++jj) {
-      fuse_load8(f, s, r, kk + 16 * jj, x[jj]);
-      g[jj][0] = *(const float4*)(f.g[s] + kk + 16 * jj);
-      g[jj][1] = *(const float4*)(f.g[s] + kk + 16 * jj + 4);
-    }
-    u32x4 xf[2][KPS];
-    float ss = 0.f;
-#pragma unroll
-    for (int jj = 0; jj < KPS; ++jj) {
-      const float gg[8] = {g[jj][0].x, g[jj][0].y, g[jj][0].z, g[jj][0].w,
-                           g[jj][1].x, g[jj][1].y, g[jj][1].z, g[jj][1].w};
-      uint32_t hi[4], lo[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        ss = fmaf(x[jj][2 * e], x[jj][2 * e], ss);
-        ss = fmaf(x[jj][2 * e + 1], x[jj][2 * e + 1], ss);
-        split2(x[jj][2 * e] * gg[2 * e], x[jj][2 * e + 1] * gg[2 * e + 1], hi[e], lo[e]);
-      }
-      xf[0][jj] = u32x4{hi[0], hi[1], hi[2], hi[3]};
-      xf[1][jj] = u32x4{lo[0], lo[1], lo[2], lo[3]};
-    }
-    // the row's sum of squares over this wave's 128 k (lanes lk = 0, 1 hold
-    // its two halves); one workgroup per split writes it
-    ss += shfl_xor(ss, 32);
-    if (j == 0 && lk == 0 && lr < p.M) f.ssp[(size_t)(z * kSkStream + wave) * p.M + lr] = ss;
-    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
-    skinny_stream<2>(p, xf, k0, t0, my, lane, wave, smem, red);
+    const void* rb;
+    int dt;
+    bool zero;
+    fuse_row(f, s, min(lr, p.M - 1), rb, dt, zero);
+    if (dt == DMTP_BF16)
+      fuse_stream<true>(p, f, z, j, t0, my, lane, wave, smem, red, rb, zero);
+    else
+      fuse_stream<false>(p, f, z, j, t0, my, lane, wave, smem, red, rb, zero);
     return;
   }
   skinny_sum(p, z, t0, my, lane, red);
