@@ -862,25 +862,45 @@ __global__ __launch_bounds__(256) void fuse_finish_kernel(const float* __restric
   const int m = blockIdx.y;
   const int n = 4 * (blockIdx.x * 256 + threadIdx.x);
   const size_t plane = (size_t)M * H;
-  // issue the partial loads before the scales are known
-  float4 v[kSkMaxSplits];
+  // Loads in dependency order, every one issued before the first sum (vmcnt
+  // counts in issue order, so a load waited for early would wait for all
+  // those before it): the residual row's start (an id lookup) and this
+  // row's sums of squares (wave 0; at most 2 x 64 ranges), then the first
+  // eight partials -- unconditional, columns clamped into the row and splits
+  // past the last repeating it, so that no sum sits between them -- then the
+  // residual row itself.
+  const void* rrb = nullptr;
+  int rdt = DMTP_F32;
+  bool rzero = true;
+  if (has_res) fuse_row(res, 0, m, rrb, rdt, rzero);
+  const int nw = splits * kSkStream, w1 = z1 * kSkStream;
+  float q[2] = {0.f, 0.f};
+  if (threadIdx.x < kWave) {
 #pragma unroll
-  for (int z = 0; z < kSkMaxSplits; ++z)
-    if (z < splits && n < H) v[z] = *(const float4*)(part + z * plane + (size_t)m * H + n);
+    for (int t = 0; t < 2; ++t) q[t] = ssp[(size_t)min((int)threadIdx.x + t * kWave, nw - 1) * M + m];
+  }
+  const float* pp = part + (size_t)m * H + (n < H ? n : H - 4);
+  float4 v[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) v[u] = *(const float4*)(pp + (size_t)min(u, splits - 1) * plane);
   float4 rv = make_float4(0.f, 0.f, 0.f, 0.f);
   if (has_res && n < H) {
-    float x[8];
-    fuse_load8(res, 0, m, n & ~7, x);
-    const int o = n & 7;
-    rv = make_float4(x[o], x[o + 1], x[o + 2], x[o + 3]);
+    if (rdt == DMTP_BF16) {
+      const uint2 w = *(const uint2*)((const uint16_t*)rrb + n);
+      rv = make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                       __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u));
+    } else {
+      rv = *(const float4*)((const float*)rrb + n);
+    }
+    if (rzero) rv = make_float4(0.f, 0.f, 0.f, 0.f);
   }
   if (threadIdx.x < kWave) {
-    const int nw = splits * kSkStream, w1 = z1 * kSkStream;
     double a = 0.0, b = 0.0;
-    for (int i = threadIdx.x; i < nw; i += kWave) {
-      const double q = ssp[(size_t)i * M + m];
-      if (i < w1) a += q;
-      else b += q;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int i = threadIdx.x + t * kWave;
+      if (i < w1) a += q[t];
+      else if (i < nw) b += q[t];
     }
     a = wave_sum(a);
     b = wave_sum(b);
@@ -889,15 +909,20 @@ __global__ __launch_bounds__(256) void fuse_finish_kernel(const float* __restric
       scale[1] = (float)(1.0 / sqrt(b / H + (double)eps));
     }
   }
+  // each stream's partials in split order, eight at a time
+  float4 s1 = make_float4(0.f, 0.f, 0.f, 0.f), s2 = s1;
+  for (int z0 = 0;; z0 += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (z0 + u < z1) add4f(s1, v[u]);
+      else if (z0 + u < splits) add4f(s2, v[u]);
+    }
+    if (z0 + 8 >= splits) break;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = *(const float4*)(pp + (size_t)min(z0 + 8 + u, splits - 1) * plane);
+  }
   __syncthreads();
   if (n >= H) return;
-  // each stream's partials in split order (register indices fixed at compile time)
-  float4 s1 = make_float4(0.f, 0.f, 0.f, 0.f), s2 = s1;
-#pragma unroll
-  for (int z = 0; z < kSkMaxSplits; ++z) {
-    if (z < z1) add4f(s1, v[z]);
-    else if (z < splits) add4f(s2, v[z]);
-  }
   const float c1 = scale[0], c2 = scale[1];
   float4 y;
   y.x = rv.x + (s1.x * c1 + s2.x * c2);
