@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define DMTP_ABI_VERSION 5
+#define DMTP_ABI_VERSION 6
 
 enum dmtp_status {
   DMTP_OK = 0,
@@ -330,10 +330,35 @@ typedef struct {
    * path (which then records neither). */
   void* gemm_start_event;
   void* gemm_stop_event;
+  /* Optional: W in the packed layout written by dmtp_head_pack (bf16 only),
+   * 16-byte aligned.  The register-input matrix-core GEMM (bf16, H a multiple
+   * of 128, more than 128 input rows per row chunk of at most 448) then
+   * streams its weight stages from it, each one contiguous 16 KB block,
+   * instead of 128 runs of 128 bytes of W; results are bit-identical.  The
+   * other kernels read W, which stays required.  NULL: W only. */
+  const void* w_packed;
 } dmtp_head_desc;
 
 size_t dmtp_lm_head_ws(const dmtp_head_desc* d);
 int dmtp_lm_head(const dmtp_head_desc* d, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ----------------------------------------------------- packed head weight ----
+ * Not a step of the pages: a one-time copy of the shared head matrix W
+ * [V, H] (bf16, H a multiple of 64) into the order in which the LM-head GEMM
+ * streams it, made when the weights are loaded and passed to dmtp_lm_head as
+ * w_packed.  Vocabulary tile t (rows 128 t .. 128 t + 127; rows at or past V
+ * are zeros) occupies bytes [t 256 H, (t + 1) 256 H) of out; within it, block
+ * s (H / 64 blocks of 16384 bytes) holds columns 64 s .. 64 s + 63 of the
+ * tile's rows as 1024 pieces of 8 elements: piece 8 r + j is columns
+ * 64 s + 8 (j ^ ((r >> 1) & 7)) .. + 7 of row 128 t + r.  That is the image
+ * of the GEMM's LDS stage, so a stage is one contiguous copy.
+ * dmtp_head_pack_bytes: the size of out, ceil(V / 128) 256 H bytes (0 for an
+ * unsupported V or H).  dmtp_head_pack: W and out on the current device,
+ * 16-byte aligned, out_bytes at least that size; dtype must be DMTP_BF16.
+ * The copy is enqueued on stream; errors as for the other calls. */
+size_t dmtp_head_pack_bytes(int32_t V, int32_t H);
+int dmtp_head_pack(const void* W, int32_t V, int32_t H, int32_t dtype, void* out, size_t out_bytes,
+                   hipStream_t stream);
 
 /* --------------------------------------------------------------- verify ----
  * Block verification (DMTP blog section 5 step 3; the colibri notes on

@@ -19,7 +19,8 @@ from ._abi import (DMTP_BF16, DMTP_F32, DMTP_NO_DRAW, DmtpError, DraftDesc, Fuse
 
 lib = _abi.load()
 
-__all__ = ["lib", "fuse", "fuse_noalloc", "mtp_block", "ctx_kv", "block_draft", "lm_head", "verify", "accept_stats", "call",
+__all__ = ["lib", "fuse", "fuse_noalloc", "mtp_block", "ctx_kv", "block_draft", "lm_head", "pack_head_weight", "verify",
+           "accept_stats", "call",
            "workspace_bytes",
            "DMTP_F32", "DMTP_BF16", "DMTP_NO_DRAW", "DmtpError", "version"]
 
@@ -216,8 +217,9 @@ def lm_head(W: torch.Tensor, segments: Sequence[HeadSegment], token: torch.Tenso
             logits: Optional[torch.Tensor] = None, prepared: Optional[torch.Tensor] = None,
             row_max: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
             gap: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
-            run: bool = True) -> HeadDesc:
-    """Shared LM head with argmax / Gumbel-max draws (dmtp_lm_head)."""
+            w_packed: Optional[torch.Tensor] = None, run: bool = True) -> HeadDesc:
+    """Shared LM head with argmax / Gumbel-max draws (dmtp_lm_head).  w_packed:
+    W's packed copy from pack_head_weight, streamed by the matrix-core GEMM."""
     D = HeadDesc()
     D.V, D.H = W.shape
     D.dtype = dtype_code(W.dtype)
@@ -232,9 +234,29 @@ def lm_head(W: torch.Tensor, segments: Sequence[HeadSegment], token: torch.Tenso
     D.logits_rows = logits.shape[0] if logits is not None else 0
     D.prepared, D.token = _ptr(prepared), _ptr(token)
     D.row_max, D.lse, D.gap = _ptr(row_max), _ptr(lse), _ptr(gap)
+    D.w_packed = _ptr(w_packed)
+    if w_packed is not None:
+        D._keep.append(w_packed)
     if run:
         call("lm_head", D, ws)
     return D
+
+
+def pack_head_weight(W: torch.Tensor) -> torch.Tensor:
+    """W [V, H] bf16 copied once into the layout the LM-head GEMM streams
+    (dmtp_head_pack); pass the result to lm_head as w_packed."""
+    if W.dtype != torch.bfloat16 or W.dim() != 2 or not W.is_contiguous():
+        raise ValueError("pack_head_weight takes a contiguous bf16 [V, H] matrix")
+    V, H = W.shape
+    n = lib.dmtp_head_pack_bytes(V, H)
+    if n == 0:
+        raise ValueError(f"unsupported head shape V={V}, H={H}")
+    out = torch.empty(n // 2, dtype=torch.bfloat16, device=W.device)
+    st = lib.dmtp_head_pack(ctypes.c_void_p(W.data_ptr()), V, H, DMTP_BF16,
+                            ctypes.c_void_p(out.data_ptr()), n, ctypes.c_void_p(_stream()))
+    if st != 0:
+        raise DmtpError("dmtp_head_pack", st, lib.dmtp_status_str(st).decode())
+    return out
 
 
 def verify(*, B: int, K: int, V: int, t1: torch.Tensor, drafts: Optional[torch.Tensor],

@@ -62,7 +62,8 @@ class HeadDesc(ctypes.Structure):
                 ("plant_row", c_void_p), ("store_row", c_void_p), ("logits", c_void_p),
                 ("logits_rows", c_int32), ("prepared", c_void_p), ("token", c_void_p),
                 ("row_max", c_void_p), ("lse", c_void_p), ("gap", c_void_p),
-                ("gemm_start_event", c_void_p), ("gemm_stop_event", c_void_p)]
+                ("gemm_start_event", c_void_p), ("gemm_stop_event", c_void_p),
+                ("w_packed", c_void_p)]
 
 
 class VerifyDesc(ctypes.Structure):
@@ -104,7 +105,7 @@ _STRUCTS = [Rows, FuseDesc, Layer, DraftDesc, HeadSegment, HeadDesc, VerifyDesc,
 SYMBOLS = ["dmtp_fuse", "dmtp_fuse_ws", "dmtp_fuse_noalloc", "dmtp_mtp_block", "dmtp_mtp_block_ws", "dmtp_ctx_kv",
            "dmtp_ctx_kv_ws", "dmtp_block_draft",
            "dmtp_block_draft_ws", "dmtp_lm_head",
-           "dmtp_lm_head_ws", "dmtp_verify", "dmtp_verify_ws", "dmtp_accept_stats",
+           "dmtp_lm_head_ws", "dmtp_head_pack", "dmtp_head_pack_bytes", "dmtp_verify", "dmtp_verify_ws", "dmtp_accept_stats",
            "dmtp_status_str", "dmtp_version", "dmtp_struct_size"]
 
 
@@ -130,6 +131,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         q.restype = c_size_t
     lib.dmtp_fuse_noalloc.argtypes = [POINTER(FuseDesc), c_void_p]
     lib.dmtp_fuse_noalloc.restype = c_int
+    lib.dmtp_head_pack_bytes.argtypes = [c_int32, c_int32]
+    lib.dmtp_head_pack_bytes.restype = c_size_t
+    lib.dmtp_head_pack.argtypes = [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_size_t, c_void_p]
+    lib.dmtp_head_pack.restype = c_int
     lib.dmtp_accept_stats.argtypes = [POINTER(StatsDesc), c_void_p]
     lib.dmtp_accept_stats.restype = c_int
     lib.dmtp_status_str.argtypes = [c_int]

@@ -378,6 +378,10 @@ int validate_head(const dmtp_head_desc* d, int* M_out) {
   if (d->temperature) CHECK(d->draw_key && d->store_row && d->logits, DMTP_E_NULL);
   if (d->store_row) CHECK(d->logits != nullptr && d->logits_rows >= 1, DMTP_E_NULL);
   if (d->prepared) CHECK(aligned16(d->prepared), DMTP_E_ALIGN);
+  if (d->w_packed) {
+    CHECK(d->dtype == DMTP_BF16, DMTP_E_DTYPE);
+    CHECK(aligned16(d->w_packed), DMTP_E_ALIGN);
+  }
   *M_out = (int)M;
   return DMTP_OK;
 }
@@ -615,6 +619,23 @@ int dmtp_lm_head(const dmtp_head_desc* d, void* ws, size_t ws_bytes, hipStream_t
   return launch_status(lm_head_run(*d, M, ws, stream));
 }
 
+size_t dmtp_head_pack_bytes(int32_t V, int32_t H) {
+  if (V < 2 || V > (1 << 26) || H < 64 || H > 16384 || H % 64 != 0) return 0;
+  return head_pack_bytes(V, H);
+}
+
+int dmtp_head_pack(const void* W, int32_t V, int32_t H, int32_t dtype, void* out, size_t out_bytes,
+                   hipStream_t stream) {
+  CHECK(W != nullptr && out != nullptr, DMTP_E_NULL);
+  CHECK(V >= 2 && V <= (1 << 26) && H >= 64 && H <= 16384 && H % 64 == 0, DMTP_E_SHAPE);
+  CHECK(dtype == DMTP_BF16, DMTP_E_DTYPE);
+  CHECK(aligned16(W) && aligned16(out), DMTP_E_ALIGN);
+  CHECK(out_bytes >= head_pack_bytes(V, H), DMTP_E_WORKSPACE);
+  int e = check_device();
+  if (e != DMTP_OK) return e;
+  return launch_status(head_pack_run(W, V, H, out, stream));
+}
+
 size_t dmtp_verify_ws(const dmtp_verify_desc* d) {
   if (validate_verify(d) != DMTP_OK) return 0;
   return verify_ws_bytes(*d);
@@ -653,7 +674,7 @@ const char* dmtp_status_str(int s) {
   }
 }
 
-const char* dmtp_version(void) { return "dmtp 0.5.0 (gfx950, ABI 5)"; }
+const char* dmtp_version(void) { return "dmtp 0.6.0 (gfx950, ABI 6)"; }
 
 size_t dmtp_struct_size(int which) {
   switch (which) {

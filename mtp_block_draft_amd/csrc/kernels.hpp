@@ -146,6 +146,10 @@ hipError_t attention(const AttnPlan& p, const float* q, const float* kb, const f
 // ---------------------------------------------------------------- LM head --
 size_t lm_head_ws_bytes(const dmtp_head_desc& d, int M);
 hipError_t lm_head_run(const dmtp_head_desc& d, int M, void* ws, hipStream_t s);
+// The packed copy of the head matrix that the register-input LM-head GEMM
+// streams (layout in the header, at dmtp_head_pack): its size and the copy.
+size_t head_pack_bytes(int V, int H);
+hipError_t head_pack_run(const void* W, int V, int H, void* out, hipStream_t s);
 
 // ----------------------------------------------------------------- verify --
 size_t verify_ws_bytes(const dmtp_verify_desc& d);

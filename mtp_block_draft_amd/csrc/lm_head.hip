@@ -82,6 +82,7 @@ struct HeadParams {
   int n_seg, M, H, V, dtype;
   float eps;
   const void* W;
+  const void* Wp;        // W in the packed stage layout (dmtp_head_pack), or NULL
   const float* temperature;
   const uint64_t* draw_key;
   uint64_t seed;
@@ -602,7 +603,7 @@ struct HeadXr {
   static_assert(W_INSTR % 4 == 0 && NW >= 2 && WAIT_N < 64, "copies");
 };
 
-template <int TQ, int NW>
+template <int TQ, int NW, bool PK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void head_gemm_xr_kernel(HeadParams p, int n_mchunks) {
   typedef HeadXr<TQ, NW> C;
@@ -627,14 +628,17 @@ void head_gemm_xr_kernel(HeadParams p, int n_mchunks) {
   // of the tile, lane idx = 64 (WPW wave + q) + lane supplying row idx / CPR,
   // the chunk that lands at position idx % CPR.  The descriptor ends at row V,
   // so the rows of the last tile past V read as zeros (their columns are
-  // masked).
-  const buf_rsrc wr = make_rsrc((const uint16_t*)p.W + (size_t)v0 * H, min(C::BV, V - v0) * H * 2);
+  // masked).  PK: the packed copy holds each stage as exactly that LDS image,
+  // 16 KB in a row (rows past V stored as zeros), so lane idx reads 16 idx.
+  const buf_rsrc wr = PK ? make_rsrc((const uint16_t*)p.Wp + (size_t)v0 * H, C::BV * H * 2)
+                         : make_rsrc((const uint16_t*)p.W + (size_t)v0 * H, min(C::BV, V - v0) * H * 2);
+  constexpr uint32_t w_ss = PK ? C::STAGE * 2 : C::WK * 2;   // bytes between stages
   uint32_t woff[C::WPW];
   int wdst[C::WPW];
 #pragma unroll
   for (int q = 0; q < C::WPW; ++q) {
     const int idx = (wave * C::WPW + q) * 64 + lane, r = idx / C::CPR;
-    woff[q] = (uint32_t)(r * H * 2 + 16 * swz_chunk<C::WK>(r, idx % C::CPR));
+    woff[q] = PK ? (uint32_t)(16 * idx) : (uint32_t)(r * H * 2 + 16 * swz_chunk<C::WK>(r, idx % C::CPR));
     wdst[q] = (wave * C::WPW + q) * 512;
   }
   // Input fragment t (B operand): row rw0 + 16 t + fr, k chunk fg of the
@@ -663,7 +667,7 @@ void head_gemm_xr_kernel(HeadParams p, int n_mchunks) {
   auto issue_w = [&](int stage, int slot) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < C::WPW; ++q)
-      buf_dma16(wr, woff[q], (uint32_t)stage * C::WK * 2, smem + slot * C::STAGE + wdst[q]);
+      buf_dma16(wr, woff[q], (uint32_t)stage * w_ss, smem + slot * C::STAGE + wdst[q]);
   };
   u32x4 wf[2][C::NU];   // weight fragments (A operand) of a 32-wide slice, double-buffered
   // fragments of slice k: stage k / 2 (in slot (k / 2) % NW), chunks 4 (k % 2) + fg
@@ -882,12 +886,15 @@ hipError_t launch_head_xr(const HeadParams& p, int n_mchunks, const GemmEvents& 
   static_assert(C::LDS_BYTES <= 160 * 1024, "head LDS");
   const int total = p.n_vtiles * n_mchunks;
   const dim3 grid(8 * ((total + 7) / 8));
-  if (ev.start && ev.stop)
-    hipExtLaunchKernelGGL((head_gemm_xr_kernel<TQ, C::NW>), grid, dim3(C::THREADS), (uint32_t)C::LDS_BYTES, s,
-                          ev.start, ev.stop, 0u, p, n_mchunks);
-  else
-    hipLaunchKernelGGL((head_gemm_xr_kernel<TQ, C::NW>), grid, dim3(C::THREADS), C::LDS_BYTES, s, p, n_mchunks);
-  return hipGetLastError();
+  auto go = [&](auto kern) {
+    if (ev.start && ev.stop)
+      hipExtLaunchKernelGGL(kern, grid, dim3(C::THREADS), (uint32_t)C::LDS_BYTES, s, ev.start, ev.stop, 0u, p,
+                            n_mchunks);
+    else
+      hipLaunchKernelGGL(kern, grid, dim3(C::THREADS), C::LDS_BYTES, s, p, n_mchunks);
+    return hipGetLastError();
+  };
+  return p.Wp ? go(head_gemm_xr_kernel<TQ, C::NW, true>) : go(head_gemm_xr_kernel<TQ, C::NW, false>);
 }
 
 // Row chunks of at most 448 rows, split evenly; TB = 64-row tiles per
@@ -1424,7 +1431,38 @@ WsLayout ws_layout(const dmtp_head_desc& d, int M) {
   return w;
 }
 
+// The packed copy of W: one thread per 16-byte piece of out.  Piece 8 r + j of
+// block s of tile t is columns 64 s + 8 (j ^ ((r >> 1) & 7)) .. + 7 of row
+// 128 t + r (zeros past V): the stage image of the register-input GEMM.
+constexpr int kPackBV = 128, kPackWK = 64;
+__global__ void head_pack_kernel(const uint16_t* __restrict__ W, int V, int H, uint4* __restrict__ out,
+                                 size_t pieces) {
+  const int per_row = kPackWK / 8, per_block = kPackBV * per_row, blocks = H / kPackWK;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < pieces; i += (size_t)gridDim.x * blockDim.x) {
+    const int idx = (int)(i % per_block);
+    const size_t tb = i / per_block;
+    const int sblk = (int)(tb % blocks);
+    const size_t t = tb / blocks;
+    const int r = idx / per_row, j = idx % per_row;
+    const size_t row = t * kPackBV + r;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (row < (size_t)V)
+      v = *(const uint4*)(W + row * H + kPackWK * sblk + 8 * swz_chunk<kPackWK>(r, j));
+    out[i] = v;
+  }
+}
+
 }  // namespace
+
+size_t head_pack_bytes(int V, int H) { return (size_t)((V + kPackBV - 1) / kPackBV) * kPackBV * H * 2; }
+
+hipError_t head_pack_run(const void* W, int V, int H, void* out, hipStream_t s) {
+  static_assert(kPackBV == HeadXr<7>::BV && kPackWK == HeadXr<7>::WK, "stage of the register-input GEMM");
+  const size_t pieces = head_pack_bytes(V, H) / 16;
+  const int blocks = (int)std::min<size_t>((pieces + 255) / 256, 8192);
+  hipLaunchKernelGGL(head_pack_kernel, dim3(blocks), dim3(256), 0, s, (const uint16_t*)W, V, H, (uint4*)out, pieces);
+  return hipGetLastError();
+}
 
 size_t lm_head_ws_bytes(const dmtp_head_desc& d, int M) { return ws_layout(d, M).total; }
 
@@ -1446,6 +1484,7 @@ hipError_t lm_head_run(const dmtp_head_desc& d, int M, void* ws, hipStream_t s) 
   p.dtype = d.dtype;
   p.eps = d.eps;
   p.W = d.W;
+  p.Wp = (d.dtype == DMTP_BF16 && d.H % 128 == 0) ? d.w_packed : nullptr;
   p.temperature = d.temperature;
   p.draw_key = d.draw_key;
   p.seed = d.seed;

@@ -43,7 +43,7 @@ import numpy as np
 import torch
 
 from . import (DMTP_NO_DRAW, accept_stats, block_draft, call, fuse, head_segment, layer_arg, lib,
-               lm_head, mtp_block, verify, workspace_bytes)
+               lm_head, mtp_block, pack_head_weight, verify, workspace_bytes)
 
 
 def _dev(a: np.ndarray, dtype: torch.dtype, device) -> torch.Tensor:
@@ -51,7 +51,8 @@ def _dev(a: np.ndarray, dtype: torch.dtype, device) -> torch.Tensor:
 
 
 class Round:
-    def __init__(self, inp, h_target: Optional[np.ndarray] = None, device: str = "cuda"):
+    def __init__(self, inp, h_target: Optional[np.ndarray] = None, device: str = "cuda",
+                 pack_head: bool = True):
         cfg = inp.cfg
         self.cfg = cfg
         B, H, V, K = cfg.B, cfg.H, cfg.V, cfg.K
@@ -63,6 +64,10 @@ class Round:
 
         self.emb = up(inp.emb)
         self.w_head = up(inp.w_head)
+        # the head matrix's packed copy (made once, with the weights), which the
+        # matrix-core LM-head GEMM streams as contiguous 16 KB stages
+        self.w_head_packed = (pack_head_weight(self.w_head)
+                              if pack_head and tdt == torch.bfloat16 and H % 64 == 0 else None)
         self.fuse_M = up(inp.fuse_M)
         self.fuse_W = up(inp.fuse_W)
         g = {k: up(getattr(inp, k), f32) for k in ("g_h", "g_e", "g_e2", "g_m", "g_f", "g_final")}
@@ -180,7 +185,8 @@ class Round:
                                  temperature=self.t1_temp, draw_key=self.t1_key, seed=self.seed,
                                  plant_row=self.plant_row, store_row=self.t1_store,
                                  logits=self.logits, prepared=self.t1_prep, row_max=self.t1_max,
-                                 lse=self.t1_lse, gap=self.t1_gap, run=False)
+                                 lse=self.t1_lse, gap=self.t1_gap, w_packed=self.w_head_packed,
+                                 run=False)
         t1_ids = self.t1_token[:B]
         self.d_fuse_delta = fuse(self.x_t1, self.fuse_W, g["g_e2"], g["g_m"], x1_ids=t1_ids,
                                  x2=self.h_mtp, res_ids=t1_ids, table=self.emb, eps=eps, run=False)
@@ -195,7 +201,7 @@ class Round:
         self.d_head_c = lm_head(self.w_head, [head_segment(self.head_in)], self.tok, eps=eps,
                                 temperature=self.c_temp, draw_key=self.c_key, seed=self.seed,
                                 store_row=self.c_store, logits=self.logits, row_max=self.rmax,
-                                lse=self.lse, gap=self.gap, run=False)
+                                lse=self.lse, gap=self.gap, w_packed=self.w_head_packed, run=False)
         self.d_verify = verify(B=B, K=K, V=V, t1=t1_ids, drafts=self.tok[:nd],
                                target=self.tok[nd:], accept_len=self.accept_len,
                                out_tokens=self.out_tokens, n_out=self.n_out,

@@ -145,6 +145,31 @@ def test_lm_head_argument_errors(lib):
     assert need > 0 and _call(lib, "dmtp_lm_head", d, ws_bytes=need - 1) == -4
 
 
+def test_head_pack_argument_errors(lib):
+    # size: ceil(V / 128) tiles of 128 rows x H bf16
+    assert lib.dmtp_head_pack_bytes(151936, 2048) == 1187 * 128 * 2048 * 2
+    assert lib.dmtp_head_pack_bytes(7001, 512) == 55 * 128 * 512 * 2
+    assert lib.dmtp_head_pack_bytes(1, 512) == 0 and lib.dmtp_head_pack_bytes(300, 96) == 0
+    n = lib.dmtp_head_pack_bytes(300, 128)
+    ok = dict(W=FAKE, V=300, H=128, dtype=abi.DMTP_BF16, out=FAKE, nb=n)
+
+    def pack(**kw):
+        a = {**ok, **kw}
+        return lib.dmtp_head_pack(a["W"], a["V"], a["H"], a["dtype"], a["out"], a["nb"], None)
+
+    assert pack(W=0) == -1 and pack(out=0) == -1
+    assert pack(H=96) == -2 and pack(V=1) == -2
+    assert pack(dtype=abi.DMTP_F32) == -3
+    assert pack(out=FAKE + 8) == -5 and pack(W=FAKE + 8) == -5
+    assert pack(nb=n - 1) == -4
+    assert pack() == -6               # valid, but no gfx950 here
+    # the head call: a packed copy is bf16 only and 16-byte aligned
+    assert _call(lib, "dmtp_lm_head", _head_desc(w_packed=FAKE + 8)) == -5
+    d = _head_desc(w_packed=FAKE, dtype=abi.DMTP_F32)
+    d.seg[0].dtype = abi.DMTP_F32
+    assert _call(lib, "dmtp_lm_head", d) == -3
+
+
 def test_verify_argument_errors(lib):
     d = abi.VerifyDesc()
     d.B, d.K, d.V = 3, 7, 1000

@@ -257,6 +257,58 @@ def test_lm_head_rows_do_not_depend_on_the_batch(dm):
     assert all(tok_s[i] == tok_a[i] or gap_a[i] < 1e-4 for i in range(32))
 
 
+def test_head_pack_layout(dm):
+    # the packed copy against its definition: block s of tile t holds, as
+    # piece 8 r + j, columns 64 s + 8 (j ^ ((r >> 1) & 7)) .. + 7 of row
+    # 128 t + r, with zero rows past V
+    V, H = 300, 192
+    print(f"head pack layout V={V} H={H}", flush=True)
+    rng = np.random.default_rng(5)
+    W = torch.from_numpy(rng.standard_normal((V, H)).astype(np.float32)).to(torch.bfloat16).cuda()
+    got = dm.pack_head_weight(W).view(torch.int16).cpu().numpy()
+    T = (V + 127) // 128
+    Wp = np.zeros((T * 128, H), np.int16)
+    Wp[:V] = W.view(torch.int16).cpu().numpy()
+    r = np.arange(128)[:, None]
+    j = np.arange(8)[None, :]
+    src = j ^ ((r >> 1) & 7)                                  # [128, 8] source chunk of piece (r, j)
+    want = []
+    for t in range(T):
+        for sb in range(H // 64):
+            blk = Wp[128 * t:128 * t + 128, 64 * sb:64 * sb + 64].reshape(128, 8, 8)
+            want.append(blk[r, src, :].reshape(-1))
+    np.testing.assert_array_equal(got, np.concatenate(want))
+
+
+@pytest.mark.parametrize("V,H,M", [(7001, 512, 200), (7001, 512, 448), (20000, 2048, 448),
+                                   (9000, 5120, 256), (3000, 1024, 901)])
+def test_lm_head_packed_weights_bit_identical(dm, V, H, M):
+    # The register-input GEMM (4, 5 and 7 row tiles per wave; one and three
+    # row chunks; ragged last vocabulary tiles) streaming the packed copy
+    # gives every output bit for bit as it does from W.  A packed copy of a
+    # zero matrix then shows the kernel reads the copy, not W.
+    print(f"lm_head packed V={V} H={H} M={M}", flush=True)
+    W, hid, g, rows, strided, x = _head_case(41 + M, H, V, "bf16", M_norm=0, M_rows=M, M_strided=0)
+    Wt, X = _t(W, torch.bfloat16), _t(rows, torch.bfloat16)
+    n_st = min(M, 6)
+    store = torch.full((M,), -1, dtype=torch.int32, device="cuda")
+    store[torch.arange(0, M, max(1, M // n_st), device="cuda")[:n_st]] = torch.arange(n_st, dtype=torch.int32,
+                                                                                       device="cuda")
+    outs = []
+    for wp in (None, dm.pack_head_weight(Wt), dm.pack_head_weight(torch.zeros_like(Wt))):
+        tok = torch.empty(M, dtype=torch.int32, device="cuda")
+        lse = torch.empty(M, dtype=torch.float32, device="cuda")
+        rmax = torch.empty(M, dtype=torch.float32, device="cuda")
+        gap = torch.empty(M, dtype=torch.float32, device="cuda")
+        logits = torch.full((n_st, V), float("nan"), dtype=torch.float32, device="cuda")
+        dm.lm_head(Wt, [dm.head_segment(X)], tok, lse=lse, row_max=rmax, gap=gap, store_row=store,
+                   logits=logits, w_packed=wp)
+        outs.append([v.cpu().numpy() for v in (tok, lse, rmax, gap, logits)])
+    for a, b in zip(outs[0], outs[1]):
+        np.testing.assert_array_equal(a, b)
+    assert np.all(outs[2][2] == 0) and np.all(outs[2][4] == 0)
+
+
 @pytest.mark.parametrize("H", [512, 1024, 1536, 2048])
 @pytest.mark.parametrize("M", [1, 9, 32])
 def test_lm_head_at_most_32_rows(dm, H, M):
