@@ -599,12 +599,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(
     float part = 0.f;
 #pragma unroll
     for (int i = 0; i < DL; ++i) part = fmaf(qv[i], kvs[j * D + lane + kWave * i], part);
-    const float sj = wave_sum(part) * scale;
+    const float sj = wave_sum_dpp(part) * scale;
     s_lane = lane == j ? sj : s_lane;
   }
-  M = fmaxf(M, s_lane);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, shfl_xor(M, off));
+  M = wave_max_dpp(fmaxf(M, s_lane));
   float Lsum = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -613,7 +611,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(
     Lsum = fmaf(w, lc[i], Lsum);
   }
   const float wb = lane < nvis ? expf(s_lane - M) : 0.f;
-  Lsum = wave_sum(Lsum + wb);
+  Lsum = wave_sum_dpp(Lsum + wb);
   __threadfence_block();
   __builtin_amdgcn_wave_barrier();
 
