@@ -469,13 +469,14 @@ __global__ __launch_bounds__(64 * kAttnQtw) __attribute__((amdgpu_waves_per_eu(2
     float mx = s[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
-    mx = fmaxf(mx, shfl_xor(mx, 32));
     // The exponentials are taken against a reference max m_run, moved (and O
     // and l rescaled) only when some row's max exceeds it by more than 2^8:
     // the (m, l, O) triple stays exact for any reference, and a stale one
-    // keeps every weight at most 2^8.
+    // keeps every weight at most 2^8.  mx is the max of this lane's half of
+    // the row's keys; the two halves (lanes l and l ^ 32) share m_run, so the
+    // row max is exchanged only when the reference moves.
     if (__ballot(mx > m_run + 8.f) != 0) {
-      const float m_new = fmaxf(m_run, mx);
+      const float m_new = fmaxf(m_run, fmaxf(mx, shfl_xor(mx, 32)));
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first tile
       l_run *= alpha;
 #pragma unroll
@@ -493,8 +494,7 @@ __global__ __launch_bounds__(64 * kAttnQtw) __attribute__((amdgpu_waves_per_eu(2
       ps += p0 + p1;
       split_pair(p0, p1, ph[i / 2], pl[i / 2]);
     }
-    ps += shfl_xor(ps, 32);
-    l_run += ps;
+    l_run += ps;   // this lane's half of the row; the halves are added at the end
 
     // O^T[dd][query] += V^T P^T over the tile's keys in two k-steps; k-step ks
     // takes this lane group's keys 16 ks + 4 g + (0..3) and 16 ks + 8 + 4 g + (0..3),
@@ -515,6 +515,7 @@ __global__ __launch_bounds__(64 * kAttnQtw) __attribute__((amdgpu_waves_per_eu(2
     }
   }
 
+  l_run += shfl_xor(l_run, 32);
   // partial: O^T element i of tile dt is dd = 32 dt + 8 (i / 4) + 4 g + i % 4 of query qrow
   if (!live) return;
 #pragma unroll
