@@ -600,10 +600,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(
     float part = 0.f;
 #pragma unroll
     for (int i = 0; i < DL; ++i) part = fmaf(qv[i], kvs[j * D + lane + kWave * i], part);
-    const float sj = wave_sum_dpp(part) * scale;
+    const float sj = wave_sum(part) * scale;
     s_lane = lane == j ? sj : s_lane;
   }
-  M = wave_max_dpp(fmaxf(M, s_lane));
+  M = wave_max(fmaxf(M, s_lane));
   float Lsum = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -612,7 +612,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(
     Lsum = fmaf(w, lc[i], Lsum);
   }
   const float wb = lane < nvis ? expf(s_lane - M) : 0.f;
-  Lsum = wave_sum_dpp(Lsum + wb);
+  Lsum = wave_sum(Lsum + wb);
   __threadfence_block();
   __builtin_amdgcn_wave_barrier();
 

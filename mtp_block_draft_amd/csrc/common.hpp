@@ -85,45 +85,52 @@ __device__ __forceinline__ T shfl_xor(T v, int mask) {
   return __shfl_xor(v, mask, kWave);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-  for (int o = 32; o > 0; o >>= 1) v += shfl_xor(v, o);
-  return v;
-}
-
 // Wave-wide sum and maximum by DPP moves, with no LDS round trip: pairs and
 // pairs of pairs within each quad, the mirrors within each 8- and 16-lane
 // row, then row 0's total into row 1 and row 2's into row 3, and lane 31's
 // into rows 2 and 3; lane 63 then holds the whole wave's result, which is
 // returned to every lane (a wave-uniform value).  Summation order: quads,
-// eighths, rows, then (r0 + r1) + (r2 + r3).
+// eighths, rows, then (r0 + r1) + (r2 + r3).  Every lane of the wave must be
+// active: the moves read the registers of all 64 lanes.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ int dpp_mov_i(int v, int old) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROWS, 0xF, false);
+}
 template <int CTRL, int ROWS = 0xF>
 __device__ __forceinline__ float dpp_mov(float v, float old) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
-                                                               __builtin_bit_cast(int, v), CTRL, ROWS, 0xF,
-                                                               false));
+  return __builtin_bit_cast(float, dpp_mov_i<CTRL, ROWS>(__builtin_bit_cast(int, v), __builtin_bit_cast(int, old)));
 }
-__device__ __forceinline__ float wave_sum_dpp(float v) {
-  v += dpp_mov<0xB1>(v, 0.f);          // quad_perm [1, 0, 3, 2]
-  v += dpp_mov<0x4E>(v, 0.f);          // quad_perm [2, 3, 0, 1]
-  v += dpp_mov<0x141>(v, 0.f);         // row_half_mirror
-  v += dpp_mov<0x140>(v, 0.f);         // row_mirror
-  v += dpp_mov<0x142, 0xA>(v, 0.f);    // row_bcast15 into rows 1 and 3
-  v += dpp_mov<0x143, 0xC>(v, 0.f);    // row_bcast31 into rows 2 and 3
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ double dpp_mov(double v, double old) {
+  const int lo = dpp_mov_i<CTRL, ROWS>(__double2loint(v), __double2loint(old));
+  const int hi = dpp_mov_i<CTRL, ROWS>(__double2hiint(v), __double2hiint(old));
+  return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ float lane63(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
-__device__ __forceinline__ float wave_max_dpp(float v) {
+__device__ __forceinline__ double lane63(double v) {
+  return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), 63),
+                          __builtin_amdgcn_readlane(__double2loint(v), 63));
+}
+template <class T>
+__device__ __forceinline__ T wave_sum(T v) {
+  v += dpp_mov<0xB1>(v, T(0));          // quad_perm [1, 0, 3, 2]
+  v += dpp_mov<0x4E>(v, T(0));          // quad_perm [2, 3, 0, 1]
+  v += dpp_mov<0x141>(v, T(0));         // row_half_mirror
+  v += dpp_mov<0x140>(v, T(0));         // row_mirror
+  v += dpp_mov<0x142, 0xA>(v, T(0));    // row_bcast15 into rows 1 and 3
+  v += dpp_mov<0x143, 0xC>(v, T(0));    // row_bcast31 into rows 2 and 3
+  return lane63(v);
+}
+__device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, dpp_mov<0xB1>(v, v));
   v = fmaxf(v, dpp_mov<0x4E>(v, v));
   v = fmaxf(v, dpp_mov<0x141>(v, v));
   v = fmaxf(v, dpp_mov<0x140>(v, v));
   v = fmaxf(v, dpp_mov<0x142, 0xA>(v, v));
   v = fmaxf(v, dpp_mov<0x143, 0xC>(v, v));
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
-}
-
-__device__ __forceinline__ double wave_sum(double v) {
-  for (int o = 32; o > 0; o >>= 1) v += shfl_xor(v, o);
-  return v;
+  return lane63(v);
 }
 
 // --------------------------------------------------------- Philox4x64-10 ----
