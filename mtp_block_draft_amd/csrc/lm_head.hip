@@ -182,12 +182,32 @@ __global__ __launch_bounds__(kPrepThreads) void head_prep_kernel(HeadParams p) {
     const double inv = 1.0 / sqrt(t / H + (double)p.eps);
     for (int i = threadIdx.x; i < H; i += blockDim.x)
       store_elem(p.prepared, p.dtype, oidx(i), (float)((double)xr[i] * inv * sg.g[i]));
-  } else if (p.dtype == DMTP_BF16) {
-    const uint16_t* xr = (const uint16_t*)sg.x + (size_t)m * sg.ld;
-    for (int i = threadIdx.x; i < H; i += blockDim.x) ((uint16_t*)p.prepared)[oidx(i)] = xr[i];
   } else {
-    const float* xr = (const float*)sg.x + (size_t)m * sg.ld;
-    for (int i = threadIdx.x; i < H; i += blockDim.x) ((float*)p.prepared)[oidx(i)] = xr[i];
+    // rows already in the head dtype: 16-byte pieces (8 bf16 or 4 float32
+    // elements, which every output layout keeps together; H is a multiple of
+    // 64 and rows and strides are 16-byte aligned), all loads of the row
+    // issued before the first store
+    const int per = p.dtype == DMTP_BF16 ? 8 : 4;
+    const char* xr = (const char*)sg.x + (size_t)m * sg.ld * (p.dtype == DMTP_BF16 ? 2 : 4);
+    const int np = H / per;
+    constexpr int KP = 8;   // pieces per thread per pass: 8 x 256 x 8 = 16384 bf16 elements
+    for (int j0 = 0; j0 < np; j0 += KP * kPrepThreads) {
+      uint4 v[KP];
+#pragma unroll
+      for (int k = 0; k < KP; ++k) {
+        const int j = j0 + threadIdx.x + kPrepThreads * k;
+        if (j < np) v[k] = *(const uint4*)(xr + (size_t)16 * j);
+      }
+#pragma unroll
+      for (int k = 0; k < KP; ++k) {
+        const int j = j0 + threadIdx.x + kPrepThreads * k;
+        if (j < np) {
+          const size_t o = oidx(per * j);
+          if (p.dtype == DMTP_BF16) *(uint4*)((uint16_t*)p.prepared + o) = v[k];
+          else *(uint4*)((float*)p.prepared + o) = v[k];
+        }
+      }
+    }
   }
 }
 
