@@ -326,6 +326,20 @@ __global__ __launch_bounds__(256) void rope_split_kernel(SplitOut o, const int32
   const int m = blockIdx.x;
   const int b = m / S, s = m % S;
   const int G = Hq / Hkv, NQ = S * G, half = d / 2;
+  // rotated heads: Hq query heads then Hkv key heads, four pairs per item;
+  // then the value heads, four elements per item
+  const int quads = (Hq + Hkv) * half / 4, vquads = Hkv * d / 4;
+  // the partial loads of each thread's first items go out before the angles
+  // are computed, so that their latency overlaps the float64 sincos
+  const int e0 = threadIdx.x;
+  SplitAcc<4> p1, p2;
+  SplitAcc<8> pv;
+  if (e0 < quads) {
+    const int h = (4 * e0) / half, i0 = (4 * e0) % half;
+    split_issue4(o, m, h * d + i0, p1);
+    split_issue4(o, m, h * d + i0 + half, p2);
+  }
+  if (e0 < vquads) split_issue4(o, m, (Hq + Hkv) * d + 4 * e0, pv);
   const int pos = ctx_len_of(cu_ctx, b, ctx_rows) + s;
   const double lnb = log((double)rope_base);
   for (int i = threadIdx.x; i < half; i += blockDim.x) {
@@ -336,32 +350,37 @@ __global__ __launch_bounds__(256) void rope_split_kernel(SplitOut o, const int32
     cs[i] = cv;
   }
   __syncthreads();
-  // rotated heads: Hq query heads then Hkv key heads; four pairs per thread
-  const int quads = (Hq + Hkv) * half / 4;
-  for (int e = threadIdx.x; e < quads; e += blockDim.x) {
+  auto rotate = [&](int e, const SplitAcc<4>& a, const SplitAcc<4>& c) __attribute__((always_inline)) {
     const int h = (4 * e) / half, i0 = (4 * e) % half;
-    SplitAcc<4> p1, p2;
-    split_issue4(o, m, h * d + i0, p1);
-    split_issue4(o, m, h * d + i0 + half, p2);
-    const float4 x1 = split_finish4(o, m, h * d + i0, p1), x2 = split_finish4(o, m, h * d + i0 + half, p2);
+    const float4 x1 = split_finish4(o, m, h * d + i0, a), x2 = split_finish4(o, m, h * d + i0 + half, c);
     const float a1[4] = {x1.x, x1.y, x1.z, x1.w}, a2[4] = {x2.x, x2.y, x2.z, x2.w};
     float r1[4], r2[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const double c = cs[i0 + t], sv = sn[i0 + t];
-      r1[t] = (float)((double)a1[t] * c - (double)a2[t] * sv);
-      r2[t] = (float)((double)a2[t] * c + (double)a1[t] * sv);
+      const double cc = cs[i0 + t], sv = sn[i0 + t];
+      r1[t] = (float)((double)a1[t] * cc - (double)a2[t] * sv);
+      r2[t] = (float)((double)a2[t] * cc + (double)a1[t] * sv);
     }
     float* dst = h < Hq ? q + (((size_t)b * Hkv + h / G) * NQ + s * G + h % G) * d
                         : kb + (((size_t)b * Hkv + (h - Hq)) * S + s) * d;
     *(float4*)(dst + i0) = make_float4(r1[0], r1[1], r1[2], r1[3]);
     *(float4*)(dst + i0 + half) = make_float4(r2[0], r2[1], r2[2], r2[3]);
-  }
-  for (int e = threadIdx.x; e < Hkv * d / 4; e += blockDim.x) {
+  };
+  auto value = [&](int e, const SplitAcc<8>& a) __attribute__((always_inline)) {
     const int h = (4 * e) / d, i = (4 * e) % d;
-    SplitAcc<8> pv;
+    *(float4*)(vb + (((size_t)b * Hkv + h) * S + s) * d + i) = split_finish4(o, m, (Hq + Hkv) * d + 4 * e, a);
+  };
+  if (e0 < quads) rotate(e0, p1, p2);
+  if (e0 < vquads) value(e0, pv);
+  for (int e = e0 + blockDim.x; e < quads; e += blockDim.x) {
+    const int h = (4 * e) / half, i0 = (4 * e) % half;
+    split_issue4(o, m, h * d + i0, p1);
+    split_issue4(o, m, h * d + i0 + half, p2);
+    rotate(e, p1, p2);
+  }
+  for (int e = e0 + blockDim.x; e < vquads; e += blockDim.x) {
     split_issue4(o, m, (Hq + Hkv) * d + 4 * e, pv);
-    *(float4*)(vb + (((size_t)b * Hkv + h) * S + s) * d + i) = split_finish4(o, m, (Hq + Hkv) * d + 4 * e, pv);
+    value(e, pv);
   }
 }
 
