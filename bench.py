@@ -57,13 +57,16 @@ HEAD_SOURCES = ("mtp_block_draft_amd/csrc/lm_head.hip", "mtp_block_draft_amd/csr
 TRAFFIC_SUMMARY = "profiles/lm_head_gemm_b32_448rows_counters.md"
 
 
-def head_kernel_name(M: int) -> str:
+def head_kernel_name(M: int, packed: bool = False) -> str:
     """The kernel dmtp_lm_head runs for its vocabulary GEMM over M bf16 rows (H a
     multiple of 128, more than 32 rows): row chunks of at most 448, 64-row tiles
-    per workgroup; three or more tiles take the register-input kernel."""
+    per workgroup; three or more tiles take the register-input kernel, which
+    streams the packed copy of the weights when the call is given one."""
     nc = -(-M // 448)
     tb = -(-(-(-M // nc)) // 64)
-    return f"head_gemm_xr_kernel<{tb}, 4>" if tb >= 3 else f"head_gemm_mf32_kernel<{tb}, 64>"
+    if tb >= 3:
+        return f"head_gemm_xr_kernel<{tb}, 4, {'true' if packed else 'false'}>"
+    return f"head_gemm_mf32_kernel<{tb}, 64>"
 
 
 def head_fingerprint() -> str:
@@ -515,7 +518,7 @@ def main() -> int:
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4),
                 "traffic": None if traffic is None else round(traffic),
-                "kernel": f"{head_kernel_name(M)} of dmtp_lm_head over {M} rows (bf16 GEMM "
+                "kernel": f"{head_kernel_name(M, R.w_head_packed is not None)} of dmtp_lm_head over {M} rows (bf16 GEMM "
                           f"with fused row statistics), timed by the events of its own "
                           f"dispatch on each of {n_k} rounds of a dedicated pass",
                 "algorithmic_flops": flops, "algorithmic_bytes": w_bytes + M * cfg.H * 2,
