@@ -331,11 +331,12 @@ typedef struct {
   void* gemm_start_event;
   void* gemm_stop_event;
   /* Optional: W in the packed layout written by dmtp_head_pack (bf16 only),
-   * 16-byte aligned.  The register-input matrix-core GEMM (bf16, H a multiple
-   * of 128, more than 128 input rows per row chunk of at most 448) then
-   * streams its weight stages from it, each one contiguous 16 KB block,
+   * 16-byte aligned.  The matrix-core GEMMs of bf16 calls with H a multiple
+   * of 128 (more than 32 input rows, or any number when H is above 2048) then
+   * stream their weight stages from it, each one contiguous 16 KB block,
    * instead of 128 runs of 128 bytes of W; results are bit-identical.  The
-   * other kernels read W, which stays required.  NULL: W only. */
+   * weight-streaming kernel of calls of at most 32 rows (H up to 2048) reads
+   * W, which stays required.  NULL: W only. */
   const void* w_packed;
 } dmtp_head_desc;
 

@@ -310,7 +310,7 @@ struct HeadMf32 {
   static_assert(W_INSTR % 4 == 0 && X_INSTR % 4 == 0 && KS % 2 == 0, "tile");
 };
 
-template <int TB, int BK, int NBUF>
+template <int TB, int BK, int NBUF, bool PK = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void head_gemm_mf32_kernel(HeadParams p, int n_mchunks) {
   typedef HeadMf32<TB, BK, NBUF> C;
@@ -360,7 +360,10 @@ void head_gemm_mf32_kernel(HeadParams p, int n_mchunks) {
   for (int q = 0; q < C::PER_WAVE; ++q) {
     if (q < C::WPW) {
       const int idx = (wave * C::WPW + q) * 64 + lane, r = idx / C::CPR;
-      src[q] = W + (size_t)min(v0 + r, V - 1) * H + 8 * swz_chunk<BK>(r, idx % C::CPR);
+      // PK (64-wide slices): the packed copy holds each slice's weight stage
+      // as its LDS image, 16 KB in a row per 128-row tile
+      src[q] = PK ? (const uint16_t*)p.Wp + (size_t)v0 * H + 8 * idx
+                  : W + (size_t)min(v0 + r, V - 1) * H + 8 * swz_chunk<BK>(r, idx % C::CPR);
       dst[q] = (wave * C::WPW + q) * 512;
     } else {
       const int qq = q - C::WPW;
@@ -374,7 +377,7 @@ void head_gemm_mf32_kernel(HeadParams p, int n_mchunks) {
   // from evicting the input rows every workgroup re-reads.
   auto issue_one = [&](int slice, int q) __attribute__((always_inline)) {
     if (q < C::WPW)
-      lds_dma16<2>(src[q] + slice * C::BK, smem + (slice % C::NBUF) * C::STAGE + dst[q]);
+      lds_dma16<2>(src[q] + (size_t)slice * (PK ? C::BV * C::BK : C::BK), smem + (slice % C::NBUF) * C::STAGE + dst[q]);
     else
       lds_dma16(src[q] + (size_t)slice * x_ss, smem + (slice % C::NBUF) * C::STAGE + dst[q]);
   };
@@ -885,18 +888,24 @@ hipError_t launch_head_mf32(const HeadParams& p, int n_mchunks, const GemmEvents
   typedef HeadMf32<TB, BK, NBUF> C;
   static_assert(C::LDS_BYTES <= 160 * 1024, "head LDS");
   static_assert(C::NBUF >= 2 && C::PER_WAVE * (C::NBUF - 2) < 64, "vmcnt");
-  hipError_t e = hipFuncSetAttribute((const void*)head_gemm_mf32_kernel<TB, BK, NBUF>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES);
-  if (e != hipSuccess) return e;
   const int total = p.n_vtiles * n_mchunks;
   const dim3 grid(8 * ((total + 7) / 8));
-  if (ev.start && ev.stop)
-    hipExtLaunchKernelGGL((head_gemm_mf32_kernel<TB, BK, NBUF>), grid, dim3(C::THREADS),
-                          (uint32_t)C::LDS_BYTES, s, ev.start, ev.stop, 0u, p, n_mchunks);
-  else
-    hipLaunchKernelGGL((head_gemm_mf32_kernel<TB, BK, NBUF>), grid, dim3(C::THREADS), C::LDS_BYTES,
-                       s, p, n_mchunks);
-  return hipGetLastError();
+  auto go = [&](auto kern) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)C::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    if (ev.start && ev.stop)
+      hipExtLaunchKernelGGL(kern, grid, dim3(C::THREADS), (uint32_t)C::LDS_BYTES, s, ev.start, ev.stop, 0u, p,
+                            n_mchunks);
+    else
+      hipLaunchKernelGGL(kern, grid, dim3(C::THREADS), C::LDS_BYTES, s, p, n_mchunks);
+    return hipGetLastError();
+  };
+  // the packed copy's stages are 64 wide
+  if constexpr (BK == 64) {
+    if (p.Wp) return go(head_gemm_mf32_kernel<TB, BK, NBUF, true>);
+  }
+  return go(head_gemm_mf32_kernel<TB, BK, NBUF, false>);
 }
 
 

@@ -281,12 +281,14 @@ def test_head_pack_layout(dm):
 
 
 @pytest.mark.parametrize("V,H,M", [(7001, 512, 200), (7001, 512, 448), (20000, 2048, 448),
-                                   (9000, 5120, 256), (3000, 1024, 901)])
+                                   (9000, 5120, 256), (3000, 1024, 901), (9000, 5120, 8),
+                                   (7001, 512, 64), (20000, 2048, 100)])
 def test_lm_head_packed_weights_bit_identical(dm, V, H, M):
     # The register-input GEMM (4, 5 and 7 row tiles per wave; one and three
-    # row chunks; ragged last vocabulary tiles) streaming the packed copy
-    # gives every output bit for bit as it does from W.  A packed copy of a
-    # zero matrix then shows the kernel reads the copy, not W.
+    # row chunks; ragged last vocabulary tiles) and the 64-wide-slice kernel
+    # of calls of 33 .. 128 rows, or of fewer rows when H is above 2048,
+    # streaming the packed copy give every output bit for bit as they do from
+    # W.  A packed copy of a zero matrix then shows the kernel reads the copy.
     print(f"lm_head packed V={V} H={H} M={M}", flush=True)
     W, hid, g, rows, strided, x = _head_case(41 + M, H, V, "bf16", M_norm=0, M_rows=M, M_strided=0)
     Wt, X = _t(W, torch.bfloat16), _t(rows, torch.bfloat16)
