@@ -214,9 +214,9 @@ __global__ __launch_bounds__(kRowThreads) void fuse_prep_kernel(RowSrc x1, RowSr
                                                                 float* __restrict__ out) {
   __shared__ double red[2][kRowThreads / kWave];
   const int r = blockIdx.x;
-  // up to 8 float4 per thread, the residual and the gains are loaded with the
+  // up to 4 float4 per thread, the residual and the gains are loaded with the
   // rows; longer rows load them in the store loop to stay within registers
-  constexpr bool PRE = V4 <= 8;
+  constexpr bool PRE = V4 <= 4;
   constexpr int VP = PRE ? V4 : 1;
   float4 a[V4], c[V4], e[VP], ga[VP], gc[VP];
 #pragma unroll
@@ -507,10 +507,12 @@ RowSrc src_of(const dmtp_rows& r, int w_dtype) {
   return s;
 }
 
-// float4 groups per thread for a row of H elements (H % 4 == 0, H <= 16384).
+// float4 groups per thread for a row of H elements (H % 4 == 0, H <= 16384,
+// so at most 8 with kRowThreads = 512; the callers validate H).
 int v4_of(int H) {
+  static_assert(16384 / 4 <= 8 * kRowThreads, "row width");
   const int g = (H / 4 + kRowThreads - 1) / kRowThreads;
-  return g <= 1 ? 1 : g <= 2 ? 2 : g <= 4 ? 4 : g <= 8 ? 8 : 16;
+  return g <= 1 ? 1 : g <= 2 ? 2 : g <= 4 ? 4 : 8;
 }
 
 }  // namespace
@@ -534,7 +536,7 @@ hipError_t residual_rmsnorm(const SplitOut& x, float* X, size_t ldx, int write_x
     hipLaunchKernelGGL(residual_rmsnorm_kernel<n>, dim3(rows), dim3(kRowThreads), 0, s, x, X, ldx,  \
                        write_x, g, eps, y, pst, H);                                                \
     break;
-    DMTP_CASE(1) DMTP_CASE(2) DMTP_CASE(4) DMTP_CASE(8) DMTP_CASE(16)
+    DMTP_CASE(1) DMTP_CASE(2) DMTP_CASE(4) DMTP_CASE(8)
 #undef DMTP_CASE
   }
   return hipGetLastError();
@@ -550,7 +552,7 @@ hipError_t fuse_prep(const dmtp_fuse_desc& d, uint16_t* cat, hipStream_t s) {
     hipLaunchKernelGGL(fuse_prep_kernel<n>, dim3(d.rows), dim3(kRowThreads), 0, s, a, b, r,         \
                        has_res, d.g1, d.g2, d.eps, d.H, cat, pst, d.out);                          \
     break;
-    DMTP_CASE(1) DMTP_CASE(2) DMTP_CASE(4) DMTP_CASE(8) DMTP_CASE(16)
+    DMTP_CASE(1) DMTP_CASE(2) DMTP_CASE(4) DMTP_CASE(8)
 #undef DMTP_CASE
   }
   return hipGetLastError();
@@ -567,7 +569,7 @@ hipError_t build_slots(const dmtp_draft_desc& d, float* X, const float* g, uint1
                        d.x_t1, d.emb, d.dtype, d.mask_id, d.V, S, d.n_anchor, d.H, X, g, d.eps, y, \
                        pst);                                                                       \
     break;
-    DMTP_CASE(1) DMTP_CASE(2) DMTP_CASE(4) DMTP_CASE(8) DMTP_CASE(16)
+    DMTP_CASE(1) DMTP_CASE(2) DMTP_CASE(4) DMTP_CASE(8)
 #undef DMTP_CASE
   }
   return hipGetLastError();
@@ -608,7 +610,7 @@ hipError_t finish_rows(const SplitOut& x, float* out, size_t ldo, int rows, int 
   case n:                                                                                          \
     hipLaunchKernelGGL(finish_rows_kernel<n>, dim3(rows), dim3(kRowThreads), 0, s, x, out, ldo, H);  \
     break;
-    DMTP_CASE(1) DMTP_CASE(2) DMTP_CASE(4) DMTP_CASE(8) DMTP_CASE(16)
+    DMTP_CASE(1) DMTP_CASE(2) DMTP_CASE(4) DMTP_CASE(8)
 #undef DMTP_CASE
   }
   return hipGetLastError();
@@ -630,7 +632,7 @@ hipError_t final_norm_mask(const SplitOut& x, const float* g, float eps, int B, 
     hipLaunchKernelGGL(final_norm_kernel<n>, dim3(B * (K - 1)), dim3(kRowThreads), 0, s, x, g, eps,  \
                        S, n_anchor, K - 1, H, dtype, out);                                         \
     break;
-    DMTP_CASE(1) DMTP_CASE(2) DMTP_CASE(4) DMTP_CASE(8) DMTP_CASE(16)
+    DMTP_CASE(1) DMTP_CASE(2) DMTP_CASE(4) DMTP_CASE(8)
 #undef DMTP_CASE
   }
   return hipGetLastError();

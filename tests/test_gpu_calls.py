@@ -66,6 +66,13 @@ def test_fuse(dm, dt, rows, H, residual):
     assert err < 1e-5
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_fuse_rows_wider_than_8192(dm, dt):
+    # more than 32 rows take the prologue path; at H = 8256 each of its threads
+    # holds 8 float4 of both streams and loads gains and residual as it stores
+    test_fuse(dm, dt, 33, 8256, True)
+
+
 @pytest.mark.parametrize("rows,H", [(32, 2048), (7, 512), (1, 4096), (8, 5120), (33, 1024)])
 def test_fuse_residual_layout(dm, rows, H):
     """The DMTP residual's operand layout: x1 = ids of T1, x2 = float32 MTP rows,
