@@ -1265,14 +1265,9 @@ __global__ void head_plan_kernel(HeadParams p) {
 // kDrawBlock entries; its mass sum exp((l_j - max) / t) is added lane by lane
 // and then over the 16 lanes in a fixed order.  One exp2 per entry: the pass
 // is bound by the read of the logits.
-#ifndef DMTP_MASS_U
-#define DMTP_MASS_U 4
-#endif
-#ifndef DMTP_MASS_GRID
-#define DMTP_MASS_GRID 8192
-#endif
 constexpr int kMassWaves = 4;
-constexpr int kMassU = DMTP_MASS_U;
+constexpr int kMassU = 4;
+constexpr int kMassGrid = 8192;                  // workgroups of the mass pass (grid-stride over the items)
 constexpr int kMassChunk = kWave * 8 * kMassU;   // 2048 vocabulary entries per item
 static_assert(kMassChunk % kDrawBlock == 0 && kDrawBlock == 16 * 8, "block layout of a mass item");
 static_assert(512 * kMassU == kMassChunk, "group stride");
@@ -1577,7 +1572,7 @@ hipError_t lm_head_run(const dmtp_head_desc& d, int M, void* ws, hipStream_t s) 
   if (d.temperature && !p.block_stats) {
     hipLaunchKernelGGL(head_plan_kernel, dim3(1), dim3(1024), 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(head_mass_kernel, dim3(DMTP_MASS_GRID), dim3(kMassWaves * kWave), 0, s, p);
+    hipLaunchKernelGGL(head_mass_kernel, dim3(kMassGrid), dim3(kMassWaves * kWave), 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   hipLaunchKernelGGL(head_finalize_kernel, dim3(M), dim3(kFinThreads), 0, s, p);

@@ -28,26 +28,12 @@ namespace {
 // 512 entries of each row per work item and a grid that covers every item of
 // a batch-128 draw in one pass: measured faster than longer items (the pass is
 // short, so its memory latency chain dominates)
-#ifndef DMTP_MASS_U
-#define DMTP_MASS_U 1
-#endif
-#ifndef DMTP_MASS_GRID
-#define DMTP_MASS_GRID 8192
-#endif
-#ifndef DMTP_MASS_NT
-#define DMTP_MASS_NT 0
-#endif
 constexpr int kScanWaves = 4;
-constexpr int kScanU = DMTP_MASS_U;
+constexpr int kScanU = 1;
+constexpr int kScanGrid = 8192;   // workgroups of the mass pass (grid-stride over the items)
 
-// 16 bytes of a logits row that is read once (non-temporal when DMTP_MASS_NT)
-__device__ __forceinline__ float4 ld_row4(const float* q) {
-  if constexpr (DMTP_MASS_NT) {
-    const f32x4_t v = __builtin_nontemporal_load((const f32x4_t*)q);
-    return make_float4(v[0], v[1], v[2], v[3]);
-  }
-  return *(const float4*)q;
-}
+// 16 bytes of a logits row
+__device__ __forceinline__ float4 ld_row4(const float* q) { return *(const float4*)q; }
 constexpr int kChunk = kWave * 8 * kScanU;
 static_assert(kChunk % kDrawBlock == 0 && kDrawBlock == 16 * 8, "block layout of a mass item");
 
@@ -491,7 +477,7 @@ hipError_t verify_run(const dmtp_verify_desc& d, void* ws, hipStream_t s) {
   hipLaunchKernelGGL(verify_main_kernel, dim3(1), dim3(vthreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !d.temperature || d.target_only) return e;
-  hipLaunchKernelGGL(verify_mass_kernel, dim3(DMTP_MASS_GRID), dim3(kScanWaves * kWave), 0, s, p);
+  hipLaunchKernelGGL(verify_mass_kernel, dim3(kScanGrid), dim3(kScanWaves * kWave), 0, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(verify_final_kernel, dim3(d.B), dim3(kFinThreads), 0, s, p);
   return hipGetLastError();
