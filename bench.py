@@ -434,7 +434,11 @@ def main() -> int:
           f"{np.median(cold_us):.1f} us", file=sys.stderr, flush=True)
 
     # ---- the dominant kernel, timed by the events attached to its own
-    # dispatch on every round of a dedicated pass
+    # dispatch on every round of a dedicated pass, after untimed rounds that
+    # let the caches and clocks settle from the flushes above
+    n_settle = 16
+    for _ in range(n_settle):
+        one_round()
     n_k = max(args.kernel_rounds, 1)
     gev = []
     for _ in range(n_k):
@@ -465,7 +469,7 @@ def main() -> int:
     torch.cuda.synchronize()
     per_call_us = [1000.0 * float(np.median([evs[k][i][0].elapsed_time(evs[k][i][1])
                                              for k in range(n_diag)])) for i in range(n_calls)]
-    pre_rounds = 2 * n_dist + n_k + 1 + n_diag
+    pre_rounds = 2 * n_dist + n_settle + n_k + 1 + n_diag
 
     # ---- the headline: W untimed rounds, then exactly K rounds back to back,
     # with nothing but the round's calls between the two events.  It runs after
