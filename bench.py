@@ -19,6 +19,9 @@ timed loop:
       of a dedicated pass;
   phases    per-call medians with each call's algorithmic bytes and its
       fraction of the HBM (or matrix-core) peak;
+  attention the drafter's context-attention kernel (first layer), timed by
+      the events of its own dispatch in the same pass as the dominant kernel,
+      against the context K/V bytes it reads;
   cpu_baseline  the CPU oracle on a bounded sample, with the host CPU model.
 """
 from __future__ import annotations
@@ -363,10 +366,13 @@ def main() -> int:
                                         ctypes.c_void_p]
     hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
     head_desc = R.d_head_c
+    draft_desc = R.d_draft
 
-    def one_round(gemm_ev=None, call_evs=None):
+    def one_round(gemm_ev=None, call_evs=None, attn_ev=None):
         head_desc.gemm_start_event = gemm_ev[0] if gemm_ev else None
         head_desc.gemm_stop_event = gemm_ev[1] if gemm_ev else None
+        draft_desc.attn_start_event = attn_ev[0] if attn_ev else None
+        draft_desc.attn_stop_event = attn_ev[1] if attn_ev else None
         for i, (fn, ref) in enumerate(R._fns):
             if call_evs is not None:
                 call_evs[i][0].record(stream)
@@ -440,24 +446,36 @@ def main() -> int:
     for _ in range(n_settle):
         one_round()
     n_k = max(args.kernel_rounds, 1)
-    gev = []
-    for _ in range(n_k):
-        pair = (ctypes.c_void_p(), ctypes.c_void_p())
-        if hip.hipEventCreate(ctypes.byref(pair[0])) or hip.hipEventCreate(ctypes.byref(pair[1])):
-            raise RuntimeError("hipEventCreate failed")
-        gev.append(pair)
+
+    def hip_pairs():
+        out = []
+        for _ in range(n_k):
+            pair = (ctypes.c_void_p(), ctypes.c_void_p())
+            if hip.hipEventCreate(ctypes.byref(pair[0])) or hip.hipEventCreate(ctypes.byref(pair[1])):
+                raise RuntimeError("hipEventCreate failed")
+            out.append(pair)
+        return out
+
+    def hip_elapsed_us(pairs):
+        out = []
+        for a, b in pairs:
+            ms = ctypes.c_float()
+            if hip.hipEventElapsedTime(ctypes.byref(ms), a, b):
+                raise RuntimeError("hipEventElapsedTime failed")
+            out.append(1000.0 * ms.value)
+            hip.hipEventDestroy(a)
+            hip.hipEventDestroy(b)
+        return out
+
+    # the context attention of the drafter's first layer is timed the same
+    # way, in the same rounds (a kernel inside the block_draft call)
+    gev, aev = hip_pairs(), hip_pairs()
     for k in range(n_k):
-        one_round(gemm_ev=gev[k])
+        one_round(gemm_ev=gev[k], attn_ev=aev[k])
     torch.cuda.synchronize()
-    gemm_us = []
-    for a, b in gev:
-        ms = ctypes.c_float()
-        if hip.hipEventElapsedTime(ctypes.byref(ms), a, b):
-            raise RuntimeError("hipEventElapsedTime failed")
-        gemm_us.append(1000.0 * ms.value)
-        hip.hipEventDestroy(a)
-        hip.hipEventDestroy(b)
-    one_round()   # leaves the descriptor without events
+    gemm_us = hip_elapsed_us(gev)
+    attn_us = hip_elapsed_us(aev)
+    one_round()   # leaves the descriptors without events
     torch.cuda.synchronize()
 
     # ---- per-call durations, from a separate pass (events between calls add
@@ -542,6 +560,20 @@ def main() -> int:
             e["mfma_frac"] = round(m["flops"] / (us * 1e-6) / 1e12 / peak, 4)
         phases[name] = e
 
+    # context K/V bytes the first layer's attention kernel reads (the last
+    # `window` rows of each sequence, keys and values of every kv head)
+    L = np.asarray(inp.ctx_len, dtype=np.int64)
+    if cfg.window:
+        L = np.minimum(L, cfg.window)
+    attn_bytes = int(L.sum()) * 2 * cfg.Hkv * cfg.d * (2 if cfg.dtype == "bf16" else 4)
+    attn_avg = float(np.mean(attn_us))
+    attention = {"kernel": "context attention of draft layer 0 (attn_wave_kernel), timed by the "
+                           f"events of its own dispatch on each of {n_k} rounds of the same pass",
+                 "bound": "hbm", "bytes": attn_bytes, "avg_us": round(attn_avg, 2),
+                 "median_us": _pct(attn_us, 50), "p10_us": _pct(attn_us, 10),
+                 "p90_us": _pct(attn_us, 90),
+                 "hbm_frac": round(attn_bytes / (attn_avg * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+
     greedy = not bool((inp.tau > 0).any())
     out = {
         "metric": METRIC, "value": round(rounds_s, 2), "unit": "rounds/s", "n_gpus": 1,
@@ -560,6 +592,7 @@ def main() -> int:
         "round_us_cold": dict(_dist(cold_us), note="each round after 512 MB of writes that "
                               "evict the 256 MB last-level cache"),
         "phases": phases,
+        "attention": attention,
         "roofline": roofline,
         "host_cpu": host_cpu_model(),
     }

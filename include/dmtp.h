@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define DMTP_ABI_VERSION 6
+#define DMTP_ABI_VERSION 7
 
 enum dmtp_status {
   DMTP_OK = 0,
@@ -179,6 +179,15 @@ typedef struct {
   const dmtp_layer* layers;   /* HOST array of n_layers entries */
   const float* g_final;   /* [H] */
   void* out;              /* [B, K - 1, H] in dtype */
+  /* Optional profiling hook: when both are set (hipEvent_t handles created
+   * with timing enabled), the context-attention kernel of layer 0 (bf16
+   * context K/V) is launched with them as its start and stop events, taken
+   * from that kernel's own dispatch, so hipEventElapsedTime(start, stop) is
+   * its duration and no extra command enters the stream.  Ignored when no
+   * context row is read or the context is float32 (then neither is
+   * recorded). */
+  void* attn_start_event;
+  void* attn_stop_event;
 } dmtp_draft_desc;
 
 size_t dmtp_block_draft_ws(const dmtp_draft_desc* d);

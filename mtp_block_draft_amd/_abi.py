@@ -47,7 +47,8 @@ class DraftDesc(ctypes.Structure):
                 ("max_ctx", c_int32), ("ctx_rows", c_int32), ("V", c_int32),
                 ("anchor_ids", c_void_p), ("x_t1", c_void_p), ("mask_id", c_int32),
                 ("emb", c_void_p), ("cu_ctx", c_void_p), ("layers", POINTER(Layer)),
-                ("g_final", c_void_p), ("out", c_void_p)]
+                ("g_final", c_void_p), ("out", c_void_p),
+                ("attn_start_event", c_void_p), ("attn_stop_event", c_void_p)]
 
 
 class HeadSegment(ctypes.Structure):

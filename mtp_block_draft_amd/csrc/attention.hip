@@ -18,6 +18,8 @@
 // single exchange with lane l ^ 32; O^T += V^T P^T takes the V^T operand from
 // the transposing LDS read (ds_read_b64_tr_b16) and P^T straight from the
 // softmax registers.  The float32 K/V path keeps the workgroup kernel.
+#include <hip/hip_ext.h>
+
 #include "dma.hpp"
 #include "kernels.hpp"
 
@@ -768,7 +770,7 @@ size_t attn_ws_bytes(const AttnPlan& p) {
 template <int D, int NBUF>
 hipError_t launch_wave_n(const AttnPlan& p, const float* q, const void* ck, const void* cv,
                          const int32_t* cu, int ctx_rows, float* po, float* pml, float scale,
-                         hipStream_t s) {
+                         hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   typedef WaveAttn<D, NBUF> C;
   hipError_t e = hipFuncSetAttribute((const void*)attn_wave_kernel<D, NBUF>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES);
@@ -776,22 +778,27 @@ hipError_t launch_wave_n(const AttnPlan& p, const float* q, const void* ck, cons
   const int qtiles = p.nqp / 32;
   const int qtw = qtiles < kAttnQtw ? qtiles : kAttnQtw;
   dim3 grid(p.n_chunks, p.Hkv * ((qtiles + qtw - 1) / qtw), p.B);
-  hipLaunchKernelGGL((attn_wave_kernel<D, NBUF>), grid, dim3(64 * qtw), C::LDS_BYTES, s, q, (const uint16_t*)ck,
-                     (const uint16_t*)cv, cu, ctx_rows, p.Hkv, p.NQ, p.nqp, p.chunk, p.n_chunks,
-                     p.window, scale, po, pml);
+  if (e0 && e1)
+    hipExtLaunchKernelGGL((attn_wave_kernel<D, NBUF>), grid, dim3(64 * qtw), (uint32_t)C::LDS_BYTES, s, e0, e1,
+                          0u, q, (const uint16_t*)ck, (const uint16_t*)cv, cu, ctx_rows, p.Hkv, p.NQ, p.nqp,
+                          p.chunk, p.n_chunks, p.window, scale, po, pml);
+  else
+    hipLaunchKernelGGL((attn_wave_kernel<D, NBUF>), grid, dim3(64 * qtw), C::LDS_BYTES, s, q,
+                       (const uint16_t*)ck, (const uint16_t*)cv, cu, ctx_rows, p.Hkv, p.NQ, p.nqp, p.chunk,
+                       p.n_chunks, p.window, scale, po, pml);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_wave(const AttnPlan& p, const float* q, const void* ck, const void* cv,
                        const int32_t* cu, int ctx_rows, float* po, float* pml, float scale,
-                       hipStream_t s) {
-  return launch_wave_n<D, 2>(p, q, ck, cv, cu, ctx_rows, po, pml, scale, s);
+                       hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  return launch_wave_n<D, 2>(p, q, ck, cv, cu, ctx_rows, po, pml, scale, s, e0, e1);
 }
 
 hipError_t attention(const AttnPlan& p, const float* q, const float* kb, const float* vb,
                      const void* ctx_k, const void* ctx_v, const int32_t* cu_ctx, int ctx_rows,
-                     float* ws, uint16_t* o, hipStream_t s) {
+                     float* ws, uint16_t* o, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
   const int nqp = p.nqp;
   const size_t slots = (size_t)p.B * p.Hkv * (p.n_chunks > 0 ? p.n_chunks : 1);
   float* po = ws;
@@ -799,8 +806,8 @@ hipError_t attention(const AttnPlan& p, const float* q, const float* kb, const f
   const float scale = (float)(1.0 / sqrt((double)p.d));
   hipError_t e = hipSuccess;
   if (p.n_chunks > 0 && !p.kv_f32) {
-    e = p.d == 64 ? launch_wave<64>(p, q, ctx_k, ctx_v, cu_ctx, ctx_rows, po, pml, scale, s)
-                  : launch_wave<128>(p, q, ctx_k, ctx_v, cu_ctx, ctx_rows, po, pml, scale, s);
+    e = p.d == 64 ? launch_wave<64>(p, q, ctx_k, ctx_v, cu_ctx, ctx_rows, po, pml, scale, s, ev_start, ev_stop)
+                  : launch_wave<128>(p, q, ctx_k, ctx_v, cu_ctx, ctx_rows, po, pml, scale, s, ev_start, ev_stop);
     if (e != hipSuccess) return e;
   } else if (p.n_chunks > 0) {
     const int cr = ctx_rows;

@@ -115,17 +115,18 @@ struct Stack {
   const dmtp_layer* layers;
   const int32_t* cu_ctx;
   int causal;
+  void* attn_ev[2];   // optional start/stop events of layer 0's context attention
 };
 
 Stack stack_of(const dmtp_draft_desc* d) {
   return Stack{d->B, d->K - 1 + d->n_anchor, d->H, d->Hq, d->Hkv, d->d, d->F, d->n_layers,
                d->dtype, d->eps, d->rope_base, d->window, d->max_ctx, d->ctx_rows, d->layers,
-               d->cu_ctx, 0};
+               d->cu_ctx, 0, {d->attn_start_event, d->attn_stop_event}};
 }
 
 Stack stack_of(const dmtp_mtp_desc* d) {
   return Stack{d->B, d->S, d->H, d->Hq, d->Hkv, d->d, d->F, d->n_layers, d->dtype, d->eps,
-               d->rope_base, 0, d->max_ctx, d->ctx_rows, d->layers, d->cu_ctx, 1};
+               d->rope_base, 0, d->max_ctx, d->ctx_rows, d->layers, d->cu_ctx, 1, {nullptr, nullptr}};
 }
 
 struct DraftWs {
@@ -210,8 +211,10 @@ hipError_t run_stack(const Stack& d, const DraftWs& w, char* b, void* const* k_n
         (h = export_kv(kb, vb, d.B, S, d.Hkv, d.d, d.dtype, k_new ? k_new[l] : nullptr,
                        v_new ? v_new[l] : nullptr, stream)) != hipSuccess)
       break;
-    if ((h = attention(w.plan, q, kb, vb, L.ctx_k, L.ctx_v, d.cu_ctx, d.ctx_rows, aws, o,
-                       stream)) != hipSuccess)
+    const bool ev = l == 0 && d.attn_ev[0] && d.attn_ev[1];
+    if ((h = attention(w.plan, q, kb, vb, L.ctx_k, L.ctx_v, d.cu_ctx, d.ctx_rows, aws, o, stream,
+                       ev ? (hipEvent_t)d.attn_ev[0] : nullptr, ev ? (hipEvent_t)d.attn_ev[1] : nullptr)) !=
+        hipSuccess)
       break;
     GemmArgs g2{o, pst_o, (size_t)od, R, L.wo, wf32, (size_t)od, d.H, od, X, (size_t)d.H, X,
                 (size_t)d.H};
@@ -674,7 +677,7 @@ const char* dmtp_status_str(int s) {
   }
 }
 
-const char* dmtp_version(void) { return "dmtp 0.6.0 (gfx950, ABI 6)"; }
+const char* dmtp_version(void) { return "dmtp 0.7.0 (gfx950, ABI 7)"; }
 
 size_t dmtp_struct_size(int which) {
   switch (which) {

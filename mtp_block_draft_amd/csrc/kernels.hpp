@@ -139,9 +139,12 @@ int attn_max_nq(int d, int kv_f32);
 size_t attn_ws_bytes(const AttnPlan& p);
 // o [B * S, Hq * d] = attention of the block queries over context + block
 // keys, written as bf16 planes [2][B * S][Hq * d].
+// ev_start / ev_stop (both or neither): events of the bf16 context kernel's
+// own dispatch (hipExtLaunchKernel), for timing it alone.
 hipError_t attention(const AttnPlan& p, const float* q, const float* kb, const float* vb,
                      const void* ctx_k, const void* ctx_v, const int32_t* cu_ctx, int ctx_rows,
-                     float* ws, uint16_t* o, hipStream_t s);
+                     float* ws, uint16_t* o, hipStream_t s, hipEvent_t ev_start = nullptr,
+                     hipEvent_t ev_stop = nullptr);
 
 // ---------------------------------------------------------------- LM head --
 size_t lm_head_ws_bytes(const dmtp_head_desc& d, int M);
