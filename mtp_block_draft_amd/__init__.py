@@ -9,7 +9,7 @@ implementation to fall back on.
 from __future__ import annotations
 
 import ctypes
-from typing import Optional, Sequence
+from typing import Optional, Sequence, Tuple
 
 import torch
 
@@ -125,8 +125,11 @@ def block_draft(out: torch.Tensor, *, B: int, H: int, Hq: int, Hkv: int, d: int,
                 x_t1: torch.Tensor, mask_id: int, emb: torch.Tensor, cu_ctx: torch.Tensor,
                 max_ctx: int, ctx_rows: int, g_final: torch.Tensor, eps: float = 1e-6,
                 rope_base: float = 1e6, window: int = 0, ws: Optional[torch.Tensor] = None,
-                run: bool = True) -> DraftDesc:
-    """Block drafter layers + final norm of the MASK slots (dmtp_block_draft)."""
+                run: bool = True, attn_events: Optional[Tuple[int, int]] = None) -> DraftDesc:
+    """Block drafter layers + final norm of the MASK slots (dmtp_block_draft).
+
+    attn_events: optional (start, stop) hipEvent_t handles that time the
+    first layer's context-attention kernel from its own dispatch."""
     D = DraftDesc()
     D.B, D.H, D.Hq, D.Hkv, D.d, D.F = B, H, Hq, Hkv, d, F
     D.n_layers, D.K, D.n_anchor = len(layers), K, n_anchor
@@ -139,6 +142,8 @@ def block_draft(out: torch.Tensor, *, B: int, H: int, Hq: int, Hkv: int, d: int,
     D.anchor_ids = _ptr(anchor_ids)
     D.x_t1, D.mask_id, D.emb, D.cu_ctx = _ptr(x_t1), mask_id, _ptr(emb), _ptr(cu_ctx)
     D.g_final, D.out = _ptr(g_final), _ptr(out)
+    if attn_events is not None:
+        D.attn_start_event, D.attn_stop_event = attn_events
     if run:
         call("block_draft", D, ws)
     return D

@@ -488,6 +488,54 @@ def test_block_draft(dm, dt, shape):
         assert np.mean(got != ref) < 0.02
 
 
+def _hip_runtime():
+    """The HIP runtime torch has loaded, for event handles (ctypes)."""
+    import ctypes
+    path = next(l.split()[-1] for l in open("/proc/self/maps").read().splitlines()
+                if "libamdhip64" in l)
+    hip = ctypes.CDLL(path)
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return hip
+
+
+def test_block_draft_attention_events(dm):
+    # The profiling hook of the draft descriptor: the first layer's context
+    # attention launched with a start/stop event pair of its own dispatch.
+    # Outputs bit for bit as without it, and a positive duration.
+    import ctypes
+    shape = dict(B=3, H=256, Hq=4, Hkv=2, d=64, F=512, NL=2, K=7, n_anchor=2, ctx_lens=[1500, 333, 64])
+    print("block_draft attention events", shape, flush=True)
+    c = _draft_case(77, "bf16", **shape)
+    B, H, K, na = shape["B"], shape["H"], shape["K"], shape["n_anchor"]
+    td, f32 = TD["bf16"], torch.float32
+    lt = [{k: _t(v, f32 if k.startswith("g_") else td) for k, v in L.items()} for L in c["layers"]]
+    Ls = [dm.layer_arg(**L) for L in lt]
+    V = c["emb"].shape[0]
+    hip = _hip_runtime()
+    ev = (ctypes.c_void_p(), ctypes.c_void_p())
+    assert hip.hipEventCreate(ctypes.byref(ev[0])) == 0 and hip.hipEventCreate(ctypes.byref(ev[1])) == 0
+    outs = []
+    for events in (None, (ev[0].value, ev[1].value)):
+        out = torch.empty(B * (K - 1), H, dtype=td, device="cuda")
+        dm.block_draft(out, B=B, H=H, Hq=shape["Hq"], Hkv=shape["Hkv"], d=shape["d"], F=shape["F"], K=K,
+                       n_anchor=na, layers=Ls, anchor_ids=_t(c["anchor"], torch.int32),
+                       x_t1=_t(c["x_t1"], f32), mask_id=V - 1, emb=_t(c["emb"], td),
+                       cu_ctx=_t(c["cu"], torch.int32), max_ctx=int(max(c["ctx_lens"])),
+                       ctx_rows=int(c["cu"][-1]), g_final=_t(c["g_final"], f32), attn_events=events)
+        torch.cuda.synchronize()
+        outs.append(out.view(torch.int16).cpu().numpy())
+    ms = ctypes.c_float()
+    assert hip.hipEventElapsedTime(ctypes.byref(ms), ev[0], ev[1]) == 0
+    hip.hipEventDestroy(ev[0])
+    hip.hipEventDestroy(ev[1])
+    print("  attention kernel", 1000.0 * ms.value, "us")
+    assert ms.value > 0.0
+    np.testing.assert_array_equal(outs[0], outs[1])
+
+
 # ---------------------------------------------------------------- MTP block
 
 
