@@ -22,6 +22,9 @@ timed loop:
   attention the drafter's context-attention kernel (first layer), timed by
       the events of its own dispatch in the same pass as the dominant kernel,
       against the context K/V bytes it reads;
+  verify_scan  (sampled workloads verified by rejection sampling) the
+      verifier's pass over the drawn rows' logits, timed the same way, against
+      the float32 rows it reads;
   cpu_baseline  the CPU oracle on a bounded sample, with the host CPU model.
 """
 from __future__ import annotations
@@ -367,12 +370,18 @@ def main() -> int:
     hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
     head_desc = R.d_head_c
     draft_desc = R.d_draft
+    verify_desc = R.d_verify
+    # the verifier's pass over the drawn rows' logits runs when sequences are
+    # sampled and verified by rejection sampling
+    has_scan = bool((inp.tau > 0).any()) and cfg.verify == "rejection"
 
-    def one_round(gemm_ev=None, call_evs=None, attn_ev=None):
+    def one_round(gemm_ev=None, call_evs=None, attn_ev=None, mass_ev=None):
         head_desc.gemm_start_event = gemm_ev[0] if gemm_ev else None
         head_desc.gemm_stop_event = gemm_ev[1] if gemm_ev else None
         draft_desc.attn_start_event = attn_ev[0] if attn_ev else None
         draft_desc.attn_stop_event = attn_ev[1] if attn_ev else None
+        verify_desc.mass_start_event = mass_ev[0] if mass_ev else None
+        verify_desc.mass_stop_event = mass_ev[1] if mass_ev else None
         for i, (fn, ref) in enumerate(R._fns):
             if call_evs is not None:
                 call_evs[i][0].record(stream)
@@ -470,11 +479,13 @@ def main() -> int:
     # the context attention of the drafter's first layer is timed the same
     # way, in the same rounds (a kernel inside the block_draft call)
     gev, aev = hip_pairs(), hip_pairs()
+    mev = hip_pairs() if has_scan else [None] * n_k
     for k in range(n_k):
-        one_round(gemm_ev=gev[k], attn_ev=aev[k])
+        one_round(gemm_ev=gev[k], attn_ev=aev[k], mass_ev=mev[k])
     torch.cuda.synchronize()
     gemm_us = hip_elapsed_us(gev)
     attn_us = hip_elapsed_us(aev)
+    mass_us = hip_elapsed_us(mev) if has_scan else None
     one_round()   # leaves the descriptors without events
     torch.cuda.synchronize()
 
@@ -574,6 +585,25 @@ def main() -> int:
                  "p90_us": _pct(attn_us, 90),
                  "hbm_frac": round(attn_bytes / (attn_avg * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
 
+    scan = None
+    if has_scan:
+        # the rows the pass reads: p and q of each residual draw, p of each
+        # bonus draw (sampled sequences; the round is seeded, so every round
+        # draws the same)
+        acc_len = R.accept_len.cpu().numpy()
+        samp = np.asarray(inp.tau) > 0
+        n_res = int(((acc_len < cfg.K) & samp).sum())
+        n_bon = int(((acc_len >= cfg.K) & samp).sum())
+        scan_bytes = (2 * n_res + n_bon) * cfg.V * 4
+        m_avg = float(np.mean(mass_us))
+        scan = {"kernel": "verify_mass_kernel (block masses of max(0, p - q) and of p over the drawn "
+                          f"rows), timed by the events of its own dispatch on each of {n_k} rounds of "
+                          "the same pass",
+                "bound": "hbm", "residual_draws": n_res, "bonus_draws": n_bon, "bytes": scan_bytes,
+                "avg_us": round(m_avg, 2), "median_us": _pct(mass_us, 50),
+                "p10_us": _pct(mass_us, 10), "p90_us": _pct(mass_us, 90),
+                "hbm_frac": round(scan_bytes / (m_avg * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+
     greedy = not bool((inp.tau > 0).any())
     out = {
         "metric": METRIC, "value": round(rounds_s, 2), "unit": "rounds/s", "n_gpus": 1,
@@ -596,6 +626,8 @@ def main() -> int:
         "roofline": roofline,
         "host_cpu": host_cpu_model(),
     }
+    if scan is not None:
+        out["verify_scan"] = scan
     if graph_ms_step is not None:
         out["eager_rounds_per_s"] = round(1000.0 / eager_ms_step, 2)
     if args.ctx_kv:

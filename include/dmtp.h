@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define DMTP_ABI_VERSION 7
+#define DMTP_ABI_VERSION 8
 
 enum dmtp_status {
   DMTP_OK = 0,
@@ -413,6 +413,14 @@ typedef struct {
   int32_t* out_tokens;        /* [B, K + 1] */
   int32_t* n_out;             /* [B] */
   int32_t target_only;        /* 0: greedy (t = 0) / rejection (t > 0); 1: target-only */
+  /* Optional profiling hook: when both are set (hipEvent_t handles created
+   * with timing enabled), the pass over the drawn rows' logits (the block
+   * masses of max(0, p - q) and of p) is launched with them as its start and
+   * stop events, taken from that kernel's own dispatch.  Ignored when the
+   * call has no such pass (greedy or target-only; then neither is
+   * recorded). */
+  void* mass_start_event;
+  void* mass_stop_event;
 } dmtp_verify_desc;
 
 size_t dmtp_verify_ws(const dmtp_verify_desc* d);

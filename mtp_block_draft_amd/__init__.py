@@ -271,8 +271,12 @@ def verify(*, B: int, K: int, V: int, t1: torch.Tensor, drafts: Optional[torch.T
            draft_lse: Optional[torch.Tensor] = None, target_lse: Optional[torch.Tensor] = None,
            u_acc: Optional[torch.Tensor] = None, seed: int = 0,
            final_key: Optional[torch.Tensor] = None, target_only: bool = False,
-           ws: Optional[torch.Tensor] = None, run: bool = True) -> VerifyDesc:
-    """Greedy, rejection-sampling or target-only block verification (dmtp_verify)."""
+           ws: Optional[torch.Tensor] = None, run: bool = True,
+           mass_events: Optional[Tuple[int, int]] = None) -> VerifyDesc:
+    """Greedy, rejection-sampling or target-only block verification (dmtp_verify).
+
+    mass_events: optional (start, stop) hipEvent_t handles that time the pass
+    over the drawn rows' logits from its own dispatch."""
     D = VerifyDesc()
     D.B, D.K, D.V = B, K, V
     D.t1, D.drafts, D.target = _ptr(t1), _ptr(drafts), _ptr(target)
@@ -281,6 +285,8 @@ def verify(*, B: int, K: int, V: int, t1: torch.Tensor, drafts: Optional[torch.T
     D.u_acc, D.seed, D.final_key = _ptr(u_acc), seed, _ptr(final_key)
     D.accept_len, D.out_tokens, D.n_out = _ptr(accept_len), _ptr(out_tokens), _ptr(n_out)
     D.target_only = 1 if target_only else 0
+    if mass_events is not None:
+        D.mass_start_event, D.mass_stop_event = mass_events
     if run:
         call("verify", D, ws)
     return D

@@ -73,7 +73,8 @@ class VerifyDesc(ctypes.Structure):
                 ("logits", c_void_p), ("t1_lse", c_void_p), ("draft_lse", c_void_p),
                 ("target_lse", c_void_p), ("u_acc", c_void_p), ("seed", c_uint64),
                 ("final_key", c_void_p), ("accept_len", c_void_p), ("out_tokens", c_void_p),
-                ("n_out", c_void_p), ("target_only", c_int32)]
+                ("n_out", c_void_p), ("target_only", c_int32),
+                ("mass_start_event", c_void_p), ("mass_stop_event", c_void_p)]
 
 
 class StatsDesc(ctypes.Structure):

@@ -677,7 +677,7 @@ const char* dmtp_status_str(int s) {
   }
 }
 
-const char* dmtp_version(void) { return "dmtp 0.7.0 (gfx950, ABI 7)"; }
+const char* dmtp_version(void) { return "dmtp 0.8.0 (gfx950, ABI 8)"; }
 
 size_t dmtp_struct_size(int which) {
   switch (which) {

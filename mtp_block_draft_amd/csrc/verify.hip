@@ -14,6 +14,8 @@
 //          correction/bonus token
 //   stats  acceptance histogram of a batch of verify rounds, added to a running
 //          histogram, and the statistics derived from it
+#include <hip/hip_ext.h>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -477,7 +479,11 @@ hipError_t verify_run(const dmtp_verify_desc& d, void* ws, hipStream_t s) {
   hipLaunchKernelGGL(verify_main_kernel, dim3(1), dim3(vthreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !d.temperature || d.target_only) return e;
-  hipLaunchKernelGGL(verify_mass_kernel, dim3(kScanGrid), dim3(kScanWaves * kWave), 0, s, p);
+  if (d.mass_start_event && d.mass_stop_event)
+    hipExtLaunchKernelGGL(verify_mass_kernel, dim3(kScanGrid), dim3(kScanWaves * kWave), 0u, s,
+                          (hipEvent_t)d.mass_start_event, (hipEvent_t)d.mass_stop_event, 0u, p);
+  else
+    hipLaunchKernelGGL(verify_mass_kernel, dim3(kScanGrid), dim3(kScanWaves * kWave), 0, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(verify_final_kernel, dim3(d.B), dim3(kFinThreads), 0, s, p);
   return hipGetLastError();

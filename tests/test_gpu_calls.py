@@ -730,6 +730,50 @@ def test_verify_greedy_and_sampled(dm, V):
         assert L == k
 
 
+def test_verify_mass_pass_events(dm):
+    # The profiling hook of the verify descriptor: the pass over the drawn
+    # rows' logits launched with a start/stop event pair of its own dispatch.
+    # Outputs bit for bit as without it, and a positive duration.
+    import ctypes
+    B, K, V = 8, 4, 3001
+    print(f"verify mass events B={B} K={K} V={V}", flush=True)
+    r = np.random.default_rng(11)
+    tau = np.full(B, 1.0, np.float32)
+    logits = (1.5 * r.standard_normal((B, 2 * K + 1, V))).astype(np.float32)
+    drafts = r.integers(0, V, size=(B, K)).astype(np.int32)
+    target = logits[:, K:, :].argmax(-1).astype(np.int32)
+    u = (r.integers(0, 1 << 24, size=(B, K)) * 2.0 ** -24).astype(np.float32)
+    u[::2] = 0.0                              # every second sequence accepts all: a bonus draw
+    lse = _softmax_lse(logits.astype(np.float64), 1.0).astype(np.float32)
+    fkeys = np.arange(B, dtype=np.uint64) + np.uint64(1 << 35)
+    hip = _hip_runtime()
+    ev = (ctypes.c_void_p(), ctypes.c_void_p())
+    assert hip.hipEventCreate(ctypes.byref(ev[0])) == 0 and hip.hipEventCreate(ctypes.byref(ev[1])) == 0
+    outs = []
+    for events in (None, (ev[0].value, ev[1].value)):
+        acc = torch.empty(B, dtype=torch.int32, device="cuda")
+        out = torch.empty(B, K + 1, dtype=torch.int32, device="cuda")
+        n_out = torch.empty(B, dtype=torch.int32, device="cuda")
+        dm.verify(B=B, K=K, V=V, t1=_t(drafts[:, 0], torch.int32), drafts=_t(drafts[:, 1:], torch.int32),
+                  target=_t(target, torch.int32), accept_len=acc, out_tokens=out, n_out=n_out,
+                  temperature=_t(tau, torch.float32),
+                  logits=_t(logits.reshape(B * (2 * K + 1), V), torch.float32),
+                  t1_lse=_t(lse[:, 0], torch.float32), draft_lse=_t(lse[:, 1:K], torch.float32),
+                  target_lse=_t(lse[:, K:], torch.float32), u_acc=_t(u, torch.float32), seed=5,
+                  final_key=_t(fkeys.view(np.int64), torch.int64), mass_events=events)
+        torch.cuda.synchronize()
+        outs.append([acc.cpu().numpy(), out.cpu().numpy(), n_out.cpu().numpy()])
+    ms = ctypes.c_float()
+    assert hip.hipEventElapsedTime(ctypes.byref(ms), ev[0], ev[1]) == 0
+    hip.hipEventDestroy(ev[0])
+    hip.hipEventDestroy(ev[1])
+    print("  mass pass", 1000.0 * ms.value, "us; accepted", outs[0][0].tolist())
+    assert ms.value > 0.0
+    assert np.all(outs[0][0][::2] == K)       # the planted bonus draws ran
+    for a, b in zip(outs[0], outs[1]):
+        np.testing.assert_array_equal(a, b)
+
+
 def test_verify_target_only_compares_with_the_picks(dm):
     """Target-only: every sequence, sampled or not, commits the matching prefix of
     its candidates and the target's pick at the first mismatch (or the bonus);
