@@ -204,7 +204,8 @@ def test_long_block16_full_size(rnd):
     cfg = synth.CONFIGS["long_block16_bf16"]
     inp = synth.make_inputs(cfg)
     R, g = _run(rnd, inp)
-    res, rep = compare_round(inp, g, seqs=[0, 2, 5, 7])
+    # with the window test's sequences 3 and 6, every sequence of the batch is checked
+    res, rep = compare_round(inp, g, seqs=[0, 1, 2, 4, 5, 7])
     _report(cfg.name, rep)
 
 
